@@ -1,0 +1,258 @@
+"""Benchmark of the CSA/HCA attention hot path on one MI355X.
+
+Default workload (the configuration the headline metric is quoted on): CSA
+decode in the V4-Flash shape -- 32 sequences of 131072 tokens (32768
+compressed entries of dim 512), 64 indexer heads x 128, top-k 512, 64 query
+heads x 512, a 128-token window and a sink, bf16. One step is one decode token
+per sequence through the whole path:
+    csa_compress   (entry N-1 completes at this token: n is a multiple of m)
+    indexer_score  (the dominant HBM stream)
+    indexer_topk
+    sparse_mqa_decode (split attention + combine)
+Inputs are synthetic (seeded generator), resident in HBM before timing, and
+rotated over several device replicas so that no step reads cache-resident
+data from the previous one.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c5|c4|c3]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA decode tokens/sec + indexer/KV HBM GB/s at 128K–1M ctx; prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4"])
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def _src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_attention_06_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_file: str, src_files):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(p):
+        return None
+    vals = {}
+    for line in open(p):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != _src_hash(src_files):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    a = _args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import long_context_attention_06_amd as L
+    from synth import gen
+
+    cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4}[a.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    x = gen.gen_decode(cfg, with_compress=(cfg.kind == "csa_decode"))
+    print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def bf(v):
+        return torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).to(dev)
+
+    def td(v):
+        return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+
+    B, N, H, D, W, m = cfg.B, cfg.N, cfg.H, cfg.D, cfg.W, cfg.m
+    base = {"q": bf(x["q"]), "kv_comp": bf(x["kv_comp"]), "kv_win": bf(x["kv_win"])}
+    if cfg.kind == "csa_decode":
+        base["q_idx"] = bf(x["q_idx"][:, None])
+        base["w"] = td(x["w"][:, None])
+        if cfg.k_dtype == "fp8":
+            base["k_idx"] = td(x["k_idx_codes"])
+            base["k_scale"] = td(x["k_scale"])
+        else:
+            base["k_idx"] = bf(x["k_idx"])
+        for nm in ("Ca", "Cb", "Za", "Zb"):
+            base[nm] = bf(x[nm])
+    shared = {"sink": td(x["sink"]), "Ba": td(x["Ba"]), "Bb": td(x["Bb"]),
+              "q_pos": td(np.full((B, 1), cfg.n - 1, np.int32)), "n_comp": td(np.full((B,), N, np.int32)),
+              "win_len": td(np.full((B,), min(W, cfg.n), np.int32))}
+    reps = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(a.replicas - 1)]
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    if cfg.kind == "csa_decode":
+        k = cfg.top_k
+        scores = torch.empty((B, 1, N), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+        ws_t = torch.empty(max(1, L.indexer_topk_workspace_bytes(B, 1, N, k)), dtype=torch.uint8, device=dev)
+        ws_a = torch.empty(max(1, L.sparse_mqa_decode_workspace_bytes(B, H, D, k, W)), dtype=torch.uint8, device=dev)
+    else:
+        ws_a = torch.empty(max(1, L.hca_dense_mqa_workspace_bytes(B, H, D, N, W)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    def rec(ev, i):
+        if ev is not None:
+            ev[i].record(stream)
+
+    def step(r, ev=None):
+        rec(ev, 0)
+        if cfg.kind == "csa_decode":
+            L.csa_compress(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"], r["kv_comp"], m=m,
+                           tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, stream=s)
+            rec(ev, 1)
+            L.indexer_score(r["q_idx"], r["w"], r["k_idx"], r.get("k_scale"), shared["q_pos"], shared["n_comp"],
+                            scores, m=m, stream=s)
+            rec(ev, 2)
+            L.indexer_topk(scores, shared["q_pos"], shared["n_comp"], idx, m=m, ws=ws_t, stream=s)
+            rec(ev, 3)
+            L.sparse_mqa_decode(r["q"], r["kv_comp"], idx.view(B, k), r["kv_win"], shared["win_len"], shared["sink"],
+                                out, scale=1.0, ws=ws_a, stream=s)
+        else:
+            rec(ev, 1)
+            rec(ev, 2)
+            rec(ev, 3)
+            L.hca_dense_mqa(r["q"], r["kv_comp"], shared["n_comp"], shared["q_pos"].view(B), r["kv_win"],
+                            shared["win_len"], shared["sink"], out, m=m, ws=ws_a, stream=s)
+
+    for i in range(a.warmup):
+        step(reps[i % len(reps)])
+    torch.cuda.synchronize()
+    # (1) the headline: K plain steps between two events
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e_start.record(stream)
+    t_wall = time.perf_counter()
+    for i in range(a.steps):
+        step(reps[i % len(reps)])
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = e_start.elapsed_time(e_end) / a.steps
+    # (2) the same K steps with an event at every phase boundary:
+    # [0] compress [1] indexer scan [2] top-k [3] attention [next 0]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    e_fin = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    for i in range(a.steps):
+        step(reps[i % len(reps)], evs[i])
+    e_fin.record(stream)
+    torch.cuda.synchronize()
+    nxt = [evs[i + 1][0] for i in range(a.steps - 1)] + [e_fin]
+    ph = np.array([[evs[i][0].elapsed_time(evs[i][1]), evs[i][1].elapsed_time(evs[i][2]),
+                    evs[i][2].elapsed_time(evs[i][3]), evs[i][3].elapsed_time(nxt[i])] for i in range(a.steps)])
+    ph_mean = ph.mean(axis=0)
+    scan_avg = float(ph_mean[1])
+    attn_avg = float(ph_mean[3])
+
+    tokens_per_s = B / (ms_step * 1e-3)
+    res = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+    }
+    if cfg.kind == "csa_decode":
+        kbytes = N * cfg.D_I * (1 if cfg.k_dtype == "fp8" else 2) + (N * 4 if cfg.k_dtype == "fp8" else 0)
+        scan_bytes = B * (kbytes + cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4)  # keys (+scales), q_idx, w
+        step_bytes = B * (kbytes + cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4 + k * D * 2 + W * D * 2 + H * D * 2 * 2 + k * 4)
+        res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
+                         "m": m, "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I,
+                         "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype}
+        res["roofline"] = {"bound": "hbm", "kernel": "idx_scan_bf16_kernel", "achieved": round(scan_bytes / (scan_avg * 1e-3) / 1e9, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(scan_bytes / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "traffic": _traffic("idx_scan_c2_traffic.txt" if a.workload == "c2" else "idx_scan_c5_traffic.txt",
+                                               ["indexer.hip", "common.h"]),
+                           "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_ms": round(scan_avg, 4)}
+        res["phases_ms"] = {"compress": round(float(ph_mean[0]), 4), "indexer_scan": round(scan_avg, 4),
+                            "topk": round(float(ph_mean[2]), 4), "attention": round(attn_avg, 4)}
+        res["step_hbm_gbs"] = round(step_bytes / (ms_step * 1e-3) / 1e9, 1)
+        res["indexer_kv_hbm_gbs"] = res["roofline"]["achieved"]
+    else:
+        hbytes = B * ((N + W) * D * 2 + H * D * 2 * 2)
+        res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
+                         "m": m, "heads": H, "head_dim": D, "window": W}
+        res["roofline"] = {"bound": "hbm", "kernel": "attn_kernel (HCA split) + combine",
+                           "achieved": round(hbytes / (attn_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(hbytes / (attn_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "traffic": None, "algorithmic_bytes_per_launch": hbytes, "avg_launch_ms": round(attn_avg, 4)}
+    res["wall_s_timed"] = round(wall, 3)
+
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(cfg, x, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, x, budget_s: float):
+    """The float64 oracle on the host cores, on whole sequences of the same
+    workload until the time budget is used (at least one sequence)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    done = 0
+    t0 = time.perf_counter()
+    m = cfg.m
+    while done < cfg.B and (done == 0 or time.perf_counter() - t0 < budget_s):
+        b = done
+        if cfg.kind == "csa_decode":
+            ent = oracle.compress(x["Ca"][b], x["Cb"][b], x["Za"][b], x["Zb"][b], x["Ba"], x["Bb"], m,
+                                  blocks=range(1, 2))[0]
+            comp = x["kv_comp"][b].astype(np.float64)
+            comp[cfg.N - 1] = ent
+            if cfg.k_dtype == "fp8":
+                keys, sc = oracle.e4m3_decode(x["k_idx_codes"][b]), x["k_scale"][b]
+            else:
+                keys, sc = x["k_idx"][b], None
+            oracle.csa_query(x["q"][b], x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, cfg.N, m, cfg.top_k,
+                             x["kv_win"][b], x["sink"], k_scale=sc)
+        else:
+            oracle.hca_query(x["q"][b], x["kv_comp"][b], cfg.n - 1, cfg.N, m, x["kv_win"][b], x["sink"])
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {cfg.B} sequences of one decode step ({cfg.name}), float64 NumPy, "
+                      f"{dt:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

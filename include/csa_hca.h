@@ -1,0 +1,208 @@
+/*
+ * csa_hca.h — C ABI of the MI355X (gfx950) library for DeepSeek-V4's hybrid
+ * long-context attention: CSA (compressed sparse attention) and HCA (heavily
+ * compressed attention).
+ *
+ * What the calls compute (sources are web pages on DeepSeek-V4, cited by
+ * title and section):
+ *   [CSDN]   "DeepSeek V4 脱离 CUDA 全栈国产化：1.6T MoE 逐层拆解 + 昇腾迁移数据"
+ *            (deepseek.csdn.net), section 二 "CSA + HCA 混合注意力": CSA is
+ *            compress -> lightning indexer + top-k -> shared-KV MQA (the
+ *            CComp_i equation gives the compression); HCA compresses 128
+ *            tokens per entry and attends densely, with a 128-token window.
+ *   [LIDUOS] liduos.com "deepseek-v4-engineering-tradeoffs", section
+ *            "1M Context 的结构与取舍": the sliding window keeps the latest 128
+ *            raw tokens; an attention sink lets a head attend to nothing.
+ *   [LQNN]   "Deepseek-V4 技术报告里最值得复现的三个改动" (m.lqnn.cn), section 3
+ *            (m=4, 64x128 indexer, top_k 512, m'=128, 64 heads x 512, window
+ *            128) and section 5 (tokens after the last full block of m are not
+ *            compressed).
+ *   [WIKI]   DeepTech wiki summary, batch-invariance note: a token's output is
+ *            bitwise the same wherever it sits in a batch.
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers owned by the caller, unless stated. The
+ *     library allocates nothing, frees nothing and keeps no state between
+ *     calls. Scratch memory comes in through (ws, ws_bytes); each op has a
+ *     pure host-side query <op>_workspace_bytes(...). ws must be 256-byte
+ *     aligned; its contents on entry do not matter.
+ *   - stream is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *     kernels on it: no host synchronisation, no device-to-host copy, no
+ *     memset; they can be captured in a HIP graph.
+ *   - Tensors are dense and row-major; the innermost index is the feature.
+ *     Indices, positions and lengths are int32.
+ *   - dtype codes: CSA_F32, CSA_BF16 (storage of activations and caches),
+ *     CSA_FP8_E4M3 (OCP E4M3 "FN", indexer keys only, with a per-entry fp32
+ *     scale). Arithmetic is fp32 (bf16 x bf16 products accumulate in fp32).
+ *   - Return codes: CSA_OK, CSA_INVALID_ARG (a null pointer that must not be
+ *     null, a negative or inconsistent size), CSA_UNSUPPORTED (a valid
+ *     combination with no kernel instantiation), CSA_WORKSPACE_TOO_SMALL,
+ *     CSA_HIP_ERROR (a launch failed). Argument checks finish before the first
+ *     HIP call, so a rejected call touches neither the device nor the stream.
+ *     csa_last_error() returns the calling thread's message for its last
+ *     failed call. No C++ exception crosses this boundary.
+ *   - Device-side data (indices, positions, lengths) is not validated on the
+ *     host; kernels clamp it: an index outside [0, N_max) is skipped, a
+ *     length is clamped to its buffer, a position to the rows that exist.
+ *   - Results are deterministic and batch invariant: reductions run in a
+ *     fixed order and split counts depend on per-sequence shape arguments
+ *     only, never on the batch size or on which sequence is which.
+ */
+#ifndef CSA_HCA_H
+#define CSA_HCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_HCA_VERSION 1
+
+enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 };
+
+enum {
+  CSA_OK = 0,
+  CSA_INVALID_ARG = -1,
+  CSA_UNSUPPORTED = -2,
+  CSA_WORKSPACE_TOO_SMALL = -3,
+  CSA_HIP_ERROR = -4
+};
+
+/* csa_compress flags */
+enum { CSA_OVERLAP = 1, CSA_JOINT_SOFTMAX = 2 };
+
+int csa_hca_version(void);
+const char* csa_last_error(void);
+
+/*
+ * csa_compress — KV compression, [CSDN] CSA step 1 (the CComp_i equation).
+ *
+ * For every sequence b < B and block i in [blk_begin, blk_end), channel c < d:
+ *   out[b, i, c] = sum_j softmax_j(Za[t_a(j), c] + Ba[j, c]) * Ca[t_a(j), c]
+ *                + sum_j softmax_j(Zb[t_b(j), c] + Bb[j, c]) * Cb[t_b(j), c]
+ * with t_a(j) = m*i + j, t_b(j) = m*(i-1) + j, j < m; the second (overlap)
+ * term is present only with CSA_OVERLAP and i >= 1. With CSA_JOINT_SOFTMAX
+ * (requires CSA_OVERLAP) one softmax runs over all 2m logits of both blocks.
+ *
+ *   Ca, Cb, Za, Zb : [B, n_rows, d] in in_dt; row r of sequence b holds token
+ *                    t = tok_begin + r. Cb, Zb, Bb may be NULL without
+ *                    CSA_OVERLAP (single-branch compression, as for HCA).
+ *   Ba, Bb         : [m, d] fp32 positional biases (index j = position in block).
+ *   out            : [B, out_cap, d] in out_dt; only rows [blk_begin, blk_end)
+ *                    are written (decode appends one block: blk_end-1 .. blk_end).
+ * Requirements: m*blk_end <= tok_begin + n_rows (a block is formed only from m
+ * complete tokens: trailing tokens form no entry, [LQNN] section 5);
+ * m*blk_begin >= tok_begin, and with CSA_OVERLAP and blk_begin >= 1 also
+ * m*(blk_begin-1) >= tok_begin; blk_end <= out_cap; 1 <= m <= 1024.
+ * Supported: in_dt in {F32, BF16}, out_dt in {F32, BF16}, d % 8 == 0.
+ */
+int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
+                 const float* Ba, const float* Bb, void* out,
+                 int64_t B, int64_t n_rows, int64_t tok_begin, int d, int m,
+                 int64_t blk_begin, int64_t blk_end, int64_t out_cap,
+                 int flags, int in_dt, int out_dt, void* stream);
+
+/*
+ * indexer_score — lightning-indexer scores, [CSDN] CSA step 2.
+ *
+ * For query t of sequence b at position p = q_pos[b, t], the visible entries
+ * are i < V = min(n_comp[b], floor((p+1)/m), N_max), and
+ *   scores[b, t, i] = sum_h w[b, t, h] * max(0, sigma_i * <q_idx[b,t,h,:], k_idx[b,i,:]>)
+ * where sigma_i = k_scale[b, i] for fp8 keys and 1 otherwise.
+ *
+ *   q_idx   : [B, Tq, H_I, D_I] in q_dt          w      : [B, Tq, H_I] fp32
+ *   k_idx   : [B, N_max, D_I] in k_dt            k_scale: [B, N_max] fp32 (fp8 keys only, else NULL)
+ *   q_pos   : [B, Tq] int32                      n_comp : [B] int32
+ *   scores  : [B, Tq, N_max] fp32; entries i >= V are left unspecified.
+ * Supported: (H_I, D_I) in {(64, 128) with q_dt BF16 and k_dt BF16 or FP8_E4M3,
+ * (4, 32) with q_dt = k_dt = F32}. N_max <= 2^24.
+ */
+int indexer_score(const void* q_idx, const float* w, const void* k_idx, const float* k_scale,
+                  const int32_t* q_pos, const int32_t* n_comp,
+                  int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m,
+                  int q_dt, int k_dt, float* scores, void* stream);
+
+/*
+ * indexer_topk — top-k selection over indexer scores, [CSDN] CSA step 2.
+ *
+ * Row (b, t) keeps K' = min(top_k, V) entries with the largest scores among
+ * i < V (V as in indexer_score); equal scores go to the lower index. The
+ * kept indices are written to topk_idx[b, t, 0..K'-1] in ascending index
+ * order and the rest of the row is -1. topk_score (nullable) receives the
+ * matching scores (rest: -inf). Exact: no approximate selection.
+ *   scores : [B, Tq, N_max] fp32     topk_idx : [B, Tq, top_k] int32
+ * Supported: 1 <= top_k <= 4096, N_max <= 2^24.
+ */
+int indexer_topk(const float* scores, const int32_t* q_pos, const int32_t* n_comp,
+                 int64_t B, int64_t Tq, int64_t N_max, int m, int top_k,
+                 int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes, void* stream);
+size_t indexer_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k);
+
+/* indexer_score_topk — indexer_score followed by indexer_topk, the scores
+ * living in the workspace. Same arguments and support as the two calls. */
+int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, const float* k_scale,
+                       const int32_t* q_pos, const int32_t* n_comp,
+                       int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int top_k,
+                       int q_dt, int k_dt, int32_t* topk_idx, float* topk_score,
+                       void* ws, size_t ws_bytes, void* stream);
+size_t indexer_score_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k);
+
+/*
+ * Shared-KV multi-query attention with a sink ([CSDN] CSA step 3 and HCA;
+ * [LIDUOS] window and sink). For one query token and every head h < H over a
+ * multiset R of rows (each row is both key and value):
+ *   l_r = scale * <q_h, r>,  M = max(sink_h, max_r l_r),
+ *   Z_h = e^{sink_h - M} + sum_r e^{l_r - M},
+ *   out_h = sum_r e^{l_r - M} r / Z_h,   lse_h = M + ln Z_h.
+ * sink may be NULL (no sink: sink_h = -inf). With R empty and no sink,
+ * out_h = 0 and lse_h = -inf. Rows present in two sources count twice.
+ * Supported: (H, D) in {(64, 512) with kv_dt BF16, (4, 64) with kv_dt F32};
+ * out_dt in {F32, BF16}; q has the dtype kv_dt.
+ */
+
+/* sparse_mqa_decode — one query per sequence (position: the last token).
+ *   q      : [B, H, D]           kv_comp : [B, N_max, D]
+ *   topk_idx : [B, top_k] int32, -1 = empty slot; rows kv_comp[b, idx]
+ *   kv_win : [B, W, D]; rows 0 .. win_len[b]-1 are the window (any order)
+ *   win_len: [B] int32           sink    : [H] fp32 (nullable)
+ *   out    : [B, H, D] in out_dt lse     : [B, H] fp32 (nullable)
+ * R = {kv_comp[b, i] : i in topk_idx[b]} + the win_len[b] window rows. */
+int sparse_mqa_decode(const void* q, const void* kv_comp, const int32_t* topk_idx,
+                      const void* kv_win, const int32_t* win_len, const float* sink, float scale,
+                      int64_t B, int H, int D, int64_t N_max, int top_k, int W,
+                      int kv_dt, int out_dt, void* out, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
+size_t sparse_mqa_decode_workspace_bytes(int64_t B, int H, int D, int top_k, int W);
+
+/* sparse_mqa_prefill — Tq queries of one sequence.
+ *   q      : [Tq, H, D]          kv_comp : [N, D]
+ *   topk_idx : [Tq, top_k] int32 (-1 = empty)
+ *   kv_tok : [T_tok, D] raw per-token KV; query t at position p = q_pos[t]
+ *            uses window rows kv_tok[max(0, p-W+1) .. p] ([LIDUOS]: the latest
+ *            W raw tokens, the current one included)
+ *   out    : [Tq, H, D]          lse : [Tq, H] (nullable) */
+int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_idx,
+                       const void* kv_tok, const int32_t* q_pos, const float* sink, float scale,
+                       int64_t Tq, int H, int D, int64_t N, int64_t T_tok, int top_k, int W,
+                       int kv_dt, int out_dt, void* out, float* lse,
+                       void* ws, size_t ws_bytes, void* stream);
+size_t sparse_mqa_prefill_workspace_bytes(int64_t Tq, int H, int D, int top_k, int W);
+
+/* hca_dense_mqa — HCA decode: one query per sequence over ALL visible
+ * compressed entries i < V = min(n_comp[b], floor((q_pos[b]+1)/m), N_max)
+ * plus the win_len[b] window rows. Shapes as in sparse_mqa_decode, with
+ * n_comp, q_pos : [B] int32. */
+int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, const int32_t* q_pos,
+                  int m, const void* kv_win, const int32_t* win_len, const float* sink, float scale,
+                  int64_t B, int H, int D, int64_t N_max, int W,
+                  int kv_dt, int out_dt, void* out, float* lse,
+                  void* ws, size_t ws_bytes, void* stream);
+size_t hca_dense_mqa_workspace_bytes(int64_t B, int H, int D, int64_t N_max, int W);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_HCA_H */

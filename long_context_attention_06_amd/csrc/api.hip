@@ -1,0 +1,334 @@
+// C ABI of the CSA/HCA attention library: argument validation (host only,
+// before any HIP call), workspace sizing, split planning and kernel dispatch.
+// The operations and their sources are documented in include/csa_hca.h.
+#include <string>
+
+#include "../../include/csa_hca.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define REQ(cond, code, msg)          \
+  do {                                \
+    if (!(cond)) return fail(code, msg); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char* op) {
+  if (e == hipSuccess) return CSA_OK;
+  return fail(CSA_HIP_ERROR, std::string(op) + ": " + hipGetErrorString(e));
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Rows per split of the decode attention. Depends only on per-query shape
+// arguments, so a sequence's result never depends on the batch.
+constexpr int SPARSE_SPLIT_ROWS = 128;
+constexpr int HCA_SPLIT_ROWS = 512;
+
+int nsplit_for(int64_t slots, int rows) { return slots <= rows ? 1 : (int)((slots + rows - 1) / rows); }
+
+size_t attn_ws(int64_t nq, int H, int D, int nsplit) {
+  if (nsplit <= 1) return 0;
+  return round256((size_t)nq * nsplit * H * D * 4) + round256((size_t)nq * nsplit * H * 2 * 4);
+}
+
+bool attn_supported(int H, int D, int kv_dt) {
+  return (kv_dt == CSA_BF16 && D == 512 && H > 32 && H <= 64) || (kv_dt == CSA_F32 && D == 64 && H >= 1 && H <= 32);
+}
+
+int check_attn_common(const void* q, const void* out, int H, int D, int kv_dt, int out_dt, int W, int top_k) {
+  REQ(q && out, CSA_INVALID_ARG, "q and out must not be NULL");
+  REQ(H > 0 && D > 0, CSA_INVALID_ARG, "H and D must be positive");
+  REQ(W >= 0 && top_k >= 0, CSA_INVALID_ARG, "W and top_k must be >= 0");
+  REQ(kv_dt == CSA_F32 || kv_dt == CSA_BF16 || kv_dt == CSA_FP8_E4M3, CSA_INVALID_ARG, "unknown kv_dt");
+  REQ(out_dt == CSA_F32 || out_dt == CSA_BF16 || out_dt == CSA_FP8_E4M3, CSA_INVALID_ARG, "unknown out_dt");
+  REQ(out_dt != CSA_FP8_E4M3, CSA_UNSUPPORTED, "out_dt must be F32 or BF16");
+  REQ(attn_supported(H, D, kv_dt), CSA_UNSUPPORTED,
+      "unsupported (H, D, kv_dt): supported are (33..64, 512, BF16) and (1..32, 64, F32)");
+  REQ(aligned16(q), CSA_INVALID_ARG, "q must be 16-byte aligned");
+  REQ(out_dt != CSA_F32 || aligned16(out), CSA_INVALID_ARG, "out must be 16-byte aligned");
+  return CSA_OK;
+}
+
+int check_indexer(const void* q_idx, const float* w, const void* k_idx, const float* k_scale, const int32_t* q_pos,
+                  const int32_t* n_comp, int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int q_dt,
+                  int k_dt) {
+  REQ(q_idx && w && k_idx && q_pos && n_comp, CSA_INVALID_ARG, "q_idx, w, k_idx, q_pos, n_comp must not be NULL");
+  REQ(B >= 0 && Tq >= 0 && N_max >= 0, CSA_INVALID_ARG, "B, Tq, N_max must be >= 0");
+  REQ(H_I > 0 && D_I > 0, CSA_INVALID_ARG, "H_I and D_I must be positive");
+  REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");
+  REQ(q_dt >= CSA_F32 && q_dt <= CSA_FP8_E4M3 && k_dt >= CSA_F32 && k_dt <= CSA_FP8_E4M3, CSA_INVALID_ARG,
+      "unknown dtype");
+  REQ(k_dt != CSA_FP8_E4M3 || k_scale, CSA_INVALID_ARG, "fp8 keys need k_scale");
+  REQ(N_max <= (int64_t(1) << 24), CSA_UNSUPPORTED, "N_max above 2^24");
+  REQ(B * Tq <= 65535, CSA_UNSUPPORTED, "B*Tq above 65535 rows per call");
+  const bool big = H_I == 64 && D_I == 128 && q_dt == CSA_BF16 && (k_dt == CSA_BF16 || k_dt == CSA_FP8_E4M3);
+  const bool tiny = H_I <= 32 && D_I == 32 && q_dt == CSA_F32 && k_dt == CSA_F32;
+  REQ(big || tiny, CSA_UNSUPPORTED,
+      "unsupported indexer shape/dtype: (64, 128) bf16 q with bf16/fp8 keys, or (<=32, 32) fp32");
+  REQ(aligned16(q_idx) && aligned16(k_idx), CSA_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
+  return CSA_OK;
+}
+
+int check_topk(const float* scores, const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq,
+               int64_t N_max, int m, int top_k, const int32_t* topk_idx) {
+  REQ(scores && q_pos && n_comp && topk_idx, CSA_INVALID_ARG, "scores, q_pos, n_comp, topk_idx must not be NULL");
+  REQ(B >= 0 && Tq >= 0 && N_max >= 0, CSA_INVALID_ARG, "B, Tq, N_max must be >= 0");
+  REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");
+  REQ(top_k >= 1, CSA_INVALID_ARG, "top_k must be >= 1");
+  REQ(top_k <= 4096, CSA_UNSUPPORTED, "top_k above 4096");
+  REQ(N_max <= (int64_t(1) << 24), CSA_UNSUPPORTED, "N_max above 2^24");
+  REQ(B * Tq <= 0x7fffffff, CSA_UNSUPPORTED, "too many rows");
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_hca_version(void) { return CSA_HCA_VERSION; }
+
+const char* csa_last_error(void) { return g_err.c_str(); }
+
+int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba, const float* Bb,
+                 void* out, int64_t B, int64_t n_rows, int64_t tok_begin, int d, int m, int64_t blk_begin,
+                 int64_t blk_end, int64_t out_cap, int flags, int in_dt, int out_dt, void* stream) {
+  REQ((flags & ~(CSA_OVERLAP | CSA_JOINT_SOFTMAX)) == 0, CSA_INVALID_ARG, "unknown flags");
+  const bool overlap = flags & CSA_OVERLAP, joint = flags & CSA_JOINT_SOFTMAX;
+  REQ(!joint || overlap, CSA_INVALID_ARG, "CSA_JOINT_SOFTMAX needs CSA_OVERLAP");
+  REQ(Ca && Za && Ba && out, CSA_INVALID_ARG, "Ca, Za, Ba, out must not be NULL");
+  REQ(!overlap || (Cb && Zb && Bb), CSA_INVALID_ARG, "CSA_OVERLAP needs Cb, Zb, Bb");
+  REQ(B >= 0 && n_rows >= 0 && tok_begin >= 0, CSA_INVALID_ARG, "B, n_rows, tok_begin must be >= 0");
+  REQ(d > 0, CSA_INVALID_ARG, "d must be positive");
+  REQ(m >= 1 && m <= 1024, CSA_INVALID_ARG, "m must be in [1, 1024]");
+  REQ(0 <= blk_begin && blk_begin <= blk_end, CSA_INVALID_ARG, "need 0 <= blk_begin <= blk_end");
+  REQ(blk_end <= out_cap, CSA_INVALID_ARG, "blk_end exceeds out_cap");
+  REQ(in_dt == CSA_F32 || in_dt == CSA_BF16 || in_dt == CSA_FP8_E4M3, CSA_INVALID_ARG, "unknown in_dt");
+  REQ(out_dt == CSA_F32 || out_dt == CSA_BF16 || out_dt == CSA_FP8_E4M3, CSA_INVALID_ARG, "unknown out_dt");
+  REQ(in_dt != CSA_FP8_E4M3 && out_dt != CSA_FP8_E4M3, CSA_UNSUPPORTED, "compress supports F32 and BF16 only");
+  REQ(d % 8 == 0, CSA_UNSUPPORTED, "d must be a multiple of 8");
+  if (blk_end > blk_begin) {
+    REQ(m * blk_end <= tok_begin + n_rows, CSA_INVALID_ARG,
+        "block range needs tokens beyond the provided rows (a block is formed only from m complete tokens)");
+    REQ(m * blk_begin >= tok_begin, CSA_INVALID_ARG, "block range starts before tok_begin");
+    REQ(!overlap || blk_begin == 0 || m * (blk_begin - 1) >= tok_begin, CSA_INVALID_ARG,
+        "overlap branch of blk_begin needs the previous block's tokens");
+  }
+  REQ(aligned16(Ca) && aligned16(Za) && aligned16(Ba) && aligned16(out), CSA_INVALID_ARG,
+      "tensors must be 16-byte aligned");
+  REQ(!overlap || (aligned16(Cb) && aligned16(Zb) && aligned16(Bb)), CSA_INVALID_ARG,
+      "tensors must be 16-byte aligned");
+  csa::CompressLaunch a{Ca, Cb, Za, Zb, Ba, Bb, out, B, n_rows, tok_begin, blk_begin, blk_end, out_cap, d, m,
+                        overlap, joint, in_dt, out_dt};
+  return hip_status(csa::run_compress(a, (hipStream_t)stream), "csa_compress");
+}
+
+int indexer_score(const void* q_idx, const float* w, const void* k_idx, const float* k_scale, const int32_t* q_pos,
+                  const int32_t* n_comp, int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int q_dt,
+                  int k_dt, float* scores, void* stream) {
+  int rc = check_indexer(q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, q_dt, k_dt);
+  if (rc) return rc;
+  REQ(scores, CSA_INVALID_ARG, "scores must not be NULL");
+  csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, scores};
+  return hip_status(csa::run_indexer(a, (hipStream_t)stream), "indexer_score");
+}
+
+size_t indexer_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k) {
+  if (B < 0 || Tq < 0 || N_max < 0) return 0;
+  return round256(csa::topk_ws_bytes(B, Tq, N_max, top_k));
+}
+
+int indexer_topk(const float* scores, const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq,
+                 int64_t N_max, int m, int top_k, int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                 void* stream) {
+  int rc = check_topk(scores, q_pos, n_comp, B, Tq, N_max, m, top_k, topk_idx);
+  if (rc) return rc;
+  const size_t need = indexer_topk_workspace_bytes(B, Tq, N_max, top_k);
+  REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
+  csa::TopkLaunch a{scores, q_pos, n_comp, B, Tq, N_max, m, top_k, topk_idx, topk_score, ws, ws_bytes};
+  return hip_status(csa::run_topk(a, (hipStream_t)stream), "indexer_topk");
+}
+
+size_t indexer_score_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k) {
+  if (B < 0 || Tq < 0 || N_max < 0) return 0;
+  return round256((size_t)B * Tq * N_max * 4) + indexer_topk_workspace_bytes(B, Tq, N_max, top_k);
+}
+
+int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, const float* k_scale,
+                       const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq, int H_I, int D_I,
+                       int64_t N_max, int m, int top_k, int q_dt, int k_dt, int32_t* topk_idx, float* topk_score,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_indexer(q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, q_dt, k_dt);
+  if (rc) return rc;
+  REQ(topk_idx, CSA_INVALID_ARG, "topk_idx must not be NULL");
+  REQ(top_k >= 1, CSA_INVALID_ARG, "top_k must be >= 1");
+  REQ(top_k <= 4096, CSA_UNSUPPORTED, "top_k above 4096");
+  const size_t need = indexer_score_topk_workspace_bytes(B, Tq, N_max, top_k);
+  REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
+  REQ(((uintptr_t)ws & 255u) == 0, CSA_INVALID_ARG, "ws must be 256-byte aligned");
+  float* scores = reinterpret_cast<float*>(ws);
+  const size_t sbytes = round256((size_t)B * Tq * N_max * 4);
+  csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, scores};
+  hipStream_t st = (hipStream_t)stream;
+  rc = hip_status(csa::run_indexer(a, st), "indexer_score_topk");
+  if (rc) return rc;
+  csa::TopkLaunch t{scores, q_pos, n_comp, B, Tq, N_max, m, top_k, topk_idx, topk_score,
+                    reinterpret_cast<uint8_t*>(ws) + sbytes, ws_bytes - sbytes};
+  return hip_status(csa::run_topk(t, st), "indexer_score_topk");
+}
+
+size_t sparse_mqa_decode_workspace_bytes(int64_t B, int H, int D, int top_k, int W) {
+  if (B < 0 || H <= 0 || D <= 0 || top_k < 0 || W < 0) return 0;
+  return attn_ws(B, H, D, nsplit_for((int64_t)top_k + W, SPARSE_SPLIT_ROWS));
+}
+
+int sparse_mqa_decode(const void* q, const void* kv_comp, const int32_t* topk_idx, const void* kv_win,
+                      const int32_t* win_len, const float* sink, float scale, int64_t B, int H, int D, int64_t N_max,
+                      int top_k, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int rc = check_attn_common(q, out, H, D, kv_dt, out_dt, W, top_k);
+  if (rc) return rc;
+  REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
+  REQ(top_k == 0 || (kv_comp && topk_idx), CSA_INVALID_ARG, "kv_comp and topk_idx must not be NULL");
+  REQ(W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
+  REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
+  const int ns = nsplit_for((int64_t)top_k + W, SPARSE_SPLIT_ROWS);
+  const size_t need = attn_ws(B, H, D, ns);
+  REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
+  REQ(((uintptr_t)ws & 255u) == 0, CSA_INVALID_ARG, "ws must be 256-byte aligned");
+  REQ(B <= 0x7fffffff, CSA_UNSUPPORTED, "B too large");
+  csa::AttnLaunch a{};
+  a.src = 0;
+  a.q = q;
+  a.kv_comp = kv_comp;
+  a.idx = topk_idx;
+  a.kv_win = kv_win;
+  a.win_len = win_len;
+  a.sink = sink;
+  a.scale = scale;
+  a.nq = B;
+  a.N_max = N_max;
+  a.H = H;
+  a.D = D;
+  a.top_k = top_k;
+  a.W = W;
+  a.m_rate = 1;
+  a.kv_dt = kv_dt;
+  a.out_dt = out_dt;
+  a.slots = top_k + W;
+  a.split_rows = ns > 1 ? SPARSE_SPLIT_ROWS : a.slots;
+  a.nsplit = ns;
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + round256((size_t)B * ns * H * D * 4));
+  a.out = out;
+  a.lse = lse;
+  if (W == 0) a.win_len = nullptr;
+  return hip_status(csa::run_attn(a, (hipStream_t)stream), "sparse_mqa_decode");
+}
+
+size_t sparse_mqa_prefill_workspace_bytes(int64_t, int, int, int, int) { return 0; }
+
+int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_idx, const void* kv_tok,
+                       const int32_t* q_pos, const float* sink, float scale, int64_t Tq, int H, int D, int64_t N,
+                       int64_t T_tok, int top_k, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws,
+                       size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_attn_common(q, out, H, D, kv_dt, out_dt, W, top_k);
+  if (rc) return rc;
+  REQ(Tq >= 0 && N >= 0 && T_tok >= 0, CSA_INVALID_ARG, "Tq, N, T_tok must be >= 0");
+  REQ(q_pos, CSA_INVALID_ARG, "q_pos must not be NULL");
+  REQ(top_k == 0 || (kv_comp && topk_idx), CSA_INVALID_ARG, "kv_comp and topk_idx must not be NULL");
+  REQ(W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
+  REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
+  REQ(Tq <= 0x7fffffff, CSA_UNSUPPORTED, "Tq too large");
+  csa::AttnLaunch a{};
+  a.src = 2;
+  a.q = q;
+  a.kv_comp = kv_comp;
+  a.idx = topk_idx;
+  a.kv_win = kv_tok;
+  a.q_pos = q_pos;
+  a.sink = sink;
+  a.scale = scale;
+  a.nq = Tq;
+  a.N_max = N;
+  a.T_tok = T_tok;
+  a.H = H;
+  a.D = D;
+  a.top_k = top_k;
+  a.W = W;
+  a.m_rate = 1;
+  a.kv_dt = kv_dt;
+  a.out_dt = out_dt;
+  a.slots = top_k + W;
+  a.split_rows = a.slots;
+  a.nsplit = 1;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(csa::run_attn(a, (hipStream_t)stream), "sparse_mqa_prefill");
+}
+
+size_t hca_dense_mqa_workspace_bytes(int64_t B, int H, int D, int64_t N_max, int W) {
+  if (B < 0 || H <= 0 || D <= 0 || N_max < 0 || W < 0) return 0;
+  return attn_ws(B, H, D, nsplit_for(N_max + W, HCA_SPLIT_ROWS));
+}
+
+int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, const int32_t* q_pos, int m,
+                  const void* kv_win, const int32_t* win_len, const float* sink, float scale, int64_t B, int H, int D,
+                  int64_t N_max, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int rc = check_attn_common(q, out, H, D, kv_dt, out_dt, W, 0);
+  if (rc) return rc;
+  REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
+  REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");
+  REQ(N_max == 0 || (kv_comp && n_comp && q_pos), CSA_INVALID_ARG, "kv_comp, n_comp, q_pos must not be NULL");
+  REQ(W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
+  REQ(N_max + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
+  const int ns = nsplit_for(N_max + W, HCA_SPLIT_ROWS);
+  const size_t need = attn_ws(B, H, D, ns);
+  REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
+  REQ(((uintptr_t)ws & 255u) == 0, CSA_INVALID_ARG, "ws must be 256-byte aligned");
+  REQ(B <= 0x7fffffff, CSA_UNSUPPORTED, "B too large");
+  csa::AttnLaunch a{};
+  a.src = 1;
+  a.q = q;
+  a.kv_comp = kv_comp;
+  a.kv_win = kv_win;
+  a.win_len = win_len;
+  a.n_comp = n_comp;
+  a.q_pos = q_pos;
+  a.sink = sink;
+  a.scale = scale;
+  a.nq = B;
+  a.N_max = N_max;
+  a.H = H;
+  a.D = D;
+  a.W = W;
+  a.m_rate = m;
+  a.kv_dt = kv_dt;
+  a.out_dt = out_dt;
+  a.slots = (int)(N_max + W);
+  a.split_rows = ns > 1 ? HCA_SPLIT_ROWS : a.slots;
+  a.nsplit = ns;
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + round256((size_t)B * ns * H * D * 4));
+  a.out = out;
+  a.lse = lse;
+  return hip_status(csa::run_attn(a, (hipStream_t)stream), "hca_dense_mqa");
+}
+
+}  // extern "C"

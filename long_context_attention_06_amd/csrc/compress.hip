@@ -1,0 +1,177 @@
+// CSA / HCA KV compression for gfx950.
+//
+// Computes the compression equation of DeepSeek V4 脱离 CUDA 全栈国产化
+// (deepseek.csdn.net, section 二, CSA step 1, the CComp_i equation): entry i
+// of a sequence is, per channel, a softmax-weighted sum of the m candidate
+// values of block i (logits Z_a plus the positional bias B_a) plus, with the
+// overlap branch, a second softmax-weighted sum over block i-1 (Z_b + B_b,
+// C_b). Tokens after the last complete block form no entry (m.lqnn.cn
+// "Deepseek-V4 技术报告里最值得复现的三个改动", section 5).
+//
+// The op is a pure HBM stream: every input element is read once. One thread
+// owns 8 consecutive channels of one entry, so a wave reads whole 1 KiB rows
+// with 16-byte loads. The softmax runs online over the block in groups of
+// four tokens (one rescale per group), in fp32 and the exp2 domain.
+#include "common.h"
+#include "kernels.h"
+
+namespace csa {
+
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float* f) {
+  if constexpr (DT == DT_BF16) {
+    unpack_bf16x8(ld16(reinterpret_cast<const uint16_t*>(base) + off), f);
+  } else {
+    const float* p = reinterpret_cast<const float*>(base) + off;
+    f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+    f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = a[e];
+      f[4 + e] = b[e];
+    }
+  }
+}
+
+struct SoftAcc {
+  float mx[8], sm[8], acc[8];
+  __device__ void init() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mx[e] = -INFINITY;
+      sm[e] = 0.f;
+      acc[e] = 0.f;
+    }
+  }
+  // feed up to 4 tokens at once: z2 in the exp2 domain
+  template <int NTOK>
+  __device__ void feed(const float (*z2)[8], const float (*c)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float gm = z2[0][e];
+#pragma unroll
+      for (int t = 1; t < NTOK; ++t) gm = fmaxf(gm, z2[t][e]);
+      const float nm = fmaxf(mx[e], gm);
+      const float a = exp2f(mx[e] - nm);  // 0 on the first group
+      float s = sm[e] * a, v = acc[e] * a;
+#pragma unroll
+      for (int t = 0; t < NTOK; ++t) {
+        const float p = exp2f(z2[t][e] - nm);
+        s += p;
+        v += p * c[t][e];
+      }
+      mx[e] = nm;
+      sm[e] = s;
+      acc[e] = v;
+    }
+  }
+};
+
+template <int IN_DT>
+__device__ __forceinline__ void feed_block(SoftAcc& S, const void* Cx, const void* Zx, const float* Bx, int64_t row0,
+                                           int d, int m, int c0) {
+  // rows row0 .. row0+m-1 of [*, d] tensors; bias rows 0..m-1
+  int j = 0;
+  for (; j + 4 <= m; j += 4) {
+    float z[4][8], c[4][8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      load8<IN_DT>(Zx, (row0 + j + t) * d + c0, z[t]);
+      load8<IN_DT>(Cx, (row0 + j + t) * d + c0, c[t]);
+      const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(Bx + (int64_t)(j + t) * d + c0);
+      const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(Bx + (int64_t)(j + t) * d + c0 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[t][e] = (z[t][e] + b0[e]) * LOG2E_F;
+        z[t][4 + e] = (z[t][4 + e] + b1[e]) * LOG2E_F;
+      }
+    }
+    S.feed<4>(z, c);
+  }
+  for (; j < m; ++j) {
+    float z[1][8], c[1][8];
+    load8<IN_DT>(Zx, (row0 + j) * d + c0, z[0]);
+    load8<IN_DT>(Cx, (row0 + j) * d + c0, c[0]);
+    const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(Bx + (int64_t)j * d + c0);
+    const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(Bx + (int64_t)j * d + c0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      z[0][e] = (z[0][e] + b0[e]) * LOG2E_F;
+      z[0][4 + e] = (z[0][4 + e] + b1[e]) * LOG2E_F;
+    }
+    S.feed<1>(z, c);
+  }
+}
+
+template <int IN_DT, int OUT_DT>
+__global__ void __launch_bounds__(256)
+compress_kernel(const void* __restrict__ Ca, const void* __restrict__ Cb, const void* __restrict__ Za,
+                const void* __restrict__ Zb, const float* __restrict__ Ba, const float* __restrict__ Bb,
+                void* __restrict__ out, int64_t B, int64_t n_rows, int64_t tok_begin, int64_t blk_begin,
+                int64_t nblk, int64_t out_cap, int d, int m, int overlap, int joint) {
+  const int groups = d / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = B * nblk * groups;
+  if (gid >= total) return;
+  const int cg = (int)(gid % groups);
+  const int64_t t = gid / groups;
+  const int64_t i = blk_begin + t % nblk;
+  const int64_t b = t / nblk;
+  const int c0 = cg * 8;
+
+  SoftAcc A, Bs;
+  A.init();
+  const int64_t rowa = b * n_rows + (m * i - tok_begin);
+  feed_block<IN_DT>(A, Ca, Za, Ba, rowa, d, m, c0);
+  float res[8];
+  const bool has_b = overlap && i >= 1;
+  if (has_b) {
+    const int64_t rowb = b * n_rows + (m * (i - 1) - tok_begin);
+    if (joint) {
+      feed_block<IN_DT>(A, Cb, Zb, Bb, rowb, d, m, c0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) res[e] = A.acc[e] / A.sm[e];
+    } else {
+      Bs.init();
+      feed_block<IN_DT>(Bs, Cb, Zb, Bb, rowb, d, m, c0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) res[e] = A.acc[e] / A.sm[e] + Bs.acc[e] / Bs.sm[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) res[e] = A.acc[e] / A.sm[e];
+  }
+  const int64_t o = (b * out_cap + i) * d + c0;
+  if constexpr (OUT_DT == DT_BF16) {
+    u32x4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(res[2 * e], res[2 * e + 1]);
+    st16(reinterpret_cast<uint16_t*>(out) + o, v);
+  } else {
+    float* p = reinterpret_cast<float*>(out) + o;
+    f32x4_t v0 = {res[0], res[1], res[2], res[3]}, v1 = {res[4], res[5], res[6], res[7]};
+    *reinterpret_cast<f32x4_t*>(p) = v0;
+    *reinterpret_cast<f32x4_t*>(p + 4) = v1;
+  }
+}
+
+template <int IN_DT, int OUT_DT>
+static hipError_t launch(const CompressLaunch& a, hipStream_t st) {
+  const int64_t nblk = a.blk_end - a.blk_begin;
+  const int64_t total = a.B * nblk * (a.d / 8);
+  const int64_t grid = (total + 255) / 256;
+  hipLaunchKernelGGL((compress_kernel<IN_DT, OUT_DT>), dim3((unsigned)grid), dim3(256), 0, st, a.Ca, a.Cb, a.Za,
+                     a.Zb, a.Ba, a.Bb, a.out, a.B, a.n_rows, a.tok_begin, a.blk_begin, nblk, a.out_cap, a.d, a.m,
+                     (int)a.overlap, (int)a.joint);
+  return hipGetLastError();
+}
+
+hipError_t run_compress(const CompressLaunch& a, hipStream_t st) {
+  if (a.B == 0 || a.blk_end <= a.blk_begin) return hipSuccess;
+  if (a.in_dt == DT_BF16 && a.out_dt == DT_BF16) return launch<DT_BF16, DT_BF16>(a, st);
+  if (a.in_dt == DT_BF16 && a.out_dt == DT_F32) return launch<DT_BF16, DT_F32>(a, st);
+  if (a.in_dt == DT_F32 && a.out_dt == DT_BF16) return launch<DT_F32, DT_BF16>(a, st);
+  return launch<DT_F32, DT_F32>(a, st);
+}
+
+}  // namespace csa

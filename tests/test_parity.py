@@ -1,0 +1,334 @@
+"""GPU parity: each C-ABI op against the float64 CPU oracle on seeded inputs, at
+sizes the oracle finishes in seconds that span several tiles and ragged
+tails, plus edge cases (empty sets, V < k, ties, padding, invalid indices)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import gen
+from tests.parity_util import DEV, bf, check_out, check_topk_row, dev, host
+
+pytestmark = pytest.mark.gpu
+
+L = None
+
+
+def setup_module(module):
+    global L
+    import long_context_attention_06_amd as lib
+    L = lib
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _g(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------ compress
+
+def _compress_case(B, n_rows, tok_begin, d, m, blk_begin, blk_end, dt, out_dt, overlap=True, joint=False,
+                   seed=0, out_cap=None):
+    _say("compress", B, n_rows, tok_begin, d, m, blk_begin, blk_end, dt, out_dt, overlap, joint)
+    g = _g(seed)
+    arrs = [g.standard_normal((B, n_rows, d)).astype(np.float32) for _ in range(4)]
+    if dt == "bf16":
+        arrs = [gen.bf16_round(a) for a in arrs]
+    Ba = g.standard_normal((m, d)).astype(np.float32)
+    Bb = g.standard_normal((m, d)).astype(np.float32)
+    up = bf if dt == "bf16" else dev
+    Ca, Cb, Za, Zb = (up(a) for a in arrs)
+    out_cap = out_cap or blk_end
+    tdt = torch.bfloat16 if out_dt == "bf16" else torch.float32
+    out = torch.full((B, out_cap, d), 7.0, dtype=tdt, device=DEV)
+    L.csa_compress(Ca, Cb if overlap else None, Za, Zb if overlap else None, dev(Ba), dev(Bb) if overlap else None,
+                   out, m=m, tok_begin=tok_begin, blk_begin=blk_begin, blk_end=blk_end, overlap=overlap, joint=joint)
+    torch.cuda.synchronize()
+    got = host(out)
+    for b in range(B):
+        # oracle works on absolute token indices: pad the rows before tok_begin
+        pad = np.zeros((tok_begin, d), np.float32)
+        full = [np.concatenate([pad, a[b]]) for a in arrs]
+        ref = oracle.compress(full[0], full[1], full[2], full[3], Ba, Bb, m, overlap=overlap, joint=joint,
+                              blocks=range(blk_begin, blk_end))
+        tight = 1e-5 if out_dt == "f32" else 2.0 ** -8 * max(1.0, np.abs(ref).max())
+        check_out(got[b, blk_begin:blk_end], ref, tight, f"compress b={b}")
+        # rows outside [blk_begin, blk_end) untouched
+        assert np.all(got[b, :blk_begin] == 7.0) and np.all(got[b, blk_end:] == 7.0)
+
+
+def test_compress_tiny_f32():
+    _compress_case(1, 1027, 0, 64, 4, 0, 256, "f32", "f32")  # 3 tail tokens dropped
+
+
+def test_compress_tiny_f32_joint():
+    _compress_case(2, 64, 0, 64, 4, 0, 16, "f32", "f32", joint=True, seed=1)
+
+
+def test_compress_bf16():
+    _compress_case(1, 4099, 0, 512, 4, 0, 1024, "bf16", "bf16", seed=2)
+    _compress_case(2, 257, 0, 512, 4, 0, 64, "bf16", "f32", seed=3)
+
+
+def test_compress_decode_append():
+    # rows hold tokens n-8 .. n-1 of each sequence; the step writes entry N-1
+    n, m = 4096, 4
+    _compress_case(3, 8, n - 8, 512, m, n // m - 1, n // m, "bf16", "bf16", seed=4, out_cap=n // m)
+
+
+def test_compress_hca_single_branch():
+    _compress_case(2, 128 * 5 + 7, 0, 512, 128, 0, 5, "bf16", "f32", overlap=False, seed=5)
+    _compress_case(1, 130, 0, 64, 5, 3, 26, "f32", "f32", seed=6)  # m not a power of two, mid range
+
+
+# ------------------------------------------------------------------ indexer
+
+def _indexer_case(B, Tq, N_max, n_comp, q_pos, m, top_k, kdt, seed=0, H_I=64, D_I=128, wdist="normal"):
+    _say("indexer", B, Tq, N_max, n_comp, m, top_k, kdt)
+    g = _g(seed)
+    qdt = "f32" if kdt == "f32" else "bf16"
+    q_idx = g.standard_normal((B, Tq, H_I, D_I)).astype(np.float32) / math.sqrt(D_I)
+    if qdt == "bf16":
+        q_idx = gen.bf16_round(q_idx)
+    w = (g.standard_normal((B, Tq, H_I)) if wdist == "normal" else g.uniform(0, 1, (B, Tq, H_I))).astype(np.float32)
+    k = g.standard_normal((B, N_max, D_I)).astype(np.float32)
+    scale = None
+    if kdt == "fp8":
+        codes, scale = gen.e4m3_quantize_rows(k)
+        kval = oracle.e4m3_decode(codes)
+        k_t = dev(codes)
+        sc_t = dev(scale)
+    elif kdt == "bf16":
+        k = gen.bf16_round(k)
+        kval = k
+        k_t, sc_t = bf(k), None
+    else:
+        kval = k
+        k_t, sc_t = dev(k), None
+    q_t = bf(q_idx) if qdt == "bf16" else dev(q_idx)
+    qp = dev(np.asarray(q_pos, np.int32).reshape(B, Tq))
+    nc = dev(np.asarray(n_comp, np.int32))
+    scores = torch.full((B, Tq, N_max), float("nan"), device=DEV)
+    L.indexer_score(q_t, dev(w), k_t, sc_t, qp, nc, scores, m=m)
+    idx = torch.empty((B, Tq, top_k), dtype=torch.int32, device=DEV)
+    idx2 = torch.empty_like(idx)
+    tsc = torch.empty((B, Tq, top_k), device=DEV)
+    L.indexer_topk(scores, qp, nc, idx, tsc, m=m)
+    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx2, m=m)
+    torch.cuda.synchronize()
+    S, I, I2, TS = host(scores), host(idx), host(idx2), host(tsc)
+    assert np.array_equal(I, I2), "indexer_score_topk != indexer_score + indexer_topk"
+    qpos = np.asarray(q_pos).reshape(B, Tq)
+    for b in range(B):
+        for t in range(Tq):
+            V = oracle.visible(qpos[b, t], n_comp[b], m)
+            V = min(V, N_max)
+            ref = oracle.indexer_scores(q_idx[b, t], w[b, t], kval[b], V, None if scale is None else scale[b])
+            got = S[b, t, :V]
+            err = np.abs(got - ref).max() if V else 0.0
+            # fp32 accumulation of bf16 products over 128 dims, 64 heads
+            amax = np.abs(ref).max(initial=0.0)
+            bound = 1e-5 * (1 + amax) if kdt == "f32" else 2e-5 * (1 + amax) * 8
+            assert err <= bound, f"scores b={b} t={t}: {err:.2e} > {bound:.2e}"
+            oidx = oracle.topk_select(ref, top_k)
+            check_topk_row(I[b, t], oidx, ref, top_k, f"topk b={b} t={t}")
+            K = min(top_k, V)
+            # returned scores are the GPU scores of the returned indices
+            assert np.array_equal(TS[b, t, :K], S[b, t, I[b, t, :K]])
+            assert np.all(np.isneginf(TS[b, t, K:]))
+
+
+def test_indexer_bf16_decode():
+    _indexer_case(3, 1, 1000, [1000, 777, 3], [3999, 3999, 3999], 4, 64, "bf16", seed=10)
+
+
+def test_indexer_fp8_decode():
+    _indexer_case(2, 1, 2100, [2100, 2100], [8399, 5000], 4, 256, "fp8", seed=11)
+
+
+def test_indexer_bf16_prefill_rows():
+    # 40 queries of one sequence at scattered positions: V from 0 to 600
+    pos = np.sort(_g(12).integers(0, 2400, 40))
+    pos[:3] = [0, 2, 3]  # V = 0, 0, 1
+    _indexer_case(1, 40, 600, [600], pos, 4, 32, "bf16", seed=12)
+
+
+def test_indexer_tiny_f32_c1():
+    pos = np.arange(960, 1024)
+    _indexer_case(1, 64, 256, [256], pos, 4, 16, "f32", seed=13, H_I=4, D_I=32, wdist="uniform")
+
+
+# ------------------------------------------------------------------ top-k alone
+
+def _topk_case(rows, N_max, Vs, k, dist, seed=0):
+    _say("topk", rows, N_max, k, dist)
+    g = _g(seed)
+    if dist == "ties":
+        s = g.integers(-3, 4, (rows, N_max)).astype(np.float32)
+    elif dist == "zeros":
+        s = np.zeros((rows, N_max), np.float32)
+        s[:, ::7] = -0.0
+    else:
+        s = g.standard_normal((rows, N_max)).astype(np.float32) * 5
+    m = 1
+    qp = np.asarray(Vs, np.int32) - 1  # V = min(n_comp, q_pos + 1)
+    nc = np.full((1,), N_max, np.int32)
+    idx = torch.empty((1, rows, k), dtype=torch.int32, device=DEV)
+    L.indexer_topk(dev(s.reshape(1, rows, N_max)), dev(qp.reshape(1, rows)), dev(nc), idx, m=m)
+    torch.cuda.synchronize()
+    I = host(idx)[0]
+    for r in range(rows):
+        V = max(0, min(Vs[r], N_max))
+        ref = oracle.topk_select(s[r, :V].astype(np.float64), k)
+        assert np.array_equal(I[r], ref), f"row {r}: exact selection differs"
+
+
+def test_topk_exact_normal():
+    _topk_case(6, 5000, [5000, 4999, 1, 0, 100, 3000], 300, "normal", seed=20)
+
+
+def test_topk_ties_lower_index_wins():
+    _topk_case(4, 3000, [3000, 2000, 50, 7], 100, "ties", seed=21)
+    _topk_case(2, 500, [500, 500], 17, "zeros", seed=22)
+
+
+def test_topk_global_mode_large_row():
+    _topk_case(2, 40000, [40000, 33000], 1024, "normal", seed=23)  # beyond the LDS key cache
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_tight(ref, kv_dt="bf16"):
+    """P is rounded to bf16 for the PV product and bf16 outputs are rounded
+    once more: a relative error of about 2^-8 of the output scale."""
+    return (2.0 ** -7 if kv_dt == "bf16" else 1e-5) * max(1.0, float(np.abs(ref).max(initial=0.0)))
+
+
+def test_sparse_decode_edge_rows():
+    _say("sparse_decode", "edge")
+    g = _g(30)
+    B, H, D, N_max, k, W = 4, 64, 512, 700, 300, 128
+    q = gen.bf16_round(g.standard_normal((B, H, D)).astype(np.float32) / math.sqrt(D))
+    kv = gen.bf16_round(g.standard_normal((B, N_max, D)).astype(np.float32))
+    win = gen.bf16_round(g.standard_normal((B, W, D)).astype(np.float32))
+    idx = np.sort(g.choice(N_max, size=(B, k)), axis=1).astype(np.int32)
+    idx[0, 250:] = -1          # short selection
+    idx[1, :] = -1             # nothing selected: window + sink only
+    idx[2, 10] = idx[2, 11]    # a duplicate row counts twice
+    idx[3, 5] = N_max + 3      # out of range: skipped
+    win_len = np.array([128, 5, 0, 77], np.int32)
+    sink = g.standard_normal(H).astype(np.float32)
+    for out_dt in ("bf16", "f32"):
+        out = torch.empty((B, H, D), dtype=torch.bfloat16 if out_dt == "bf16" else torch.float32, device=DEV)
+        lse = torch.empty((B, H), device=DEV)
+        L.sparse_mqa_decode(bf(q), bf(kv), dev(idx), bf(win), dev(win_len), dev(sink), out, lse, scale=1.0)
+        torch.cuda.synchronize()
+        O, LS = host(out), host(lse)
+        for b in range(B):
+            ids = idx[b][(idx[b] >= 0) & (idx[b] < N_max)]
+            rows = np.concatenate([kv[b][ids], win[b][:win_len[b]]])
+            ref, rlse = oracle.attend(q[b], rows, sink)
+            check_out(O[b], ref, _attn_tight(ref), f"sparse_decode b={b} {out_dt}")
+            assert np.abs(LS[b] - rlse).max() < 1e-3
+
+
+def test_sparse_decode_no_sink_empty():
+    _say("sparse_decode", "empty")
+    B, H, D = 1, 64, 512
+    q = torch.zeros((B, H, D), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((B, 8, D), dtype=torch.bfloat16, device=DEV)
+    idx = torch.full((B, 16), -1, dtype=torch.int32, device=DEV)
+    out = torch.full((B, H, D), 3.0, device=DEV)
+    lse = torch.zeros((B, H), device=DEV)
+    L.sparse_mqa_decode(q, kv, idx, None, None, None, out, lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_hca_decode():
+    _say("hca_decode")
+    g = _g(31)
+    B, H, D, N_max, W, m = 3, 64, 512, 1500, 128, 128
+    q = gen.bf16_round(g.standard_normal((B, H, D)).astype(np.float32) / math.sqrt(D))
+    kv = gen.bf16_round(g.standard_normal((B, N_max, D)).astype(np.float32))
+    win = gen.bf16_round(g.standard_normal((B, W, D)).astype(np.float32))
+    n_comp = np.array([1500, 1500, 40], np.int32)
+    q_pos = np.array([1500 * 128 + 5, 1000 * 128 - 1, 10 ** 6], np.int32)  # V = 1500, 1000, 40
+    win_len = np.array([128, 128, 3], np.int32)
+    sink = g.standard_normal(H).astype(np.float32)
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H), device=DEV)
+    L.hca_dense_mqa(bf(q), bf(kv), dev(n_comp), dev(q_pos), bf(win), dev(win_len), dev(sink), out, lse, m=m)
+    torch.cuda.synchronize()
+    O, LS = host(out), host(lse)
+    for b in range(B):
+        ref, rlse = oracle.hca_query(q[b], kv[b], int(q_pos[b]), int(n_comp[b]), m, win[b][:win_len[b]], sink)
+        check_out(O[b], ref, _attn_tight(ref), f"hca b={b}")
+        assert np.abs(LS[b] - rlse).max() < 1e-3
+
+
+def test_sparse_prefill():
+    _say("sparse_prefill")
+    g = _g(32)
+    Tq, H, D, N, T_tok, k, W = 50, 64, 512, 300, 1200, 64, 128
+    q = gen.bf16_round(g.standard_normal((Tq, H, D)).astype(np.float32) / math.sqrt(D))
+    kv = gen.bf16_round(g.standard_normal((N, D)).astype(np.float32))
+    tok = gen.bf16_round(g.standard_normal((T_tok, D)).astype(np.float32))
+    pos = np.sort(g.integers(0, T_tok, Tq)).astype(np.int32)
+    pos[0] = 0
+    idx = np.sort(g.choice(N, size=(Tq, k)), axis=1).astype(np.int32)
+    idx[3, 20:] = -1
+    sink = g.standard_normal(H).astype(np.float32)
+    out = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((Tq, H), device=DEV)
+    L.sparse_mqa_prefill(bf(q), bf(kv), dev(idx), bf(tok), dev(pos), dev(sink), out, lse, W=W)
+    torch.cuda.synchronize()
+    O, LS = host(out), host(lse)
+    for t in range(Tq):
+        ids = idx[t][idx[t] >= 0]
+        rows = np.concatenate([kv[ids], oracle.window_rows(tok, int(pos[t]), W)])
+        ref, rlse = oracle.attend(q[t], rows, sink)
+        check_out(O[t], ref, _attn_tight(ref), f"prefill t={t}")
+        assert np.abs(LS[t] - rlse).max() < 1e-3
+
+
+# ------------------------------------------------------------------ whole paths
+
+def test_tiny_csa_pipeline_c1():
+    """Tiny fp32 CSA end to end: compress -> score/top-k -> sparse MQA with
+    window and sink, the 64 last positions of a 1024-token sequence."""
+    cfg = gen.C1
+    _say("c1 pipeline")
+    tok = gen.gen_prefill_tokens(cfg)
+    qs = gen.gen_prefill_queries(cfg, 0)
+    N, d, m = cfg.N, cfg.D, cfg.m
+    comp = torch.empty((1, N, d), device=DEV)
+    L.csa_compress(*(dev(tok[k][None]) for k in ("Ca", "Cb", "Za", "Zb")), dev(tok["Ba"]), dev(tok["Bb"]), comp, m=m)
+    Tq = cfg.Tq
+    qp = dev(qs["q_pos"][None])
+    nc = dev(np.array([N], np.int32))
+    idx = torch.empty((1, Tq, cfg.top_k), dtype=torch.int32, device=DEV)
+    L.indexer_score_topk(dev(qs["q_idx"][None]), dev(qs["w"][None]), dev(tok["k_idx"][None]), None, qp, nc, idx, m=m)
+    out = torch.empty((Tq, cfg.H, d), device=DEV)
+    lse = torch.empty((Tq, cfg.H), device=DEV)
+    L.sparse_mqa_prefill(dev(qs["q"]), comp[0], idx[0], dev(tok["kv_tok"]), qp[0], dev(tok["sink"]), out, lse, W=cfg.W)
+    torch.cuda.synchronize()
+    ref_comp = oracle.compress(tok["Ca"], tok["Cb"], tok["Za"], tok["Zb"], tok["Ba"], tok["Bb"], m)
+    check_out(host(comp)[0], ref_comp, 1e-5, "c1 compress")
+    I, O = host(idx)[0], host(out)
+    for t in range(Tq):
+        p = int(qs["q_pos"][t])
+        oidx, o_ref, lse_ref, s = oracle.csa_query(qs["q"][t], qs["q_idx"][t], qs["w"][t], ref_comp, tok["k_idx"], p,
+                                                   N, m, cfg.top_k, oracle.window_rows(tok["kv_tok"], p, cfg.W),
+                                                   tok["sink"])
+        check_topk_row(I[t], oidx, s, cfg.top_k, f"c1 t={t}")
+        if np.array_equal(I[t], oidx):
+            check_out(O[t], o_ref, _attn_tight(o_ref, "f32"), f"c1 out t={t}")
+        rows = np.concatenate([ref_comp[I[t][I[t] >= 0]], oracle.window_rows(tok["kv_tok"], p, cfg.W)])
+        o_own, _ = oracle.attend(qs["q"][t], rows, tok["sink"])
+        check_out(O[t], o_own, _attn_tight(o_own, "f32"), f"c1 out on gpu idx t={t}")

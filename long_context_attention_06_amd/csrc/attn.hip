@@ -95,12 +95,21 @@ struct RowSrc {
   int W;
 };
 
+// The memory-resident part of a slot (its top-k index); loaded one tile ahead
+// of the row itself so the index -> row dependency never stalls a tile.
+template <int SRC>
+__device__ __forceinline__ int slot_code(const RowSrc& s, int64_t qi, int j) {
+  if ((SRC == SRC_SPARSE_DEC || SRC == SRC_SPARSE_PRE) && j < s.top_k) return s.idx[qi * s.top_k + j];
+  return 0;
+}
+
 template <int SRC, int ROWB>
-__device__ __forceinline__ const uint8_t* slot_row(const RowSrc& s, int64_t qi, int j, int lim0, int lim1) {
+__device__ __forceinline__ const uint8_t* slot_row(const RowSrc& s, int64_t qi, int j, int code, int lim0,
+                                                   int lim1) {
   // lim0: SPARSE: window length; HCA: visible entries V.  lim1: PRE: position p
   if (SRC == SRC_SPARSE_DEC || SRC == SRC_SPARSE_PRE) {
     if (j < s.top_k) {
-      int id = s.idx[qi * s.top_k + j];
+      const int id = code;
       if (id < 0 || id >= s.N_max) return nullptr;
       int64_t row = (SRC == SRC_SPARSE_DEC) ? qi * s.N_max + id : (int64_t)id;
       return s.kv_comp + row * ROWB;
@@ -197,13 +206,22 @@ attn_kernel(const T* __restrict__ q, RowSrc src, const int32_t* __restrict__ win
   const int lrs = tid / C::CPR;
   u32x4_t pre[C::PASSES];
   int prev[C::PASSES];
+  int pcode[C::PASSES];
+  auto fetch_code = [&](int tile) {
+    const int base = s_begin + tile * C::TR;
+#pragma unroll
+    for (int ps = 0; ps < C::PASSES; ++ps) {
+      const int j = base + lrs + ps * C::RPP;
+      pcode[ps] = (j < s_end) ? slot_code<SRC>(src, qi, j) : -1;
+    }
+  };
   auto fetch = [&](int tile) {
     const int base = s_begin + tile * C::TR;
 #pragma unroll
     for (int ps = 0; ps < C::PASSES; ++ps) {
       const int r = lrs + ps * C::RPP;
       const int j = base + r;
-      const uint8_t* rp = (j < s_end) ? slot_row<SRC, ROWB>(src, qi, j, lim0, lim1) : nullptr;
+      const uint8_t* rp = (j < s_end) ? slot_row<SRC, ROWB>(src, qi, j, pcode[ps], lim0, lim1) : nullptr;
       prev[ps] = rp != nullptr;
       u32x4_t v = {0, 0, 0, 0};
       if (rp) v = ld16(rp + lc * 16);
@@ -240,10 +258,17 @@ attn_kernel(const T* __restrict__ q, RowSrc src, const int32_t* __restrict__ win
   const int sm_rg = l / C::HS;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  if (ntiles > 0) fetch(0);
+  if (ntiles > 0) {
+    fetch_code(0);
+    fetch(0);
+    if (ntiles > 1) fetch_code(1);
+  }
   for (int tile = 0; tile < ntiles; ++tile) {
     const int any = __syncthreads_or(stash());
-    if (tile + 1 < ntiles) fetch(tile + 1);
+    if (tile + 1 < ntiles) {
+      fetch(tile + 1);  // uses the codes loaded one iteration ago
+      if (tile + 2 < ntiles) fetch_code(tile + 2);
+    }
     if (!any) continue;
 
     // ---- S^T partial = R(rows x DW) * Q^T(DW x 32 heads)
@@ -444,43 +469,67 @@ attn_kernel(const T* __restrict__ q, RowSrc src, const int32_t* __restrict__ win
 }
 
 // Merge split partials in fixed order s = 0..nsplit-1 and add the sink.
+// One wave per (query, head); lanes cover the head's dims in float4 chunks.
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                     const float* __restrict__ sink, int H, int D, int nsplit,
                     void* __restrict__ out, float* __restrict__ lse, int out_dt) {
   const int64_t qi = blockIdx.x;
-  const int D4 = D / 4;
-  const int items = H * D4;
-  for (int it = threadIdx.x; it < items; it += blockDim.x) {
-    const int h = it / D4, d4 = it % D4;
-    const float s2 = sink ? sink[h] * LOG2E_F : -INFINITY;
-    float M = s2;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((qi * nsplit + s) * H + h) * 2]);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float Z = 0.0f;
-    if (M != -INFINITY) {
-      Z = exp2f(s2 - M);
-      for (int s = 0; s < nsplit; ++s) {
-        const int64_t pb = (qi * nsplit + s) * H + h;
-        const float ms = part_ml[pb * 2], ls = part_ml[pb * 2 + 1];
-        const float a = exp2f(ms - M);  // 0 for an empty split (ms = -inf)
-        Z += ls * a;
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part_o + pb * D + d4 * 4);
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (h >= H) return;
+  const float s2 = sink ? sink[h] * LOG2E_F : -INFINITY;
+  const int64_t row0 = qi * nsplit * (int64_t)H + h;  // partial (qi, s, h) at row0 + s*H
+  float M = s2;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(row0 + (int64_t)s * H) * 2]);
+  constexpr int MAXC = 2;  // float4 chunks per lane (D <= 512)
+  f32x4_t acc[MAXC];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += v[e] * a;
+  for (int c = 0; c < MAXC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float Z = 0.0f;
+  if (M != -INFINITY) {
+    Z = exp2f(s2 - M);
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+      f32x4_t v[4][MAXC];
+      float a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = s0 + u;
+        a[u] = 0.0f;
+        if (s < nsplit) {
+          const int64_t pb = row0 + (int64_t)s * H;
+          a[u] = exp2f(part_ml[pb * 2] - M);  // 0 for an empty split (m = -inf)
+          Z += part_ml[pb * 2 + 1] * a[u];
+#pragma unroll
+          for (int c = 0; c < MAXC; ++c) {
+            const int d = (c * 64 + l) * 4;
+            v[u][c] = d < D ? *reinterpret_cast<const f32x4_t*>(part_o + pb * D + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        }
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[c][e] += v[u][c][e] * a[u];
     }
-    const float inv = (M != -INFINITY) ? 1.0f / Z : 0.0f;
-    const int64_t o = (qi * H + h) * (int64_t)D + d4 * 4;
+  }
+  const float inv = (M != -INFINITY) ? 1.0f / Z : 0.0f;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int d = (c * 64 + l) * 4;
+    if (d >= D) continue;
+    const int64_t o = (qi * H + h) * (int64_t)D + d;
     if (out_dt == DT_BF16) {
-      u32x2_t w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+      u32x2_t w = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv), pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
       *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(out) + o) = w;
     } else {
-      f32x4_t w = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+      f32x4_t w = {acc[c][0] * inv, acc[c][1] * inv, acc[c][2] * inv, acc[c][3] * inv};
       *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + o) = w;
     }
-    if (lse && d4 == 0) lse[qi * H + h] = (M != -INFINITY) ? (M + log2f(Z)) * LN2_F : -INFINITY;
   }
+  if (lse && l == 0) lse[qi * H + h] = (M != -INFINITY) ? (M + log2f(Z)) * LN2_F : -INFINITY;
 }
 
 // ----------------------------------------------------------------------------
@@ -504,8 +553,8 @@ static hipError_t launch_attn(const AttnLaunch& a, hipStream_t st) {
                      a.part_ml, a.out, a.lse, a.out_dt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)a.nq), dim3(256), 0, st, a.part_o, a.part_ml, a.sink,
-                     a.H, D, a.nsplit, a.out, a.lse, a.out_dt);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)a.nq, (unsigned)((a.H + 3) / 4)), dim3(256), 0, st,
+                     a.part_o, a.part_ml, a.sink, a.H, D, a.nsplit, a.out, a.lse, a.out_dt);
   return hipGetLastError();
 }
 

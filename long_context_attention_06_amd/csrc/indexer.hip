@@ -9,91 +9,145 @@
 //
 // Design: the scan over keys is the dominant HBM stream of CSA decode. It is
 // a [64 heads x 128] x [128 x entries] contraction, run on
-// v_mfma_f32_32x32x16_bf16 with heads as M (two 32-row tiles) and entries as
-// N (32 per column block). The query operand stays in registers for the whole
-// workgroup. Each lane reads 128 contiguous bytes of one key row (bf16) or 64
-// (FP8, decoded exactly to bf16 in registers; the scale is applied after the
-// head sum since it is positive). The epilogue never leaves registers: a lane
-// holds 16 heads of one entry per tile, applies ReLU and w, sums, and one
-// cross-half shuffle completes the 64-head sum. K dims are visited in a
-// permuted order (lane half g covers dims g*64..g*64+63), identical for q and
+// v_mfma_f32_16x16x32_bf16 with heads as M (four 16-row tiles) and entries as
+// N (16 per wave). The query operand stays in registers for the whole
+// workgroup. Keys go HBM -> registers (coalesced) -> LDS (swizzled) -> MFMA
+// operands; FP8 keys are decoded exactly to bf16 after the LDS read and their
+// scale is applied after the head sum (it is positive). The epilogue never leaves registers: a lane
+// holds 16 heads of one entry per tile, applies ReLU and w, sums, and two
+// cross-lane shuffles complete the 64-head sum. K dims are visited in a
+// permuted order (lane group G covers dims G*32..G*32+31), identical for q and
 // k, which leaves the dot products unchanged.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace csa {
 
-// bf16 / fp8 keys, 64 heads x 128 dims.  Grid: (tile groups, rows).
-// A workgroup (4 waves) walks entry tiles of 256 (64 per wave) of one query row.
+// bf16 / fp8 keys, 64 heads x 128 dims.  Grid: (workgroups per row, rows).
+// A workgroup (4 waves) walks tiles of 64 entries of one query row with a
+// stride of gridDim.x tiles. Each tile is read with fully coalesced 16-byte
+// loads (the workgroup covers contiguous 4 KiB per instruction), staged in a
+// double-buffered LDS tile with an XOR swizzle of the 16-byte chunk index
+// (chunk ^ (row & 7)), and read back in the operand layout of
+// v_mfma_f32_16x16x32_bf16 with conflict-free ds_read_b128: wave w owns
+// entries 16w..16w+15 of the tile (N = 16), heads are four 16-row M tiles.
+// Two tiles per workgroup are in flight while one is computed.
 template <int KDT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                      const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
                      const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
                      int64_t N_max, int m, float* __restrict__ scores) {
-  constexpr int H = 64, DI = 128, KS = 8;  // k-steps of 16
-  constexpr int KROW = (KDT == DT_FP8) ? DI : DI * 2;  // bytes per key row
-  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int g = l >> 5, l32 = l & 31;
+  constexpr int H = 64, DI = 128, KS = 4;               // k-steps of 32
+  constexpr int KROW = (KDT == DT_FP8) ? DI : DI * 2;   // bytes per key row
+  constexpr int TE = 64;                                // entries per tile
+  constexpr int TB = TE * KROW;                         // tile bytes
+  constexpr int LPT = TB / (256 * 16);                  // 16-byte loads per thread per tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][TB];
+  __shared__ __attribute__((aligned(16))) float lds_w[H];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63, wv = tid >> 6;
+  const int G = l >> 4, l16 = l & 15;  // k-group (4 x 8 dims) and column of the MFMA operands
   const int64_t row = blockIdx.y;
   const int64_t b = row / Tq;
   int64_t V = min((int64_t)n_comp[b], ((int64_t)q_pos[row] + 1) / m);
   V = max((int64_t)0, min(V, N_max));
-  const int64_t ntiles = (V + 255) / 256;
+  const int64_t ntiles = (V + TE - 1) / TE;
   if ((int64_t)blockIdx.x >= ntiles) return;
+  const int64_t nmine = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // tiles of this workgroup
 
-  // query operand: A[m = head][k], lane (head mt*32+l32, half g) holds dims g*64 + s*8 + 0..7
-  bf16x8_t qa[2][KS];
-  float wr[2][16];
+  // query operand A[m = head][k]: lane (head mt*16 + l16, group G) holds dims
+  // G*32 + s*8 + 0..7 for k-step s (a fixed permutation of the 128 dims,
+  // applied identically to the keys)
+  bf16x8_t qa[4][KS];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const uint16_t* qp = q_idx + (row * H + mt * 32 + l32) * DI + g * 64;
+  for (int mt = 0; mt < 4; ++mt) {
+    const uint16_t* qp = q_idx + (row * H + mt * 16 + l16) * DI + G * 32;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qa[mt][s] = as_bf16x8(ld16(qp + s * 8));
-#pragma unroll
-    for (int r = 0; r < 16; ++r) wr[mt][r] = w[row * H + mt * 32 + (r >> 2) * 8 + g * 4 + (r & 3)];
   }
+  if (tid < H) lds_w[tid] = w[row * H + tid];  // visible after the first barrier
   const uint8_t* kb = k_idx + b * N_max * KROW;
   float* srow = scores + row * N_max;
 
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  u32x4_t rg[2][LPT];
+  // register ring slots and LDS buffers are compile-time indices (a runtime
+  // index would move the ring to scratch memory)
+  auto load = [&](auto SLOT, int64_t tile) {
+    constexpr int slot = decltype(SLOT)::value;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int64_t e = tile * 256 + wv * 64 + cb * 32 + l32;
-      const bool ok = e < V;
-      bf16x8_t kbv[KS];
-      if constexpr (KDT == DT_FP8) {
-        const uint8_t* kp = kb + (ok ? e : 0) * KROW + g * 64;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          u32x4_t v = ok ? ld16(kp + c * 16) : u32x4_t{0, 0, 0, 0};
-          u32x2_t a0 = fp8x4_to_bf16x4(v[0]), a1 = fp8x4_to_bf16x4(v[1]);
-          u32x2_t a2 = fp8x4_to_bf16x4(v[2]), a3 = fp8x4_to_bf16x4(v[3]);
-          kbv[2 * c] = as_bf16x8(u32x4_t{a0[0], a0[1], a1[0], a1[1]});
-          kbv[2 * c + 1] = as_bf16x8(u32x4_t{a2[0], a2[1], a3[0], a3[1]});
-        }
-      } else {
-        const uint8_t* kp = kb + (ok ? e : 0) * KROW + g * 128;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kbv[s] = as_bf16x8(ok ? ld16(kp + s * 16) : u32x4_t{0, 0, 0, 0});
-      }
-      float part = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x16_t acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mfma32(qa[mt][s], kbv[s], acc);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) part += wr[mt][r] * fmaxf(acc[r], 0.0f);
-      }
-      part += shfl_xor(part, 32);
-      if (g == 0 && ok) {
-        if constexpr (KDT == DT_FP8) part *= k_scale[b * N_max + e];
-        srow[e] = part;
-      }
+    for (int j = 0; j < LPT; ++j) {
+      const int o = (j * 256 + tid) * 16;  // byte offset inside the tile
+      const int64_t e = tile * TE + o / KROW;
+      rg[slot][j] = (e < V) ? ld16(kb + e * KROW + (o % KROW)) : u32x4_t{0, 0, 0, 0};
     }
+  };
+  auto stash = [&](auto SLOT) {
+    constexpr int slot = decltype(SLOT)::value;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int o = (j * 256 + tid) * 16;
+      const int r = o / KROW, c = (o % KROW) / 16;
+      *reinterpret_cast<u32x4_t*>(&lds_k[slot][r * KROW + ((c ^ (r & 7)) * 16)]) = rg[slot][j];
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto body = [&](int64_t it, auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
+    const int64_t tile = blockIdx.x + it * gridDim.x;
+    stash(BUF);
+    if (it + 2 < nmine) load(BUF, blockIdx.x + (it + 2) * gridDim.x);
+    __syncthreads();
+
+    const int el = wv * 16 + l16;  // entry inside the tile
+    const int64_t e = tile * TE + el;
+    const uint8_t* kr = &lds_k[buf][el * KROW];
+    const int sw = el & 7;
+    bf16x8_t kbv[KS];
+    if constexpr (KDT == DT_FP8) {
+      // dims G*32 + s*8 .. : bytes G*32 + s*8, i.e. chunk G*2 + s/2, half s%2
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + (((G * 2 + c) ^ sw) * 16));
+        const u32x2_t a0 = fp8x4_to_bf16x4(v[0]), a1 = fp8x4_to_bf16x4(v[1]);
+        const u32x2_t a2 = fp8x4_to_bf16x4(v[2]), a3 = fp8x4_to_bf16x4(v[3]);
+        kbv[2 * c] = as_bf16x8(u32x4_t{a0[0], a0[1], a1[0], a1[1]});
+        kbv[2 * c + 1] = as_bf16x8(u32x4_t{a2[0], a2[1], a3[0], a3[1]});
+      }
+    } else {
+      // dims G*32 + s*8 .. : chunk G*4 + s
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        kbv[s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + (((G * 4 + s) ^ sw) * 16)));
+    }
+    float part = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], kbv[s], acc);
+      // accumulator row r of this lane is head mt*16 + G*4 + r
+      const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[mt * 16 + G * 4]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part += wv4[r] * fmaxf(acc[r], 0.0f);
+    }
+    part += shfl_xor(part, 16);
+    part += shfl_xor(part, 32);
+    if (G == 0 && e < V) {
+      if constexpr (KDT == DT_FP8) part *= k_scale[b * N_max + e];
+      srow[e] = part;
+    }
+  };
+  load(I0{}, blockIdx.x);
+  if (nmine > 1) load(I1{}, blockIdx.x + gridDim.x);
+  for (int64_t it = 0; it < nmine; it += 2) {
+    body(it, I0{});
+    if (it + 1 < nmine) body(it + 1, I1{});
   }
 }
 
@@ -145,9 +199,10 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
   const int64_t rows = a.B * a.Tq;
   if (rows == 0 || a.N_max == 0) return hipSuccess;
   if (a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16) {
-    const int64_t ntiles = (a.N_max + 255) / 256;
-    // enough workgroups per row to fill the chip, each walking a few tiles
-    int64_t per_row = (2048 + rows - 1) / rows;
+    const int64_t ntiles = (a.N_max + 63) / 64;
+    // a few workgroups per CU in total, each walking a strided run of tiles
+    // of its row
+    int64_t per_row = (512 + rows - 1) / rows;
     per_row = max((int64_t)1, min(ntiles, per_row));
     dim3 grid((unsigned)per_row, (unsigned)rows);
     if (a.k_dt == DT_FP8)

@@ -80,7 +80,7 @@ topk_row_kernel(const float* __restrict__ scores, const int32_t* __restrict__ q_
   uint32_t* hist = smem;                                  // TK_BINS
   int* red = reinterpret_cast<int*>(smem + TK_BINS);      // 32 ints
   int* res = red + 32;                                    // 32 ints
-  uint32_t* kc = smem + TK_BINS + 64;                     // key cache
+  uint32_t* kc = smem + TK_BINS + 64;                     // key cache (16-byte aligned)
 
   const int t = threadIdx.x, l = t & 63, wv = t >> 6;
   const int64_t row = blockIdx.x;
@@ -101,7 +101,30 @@ topk_row_kernel(const float* __restrict__ scores, const int32_t* __restrict__ q_
   }
   const bool cached = V <= cache_cap;
   if (cached) {
-    for (int i = t; i < V; i += TK_NT) kc[i] = f32_key(srow[i]);
+    // 16-byte loads, 8 in flight per thread, when the row is 16-byte aligned
+    if ((reinterpret_cast<uintptr_t>(srow) & 15) == 0) {
+      const int V4 = V >> 2;
+      const f32x4_t* s4 = reinterpret_cast<const f32x4_t*>(srow);
+      for (int i0 = t; i0 < V4; i0 += TK_NT * 8) {
+        f32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * TK_NT;
+          if (i < V4) v[u] = s4[i];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * TK_NT;
+          if (i < V4) {
+            u32x4_t k4 = {f32_key(v[u][0]), f32_key(v[u][1]), f32_key(v[u][2]), f32_key(v[u][3])};
+            *reinterpret_cast<u32x4_t*>(kc + 4 * i) = k4;
+          }
+        }
+      }
+      for (int i = 4 * V4 + t; i < V; i += TK_NT) kc[i] = f32_key(srow[i]);
+    } else {
+      for (int i = t; i < V; i += TK_NT) kc[i] = f32_key(srow[i]);
+    }
   }
   // (the first histogram clear below is followed by a barrier)
 

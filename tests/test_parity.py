@@ -197,8 +197,15 @@ def test_topk_ties_lower_index_wins():
     _topk_case(2, 500, [500, 500], 17, "zeros", seed=22)
 
 
-def test_topk_global_mode_large_row():
-    _topk_case(2, 40000, [40000, 33000], 1024, "normal", seed=23)  # beyond the LDS key cache
+def test_topk_two_level_rows():
+    # rows longer than one 32768-key chunk go through chunk winners + a second selection;
+    # rows of one launch may end in either chunk
+    _topk_case(3, 40000, [40000, 33000, 20000], 1024, "normal", seed=23)
+
+
+def test_topk_multilevel_ties():
+    # 600000 keys, top 4096: four levels; integer scores make ties cross chunks
+    _topk_case(2, 600000, [600000, 431111], 4096, "ties", seed=24)
 
 
 # ------------------------------------------------------------------ attention

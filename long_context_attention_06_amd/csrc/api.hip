@@ -1,6 +1,7 @@
 // C ABI of the CSA/HCA attention library: argument validation (host only,
 // before any HIP call), workspace sizing, split planning and kernel dispatch.
 // The operations and their sources are documented in include/csa_hca.h.
+#include <algorithm>
 #include <string>
 
 #include "../../include/csa_hca.h"
@@ -32,9 +33,14 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 // Rows per split of the decode attention. Depends only on per-query shape
 // arguments, so a sequence's result never depends on the batch.
 constexpr int SPARSE_SPLIT_ROWS = 128;
-constexpr int HCA_SPLIT_ROWS = 512;
+constexpr int HCA_MAX_SPLITS = 16;  // dense rows are long: at most 16 splits of whole 32-row tiles
 
 int nsplit_for(int64_t slots, int rows) { return slots <= rows ? 1 : (int)((slots + rows - 1) / rows); }
+
+int hca_split_rows(int64_t slots) {
+  const int64_t per = (slots + HCA_MAX_SPLITS - 1) / HCA_MAX_SPLITS;
+  return (int)std::max<int64_t>(32, (per + 31) / 32 * 32);
+}
 
 size_t attn_ws(int64_t nq, int H, int D, int nsplit) {
   if (nsplit <= 1) return 0;
@@ -42,7 +48,7 @@ size_t attn_ws(int64_t nq, int H, int D, int nsplit) {
 }
 
 bool attn_supported(int H, int D, int kv_dt) {
-  return (kv_dt == CSA_BF16 && D == 512 && H > 32 && H <= 64) || (kv_dt == CSA_F32 && D == 64 && H >= 1 && H <= 32);
+  return (kv_dt == CSA_BF16 && D == 512 && H > 48 && H <= 64) || (kv_dt == CSA_F32 && D == 64 && H >= 1 && H <= 16);
 }
 
 int check_attn_common(const void* q, const void* out, int H, int D, int kv_dt, int out_dt, int W, int top_k) {
@@ -53,7 +59,7 @@ int check_attn_common(const void* q, const void* out, int H, int D, int kv_dt, i
   REQ(out_dt == CSA_F32 || out_dt == CSA_BF16 || out_dt == CSA_FP8_E4M3, CSA_INVALID_ARG, "unknown out_dt");
   REQ(out_dt != CSA_FP8_E4M3, CSA_UNSUPPORTED, "out_dt must be F32 or BF16");
   REQ(attn_supported(H, D, kv_dt), CSA_UNSUPPORTED,
-      "unsupported (H, D, kv_dt): supported are (33..64, 512, BF16) and (1..32, 64, F32)");
+      "unsupported (H, D, kv_dt): supported are (49..64, 512, BF16) and (1..16, 64, F32)");
   REQ(aligned16(q), CSA_INVALID_ARG, "q must be 16-byte aligned");
   REQ(out_dt != CSA_F32 || aligned16(out), CSA_INVALID_ARG, "out must be 16-byte aligned");
   return CSA_OK;
@@ -254,6 +260,7 @@ int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_i
   REQ(W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
   REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
   REQ(Tq <= 0x7fffffff, CSA_UNSUPPORTED, "Tq too large");
+  REQ(top_k <= 1024, CSA_UNSUPPORTED, "sparse_mqa_prefill supports top_k <= 1024");
   csa::AttnLaunch a{};
   a.src = 2;
   a.q = q;
@@ -283,7 +290,7 @@ int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_i
 
 size_t hca_dense_mqa_workspace_bytes(int64_t B, int H, int D, int64_t N_max, int W) {
   if (B < 0 || H <= 0 || D <= 0 || N_max < 0 || W < 0) return 0;
-  return attn_ws(B, H, D, nsplit_for(N_max + W, HCA_SPLIT_ROWS));
+  return attn_ws(B, H, D, nsplit_for(N_max + W, hca_split_rows(N_max + W)));
 }
 
 int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, const int32_t* q_pos, int m,
@@ -297,7 +304,8 @@ int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, con
   REQ(N_max == 0 || (kv_comp && n_comp && q_pos), CSA_INVALID_ARG, "kv_comp, n_comp, q_pos must not be NULL");
   REQ(W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
   REQ(N_max + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
-  const int ns = nsplit_for(N_max + W, HCA_SPLIT_ROWS);
+  const int hsr = hca_split_rows(N_max + W);
+  const int ns = nsplit_for(N_max + W, hsr);
   const size_t need = attn_ws(B, H, D, ns);
   REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
   REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
@@ -322,7 +330,7 @@ int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, con
   a.kv_dt = kv_dt;
   a.out_dt = out_dt;
   a.slots = (int)(N_max + W);
-  a.split_rows = ns > 1 ? HCA_SPLIT_ROWS : a.slots;
+  a.split_rows = ns > 1 ? hsr : a.slots;
   a.nsplit = ns;
   a.part_o = reinterpret_cast<float*>(ws);
   a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + round256((size_t)B * ns * H * D * 4));

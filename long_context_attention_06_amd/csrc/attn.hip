@@ -10,23 +10,28 @@
 // l_r = scale * <q_h, r> for every row r of the multiset plus a sink logit,
 // then the weighted sum of the rows (each row is key and value at once).
 //
-// Design (MI355X-first):
-//  * A workgroup owns one query token (all 64 heads) and a contiguous range of
-//    row slots ("split"). Rows are processed in tiles of 32: the tile is
-//    loaded with coalesced 16-byte loads into LDS, row-major with an XOR
-//    chunk swizzle, and prefetched into registers one tile ahead.
-//  * 8 waves = 4 dims-quarters x 2 head-halves. S^T = R Q^T runs on
-//    v_mfma_f32_32x32x16_bf16 with M = rows, N = heads, each wave covering its
-//    128 dims; partial logits meet in LDS. Every wave then runs the online
-//    softmax for 8 heads (fp32, exp2 domain) and writes P (bf16) to LDS.
-//  * O += P R runs on the same MFMA with M = heads, N = dims. Its B operand
-//    (8 consecutive rows of one dim) comes from the row-major tile through
-//    ds_read_b64_tr_b16, so the tile is stored once for both products.
-//  * Splits write unnormalised (O, m, l) partials; a combine kernel merges
-//    them in fixed split order and adds the sink. Split sizes depend only on
-//    the per-query slot count, so results are batch invariant.
-//  * The fp32 instantiation (tiny shapes) uses v_mfma_f32_32x32x2f32 with the
-//    same structure; its tile has a padded pitch instead of the swizzle.
+// Design (MI355X-first, heads split across waves):
+//  * A workgroup owns one query token and a contiguous range of row slots (a
+//    "split"). Wave w owns heads 16w..16w+15 over all D dims, so the online
+//    softmax of a head never leaves its wave and no logits cross waves.
+//  * Rows are processed in tiles of 32, double-buffered in LDS (row-major,
+//    16-byte chunks XOR-swizzled), loaded with coalesced 16-byte loads into
+//    a ring of two register tiles (the HBM latency needs deep prefetch): one barrier per tile. Top-k indices of the
+//    split are staged in LDS first, so no tile waits on an index load.
+//  * S^T = R Q^T on v_mfma_f32_16x16x32_bf16 (M = 16 rows, N = 16 heads,
+//    K = 32 dims); Q stays in registers. The accumulator layout gives each
+//    lane 8 rows of one head, which is exactly the P operand of the next
+//    product once the 32 tile rows are taken in a permuted K order.
+//  * O += P R on the same MFMA (M = 16 heads, N = 16 dims, K = 32 rows); its
+//    R operand (4 consecutive rows of one dim per read) comes from the
+//    row-major tile through ds_read_b64_tr_b16, in the same K order.
+//  * Splits write unnormalised (O, m, l) partials (exp2 domain); a combine
+//    kernel merges them in fixed split order and adds the sink. Split sizes
+//    depend only on per-query shape arguments: results are batch invariant.
+//  * The fp32 instantiation (tiny shapes) runs v_mfma_f32_16x16x4f32 with
+//    the same structure; its tile has a padded pitch instead of the swizzle.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -34,55 +39,36 @@ namespace csa {
 
 enum { SRC_SPARSE_DEC = 0, SRC_HCA_DEC = 1, SRC_SPARSE_PRE = 2 };
 
+// XOR swizzle of the 16-byte chunk index inside each 256-byte group of a
+// tile row. Sixteen consecutive rows map one chunk to sixteen different
+// chunk slots (b128 reads of a column by 16 rows are conflict-free with 64
+// banks, and with 32 banks for any 8 of them), and the 4 rows x 2 chunks of a
+// transpose read land in 8 different slots.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8); }
+
+// Lazy rescaling of the online softmax: the exponent reference of a head
+// only moves when a tile's maximum exceeds it by more than this (log2 units),
+// so P <= 2^8 and the O accumulators are rarely touched.
+constexpr float RESCALE_SLACK = 8.0f;
+
+__device__ __forceinline__ f32x4_t mfma_s(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_s(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <typename T>
-struct OpTraits;
+struct HsTraits;
 template <>
-struct OpTraits<uint16_t> {  // bf16 storage
-  static constexpr int KSTEP = 16, VPL = 8;
+struct HsTraits<uint16_t> {  // bf16 storage: 16x16x32, 8 values per lane
+  static constexpr int KSTEP = 32, VPL = 8;
   typedef bf16x8_t op_t;
 };
 template <>
-struct OpTraits<float> {
-  static constexpr int KSTEP = 2, VPL = 1;
+struct HsTraits<float> {  // fp32 storage: 16x16x4, 1 value per lane
+  static constexpr int KSTEP = 4, VPL = 1;
   typedef float op_t;
-};
-
-// XOR swizzle of the 16-byte chunk index inside each 128-byte group of a
-// tile row. Eight consecutive rows map a chunk to eight different bank
-// groups (conflict-free b128 reads of one column by 32 rows), and the four
-// rows of a transpose read cover all 32 banks.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
-
-template <typename T, int HP, int D, int NWD, int NWH>
-struct AttnCfg {
-  static constexpr int NW = NWD * NWH;
-  static constexpr int NT = 64 * NW;
-  static constexpr int HPW = HP / NWH;  // heads per wave in QK / PV (32)
-  static constexpr int DW = D / NWD;    // dims per wave
-  static constexpr int ES = sizeof(T);
-  static constexpr int KSTEP = OpTraits<T>::KSTEP;
-  static constexpr int VPL = OpTraits<T>::VPL;
-  static constexpr int KSQ = DW / KSTEP;  // QK k-steps per wave
-  static constexpr int TR = 32;           // rows per tile
-  static constexpr int CPR = D * ES / 16; // 16-byte chunks per row
-  static constexpr int RPP = NT / CPR;    // rows per load pass
-  static constexpr int PASSES = TR / RPP;
-  static constexpr int HS = HP / NW;      // heads per wave in the softmax
-  static constexpr int LPH = 64 / HS;     // lanes per head in the softmax
-  static constexpr int RPL = TR / LPH;    // rows per lane in the softmax
-  static constexpr int NTD = DW / 32;     // PV N-tiles per wave
-  static constexpr int SP = TR + 4;       // Spart pitch (floats)
-  static constexpr bool BF = (ES == 2);
-  static constexpr int RPITCH = BF ? D * 2 : (D + 1) * 4;  // tile row pitch (bytes)
-  static constexpr int PP = BF ? (TR + 8) : (TR + 1);      // P pitch (elements)
-  static constexpr int LDS_R = TR * RPITCH;
-  static constexpr int LDS_S = NWD * HP * SP * 4;
-  static constexpr int LDS_P = HP * PP * ES;
-  static_assert(HPW == 32, "one 32-head MFMA tile per wave");
-  static_assert(DW % 32 == 0, "dims per wave must fill PV N-tiles");
-  static_assert(NT % CPR == 0 && TR % RPP == 0, "tile load mapping");
-  static_assert(RPL * LPH == TR && HS * NW == HP, "softmax mapping");
-  static_assert(RPL % 4 == 0, "softmax reads in float4");
 };
 
 struct RowSrc {
@@ -133,324 +119,287 @@ __device__ __forceinline__ const uint8_t* slot_row(const RowSrc& s, int64_t qi, 
   }
 }
 
-template <typename T, int HP, int D, int NWD, int NWH, int SRC>
-__global__ void __launch_bounds__(64 * NWD * NWH)
+template <typename T, int D, int NWAV, int SRC>
+__global__ void __launch_bounds__(64 * NWAV) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_kernel(const T* __restrict__ q, RowSrc src, const int32_t* __restrict__ win_len,
             const int32_t* __restrict__ n_comp, const int32_t* __restrict__ q_pos, int m_rate,
             const float* __restrict__ sink, float scale_log2, int H, int slots, int split_rows,
             float* __restrict__ part_o, float* __restrict__ part_ml, void* __restrict__ out,
             float* __restrict__ lse, int out_dt) {
-  typedef AttnCfg<T, HP, D, NWD, NWH> C;
-  typedef typename OpTraits<T>::op_t op_t;
-  constexpr int ROWB = D * C::ES;
+  typedef typename HsTraits<T>::op_t op_t;
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int KSTEP = HsTraits<T>::KSTEP, VPL = HsTraits<T>::VPL;
+  constexpr int ES = sizeof(T);
+  constexpr int NT = 64 * NWAV;
+  constexpr int TR = 32;                         // rows per tile
+  constexpr int ROWB = D * ES;                   // bytes per row
+  constexpr int RPITCH = BF ? ROWB : ROWB + 4;   // LDS row pitch (bytes)
+  constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
+  constexpr int RPP = NT / CPR;                  // rows per load pass
+  constexpr int PASSES = TR / RPP;
+  constexpr int KSQ = D / KSTEP;                 // QK k-steps
+  constexpr int NTD = D / 16;                    // PV N-tiles
+  static_assert(NT % CPR == 0 && TR % RPP == 0, "tile load mapping");
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_r[C::LDS_R];
-  __shared__ __attribute__((aligned(16))) float lds_s[C::LDS_S / 4];
-  __shared__ __attribute__((aligned(16))) T lds_p[HP * C::PP];
-  __shared__ __attribute__((aligned(16))) float lds_alpha[HP];
-  __shared__ __attribute__((aligned(16))) float lds_ml[HP * 2];
-  __shared__ int lds_valid[C::TR];
-  __shared__ int lds_flag[C::NW];
+  constexpr int PF = 2;            // tiles in flight in the register ring
+  constexpr int CODE_MAX = 1024;   // top-k slots per split staged in LDS
+  __shared__ __attribute__((aligned(16))) uint8_t lds_r[2][TR * RPITCH];
+  __shared__ int lds_valid[2][TR];
+  __shared__ int lds_code[(SRC == SRC_HCA_DEC) ? 1 : CODE_MAX];
 
   const int tid = threadIdx.x;
-  const int l = tid & 63;
-  const int wv = tid >> 6;
-  const int g = l >> 5;       // k-group of the MFMA operand
-  const int l32 = l & 31;
-  const int dq = wv % NWD;    // dims quarter
-  const int hh = wv / NWD;    // head half
+  const int l = tid & 63, wv = tid >> 6;
+  const int G = l >> 4, l16 = l & 15;
   const int64_t qi = blockIdx.x;  // query (decode: sequence)
-  const int sp = blockIdx.y;       // split
+  const int sp = blockIdx.y;      // split
   const int nsplit = gridDim.y;
+  const int head = wv * 16 + l16;  // this lane's head in S^T / P / softmax
 
-  // per-query limits
   int lim0 = 0, lim1 = 0;
   if (SRC == SRC_SPARSE_DEC) {
     lim0 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
   } else if (SRC == SRC_HCA_DEC) {
     if (n_comp) {
-      int64_t v = min((int64_t)n_comp[qi], ((int64_t)q_pos[qi] + 1) / m_rate);
+      const int64_t v = min((int64_t)n_comp[qi], ((int64_t)q_pos[qi] + 1) / m_rate);
       lim0 = (int)max((int64_t)0, min(v, src.N_max));
     }
     lim1 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
   } else {
     lim1 = q_pos[qi];
   }
-
   const int s_begin = sp * split_rows;
   const int s_end = min(slots, s_begin + split_rows);
-  const int ntiles = (s_end > s_begin) ? (s_end - s_begin + C::TR - 1) / C::TR : 0;
+  const int ntiles = (s_end > s_begin) ? (s_end - s_begin + TR - 1) / TR : 0;
 
-  // ---- Q^T operands for this wave (heads hh*32 + l32, dims of quarter dq).
-  op_t qb[C::KSQ];
+  // ---- Q^T operand (B of S^T = R Q^T): lane (head, G), dims s*KSTEP + G*VPL + 0..VPL-1
+  op_t qb[KSQ];
   {
-    const int head = hh * 32 + l32;
-    const int dim0 = dq * C::DW + g * (C::DW / 2);
-    if constexpr (C::BF) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(q) + (qi * H + head) * (int64_t)D + dim0;
+    const bool hok = head < H;
+    if constexpr (BF) {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(q) + (qi * H + (hok ? head : 0)) * (int64_t)D + G * 8;
 #pragma unroll
-      for (int s = 0; s < C::KSQ; ++s) {
-        u32x4_t v = {0, 0, 0, 0};
-        if (head < H) v = ld16(qp + s * 8);
-        qb[s] = as_bf16x8(v);
-      }
+      for (int s = 0; s < KSQ; ++s) qb[s] = as_bf16x8(hok ? ld16(qp + s * 32) : u32x4_t{0, 0, 0, 0});
     } else {
-      const float* qp = reinterpret_cast<const float*>(q) + (qi * H + head) * (int64_t)D + dim0;
+      const float* qp = reinterpret_cast<const float*>(q) + (qi * H + (hok ? head : 0)) * (int64_t)D + G;
 #pragma unroll
-      for (int s = 0; s < C::KSQ; ++s) qb[s] = (head < H) ? qp[s] : 0.0f;
+      for (int s = 0; s < KSQ; ++s) qb[s] = hok ? qp[s * 4] : 0.0f;
     }
   }
 
-  // ---- tile loader: thread handles chunk c of rows rsub + ps*RPP
-  const int lc = tid % C::CPR;
-  const int lrs = tid / C::CPR;
-  u32x4_t pre[C::PASSES];
-  int prev[C::PASSES];
-  int pcode[C::PASSES];
-  auto fetch_code = [&](int tile) {
-    const int base = s_begin + tile * C::TR;
-#pragma unroll
-    for (int ps = 0; ps < C::PASSES; ++ps) {
-      const int j = base + lrs + ps * C::RPP;
-      pcode[ps] = (j < s_end) ? slot_code<SRC>(src, qi, j) : -1;
-    }
-  };
-  auto fetch = [&](int tile) {
-    const int base = s_begin + tile * C::TR;
-#pragma unroll
-    for (int ps = 0; ps < C::PASSES; ++ps) {
-      const int r = lrs + ps * C::RPP;
-      const int j = base + r;
-      const uint8_t* rp = (j < s_end) ? slot_row<SRC, ROWB>(src, qi, j, pcode[ps], lim0, lim1) : nullptr;
-      prev[ps] = rp != nullptr;
-      u32x4_t v = {0, 0, 0, 0};
-      if (rp) v = ld16(rp + lc * 16);
-      pre[ps] = v;
-    }
-  };
-  auto stash = [&]() -> int {
-    int any = 0;
-#pragma unroll
-    for (int ps = 0; ps < C::PASSES; ++ps) {
-      const int r = lrs + ps * C::RPP;
-      if constexpr (C::BF) {
-        const int phys = lc ^ swz(r);
-        *reinterpret_cast<u32x4_t*>(lds_r + r * C::RPITCH + phys * 16) = pre[ps];
-      } else {
-        float* dst = reinterpret_cast<float*>(lds_r + r * C::RPITCH) + lc * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(pre[ps][e]);
-      }
-      if (lc == 0) lds_valid[r] = prev[ps];
-      any |= prev[ps];
-    }
-    return any;
-  };
-
-  f32x16_t oacc[C::NTD];
-#pragma unroll
-  for (int nt = 0; nt < C::NTD; ++nt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[nt][r] = 0.0f;
-
-  // softmax state of this lane's head (owned across tiles)
-  const int sm_head = wv * C::HS + (l % C::HS);
-  const int sm_rg = l / C::HS;
-  float m_run = -INFINITY, l_run = 0.0f;
-
-  if (ntiles > 0) {
-    fetch_code(0);
-    fetch(0);
-    if (ntiles > 1) fetch_code(1);
-  }
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int any = __syncthreads_or(stash());
-    if (tile + 1 < ntiles) {
-      fetch(tile + 1);  // uses the codes loaded one iteration ago
-      if (tile + 2 < ntiles) fetch_code(tile + 2);
-    }
-    if (!any) continue;
-
-    // ---- S^T partial = R(rows x DW) * Q^T(DW x 32 heads)
-    f32x16_t sacc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
-    {
-      const int row = l32;
-      if constexpr (C::BF) {
-        const int c0 = (dq * C::DW + g * (C::DW / 2)) / 8;
-        const uint8_t* rb = lds_r + row * C::RPITCH;
-        const int sw = swz(row);
-#pragma unroll
-        for (int s = 0; s < C::KSQ; ++s) {
-          u32x4_t a = *reinterpret_cast<const u32x4_t*>(rb + ((c0 + s) ^ sw) * 16);
-          sacc = mfma32(as_bf16x8(a), qb[s], sacc);
-        }
-      } else {
-        const float* rb = reinterpret_cast<const float*>(lds_r + row * C::RPITCH) + dq * C::DW + g * (C::DW / 2);
-#pragma unroll
-        for (int s = 0; s < C::KSQ; ++s) sacc = mfma32(rb[s], qb[s], sacc);
-      }
-    }
-    {
-      float* sp_base = lds_s + (dq * HP + hh * 32 + l32) * C::SP + g * 4;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4_t v = {sacc[r4 * 4 + 0], sacc[r4 * 4 + 1], sacc[r4 * 4 + 2], sacc[r4 * 4 + 3]};
-        *reinterpret_cast<f32x4_t*>(sp_base + r4 * 8) = v;
-      }
-    }
+  // ---- top-k indices of this split, staged once in LDS (sparse row sources)
+  if (SRC == SRC_SPARSE_DEC || SRC == SRC_SPARSE_PRE) {
+    const int ncode = min(s_end, src.top_k) - s_begin;  // slots of this split that are top-k slots
+    for (int i = tid; i < ncode; i += NT) lds_code[i] = slot_code<SRC>(src, qi, s_begin + i);
     __syncthreads();
+  }
 
-    // ---- online softmax for heads [wv*HS, (wv+1)*HS)
-    {
-      float sv[C::RPL];
+  // ---- tile loader: thread handles chunk lc of rows lrs + ps*RPP. Tiles go
+  // HBM -> register ring (PF tiles deep) -> LDS double buffer -> MFMA.
+  const int lc = tid % CPR, lrs = tid / CPR;
+  u32x4_t pre[PF][PASSES];
+  uint32_t prevm[PF];
+  auto fetch = [&](auto SLOT, int tile) {
+    constexpr int slot = decltype(SLOT)::value;
+    const int base = s_begin + tile * TR;
+    uint32_t vm = 0;
 #pragma unroll
-      for (int i = 0; i < C::RPL; ++i) sv[i] = 0.0f;
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int j = base + lrs + ps * RPP;
+      const int code = (j < s_end && j - s_begin < CODE_MAX && (SRC != SRC_HCA_DEC) && j < src.top_k)
+                           ? lds_code[j - s_begin] : -1;
+      const uint8_t* rp = (j < s_end) ? slot_row<SRC, ROWB>(src, qi, j, code, lim0, lim1) : nullptr;
+      vm |= (rp != nullptr ? 1u : 0u) << ps;
+      pre[slot][ps] = rp ? ld16(rp + lc * 16) : u32x4_t{0, 0, 0, 0};
+    }
+    prevm[slot] = vm;
+  };
+  auto stash = [&](auto SLOT, int buf) -> int {
+    constexpr int slot = decltype(SLOT)::value;
 #pragma unroll
-      for (int d = 0; d < NWD; ++d) {
-        const float* src_s = lds_s + (d * HP + sm_head) * C::SP + sm_rg * C::RPL;
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int r = lrs + ps * RPP;
+      if constexpr (BF) {
+        *reinterpret_cast<u32x4_t*>(&lds_r[buf][r * RPITCH + ((lc ^ swz(r)) * 16)]) = pre[slot][ps];
+      } else {
+        float* dst = reinterpret_cast<float*>(&lds_r[buf][r * RPITCH]) + lc * 4;
 #pragma unroll
-        for (int i4 = 0; i4 < C::RPL / 4; ++i4) {
-          f32x4_t v = *reinterpret_cast<const f32x4_t*>(src_s + i4 * 4);
+        for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(pre[slot][ps][e]);
+      }
+      if (lc == 0) lds_valid[buf][r] = (prevm[slot] >> ps) & 1;
+    }
+    return prevm[slot] != 0;
+  };
+
+  f32x4_t oacc[NTD];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sv[i4 * 4 + e] += v[e];
+  for (int nt = 0; nt < NTD; ++nt) oacc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;  // for `head`, replicated over G
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  static_assert(PF == 2, "ring of two tiles");
+  int any_next = 0;
+  if (ntiles > 0) {
+    fetch(I0{}, 0);
+    any_next = stash(I0{}, 0);
+    if (ntiles > 1) fetch(I1{}, 1);
+    if (ntiles > 2) fetch(I0{}, 2);
+    any_next = __syncthreads_or(any_next);
+  }
+  // one tile: stage tile+1 (ring slot SLOT) into the other LDS buffer, refill
+  // the slot with tile+1+PF, compute tile from LDS, one barrier
+  auto body = [&](int tile, auto SLOT) {
+    const int buf = tile & 1;
+    const int any = any_next;
+    if (tile + 1 < ntiles) {
+      any_next = stash(SLOT, buf ^ 1);
+      if (tile + 1 + PF < ntiles) fetch(SLOT, tile + 1 + PF);
+    }
+    if (any) {
+      const uint8_t* R = lds_r[buf];  // tile `tile`
+      // ---- S^T[mt] = R(rows mt*16..) Q^T : lane holds rows mt*16 + G*4 + r of `head`
+      f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int row = mt * 16 + l16;
+        // dims s*32 + G*8 .. +8 live in chunk 4s + G = 16*(s/4) + (4*(s%4) + G)
+        int qofs[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) qofs[v] = row * RPITCH + (((4 * v + G) ^ swz(row)) * 16);
+#pragma unroll
+        for (int s = 0; s < KSQ; ++s) {
+          op_t a;
+          if constexpr (BF) {
+            a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(R + qofs[s & 3] + (s >> 2) * 256));
+          } else {
+            a = reinterpret_cast<const float*>(R + row * RPITCH)[s * 4 + G];
+          }
+          sacc[mt] = mfma_s(a, qb[s], sacc[mt]);
+          if ((s & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bound live operands
         }
       }
+      // ---- online softmax of `head` over this tile's 32 rows (exp2 domain)
+      float sv[8];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < C::RPL; ++i) {
-        const bool ok = lds_valid[sm_rg * C::RPL + i] != 0;
-        sv[i] = ok ? sv[i] * scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, sv[i]);
-      }
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int msk = C::HS; msk < 64; msk <<= 1) tmax = fmaxf(tmax, shfl_xor(tmax, msk));
-      const float m_new = fmaxf(m_run, tmax);
-      float alpha = 1.0f;
-      float psum = 0.0f;
-      float pv[C::RPL];
+        for (int r = 0; r < 4; ++r) {
+          const int row = mt * 16 + G * 4 + r;
+          const float v = lds_valid[buf][row] ? sacc[mt][r] * scale_log2 : -INFINITY;
+          sv[mt * 4 + r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      // m_run is the exponent reference (not necessarily the running max): it
+      // moves to the tile max only when that exceeds it by RESCALE_SLACK
+      const bool move = tmax > m_run + RESCALE_SLACK || (m_run == -INFINITY && tmax != -INFINITY);
+      const float m_new = move ? tmax : m_run;
+      float alpha = 1.0f, psum = 0.0f;
+      float pv[8];
       if (m_new == -INFINITY) {
 #pragma unroll
-        for (int i = 0; i < C::RPL; ++i) pv[i] = 0.0f;
+        for (int i = 0; i < 8; ++i) pv[i] = 0.0f;
       } else {
-        alpha = exp2f(m_run - m_new);
+        if (move) alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
 #pragma unroll
-        for (int i = 0; i < C::RPL; ++i) {
-          const float p = exp2f(sv[i] - m_new);
-          pv[i] = p;  // rounded to bf16 when stored for the PV product
-          psum += p;
+        for (int i = 0; i < 8; ++i) {
+          pv[i] = __builtin_amdgcn_exp2f(sv[i] - m_new);
+          psum += pv[i];
         }
       }
-#pragma unroll
-      for (int msk = C::HS; msk < 64; msk <<= 1) psum += shfl_xor(psum, msk);
+      psum += shfl_xor(psum, 16);
+      psum += shfl_xor(psum, 32);
       l_run = l_run * alpha + psum;
       m_run = m_new;
-      if constexpr (C::BF) {
-        uint32_t w0 = pack_bf16x2(pv[0], pv[1]), w1 = pack_bf16x2(pv[2], pv[3]);
-        u32x2_t v = {w0, w1};
-        *reinterpret_cast<u32x2_t*>(lds_p + sm_head * C::PP + sm_rg * C::RPL) = v;
+      // ---- rescale O rows (heads G*4 + r of this wave) when a max moved
+      if (__any(alpha != 1.0f)) {
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, G * 4 + r, 64);
+#pragma unroll
+        for (int nt = 0; nt < NTD; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[nt][r] *= ar[r];
+      }
+      // ---- O += P R, K in the order (rows G*4 + 0..3 of M-tile 0, then of M-tile 1)
+      if constexpr (BF) {
+        const bf16x8_t pa = as_bf16x8(u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                               pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
+        // transpose-read source of this lane: rows rowa / rowa+16, dims nt*16 + 4*(l16%4) .. +3,
+        // i.e. chunk 2nt + c0 (c0 = bit 1 of l16), byte cb inside it; chunk 2nt + c0 = 16*(nt/8) + (2*(nt%8) + c0)
+        const int rowa = G * 4 + (l16 >> 2), rowb = rowa + 16;
+        const int c0 = (l16 >> 1) & 1, cb = (l16 & 1) * 8;
+        const int swa = swz(rowa), swb = swz(rowb);
+        int oa[8], ob[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          oa[u] = rowa * RPITCH + (((2 * u + c0) ^ swa) * 16) + cb;
+          ob[u] = rowb * RPITCH + (((2 * u + c0) ^ swb) * 16) + cb;
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTD; ++nt) {
+          auto* pa4 = (s16x4_t __attribute__((address_space(3)))*)(R + oa[nt & 7] + (nt >> 3) * 256);
+          auto* pb4 = (s16x4_t __attribute__((address_space(3)))*)(R + ob[nt & 7] + (nt >> 3) * 256);
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa4);
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pb4);
+          const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[nt] = mfma_s(pa, bv, oacc[nt]);
+          if ((nt & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bound live operands
+        }
       } else {
 #pragma unroll
-        for (int i = 0; i < C::RPL; ++i) lds_p[sm_head * C::PP + sm_rg * C::RPL + i] = pv[i];
-      }
-      if (sm_rg == 0) lds_alpha[sm_head] = alpha;
-      const bool need = __any(alpha != 1.0f);
-      if (l == 0) lds_flag[wv] = need;
-    }
-    __syncthreads();
-
-    // ---- O = O*alpha + P R   (heads hh*32.., dims dq*DW..)
-    {
-      int need = 0;
+        for (int j = 0; j < 8; ++j) {  // K = 4 rows per step: lane G holds row (j/4)*16 + G*4 + j%4
+          const int row = (j >> 2) * 16 + G * 4 + (j & 3);
+          const float* rr = reinterpret_cast<const float*>(R + row * RPITCH);
 #pragma unroll
-      for (int w = 0; w < C::NW; ++w) need |= lds_flag[w];
-      if (need) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          f32x4_t a = *reinterpret_cast<const f32x4_t*>(lds_alpha + hh * 32 + r4 * 8 + g * 4);
-#pragma unroll
-          for (int nt = 0; nt < C::NTD; ++nt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) oacc[nt][r4 * 4 + e] *= a[e];
-        }
-      }
-      const int head = hh * 32 + l32;
-#pragma unroll
-      for (int s = 0; s < C::TR / C::KSTEP; ++s) {
-        op_t a;
-        if constexpr (C::BF) {
-          a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(lds_p + head * C::PP + s * 16 + g * 8));
-        } else {
-          a = lds_p[head * C::PP + s * 2 + g];
-        }
-#pragma unroll
-        for (int nt = 0; nt < C::NTD; ++nt) {
-          op_t b;
-          if constexpr (C::BF) {
-            const int g16 = l >> 4, j = l & 15;
-            const int col = dq * C::DW + nt * 32 + (g16 & 1) * 16 + 4 * (j & 3);
-            const int rowa = s * 16 + (g16 >> 1) * 8 + (j >> 2);
-            const int rowb = rowa + 4;
-            const int ch = col >> 3, cb = (col & 7) * 2;
-            auto* pa = (s16x4_t __attribute__((address_space(3)))*)(lds_r + rowa * C::RPITCH + ((ch ^ swz(rowa)) * 16) + cb);
-            auto* pb = (s16x4_t __attribute__((address_space(3)))*)(lds_r + rowb * C::RPITCH + ((ch ^ swz(rowb)) * 16) + cb);
-            s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa);
-            s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pb);
-            u32x4_t bv;
-            bv[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-            bv[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-            bv[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-            bv[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-            b = as_bf16x8(bv);
-          } else {
-            const float* rb = reinterpret_cast<const float*>(lds_r + (s * 2 + g) * C::RPITCH);
-            b = rb[dq * C::DW + nt * 32 + l32];
-          }
-          oacc[nt] = mfma32(a, b, oacc[nt]);
+          for (int nt = 0; nt < NTD; ++nt) oacc[nt] = mfma_s(pv[j], rr[nt * 16 + l16], oacc[nt]);
         }
       }
     }
-    __syncthreads();
+    if (tile + 1 < ntiles) any_next = __syncthreads_or(any_next);
+  };
+  for (int t0 = 0; t0 < ntiles; t0 += PF) {
+    body(t0, I1{});
+    if (t0 + 1 < ntiles) body(t0 + 1, I0{});
   }
 
-  // ---- epilogue
-  if (sm_rg == 0) {
-    lds_ml[sm_head * 2 + 0] = m_run;
-    lds_ml[sm_head * 2 + 1] = l_run;
+  // ---- epilogue: O rows are heads wv*16 + G*4 + r; their (m, l) live in lanes G*4 + r
+  float mr[4], lr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mr[r] = __shfl(m_run, G * 4 + r, 64);
+    lr[r] = __shfl(l_run, G * 4 + r, 64);
   }
-  __syncthreads();
   if (part_o != nullptr) {
-    // split partials: unnormalised O (relative to m), m, l  (exp2 domain)
     const int64_t pbase = (qi * nsplit + sp) * (int64_t)H;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int head = hh * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-      if (head >= H) continue;
+    for (int r = 0; r < 4; ++r) {
+      const int h = wv * 16 + G * 4 + r;
+      if (h >= H) continue;
 #pragma unroll
-      for (int nt = 0; nt < C::NTD; ++nt)
-        part_o[(pbase + head) * D + dq * C::DW + nt * 32 + l32] = oacc[nt][r];
+      for (int nt = 0; nt < NTD; ++nt) part_o[(pbase + h) * D + nt * 16 + l16] = oacc[nt][r];
     }
-    if (sm_rg == 0 && sm_head < H) {
-      part_ml[(pbase + sm_head) * 2 + 0] = m_run;
-      part_ml[(pbase + sm_head) * 2 + 1] = l_run;
+    if (G == 0 && head < H) {
+      part_ml[(pbase + head) * 2 + 0] = m_run;
+      part_ml[(pbase + head) * 2 + 1] = l_run;
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int head = hh * 32 + (r >> 2) * 8 + g * 4 + (r & 3);
-      if (head >= H) continue;
-      const float mh = lds_ml[head * 2], lh = lds_ml[head * 2 + 1];
-      const float s2 = sink ? sink[head] * LOG2E_F : -INFINITY;
-      const float M = fmaxf(mh, s2);
+    for (int r = 0; r < 4; ++r) {
+      const int h = wv * 16 + G * 4 + r;
+      if (h >= H) continue;
+      const float s2 = sink ? sink[h] * LOG2E_F : -INFINITY;
+      const float M = fmaxf(mr[r], s2);
       float fac = 0.0f;
       if (M != -INFINITY) {
-        const float a = exp2f(mh - M);
-        fac = a / (lh * a + exp2f(s2 - M));
+        const float a = exp2f(mr[r] - M);
+        fac = a / (lr[r] * a + exp2f(s2 - M));
       }
 #pragma unroll
-      for (int nt = 0; nt < C::NTD; ++nt) {
-        const int64_t o = (qi * H + head) * (int64_t)D + dq * C::DW + nt * 32 + l32;
+      for (int nt = 0; nt < NTD; ++nt) {
+        const int64_t o = (qi * H + h) * (int64_t)D + nt * 16 + l16;
         const float v = oacc[nt][r] * fac;
         if (out_dt == DT_BF16)
           reinterpret_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16(v);
@@ -458,12 +407,12 @@ attn_kernel(const T* __restrict__ q, RowSrc src, const int32_t* __restrict__ win
           reinterpret_cast<float*>(out)[o] = v;
       }
     }
-    if (lse && sm_rg == 0 && sm_head < H) {
-      const float s2 = sink ? sink[sm_head] * LOG2E_F : -INFINITY;
+    if (lse && G == 0 && head < H) {
+      const float s2 = sink ? sink[head] * LOG2E_F : -INFINITY;
       const float M = fmaxf(m_run, s2);
       float v = -INFINITY;
       if (M != -INFINITY) v = (M + log2f(l_run * exp2f(m_run - M) + exp2f(s2 - M))) * LN2_F;
-      lse[qi * H + sm_head] = v;
+      lse[qi * H + head] = v;
     }
   }
 }
@@ -536,7 +485,7 @@ attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ 
 // host-side launchers
 // ----------------------------------------------------------------------------
 
-template <typename T, int HP, int D, int NWD, int NWH, int SRC>
+template <typename T, int D, int NWAV, int SRC>
 static hipError_t launch_attn(const AttnLaunch& a, hipStream_t st) {
   RowSrc src;
   src.kv_comp = reinterpret_cast<const uint8_t*>(a.kv_comp);
@@ -547,10 +496,9 @@ static hipError_t launch_attn(const AttnLaunch& a, hipStream_t st) {
   src.top_k = a.top_k;
   src.W = a.W;
   dim3 grid((unsigned)a.nq, a.nsplit);
-  hipLaunchKernelGGL((attn_kernel<T, HP, D, NWD, NWH, SRC>), grid, dim3(64 * NWD * NWH), 0, st,
-                     reinterpret_cast<const T*>(a.q), src, a.win_len, a.n_comp, a.q_pos, a.m_rate, a.sink,
-                     a.scale * LOG2E_F, a.H, a.slots, a.split_rows, a.nsplit > 1 ? a.part_o : nullptr,
-                     a.part_ml, a.out, a.lse, a.out_dt);
+  hipLaunchKernelGGL((attn_kernel<T, D, NWAV, SRC>), grid, dim3(64 * NWAV), 0, st, reinterpret_cast<const T*>(a.q),
+                     src, a.win_len, a.n_comp, a.q_pos, a.m_rate, a.sink, a.scale * LOG2E_F, a.H, a.slots,
+                     a.split_rows, a.nsplit > 1 ? a.part_o : nullptr, a.part_ml, a.out, a.lse, a.out_dt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)a.nq, (unsigned)((a.H + 3) / 4)), dim3(256), 0, st,
@@ -560,10 +508,8 @@ static hipError_t launch_attn(const AttnLaunch& a, hipStream_t st) {
 
 template <int SRC>
 static hipError_t dispatch_src(const AttnLaunch& a, hipStream_t st) {
-  if (a.kv_dt == DT_BF16 && a.D == 512 && a.H <= 64 && a.H > 32)
-    return launch_attn<uint16_t, 64, 512, 4, 2, SRC>(a, st);
-  if (a.kv_dt == DT_F32 && a.D == 64 && a.H <= 32)
-    return launch_attn<float, 32, 64, 2, 1, SRC>(a, st);
+  if (a.kv_dt == DT_BF16 && a.D == 512 && a.H > 48 && a.H <= 64) return launch_attn<uint16_t, 512, 4, SRC>(a, st);
+  if (a.kv_dt == DT_F32 && a.D == 64 && a.H <= 16) return launch_attn<float, 64, 1, SRC>(a, st);
   return hipErrorInvalidValue;
 }
 

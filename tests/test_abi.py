@@ -102,7 +102,7 @@ def test_attention_validation():
     h = L.lib.hca_dense_mqa
     assert h(P, P, P, P, 0, P, P, P, 1.0, 2, 64, 512, 100, 8, 1, 1, P, None, None, 0, None) == L.INVALID_ARG
     needh = L.hca_dense_mqa_workspace_bytes(16, 64, 512, 8192, 128)
-    assert needh == 16 * 17 * 64 * 512 * 4 + 16 * 17 * 64 * 2 * 4
+    assert needh == 16 * 16 * 64 * 512 * 4 + 16 * 16 * 64 * 2 * 4
     p = L.lib.sparse_mqa_prefill
     assert p(P, P, P, P, None, P, 1.0, 4, 64, 512, 100, 400, 16, 8, 1, 1, P, None, None, 0, None) == L.INVALID_ARG
     assert p(P, P, P, P, P, P, 1.0, 4, 64, 512, 100, 400, 16, 8, 1, 2, P, None, None, 0, None) == L.UNSUPPORTED

@@ -41,7 +41,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4"])
+    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4", "c3"])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -86,9 +86,11 @@ def main():
     import long_context_attention_06_amd as L
     from synth import gen
 
-    cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4}[a.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.workload == "c3":
+        return bench_prefill(a, torch, L, gen, dev)
+    cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4}[a.workload]
     t0 = time.time()
     x = gen.gen_decode(cfg, with_compress=(cfg.kind == "csa_decode"))
     print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -218,6 +220,137 @@ def main():
     if not a.no_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, x, a.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def prefill_flops(cfg, pos):
+    """Algorithmic FLOPs of a prefill chunk: indexer over visible pairs,
+    sparse MQA over min(k, V) selected rows and the window rows."""
+    V = np.minimum(cfg.N, (pos.astype(np.int64) + 1) // cfg.m)
+    win = np.minimum(cfg.W, pos.astype(np.int64) + 1)
+    idx = float(V.sum()) * cfg.H_I * cfg.D_I * 2
+    mqa = float((np.minimum(cfg.top_k, V) + win).sum()) * cfg.H * cfg.D * 4
+    return idx, mqa
+
+
+def bench_prefill(a, torch, L, gen, dev):
+    """CSA prefill of one 65536-token sequence: compression of all tokens, then
+    16 chunks of 4096 queries through scores, top-k and sparse MQA."""
+    cfg = gen.C3
+    t0 = time.time()
+    tok = gen.gen_prefill_tokens(cfg)
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).to(dev)
+    td = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+    N, m, D, H, k, W = cfg.N, cfg.m, cfg.D, cfg.H, cfg.top_k, cfg.W
+    Ca, Cb, Za, Zb = (bf(tok[nm][None]) for nm in ("Ca", "Cb", "Za", "Zb"))
+    Ba, Bb, sink = td(tok["Ba"]), td(tok["Bb"]), td(tok["sink"])
+    kv_tok, k_idx = bf(tok["kv_tok"]), bf(tok["k_idx"][None])
+    comp = torch.empty((1, N, D), dtype=torch.bfloat16, device=dev)
+    nch = gen.num_chunks(cfg)
+    chunks = []
+    for c in range(nch):
+        qs = gen.gen_prefill_queries(cfg, c)
+        chunks.append({"q": bf(qs["q"]), "q_idx": bf(qs["q_idx"][None]), "w": td(qs["w"][None]),
+                       "q_pos": td(qs["q_pos"][None]), "pos_np": qs["q_pos"]})
+    print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    T = gen.QCHUNK
+    n_comp = td(np.array([N], np.int32))
+    scores = torch.empty((1, T, N), dtype=torch.float32, device=dev)
+    idx = torch.empty((1, T, k), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    ws_t = torch.empty(max(1, L.indexer_topk_workspace_bytes(1, T, N, k)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    def run(ev=None):
+        if ev is not None: ev[0].record(stream)
+        L.csa_compress(Ca, Cb, Za, Zb, Ba, Bb, comp, m=m, stream=s)
+        if ev is not None: ev[1].record(stream)
+        for c, ch in enumerate(chunks):
+            L.indexer_score(ch["q_idx"], ch["w"], k_idx, None, ch["q_pos"], n_comp, scores, m=m, stream=s)
+            if ev is not None: ev[2 + 3 * c].record(stream)
+            L.indexer_topk(scores, ch["q_pos"], n_comp, idx, m=m, ws=ws_t, stream=s)
+            if ev is not None: ev[3 + 3 * c].record(stream)
+            L.sparse_mqa_prefill(ch["q"], comp[0], idx[0], kv_tok, ch["q_pos"][0], sink, out, W=W, stream=s)
+            if ev is not None: ev[4 + 3 * c].record(stream)
+
+    for _ in range(max(1, a.warmup)):
+        run()
+    torch.cuda.synchronize()
+    steps = max(1, min(a.steps, 5))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + 3 * nch)]
+    run(ev)
+    torch.cuda.synchronize()
+    comp_ms = ev[0].elapsed_time(ev[1])
+    prev = [ev[1]] + [ev[4 + 3 * c] for c in range(nch - 1)]
+    idx_ms = [prev[c].elapsed_time(ev[2 + 3 * c]) for c in range(nch)]
+    topk_ms = [ev[2 + 3 * c].elapsed_time(ev[3 + 3 * c]) for c in range(nch)]
+    attn_ms = [ev[3 + 3 * c].elapsed_time(ev[4 + 3 * c]) for c in range(nch)]
+    fl = [prefill_flops(cfg, ch["pos_np"]) for ch in chunks]
+    idx_fl, mqa_fl = sum(f[0] for f in fl), sum(f[1] for f in fl)
+    total_fl = idx_fl + mqa_fl
+    idx_tfs = idx_fl / (sum(idx_ms) * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(cfg.n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": max(1, a.warmup), "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.n, "query_chunk": T, "compressed_entries": N, "m": m,
+                   "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I, "heads": H, "head_dim": D,
+                   "window": W},
+        "prefill_tflops": round(total_fl / (ms * 1e-3) / 1e12, 2),
+        "algorithmic_tflop": round(total_fl / 1e12, 3),
+        "roofline": {"bound": "mfma", "kernel": "idx_prefill_kernel", "achieved": round(idx_tfs, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_all_launches": idx_fl,
+                     "avg_launch_ms": round(float(np.mean(idx_ms)), 4)},
+        "phases_ms": {"compress": round(comp_ms, 4), "indexer_total": round(sum(idx_ms), 4),
+                      "topk_total": round(sum(topk_ms), 4), "attention_total": round(sum(attn_ms), 4)},
+        "mqa_tflops": round(mqa_fl / (sum(attn_ms) * 1e-3) / 1e12, 2),
+    }
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_prefill_baseline(cfg, tok, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_prefill_baseline(cfg, tok, budget_s: float):
+    """The oracle on the host: compression of the whole sequence is timed,
+    then queries of the last chunk one by one until the budget is spent; the
+    rate is extrapolated to all queries by visible-pair counts."""
+    import oracle
+    from synth import gen
+    t0 = time.perf_counter()
+    comp = oracle.compress(tok["Ca"], tok["Cb"], tok["Za"], tok["Zb"], tok["Ba"], tok["Bb"], cfg.m)
+    t_comp = time.perf_counter() - t0
+    qs = gen.gen_prefill_queries(cfg, gen.num_chunks(cfg) - 1)
+    t1 = time.perf_counter()
+    done, pairs = 0, 0
+    while done < len(qs["q_pos"]) and (done == 0 or time.perf_counter() - t1 < budget_s):
+        i = len(qs["q_pos"]) - 1 - done
+        p = int(qs["q_pos"][i])
+        oracle.csa_query(qs["q"][i], qs["q_idx"][i], qs["w"][i], comp, tok["k_idx"], p, cfg.N, cfg.m, cfg.top_k,
+                         oracle.window_rows(tok["kv_tok"], p, cfg.W), tok["sink"])
+        pairs += min(cfg.N, (p + 1) // cfg.m)
+        done += 1
+    t_q = time.perf_counter() - t1
+    all_pairs = float(np.minimum(cfg.N, (np.arange(cfg.n, dtype=np.int64) + 1) // cfg.m).sum())
+    est = t_comp + t_q * all_pairs / max(pairs, 1)
+    return {"value": round(cfg.n / est, 3), "unit": "tokens/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"compression of all {cfg.n} tokens ({t_comp:.1f}s) + {done} queries of the last chunk "
+                      f"({t_q:.1f}s), extrapolated to all queries by visible-pair counts"}
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return 1
 
 
 def cpu_baseline(cfg, x, budget_s: float):

@@ -151,6 +151,142 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
   }
 }
 
+// Prefill: many queries of one sequence. A workgroup of 8 waves owns 8
+// consecutive query rows (wave w <-> row 8*blockIdx.x + w); each 64-entry key
+// tile is loaded once (coalesced, XOR-swizzled LDS, double-buffered) and used
+// by all 8 waves, so HBM/L2 key traffic drops 8x against the row kernel. Per
+// wave and tile: 4 M-tiles (heads) x 4 N-tiles (entries) x 4 k-steps of
+// v_mfma_f32_16x16x32_bf16. The workgroup walks tiles up to the largest
+// visible count of its rows; entries a row cannot see are not written.
+template <int KDT>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+                   const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
+                   const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
+                   int64_t N_max, int m, float* __restrict__ scores) {
+  constexpr int H = 64, DI = 128, KS = 4, QB = 8;
+  constexpr int KROW = (KDT == DT_FP8) ? DI : DI * 2;
+  constexpr int TE = 64;
+  constexpr int TB = TE * KROW;
+  constexpr int NT = 64 * QB;
+  constexpr int LPT = (TB + NT * 16 - 1) / (NT * 16);  // 16-byte loads per thread per tile
+  static_assert(TB % (NT * 16) == 0 || TB < NT * 16, "tile load mapping");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][TB];
+  __shared__ __attribute__((aligned(16))) float lds_w[QB][H];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63, wv = tid >> 6;
+  const int G = l >> 4, l16 = l & 15;
+  const int64_t b = blockIdx.y;
+  const int64_t t = (int64_t)blockIdx.x * QB + wv;  // this wave's query inside sequence b
+  const bool qok = t < Tq;
+  const int64_t row = b * Tq + (qok ? t : 0);
+  int64_t Vq = 0;
+  if (qok) {
+    Vq = min((int64_t)n_comp[b], ((int64_t)q_pos[row] + 1) / m);
+    Vq = max((int64_t)0, min(Vq, N_max));
+  }
+  // largest visible count over the workgroup's rows (rows are not assumed sorted)
+  __shared__ int64_t lds_vmax[QB];
+  if (l == 0) lds_vmax[wv] = Vq;
+  if (tid < H * QB) {
+    const int qq = tid / H, h = tid % H;
+    const int64_t tq = (int64_t)blockIdx.x * QB + qq;
+    lds_w[qq][h] = tq < Tq ? w[(b * Tq + tq) * H + h] : 0.0f;
+  }
+  __syncthreads();
+  int64_t Vmax = 0;
+#pragma unroll
+  for (int i = 0; i < QB; ++i) Vmax = max(Vmax, lds_vmax[i]);
+  const int64_t ntiles = (Vmax + TE - 1) / TE;
+  if (ntiles == 0) return;
+
+  bf16x8_t qa[4][KS];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const uint16_t* qp = q_idx + (row * H + mt * 16 + l16) * DI + G * 32;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qa[mt][s] = as_bf16x8(qok ? ld16(qp + s * 8) : u32x4_t{0, 0, 0, 0});
+  }
+  const uint8_t* kb = k_idx + b * N_max * KROW;
+  float* srow = scores + row * N_max;
+
+  u32x4_t rg[2][LPT];
+  auto load = [&](auto SLOT, int64_t tile) {
+    constexpr int slot = decltype(SLOT)::value;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int o = (j * NT + tid) * 16;
+      const int64_t e = tile * TE + o / KROW;
+      rg[slot][j] = (o < TB && e < Vmax) ? ld16(kb + e * KROW + (o % KROW)) : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto stash = [&](auto SLOT) {
+    constexpr int slot = decltype(SLOT)::value;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int o = (j * NT + tid) * 16;
+      if (o >= TB) continue;
+      const int r = o / KROW, c = (o % KROW) / 16;
+      *reinterpret_cast<u32x4_t*>(&lds_k[slot][r * KROW + ((c ^ (r & 7)) * 16)]) = rg[slot][j];
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto body = [&](int64_t tile, auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
+    stash(BUF);
+    if (tile + 2 < ntiles) load(BUF, tile + 2);
+    __syncthreads();
+    if (qok && tile * TE < Vq) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int el = nt * 16 + l16;
+        const uint8_t* kr = &lds_k[buf][el * KROW];
+        const int sw = el & 7;
+        bf16x8_t kbv[KS];
+        if constexpr (KDT == DT_FP8) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + (((G * 2 + c) ^ sw) * 16));
+            const u32x2_t a0 = fp8x4_to_bf16x4(v[0]), a1 = fp8x4_to_bf16x4(v[1]);
+            const u32x2_t a2 = fp8x4_to_bf16x4(v[2]), a3 = fp8x4_to_bf16x4(v[3]);
+            kbv[2 * c] = as_bf16x8(u32x4_t{a0[0], a0[1], a1[0], a1[1]});
+            kbv[2 * c + 1] = as_bf16x8(u32x4_t{a2[0], a2[1], a3[0], a3[1]});
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+            kbv[s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + (((G * 4 + s) ^ sw) * 16)));
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], kbv[s], acc);
+          const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[wv][mt * 16 + G * 4]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part += wv4[r] * fmaxf(acc[r], 0.0f);
+        }
+        part += shfl_xor(part, 16);
+        part += shfl_xor(part, 32);
+        const int64_t e = tile * TE + el;
+        if (G == 0 && e < Vq) {
+          if constexpr (KDT == DT_FP8) part *= k_scale[b * N_max + e];
+          srow[e] = part;
+        }
+      }
+    }
+  };
+  load(I0{}, 0);
+  if (ntiles > 1) load(I1{}, 1);
+  for (int64_t it = 0; it < ntiles; it += 2) {
+    body(it, I0{});
+    if (it + 1 < ntiles) body(it + 1, I1{});
+  }
+}
+
 // fp32 keys and queries, up to 32 heads (tiny shapes): v_mfma_f32_32x32x2f32,
 // heads padded to 32 with zero rows. D_I = 32.
 __global__ void __launch_bounds__(256)
@@ -198,6 +334,19 @@ idx_scan_f32_kernel(const float* __restrict__ q_idx, const float* __restrict__ w
 hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
   const int64_t rows = a.B * a.Tq;
   if (rows == 0 || a.N_max == 0) return hipSuccess;
+  if (a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16 && a.Tq >= 8) {
+    // many queries per sequence: key tiles shared by 8 queries per workgroup
+    dim3 grid((unsigned)((a.Tq + 7) / 8), (unsigned)a.B);
+    if (a.k_dt == DT_FP8)
+      hipLaunchKernelGGL((idx_prefill_kernel<DT_FP8>), grid, dim3(512), 0, st,
+                         reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
+                         a.k_scale, a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
+    else
+      hipLaunchKernelGGL((idx_prefill_kernel<DT_BF16>), grid, dim3(512), 0, st,
+                         reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
+                         a.k_scale, a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
+    return hipGetLastError();
+  }
   if (a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16) {
     const int64_t ntiles = (a.N_max + 63) / 64;
     // a few workgroups per CU in total, each walking a strided run of tiles

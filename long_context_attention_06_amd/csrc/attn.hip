@@ -10,14 +10,10 @@
 // l_r = scale * <q_h, r> for every row r of the multiset plus a sink logit,
 // then the weighted sum of the rows (each row is key and value at once).
 //
-// Design (MI355X-first, heads split across waves):
+// Design (MI355X-first):
 //  * A workgroup owns one query token and a contiguous range of row slots (a
-//    "split"). Wave w owns heads 16w..16w+15 over all D dims, so the online
-//    softmax of a head never leaves its wave and no logits cross waves.
-//  * Rows are processed in tiles of 32, double-buffered in LDS (row-major,
-//    16-byte chunks XOR-swizzled), loaded with coalesced 16-byte loads into
-//    a ring of two register tiles (the HBM latency needs deep prefetch): one barrier per tile. Top-k indices of the
-//    split are staged in LDS first, so no tile waits on an index load.
+//    "split"). Rows are processed in tiles of 32 held row-major in LDS with
+//    their 16-byte chunks XOR-swizzled.
 //  * S^T = R Q^T on v_mfma_f32_16x16x32_bf16 (M = 16 rows, N = 16 heads,
 //    K = 32 dims); Q stays in registers. The accumulator layout gives each
 //    lane 8 rows of one head, which is exactly the P operand of the next
@@ -25,11 +21,15 @@
 //  * O += P R on the same MFMA (M = 16 heads, N = 16 dims, K = 32 rows); its
 //    R operand (4 consecutive rows of one dim per read) comes from the
 //    row-major tile through ds_read_b64_tr_b16, in the same K order.
+//  * Online softmax in the exp2 domain with a lazily moved reference: the O
+//    accumulators are only rescaled when a logit exceeds the reference by
+//    RESCALE_SLACK, which after the first tile is rare.
 //  * Splits write unnormalised (O, m, l) partials (exp2 domain); a combine
 //    kernel merges them in fixed split order and adds the sink. Split sizes
 //    depend only on per-query shape arguments: results are batch invariant.
-//  * The fp32 instantiation (tiny shapes) runs v_mfma_f32_16x16x4f32 with
-//    the same structure; its tile has a padded pitch instead of the swizzle.
+//  * bf16 rows of 512 dims (the model's shape) run attn_bf16_kernel: eight
+//    waves, rows moved HBM -> LDS by DMA. fp32 rows of small dims (the tiny
+//    reference shapes) run attn_f32_kernel on v_mfma_f32_16x16x4f32.
 #include <type_traits>
 
 #include "common.h"
@@ -40,36 +40,18 @@ namespace csa {
 enum { SRC_SPARSE_DEC = 0, SRC_HCA_DEC = 1, SRC_SPARSE_PRE = 2 };
 
 // XOR swizzle of the 16-byte chunk index inside each 256-byte group of a
-// tile row. Sixteen consecutive rows map one chunk to sixteen different
-// chunk slots (b128 reads of a column by 16 rows are conflict-free with 64
-// banks, and with 32 banks for any 8 of them), and the 4 rows x 2 chunks of a
-// transpose read land in 8 different slots.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8); }
+// tile row (rows are 1 KB, so every row starts in bank group 0). A b128 read
+// takes one chunk of 16 consecutive rows; with 64 banks of 4 bytes, row & 15
+// puts those 16 chunks in 16 different 16-byte bank groups (measured on
+// gfx950: full 256 B/clk, against 150 B/clk for a 3-bit rotation). The
+// transpose reads (4 rows x 32 bytes per 16 lanes) run at the rate of that
+// instruction with either choice.
+__device__ __forceinline__ int swz(int row) { return row & 15; }
 
 // Lazy rescaling of the online softmax: the exponent reference of a head
 // only moves when a tile's maximum exceeds it by more than this (log2 units),
 // so P <= 2^8 and the O accumulators are rarely touched.
 constexpr float RESCALE_SLACK = 8.0f;
-
-__device__ __forceinline__ f32x4_t mfma_s(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma_s(float a, float b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-template <typename T>
-struct HsTraits;
-template <>
-struct HsTraits<uint16_t> {  // bf16 storage: 16x16x32, 8 values per lane
-  static constexpr int KSTEP = 32, VPL = 8;
-  typedef bf16x8_t op_t;
-};
-template <>
-struct HsTraits<float> {  // fp32 storage: 16x16x4, 1 value per lane
-  static constexpr int KSTEP = 4, VPL = 1;
-  typedef float op_t;
-};
 
 struct RowSrc {
   const uint8_t* kv_comp;
@@ -119,21 +101,359 @@ __device__ __forceinline__ const uint8_t* slot_row(const RowSrc& s, int64_t qi, 
   }
 }
 
-template <typename T, int D, int NWAV, int SRC>
+// ----------------------------------------------------------------------------
+// bf16 rows of D = 512: eight waves, rows gathered into LDS by DMA
+// ----------------------------------------------------------------------------
+//
+// Wave w owns heads 16*(w%4) .. +15 and the dim half 256*(w/4) .. +255. S^T of
+// a 32-row tile is a sum over both dim halves: each wave of a pair (w, w^4)
+// computes its half, the pair swaps partials through LDS, and both then hold
+// the same S^T (float addition commutes), run the same softmax and each
+// accumulates O for its own 256 dims: O (64 VGPRs) and Q (32) stay in
+// architectural registers, two waves per SIMD.
+//
+// Rows reach LDS by global_load_lds_dwordx4: one instruction moves one 1 KB
+// row (lane i -> 16-byte chunk i), with no register staging. The row list of
+// the workgroup is built once (invalid slots dropped, slot order kept), so a
+// row address is one LDS word plus scalar arithmetic. A ring of four 32 KB
+// tiles keeps three tiles in flight; waits are explicit vmcnt counts (four
+// row loads per wave per tile), and each tile costs two barriers (tile ready,
+// S^T partials swapped).
+
+namespace bfk {
+constexpr int D = 512, ROWB = 1024, TR = 32, NW = 8, NT = 512, NBUF = 4;
+constexpr int TILEB = TR * ROWB;  // 32 KB
+constexpr int TAB_MAX = 2048;     // rows of one workgroup for the table-driven sources
+}  // namespace bfk
+
+// One 1 KB row -> LDS: lane i copies bytes voff..voff+15 of the row to
+// lds_addr + 16 i. M0 carries the LDS address; the row base is wave-uniform.
+__device__ __forceinline__ void dma_row(const uint8_t* row, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(row), "{m0}"(lds_addr) : "memory");
+}
+// Wait until at most N row loads of this wave are in flight and every LDS
+// access of this wave is done, then join the workgroup.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+
+template <int SRC>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __restrict__ win_len,
+                 const int32_t* __restrict__ n_comp, const int32_t* __restrict__ q_pos, int m_rate,
+                 const float* __restrict__ sink, float scale_log2, int H, int slots, int split_rows,
+                 float* __restrict__ part_o, float* __restrict__ part_ml, void* __restrict__ out,
+                 float* __restrict__ lse, int out_dt) {
+  using namespace bfk;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TILEB];
+  __shared__ __attribute__((aligned(16))) f32x4_t xchg[NW][2][64];
+  __shared__ __attribute__((aligned(16))) int tab[SRC == SRC_HCA_DEC ? 4 : TAB_MAX];
+  __shared__ int cnt[NW];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = l >> 4, l16 = l & 15;
+  const int hg = w & 3, dh = w >> 2;
+  const int64_t qi = blockIdx.x;  // query (decode: sequence)
+  const int sp = blockIdx.y;      // split
+  const int nsplit = gridDim.y;
+  const int head = hg * 16 + l16;  // this lane's head in S^T / P / softmax
+
+  int lim0 = 0, lim1 = 0;  // SPARSE_DEC: window length; HCA: V, window length; PRE: position
+  if (SRC == SRC_SPARSE_DEC) {
+    lim0 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
+  } else if (SRC == SRC_HCA_DEC) {
+    if (n_comp) {
+      const int64_t v = min((int64_t)n_comp[qi], ((int64_t)q_pos[qi] + 1) / m_rate);
+      lim0 = (int)max((int64_t)0, min(v, src.N_max));
+    }
+    lim1 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
+  } else {
+    lim1 = q_pos[qi];
+  }
+  const int s_begin = sp * split_rows;
+  const int s_end = min(slots, s_begin + split_rows);
+  const uint8_t* comp_base = src.kv_comp + (SRC == SRC_SPARSE_PRE ? 0 : qi * src.N_max * ROWB);
+  const uint8_t* win_base = src.kv_win + (SRC == SRC_SPARSE_PRE ? 0 : qi * (int64_t)src.W * ROWB);
+
+  // ---- Q^T operand (B of S^T = R Q^T): lane (head, G), dims 256 dh + 32 s + 8 G .. +7
+  bf16x8_t qb[8];
+  {
+    const bool hok = head < H;
+    const uint16_t* qp = q + (qi * H + (hok ? head : 0)) * (int64_t)D + dh * 256 + G * 8;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(hok ? ld16(qp + s * 32) : u32x4_t{0, 0, 0, 0});
+  }
+
+  // ---- the rows of this split, invalid slots dropped, slot order kept
+  int n_rows = 0, len1 = 0, w0 = 0;
+  if (SRC == SRC_HCA_DEC) {
+    // slots [0, N_max) are compressed entries (valid below V), then the window
+    len1 = max(0, min(s_end, lim0) - s_begin);
+    const int a2 = max(s_begin, (int)src.N_max), b2 = min(s_end, (int)src.N_max + lim1);
+    w0 = a2 - (int)src.N_max;
+    n_rows = len1 + max(0, b2 - a2);
+  } else {
+    for (int c0 = s_begin; c0 < s_end; c0 += NT) {
+      const int j = c0 + tid;
+      int e = 0;
+      bool ok = false;
+      if (j < s_end) {
+        if (j < src.top_k) {
+          const int id = src.idx[qi * src.top_k + j];
+          ok = id >= 0 && id < src.N_max;
+          e = id;
+        } else {
+          const int ww = j - src.top_k;
+          int row = ww;
+          if (SRC == SRC_SPARSE_DEC) {
+            ok = ww < lim0;
+          } else {
+            const int64_t tok = (int64_t)lim1 - src.W + 1 + ww;
+            ok = tok >= 0 && tok < src.T_tok;
+            row = (int)tok;
+          }
+          e = (int)(0x80000000u | (uint32_t)row);
+        }
+      }
+      const uint64_t bal = __ballot(ok);
+      const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (l == 0) cnt[w] = __popcll(bal);
+      __syncthreads();
+      int off = n_rows, tot = 0;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const int c = cnt[v];
+        off += v < w ? c : 0;
+        tot += c;
+      }
+      if (ok) tab[off + rank] = e;
+      n_rows += tot;
+      __syncthreads();
+    }
+    // pad to a whole tile with a valid row (those rows are masked), so a wave
+    // reads the entries of its four rows with one 16-byte LDS read
+    const int padded = (n_rows + TR - 1) / TR * TR;
+    if (n_rows > 0 && n_rows + tid < padded) tab[n_rows + tid] = tab[0];
+    __syncthreads();
+  }
+  const int ntiles = (n_rows + TR - 1) / TR;
+
+  // ---- row loads: wave w moves rows 4w .. 4w+3 of a tile; the lane offset
+  // applies the tile's chunk swizzle on the global side
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((l ^ swz(4 * w + i)) * 16);
+  auto issue = [&](int t) {
+    const int c0 = t * TR + 4 * w;  // first of this wave's four rows
+    const uint32_t dst = ring_lds + (uint32_t)((t & (NBUF - 1)) * TILEB + 4 * w * ROWB);
+    if (SRC == SRC_HCA_DEC) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int c = c0 + i;
+        if (c >= n_rows) c = t * TR;  // rows past the end repeat a valid row; they are masked
+        const uint8_t* p =
+            c < len1 ? comp_base + (int64_t)(s_begin + c) * ROWB : win_base + (int64_t)(w0 + c - len1) * ROWB;
+        dma_row(uniform_ptr(p), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+      }
+    } else {
+      const u32x4_t e4 = *reinterpret_cast<const u32x4_t*>(&tab[c0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = (int)__builtin_amdgcn_readfirstlane(e4[i]);
+        const uint8_t* p = e >= 0 ? comp_base + (int64_t)e * ROWB : win_base + (int64_t)(e & 0x7fffffff) * ROWB;
+        dma_row(uniform_ptr(p), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+      }
+    }
+  };
+
+  f32x4_t o[16];
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt) o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_run = 0.0f;  // `head`: exponent reference, partial sum of this lane's rows
+
+  // LDS offsets (within a tile, plus 512 dh) of this lane's QK and PV reads
+  int qofs[2][4], pofs[2][8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int row = mt * 16 + l16;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) qofs[mt][v] = row * ROWB + (((4 * v + G) ^ swz(row)) * 16) + dh * 512;
+  }
+  {
+    const int rowa = G * 4 + (l16 >> 2), rowb = rowa + 16;
+    const int c0 = (l16 >> 1) & 1, cb = (l16 & 1) * 8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      pofs[0][u] = rowa * ROWB + (((2 * u + c0) ^ swz(rowa)) * 16) + cb + dh * 512;
+      pofs[1][u] = rowb * ROWB + (((2 * u + c0) ^ swz(rowb)) * 16) + cb + dh * 512;
+    }
+  }
+
+  // consume Q here: the compiler's wait for its loads lands before the first
+  // row load, so its load tracking never waits on rows in flight in the loop
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(qb[s]));
+  for (int t = 0; t < ntiles && t < NBUF - 1; ++t) issue(t);
+  for (int t = 0; t < ntiles; ++t) {
+    const int ahead = min(NBUF - 2, ntiles - 1 - t);  // tiles issued after this one
+    if (ahead >= 2)
+      vm_barrier<8>();
+    else if (ahead == 1)
+      vm_barrier<4>();
+    else
+      vm_barrier<0>();
+    // the buffer of tile t-1 is free: every wave has passed this barrier
+    if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);
+    const uint8_t* R = ring + (t & (NBUF - 1)) * TILEB;
+
+    // ---- partial S^T over this wave's 256 dims, two 16-row M-tiles
+    f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(R + qofs[0][s & 3] + (s >> 2) * 256));
+      const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(R + qofs[1][s & 3] + (s >> 2) * 256));
+      sa = mfma16(a0, qb[s], sa);
+      sb = mfma16(a1, qb[s], sb);
+    }
+    // ---- swap partials with the other dim half
+    xchg[w][0][l] = sa;
+    xchg[w][1][l] = sb;
+    vm_barrier<63>();
+    sa += xchg[w ^ 4][0][l];
+    sb += xchg[w ^ 4][1][l];
+
+    // ---- softmax of `head` over this lane's 8 rows (mt*16 + 4G + r), exp2 domain
+    const int nvalid = n_rows - t * TR;
+    float sv[8];
+    float lm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float va = (4 * G + r < nvalid) ? sa[r] * scale_log2 : -INFINITY;
+      const float vb = (16 + 4 * G + r < nvalid) ? sb[r] * scale_log2 : -INFINITY;
+      sv[r] = va;
+      sv[4 + r] = vb;
+      lm = fmaxf(lm, fmaxf(va, vb));
+    }
+    // m_ref only moves when a row exceeds it by RESCALE_SLACK (always on the first tile)
+    if (__builtin_expect(__any(lm > m_ref + RESCALE_SLACK), 0)) {
+      float tmax = fmaxf(lm, shfl_xor(lm, 16));
+      tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+      const float m_new = tmax > m_ref + RESCALE_SLACK ? tmax : m_ref;
+      const float alpha = (m_new == m_ref) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
+      m_ref = m_new;
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, G * 4 + r, 64);  // O rows are heads 16 hg + 4G + r
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[nt][r] *= ar[r];
+    }
+    const float mr = (m_ref == -INFINITY) ? 0.0f : m_ref;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(sv[i] - mr);
+      l_run += pv[i];
+    }
+
+    // ---- O += P R over this wave's dims; K order: rows 4G + 0..3, then 16 + 4G + 0..3
+    const bf16x8_t pa = as_bf16x8(u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                           pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt) {
+      auto* pa4 = (s16x4_t __attribute__((address_space(3)))*)(R + pofs[0][nt & 7] + (nt >> 3) * 256);
+      auto* pb4 = (s16x4_t __attribute__((address_space(3)))*)(R + pofs[1][nt & 7] + (nt >> 3) * 256);
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa4);
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pb4);
+      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[nt] = mfma16(pa, bv, o[nt]);
+    }
+  }
+
+  // ---- epilogue: O rows are heads 16 hg + 4G + r; their (m, l) live in lanes 4G + r
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  float mrr[4], lrr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mrr[r] = __shfl(m_ref, G * 4 + r, 64);
+    lrr[r] = __shfl(l_run, G * 4 + r, 64);
+  }
+  const int dbase = dh * 256 + l16;
+  if (part_o != nullptr) {
+    const int64_t pbase = (qi * nsplit + sp) * (int64_t)H;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = hg * 16 + G * 4 + r;
+      if (h >= H) continue;
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt) part_o[(pbase + h) * D + dbase + nt * 16] = o[nt][r];
+    }
+    if (dh == 0 && G == 0 && head < H) {
+      part_ml[(pbase + head) * 2 + 0] = m_ref;
+      part_ml[(pbase + head) * 2 + 1] = l_run;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = hg * 16 + G * 4 + r;
+      if (h >= H) continue;
+      const float s2 = sink ? sink[h] * LOG2E_F : -INFINITY;
+      const float M = fmaxf(mrr[r], s2);
+      float fac = 0.0f;
+      if (M != -INFINITY) {
+        const float a = exp2f(mrr[r] - M);
+        fac = a / (lrr[r] * a + exp2f(s2 - M));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt) {
+        const int64_t oo = (qi * H + h) * (int64_t)D + dbase + nt * 16;
+        const float v = o[nt][r] * fac;
+        if (out_dt == DT_BF16)
+          reinterpret_cast<uint16_t*>(out)[oo] = (uint16_t)f32_to_bf16(v);
+        else
+          reinterpret_cast<float*>(out)[oo] = v;
+      }
+    }
+    if (lse && dh == 0 && G == 0 && head < H) {
+      const float s2 = sink ? sink[head] * LOG2E_F : -INFINITY;
+      const float M = fmaxf(m_ref, s2);
+      float v = -INFINITY;
+      if (M != -INFINITY) v = (M + log2f(l_run * exp2f(m_ref - M) + exp2f(s2 - M))) * LN2_F;
+      lse[qi * H + head] = v;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// fp32 rows (small head dims): four-wave heads split, register-staged tiles
+// ----------------------------------------------------------------------------
+
+template <int D, int NWAV, int SRC>
 __global__ void __launch_bounds__(64 * NWAV) __attribute__((amdgpu_waves_per_eu(1, 1)))
-attn_kernel(const T* __restrict__ q, RowSrc src, const int32_t* __restrict__ win_len,
+attn_f32_kernel(const float* __restrict__ q, RowSrc src, const int32_t* __restrict__ win_len,
             const int32_t* __restrict__ n_comp, const int32_t* __restrict__ q_pos, int m_rate,
             const float* __restrict__ sink, float scale_log2, int H, int slots, int split_rows,
             float* __restrict__ part_o, float* __restrict__ part_ml, void* __restrict__ out,
             float* __restrict__ lse, int out_dt) {
-  typedef typename HsTraits<T>::op_t op_t;
-  constexpr bool BF = sizeof(T) == 2;
-  constexpr int KSTEP = HsTraits<T>::KSTEP, VPL = HsTraits<T>::VPL;
-  constexpr int ES = sizeof(T);
+  constexpr int KSTEP = 4;
+  constexpr int ES = 4;
   constexpr int NT = 64 * NWAV;
   constexpr int TR = 32;                         // rows per tile
   constexpr int ROWB = D * ES;                   // bytes per row
-  constexpr int RPITCH = BF ? ROWB : ROWB + 4;   // LDS row pitch (bytes)
+  constexpr int RPITCH = ROWB + 4;               // LDS row pitch (bytes), padded
   constexpr int CPR = ROWB / 16;                 // 16-byte chunks per row
   constexpr int RPP = NT / CPR;                  // rows per load pass
   constexpr int PASSES = TR / RPP;
@@ -172,18 +492,12 @@ attn_kernel(const T* __restrict__ q, RowSrc src, const int32_t* __restrict__ win
   const int ntiles = (s_end > s_begin) ? (s_end - s_begin + TR - 1) / TR : 0;
 
   // ---- Q^T operand (B of S^T = R Q^T): lane (head, G), dims s*KSTEP + G*VPL + 0..VPL-1
-  op_t qb[KSQ];
+  float qb[KSQ];
   {
     const bool hok = head < H;
-    if constexpr (BF) {
-      const uint16_t* qp = reinterpret_cast<const uint16_t*>(q) + (qi * H + (hok ? head : 0)) * (int64_t)D + G * 8;
+    const float* qp = q + (qi * H + (hok ? head : 0)) * (int64_t)D + G;
 #pragma unroll
-      for (int s = 0; s < KSQ; ++s) qb[s] = as_bf16x8(hok ? ld16(qp + s * 32) : u32x4_t{0, 0, 0, 0});
-    } else {
-      const float* qp = reinterpret_cast<const float*>(q) + (qi * H + (hok ? head : 0)) * (int64_t)D + G;
-#pragma unroll
-      for (int s = 0; s < KSQ; ++s) qb[s] = hok ? qp[s * 4] : 0.0f;
-    }
+    for (int s = 0; s < KSQ; ++s) qb[s] = hok ? qp[s * 4] : 0.0f;
   }
 
   // ---- top-k indices of this split, staged once in LDS (sparse row sources)
@@ -218,13 +532,9 @@ attn_kernel(const T* __restrict__ q, RowSrc src, const int32_t* __restrict__ win
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       const int r = lrs + ps * RPP;
-      if constexpr (BF) {
-        *reinterpret_cast<u32x4_t*>(&lds_r[buf][r * RPITCH + ((lc ^ swz(r)) * 16)]) = pre[slot][ps];
-      } else {
-        float* dst = reinterpret_cast<float*>(&lds_r[buf][r * RPITCH]) + lc * 4;
+      float* dst = reinterpret_cast<float*>(&lds_r[buf][r * RPITCH]) + lc * 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(pre[slot][ps][e]);
-      }
+      for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(pre[slot][ps][e]);
       if (lc == 0) lds_valid[buf][r] = (prevm[slot] >> ps) & 1;
     }
     return prevm[slot] != 0;
@@ -262,20 +572,10 @@ attn_kernel(const T* __restrict__ q, RowSrc src, const int32_t* __restrict__ win
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int row = mt * 16 + l16;
-        // dims s*32 + G*8 .. +8 live in chunk 4s + G = 16*(s/4) + (4*(s%4) + G)
-        int qofs[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) qofs[v] = row * RPITCH + (((4 * v + G) ^ swz(row)) * 16);
 #pragma unroll
         for (int s = 0; s < KSQ; ++s) {
-          op_t a;
-          if constexpr (BF) {
-            a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(R + qofs[s & 3] + (s >> 2) * 256));
-          } else {
-            a = reinterpret_cast<const float*>(R + row * RPITCH)[s * 4 + G];
-          }
-          sacc[mt] = mfma_s(a, qb[s], sacc[mt]);
-          if ((s & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bound live operands
+          const float a = reinterpret_cast<const float*>(R + row * RPITCH)[s * 4 + G];
+          sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qb[s], sacc[mt], 0, 0, 0);
         }
       }
       // ---- online softmax of `head` over this tile's 32 rows (exp2 domain)
@@ -323,39 +623,14 @@ attn_kernel(const T* __restrict__ q, RowSrc src, const int32_t* __restrict__ win
 #pragma unroll
           for (int r = 0; r < 4; ++r) oacc[nt][r] *= ar[r];
       }
-      // ---- O += P R, K in the order (rows G*4 + 0..3 of M-tile 0, then of M-tile 1)
-      if constexpr (BF) {
-        const bf16x8_t pa = as_bf16x8(u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                               pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
-        // transpose-read source of this lane: rows rowa / rowa+16, dims nt*16 + 4*(l16%4) .. +3,
-        // i.e. chunk 2nt + c0 (c0 = bit 1 of l16), byte cb inside it; chunk 2nt + c0 = 16*(nt/8) + (2*(nt%8) + c0)
-        const int rowa = G * 4 + (l16 >> 2), rowb = rowa + 16;
-        const int c0 = (l16 >> 1) & 1, cb = (l16 & 1) * 8;
-        const int swa = swz(rowa), swb = swz(rowb);
-        int oa[8], ob[8];
+      // ---- O += P R; K = 4 rows per step: lane G holds row (j/4)*16 + G*4 + j%4
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          oa[u] = rowa * RPITCH + (((2 * u + c0) ^ swa) * 16) + cb;
-          ob[u] = rowb * RPITCH + (((2 * u + c0) ^ swb) * 16) + cb;
-        }
+      for (int j = 0; j < 8; ++j) {
+        const int row = (j >> 2) * 16 + G * 4 + (j & 3);
+        const float* rr = reinterpret_cast<const float*>(R + row * RPITCH);
 #pragma unroll
-        for (int nt = 0; nt < NTD; ++nt) {
-          auto* pa4 = (s16x4_t __attribute__((address_space(3)))*)(R + oa[nt & 7] + (nt >> 3) * 256);
-          auto* pb4 = (s16x4_t __attribute__((address_space(3)))*)(R + ob[nt & 7] + (nt >> 3) * 256);
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa4);
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pb4);
-          const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[nt] = mfma_s(pa, bv, oacc[nt]);
-          if ((nt & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bound live operands
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {  // K = 4 rows per step: lane G holds row (j/4)*16 + G*4 + j%4
-          const int row = (j >> 2) * 16 + G * 4 + (j & 3);
-          const float* rr = reinterpret_cast<const float*>(R + row * RPITCH);
-#pragma unroll
-          for (int nt = 0; nt < NTD; ++nt) oacc[nt] = mfma_s(pv[j], rr[nt * 16 + l16], oacc[nt]);
-        }
+        for (int nt = 0; nt < NTD; ++nt)
+          oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[j], rr[nt * 16 + l16], oacc[nt], 0, 0, 0);
       }
     }
     if (tile + 1 < ntiles) any_next = __syncthreads_or(any_next);
@@ -485,8 +760,7 @@ attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ 
 // host-side launchers
 // ----------------------------------------------------------------------------
 
-template <typename T, int D, int NWAV, int SRC>
-static hipError_t launch_attn(const AttnLaunch& a, hipStream_t st) {
+static RowSrc row_src(const AttnLaunch& a) {
   RowSrc src;
   src.kv_comp = reinterpret_cast<const uint8_t*>(a.kv_comp);
   src.kv_win = reinterpret_cast<const uint8_t*>(a.kv_win);
@@ -495,21 +769,43 @@ static hipError_t launch_attn(const AttnLaunch& a, hipStream_t st) {
   src.T_tok = a.T_tok;
   src.top_k = a.top_k;
   src.W = a.W;
-  dim3 grid((unsigned)a.nq, a.nsplit);
-  hipLaunchKernelGGL((attn_kernel<T, D, NWAV, SRC>), grid, dim3(64 * NWAV), 0, st, reinterpret_cast<const T*>(a.q),
-                     src, a.win_len, a.n_comp, a.q_pos, a.m_rate, a.sink, a.scale * LOG2E_F, a.H, a.slots,
-                     a.split_rows, a.nsplit > 1 ? a.part_o : nullptr, a.part_ml, a.out, a.lse, a.out_dt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
+  return src;
+}
+
+static hipError_t launch_combine(const AttnLaunch& a, hipStream_t st) {
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)a.nq, (unsigned)((a.H + 3) / 4)), dim3(256), 0, st,
-                     a.part_o, a.part_ml, a.sink, a.H, D, a.nsplit, a.out, a.lse, a.out_dt);
+                     a.part_o, a.part_ml, a.sink, a.H, a.D, a.nsplit, a.out, a.lse, a.out_dt);
   return hipGetLastError();
 }
 
 template <int SRC>
+static hipError_t launch_bf16(const AttnLaunch& a, hipStream_t st) {
+  if (SRC != SRC_HCA_DEC && a.split_rows > bfk::TAB_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)a.nq, a.nsplit);
+  hipLaunchKernelGGL((attn_bf16_kernel<SRC>), grid, dim3(bfk::NT), 0, st, reinterpret_cast<const uint16_t*>(a.q),
+                     row_src(a), a.win_len, a.n_comp, a.q_pos, a.m_rate, a.sink, a.scale * LOG2E_F, a.H, a.slots,
+                     a.split_rows, a.nsplit > 1 ? a.part_o : nullptr, a.part_ml, a.out, a.lse, a.out_dt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  return launch_combine(a, st);
+}
+
+template <int D, int NWAV, int SRC>
+static hipError_t launch_f32(const AttnLaunch& a, hipStream_t st) {
+  dim3 grid((unsigned)a.nq, a.nsplit);
+  hipLaunchKernelGGL((attn_f32_kernel<D, NWAV, SRC>), grid, dim3(64 * NWAV), 0, st,
+                     reinterpret_cast<const float*>(a.q), row_src(a), a.win_len, a.n_comp, a.q_pos, a.m_rate, a.sink,
+                     a.scale * LOG2E_F, a.H, a.slots, a.split_rows, a.nsplit > 1 ? a.part_o : nullptr, a.part_ml,
+                     a.out, a.lse, a.out_dt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  return launch_combine(a, st);
+}
+
+template <int SRC>
 static hipError_t dispatch_src(const AttnLaunch& a, hipStream_t st) {
-  if (a.kv_dt == DT_BF16 && a.D == 512 && a.H > 48 && a.H <= 64) return launch_attn<uint16_t, 512, 4, SRC>(a, st);
-  if (a.kv_dt == DT_F32 && a.D == 64 && a.H <= 16) return launch_attn<float, 64, 1, SRC>(a, st);
+  if (a.kv_dt == DT_BF16 && a.D == 512 && a.H > 48 && a.H <= 64) return launch_bf16<SRC>(a, st);
+  if (a.kv_dt == DT_F32 && a.D == 64 && a.H <= 16) return launch_f32<64, 1, SRC>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -25,12 +25,22 @@
 
 namespace csa {
 
+// XOR swizzle of the 16-byte chunk index of key row r in an LDS tile. The
+// operand reads take one chunk of each of 16 consecutive rows; with 64 banks
+// of 4 bytes those 16 chunks must fall in 16 different 16-byte bank groups.
+// bf16 rows are 256 bytes (every row starts in group 0): chunk ^ (r & 15).
+// fp8 rows are 128 bytes (odd rows start in group 8): chunk ^ ((r >> 1) & 7).
+template <int KDT>
+__device__ __forceinline__ int kswz(int r) {
+  return KDT == DT_FP8 ? ((r >> 1) & 7) : (r & 15);
+}
+
 // bf16 / fp8 keys, 64 heads x 128 dims.  Grid: (workgroups per row, rows).
 // A workgroup (4 waves) walks tiles of 64 entries of one query row with a
 // stride of gridDim.x tiles. Each tile is read with fully coalesced 16-byte
 // loads (the workgroup covers contiguous 4 KiB per instruction), staged in a
 // double-buffered LDS tile with an XOR swizzle of the 16-byte chunk index
-// (chunk ^ (row & 7)), and read back in the operand layout of
+// (kswz), and read back in the operand layout of
 // v_mfma_f32_16x16x32_bf16 with conflict-free ds_read_b128: wave w owns
 // entries 16w..16w+15 of the tile (N = 16), heads are four 16-row M tiles.
 // Two tiles per workgroup are in flight while one is computed.
@@ -91,7 +101,7 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
     for (int j = 0; j < LPT; ++j) {
       const int o = (j * 256 + tid) * 16;
       const int r = o / KROW, c = (o % KROW) / 16;
-      *reinterpret_cast<u32x4_t*>(&lds_k[slot][r * KROW + ((c ^ (r & 7)) * 16)]) = rg[slot][j];
+      *reinterpret_cast<u32x4_t*>(&lds_k[slot][r * KROW + ((c ^ kswz<KDT>(r)) * 16)]) = rg[slot][j];
     }
   };
 
@@ -107,7 +117,7 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
     const int el = wv * 16 + l16;  // entry inside the tile
     const int64_t e = tile * TE + el;
     const uint8_t* kr = &lds_k[buf][el * KROW];
-    const int sw = el & 7;
+    const int sw = kswz<KDT>(el);
     bf16x8_t kbv[KS];
     if constexpr (KDT == DT_FP8) {
       // dims G*32 + s*8 .. : bytes G*32 + s*8, i.e. chunk G*2 + s/2, half s%2
@@ -228,7 +238,7 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
       const int o = (j * NT + tid) * 16;
       if (o >= TB) continue;
       const int r = o / KROW, c = (o % KROW) / 16;
-      *reinterpret_cast<u32x4_t*>(&lds_k[slot][r * KROW + ((c ^ (r & 7)) * 16)]) = rg[slot][j];
+      *reinterpret_cast<u32x4_t*>(&lds_k[slot][r * KROW + ((c ^ kswz<KDT>(r)) * 16)]) = rg[slot][j];
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -243,7 +253,7 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
       for (int nt = 0; nt < 4; ++nt) {
         const int el = nt * 16 + l16;
         const uint8_t* kr = &lds_k[buf][el * KROW];
-        const int sw = el & 7;
+        const int sw = kswz<KDT>(el);
         bf16x8_t kbv[KS];
         if constexpr (KDT == DT_FP8) {
 #pragma unroll

@@ -158,8 +158,8 @@ size_t indexer_score_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, 
  *   out_h = sum_r e^{l_r - M} r / Z_h,   lse_h = M + ln Z_h.
  * sink may be NULL (no sink: sink_h = -inf). With R empty and no sink,
  * out_h = 0 and lse_h = -inf. Rows present in two sources count twice.
- * Supported: (H, D) in {(64, 512) with kv_dt BF16, (4, 64) with kv_dt F32};
- * out_dt in {F32, BF16}; q has the dtype kv_dt.
+ * Supported: D = 512 with kv_dt BF16 and 49 <= H <= 64, or D = 64 with
+ * kv_dt F32 and 1 <= H <= 16; out_dt in {F32, BF16}; q has the dtype kv_dt.
  */
 
 /* sparse_mqa_decode — one query per sequence (position: the last token).
@@ -182,7 +182,8 @@ size_t sparse_mqa_decode_workspace_bytes(int64_t B, int H, int D, int top_k, int
  *   kv_tok : [T_tok, D] raw per-token KV; query t at position p = q_pos[t]
  *            uses window rows kv_tok[max(0, p-W+1) .. p] ([LIDUOS]: the latest
  *            W raw tokens, the current one included)
- *   out    : [Tq, H, D]          lse : [Tq, H] (nullable) */
+ *   out    : [Tq, H, D]          lse : [Tq, H] (nullable)
+ * Supported: top_k <= 1024 and top_k + W <= 2048. Needs no workspace. */
 int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_idx,
                        const void* kv_tok, const int32_t* q_pos, const float* sink, float scale,
                        int64_t Tq, int H, int D, int64_t N, int64_t T_tok, int top_k, int W,

@@ -11,8 +11,8 @@
 // Algorithm. A 1024-thread workgroup owns one chunk of up to 32768 keys of a
 // row, cached in LDS as order-preserving uint32 keys. A three-digit radix
 // select (11 + 11 + 10 bits) with integer LDS histograms finds the exact
-// chunk-local K-th key T; each digit is chosen by a block-wide scan of bin
-// counts from the top. The chunk is then compacted in index order (per-wave
+// chunk-local K-th key T; each digit is chosen by one wave that holds the
+// bin counts in registers and scans them from the top. The chunk is then compacted in index order (per-wave
 // counts, a scan over waves, ballot prefix sums): all keys > T and the
 // lowest-index ties == T. A row that fits one chunk is finished in one launch.
 // A longer row writes each chunk's top K (key, index) pairs, in index order;
@@ -47,19 +47,6 @@ __device__ __forceinline__ int wave_incl_scan(int v, int l) {
     if (l >= o) v += t;
   }
   return v;
-}
-
-// Block-wide exclusive scan (thread order) of one int per thread.
-__device__ __forceinline__ int block_excl_scan(int v, int* red) {
-  const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int inc = wave_incl_scan(v, l);
-  if (l == 63) red[wv] = inc;
-  __syncthreads();
-  int off = 0;
-#pragma unroll
-  for (int u = 0; u < TK_NW; ++u) off += (u < wv) ? red[u] : 0;
-  __syncthreads();
-  return off + inc - v;
 }
 
 // Given counts of nb bins, find the bin b with (count above b) < need <=
@@ -97,28 +84,6 @@ __device__ __forceinline__ void find_bin_wave(const uint32_t* hist, int nb, int 
       }
       out[0] = bin;
       out[1] = cab;
-    }
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int need, int* red, int* out) {
-  const int bpt = nb / TK_NT;  // 1 or 2
-  const int t = threadIdx.x;
-  const int hi = nb - t * bpt;  // thread t owns bins [hi - bpt, hi), scanned high to low
-  int loc = 0;
-  for (int u = 1; u <= bpt; ++u) loc += (int)hist[hi - u];
-  const int above = block_excl_scan(loc, red);
-  if (above < need && need <= above + loc) {
-    int c = above;
-    for (int u = 1; u <= bpt; ++u) {
-      const int cnt = (int)hist[hi - u];
-      if (need <= c + cnt) {
-        out[0] = hi - u;
-        out[1] = c;
-        break;
-      }
-      c += cnt;
     }
   }
   __syncthreads();

@@ -106,3 +106,6 @@ def test_attention_validation():
     p = L.lib.sparse_mqa_prefill
     assert p(P, P, P, P, None, P, 1.0, 4, 64, 512, 100, 400, 16, 8, 1, 1, P, None, None, 0, None) == L.INVALID_ARG
     assert p(P, P, P, P, P, P, 1.0, 4, 64, 512, 100, 400, 16, 8, 1, 2, P, None, None, 0, None) == L.UNSUPPORTED
+    # rows per query beyond the kernel's row table
+    assert p(P, P, P, P, P, P, 1.0, 4, 64, 512, 100, 4000, 1024, 1025, 1, 1, P, None, None, 0, None) == L.UNSUPPORTED
+    assert "top_k + W" in _err()

@@ -227,7 +227,7 @@ def main():
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
                          "m": m, "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I,
                          "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype}
-        res["roofline"] = {"bound": "hbm", "kernel": "idx_scan_bf16_kernel", "achieved": round(scan_bytes / (scan_avg * 1e-3) / 1e9, 1),
+        res["roofline"] = {"bound": "hbm", "kernel": "idx_scan_fp8_kernel" if cfg.k_dtype == "fp8" else "idx_scan_bf16_kernel", "achieved": round(scan_bytes / (scan_avg * 1e-3) / 1e9, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(scan_bytes / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "traffic": _traffic("idx_scan_c2_traffic.txt" if a.workload == "c2" else "idx_scan_c5_traffic.txt",

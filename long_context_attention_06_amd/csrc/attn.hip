@@ -126,22 +126,112 @@ constexpr int TILEB = TR * ROWB;  // 32 KB
 constexpr int TAB_MAX = 2048;     // rows of one workgroup for the table-driven sources
 }  // namespace bfk
 
-// One 1 KB row -> LDS: lane i copies bytes voff..voff+15 of the row to
-// lds_addr + 16 i. M0 carries the LDS address; the row base is wave-uniform.
-__device__ __forceinline__ void dma_row(const uint8_t* row, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(row), "{m0}"(lds_addr) : "memory");
+
+// What a workgroup knows about its query and split: the per-query limits of
+// the row sources, where the compressed and window rows live, and the split's
+// compacted row list (HCA: two contiguous ranges; sparse: a table in LDS).
+struct QRows {
+  int lim0, lim1;  // SPARSE_DEC: window length; HCA: V, window length; PRE: -, position
+  int s_begin, s_end;
+  const uint8_t* comp_base;
+  const uint8_t* win_base;
+  int n_rows;    // rows after dropping invalid slots
+  int len1, w0;  // HCA: rows taken from the compressed range; first window row
+};
+
+template <int SRC>
+__device__ __forceinline__ QRows query_rows(const RowSrc& src, const int32_t* __restrict__ win_len,
+                                            const int32_t* __restrict__ n_comp, const int32_t* __restrict__ q_pos,
+                                            int m_rate, int64_t qi, int sp, int slots, int split_rows) {
+  constexpr int ROWB = 1024;
+  QRows r;
+  r.lim0 = 0;
+  r.lim1 = 0;
+  if (SRC == SRC_SPARSE_DEC) {
+    r.lim0 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
+  } else if (SRC == SRC_HCA_DEC) {
+    if (n_comp) {
+      const int64_t v = min((int64_t)n_comp[qi], ((int64_t)q_pos[qi] + 1) / m_rate);
+      r.lim0 = (int)max((int64_t)0, min(v, src.N_max));
+    }
+    r.lim1 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
+  } else {
+    r.lim1 = q_pos[qi];
+  }
+  r.s_begin = sp * split_rows;
+  r.s_end = min(slots, r.s_begin + split_rows);
+  r.comp_base = src.kv_comp + (SRC == SRC_SPARSE_PRE ? 0 : qi * src.N_max * ROWB);
+  r.win_base = src.kv_win + (SRC == SRC_SPARSE_PRE ? 0 : qi * (int64_t)src.W * ROWB);
+  r.n_rows = r.len1 = r.w0 = 0;
+  if (SRC == SRC_HCA_DEC) {
+    // slots [0, N_max) are compressed entries (valid below V), then the window
+    r.len1 = max(0, min(r.s_end, r.lim0) - r.s_begin);
+    const int a2 = max(r.s_begin, (int)src.N_max), b2 = min(r.s_end, (int)src.N_max + r.lim1);
+    r.w0 = a2 - (int)src.N_max;
+    r.n_rows = r.len1 + max(0, b2 - a2);
+  }
+  return r;
 }
-// Wait until at most N row loads of this wave are in flight and every LDS
-// access of this wave is done, then join the workgroup.
-template <int N>
-__device__ __forceinline__ void vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+
+// Row table of a sparse split (all NT threads call it): entry = compressed row
+// id, or 0x80000000 | window row; invalid slots dropped, slot order kept, the
+// tail padded to a whole tile of TR with a valid row (those rows are masked).
+// Returns the row count.
+template <int SRC, int NT, int TR>
+__device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, int* tab, int* cnt) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int n_rows = 0;
+  for (int c0 = r.s_begin; c0 < r.s_end; c0 += NT) {
+    const int j = c0 + tid;
+    int e = 0;
+    bool ok = false;
+    if (j < r.s_end) {
+      if (j < src.top_k) {
+        const int id = src.idx[qi * src.top_k + j];
+        ok = id >= 0 && id < src.N_max;
+        e = id;
+      } else {
+        const int ww = j - src.top_k;
+        int row = ww;
+        if (SRC == SRC_SPARSE_DEC) {
+          ok = ww < r.lim0;
+        } else {
+          const int64_t tok = (int64_t)r.lim1 - src.W + 1 + ww;
+          ok = tok >= 0 && tok < src.T_tok;
+          row = (int)tok;
+        }
+        e = (int)(0x80000000u | (uint32_t)row);
+      }
+    }
+    const uint64_t bal = __ballot(ok);
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+    if (l == 0) cnt[w] = __popcll(bal);
+    __syncthreads();
+    int off = n_rows, tot = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const int c = cnt[v];
+      off += v < w ? c : 0;
+      tot += c;
+    }
+    if (ok) tab[off + rank] = e;
+    n_rows += tot;
+    __syncthreads();
+  }
+  const int padded = (n_rows + TR - 1) / TR * TR;
+  if (n_rows > 0 && n_rows + tid < padded) tab[n_rows + tid] = tab[0];
+  __syncthreads();
+  return n_rows;
 }
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
-  const uint64_t u = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+
+// Address of compacted row c of an HCA split / of a sparse table entry.
+__device__ __forceinline__ const uint8_t* hca_row(const QRows& r, int c) {
+  return c < r.len1 ? r.comp_base + (int64_t)(r.s_begin + c) * 1024 : r.win_base + (int64_t)(r.w0 + c - r.len1) * 1024;
+}
+__device__ __forceinline__ const uint8_t* tab_row(const QRows& r, int e) {
+  return e >= 0 ? r.comp_base + (int64_t)e * 1024 : r.win_base + (int64_t)(e & 0x7fffffff) * 1024;
 }
 
 template <int SRC>
@@ -167,22 +257,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
   const int nsplit = gridDim.y;
   const int head = hg * 16 + l16;  // this lane's head in S^T / P / softmax
 
-  int lim0 = 0, lim1 = 0;  // SPARSE_DEC: window length; HCA: V, window length; PRE: position
-  if (SRC == SRC_SPARSE_DEC) {
-    lim0 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
-  } else if (SRC == SRC_HCA_DEC) {
-    if (n_comp) {
-      const int64_t v = min((int64_t)n_comp[qi], ((int64_t)q_pos[qi] + 1) / m_rate);
-      lim0 = (int)max((int64_t)0, min(v, src.N_max));
-    }
-    lim1 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
-  } else {
-    lim1 = q_pos[qi];
-  }
-  const int s_begin = sp * split_rows;
-  const int s_end = min(slots, s_begin + split_rows);
-  const uint8_t* comp_base = src.kv_comp + (SRC == SRC_SPARSE_PRE ? 0 : qi * src.N_max * ROWB);
-  const uint8_t* win_base = src.kv_win + (SRC == SRC_SPARSE_PRE ? 0 : qi * (int64_t)src.W * ROWB);
+  QRows rr = query_rows<SRC>(src, win_len, n_comp, q_pos, m_rate, qi, sp, slots, split_rows);
 
   // ---- Q^T operand (B of S^T = R Q^T): lane (head, G), dims 256 dh + 32 s + 8 G .. +7
   bf16x8_t qb[8];
@@ -193,58 +268,8 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
     for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(hok ? ld16(qp + s * 32) : u32x4_t{0, 0, 0, 0});
   }
 
-  // ---- the rows of this split, invalid slots dropped, slot order kept
-  int n_rows = 0, len1 = 0, w0 = 0;
-  if (SRC == SRC_HCA_DEC) {
-    // slots [0, N_max) are compressed entries (valid below V), then the window
-    len1 = max(0, min(s_end, lim0) - s_begin);
-    const int a2 = max(s_begin, (int)src.N_max), b2 = min(s_end, (int)src.N_max + lim1);
-    w0 = a2 - (int)src.N_max;
-    n_rows = len1 + max(0, b2 - a2);
-  } else {
-    for (int c0 = s_begin; c0 < s_end; c0 += NT) {
-      const int j = c0 + tid;
-      int e = 0;
-      bool ok = false;
-      if (j < s_end) {
-        if (j < src.top_k) {
-          const int id = src.idx[qi * src.top_k + j];
-          ok = id >= 0 && id < src.N_max;
-          e = id;
-        } else {
-          const int ww = j - src.top_k;
-          int row = ww;
-          if (SRC == SRC_SPARSE_DEC) {
-            ok = ww < lim0;
-          } else {
-            const int64_t tok = (int64_t)lim1 - src.W + 1 + ww;
-            ok = tok >= 0 && tok < src.T_tok;
-            row = (int)tok;
-          }
-          e = (int)(0x80000000u | (uint32_t)row);
-        }
-      }
-      const uint64_t bal = __ballot(ok);
-      const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-      if (l == 0) cnt[w] = __popcll(bal);
-      __syncthreads();
-      int off = n_rows, tot = 0;
-#pragma unroll
-      for (int v = 0; v < NW; ++v) {
-        const int c = cnt[v];
-        off += v < w ? c : 0;
-        tot += c;
-      }
-      if (ok) tab[off + rank] = e;
-      n_rows += tot;
-      __syncthreads();
-    }
-    // pad to a whole tile with a valid row (those rows are masked), so a wave
-    // reads the entries of its four rows with one 16-byte LDS read
-    const int padded = (n_rows + TR - 1) / TR * TR;
-    if (n_rows > 0 && n_rows + tid < padded) tab[n_rows + tid] = tab[0];
-    __syncthreads();
-  }
+  if (SRC != SRC_HCA_DEC) rr.n_rows = build_row_table<SRC, NT, TR>(src, rr, qi, tab, cnt);
+  const int n_rows = rr.n_rows;
   const int ntiles = (n_rows + TR - 1) / TR;
 
   // ---- row loads: wave w moves rows 4w .. 4w+3 of a tile; the lane offset
@@ -261,17 +286,14 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
       for (int i = 0; i < 4; ++i) {
         int c = c0 + i;
         if (c >= n_rows) c = t * TR;  // rows past the end repeat a valid row; they are masked
-        const uint8_t* p =
-            c < len1 ? comp_base + (int64_t)(s_begin + c) * ROWB : win_base + (int64_t)(w0 + c - len1) * ROWB;
-        dma_row(uniform_ptr(p), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+        dma_row(uniform_ptr(hca_row(rr, c)), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
       }
     } else {
       const u32x4_t e4 = *reinterpret_cast<const u32x4_t*>(&tab[c0]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = (int)__builtin_amdgcn_readfirstlane(e4[i]);
-        const uint8_t* p = e >= 0 ? comp_base + (int64_t)e * ROWB : win_base + (int64_t)(e & 0x7fffffff) * ROWB;
-        dma_row(uniform_ptr(p), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+        dma_row(uniform_ptr(tab_row(rr, e)), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
       }
     }
   };

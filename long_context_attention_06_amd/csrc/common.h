@@ -52,6 +52,13 @@ __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t codes) {
   return r;
 }
 
+// 2 OCP E4M3 codes (the low or high 16 bits of a dword) -> 2 bf16 in one
+// instruction (gfx950 scaled convert, scale 1.0), exact.
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t codes, bool high) {
+  return __builtin_bit_cast(uint32_t, high ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false));
+}
+
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -66,7 +73,89 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Cross-lane steps on DPP (data-parallel primitives, GFX9 encoding): a VALU
+// operand modifier, so no LDS round trip as with ds_bpermute-based shuffles.
+// Rows are groups of 16 lanes.
+template <int CTRL, int ROW_MASK = 0xf, bool BOUND_ZERO = false>
+__device__ __forceinline__ int dpp_mov(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, BOUND_ZERO);
+}
+enum : int { DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118,
+             DPP_ROW_ROR1 = 0x121, DPP_ROW_ROR2 = 0x122, DPP_ROW_ROR4 = 0x124, DPP_ROW_ROR8 = 0x128,
+             DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143 };
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele within each row, then
+// the rows' totals carried by row broadcasts.
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += dpp_mov<DPP_ROW_SHR1, 0xf, true>(0, v);
+  v += dpp_mov<DPP_ROW_SHR2, 0xf, true>(0, v);
+  v += dpp_mov<DPP_ROW_SHR4, 0xf, true>(0, v);
+  v += dpp_mov<DPP_ROW_SHR8, 0xf, true>(0, v);
+  v += dpp_mov<DPP_ROW_BCAST15, 0xa>(0, v);
+  v += dpp_mov<DPP_ROW_BCAST31, 0xc>(0, v);
+  return v;
+}
+
+// Wave-wide reductions, result uniform (rotations within rows, then the four
+// rows' values read as scalars).
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+  v += dpp_mov<DPP_ROW_ROR8>(v, v);
+  v += dpp_mov<DPP_ROW_ROR4>(v, v);
+  v += dpp_mov<DPP_ROW_ROR2>(v, v);
+  v += dpp_mov<DPP_ROW_ROR1>(v, v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
+}
+__device__ __forceinline__ uint32_t wave_min_u32_dpp(uint32_t v) {
+  v = min(v, (uint32_t)dpp_mov<DPP_ROW_ROR8>((int)v, (int)v));
+  v = min(v, (uint32_t)dpp_mov<DPP_ROW_ROR4>((int)v, (int)v));
+  v = min(v, (uint32_t)dpp_mov<DPP_ROW_ROR2>((int)v, (int)v));
+  v = min(v, (uint32_t)dpp_mov<DPP_ROW_ROR1>((int)v, (int)v));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  v = max(v, (uint32_t)dpp_mov<DPP_ROW_ROR8>((int)v, (int)v));
+  v = max(v, (uint32_t)dpp_mov<DPP_ROW_ROR4>((int)v, (int)v));
+  v = max(v, (uint32_t)dpp_mov<DPP_ROW_ROR2>((int)v, (int)v));
+  v = max(v, (uint32_t)dpp_mov<DPP_ROW_ROR1>((int)v, (int)v));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---- HBM -> LDS without registers (global_load_lds, issued from inline asm so
+// the compiler's own load tracking never waits on it; the caller waits with
+// explicit vmcnt counts). Vector memory stores also count in vmcnt and may
+// complete out of order with loads: a loop that relies on these counts issues
+// no stores while loads are in flight.
+//
+// 16 bytes per lane: lane i copies bytes base+voff .. +15 to lds_addr + 16 i.
+__device__ __forceinline__ void dma_row(const uint8_t* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
+}
+// 4 bytes per lane: lane i copies bytes base+voff .. +3 to lds_addr + 4 i.
+__device__ __forceinline__ void dma_dword(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
+}
+// Wait until at most N vector memory operations of this wave are in flight
+// and every LDS access of this wave is done, then join the workgroup.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const T*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }

@@ -25,6 +25,10 @@
 
 namespace csa {
 
+#ifndef IDX_BF16_TE
+#define IDX_BF16_TE 64
+#endif
+
 // XOR swizzle of the 16-byte chunk index of key row r in an LDS tile. The
 // operand reads take one chunk of each of 16 consecutive rows; with 64 banks
 // of 4 bytes those 16 chunks must fall in 16 different 16-byte bank groups.
@@ -35,24 +39,26 @@ __device__ __forceinline__ int kswz(int r) {
   return KDT == DT_FP8 ? ((r >> 1) & 7) : (r & 15);
 }
 
-// bf16 / fp8 keys, 64 heads x 128 dims.  Grid: (workgroups per row, rows).
-// A workgroup (4 waves) walks tiles of 64 entries of one query row with a
+// bf16 keys, 64 heads x 128 dims.  Grid: (workgroups per row, rows).
+// A workgroup (4 waves) walks tiles of TE entries of one query row with a
 // stride of gridDim.x tiles. Each tile is read with fully coalesced 16-byte
 // loads (the workgroup covers contiguous 4 KiB per instruction), staged in a
 // double-buffered LDS tile with an XOR swizzle of the 16-byte chunk index
 // (kswz), and read back in the operand layout of
 // v_mfma_f32_16x16x32_bf16 with conflict-free ds_read_b128: wave w owns
-// entries 16w..16w+15 of the tile (N = 16), heads are four 16-row M tiles.
-// Two tiles per workgroup are in flight while one is computed.
-template <int KDT>
+// entries TE/4 w .. TE/4 (w+1) - 1 of the tile as 16-entry N tiles, heads are
+// four 16-row M tiles. Two tiles per workgroup are in flight (a register ring)
+// while one is computed.
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-                     const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
-                     const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
-                     int64_t N_max, int m, float* __restrict__ scores) {
+                     const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
+                     const int32_t* __restrict__ n_comp, int64_t Tq, int64_t N_max, int m,
+                     float* __restrict__ scores) {
+  constexpr int KDT = DT_BF16;
   constexpr int H = 64, DI = 128, KS = 4;               // k-steps of 32
-  constexpr int KROW = (KDT == DT_FP8) ? DI : DI * 2;   // bytes per key row
-  constexpr int TE = 64;                                // entries per tile
+  constexpr int KROW = DI * 2;                          // bytes per key row
+  constexpr int TE = IDX_BF16_TE;                       // entries per tile
+  constexpr int NE = TE / 64;                           // 16-entry N tiles per wave
   constexpr int TB = TE * KROW;                         // tile bytes
   constexpr int LPT = TB / (256 * 16);                  // 16-byte loads per thread per tile
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][TB];
@@ -114,43 +120,35 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
     if (it + 2 < nmine) load(BUF, blockIdx.x + (it + 2) * gridDim.x);
     __syncthreads();
 
-    const int el = wv * 16 + l16;  // entry inside the tile
-    const int64_t e = tile * TE + el;
-    const uint8_t* kr = &lds_k[buf][el * KROW];
-    const int sw = kswz<KDT>(el);
-    bf16x8_t kbv[KS];
-    if constexpr (KDT == DT_FP8) {
-      // dims G*32 + s*8 .. : bytes G*32 + s*8, i.e. chunk G*2 + s/2, half s%2
+    float part[NE];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + (((G * 2 + c) ^ sw) * 16));
-        const u32x2_t a0 = fp8x4_to_bf16x4(v[0]), a1 = fp8x4_to_bf16x4(v[1]);
-        const u32x2_t a2 = fp8x4_to_bf16x4(v[2]), a3 = fp8x4_to_bf16x4(v[3]);
-        kbv[2 * c] = as_bf16x8(u32x4_t{a0[0], a0[1], a1[0], a1[1]});
-        kbv[2 * c + 1] = as_bf16x8(u32x4_t{a2[0], a2[1], a3[0], a3[1]});
-      }
-    } else {
+    for (int n = 0; n < NE; ++n) {
+      const int el = wv * (16 * NE) + n * 16 + l16;  // entry inside the tile
+      const uint8_t* kr = &lds_k[buf][el * KROW];
+      const int sw = kswz<KDT>(el);
+      bf16x8_t kbv[KS];
       // dims G*32 + s*8 .. : chunk G*4 + s
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         kbv[s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + (((G * 4 + s) ^ sw) * 16)));
+      part[n] = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], kbv[s], acc);
+        // accumulator row r of this lane is head mt*16 + G*4 + r
+        const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[mt * 16 + G * 4]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[n] += wv4[r] * fmaxf(acc[r], 0.0f);
+      }
     }
-    float part = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], kbv[s], acc);
-      // accumulator row r of this lane is head mt*16 + G*4 + r
-      const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[mt * 16 + G * 4]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part += wv4[r] * fmaxf(acc[r], 0.0f);
-    }
-    part += shfl_xor(part, 16);
-    part += shfl_xor(part, 32);
-    if (G == 0 && e < V) {
-      if constexpr (KDT == DT_FP8) part *= k_scale[b * N_max + e];
-      srow[e] = part;
+    for (int n = 0; n < NE; ++n) {
+      part[n] += shfl_xor(part[n], 16);
+      part[n] += shfl_xor(part[n], 32);
+      const int64_t e = tile * TE + wv * (16 * NE) + n * 16 + l16;
+      if (G == 0 && e < V) srow[e] = part[n];
     }
   };
   load(I0{}, blockIdx.x);
@@ -159,6 +157,173 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
     body(it, I0{});
     if (it + 1 < nmine) body(it + 1, I1{});
   }
+}
+
+// fp8 (E4M3) keys with a per-entry fp32 scale, 64 heads x 128 dims. Grid:
+// (workgroups per row, rows). A workgroup (4 waves) walks tiles of 128
+// entries (16 KB) of one query row with a stride of gridDim.x tiles. Tiles
+// move HBM -> LDS by DMA (global_load_lds, 1 KB per wave instruction) into a
+// ring of four, so the bytes in flight cover the memory latency without
+// costing registers; the scales travel with their tile (a 4-byte DMA per
+// entry). The 16-byte chunk index is XOR-swizzled (kswz) on the way in, by
+// permuting the lanes' source addresses, and read back in the operand layout
+// of v_mfma_f32_16x16x32_bf16 with conflict-free ds_read_b128: wave w owns
+// entries 32w .. 32w+31 of the tile as two 16-entry N tiles, heads are four
+// 16-row M tiles. Codes become bf16 with v_cvt_scalef32_pk_bf16_fp8 (two per
+// instruction, exact: every E4M3 value is a bf16 value); the scale multiplies
+// the head-weighted sum. Scores collect in LDS and are written out every
+// SC_TILES tiles: no store is in flight while DMA waits are counted.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+idx_scan_fp8_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+                    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
+                    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
+                    int64_t N_max, int m, float* __restrict__ scores) {
+  constexpr int KDT = DT_FP8;
+  constexpr int H = 64, DI = 128, KS = 4;   // k-steps of 32
+  constexpr int KROW = DI;                  // bytes per key row
+  constexpr int TE = 128;                   // entries per tile
+  constexpr int NE = TE / 64;               // 16-entry N tiles per wave
+  constexpr int TB = TE * KROW;             // 16 KB
+  constexpr int NBUF = 4;                   // 64 KB ring
+  constexpr int DPW = TB / 1024 / 4;        // 1 KB DMAs per wave per tile
+  constexpr int PER_TILE = DPW + 1;         // + the scales
+  constexpr int SC_TILES = 16;              // score buffer (tiles)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[NBUF][TB];
+  __shared__ __attribute__((aligned(16))) float lds_s[NBUF][TE];
+  __shared__ __attribute__((aligned(16))) float lds_sc[SC_TILES][TE];
+  __shared__ __attribute__((aligned(16))) float lds_w[H];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = l >> 4, l16 = l & 15;  // k-group (4 x 8 dims) and column of the MFMA operands
+  const int64_t row = blockIdx.y;
+  const int64_t b = row / Tq;
+  int64_t V = min((int64_t)n_comp[b], ((int64_t)q_pos[row] + 1) / m);
+  V = max((int64_t)0, min(V, N_max));
+  const int64_t ntiles = (V + TE - 1) / TE;
+  if ((int64_t)blockIdx.x >= ntiles) return;
+  const int64_t nmine = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // tiles of this workgroup
+
+  // query operand A[m = head][k]: lane (head mt*16 + l16, group G) holds dims
+  // G*32 + s*8 + 0..7 for k-step s (a fixed permutation of the 128 dims,
+  // applied identically to the keys)
+  bf16x8_t qa[4][KS];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const uint16_t* qp = q_idx + (row * H + mt * 16 + l16) * DI + G * 32;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qa[mt][s] = as_bf16x8(ld16(qp + s * 8));
+  }
+  if (tid < H) lds_w[tid] = w[row * H + tid];  // visible after the first barrier
+  const uint8_t* kb = k_idx + b * N_max * KROW;
+  float* srow = scores + row * N_max;
+
+  // DMA j of wave wv fills tile bytes [(DPW wv + j) KB, +1 KB): lane l lands
+  // at row r, chunk slot p, and so fetches chunk p ^ kswz(r) of row r
+  int drow[DPW];
+  uint32_t dcol[DPW];
+#pragma unroll
+  for (int j = 0; j < DPW; ++j) {
+    const int byte = (DPW * wv + j) * 1024 + 16 * l;
+    drow[j] = byte / KROW;
+    dcol[j] = (uint32_t)((((byte % KROW) / 16) ^ kswz<KDT>(drow[j])) * 16);
+  }
+  auto issue = [&](int64_t it) {
+    const int64_t tile = blockIdx.x + it * gridDim.x;
+    const int buf = (int)(it & (NBUF - 1));
+    const int last = (int)min((int64_t)(TE - 1), N_max - 1 - tile * TE);  // rows past the cache repeat its end
+    const uint8_t* tb = uniform_ptr(kb + tile * TB);
+#pragma unroll
+    for (int j = 0; j < DPW; ++j)
+      dma_row(tb, (uint32_t)(min(drow[j], last) * KROW) + dcol[j], lds_addr(&lds_k[buf][(DPW * wv + j) * 1024]));
+    if (l < TE / 4)  // wave wv moves the scales of entries 32 wv .. 32 wv + 31
+      dma_dword(uniform_ptr(k_scale + b * N_max + tile * TE), (uint32_t)(min(TE / 4 * wv + l, last) * 4),
+                lds_addr(&lds_s[buf][TE / 4 * wv]));
+  };
+  auto flush = [&](int64_t it_begin, int64_t it_end) {  // scores of tiles [it_begin, it_end)
+    const int cnt = (int)(it_end - it_begin) * TE;
+    for (int k = tid; k < cnt; k += 256) {
+      const int64_t tile = blockIdx.x + (it_begin + k / TE) * gridDim.x;
+      const int64_t e = tile * TE + (k % TE);
+      if (e < V) srow[e] = lds_sc[k / TE][k % TE];
+    }
+    vm_wait_all();  // the stores retire before DMA counting resumes
+  };
+
+  // consume the query here: the compiler's wait for its loads lands before the
+  // first DMA, never inside the loop
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qa[mt][s]));
+  for (int64_t it = 0; it < nmine && it < NBUF - 1; ++it) issue(it);
+  int64_t it_flushed = 0;
+  for (int64_t it = 0; it < nmine; ++it) {
+    const int ahead = (int)min((int64_t)(NBUF - 2), nmine - 1 - it);  // tiles issued after this one
+    if (ahead >= 2)
+      vm_barrier<2 * PER_TILE>();
+    else if (ahead == 1)
+      vm_barrier<PER_TILE>();
+    else
+      vm_barrier<0>();
+    // every wave is done with tile it-1: its buffer takes tile it+NBUF-1
+    if (it + NBUF - 1 < nmine) issue(it + NBUF - 1);
+    const int buf = (int)(it & (NBUF - 1));
+    float part[NE];
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+      const int el = wv * (16 * NE) + n * 16 + l16;  // entry inside the tile
+      const uint8_t* kr = &lds_k[buf][el * KROW];
+      const int sw = kswz<KDT>(el);
+      bf16x8_t kbv[KS];
+      // dims G*32 + s*8 .. : bytes G*32 + s*8, i.e. chunk G*2 + s/2, half s%2
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + (((G * 2 + c) ^ sw) * 16));
+        u32x4_t lo, hi;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          lo[2 * q] = fp8x2_to_bf16x2(v[q], false);
+          lo[2 * q + 1] = fp8x2_to_bf16x2(v[q], true);
+          hi[2 * q] = fp8x2_to_bf16x2(v[2 + q], false);
+          hi[2 * q + 1] = fp8x2_to_bf16x2(v[2 + q], true);
+        }
+        kbv[2 * c] = as_bf16x8(lo);
+        kbv[2 * c + 1] = as_bf16x8(hi);
+      }
+      part[n] = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], kbv[s], acc);
+        // accumulator row r of this lane is head mt*16 + G*4 + r
+        const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[mt * 16 + G * 4]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[n] += wv4[r] * fmaxf(acc[r], 0.0f);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+      part[n] += shfl_xor(part[n], 16);
+      part[n] += shfl_xor(part[n], 32);
+    }
+    if (G == 0) {
+#pragma unroll
+      for (int n = 0; n < NE; ++n) {
+        const int el = wv * (16 * NE) + n * 16 + l16;
+        lds_sc[(it - it_flushed) % SC_TILES][el] = part[n] * lds_s[buf][el];
+      }
+    }
+    if (it + 1 - it_flushed == SC_TILES && it + 1 < nmine) {
+      __syncthreads();
+      flush(it_flushed, it + 1);
+      it_flushed = it + 1;
+    }
+  }
+  __syncthreads();
+  flush(it_flushed, nmine);
 }
 
 // Prefill: many queries of one sequence. A workgroup of 8 waves owns 8
@@ -358,20 +523,21 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
     return hipGetLastError();
   }
   if (a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16) {
-    const int64_t ntiles = (a.N_max + 63) / 64;
+    const int64_t te = a.k_dt == DT_FP8 ? 128 : IDX_BF16_TE;
+    const int64_t ntiles = (a.N_max + te - 1) / te;
     // a few workgroups per CU in total, each walking a strided run of tiles
     // of its row
     int64_t per_row = (512 + rows - 1) / rows;
     per_row = max((int64_t)1, min(ntiles, per_row));
     dim3 grid((unsigned)per_row, (unsigned)rows);
     if (a.k_dt == DT_FP8)
-      hipLaunchKernelGGL((idx_scan_bf16_kernel<DT_FP8>), grid, dim3(256), 0, st,
-                         reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
-                         a.k_scale, a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
+      hipLaunchKernelGGL(idx_scan_fp8_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx),
+                         a.w, reinterpret_cast<const uint8_t*>(a.k_idx), a.k_scale, a.q_pos, a.n_comp, a.Tq,
+                         a.N_max, a.m, a.scores);
     else
-      hipLaunchKernelGGL((idx_scan_bf16_kernel<DT_BF16>), grid, dim3(256), 0, st,
-                         reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
-                         a.k_scale, a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
+      hipLaunchKernelGGL(idx_scan_bf16_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx),
+                         a.w, reinterpret_cast<const uint8_t*>(a.k_idx), a.q_pos, a.n_comp, a.Tq, a.N_max, a.m,
+                         a.scores);
     return hipGetLastError();
   }
   // f32, D_I = 32, H_I <= 32

@@ -9,9 +9,10 @@
 // algorithm: selection is exact, so the output depends on the row alone.
 //
 // Algorithm. A 1024-thread workgroup owns one chunk of up to 32768 keys of a
-// row, cached in LDS as order-preserving uint32 keys. A three-digit radix
-// select (11 + 11 + 10 bits) with integer LDS histograms finds the exact
-// chunk-local K-th key T; each digit is chosen by one wave that holds the
+// row, cached in LDS as order-preserving uint32 keys. A radix select with
+// integer LDS histograms finds the exact chunk-local K-th key T: digits of up
+// to 11 bits taken below the common prefix of the chunk's smallest and largest
+// key (at most three passes); each digit is chosen by one wave that holds the
 // bin counts in registers and scans them from the top. The chunk is then compacted in index order (per-wave
 // counts, a scan over waves, ballot prefix sums): all keys > T and the
 // lowest-index ties == T. A row that fits one chunk is finished in one launch.
@@ -40,15 +41,6 @@ __device__ __forceinline__ float key_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int l) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (l >= o) v += t;
-  }
-  return v;
-}
-
 // Given counts of nb bins, find the bin b with (count above b) < need <=
 // (count of bins >= b), using wave 0 only: lane l sums the nb/64 bins
 // [nb - (l+1)*nb/64, nb - l*nb/64), one shuffle scan over lanes, and the lane
@@ -69,7 +61,7 @@ __device__ __forceinline__ void find_bin_wave(const uint32_t* hist, int nb, int 
     int loc = 0;
 #pragma unroll
     for (int u = 0; u < 32; ++u) loc += (int)v[u];
-    const int inc = wave_incl_scan(loc, l);
+    const int inc = wave_incl_scan_dpp(loc);
     const int above = inc - loc;
     if (above < need && need <= inc) {
       int c = above, bin = -1, cab = 0;
@@ -186,49 +178,81 @@ __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
     }
   }
 
-  // ---- radix select of the K-th largest key (skipped when everything is kept)
+  // ---- radix select of the K-th largest key (skipped when everything is kept).
+  // The digits start below the common prefix of the chunk's smallest and
+  // largest key, so the first histogram spreads over the chunk's own range
+  // (a fixed top digit puts scores of similar magnitude into a few bins, and
+  // the LDS atomics of a pass then serialise on them).
   uint32_t T = 0;
   int need = 0;
   if (K < n) {
-    uint32_t prefix = 0;
     need = K;
-    for (int i = t; i < 2 * TK_BINS; i += TK_NT) hist[i] = 0;
-    __syncthreads();  // also publishes the key cache
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const int nbits = pass == 2 ? 10 : 11;
-      const int nb = 1 << nbits;
-      const int hshift = shift + nbits;
-      uint32_t* h = hist + (pass & 1) * TK_BINS;
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    {
       const int n4 = n >> 2;
       const u32x4_t* k4p = reinterpret_cast<const u32x4_t*>(kc);
-      // four 16-byte LDS reads in flight per thread before their atomics
-      for (int i0 = t; i0 < n4; i0 += 4 * TK_NT) {
-        u32x4_t k4[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) k4[u] = (i0 + u * TK_NT < n4) ? k4p[i0 + u * TK_NT] : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (i0 + u * TK_NT >= n4) break;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (pass == 0 || (k4[u][e] >> hshift) == prefix)
-              atomicAdd(&h[(k4[u][e] >> shift) & (nb - 1)], 1u);
-        }
+      for (int i = t; i < n4; i += TK_NT) {
+        const u32x4_t k4 = k4p[i];
+        kmin = min(min(kmin, k4[0]), min(k4[1], min(k4[2], k4[3])));
+        kmax = max(max(kmax, k4[0]), max(k4[1], max(k4[2], k4[3])));
       }
       for (int i = 4 * n4 + t; i < n; i += TK_NT) {
-        const uint32_t k = kc[i];
-        if (pass == 0 || (k >> hshift) == prefix) atomicAdd(&h[(k >> shift) & (nb - 1)], 1u);
+        kmin = min(kmin, kc[i]);
+        kmax = max(kmax, kc[i]);
       }
-      __syncthreads();
-      find_bin_wave(h, nb, need, res);
-      prefix = (prefix << nbits) | (uint32_t)res[0];
-      need -= res[1];
-      if (pass == 0)  // pass 2 reuses this buffer; nothing reads it during pass 1
-        for (int i = t; i < TK_BINS; i += TK_NT) h[i] = 0;
     }
-    T = prefix;  // take all keys > T and the `need` lowest-index keys == T
+    kmin = wave_min_u32_dpp(kmin);
+    kmax = wave_max_u32_dpp(kmax);
+    if (l == 0) {
+      red[wv] = (int)kmin;
+      red[TK_NW + wv] = (int)kmax;
+    }
+    for (int i = t; i < 2 * TK_BINS; i += TK_NT) hist[i] = 0;
+    __syncthreads();  // also publishes the key cache
+#pragma unroll
+    for (int u = 0; u < TK_NW; ++u) {
+      kmin = min(kmin, (uint32_t)red[u]);
+      kmax = max(kmax, (uint32_t)red[TK_NW + u]);
+    }
+    if (kmin == kmax) {
+      T = kmin;  // all keys equal: the K lowest indices
+    } else {
+      int R = 32 - __builtin_clz(kmin ^ kmax);  // bits below the common prefix
+      uint32_t prefix = R >= 32 ? 0u : (kmin >> R);
+#pragma unroll 1
+      for (int pass = 0; R > 0; ++pass) {
+        const int nbits = min(11, R);
+        const int shift = R - nbits;
+        const uint32_t dmask = (1u << nbits) - 1u;
+        uint32_t* h = hist + (pass & 1) * TK_BINS;
+        auto add = [&](uint32_t k) {
+          if (R >= 32 || (k >> R) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
+        };
+        const int n4 = n >> 2;
+        const u32x4_t* k4p = reinterpret_cast<const u32x4_t*>(kc);
+        // four 16-byte LDS reads in flight per thread before their atomics
+        for (int i0 = t; i0 < n4; i0 += 4 * TK_NT) {
+          u32x4_t k4[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) k4[u] = (i0 + u * TK_NT < n4) ? k4p[i0 + u * TK_NT] : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (i0 + u * TK_NT >= n4) break;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) add(k4[u][e]);
+          }
+        }
+        for (int i = 4 * n4 + t; i < n; i += TK_NT) add(kc[i]);
+        __syncthreads();
+        find_bin_wave(h, TK_BINS, need, res);
+        prefix = (prefix << nbits) | (uint32_t)res[0];
+        need -= res[1];
+        if (pass == 0)  // pass 2 reuses this buffer; nothing reads it during pass 1
+          for (int i = t; i < TK_BINS; i += TK_NT) h[i] = 0;
+        R = shift;
+      }
+      T = prefix;  // take all keys > T and the `need` lowest-index keys == T
+    }
   } else {
     __syncthreads();  // publish the key cache
   }
@@ -258,11 +282,8 @@ __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
           eq += in && k4[u][e] == T;
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      gt += __shfl_xor(gt, o, 64);
-      eq += __shfl_xor(eq, o, 64);
-    }
+    gt = wave_sum_dpp(gt);
+    eq = wave_sum_dpp(eq);
   }
   if (l == 0) {
     red[wv] = all ? (s_hi - s_lo) : gt;
@@ -270,10 +291,13 @@ __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
   }
   __syncthreads();
   int eq_before = 0, sel_before = 0;
-  for (int u = 0; u < wv; ++u) {
+#pragma unroll
+  for (int u = 0; u < TK_NW; ++u) {
     const int gu = red[u], eu = red[TK_NW + u];
-    sel_before += gu + (all ? 0 : max(0, min(need - eq_before, eu)));
-    eq_before += eu;
+    if (u < wv) {
+      sel_before += gu + (all ? 0 : max(0, min(need - eq_before, eu)));
+      eq_before += eu;
+    }
   }
   // popcount of the mask's bits below this lane (v_mbcnt_lo/hi)
   auto below_cnt = [](uint64_t msk) {
@@ -339,6 +363,7 @@ __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
     }
   }
 }
+
 
 static int64_t pow2_at_least(int64_t x) {
   int64_t p = 1;

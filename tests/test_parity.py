@@ -188,6 +188,33 @@ def _topk_case(rows, N_max, Vs, k, dist, seed=0):
         assert np.array_equal(I[r], ref), f"row {r}: exact selection differs"
 
 
+def test_indexer_fp8_all_codes_exact():
+    """Every E4M3 code through the scoring kernels (decode scan, Tq = 1, and
+    prefill, Tq = 8): head 0 = e_c with weight +1 and head 1 = -e_c with weight
+    -1 give s_i = ReLU(k_i[c]) - ReLU(-k_i[c]) = k_i[c], the decoded code, with
+    exact arithmetic; it must equal the oracle's decoding bit for bit."""
+    N, c = 320, 37
+    codes = np.zeros((N, 128), np.uint8)
+    codes[:256, c] = np.arange(256, dtype=np.uint8)
+    want = oracle.e4m3_decode(codes[:256, c])
+    finite = np.isfinite(want)
+    for Tq in (1, 8):
+        _say("fp8 codes", Tq)
+        q = np.zeros((1, Tq, 64, 128), np.float32)
+        q[..., 0, c] = 1.0
+        q[..., 1, c] = -1.0
+        w = np.zeros((1, Tq, 64), np.float32)
+        w[..., 0], w[..., 1] = 1.0, -1.0
+        scores = torch.full((1, Tq, N), 7.0, dtype=torch.float32, device=DEV)
+        L.indexer_score(bf(q), dev(w), dev(codes[None]), dev(np.ones((1, N), np.float32)),
+                        dev(np.full((1, Tq), 4 * N - 1, np.int32)), dev(np.array([N], np.int32)), scores, m=4)
+        torch.cuda.synchronize()
+        got = host(scores)[0]
+        for t in range(Tq):
+            assert np.array_equal(got[t, :256][finite], want[finite]), f"Tq={Tq} row {t}"
+            assert np.all(got[t, 256:] == 0.0)
+
+
 def test_topk_exact_normal():
     _topk_case(6, 5000, [5000, 4999, 1, 0, 100, 3000], 300, "normal", seed=20)
 
@@ -201,6 +228,14 @@ def test_topk_two_level_rows():
     # rows longer than one 32768-key chunk go through chunk winners + a second selection;
     # rows of one launch may end in either chunk
     _topk_case(3, 40000, [40000, 33000, 20000], 1024, "normal", seed=23)
+
+
+def test_topk_wave_levels_ties_and_ragged():
+    # top_k <= 1024 runs one wave per 4096-key chunk: five levels for 300001 keys,
+    # integer scores tie across chunks, rows end mid-chunk and mid-lane
+    _topk_case(3, 300001, [300001, 123457, 4099], 1024, "ties", seed=25)
+    _topk_case(5, 9001, [9001, 4097, 4096, 1, 0], 1, "normal", seed=26)
+    _topk_case(2, 8193, [8193, 8190], 7, "zeros", seed=27)
 
 
 def test_topk_multilevel_ties():

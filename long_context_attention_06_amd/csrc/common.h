@@ -96,6 +96,16 @@ __device__ __forceinline__ int wave_incl_scan_dpp(int v) {
   return v;
 }
 
+// Sum over the four 16-lane rows of a wave, per column: lane l gets
+// x[l%16] + x[l%16 + 16] + x[l%16 + 32] + x[l%16 + 48]. gfx950's permlane
+// swaps exchange rows as plain VALU operations (no LDS round trip).
+__device__ __forceinline__ float sum_rows16(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Wave-wide reductions, result uniform (rotations within rows, then the four
 // rows' values read as scalars).
 __device__ __forceinline__ int wave_sum_dpp(int v) {
@@ -124,6 +134,10 @@ __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// max(0, x) in one integer max on the bit pattern: negative floats (and -0)
+// are negative integers; positive values pass unchanged.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // ---- HBM -> LDS without registers (global_load_lds, issued from inline asm so
 // the compiler's own load tracking never waits on it; the caller waits with

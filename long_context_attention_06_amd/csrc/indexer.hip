@@ -140,13 +140,12 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
         // accumulator row r of this lane is head mt*16 + G*4 + r
         const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[mt * 16 + G * 4]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part[n] += wv4[r] * fmaxf(acc[r], 0.0f);
+        for (int r = 0; r < 4; ++r) part[n] += wv4[r] * relu_bits(acc[r]);
       }
     }
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
-      part[n] += shfl_xor(part[n], 16);
-      part[n] += shfl_xor(part[n], 32);
+      part[n] = sum_rows16(part[n]);
       const int64_t e = tile * TE + wv * (16 * NE) + n * 16 + l16;
       if (G == 0 && e < V) srow[e] = part[n];
     }
@@ -301,13 +300,12 @@ idx_scan_fp8_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
         // accumulator row r of this lane is head mt*16 + G*4 + r
         const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[mt * 16 + G * 4]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part[n] += wv4[r] * fmaxf(acc[r], 0.0f);
+        for (int r = 0; r < 4; ++r) part[n] += wv4[r] * relu_bits(acc[r]);
       }
     }
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
-      part[n] += shfl_xor(part[n], 16);
-      part[n] += shfl_xor(part[n], 32);
+      part[n] = sum_rows16(part[n]);
     }
     if (G == 0) {
 #pragma unroll
@@ -414,6 +412,7 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
     if (tile + 2 < ntiles) load(BUF, tile + 2);
     __syncthreads();
     if (qok && tile * TE < Vq) {
+      float part[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int el = nt * 16 + l16;
@@ -424,17 +423,23 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + (((G * 2 + c) ^ sw) * 16));
-            const u32x2_t a0 = fp8x4_to_bf16x4(v[0]), a1 = fp8x4_to_bf16x4(v[1]);
-            const u32x2_t a2 = fp8x4_to_bf16x4(v[2]), a3 = fp8x4_to_bf16x4(v[3]);
-            kbv[2 * c] = as_bf16x8(u32x4_t{a0[0], a0[1], a1[0], a1[1]});
-            kbv[2 * c + 1] = as_bf16x8(u32x4_t{a2[0], a2[1], a3[0], a3[1]});
+            u32x4_t lo, hi;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              lo[2 * q] = fp8x2_to_bf16x2(v[q], false);
+              lo[2 * q + 1] = fp8x2_to_bf16x2(v[q], true);
+              hi[2 * q] = fp8x2_to_bf16x2(v[2 + q], false);
+              hi[2 * q + 1] = fp8x2_to_bf16x2(v[2 + q], true);
+            }
+            kbv[2 * c] = as_bf16x8(lo);
+            kbv[2 * c + 1] = as_bf16x8(hi);
           }
         } else {
 #pragma unroll
           for (int s = 0; s < KS; ++s)
             kbv[s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + (((G * 4 + s) ^ sw) * 16)));
         }
-        float part = 0.0f;
+        part[nt] = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -442,15 +447,14 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
           for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], kbv[s], acc);
           const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[wv][mt * 16 + G * 4]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) part += wv4[r] * fmaxf(acc[r], 0.0f);
+          for (int r = 0; r < 4; ++r) part[nt] += wv4[r] * relu_bits(acc[r]);
         }
-        part += shfl_xor(part, 16);
-        part += shfl_xor(part, 32);
-        const int64_t e = tile * TE + el;
-        if (G == 0 && e < Vq) {
-          if constexpr (KDT == DT_FP8) part *= k_scale[b * N_max + e];
-          srow[e] = part;
-        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float v = sum_rows16(part[nt]);
+        const int64_t e = tile * TE + nt * 16 + l16;
+        if (G == 0 && e < Vq) srow[e] = KDT == DT_FP8 ? v * k_scale[b * N_max + e] : v;
       }
     }
   };
@@ -500,7 +504,7 @@ idx_scan_f32_kernel(const float* __restrict__ q_idx, const float* __restrict__ w
     for (int s = 0; s < KS; ++s) acc = mfma32(qa[s], ok ? kp[s] : 0.0f, acc);
     float part = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.0f);
+    for (int r = 0; r < 16; ++r) part += wr[r] * relu_bits(acc[r]);
     part += shfl_xor(part, 32);
     if (g == 0 && ok) srow[e] = part;
   }

@@ -19,16 +19,16 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// Round-to-nearest-even fp32 -> bf16 bits; NaN stays NaN.
+// Round-to-nearest-even fp32 -> bf16 bits (v_cvt_pk_bf16_f32 on gfx950); NaN
+// stays NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Unpack 8 bf16 held in a 16-byte vector to fp32.

@@ -726,39 +726,71 @@ attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ 
   if (h >= H) return;
   const float s2 = sink ? sink[h] * LOG2E_F : -INFINITY;
   const int64_t row0 = qi * nsplit * (int64_t)H + h;  // partial (qi, s, h) at row0 + s*H
-  float M = s2;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(row0 + (int64_t)s * H) * 2]);
   constexpr int MAXC = 2;  // float4 chunks per lane (D <= 512)
   f32x4_t acc[MAXC];
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float Z = 0.0f;
-  if (M != -INFINITY) {
-    Z = exp2f(s2 - M);
-    for (int s0 = 0; s0 < nsplit; s0 += 4) {
-      f32x4_t v[4][MAXC];
-      float a[4];
+  float M = s2, Z = 0.0f;
+  constexpr int U1 = 16;
+  if (nsplit <= U1) {
+    // every partial of the head in one round of loads, then the same merge
+    float mv[U1], lv[U1];
+    f32x4_t v[U1][MAXC];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s = s0 + u;
-        a[u] = 0.0f;
-        if (s < nsplit) {
-          const int64_t pb = row0 + (int64_t)s * H;
-          a[u] = exp2f(part_ml[pb * 2] - M);  // 0 for an empty split (m = -inf)
-          Z += part_ml[pb * 2 + 1] * a[u];
+    for (int u = 0; u < U1; ++u) {
+      const int64_t pb = row0 + (int64_t)u * H;
+      const bool in = u < nsplit;
+      mv[u] = in ? part_ml[pb * 2] : -INFINITY;
+      lv[u] = in ? part_ml[pb * 2 + 1] : 0.0f;
 #pragma unroll
-          for (int c = 0; c < MAXC; ++c) {
-            const int d = (c * 64 + l) * 4;
-            v[u][c] = d < D ? *reinterpret_cast<const f32x4_t*>(part_o + pb * D + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
-        }
+      for (int c = 0; c < MAXC; ++c) {
+        const int d = (c * 64 + l) * 4;
+        v[u][c] = (in && d < D) ? *reinterpret_cast<const f32x4_t*>(part_o + pb * D + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U1; ++u) M = fmaxf(M, mv[u]);
+    if (M != -INFINITY) {
+      Z = exp2f(s2 - M);
+#pragma unroll
+      for (int u = 0; u < U1; ++u) {
+        const float a = exp2f(mv[u] - M);  // 0 for an empty or absent split (m = -inf)
+        Z += lv[u] * a;
 #pragma unroll
         for (int c = 0; c < MAXC; ++c)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[c][e] += v[u][c][e] * a[u];
+          for (int e = 0; e < 4; ++e) acc[c][e] += v[u][c][e] * a;
+      }
+    }
+  } else {
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(row0 + (int64_t)s * H) * 2]);
+    if (M != -INFINITY) {
+      Z = exp2f(s2 - M);
+      for (int s0 = 0; s0 < nsplit; s0 += 4) {
+        f32x4_t v[4][MAXC];
+        float a[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int s = s0 + u;
+          a[u] = 0.0f;
+          if (s < nsplit) {
+            const int64_t pb = row0 + (int64_t)s * H;
+            a[u] = exp2f(part_ml[pb * 2] - M);  // 0 for an empty split (m = -inf)
+            Z += part_ml[pb * 2 + 1] * a[u];
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) {
+              const int d = (c * 64 + l) * 4;
+              v[u][c] = d < D ? *reinterpret_cast<const f32x4_t*>(part_o + pb * D + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int c = 0; c < MAXC; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[c][e] += v[u][c][e] * a[u];
+      }
     }
   }
   const float inv = (M != -INFINITY) ? 1.0f / Z : 0.0f;

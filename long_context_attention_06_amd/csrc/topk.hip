@@ -94,7 +94,216 @@ struct TopkArgs {
   float* out_score;        // final, nullable
   uint32_t* nkey;          // next level: [rows, nchunk, top_k]
   int32_t* nidx;
+  // threshold path: per-row threshold key, per-chunk candidates and counts
+  uint32_t* thr;           // [rows]
+  uint32_t* fkey;          // [rows, nfch * TK_FCH]
+  int32_t* fidx;
+  int32_t* fcnt;           // [rows, nfch]
+  int nfch;
 };
+
+constexpr int TK_FCH = 4096;     // keys per workgroup of the filter
+constexpr int TK_SAMPLE = 4096;  // scores sampled per row for the threshold
+constexpr int TK_FCH_MAX = 1024; // filter chunks per row the final kernel can gather
+
+__device__ __forceinline__ int64_t visible_of(const TopkArgs& a, int64_t row) {
+  const int64_t b = row / a.Tq;
+  const int64_t v = min((int64_t)a.n_comp[b], ((int64_t)a.q_pos[row] + 1) / a.m);
+  return max((int64_t)0, min(v, a.N_max));
+}
+
+// Where the select and the compaction read keys: the workgroup's LDS cache,
+// or a row of scores in memory converted on the fly (positions >= lim read 0).
+struct LdsKeys {
+  const uint32_t* kc;
+  __device__ __forceinline__ u32x4_t load4(int i4) const { return reinterpret_cast<const u32x4_t*>(kc)[i4]; }
+  __device__ __forceinline__ uint32_t load1(int i) const { return kc[i]; }
+};
+struct RowKeys {
+  const float* s;
+  int lim;
+  bool aligned;
+  __device__ __forceinline__ u32x4_t load4(int i4) const {
+    const int p = 4 * i4;
+    if (aligned && p + 3 < lim) {
+      const f32x4_t v = reinterpret_cast<const f32x4_t*>(s)[i4];
+      return u32x4_t{f32_key(v[0]), f32_key(v[1]), f32_key(v[2]), f32_key(v[3])};
+    }
+    u32x4_t r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = p + e < lim ? f32_key(s[p + e]) : 0u;
+    return r;
+  }
+  __device__ __forceinline__ uint32_t load1(int i) const { return f32_key(s[i]); }
+};
+
+// Exact K-th largest key T of keys [0, n) (0 < K < n) and how many keys equal
+// to T belong to the top K (`need`). All threads call it. The digits start
+// below the common prefix of the smallest and largest key, so the first
+// histogram spreads over the keys' own range (a fixed top digit puts scores of
+// similar magnitude into a few bins, and the LDS atomics of a pass then
+// serialise on them).
+template <class KS>
+__device__ void block_select(const KS& ks, int n, int K, uint32_t* hist, int* red, int* res, uint32_t& T,
+                             int& need) {
+  const int t = threadIdx.x, l = t & 63, wv = t >> 6;
+  need = K;
+  const int n4 = n >> 2;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int i = t; i < n4; i += TK_NT) {
+    const u32x4_t k4 = ks.load4(i);
+    kmin = min(min(kmin, k4[0]), min(k4[1], min(k4[2], k4[3])));
+    kmax = max(max(kmax, k4[0]), max(k4[1], max(k4[2], k4[3])));
+  }
+  for (int i = 4 * n4 + t; i < n; i += TK_NT) {
+    const uint32_t k = ks.load1(i);
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
+  }
+  kmin = wave_min_u32_dpp(kmin);
+  kmax = wave_max_u32_dpp(kmax);
+  if (l == 0) {
+    red[wv] = (int)kmin;
+    red[TK_NW + wv] = (int)kmax;
+  }
+  for (int i = t; i < 2 * TK_BINS; i += TK_NT) hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < TK_NW; ++u) {
+    kmin = min(kmin, (uint32_t)red[u]);
+    kmax = max(kmax, (uint32_t)red[TK_NW + u]);
+  }
+  if (kmin == kmax) {
+    T = kmin;  // all keys equal: the K lowest positions
+    __syncthreads();  // every wave has read red[] before the caller reuses it
+    return;
+  }
+  int R = 32 - __builtin_clz(kmin ^ kmax);  // bits below the common prefix
+  uint32_t prefix = R >= 32 ? 0u : (kmin >> R);
+#pragma unroll 1
+  for (int pass = 0; R > 0; ++pass) {
+    const int nbits = min(11, R);
+    const int shift = R - nbits;
+    const uint32_t dmask = (1u << nbits) - 1u;
+    uint32_t* h = hist + (pass & 1) * TK_BINS;
+    auto add = [&](uint32_t k) {
+      if (R >= 32 || (k >> R) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
+    };
+    // four 16-byte reads in flight per thread before their atomics
+    for (int i0 = t; i0 < n4; i0 += 4 * TK_NT) {
+      u32x4_t k4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) k4[u] = (i0 + u * TK_NT < n4) ? ks.load4(i0 + u * TK_NT) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (i0 + u * TK_NT >= n4) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) add(k4[u][e]);
+      }
+    }
+    for (int i = 4 * n4 + t; i < n; i += TK_NT) add(ks.load1(i));
+    __syncthreads();
+    find_bin_wave(h, TK_BINS, need, res);
+    prefix = (prefix << nbits) | (uint32_t)res[0];
+    need -= res[1];
+    if (pass == 0)  // pass 2 reuses this buffer; nothing reads it during pass 1
+      for (int i = t; i < TK_BINS; i += TK_NT) h[i] = 0;
+    R = shift;
+  }
+  T = prefix;  // take all keys > T and the `need` lowest-position keys == T
+}
+
+// Ordered compaction of the selection in position order: all keys > T and
+// the first `need` keys == T (every key when all == true). emit(pos, key, i)
+// receives output slot pos < top_k, the key and its position; slots K..top_k-1
+// go to pad(pos). Each wave owns a contiguous segment; a lane handles 4
+// consecutive keys per step; index-order prefixes come from ballots of the
+// bits of the per-lane counts (0..4).
+template <class KS, class Emit, class Pad>
+__device__ void block_compact(const KS& ks, int n, int K, bool all, uint32_t T, int need, int top_k, int* red,
+                              Emit emit, Pad pad) {
+  const int t = threadIdx.x, l = t & 63, wv = t >> 6;
+  const int seg = ((n + TK_NW - 1) / TK_NW + 255) / 256 * 256;
+  const int s_lo = min(n, wv * seg), s_hi = min(n, s_lo + seg);
+  int gt = 0, eq = 0;
+  if (!all) {
+    for (int base = s_lo; base < s_hi; base += 512) {
+      u32x4_t k4[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i0 = base + u * 256 + 4 * l;
+        k4[u] = i0 < s_hi ? ks.load4(i0 >> 2) : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool in = base + u * 256 + 4 * l + e < s_hi;
+          gt += in && k4[u][e] > T;
+          eq += in && k4[u][e] == T;
+        }
+    }
+    gt = wave_sum_dpp(gt);
+    eq = wave_sum_dpp(eq);
+  }
+  if (l == 0) {
+    red[wv] = all ? (s_hi - s_lo) : gt;
+    red[TK_NW + wv] = eq;
+  }
+  __syncthreads();
+  int eq_before = 0, sel_before = 0;
+#pragma unroll
+  for (int u = 0; u < TK_NW; ++u) {
+    const int gu = red[u], eu = red[TK_NW + u];
+    if (u < wv) {
+      sel_before += gu + (all ? 0 : max(0, min(need - eq_before, eu)));
+      eq_before += eu;
+    }
+  }
+  // popcount of the mask's bits below this lane (v_mbcnt_lo/hi)
+  auto below_cnt = [](uint64_t msk) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
+  };
+  auto excl3 = [&](int v, int& total) {  // wave exclusive prefix and total of v in 0..7
+    const uint64_t b0 = __ballot(v & 1), b1 = __ballot(v & 2), b2 = __ballot(v & 4);
+    total = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+    return below_cnt(b0) + 2 * below_cnt(b1) + 4 * below_cnt(b2);
+  };
+  int run_sel = 0, run_eq = 0;
+  for (int base = s_lo; base < s_hi; base += 256) {
+    const int i0 = base + 4 * l;
+    const u32x4_t k4 = i0 < s_hi ? ks.load4(i0 >> 2) : u32x4_t{0, 0, 0, 0};
+    bool in[4], eqf[4], sel[4];
+    int ne = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      in[e] = i0 + e < s_hi;
+      eqf[e] = !all && in[e] && k4[e] == T;
+      ne += eqf[e];
+    }
+    int eq_tot;
+    int r = eq_before + run_eq + excl3(ne, eq_tot);
+    int ns = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sel[e] = in[e] && (all || k4[e] > T || (eqf[e] && r < need));
+      r += eqf[e];
+      ns += sel[e];
+    }
+    int sel_tot;
+    int pos = sel_before + run_sel + excl3(ns, sel_tot);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (sel[e]) {
+        if (pos < top_k) emit(pos, k4[e], i0 + e);
+        ++pos;
+      }
+    }
+    run_sel += sel_tot;
+    run_eq += eq_tot;
+  }
+  for (int i = K + t; i < top_k; i += TK_NT) pad(i);
+}
 
 template <int SRC>
 __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
@@ -106,17 +315,10 @@ __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
   uint32_t* kc = smem + 2 * TK_BINS + 64;                  // CH keys
   int32_t* ic = reinterpret_cast<int32_t*>(kc + CH);       // TK_CANDS: indices
 
-  const int t = threadIdx.x, l = t & 63, wv = t >> 6;
+  const int t = threadIdx.x;
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x, nchunk = gridDim.x;
-  int64_t n_row;
-  if constexpr (SRC == TK_SCORES) {
-    const int64_t b = row / a.Tq;
-    const int64_t v = min((int64_t)a.n_comp[b], ((int64_t)a.q_pos[row] + 1) / a.m);
-    n_row = max((int64_t)0, min(v, a.N_max));
-  } else {
-    n_row = a.n_cand;
-  }
+  const int64_t n_row = SRC == TK_SCORES ? visible_of(a, row) : a.n_cand;
   const int64_t lo = (int64_t)c * CH;
   const int n = (int)max((int64_t)0, min(n_row - lo, (int64_t)CH));
   const int top_k = a.top_k;
@@ -177,183 +379,25 @@ __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
       }
     }
   }
+  __syncthreads();  // publish the key cache
 
-  // ---- radix select of the K-th largest key (skipped when everything is kept).
-  // The digits start below the common prefix of the chunk's smallest and
-  // largest key, so the first histogram spreads over the chunk's own range
-  // (a fixed top digit puts scores of similar magnitude into a few bins, and
-  // the LDS atomics of a pass then serialise on them).
+  const LdsKeys keys{kc};
   uint32_t T = 0;
   int need = 0;
-  if (K < n) {
-    need = K;
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
-    {
-      const int n4 = n >> 2;
-      const u32x4_t* k4p = reinterpret_cast<const u32x4_t*>(kc);
-      for (int i = t; i < n4; i += TK_NT) {
-        const u32x4_t k4 = k4p[i];
-        kmin = min(min(kmin, k4[0]), min(k4[1], min(k4[2], k4[3])));
-        kmax = max(max(kmax, k4[0]), max(k4[1], max(k4[2], k4[3])));
-      }
-      for (int i = 4 * n4 + t; i < n; i += TK_NT) {
-        kmin = min(kmin, kc[i]);
-        kmax = max(kmax, kc[i]);
-      }
-    }
-    kmin = wave_min_u32_dpp(kmin);
-    kmax = wave_max_u32_dpp(kmax);
-    if (l == 0) {
-      red[wv] = (int)kmin;
-      red[TK_NW + wv] = (int)kmax;
-    }
-    for (int i = t; i < 2 * TK_BINS; i += TK_NT) hist[i] = 0;
-    __syncthreads();  // also publishes the key cache
-#pragma unroll
-    for (int u = 0; u < TK_NW; ++u) {
-      kmin = min(kmin, (uint32_t)red[u]);
-      kmax = max(kmax, (uint32_t)red[TK_NW + u]);
-    }
-    if (kmin == kmax) {
-      T = kmin;  // all keys equal: the K lowest indices
-    } else {
-      int R = 32 - __builtin_clz(kmin ^ kmax);  // bits below the common prefix
-      uint32_t prefix = R >= 32 ? 0u : (kmin >> R);
-#pragma unroll 1
-      for (int pass = 0; R > 0; ++pass) {
-        const int nbits = min(11, R);
-        const int shift = R - nbits;
-        const uint32_t dmask = (1u << nbits) - 1u;
-        uint32_t* h = hist + (pass & 1) * TK_BINS;
-        auto add = [&](uint32_t k) {
-          if (R >= 32 || (k >> R) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
-        };
-        const int n4 = n >> 2;
-        const u32x4_t* k4p = reinterpret_cast<const u32x4_t*>(kc);
-        // four 16-byte LDS reads in flight per thread before their atomics
-        for (int i0 = t; i0 < n4; i0 += 4 * TK_NT) {
-          u32x4_t k4[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) k4[u] = (i0 + u * TK_NT < n4) ? k4p[i0 + u * TK_NT] : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (i0 + u * TK_NT >= n4) break;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) add(k4[u][e]);
-          }
-        }
-        for (int i = 4 * n4 + t; i < n; i += TK_NT) add(kc[i]);
-        __syncthreads();
-        find_bin_wave(h, TK_BINS, need, res);
-        prefix = (prefix << nbits) | (uint32_t)res[0];
-        need -= res[1];
-        if (pass == 0)  // pass 2 reuses this buffer; nothing reads it during pass 1
-          for (int i = t; i < TK_BINS; i += TK_NT) h[i] = 0;
-        R = shift;
-      }
-      T = prefix;  // take all keys > T and the `need` lowest-index keys == T
-    }
-  } else {
-    __syncthreads();  // publish the key cache
-  }
-
-  // ---- ordered compaction: each wave owns a contiguous segment; a lane
-  // handles 4 consecutive keys per step (one 16-byte LDS read); index-order
-  // prefixes come from ballots of the bits of the per-lane counts (0..4)
-  const int seg = ((n + TK_NW - 1) / TK_NW + 255) / 256 * 256;
-  const int s_lo = min(n, wv * seg), s_hi = min(n, s_lo + seg);
   const bool all = K == n;
-  const u32x4_t* kc4 = reinterpret_cast<const u32x4_t*>(kc);
-  int gt = 0, eq = 0;
-  if (!all) {
-    for (int base = s_lo; base < s_hi; base += 512) {
-      u32x4_t k4[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int i0 = base + u * 256 + 4 * l;
-        k4[u] = i0 < s_hi ? kc4[i0 >> 2] : u32x4_t{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool in = base + u * 256 + 4 * l + e < s_hi;
-          gt += in && k4[u][e] > T;
-          eq += in && k4[u][e] == T;
-        }
-    }
-    gt = wave_sum_dpp(gt);
-    eq = wave_sum_dpp(eq);
-  }
-  if (l == 0) {
-    red[wv] = all ? (s_hi - s_lo) : gt;
-    red[TK_NW + wv] = eq;
-  }
-  __syncthreads();
-  int eq_before = 0, sel_before = 0;
-#pragma unroll
-  for (int u = 0; u < TK_NW; ++u) {
-    const int gu = red[u], eu = red[TK_NW + u];
-    if (u < wv) {
-      sel_before += gu + (all ? 0 : max(0, min(need - eq_before, eu)));
-      eq_before += eu;
-    }
-  }
-  // popcount of the mask's bits below this lane (v_mbcnt_lo/hi)
-  auto below_cnt = [](uint64_t msk) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
-  };
-  auto excl3 = [&](int v, int& total) {  // wave exclusive prefix and total of v in 0..7
-    const uint64_t b0 = __ballot(v & 1), b1 = __ballot(v & 2), b2 = __ballot(v & 4);
-    total = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
-    return below_cnt(b0) + 2 * below_cnt(b1) + 4 * below_cnt(b2);
-  };
-  int run_sel = 0, run_eq = 0;
+  if (!all) block_select(keys, n, K, hist, red, res, T, need);
   const int64_t obase = final_out ? row * (int64_t)top_k : (row * nchunk + c) * (int64_t)top_k;
-  for (int base = s_lo; base < s_hi; base += 256) {
-    const int i0 = base + 4 * l;
-    const u32x4_t k4 = i0 < s_hi ? kc4[i0 >> 2] : u32x4_t{0, 0, 0, 0};
-    bool in[4], eqf[4], sel[4];
-    int ne = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      in[e] = i0 + e < s_hi;
-      eqf[e] = !all && in[e] && k4[e] == T;
-      ne += eqf[e];
+  auto emit = [&](int pos, uint32_t key, int i) {
+    const int32_t gi = SRC == TK_SCORES ? (int32_t)(lo + i) : ic[i];
+    if (final_out) {
+      a.out_idx[obase + pos] = gi;
+      if (a.out_score) a.out_score[obase + pos] = key_f32(key);
+    } else {
+      a.nkey[obase + pos] = key;
+      a.nidx[obase + pos] = gi;
     }
-    int eq_tot;
-    int r = eq_before + run_eq + excl3(ne, eq_tot);
-    int ns = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sel[e] = in[e] && (all || k4[e] > T || (eqf[e] && r < need));
-      r += eqf[e];
-      ns += sel[e];
-    }
-    int sel_tot;
-    int pos = sel_before + run_sel + excl3(ns, sel_tot);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (sel[e]) {
-        if (pos < top_k) {
-          int32_t gi;
-          if constexpr (SRC == TK_SCORES) gi = (int32_t)(lo + i0 + e);
-          else gi = ic[i0 + e];
-          if (final_out) {
-            a.out_idx[obase + pos] = gi;
-            if (a.out_score) a.out_score[obase + pos] = key_f32(k4[e]);
-          } else {
-            a.nkey[obase + pos] = k4[e];
-            a.nidx[obase + pos] = gi;
-          }
-        }
-        ++pos;
-      }
-    }
-    run_sel += sel_tot;
-    run_eq += eq_tot;
-  }
-  for (int i = K + t; i < top_k; i += TK_NT) {
+  };
+  auto pad = [&](int i) {
     if (final_out) {
       a.out_idx[obase + i] = -1;
       if (a.out_score) a.out_score[obase + i] = -INFINITY;
@@ -361,9 +405,168 @@ __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
       a.nkey[obase + i] = 0u;  // below every finite key: never selected later
       a.nidx[obase + i] = -1;
     }
-  }
+  };
+  block_compact(keys, n, K, all, T, need, top_k, red, emit, pad);
 }
 
+// ----------------------------------------------------------------------------
+// Threshold path for long rows (one sample select, one filter, one select)
+// ----------------------------------------------------------------------------
+// 1. topk_threshold_kernel: per row, the exact r-th largest key T_s of an
+//    evenly spaced sample of TK_SAMPLE scores, r chosen so that about 2 K of
+//    the row's scores lie at or above it. Rows that fit the final kernel take
+//    T_s = 0 (every key).
+// 2. topk_filter_kernel: per 4096-key chunk, the keys >= T_s with their
+//    positions, compacted in position order, and their count.
+// 3. topk_filtered_kernel: per row, the chunks' candidates gathered in chunk
+//    order (so in position order) and selected exactly. If the sample misled
+//    (fewer than K' candidates, or more than fit in LDS), it selects over the
+//    whole row read from memory instead. Either way the result is the exact
+//    top K'.
+__global__ void __launch_bounds__(TK_NT) topk_threshold_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2 * TK_BINS];
+  __shared__ int red[32], res[32];
+  __shared__ __attribute__((aligned(16))) uint32_t kc[TK_SAMPLE];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t V = visible_of(a, row);
+  if (V <= TK_CHUNK_C) {
+    if (t == 0) a.thr[row] = 0u;
+    return;
+  }
+  const int K = min((int64_t)a.top_k, V);
+  const float* src = a.scores + row * a.N_max;
+  for (int i = t; i < TK_SAMPLE; i += TK_NT) kc[i] = f32_key(src[(int64_t)i * V / TK_SAMPLE]);
+  __syncthreads();
+  const int r = (int)min((int64_t)(TK_SAMPLE - 1), (2 * (int64_t)K * TK_SAMPLE + V - 1) / V + 8);
+  uint32_t T;
+  int need;
+  block_select(LdsKeys{kc}, TK_SAMPLE, r, hist, red, res, T, need);
+  if (t == 0) a.thr[row] = T;
+}
+
+__global__ void __launch_bounds__(TK_NT) topk_filter_kernel(TopkArgs a) {
+  __shared__ int wtot[TK_NW];
+  const int t = threadIdx.x, l = t & 63, wv = t >> 6;
+  const int64_t row = blockIdx.y;
+  const int c = blockIdx.x;
+  const int64_t V = visible_of(a, row);
+  const int64_t lo = (int64_t)c * TK_FCH;
+  const int n = (int)max((int64_t)0, min(V - lo, (int64_t)TK_FCH));
+  const uint32_t thr = a.thr[row];
+  const float* src = a.scores + row * a.N_max + lo;
+  const int p = 4 * t;
+  u32x4_t k4;
+  if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && p + 3 < n) {
+    const f32x4_t v = reinterpret_cast<const f32x4_t*>(src)[t];
+    k4 = u32x4_t{f32_key(v[0]), f32_key(v[1]), f32_key(v[2]), f32_key(v[3])};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k4[e] = p + e < n ? f32_key(src[p + e]) : 0u;
+  }
+  bool sel[4];
+  int ns = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sel[e] = p + e < n && k4[e] >= thr;
+    ns += sel[e];
+  }
+  auto below_cnt = [](uint64_t msk) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
+  };
+  const uint64_t b0 = __ballot(ns & 1), b1 = __ballot(ns & 2), b2 = __ballot(ns & 4);
+  const int wsum = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+  int pos = below_cnt(b0) + 2 * below_cnt(b1) + 4 * below_cnt(b2);
+  if (l == 0) wtot[wv] = wsum;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int u = 0; u < TK_NW; ++u) {
+    const int v = wtot[u];
+    pos += u < wv ? v : 0;
+    total += v;
+  }
+  const int64_t obase = row * (int64_t)a.nfch * TK_FCH + lo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (sel[e]) {
+      a.fkey[obase + pos] = k4[e];
+      a.fidx[obase + pos] = (int32_t)(lo + p + e);
+      ++pos;
+    }
+  if (t == 0) a.fcnt[row * a.nfch + c] = total;
+}
+
+__global__ void __launch_bounds__(TK_NT) topk_filtered_kernel(TopkArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  uint32_t* hist = smem;                                   // 2 x TK_BINS
+  int* red = reinterpret_cast<int*>(smem + 2 * TK_BINS);   // 32
+  int* res = red + 32;                                     // 32
+  int* off = res + 32;                                     // TK_FCH_MAX chunk offsets, then the total
+  uint32_t* kc = reinterpret_cast<uint32_t*>(off + TK_FCH_MAX + 64);  // TK_CHUNK_C keys
+  int32_t* ic = reinterpret_cast<int32_t*>(kc + TK_CHUNK_C);          // and positions
+  const int t = threadIdx.x, l = t & 63, wv = t >> 6;
+  const int64_t row = blockIdx.x;
+  const int64_t V = visible_of(a, row);
+  const int top_k = a.top_k;
+  const int K = (int)min((int64_t)top_k, V);
+  const int nfch = a.nfch;
+  const int32_t* cnt = a.fcnt + row * nfch;
+
+  // chunk offsets in chunk order (wave 0: a lane sums a contiguous run of chunks)
+  if (wv == 0) {
+    const int per = (nfch + 63) / 64;
+    const int c0 = min(nfch, l * per), c1 = min(nfch, c0 + per);
+    int s = 0;
+    for (int c = c0; c < c1; ++c) s += cnt[c];
+    int run = wave_incl_scan_dpp(s) - s;
+    for (int c = c0; c < c1; ++c) {
+      off[c] = run;
+      run += cnt[c];
+    }
+    if (l == 63) off[TK_FCH_MAX] = run;
+  }
+  __syncthreads();
+  const int total = off[TK_FCH_MAX];
+  const int64_t obase = row * (int64_t)top_k;
+  auto emit_to = [&](auto idx_of) {
+    return [&, idx_of](int pos, uint32_t key, int i) {
+      a.out_idx[obase + pos] = idx_of(i);
+      if (a.out_score) a.out_score[obase + pos] = key_f32(key);
+    };
+  };
+  auto pad = [&](int i) {
+    a.out_idx[obase + i] = -1;
+    if (a.out_score) a.out_score[obase + i] = -INFINITY;
+  };
+  if (total >= K && total <= TK_CHUNK_C) {
+    // gather: wave wv copies chunks wv, wv + 16, ... to their offsets
+    const uint32_t* fk = a.fkey + row * (int64_t)nfch * TK_FCH;
+    const int32_t* fi = a.fidx + row * (int64_t)nfch * TK_FCH;
+    for (int c = wv; c < nfch; c += TK_NW) {
+      const int nc = cnt[c], o = off[c];
+      for (int j = l; j < nc; j += 64) {
+        kc[o + j] = fk[(int64_t)c * TK_FCH + j];
+        ic[o + j] = fi[(int64_t)c * TK_FCH + j];
+      }
+    }
+    __syncthreads();
+    const LdsKeys keys{kc};
+    uint32_t T = 0;
+    int need = 0;
+    const bool all = K == total;
+    if (!all) block_select(keys, total, K, hist, red, res, T, need);
+    block_compact(keys, total, K, all, T, need, top_k, red, emit_to([&](int i) { return ic[i]; }), pad);
+  } else {
+    const float* src = a.scores + row * a.N_max;
+    const RowKeys keys{src, (int)V, (reinterpret_cast<uintptr_t>(src) & 15) == 0};
+    uint32_t T = 0;
+    int need = 0;
+    const bool all = K == (int)V;
+    if (!all) block_select(keys, (int)V, K, hist, red, res, T, need);
+    block_compact(keys, (int)V, K, all, T, need, top_k, red, emit_to([](int i) { return (int32_t)i; }), pad);
+  }
+}
 
 static int64_t pow2_at_least(int64_t x) {
   int64_t p = 1;
@@ -393,7 +596,25 @@ static int plan_levels(int64_t rows, int64_t n0, int top_k, int64_t* nch, int64_
   return lv;
 }
 
+// Long rows (three or more levels) take the threshold path when its final
+// kernel can gather every filter chunk. Depends on shape arguments only.
+static bool use_threshold_path(int64_t rows, int64_t N_max, int top_k) {
+  int64_t nch[12], nlen[12], chunk[12];
+  const int lv = plan_levels(rows, N_max, top_k, nch, nlen, chunk);
+  const int64_t nfch = (N_max + TK_FCH - 1) / TK_FCH;
+  return lv >= 3 && nfch <= TK_FCH_MAX && top_k <= TK_CHUNK_C / 8;
+}
+
+static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// threshold path workspace: thr [rows] | fcnt [rows, nfch] | fkey, fidx [rows, nfch * TK_FCH]
+static size_t threshold_ws(int64_t rows, int64_t N_max) {
+  const int64_t nfch = (N_max + TK_FCH - 1) / TK_FCH;
+  return round256(rows * 4) + round256(rows * nfch * 4) + 2 * round256((size_t)rows * nfch * TK_FCH * 4);
+}
+
 size_t topk_ws_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k) {
+  if (use_threshold_path(B * Tq, N_max, top_k)) return threshold_ws(B * Tq, N_max);
   int64_t nch[12], nlen[12], chunk[12];
   const int lv = plan_levels(B * Tq, N_max, top_k, nch, nlen, chunk);
   size_t mx = 0;
@@ -415,6 +636,44 @@ hipError_t run_topk(const TopkLaunch& L, hipStream_t st) {
                             (int)lds_c);
     if (e != hipSuccess) return e;
     attr_set = true;
+  }
+  if (use_threshold_path(rows, L.N_max, L.top_k)) {
+    const size_t lds_f = (size_t)(2 * TK_BINS + 64 + TK_FCH_MAX + 64 + 2 * TK_CHUNK_C) * 4;
+    static bool attr_f = false;
+    if (!attr_f) {
+      hipError_t e = hipFuncSetAttribute((const void*)topk_filtered_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_f);
+      if (e != hipSuccess) return e;
+      attr_f = true;
+    }
+    const int64_t nfch = (L.N_max + TK_FCH - 1) / TK_FCH;
+    TopkArgs a{};
+    a.scores = L.scores;
+    a.q_pos = L.q_pos;
+    a.n_comp = L.n_comp;
+    a.Tq = L.Tq;
+    a.N_max = L.N_max;
+    a.m = L.m;
+    a.top_k = L.top_k;
+    a.out_idx = L.idx;
+    a.out_score = L.out_score;
+    a.nfch = (int)nfch;
+    uint8_t* w = reinterpret_cast<uint8_t*>(L.ws);
+    a.thr = reinterpret_cast<uint32_t*>(w);
+    w += round256(rows * 4);
+    a.fcnt = reinterpret_cast<int32_t*>(w);
+    w += round256(rows * nfch * 4);
+    a.fkey = reinterpret_cast<uint32_t*>(w);
+    w += round256((size_t)rows * nfch * TK_FCH * 4);
+    a.fidx = reinterpret_cast<int32_t*>(w);
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(TK_NT), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)nfch, (unsigned)rows), dim3(TK_NT), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_filtered_kernel, dim3((unsigned)rows), dim3(TK_NT), lds_f, st, a);
+    return hipGetLastError();
   }
   int64_t nch[12], nlen[12], chunk[12];
   const int lv = plan_levels(rows, L.N_max, L.top_k, nch, nlen, chunk);

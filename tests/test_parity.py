@@ -230,9 +230,17 @@ def test_topk_two_level_rows():
     _topk_case(3, 40000, [40000, 33000, 20000], 1024, "normal", seed=23)
 
 
-def test_topk_wave_levels_ties_and_ragged():
-    # top_k <= 1024 runs one wave per 4096-key chunk: five levels for 300001 keys,
-    # integer scores tie across chunks, rows end mid-chunk and mid-lane
+def test_topk_threshold_path_normal():
+    # rows needing three or more levels take a sampled threshold, a filter and one
+    # select; a short row (V <= 16384) keeps every key as a candidate
+    _topk_case(3, 200003, [200003, 150001, 17000], 1024, "normal", seed=28)
+    _topk_case(2, 100000, [100000, 99999], 256, "normal", seed=29)
+
+
+def test_topk_long_rows_ties_and_ragged():
+    # long rows of integer scores: the sampled threshold keeps too many candidates,
+    # so the final kernel selects over the whole row; ties cross chunks, rows end
+    # mid-chunk and mid-lane
     _topk_case(3, 300001, [300001, 123457, 4099], 1024, "ties", seed=25)
     _topk_case(5, 9001, [9001, 4097, 4096, 1, 0], 1, "normal", seed=26)
     _topk_case(2, 8193, [8193, 8190], 7, "zeros", seed=27)

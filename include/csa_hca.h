@@ -183,7 +183,8 @@ size_t sparse_mqa_decode_workspace_bytes(int64_t B, int H, int D, int top_k, int
  *            uses window rows kv_tok[max(0, p-W+1) .. p] ([LIDUOS]: the latest
  *            W raw tokens, the current one included)
  *   out    : [Tq, H, D]          lse : [Tq, H] (nullable)
- * Supported: top_k <= 1024 and top_k + W <= 2048. Needs no workspace. */
+ * Supported: top_k + W <= 2048 (f32 rows: also top_k <= 1024). Needs no
+ * workspace. */
 int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_idx,
                        const void* kv_tok, const int32_t* q_pos, const float* sink, float scale,
                        int64_t Tq, int H, int D, int64_t N, int64_t T_tok, int top_k, int W,

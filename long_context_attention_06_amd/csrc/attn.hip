@@ -460,6 +460,326 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
 }
 
 // ----------------------------------------------------------------------------
+// bf16 prefill: four waves of 32 heads on v_mfma_f32_32x32x16_bf16
+// ----------------------------------------------------------------------------
+//
+// In prefill the rows of every query are gathered once and the tile work is
+// bound by LDS reads. With 16-head waves each K and V byte of a tile is read
+// by four waves; here wave w owns heads 32 (w%2) .. +31 and dims 256 (w/2)
+// .. +255, so each byte is read by two. S^T (32 rows x 32 heads) comes from
+// v_mfma_f32_32x32x16_bf16 over the wave's 256 dims; the pair of waves sharing
+// heads swaps partials through LDS as in attn_bf16_kernel. In the S^T
+// accumulator a lane holds one head for 16 rows; registers 8 ks .. 8 ks + 7
+// are the P operand of k-step ks of O += P R in the K order
+//   position 8 h + j  <->  row (2 ks + j/4) 8 + 4 h + j%4      (h = lane / 32),
+// and the R operand of that k-step is two transpose reads of four consecutive
+// rows. O (32 heads x 256 dims, 128 registers) lives in accumulation
+// registers. One wave per SIMD; rows arrive by DMA as in attn_bf16_kernel
+// (eight per wave per tile).
+
+// Chunk swizzle of the 32-head kernel (16-byte chunks; 64 banks of 4 bytes
+// span 16 chunks): a 4-bit rotation of the row. Any 16 consecutive rows put
+// one chunk in 16 distinct bank groups (the K reads of the QK chain), and the
+// four rows 4i .. 4i+3 differ in the high bits, so a half-wave of transposed V
+// reads (four rows x four aligned chunks) also covers all 64 banks once.
+__device__ __forceinline__ int swz4(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+namespace p32 {
+constexpr int D = 512, ROWB = 1024, TR = 32, NW = 4, NT = 256, NBUF = 4;
+constexpr int TILEB = TR * ROWB;
+constexpr int RPW = TR / NW;     // rows each wave loads per tile
+constexpr int TAB_MAX = 2048;
+}  // namespace p32
+
+__device__ __forceinline__ f32x16_t mfma32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __restrict__ q_pos,
+                  const float* __restrict__ sink, float scale_log2, int H, int slots,
+                  void* __restrict__ out, float* __restrict__ lse, int out_dt) {
+  using namespace p32;
+  constexpr int SRC = SRC_SPARSE_PRE;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TILEB];
+  __shared__ __attribute__((aligned(16))) f32x4_t xchg[NW][4][64];
+  __shared__ __attribute__((aligned(16))) int tab[TAB_MAX];
+  __shared__ int cnt[NW];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = l >> 5, l32 = l & 31;
+  const int hg = w & 1, dh = w >> 1;
+  const int64_t qi = blockIdx.x;
+  const int head = hg * 32 + l32;  // this lane's head in S^T / P / softmax
+
+  QRows rr = query_rows<SRC>(src, nullptr, nullptr, q_pos, 1, qi, 0, slots, slots);
+
+  // ---- Q^T operand (B of S^T = R Q^T): lane (head, h), dims 256 dh + 16 s + 8 h .. +7
+  bf16x8_t qb[16];
+  {
+    const bool hok = head < H;
+    const uint16_t* qp = q + (qi * H + (hok ? head : 0)) * (int64_t)D + dh * 256 + h * 8;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qb[s] = as_bf16x8(hok ? ld16(qp + s * 16) : u32x4_t{0, 0, 0, 0});
+  }
+
+  rr.n_rows = build_row_table<SRC, NT, TR>(src, rr, qi, tab, cnt);
+  const int n_rows = rr.n_rows;
+  const int ntiles = (n_rows + TR - 1) / TR;
+
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  uint32_t voff[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) voff[i] = (uint32_t)((l ^ swz4(RPW * w + i)) * 16);
+  auto issue = [&](int t) {
+    const int c0 = t * TR + RPW * w;
+    const uint32_t dst = ring_lds + (uint32_t)((t & (NBUF - 1)) * TILEB + RPW * w * ROWB);
+    const u32x4_t e0 = *reinterpret_cast<const u32x4_t*>(&tab[c0]);
+    const u32x4_t e1 = *reinterpret_cast<const u32x4_t*>(&tab[c0 + 4]);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int e = (int)__builtin_amdgcn_readfirstlane(i < 4 ? e0[i & 3] : e1[i & 3]);
+      dma_row(uniform_ptr(tab_row(rr, e)), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+    }
+  };
+
+  f32x16_t o[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[nt][r] = 0.0f;
+  float m_ref = -INFINITY, l_run = 0.0f;
+
+  // QK A operand: row l32, dims 256 dh + 16 s + 8 h -> chunk 32 dh + 2 s + h
+  //   = 32 dh + 16 (s / 8) + ((2 (s % 8) + h) ^ swz4(row))
+  int qofs[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) qofs[v] = l32 * ROWB + (((2 * v + h) ^ swz4(l32)) * 16) + dh * 512;
+  // PV R operand (transpose read): 16-lane group g = l / 16 takes rows
+  // k0 .. k0+3 (k0 = 16 ks + 4 h, +8 for the second read) and columns
+  // n0 .. n0+15 (n0 = 256 dh + 32 nt + 16 (g % 2)); lane j of the group
+  // supplies row k0 + j/4, column n0 + 4 (j%4): chunk 32 dh + 4 nt + 2 (g%2) + (j%4)/2
+  int pofs[2][2][4];  // [ks][first/second read][nt % 4], plus 256 bytes for nt >= 4
+  {
+    const int g = l >> 4, j = l & 15;
+    const int cl = 2 * (g & 1) + ((j & 3) >> 1), cb = (j & 1) * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd) {
+        const int row = 16 * ks + 4 * h + 8 * rd + (j >> 2);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pofs[ks][rd][u] = row * ROWB + (((4 * u + cl) ^ swz4(row)) * 16) + cb + dh * 512;
+      }
+  }
+
+  // Q^T waits in accumulation registers (MFMA reads its A/B operands from
+  // either file), leaving the VGPRs to the reads in flight
+#pragma unroll
+  for (int s = 0; s < 16; ++s) asm volatile("" : "+a"(qb[s]));
+
+  // Software pipeline. With one wave per SIMD nothing else hides latency, so
+  // each wave overlaps its own phases: iteration t runs the softmax of tile t
+  // while the QK chain of tile t+1 is in the matrix core, then O += P V of
+  // tile t while the partial S of tile t+1 is swapped with the other dim half.
+  // At the top of iteration t tiles t and t+1 are resident and sv holds the
+  // full S of tile t. On the last tile the QK chain reads a stale slot and its
+  // result is dropped.
+  auto qk_reads = [&](const uint8_t* RK, u32x4_t* kr) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) kr[s] = *reinterpret_cast<const u32x4_t*>(RK + qofs[s & 7] + (s >> 3) * 256);
+  };
+  auto qk_chain = [&](const u32x4_t* kr) {
+    f32x16_t sp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sp[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) sp = mfma32x16(as_bf16x8(kr[s]), qb[s], sp);
+    return sp;
+  };
+  auto put_partial = [&](const f32x16_t& sp) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xchg[w][k][l] = f32x4_t{sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
+  };
+  auto add_partner = [&](const f32x16_t& sp) {
+    f32x16_t sv;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4_t x = xchg[w ^ 2][k][l];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[4 * k + e] = sp[4 * k + e] + x[e];
+    }
+    return sv;
+  };
+
+  f32x16_t sv;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sv[r] = 0.0f;
+  for (int t = 0; t < ntiles && t < NBUF - 1; ++t) issue(t);
+  if (ntiles > 0) {
+    if (ntiles > 2)
+      vm_barrier<RPW>();  // tiles 0 and 1 resident, tile 2 may be in flight
+    else
+      vm_barrier<0>();
+    u32x4_t kr[16];
+    qk_reads(ring, kr);
+    const f32x16_t sp = qk_chain(kr);
+    put_partial(sp);
+    vm_barrier<63>();
+    sv = add_partner(sp);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);  // the slot of tile t-1, free since the last barrier
+    const uint8_t* R = ring + (t & (NBUF - 1)) * TILEB;
+    const uint8_t* RN = ring + ((t + 1) & (NBUF - 1)) * TILEB;
+    u32x4_t kr[16];
+    qk_reads(RN, kr);
+
+    // ---- softmax of `head` over this lane's 16 rows (r/4) 8 + 4 h + r%4, exp2 domain
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = sv[r] * scale_log2;
+    if (t == ntiles - 1) {  // only the last tile holds padding rows
+      const int nvalid = n_rows - t * TR;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if ((r >> 2) * 8 + 4 * h + (r & 3) >= nvalid) x[r] = -INFINITY;
+    }
+    float lm = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) lm = fmaxf(lm, x[r]);
+    if (__builtin_expect(__any(lm > m_ref + RESCALE_SLACK), 0)) {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
+      const float tmax = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));  // over both lane halves
+      const float m_new = tmax > m_ref + RESCALE_SLACK ? tmax : m_ref;
+      const float alpha = (m_new == m_ref) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
+      m_ref = m_new;
+      // every O^T register of this lane belongs to its own head
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // scaled where it lives: a plain multiply would make the compiler keep
+          // a VGPR copy of all of O on every tile
+          float tmp;
+          asm volatile(
+              "v_accvgpr_read_b32 %1, %0\n\t"
+              "v_mul_f32 %1, %1, %2\n\t"
+              "v_accvgpr_write_b32 %0, %1"
+              : "+a"(o[nt][r]), "=&v"(tmp)
+              : "v"(alpha));
+        }
+    }
+    const float mr = (m_ref == -INFINITY) ? 0.0f : m_ref;
+
+    // ---- QK chain of tile t+1, with the exponentials of tile t between its MFMAs
+    const f32x16_t sp = qk_chain(kr);
+    float pv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pv[r] = __builtin_amdgcn_exp2f(x[r] - mr);
+      l_run += pv[r];
+    }
+    bf16x8_t pa[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      pa[ks] = as_bf16x8(u32x4_t{pack_bf16x2(pv[8 * ks], pv[8 * ks + 1]), pack_bf16x2(pv[8 * ks + 2], pv[8 * ks + 3]),
+                                 pack_bf16x2(pv[8 * ks + 4], pv[8 * ks + 5]), pack_bf16x2(pv[8 * ks + 6], pv[8 * ks + 7])});
+
+    // ---- O^T += R^T P^T of tile t over this wave's 256 dims: 8 N-tiles of 32
+    // dims, 2 k-steps of 16 rows. The operands are those of O = P R with A and
+    // B exchanged, so the accumulator holds O transposed: register r of N-tile
+    // nt is dim 32 nt + (r/4) 8 + 4 h + r%4 of this lane's head.
+    s16x4_t vr[8][2][2];  // [nt][ks][first/second four rows]
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd)
+          vr[nt][ks][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (s16x4_t __attribute__((address_space(3)))*)(R + pofs[ks][rd][nt & 3] + (nt >> 2) * 256));
+    // issue order: each QK MFMA followed by two of the V reads and four VALU
+    // (exponentials of tile t); the PV chain then finds its operands in registers
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- tile t+1's partial S goes out (once the partner has read the previous
+    // one), then the PV chain runs while the partials are swapped
+    vm_barrier<63>();
+    put_partial(sp);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t bv = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(vr[nt][ks][0], vr[nt][ks][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[nt] = mfma32x16(bv, pa[ks], o[nt]);
+      }
+    if (t + NBUF - 1 < ntiles)
+      vm_barrier<RPW>();  // tile t+2 resident, tile t+3 may be in flight
+    else
+      vm_barrier<0>();
+    sv = add_partner(sp);
+  }
+
+  // ---- epilogue: this lane's head is 32 hg + l32; register r of N-tile nt is
+  // dim 256 dh + 32 nt + (r/4) 8 + 4 h + r%4
+  {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    l_run = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+  }
+  const bool hok = head < H;
+  const float s2 = (sink && hok) ? sink[head] * LOG2E_F : -INFINITY;
+  const float M = fmaxf(m_ref, s2);
+  float fac = 0.0f;
+  if (M != -INFINITY) {
+    const float a = exp2f(m_ref - M);
+    fac = a / (l_run * a + exp2f(s2 - M));
+  }
+  const int64_t orow = (qi * H + (hok ? head : 0)) * (int64_t)D + dh * 256;
+  if (out_dt == DT_BF16) {
+    // the two lane halves hold alternate groups of four dims; one swap per
+    // dword gives each lane eight consecutive dims (16 bytes)
+    uint16_t* op = reinterpret_cast<uint16_t*>(out) + orow + 8 * h;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int r0 = 8 * p;
+        const uint32_t x0 = pack_bf16x2(o[nt][r0] * fac, o[nt][r0 + 1] * fac);
+        const uint32_t x1 = pack_bf16x2(o[nt][r0 + 2] * fac, o[nt][r0 + 3] * fac);
+        const uint32_t y0 = pack_bf16x2(o[nt][r0 + 4] * fac, o[nt][r0 + 5] * fac);
+        const uint32_t y1 = pack_bf16x2(o[nt][r0 + 6] * fac, o[nt][r0 + 7] * fac);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        if (hok) *reinterpret_cast<u32x4_t*>(op + nt * 32 + p * 16) = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+      }
+  } else if (hok) {
+    float* op = reinterpret_cast<float*>(out) + orow + 4 * h;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<f32x4_t*>(op + nt * 32 + qd * 8) =
+            f32x4_t{o[nt][4 * qd] * fac, o[nt][4 * qd + 1] * fac, o[nt][4 * qd + 2] * fac, o[nt][4 * qd + 3] * fac};
+  }
+  if (lse && dh == 0 && h == 0 && hok) {
+    float v = -INFINITY;
+    if (M != -INFINITY) v = (M + log2f(l_run * exp2f(m_ref - M) + exp2f(s2 - M))) * LN2_F;
+    lse[qi * H + head] = v;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // fp32 rows (small head dims): four-wave heads split, register-staged tiles
 // ----------------------------------------------------------------------------
 
@@ -844,6 +1164,14 @@ static hipError_t launch_bf16(const AttnLaunch& a, hipStream_t st) {
   return launch_combine(a, st);
 }
 
+static hipError_t launch_pre32(const AttnLaunch& a, hipStream_t st) {
+  if (a.nsplit != 1 || a.slots > p32::TAB_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_pre32_kernel, dim3((unsigned)a.nq), dim3(p32::NT), 0, st,
+                     reinterpret_cast<const uint16_t*>(a.q), row_src(a), a.q_pos, a.sink, a.scale * LOG2E_F, a.H,
+                     a.slots, a.out, a.lse, a.out_dt);
+  return hipGetLastError();
+}
+
 template <int D, int NWAV, int SRC>
 static hipError_t launch_f32(const AttnLaunch& a, hipStream_t st) {
   dim3 grid((unsigned)a.nq, a.nsplit);
@@ -858,7 +1186,10 @@ static hipError_t launch_f32(const AttnLaunch& a, hipStream_t st) {
 
 template <int SRC>
 static hipError_t dispatch_src(const AttnLaunch& a, hipStream_t st) {
-  if (a.kv_dt == DT_BF16 && a.D == 512 && a.H > 48 && a.H <= 64) return launch_bf16<SRC>(a, st);
+  if (a.kv_dt == DT_BF16 && a.D == 512 && a.H > 48 && a.H <= 64) {
+    if (SRC == SRC_SPARSE_PRE && a.nsplit == 1) return launch_pre32(a, st);
+    return launch_bf16<SRC>(a, st);
+  }
   if (a.kv_dt == DT_F32 && a.D == 64 && a.H <= 16) return launch_f32<64, 1, SRC>(a, st);
   return hipErrorInvalidValue;
 }

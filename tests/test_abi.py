@@ -109,3 +109,6 @@ def test_attention_validation():
     # rows per query beyond the kernel's row table
     assert p(P, P, P, P, P, P, 1.0, 4, 64, 512, 100, 4000, 1024, 1025, 1, 1, P, None, None, 0, None) == L.UNSUPPORTED
     assert "top_k + W" in _err()
+    # f32 rows stage at most 1024 top-k slots; bf16 rows take any top_k with top_k + W <= 2048
+    assert p(P, P, P, P, P, P, 1.0, 4, 16, 64, 2000, 4000, 1025, 8, 0, 0, P, None, None, 0, None) == L.UNSUPPORTED
+    assert "top_k <= 1024" in _err()

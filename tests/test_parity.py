@@ -322,10 +322,14 @@ def test_hca_decode():
         assert np.abs(LS[b] - rlse).max() < 1e-3
 
 
-def test_sparse_prefill():
-    _say("sparse_prefill")
-    g = _g(32)
-    Tq, H, D, N, T_tok, k, W = 50, 64, 512, 300, 1200, 64, 128
+@pytest.mark.parametrize("H,k,N,with_sink", [(64, 64, 300, True), (49, 1920, 3000, False), (57, 1000, 1024, True)])
+def test_sparse_prefill(H, k, N, with_sink):
+    """Prefill rows: top-k entries (some padded with -1) plus each query's own
+    window; head counts that leave part of the second 32-head group empty, no
+    sink, and the largest row table (top_k + W = 2048)."""
+    _say(f"sparse_prefill H={H} k={k}")
+    g = _g(32 + H)
+    Tq, D, T_tok, W = 50, 512, 1200, 128
     q = gen.bf16_round(g.standard_normal((Tq, H, D)).astype(np.float32) / math.sqrt(D))
     kv = gen.bf16_round(g.standard_normal((N, D)).astype(np.float32))
     tok = gen.bf16_round(g.standard_normal((T_tok, D)).astype(np.float32))
@@ -333,16 +337,17 @@ def test_sparse_prefill():
     pos[0] = 0
     idx = np.sort(g.choice(N, size=(Tq, k)), axis=1).astype(np.int32)
     idx[3, 20:] = -1
-    sink = g.standard_normal(H).astype(np.float32)
+    idx[7, :] = -1  # window rows only
+    sink = g.standard_normal(H).astype(np.float32) if with_sink else None
     out = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((Tq, H), device=DEV)
-    L.sparse_mqa_prefill(bf(q), bf(kv), dev(idx), bf(tok), dev(pos), dev(sink), out, lse, W=W)
+    L.sparse_mqa_prefill(bf(q), bf(kv), dev(idx), bf(tok), dev(pos), dev(sink) if with_sink else None, out, lse, W=W)
     torch.cuda.synchronize()
     O, LS = host(out), host(lse)
     for t in range(Tq):
         ids = idx[t][idx[t] >= 0]
         rows = np.concatenate([kv[ids], oracle.window_rows(tok, int(pos[t]), W)])
-        ref, rlse = oracle.attend(q[t], rows, sink)
+        ref, rlse = oracle.attend(q[t], rows, sink if with_sink else np.full(H, -np.inf))
         check_out(O[t], ref, _attn_tight(ref), f"prefill t={t}")
         assert np.abs(LS[t] - rlse).max() < 1e-3
 

@@ -160,6 +160,8 @@ size_t indexer_score_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, 
  * out_h = 0 and lse_h = -inf. Rows present in two sources count twice.
  * Supported: D = 512 with kv_dt BF16 and 49 <= H <= 64, or D = 64 with
  * kv_dt F32 and 1 <= H <= 16; out_dt in {F32, BF16}; q has the dtype kv_dt.
+ * scale must be positive and finite (CSA_INVALID_ARG otherwise); q and out
+ * must be 16-byte aligned.
  */
 
 /* sparse_mqa_decode — one query per sequence (position: the last token).

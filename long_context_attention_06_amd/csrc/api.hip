@@ -51,8 +51,10 @@ bool attn_supported(int H, int D, int kv_dt) {
   return (kv_dt == CSA_BF16 && D == 512 && H > 48 && H <= 64) || (kv_dt == CSA_F32 && D == 64 && H >= 1 && H <= 16);
 }
 
-int check_attn_common(const void* q, const void* out, int H, int D, int kv_dt, int out_dt, int W, int top_k) {
+int check_attn_common(const void* q, const void* out, float scale, int H, int D, int kv_dt, int out_dt, int W,
+                      int top_k) {
   REQ(q && out, CSA_INVALID_ARG, "q and out must not be NULL");
+  REQ(scale > 0.0f && scale <= 3.0e38f, CSA_INVALID_ARG, "scale must be positive and finite");
   REQ(H > 0 && D > 0, CSA_INVALID_ARG, "H and D must be positive");
   REQ(W >= 0 && top_k >= 0, CSA_INVALID_ARG, "W and top_k must be >= 0");
   REQ(kv_dt == CSA_F32 || kv_dt == CSA_BF16 || kv_dt == CSA_FP8_E4M3, CSA_INVALID_ARG, "unknown kv_dt");
@@ -61,7 +63,7 @@ int check_attn_common(const void* q, const void* out, int H, int D, int kv_dt, i
   REQ(attn_supported(H, D, kv_dt), CSA_UNSUPPORTED,
       "unsupported (H, D, kv_dt): supported are (49..64, 512, BF16) and (1..16, 64, F32)");
   REQ(aligned16(q), CSA_INVALID_ARG, "q must be 16-byte aligned");
-  REQ(out_dt != CSA_F32 || aligned16(out), CSA_INVALID_ARG, "out must be 16-byte aligned");
+  REQ(aligned16(out), CSA_INVALID_ARG, "out must be 16-byte aligned");
   return CSA_OK;
 }
 
@@ -203,7 +205,7 @@ int sparse_mqa_decode(const void* q, const void* kv_comp, const int32_t* topk_id
                       const int32_t* win_len, const float* sink, float scale, int64_t B, int H, int D, int64_t N_max,
                       int top_k, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws, size_t ws_bytes,
                       void* stream) {
-  int rc = check_attn_common(q, out, H, D, kv_dt, out_dt, W, top_k);
+  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, top_k);
   if (rc) return rc;
   REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
   REQ(top_k == 0 || (kv_comp && topk_idx), CSA_INVALID_ARG, "kv_comp and topk_idx must not be NULL");
@@ -252,7 +254,7 @@ int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_i
                        size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
-  int rc = check_attn_common(q, out, H, D, kv_dt, out_dt, W, top_k);
+  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, top_k);
   if (rc) return rc;
   REQ(Tq >= 0 && N >= 0 && T_tok >= 0, CSA_INVALID_ARG, "Tq, N, T_tok must be >= 0");
   REQ(q_pos, CSA_INVALID_ARG, "q_pos must not be NULL");
@@ -298,7 +300,7 @@ int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, con
                   const void* kv_win, const int32_t* win_len, const float* sink, float scale, int64_t B, int H, int D,
                   int64_t N_max, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws, size_t ws_bytes,
                   void* stream) {
-  int rc = check_attn_common(q, out, H, D, kv_dt, out_dt, W, 0);
+  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, 0);
   if (rc) return rc;
   REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
   REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");

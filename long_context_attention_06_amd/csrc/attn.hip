@@ -174,15 +174,17 @@ __device__ __forceinline__ QRows query_rows(const RowSrc& src, const int32_t* __
 }
 
 // Row table of a sparse split (all NT threads call it): entry = compressed row
-// id, or 0x80000000 | window row; invalid slots dropped, slot order kept, the
-// tail padded to a whole tile of TR with a valid row (those rows are masked).
-// Returns the row count.
+// id, or 0x80000000 | window row; invalid slots dropped, slot order kept (so
+// the compressed rows come first), the tail padded to a whole tile of TR with
+// the last row (those rows are masked). Returns the row count; the number of
+// compressed rows goes to *n_comp when it is given. cnt holds 2 NT/64 ints.
 template <int SRC, int NT, int TR>
-__device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, int* tab, int* cnt) {
+__device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, int* tab, int* cnt,
+                               int* n_comp = nullptr) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int n_rows = 0;
+  int n_rows = 0, n_c = 0;
   for (int c0 = r.s_begin; c0 < r.s_end; c0 += NT) {
     const int j = c0 + tid;
     int e = 0;
@@ -206,8 +208,12 @@ __device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, in
       }
     }
     const uint64_t bal = __ballot(ok);
+    const uint64_t balc = __ballot(ok && j < src.top_k);  // the whole wave votes
     const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-    if (l == 0) cnt[w] = __popcll(bal);
+    if (l == 0) {
+      cnt[w] = __popcll(bal);
+      cnt[NW + w] = __popcll(balc);
+    }
     __syncthreads();
     int off = n_rows, tot = 0;
 #pragma unroll
@@ -215,14 +221,16 @@ __device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, in
       const int c = cnt[v];
       off += v < w ? c : 0;
       tot += c;
+      n_c += cnt[NW + v];
     }
     if (ok) tab[off + rank] = e;
     n_rows += tot;
     __syncthreads();
   }
   const int padded = (n_rows + TR - 1) / TR * TR;
-  if (n_rows > 0 && n_rows + tid < padded) tab[n_rows + tid] = tab[0];
+  if (n_rows > 0 && n_rows + tid < padded) tab[n_rows + tid] = tab[n_rows - 1];
   __syncthreads();
+  if (n_comp) *n_comp = n_c;
   return n_rows;
 }
 
@@ -245,7 +253,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TILEB];
   __shared__ __attribute__((aligned(16))) f32x4_t xchg[NW][2][64];
   __shared__ __attribute__((aligned(16))) int tab[SRC == SRC_HCA_DEC ? 4 : TAB_MAX];
-  __shared__ int cnt[NW];
+  __shared__ int cnt[2 * NW];
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -504,7 +512,7 @@ attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __r
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TILEB];
   __shared__ __attribute__((aligned(16))) f32x4_t xchg[NW][4][64];
   __shared__ __attribute__((aligned(16))) int tab[TAB_MAX];
-  __shared__ int cnt[NW];
+  __shared__ int cnt[2 * NW];
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -525,9 +533,16 @@ attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __r
     for (int s = 0; s < 16; ++s) qb[s] = as_bf16x8(hok ? ld16(qp + s * 16) : u32x4_t{0, 0, 0, 0});
   }
 
-  rr.n_rows = build_row_table<SRC, NT, TR>(src, rr, qi, tab, cnt);
+  int n_comp_rows = 0;
+  rr.n_rows = build_row_table<SRC, NT, TR>(src, rr, qi, tab, cnt, &n_comp_rows);
   const int n_rows = rr.n_rows;
   const int ntiles = (n_rows + TR - 1) / TR;
+  // table entries below ncb are compressed rows, the rest window rows (the
+  // padded tail repeats the last row, so it belongs to the last row's cache)
+  const int ncb = (n_rows == n_comp_rows) ? ntiles * TR : n_comp_rows;
+  // rows of both caches below 2^22: a row's byte offset fits the DMA's 32-bit
+  // lane offset, so rows from one cache need no per-row 64-bit address
+  const bool off32 = src.N_max < (1 << 22) && src.T_tok < (1 << 22);
 
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   uint32_t voff[RPW];
@@ -538,10 +553,21 @@ attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __r
     const uint32_t dst = ring_lds + (uint32_t)((t & (NBUF - 1)) * TILEB + RPW * w * ROWB);
     const u32x4_t e0 = *reinterpret_cast<const u32x4_t*>(&tab[c0]);
     const u32x4_t e1 = *reinterpret_cast<const u32x4_t*>(&tab[c0 + 4]);
+    const bool comp_only = c0 + RPW <= ncb, win_only = c0 >= ncb;
+    if (off32 && (comp_only || win_only)) {
+      // one base for the wave's eight rows; the shift drops the window flag
+      const uint8_t* base = comp_only ? rr.comp_base : rr.win_base;
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int e = (int)__builtin_amdgcn_readfirstlane(i < 4 ? e0[i & 3] : e1[i & 3]);
-      dma_row(uniform_ptr(tab_row(rr, e)), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+      for (int i = 0; i < RPW; ++i) {
+        const uint32_t e = i < 4 ? e0[i & 3] : e1[i & 3];
+        dma_row(uniform_ptr(base), (e << 10) + voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int e = (int)__builtin_amdgcn_readfirstlane(i < 4 ? e0[i & 3] : e1[i & 3]);
+        dma_row(uniform_ptr(tab_row(rr, e)), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+      }
     }
   };
 
@@ -637,19 +663,19 @@ attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __r
     u32x4_t kr[16];
     qk_reads(RN, kr);
 
-    // ---- softmax of `head` over this lane's 16 rows (r/4) 8 + 4 h + r%4, exp2 domain
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = sv[r] * scale_log2;
+    // ---- softmax of `head` over this lane's 16 rows (r/4) 8 + 4 h + r%4, exp2
+    // domain. The scale is positive, so the max is taken on the raw scores and
+    // the scaling folds into the exponent's FMA.
     if (t == ntiles - 1) {  // only the last tile holds padding rows
       const int nvalid = n_rows - t * TR;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if ((r >> 2) * 8 + 4 * h + (r & 3) >= nvalid) x[r] = -INFINITY;
+        if ((r >> 2) * 8 + 4 * h + (r & 3) >= nvalid) sv[r] = -INFINITY;
     }
-    float lm = x[0];
+    float lm = sv[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) lm = fmaxf(lm, x[r]);
+    for (int r = 1; r < 16; ++r) lm = fmaxf(lm, sv[r]);
+    lm *= scale_log2;
     if (__builtin_expect(__any(lm > m_ref + RESCALE_SLACK), 0)) {
       const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
       const float tmax = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));  // over both lane halves
@@ -680,8 +706,8 @@ attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __r
     float pv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      pv[r] = __builtin_amdgcn_exp2f(x[r] - mr);
-      l_run += pv[r];
+      pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], scale_log2, -mr));
+      l_run += pv[r];  // fp32 weights: the log-sum-exp keeps fp32 accuracy
     }
     bf16x8_t pa[2];
 #pragma unroll

@@ -109,6 +109,10 @@ def test_attention_validation():
     # rows per query beyond the kernel's row table
     assert p(P, P, P, P, P, P, 1.0, 4, 64, 512, 100, 4000, 1024, 1025, 1, 1, P, None, None, 0, None) == L.UNSUPPORTED
     assert "top_k + W" in _err()
+    # the softmax scale must be positive and finite
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert p(P, P, P, P, P, P, bad, 4, 64, 512, 100, 400, 16, 8, 1, 1, P, None, None, 0, None) == L.INVALID_ARG
+        assert "scale" in _err()
     # f32 rows stage at most 1024 top-k slots; bf16 rows take any top_k with top_k + W <= 2048
     assert p(P, P, P, P, P, P, 1.0, 4, 16, 64, 2000, 4000, 1025, 8, 0, 0, P, None, None, 0, None) == L.UNSUPPORTED
     assert "top_k <= 1024" in _err()

@@ -103,6 +103,34 @@ __device__ __forceinline__ void feed_block(SoftAcc& S, const void* Cx, const voi
   }
 }
 
+// Raw inputs of four tokens of one block (8 channels each), loaded before
+// any arithmetic so that the loads of several blocks overlap.
+template <int IN_DT>
+struct Raw4 {
+  float z[4][8], c[4][8], b[4][8];
+  __device__ void load(const void* Cx, const void* Zx, const float* Bx, int64_t row0, int j, int d, int c0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      load8<IN_DT>(Zx, (row0 + j + t) * d + c0, z[t]);
+      load8<IN_DT>(Cx, (row0 + j + t) * d + c0, c[t]);
+      const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(Bx + (int64_t)(j + t) * d + c0);
+      const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(Bx + (int64_t)(j + t) * d + c0 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        b[t][e] = b0[e];
+        b[t][4 + e] = b1[e];
+      }
+    }
+  }
+  __device__ void feed(SoftAcc& S) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[t][e] = (z[t][e] + b[t][e]) * LOG2E_F;
+    S.feed<4>(z, c);
+  }
+};
+
 template <int IN_DT, int OUT_DT>
 __global__ void __launch_bounds__(256)
 compress_kernel(const void* __restrict__ Ca, const void* __restrict__ Cb, const void* __restrict__ Za,
@@ -122,10 +150,31 @@ compress_kernel(const void* __restrict__ Ca, const void* __restrict__ Cb, const 
   SoftAcc A, Bs;
   A.init();
   const int64_t rowa = b * n_rows + (m * i - tok_begin);
-  feed_block<IN_DT>(A, Ca, Za, Ba, rowa, d, m, c0);
   float res[8];
   const bool has_b = overlap && i >= 1;
-  if (has_b) {
+  if (m == 4) {
+    // one group per block: both blocks' loads go out before any arithmetic.
+    // Without a previous block (no overlap branch, where Cb, Zb, Bb may be
+    // null, or block 0) the second load repeats block i of Ca, Za, Ba, unused.
+    Raw4<IN_DT> ra, rb;
+    ra.load(Ca, Za, Ba, rowa, 0, d, c0);
+    rb.load(has_b ? Cb : Ca, has_b ? Zb : Za, has_b ? Bb : Ba, has_b ? rowa - m : rowa, 0, d, c0);
+    ra.feed(A);
+    if (has_b && joint) {
+      rb.feed(A);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) res[e] = A.acc[e] / A.sm[e];
+    } else if (has_b) {
+      Bs.init();
+      rb.feed(Bs);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) res[e] = A.acc[e] / A.sm[e] + Bs.acc[e] / Bs.sm[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) res[e] = A.acc[e] / A.sm[e];
+    }
+  } else if (has_b) {
+    feed_block<IN_DT>(A, Ca, Za, Ba, rowa, d, m, c0);
     const int64_t rowb = b * n_rows + (m * (i - 1) - tok_begin);
     if (joint) {
       feed_block<IN_DT>(A, Cb, Zb, Bb, rowb, d, m, c0);
@@ -138,6 +187,7 @@ compress_kernel(const void* __restrict__ Ca, const void* __restrict__ Cb, const 
       for (int e = 0; e < 8; ++e) res[e] = A.acc[e] / A.sm[e] + Bs.acc[e] / Bs.sm[e];
     }
   } else {
+    feed_block<IN_DT>(A, Ca, Za, Ba, rowa, d, m, c0);
 #pragma unroll
     for (int e = 0; e < 8; ++e) res[e] = A.acc[e] / A.sm[e];
   }
@@ -159,8 +209,10 @@ template <int IN_DT, int OUT_DT>
 static hipError_t launch(const CompressLaunch& a, hipStream_t st) {
   const int64_t nblk = a.blk_end - a.blk_begin;
   const int64_t total = a.B * nblk * (a.d / 8);
-  const int64_t grid = (total + 255) / 256;
-  hipLaunchKernelGGL((compress_kernel<IN_DT, OUT_DT>), dim3((unsigned)grid), dim3(256), 0, st, a.Ca, a.Cb, a.Za,
+  // few entries (a decode step): 64-thread groups reach more CUs
+  const int nt = total < 256 * 256 ? 64 : 256;
+  const int64_t grid = (total + nt - 1) / nt;
+  hipLaunchKernelGGL((compress_kernel<IN_DT, OUT_DT>), dim3((unsigned)grid), dim3(nt), 0, st, a.Ca, a.Cb, a.Za,
                      a.Zb, a.Ba, a.Bb, a.out, a.B, a.n_rows, a.tok_begin, a.blk_begin, nblk, a.out_cap, a.d, a.m,
                      (int)a.overlap, (int)a.joint);
   return hipGetLastError();

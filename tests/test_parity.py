@@ -84,6 +84,9 @@ def test_compress_decode_append():
 def test_compress_hca_single_branch():
     _compress_case(2, 128 * 5 + 7, 0, 512, 128, 0, 5, "bf16", "f32", overlap=False, seed=5)
     _compress_case(1, 130, 0, 64, 5, 3, 26, "f32", "f32", seed=6)  # m not a power of two, mid range
+    # m = 4 without the overlap branch: Cb, Zb, Bb are null
+    _compress_case(2, 64, 0, 512, 4, 0, 16, "bf16", "bf16", overlap=False, seed=7)
+    _compress_case(3, 8, 4096 - 8, 512, 4, 1022, 1024, "bf16", "f32", overlap=False, seed=8, out_cap=1024)
 
 
 # ------------------------------------------------------------------ indexer

@@ -173,6 +173,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+// Third dword of a raw (untyped) buffer descriptor on gfx9: 32-bit data format.
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
 __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 
 // Order-preserving map fp32 -> uint32 (larger float <=> larger key); -0 and

@@ -40,35 +40,52 @@ __device__ __forceinline__ int kswz(int r) {
 }
 
 // bf16 keys, 64 heads x 128 dims.  Grid: (workgroups per row, rows).
-// A workgroup (4 waves) walks tiles of TE entries of one query row with a
-// stride of gridDim.x tiles. Each tile is read with fully coalesced 16-byte
-// loads (the workgroup covers contiguous 4 KiB per instruction), staged in a
-// double-buffered LDS tile with an XOR swizzle of the 16-byte chunk index
-// (kswz), and read back in the operand layout of
-// v_mfma_f32_16x16x32_bf16 with conflict-free ds_read_b128: wave w owns
-// entries TE/4 w .. TE/4 (w+1) - 1 of the tile as 16-entry N tiles, heads are
-// four 16-row M tiles. Two tiles per workgroup are in flight (a register ring)
-// while one is computed.
+// A workgroup walks tiles of TE = 64 entries of one query row with a stride
+// of gridDim.x tiles; wave w owns entries 16 w .. 16 w + 15 of each tile and
+// loads its MFMA operands straight from memory: for k-step s (dims 32 s ..
+// 32 s + 31) lane (group G, entry l16) takes the 16 bytes of dims 32 s + 8 G
+// .. + 7, so each load instruction reads 64 contiguous bytes of 16 key rows.
+// The waves never wait for each other (no LDS tile, no barrier per tile).
+// Two tiles per wave are in flight (a register ring) while one is computed;
+// heads are four 16-row M tiles of v_mfma_f32_16x16x32_bf16.
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                      const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
                      const int32_t* __restrict__ n_comp, int64_t Tq, int64_t N_max, int m,
                      float* __restrict__ scores) {
-  constexpr int KDT = DT_BF16;
   constexpr int H = 64, DI = 128, KS = 4;               // k-steps of 32
   constexpr int KROW = DI * 2;                          // bytes per key row
-  constexpr int TE = IDX_BF16_TE;                       // entries per tile
-  constexpr int NE = TE / 64;                           // 16-entry N tiles per wave
-  constexpr int TB = TE * KROW;                         // tile bytes
-  constexpr int LPT = TB / (256 * 16);                  // 16-byte loads per thread per tile
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][TB];
+  constexpr int TE = IDX_BF16_TE;                       // entries per tile (16 per wave)
+  static_assert(TE == 64, "one 16-entry N tile per wave");
   __shared__ __attribute__((aligned(16))) float lds_w[H];
 
   const int tid = threadIdx.x;
   const int l = tid & 63, wv = tid >> 6;
-  const int G = l >> 4, l16 = l & 15;  // k-group (4 x 8 dims) and column of the MFMA operands
+  const int G = l >> 4, l16 = l & 15;  // k-group (8 dims of each k-step) and entry of the MFMA operands
   const int64_t row = blockIdx.y;
   const int64_t b = row / Tq;
+  const uint8_t* kb = k_idx + b * N_max * KROW + G * 16;
+
+  u32x4_t rg[3][KS];
+  // register ring slots are compile-time indices (a runtime index would move
+  // the ring to scratch memory). Every lane loads (the entry clamped to
+  // lim - 1, lim >= 1): predicated loads would leave the number in flight
+  // path-dependent and the compiler would then wait for all of them each tile.
+  // Entries at or past lim are computed but never stored. lim is N_max for the
+  // first two tiles, which go out before the row's visible count V is known,
+  // and V after.
+  auto load = [&](auto SLOT, int64_t tile, int64_t lim) {
+    constexpr int slot = decltype(SLOT)::value;
+    const int64_t e = min(tile * TE + wv * 16 + l16, lim - 1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) rg[slot][s] = ld16(kb + e * KROW + s * 64);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  load(I0{}, blockIdx.x, N_max);
+  load(I1{}, blockIdx.x + gridDim.x, N_max);
+
   int64_t V = min((int64_t)n_comp[b], ((int64_t)q_pos[row] + 1) / m);
   V = max((int64_t)0, min(V, N_max));
   const int64_t ntiles = (V + TE - 1) / TE;
@@ -76,85 +93,59 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
   const int64_t nmine = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // tiles of this workgroup
 
   // query operand A[m = head][k]: lane (head mt*16 + l16, group G) holds dims
-  // G*32 + s*8 + 0..7 for k-step s (a fixed permutation of the 128 dims,
-  // applied identically to the keys)
+  // 32 s + 8 G .. + 7 for k-step s
   bf16x8_t qa[4][KS];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const uint16_t* qp = q_idx + (row * H + mt * 16 + l16) * DI + G * 32;
+    const uint16_t* qp = q_idx + (row * H + mt * 16 + l16) * DI + G * 8;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qa[mt][s] = as_bf16x8(ld16(qp + s * 8));
+    for (int s = 0; s < KS; ++s) qa[mt][s] = as_bf16x8(ld16(qp + s * 32));
   }
-  if (tid < H) lds_w[tid] = w[row * H + tid];  // visible after the first barrier
-  const uint8_t* kb = k_idx + b * N_max * KROW;
-  float* srow = scores + row * N_max;
-
-  u32x4_t rg[2][LPT];
-  // register ring slots and LDS buffers are compile-time indices (a runtime
-  // index would move the ring to scratch memory)
-  auto load = [&](auto SLOT, int64_t tile) {
-    constexpr int slot = decltype(SLOT)::value;
+  if (tid < H) lds_w[tid] = w[row * H + tid];
+  // wait for the query and the weights here, on every lane: left pending into
+  // the loop, these loads would make each tile wait for all loads in flight
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int o = (j * 256 + tid) * 16;  // byte offset inside the tile
-      const int64_t e = tile * TE + o / KROW;
-      rg[slot][j] = (e < V) ? ld16(kb + e * KROW + (o % KROW)) : u32x4_t{0, 0, 0, 0};
-    }
-  };
-  auto stash = [&](auto SLOT) {
-    constexpr int slot = decltype(SLOT)::value;
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      const int o = (j * 256 + tid) * 16;
-      const int r = o / KROW, c = (o % KROW) / 16;
-      *reinterpret_cast<u32x4_t*>(&lds_k[slot][r * KROW + ((c ^ kswz<KDT>(r)) * 16)]) = rg[slot][j];
-    }
-  };
+    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qa[mt][s]));
+  __syncthreads();
+  f32x4_t wr[4];  // weights of heads mt*16 + G*4 + 0..3 (accumulator rows of this lane)
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) wr[mt] = *reinterpret_cast<const f32x4_t*>(&lds_w[mt * 16 + G * 4]);
+  // scores go out through a buffer descriptor of the row's V entries: the
+  // hardware drops stores past its end, so the store needs no branch (a
+  // branch would again make the count of memory operations in flight unknown)
+  const __amdgpu_buffer_rsrc_t srow =
+      __builtin_amdgcn_make_buffer_rsrc(scores + row * N_max, (short)0, (int)(V * 4), BUF_RSRC_WORD3);
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  auto body = [&](int64_t it, auto BUF) {
-    constexpr int buf = decltype(BUF)::value;
+  // tile it is in slot it % 3; the load of tile it + 2 goes to the slot the
+  // previous tile used, so no register is both read and refilled in one step
+  auto body = [&](int64_t it, auto SLOT, auto NEXT) {
+    constexpr int slot = decltype(SLOT)::value;
     const int64_t tile = blockIdx.x + it * gridDim.x;
-    stash(BUF);
-    if (it + 2 < nmine) load(BUF, blockIdx.x + (it + 2) * gridDim.x);
-    __syncthreads();
-
-    float part[NE];
+    load(NEXT, blockIdx.x + (it + 2) * gridDim.x, V);  // past the last tile: clamped, unused
+    float part = 0.0f;
 #pragma unroll
-    for (int n = 0; n < NE; ++n) {
-      const int el = wv * (16 * NE) + n * 16 + l16;  // entry inside the tile
-      const uint8_t* kr = &lds_k[buf][el * KROW];
-      const int sw = kswz<KDT>(el);
-      bf16x8_t kbv[KS];
-      // dims G*32 + s*8 .. : chunk G*4 + s
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        kbv[s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + (((G * 4 + s) ^ sw) * 16)));
-      part[n] = 0.0f;
+      for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], as_bf16x8(rg[slot][s]), acc);
+      // accumulator row r of this lane is head mt*16 + G*4 + r
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], kbv[s], acc);
-        // accumulator row r of this lane is head mt*16 + G*4 + r
-        const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[mt * 16 + G * 4]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[n] += wv4[r] * relu_bits(acc[r]);
-      }
+      for (int r = 0; r < 4; ++r) part += wr[mt][r] * relu_bits(acc[r]);
     }
-#pragma unroll
-    for (int n = 0; n < NE; ++n) {
-      part[n] = sum_rows16(part[n]);
-      const int64_t e = tile * TE + wv * (16 * NE) + n * 16 + l16;
-      if (G == 0 && e < V) srow[e] = part[n];
-    }
+    part = sum_rows16(part);
+    const int e = (int)(tile * TE) + wv * 16 + l16;
+    // lanes of groups 1..3 hold the same sums: their offset is past the end
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow, G == 0 ? e * 4 : (int)(V * 4), 0, 0);
   };
-  load(I0{}, blockIdx.x);
-  if (nmine > 1) load(I1{}, blockIdx.x + gridDim.x);
-  for (int64_t it = 0; it < nmine; it += 2) {
-    body(it, I0{});
-    if (it + 1 < nmine) body(it + 1, I1{});
+  // whole triples and unconditional loads keep the count of memory operations
+  // in flight the same on every path, so each tile waits for its own loads
+  // only; trailing tiles past the row are computed past V and dropped
+  for (int64_t it = 0; it < nmine; it += 3) {
+    body(it, I0{}, I2{});
+    body(it + 1, I1{}, I0{});
+    body(it + 2, I2{}, I1{});
   }
 }
 
@@ -527,6 +518,7 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
     return hipGetLastError();
   }
   if (a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16) {
+    if (a.N_max == 0) return hipSuccess;  // no entries: nothing to score (the kernels load entry 0 first)
     const int64_t te = a.k_dt == DT_FP8 ? 128 : IDX_BF16_TE;
     const int64_t ntiles = (a.N_max + te - 1) / te;
     // a few workgroups per CU in total, each walking a strided run of tiles

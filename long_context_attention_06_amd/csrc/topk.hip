@@ -41,42 +41,34 @@ __device__ __forceinline__ float key_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Given counts of nb bins, find the bin b with (count above b) < need <=
-// (count of bins >= b), using wave 0 only: lane l sums the nb/64 bins
-// [nb - (l+1)*nb/64, nb - l*nb/64), one shuffle scan over lanes, and the lane
-// holding the threshold walks its bins. Result: out[0] = b, out[1] = count
-// above b. Ends with a barrier that publishes out[] and frees hist.
-__device__ __forceinline__ void find_bin_wave(const uint32_t* hist, int nb, int need, int* out) {
-  if (threadIdx.x < 64) {
-    const int l = threadIdx.x;
-    const int bpl = nb >> 6;  // 32 or 16
-    const int lo_bin = nb - (l + 1) * bpl;
-    uint32_t v[32];  // this lane's bins, ascending; kept in registers for the walk
+// Given the counts of the TK_BINS bins, find the bin b with (count above b) <
+// need <= (count of bins >= b). All threads take part: wave w scans bins
+// [TK_BINS - 128 (w+1), TK_BINS - 128 w) from the top, two per lane (one
+// inclusive scan over lanes), the waves' totals meet in tot[0..TK_NW), and
+// the lane holding the threshold publishes out[0] = b, out[1] = count above b,
+// out[2] = count of b. Ends with a barrier that publishes out[] and frees hist
+// and tot.
+__device__ __forceinline__ void find_bin_block(const uint32_t* hist, int need, int* tot, int* out) {
+  static_assert(TK_BINS == 128 * TK_NW, "two bins per lane");
+  const int t = threadIdx.x, l = t & 63, wv = t >> 6;
+  const int hi = TK_BINS - 128 * wv - 2 * l - 1;  // this lane's upper bin; the lower one is hi - 1
+  const u32x2_t c2 = *reinterpret_cast<const u32x2_t*>(hist + hi - 1);
+  const int chi = (int)c2[1], clo = (int)c2[0], own = chi + clo;
+  const int inc = wave_incl_scan_dpp(own);
+  if (l == 63) tot[wv] = inc;
+  __syncthreads();
+  int above = inc - own;  // bins above this lane's, within the wave
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const u32x4_t x = (q * 4 < bpl) ? *reinterpret_cast<const u32x4_t*>(hist + lo_bin + q * 4) : u32x4_t{0, 0, 0, 0};
+  for (int q = 0; q < TK_NW / 4; ++q) {
+    const u32x4_t t4 = *reinterpret_cast<const u32x4_t*>(tot + 4 * q);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[q * 4 + e] = x[e];
-    }
-    int loc = 0;
-#pragma unroll
-    for (int u = 0; u < 32; ++u) loc += (int)v[u];
-    const int inc = wave_incl_scan_dpp(loc);
-    const int above = inc - loc;
-    if (above < need && need <= inc) {
-      int c = above, bin = -1, cab = 0;
-#pragma unroll
-      for (int u = 31; u >= 0; --u) {  // from the highest bin of the lane down
-        const int cnt = (int)v[u];
-        if (bin < 0 && u < bpl && need <= c + cnt) {
-          bin = lo_bin + u;
-          cab = c;
-        }
-        if (u < bpl) c += cnt;
-      }
-      out[0] = bin;
-      out[1] = cab;
-    }
+    for (int e = 0; e < 4; ++e) above += 4 * q + e < wv ? (int)t4[e] : 0;
+  }
+  if (above < need && need <= above + own) {
+    const bool upper = need <= above + chi;
+    out[0] = upper ? hi : hi - 1;
+    out[1] = upper ? above : above + chi;
+    out[2] = upper ? chi : clo;
   }
   __syncthreads();
 }
@@ -203,9 +195,18 @@ __device__ void block_select(const KS& ks, int n, int K, uint32_t* hist, int* re
     }
     for (int i = 4 * n4 + t; i < n; i += TK_NT) add(ks.load1(i));
     __syncthreads();
-    find_bin_wave(h, TK_BINS, need, res);
+    find_bin_block(h, need, red, res);
     prefix = (prefix << nbits) | (uint32_t)res[0];
     need -= res[1];
+    if (need == res[2] && shift > 0) {
+      // every key of the bin is selected: the threshold is just below the
+      // bin. Its lower edge exceeds the smallest key (K < n keys lie at or
+      // above it), so it is at least 1.
+      T = (prefix << shift) - 1u;
+      need = 0;
+      __syncthreads();  // every wave has read res[] before the caller reuses it
+      return;
+    }
     if (pass == 0)  // pass 2 reuses this buffer; nothing reads it during pass 1
       for (int i = t; i < TK_BINS; i += TK_NT) h[i] = 0;
     R = shift;
@@ -252,12 +253,23 @@ __device__ void block_compact(const KS& ks, int n, int K, bool all, uint32_t T, 
   }
   __syncthreads();
   int eq_before = 0, sel_before = 0;
+  {
+    int gs[TK_NW], es[TK_NW];
 #pragma unroll
-  for (int u = 0; u < TK_NW; ++u) {
-    const int gu = red[u], eu = red[TK_NW + u];
-    if (u < wv) {
-      sel_before += gu + (all ? 0 : max(0, min(need - eq_before, eu)));
-      eq_before += eu;
+    for (int q = 0; q < TK_NW / 4; ++q) {
+      const u32x4_t g4 = *reinterpret_cast<const u32x4_t*>(red + 4 * q);
+      const u32x4_t e4 = *reinterpret_cast<const u32x4_t*>(red + TK_NW + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gs[4 * q + e] = (int)g4[e];
+        es[4 * q + e] = (int)e4[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TK_NW; ++u) {
+      const bool before = u < wv;
+      sel_before += before ? gs[u] + (all ? 0 : max(0, min(need - eq_before, es[u]))) : 0;
+      eq_before += before ? es[u] : 0;
     }
   }
   // popcount of the mask's bits below this lane (v_mbcnt_lo/hi)
@@ -425,7 +437,7 @@ __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
 //    top K'.
 __global__ void __launch_bounds__(TK_NT) topk_threshold_kernel(TopkArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[2 * TK_BINS];
-  __shared__ int red[32], res[32];
+  __shared__ __attribute__((aligned(16))) int red[32], res[32];
   __shared__ __attribute__((aligned(16))) uint32_t kc[TK_SAMPLE];
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x;

@@ -355,6 +355,68 @@ def test_sparse_prefill(H, k, N, with_sink):
         assert np.abs(LS[t] - rlse).max() < 1e-3
 
 
+def test_prefill_equals_decode():
+    """The prefill output of the query at position p equals a decode step over
+    the same selected entries whose window buffer holds tokens
+    max(0, p-W+1) .. p. The two calls run different kernels (the decode one
+    in row splits plus a combine), so they agree up to rounding order and the
+    bf16 rounding of the weights."""
+    _say("prefill == decode")
+    g = _g(40)
+    Tq, H, D, N, T_tok, k, W = 24, 64, 512, 900, 1500, 400, 128
+    q = gen.bf16_round(g.standard_normal((Tq, H, D)).astype(np.float32) / math.sqrt(D))
+    kv = gen.bf16_round(g.standard_normal((N, D)).astype(np.float32))
+    tok = gen.bf16_round(g.standard_normal((T_tok, D)).astype(np.float32))
+    pos = np.sort(g.integers(0, T_tok, Tq)).astype(np.int32)
+    pos[0], pos[1], pos[-1] = 0, 5, T_tok - 1  # windows of 1 and 6 tokens, and a full one
+    idx = np.sort(g.choice(N, size=(Tq, k)), axis=1).astype(np.int32)
+    idx[2, 100:] = -1
+    sink = g.standard_normal(H).astype(np.float32)
+    out_p = torch.empty((Tq, H, D), device=DEV)
+    lse_p = torch.empty((Tq, H), device=DEV)
+    L.sparse_mqa_prefill(bf(q), bf(kv), dev(idx), bf(tok), dev(pos), dev(sink), out_p, lse_p, W=W)
+    win = np.zeros((Tq, W, D), np.float32)
+    win_len = np.minimum(W, pos + 1).astype(np.int32)
+    for t in range(Tq):
+        win[t, :win_len[t]] = tok[pos[t] - win_len[t] + 1:pos[t] + 1]
+    out_d = torch.empty((Tq, H, D), device=DEV)
+    lse_d = torch.empty((Tq, H), device=DEV)
+    L.sparse_mqa_decode(bf(q), bf(np.broadcast_to(kv, (Tq, N, D)).copy()), dev(idx), bf(win), dev(win_len),
+                        dev(sink), out_d, lse_d)
+    torch.cuda.synchronize()
+    Op, Od, Lp, Ld = host(out_p), host(out_d), host(lse_p), host(lse_d)
+    for t in range(Tq):
+        check_out(Op[t], Od[t].astype(np.float64), _attn_tight(Od[t]), f"prefill vs decode t={t}")
+    assert np.abs(Lp - Ld).max() < 1e-4
+
+
+def test_sparse_all_entries_equals_hca():
+    """Selecting every visible entry makes the sparse decode a dense one: its
+    output equals hca_dense_mqa over the same entries, window and sink (two
+    row sources and split plans, equal up to rounding order)."""
+    _say("sparse(all) == hca")
+    g = _g(41)
+    B, H, D, N, W, m = 3, 64, 512, 1000, 128, 128
+    q = gen.bf16_round(g.standard_normal((B, H, D)).astype(np.float32) / math.sqrt(D))
+    kv = gen.bf16_round(g.standard_normal((B, N, D)).astype(np.float32))
+    win = gen.bf16_round(g.standard_normal((B, W, D)).astype(np.float32))
+    win_len = np.array([W, 37, 0], np.int32)
+    sink = g.standard_normal(H).astype(np.float32)
+    idx = np.broadcast_to(np.arange(N, dtype=np.int32), (B, N)).copy()
+    out_s = torch.empty((B, H, D), device=DEV)
+    lse_s = torch.empty((B, H), device=DEV)
+    L.sparse_mqa_decode(bf(q), bf(kv), dev(idx), bf(win), dev(win_len), dev(sink), out_s, lse_s)
+    out_h = torch.empty((B, H, D), device=DEV)
+    lse_h = torch.empty((B, H), device=DEV)
+    L.hca_dense_mqa(bf(q), bf(kv), dev(np.full(B, N, np.int32)), dev(np.full(B, N * m - 1, np.int32)), bf(win),
+                    dev(win_len), dev(sink), out_h, lse_h, m=m)
+    torch.cuda.synchronize()
+    Os, Oh = host(out_s), host(out_h)
+    for b in range(B):
+        check_out(Os[b], Oh[b].astype(np.float64), _attn_tight(Oh[b]), f"sparse(all) vs hca b={b}")
+    assert np.abs(host(lse_s) - host(lse_h)).max() < 1e-4
+
+
 # ------------------------------------------------------------------ whole paths
 
 def test_tiny_csa_pipeline_c1():

@@ -336,7 +336,7 @@ def bench_prefill(a, torch, L, gen, dev):
                    "window": W},
         "prefill_tflops": round(total_fl / (ms * 1e-3) / 1e12, 2),
         "algorithmic_tflop": round(total_fl / 1e12, 3),
-        "roofline": {"bound": "mfma", "kernel": "attn_pre32_kernel (sparse prefill)", "achieved": round(mqa_tfs, 1),
+        "roofline": {"bound": "mfma", "kernel": "attn_prs_kernel (sparse prefill)", "achieved": round(mqa_tfs, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mqa_tfs / BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flops_all_launches": mqa_fl,
                      "avg_launch_ms": round(float(np.mean(attn_ms)), 4)},

@@ -468,69 +468,94 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
 }
 
 // ----------------------------------------------------------------------------
-// bf16 prefill: four waves of 32 heads on v_mfma_f32_32x32x16_bf16
+// bf16 prefill helpers
 // ----------------------------------------------------------------------------
-//
-// In prefill the rows of every query are gathered once and the tile work is
-// bound by LDS reads. With 16-head waves each K and V byte of a tile is read
-// by four waves; here wave w owns heads 32 (w%2) .. +31 and dims 256 (w/2)
-// .. +255, so each byte is read by two. S^T (32 rows x 32 heads) comes from
-// v_mfma_f32_32x32x16_bf16 over the wave's 256 dims; the pair of waves sharing
-// heads swaps partials through LDS as in attn_bf16_kernel. In the S^T
-// accumulator a lane holds one head for 16 rows; registers 8 ks .. 8 ks + 7
-// are the P operand of k-step ks of O += P R in the K order
-//   position 8 h + j  <->  row (2 ks + j/4) 8 + 4 h + j%4      (h = lane / 32),
-// and the R operand of that k-step is two transpose reads of four consecutive
-// rows. O (32 heads x 256 dims, 128 registers) lives in accumulation
-// registers. One wave per SIMD; rows arrive by DMA as in attn_bf16_kernel
-// (eight per wave per tile).
 
-// Chunk swizzle of the 32-head kernel (16-byte chunks; 64 banks of 4 bytes
+// Chunk swizzle of the prefill tiles (16-byte chunks; 64 banks of 4 bytes
 // span 16 chunks): a 4-bit rotation of the row. Any 16 consecutive rows put
 // one chunk in 16 distinct bank groups (the K reads of the QK chain), and the
 // four rows 4i .. 4i+3 differ in the high bits, so a half-wave of transposed V
 // reads (four rows x four aligned chunks) also covers all 64 banks once.
 __device__ __forceinline__ int swz4(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-namespace p32 {
-constexpr int D = 512, ROWB = 1024, TR = 32, NW = 4, NT = 256, NBUF = 4;
-constexpr int TILEB = TR * ROWB;
-constexpr int RPW = TR / NW;     // rows each wave loads per tile
-constexpr int TAB_MAX = 2048;
-}  // namespace p32
-
 __device__ __forceinline__ f32x16_t mfma32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// ----------------------------------------------------------------------------
+// bf16 prefill, rows split between the two waves of a head group
+// ----------------------------------------------------------------------------
+//
+// Four waves, one per SIMD; wave w owns heads 32 (w%2) .. +31. For S the two
+// waves of a head group split each 32-row tile: wave w computes S over all 512
+// dims for rows 16 (w/2) .. +15 on v_mfma_f32_16x16x32_bf16 (Q^T of its 32
+// heads, 128 registers, waits in accumulation registers). For O they split
+// the dims: wave w accumulates O^T for dims 256 (w/2) .. +255 over all 32 rows
+// on v_mfma_f32_32x32x16_bf16 (O^T in accumulation registers: a lane holds
+// one head, so a rescale uses the lane's own factor and the epilogue packs 8
+// consecutive dims per lane). The waves meet through P^T in LDS (bf16, [head][row],
+// double-buffered by tile parity), so a tile needs one barrier.
+//
+// P of a tile is taken against the exponent reference the pair agreed on at
+// the previous tile, which both waves hold without talking to each other. The
+// fp32/bf16 range leaves room for that: P is allowed up to 2^GUARD. A tile
+// with a logit more than GUARD above the reference (in particular the first
+// tile with a finite logit) takes the slow path: the pair exchanges exact
+// per-head maxima, moves the reference, rescales O and the running sums, and
+// recomputes P.
+//
+// Software pipeline (iteration t): the QK products of tile t+1 are issued with
+// the K reads of tile t+1 and the transposed V reads of tile t, then O += P V
+// of tile t runs with the softmax of tile t+1 in the shadow of its products.
+// One barrier per tile then covers the P^T exchange and the DMA ring.
+
+namespace prs {
+constexpr int D = 512, ROWB = 1024, TR = 32, NW = 4, NT = 256, NBUF = 4;
+constexpr int TILEB = TR * ROWB;
+constexpr int RPW = TR / NW;     // rows each wave gathers per tile
+constexpr int TAB_MAX = 2048;
+constexpr int PSTR = 40;         // bf16 per head row of a P^T buffer: 32 rows + 16 bytes of padding
+constexpr float GUARD = 64.0f;   // log2 units a logit may sit above the shared reference
+}  // namespace prs
+
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __restrict__ q_pos,
-                  const float* __restrict__ sink, float scale_log2, int H, int slots,
-                  void* __restrict__ out, float* __restrict__ lse, int out_dt) {
-  using namespace p32;
+attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __restrict__ q_pos,
+                const float* __restrict__ sink, float scale_log2, int H, int slots, void* __restrict__ out,
+                float* __restrict__ lse, int out_dt) {
+  using namespace prs;
   constexpr int SRC = SRC_SPARSE_PRE;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TILEB];
-  __shared__ __attribute__((aligned(16))) f32x4_t xchg[NW][4][64];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][2][32 * PSTR];  // [tile parity][head group] P^T
+  __shared__ __attribute__((aligned(16))) float lmx[2][2][2][64];          // [head group][row half][hq][lane]
+  __shared__ __attribute__((aligned(16))) int flg[2][NW];                  // [tile parity][wave]: P must be redone
   __shared__ __attribute__((aligned(16))) int tab[TAB_MAX];
   __shared__ int cnt[2 * NW];
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = l >> 5, l32 = l & 31;
+  const int h = l >> 5, l32 = l & 31, g16 = l >> 4, l16 = l & 15;
   const int hg = w & 1, dh = w >> 1;
   const int64_t qi = blockIdx.x;
-  const int head = hg * 32 + l32;  // this lane's head in S^T / P / softmax
+  // S / softmax layout: lane holds tile rows 16 dh + 4 g16 + i (i < 4) of heads
+  // 32 hg + 16 hq + l16 (hq < 2). O^T layout: lane holds head 32 hg + l32 = the
+  // softmax head of hq = (l >> 4) & 1, dims 256 dh + 32 nt + 8 (r/4) + 4 h + r%4.
+  const int ohq = (l >> 4) & 1;
 
   QRows rr = query_rows<SRC>(src, nullptr, nullptr, q_pos, 1, qi, 0, slots, slots);
 
-  // ---- Q^T operand (B of S^T = R Q^T): lane (head, h), dims 256 dh + 16 s + 8 h .. +7
-  bf16x8_t qb[16];
-  {
-    const bool hok = head < H;
-    const uint16_t* qp = q + (qi * H + (hok ? head : 0)) * (int64_t)D + dh * 256 + h * 8;
+  // ---- Q^T operand (B of S = K Q^T): head 32 hg + 16 hq + l16, dims 32 ks + 8 gc
+  // .. +7 with gc = the two bits of g16 swapped (the K operand takes the same
+  // dims; the order only decides which 16-byte chunk each lane group reads)
+  const int gc = ((g16 & 1) << 1) | (g16 >> 1);
+  bf16x8_t qb[2][16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qb[s] = as_bf16x8(hok ? ld16(qp + s * 16) : u32x4_t{0, 0, 0, 0});
+  for (int hq = 0; hq < 2; ++hq) {
+    const int head = 32 * hg + 16 * hq + l16;
+    const bool hok = head < H;
+    const uint16_t* qp = q + (qi * H + (hok ? head : 0)) * (int64_t)D + 8 * gc;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qb[hq][ks] = as_bf16x8(hok ? ld16(qp + 32 * ks) : u32x4_t{0, 0, 0, 0});
   }
 
   int n_comp_rows = 0;
@@ -571,78 +596,160 @@ attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __r
     }
   };
 
+  // Q^T waits in accumulation registers (MFMA reads its A/B operands from
+  // either file), leaving the VGPRs to the reads in flight
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq)
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(qb[hq][ks]));
+
   f32x16_t o[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[nt][r] = 0.0f;
-  float m_ref = -INFINITY, l_run = 0.0f;
+  // per softmax head hq: exponent reference (log2 units), the raw score above
+  // which a logit exceeds it by GUARD, and the running sum of this lane's P
+  float m_ref[2] = {-INFINITY, -INFINITY}, thr[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
 
-  // QK A operand: row l32, dims 256 dh + 16 s + 8 h -> chunk 32 dh + 2 s + h
-  //   = 32 dh + 16 (s / 8) + ((2 (s % 8) + h) ^ swz4(row))
-  int qofs[8];
+  // K operand (A of the 16x16x32 products): row 16 dh + l16, dims 32 ks + 8 gc
+  //   -> chunk 4 ks + gc = 16 (ks / 4) + ((4 (ks % 4) + gc) ^ swz4(row)).
+  // A b128 read is served in passes of lanes that share lane bits 2 and 4 (as
+  // measured: eight rows x two lane groups); with gc those two groups differ
+  // in chunk bit 0, which the rotation of the eight rows leaves fixed, so the
+  // sixteen chunks of a pass fall in sixteen distinct bank groups
+  int kofs[4];
+  {
+    const int row = 16 * dh + l16;
 #pragma unroll
-  for (int v = 0; v < 8; ++v) qofs[v] = l32 * ROWB + (((2 * v + h) ^ swz4(l32)) * 16) + dh * 512;
-  // PV R operand (transpose read): 16-lane group g = l / 16 takes rows
-  // k0 .. k0+3 (k0 = 16 ks + 4 h, +8 for the second read) and columns
-  // n0 .. n0+15 (n0 = 256 dh + 32 nt + 16 (g % 2)); lane j of the group
-  // supplies row k0 + j/4, column n0 + 4 (j%4): chunk 32 dh + 4 nt + 2 (g%2) + (j%4)/2
+    for (int v = 0; v < 4; ++v) kofs[v] = row * ROWB + (((4 * v + gc) ^ swz4(row)) * 16);
+  }
+  // V^T operand (transpose reads, rows in natural order): 16-lane group g16
+  // takes rows k0 .. k0+3 (k0 = 16 ks + 8 h, +4 for the second read) and
+  // columns n0 .. n0+15 (n0 = 256 dh + 32 nt + 16 (g16 % 2)); lane j = l16
+  // supplies row k0 + j/4, columns n0 + 4 (j%4) .. +3, so lane l receives dim
+  // n0 + j of rows k0 .. k0+3: chunk 32 dh + 4 nt + 2 (g16%2) + (j%4)/2
   int pofs[2][2][4];  // [ks][first/second read][nt % 4], plus 256 bytes for nt >= 4
   {
-    const int g = l >> 4, j = l & 15;
-    const int cl = 2 * (g & 1) + ((j & 3) >> 1), cb = (j & 1) * 8;
+    const int cl = 2 * (g16 & 1) + ((l16 & 3) >> 1), cb = (l16 & 1) * 8;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int rd = 0; rd < 2; ++rd) {
-        const int row = 16 * ks + 4 * h + 8 * rd + (j >> 2);
+        const int row = 16 * ks + 8 * h + 4 * rd + (l16 >> 2);
 #pragma unroll
         for (int u = 0; u < 4; ++u) pofs[ks][rd][u] = row * ROWB + (((4 * u + cl) ^ swz4(row)) * 16) + cb + dh * 512;
       }
   }
+  // P^T operand (B of O^T += V^T P^T): head l32, rows 16 ks + 8 h .. +7
+  const int prd = l32 * PSTR + 8 * h;
+  // P^T write: this lane's four rows 16 dh + 4 g16 .. +3 of head 16 hq + l16
+  const int pwr = l16 * PSTR + 16 * dh + 4 * g16;
 
-  // Q^T waits in accumulation registers (MFMA reads its A/B operands from
-  // either file), leaving the VGPRs to the reads in flight
+  auto k_reads = [&](const uint8_t* RK, u32x4_t* kr) {
 #pragma unroll
-  for (int s = 0; s < 16; ++s) asm volatile("" : "+a"(qb[s]));
-
-  // Software pipeline. With one wave per SIMD nothing else hides latency, so
-  // each wave overlaps its own phases: iteration t runs the softmax of tile t
-  // while the QK chain of tile t+1 is in the matrix core, then O += P V of
-  // tile t while the partial S of tile t+1 is swapped with the other dim half.
-  // At the top of iteration t tiles t and t+1 are resident and sv holds the
-  // full S of tile t. On the last tile the QK chain reads a stale slot and its
-  // result is dropped.
-  auto qk_reads = [&](const uint8_t* RK, u32x4_t* kr) {
-#pragma unroll
-    for (int s = 0; s < 16; ++s) kr[s] = *reinterpret_cast<const u32x4_t*>(RK + qofs[s & 7] + (s >> 3) * 256);
+    for (int ks = 0; ks < 16; ++ks) kr[ks] = *reinterpret_cast<const u32x4_t*>(RK + kofs[ks & 3] + (ks >> 2) * 256);
   };
-  auto qk_chain = [&](const u32x4_t* kr) {
-    f32x16_t sp;
+  auto qk = [&](const u32x4_t* kr, f32x4_t* s) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sp[r] = 0.0f;
+    for (int hq = 0; hq < 2; ++hq) s[hq] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // the two heads' chains alternate, so each product finds the previous one
+    // of its chain finished (MFMAs stay in this order; everything else moves)
 #pragma unroll
-    for (int s = 0; s < 16; ++s) sp = mfma32x16(as_bf16x8(kr[s]), qb[s], sp);
-    return sp;
-  };
-  auto put_partial = [&](const f32x16_t& sp) {
+    for (int ks = 0; ks < 16; ++ks) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xchg[w][k][l] = f32x4_t{sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
-  };
-  auto add_partner = [&](const f32x16_t& sp) {
-    f32x16_t sv;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const f32x4_t x = xchg[w ^ 2][k][l];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sv[4 * k + e] = sp[4 * k + e] + x[e];
+      for (int hq = 0; hq < 2; ++hq) s[hq] = mfma16(as_bf16x8(kr[ks]), qb[hq][ks], s[hq]);
+      __builtin_amdgcn_sched_barrier(0x7F6);
     }
-    return sv;
+  };
+  // padding rows of the last tile (every row of a tile past it) leave the
+  // softmax; branch-free, so it schedules with the products around it
+  auto mask_tail = [&](f32x4_t* s, int u) {
+    const int nvalid = n_rows - u * TR;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool pad = 16 * dh + 4 * g16 + i >= nvalid;
+      s[0][i] = pad ? -INFINITY : s[0][i];
+      s[1][i] = pad ? -INFINITY : s[1][i];
+    }
+  };
+  // P of tile u against the current reference: written to P^T buffer `buf`,
+  // summed into l_run; returns whether a logit exceeds the reference by GUARD
+  auto softmax = [&](const f32x4_t* s, int buf) {
+    bool over = false;
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+      const float mr = m_ref[hq] == -INFINITY ? 0.0f : m_ref[hq];
+      const float mx = fmaxf(fmaxf(s[hq][0], s[hq][1]), fmaxf(s[hq][2], s[hq][3]));
+      over |= mx > thr[hq];
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hq][i], scale_log2, -mr));
+        l_run[hq] += p[i];  // fp32 weights: the log-sum-exp keeps fp32 accuracy
+      }
+      *reinterpret_cast<u32x2_t*>(&pbuf[buf][hg][pwr + 16 * hq * PSTR]) =
+          u32x2_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    }
+    return over;
+  };
+  // the pair agrees on exact per-head maxima of tile u, moves the reference,
+  // rescales O and the sums, and redoes P (all four waves take this path)
+  auto slow = [&](const f32x4_t* s, int buf, const float* l_prev) {
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq)
+      lmx[hg][dh][hq][l] = fmaxf(fmaxf(s[hq][0], s[hq][1]), fmaxf(s[hq][2], s[hq][3]));
+    vm_barrier<63>();
+    float alpha[2];
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+      float tm = -INFINITY;
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) tm = fmaxf(tm, lmx[hg][d][hq][16 * gg + l16]);
+      tm *= scale_log2;
+      const float m_new = fmaxf(m_ref[hq], tm);
+      alpha[hq] = m_ref[hq] == -INFINITY ? 0.0f : (m_new == m_ref[hq] ? 1.0f : __builtin_amdgcn_exp2f(m_ref[hq] - m_new));
+      l_run[hq] = l_prev[hq] * alpha[hq];
+      m_ref[hq] = m_new;
+      thr[hq] = m_new == -INFINITY ? -INFINITY : (m_new + GUARD) / scale_log2;
+    }
+    const float ao = ohq ? alpha[1] : alpha[0];
+    if (__any(ao != 1.0f)) {
+      // every O^T register of this lane belongs to its own head
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // scaled where it lives: a plain multiply would make the compiler keep
+          // a VGPR copy of all of O
+          float tmp;
+          asm volatile(
+              "v_accvgpr_read_b32 %1, %0\n\t"
+              "v_mul_f32 %1, %1, %2\n\t"
+              "v_accvgpr_write_b32 %0, %1"
+              : "+a"(o[nt][r]), "=&v"(tmp)
+              : "v"(ao));
+        }
+    }
+    softmax(s, buf);  // cannot exceed the new reference
+    vm_barrier<63>();
+  };
+  auto post_flag = [&](bool over, int buf) {
+    const bool any = __any(over);
+    if (l == 0) flg[buf][w] = any ? 1 : 0;
+  };
+  auto flags_set = [&](int buf) {
+    const u32x4_t f = *reinterpret_cast<const u32x4_t*>(&flg[buf][0]);
+    return __builtin_amdgcn_readfirstlane(f[0] | f[1] | f[2] | f[3]) != 0;
+  };
+  auto p_reads = [&](int buf, u32x4_t* pc) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pc[ks] = *reinterpret_cast<const u32x4_t*>(&pbuf[buf][hg][prd + 16 * ks]);
   };
 
-  f32x16_t sv;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sv[r] = 0.0f;
+  u32x4_t pcur[2] = {u32x4_t{0, 0, 0, 0}, u32x4_t{0, 0, 0, 0}};  // P^T operand of the tile in hand
   for (int t = 0; t < ntiles && t < NBUF - 1; ++t) issue(t);
   if (ntiles > 0) {
     if (ntiles > 2)
@@ -650,126 +757,107 @@ attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __r
     else
       vm_barrier<0>();
     u32x4_t kr[16];
-    qk_reads(ring, kr);
-    const f32x16_t sp = qk_chain(kr);
-    put_partial(sp);
+    k_reads(ring, kr);
+    f32x4_t s[2];
+    qk(kr, s);
+    mask_tail(s, 0);
+    const float l_prev[2] = {l_run[0], l_run[1]};
+    post_flag(softmax(s, 0), 0);
     vm_barrier<63>();
-    sv = add_partner(sp);
+    if (flags_set(0)) slow(s, 0, l_prev);
+    p_reads(0, pcur);
   }
   for (int t = 0; t < ntiles; ++t) {
-    if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);  // the slot of tile t-1, free since the last barrier
+    const bool iss = t + NBUF - 1 < ntiles, nxt = t + 1 < ntiles;
+    if (iss) issue(t + NBUF - 1);  // the slot of tile t-1, free since the last barrier
     const uint8_t* R = ring + (t & (NBUF - 1)) * TILEB;
     const uint8_t* RN = ring + ((t + 1) & (NBUF - 1)) * TILEB;
-    u32x4_t kr[16];
-    qk_reads(RN, kr);
 
-    // ---- softmax of `head` over this lane's 16 rows (r/4) 8 + 4 h + r%4, exp2
-    // domain. The scale is positive, so the max is taken on the raw scores and
-    // the scaling folds into the exponent's FMA.
-    if (t == ntiles - 1) {  // only the last tile holds padding rows
-      const int nvalid = n_rows - t * TR;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if ((r >> 2) * 8 + 4 * h + (r & 3) >= nvalid) sv[r] = -INFINITY;
-    }
-    float lm = sv[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) lm = fmaxf(lm, sv[r]);
-    lm *= scale_log2;
-    if (__builtin_expect(__any(lm > m_ref + RESCALE_SLACK), 0)) {
-      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm), __float_as_uint(lm), false, false);
-      const float tmax = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));  // over both lane halves
-      const float m_new = tmax > m_ref + RESCALE_SLACK ? tmax : m_ref;
-      const float alpha = (m_new == m_ref) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_run *= alpha;
-      m_ref = m_new;
-      // every O^T register of this lane belongs to its own head
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // scaled where it lives: a plain multiply would make the compiler keep
-          // a VGPR copy of all of O on every tile
-          float tmp;
-          asm volatile(
-              "v_accvgpr_read_b32 %1, %0\n\t"
-              "v_mul_f32 %1, %1, %2\n\t"
-              "v_accvgpr_write_b32 %0, %1"
-              : "+a"(o[nt][r]), "=&v"(tmp)
-              : "v"(alpha));
-        }
-    }
-    const float mr = (m_ref == -INFINITY) ? 0.0f : m_ref;
-
-    // ---- QK chain of tile t+1, with the exponentials of tile t between its MFMAs
-    const f32x16_t sp = qk_chain(kr);
-    float pv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], scale_log2, -mr));
-      l_run += pv[r];  // fp32 weights: the log-sum-exp keeps fp32 accuracy
-    }
-    bf16x8_t pa[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      pa[ks] = as_bf16x8(u32x4_t{pack_bf16x2(pv[8 * ks], pv[8 * ks + 1]), pack_bf16x2(pv[8 * ks + 2], pv[8 * ks + 3]),
-                                 pack_bf16x2(pv[8 * ks + 4], pv[8 * ks + 5]), pack_bf16x2(pv[8 * ks + 6], pv[8 * ks + 7])});
-
-    // ---- O^T += R^T P^T of tile t over this wave's 256 dims: 8 N-tiles of 32
-    // dims, 2 k-steps of 16 rows. The operands are those of O = P R with A and
-    // B exchanged, so the accumulator holds O transposed: register r of N-tile
-    // nt is dim 32 nt + (r/4) 8 + 4 h + r%4 of this lane's head.
+    // ---- S of tile t+1 and the transposed V reads of tile t, in a fixed
+    // order: each k-step issues the K read four steps ahead and two V reads,
+    // then its two products (the heads' chains alternate). The reads stay
+    // spread over the products instead of queueing in one burst. On the last
+    // tile the products read a stale slot and their result is dropped.
+    auto k_read = [&](int ks) {
+      return *reinterpret_cast<const u32x4_t*>(RN + kofs[ks & 3] + (ks >> 2) * 256);
+    };
     s16x4_t vr[8][2][2];  // [nt][ks][first/second four rows]
+    auto v_read = [&](int i) {  // i = 4 nt + 2 ks + rd
+      const int nt = i >> 2, ks = (i >> 1) & 1, rd = i & 1;
+      vr[nt][ks][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (s16x4_t __attribute__((address_space(3)))*)(R + pofs[ks][rd][nt & 3] + (nt >> 2) * 256));
+    };
+    u32x4_t kr[16];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int ks = 0; ks < 4; ++ks) kr[ks] = k_read(ks);
+    f32x4_t s[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 16; ++ks) {
+      if (ks + 4 < 16) kr[ks + 4] = k_read(ks + 4);
+      v_read(2 * ks);
+      v_read(2 * ks + 1);
 #pragma unroll
-        for (int rd = 0; rd < 2; ++rd)
-          vr[nt][ks][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (s16x4_t __attribute__((address_space(3)))*)(R + pofs[ks][rd][nt & 3] + (nt >> 2) * 256));
-    // issue order: each QK MFMA followed by two of the V reads and four VALU
-    // (exponentials of tile t); the PV chain then finds its operands in registers
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      for (int hq = 0; hq < 2; ++hq) s[hq] = mfma16(as_bf16x8(kr[ks]), qb[hq][ks], s[hq]);
+      __builtin_amdgcn_sched_barrier(0x006);  // only VALU / SALU work moves across
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- tile t+1's partial S goes out (once the partner has read the previous
-    // one), then the PV chain runs while the partials are swapped
-    vm_barrier<63>();
-    put_partial(sp);
+    // ---- O^T += V^T P^T of tile t over this wave's 256 dims: 8 N-tiles of 32
+    // dims, 2 k-steps of 16 rows; the softmax of tile t+1 runs between them
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8_t bv = __builtin_bit_cast(
             bf16x8_t, __builtin_shufflevector(vr[nt][ks][0], vr[nt][ks][1], 0, 1, 2, 3, 4, 5, 6, 7));
-        o[nt] = mfma32x16(bv, pa[ks], o[nt]);
+        o[nt] = mfma32x16(bv, as_bf16x8(pcur[ks]), o[nt]);
       }
-    if (t + NBUF - 1 < ntiles)
-      vm_barrier<RPW>();  // tile t+2 resident, tile t+3 may be in flight
+    // (on the last tile this works on the stale S: its P^T and flag are never
+    // read and the sums are restored below)
+    const float l_prev[2] = {l_run[0], l_run[1]};
+    mask_tail(s, t + 1);
+    post_flag(softmax(s, (t + 1) & 1), (t + 1) & 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // P^T of tile t+1 written, tile t+2 resident (tile t+3 may be in flight),
+    // tile t's reads done
+    if (iss)
+      vm_barrier<RPW>();
     else
       vm_barrier<0>();
-    sv = add_partner(sp);
+    if (nxt) {
+      if (flags_set((t + 1) & 1)) slow(s, (t + 1) & 1, l_prev);
+      p_reads((t + 1) & 1, pcur);
+    } else {
+      l_run[0] = l_prev[0];
+      l_run[1] = l_prev[1];
+    }
   }
 
-  // ---- epilogue: this lane's head is 32 hg + l32; register r of N-tile nt is
-  // dim 256 dh + 32 nt + (r/4) 8 + 4 h + r%4
-  {
-    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-    l_run = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-  }
+  // ---- epilogue: l of each head over both row halves and the four row groups
+  // of a lane's head (lmx is free: the last reads of it preceded a barrier)
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq) lmx[hg][dh][hq][l] = l_run[hq];
+  vm_barrier<63>();
+  float lsum = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) lsum += lmx[hg][d][ohq][16 * gg + l16];
+  const int head = hg * 32 + l32;
   const bool hok = head < H;
+  const float mo = ohq ? m_ref[1] : m_ref[0];
   const float s2 = (sink && hok) ? sink[head] * LOG2E_F : -INFINITY;
-  const float M = fmaxf(m_ref, s2);
+  const float M = fmaxf(mo, s2);
   float fac = 0.0f;
   if (M != -INFINITY) {
-    const float a = exp2f(m_ref - M);
-    fac = a / (l_run * a + exp2f(s2 - M));
+    const float a = exp2f(mo - M);
+    fac = a / (lsum * a + exp2f(s2 - M));
   }
   const int64_t orow = (qi * H + (hok ? head : 0)) * (int64_t)D + dh * 256;
   if (out_dt == DT_BF16) {
@@ -785,9 +873,9 @@ attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __r
         const uint32_t x1 = pack_bf16x2(o[nt][r0 + 2] * fac, o[nt][r0 + 3] * fac);
         const uint32_t y0 = pack_bf16x2(o[nt][r0 + 4] * fac, o[nt][r0 + 5] * fac);
         const uint32_t y1 = pack_bf16x2(o[nt][r0 + 6] * fac, o[nt][r0 + 7] * fac);
-        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-        if (hok) *reinterpret_cast<u32x4_t*>(op + nt * 32 + p * 16) = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+        const auto sa = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto sb = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        if (hok) *reinterpret_cast<u32x4_t*>(op + nt * 32 + p * 16) = u32x4_t{sa[0], sb[0], sa[1], sb[1]};
       }
   } else if (hok) {
     float* op = reinterpret_cast<float*>(out) + orow + 4 * h;
@@ -800,7 +888,7 @@ attn_pre32_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __r
   }
   if (lse && dh == 0 && h == 0 && hok) {
     float v = -INFINITY;
-    if (M != -INFINITY) v = (M + log2f(l_run * exp2f(m_ref - M) + exp2f(s2 - M))) * LN2_F;
+    if (M != -INFINITY) v = (M + log2f(lsum * exp2f(mo - M) + exp2f(s2 - M))) * LN2_F;
     lse[qi * H + head] = v;
   }
 }
@@ -1191,8 +1279,8 @@ static hipError_t launch_bf16(const AttnLaunch& a, hipStream_t st) {
 }
 
 static hipError_t launch_pre32(const AttnLaunch& a, hipStream_t st) {
-  if (a.nsplit != 1 || a.slots > p32::TAB_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_pre32_kernel, dim3((unsigned)a.nq), dim3(p32::NT), 0, st,
+  if (a.nsplit != 1 || a.slots > prs::TAB_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_prs_kernel, dim3((unsigned)a.nq), dim3(prs::NT), 0, st,
                      reinterpret_cast<const uint16_t*>(a.q), row_src(a), a.q_pos, a.sink, a.scale * LOG2E_F, a.H,
                      a.slots, a.out, a.lse, a.out_dt);
   return hipGetLastError();

@@ -355,6 +355,50 @@ def test_sparse_prefill(H, k, N, with_sink):
         assert np.abs(LS[t] - rlse).max() < 1e-3
 
 
+def test_sparse_prefill_reference_moves():
+    """Logits that jump far above everything earlier in a query (more than the
+    2^64 headroom P has against the exponent reference the kernel carries from
+    tile to tile), queries whose first tiles hold only invalid slots, and one
+    whose only top-k row comes after nine fully invalid tiles. The kernel must
+    move its reference mid-query and rescale what it has accumulated; the
+    oracle is exact softmax over the valid rows."""
+    _say("sparse_prefill", "reference moves")
+    g = _g(45)
+    Tq, H, D, N, T_tok, k, W = 6, 64, 512, 700, 900, 320, 128
+    q = gen.bf16_round(g.standard_normal((Tq, H, D)).astype(np.float32) / math.sqrt(D))
+    kv = gen.bf16_round(g.standard_normal((N, D)).astype(np.float32))
+    tok = gen.bf16_round(g.standard_normal((T_tok, D)).astype(np.float32))
+    pos = np.sort(g.integers(300, T_tok, Tq)).astype(np.int32)
+    n_free = N - 3 * Tq  # the last entries hold rows aligned with one query each
+    idx = np.stack([g.choice(n_free, size=k, replace=False) for _ in range(Tq)]).astype(np.int32)
+    jumps = [(150, 480.0), (151, 480.0), (290, 1000.0)]  # (slot, c): logits of about c / 8 nats
+    for t in range(Tq):
+        u = q[t].astype(np.float64).sum(0)
+        u /= np.linalg.norm(u)
+        for j, (slot, c) in enumerate(jumps):
+            e = n_free + 3 * t + j
+            kv[e] = gen.bf16_round((c * (0.5 + 0.25 * t) * u).astype(np.float32))
+            idx[t, slot] = e
+    idx[2, :96] = -1  # three invalid tiles first
+    idx[5, :] = -1
+    idx[5, 300] = n_free + 3 * 5 + 2  # nine invalid tiles, then one row, then the window
+    kv[idx[5, 300]] = gen.bf16_round((600.0 * q[5].astype(np.float64).sum(0) /
+                                      np.linalg.norm(q[5].astype(np.float64).sum(0))).astype(np.float32))
+    sink = g.standard_normal(H).astype(np.float32)
+    out = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((Tq, H), device=DEV)
+    L.sparse_mqa_prefill(bf(q), bf(kv), dev(idx), bf(tok), dev(pos), dev(sink), out, lse, W=W)
+    torch.cuda.synchronize()
+    O, LS = host(out), host(lse)
+    for t in range(Tq):
+        ids = idx[t][idx[t] >= 0]
+        rows = np.concatenate([kv[ids], oracle.window_rows(tok, int(pos[t]), W)])
+        ref, rlse = oracle.attend(q[t], rows, sink)
+        assert rlse.max() > 60.0  # planted rows sit far above the first tiles' logits (about 3)
+        check_out(O[t], ref, _attn_tight(ref), f"prefill jump t={t}")
+        assert np.abs(LS[t] - rlse).max() < 1e-3
+
+
 def test_prefill_equals_decode():
     """The prefill output of the query at position p equals a decode step over
     the same selected entries whose window buffer holds tokens

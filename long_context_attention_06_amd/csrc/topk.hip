@@ -158,7 +158,7 @@ __device__ void block_select(const KS& ks, int n, int K, uint32_t* hist, int* re
     red[wv] = (int)kmin;
     red[TK_NW + wv] = (int)kmax;
   }
-  for (int i = t; i < 2 * TK_BINS; i += TK_NT) hist[i] = 0;
+  for (int i = t; i < TK_BINS; i += TK_NT) hist[i] = 0;
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < TK_NW; ++u) {
@@ -177,7 +177,7 @@ __device__ void block_select(const KS& ks, int n, int K, uint32_t* hist, int* re
     const int nbits = min(11, R);
     const int shift = R - nbits;
     const uint32_t dmask = (1u << nbits) - 1u;
-    uint32_t* h = hist + (pass & 1) * TK_BINS;
+    uint32_t* h = hist;
     auto add = [&](uint32_t k) {
       if (R >= 32 || (k >> R) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
     };
@@ -207,9 +207,14 @@ __device__ void block_select(const KS& ks, int n, int K, uint32_t* hist, int* re
       __syncthreads();  // every wave has read res[] before the caller reuses it
       return;
     }
-    if (pass == 0)  // pass 2 reuses this buffer; nothing reads it during pass 1
-      for (int i = t; i < TK_BINS; i += TK_NT) h[i] = 0;
     R = shift;
+    if (R > 0) {
+      // another pass: find_bin_block's closing barrier freed the histogram
+      // (one buffer keeps the LDS of a 16K-key chunk small enough for two
+      // workgroups per CU)
+      for (int i = t; i < TK_BINS; i += TK_NT) h[i] = 0;
+      __syncthreads();
+    }
   }
   T = prefix;  // take all keys > T and the `need` lowest-position keys == T
 }
@@ -320,11 +325,11 @@ __device__ void block_compact(const KS& ks, int n, int K, bool all, uint32_t T, 
 template <int SRC>
 __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-  uint32_t* hist = smem;                                   // 2 x TK_BINS (alternating passes)
-  int* red = reinterpret_cast<int*>(smem + 2 * TK_BINS);   // 32
+  uint32_t* hist = smem;                                   // TK_BINS
+  int* red = reinterpret_cast<int*>(smem + TK_BINS);       // 32
   int* res = red + 32;                                     // 32
   const int CH = a.chunk;
-  uint32_t* kc = smem + 2 * TK_BINS + 64;                  // CH keys
+  uint32_t* kc = smem + TK_BINS + 64;                      // CH keys
   int32_t* ic = reinterpret_cast<int32_t*>(kc + CH);       // TK_CANDS: indices
 
   const int t = threadIdx.x;
@@ -436,7 +441,7 @@ __global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
 //    whole row read from memory instead. Either way the result is the exact
 //    top K'.
 __global__ void __launch_bounds__(TK_NT) topk_threshold_kernel(TopkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[2 * TK_BINS];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
   __shared__ __attribute__((aligned(16))) int red[32], res[32];
   __shared__ __attribute__((aligned(16))) uint32_t kc[TK_SAMPLE];
   const int t = threadIdx.x;
@@ -511,8 +516,8 @@ __global__ void __launch_bounds__(TK_NT) topk_filter_kernel(TopkArgs a) {
 
 __global__ void __launch_bounds__(TK_NT) topk_filtered_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-  uint32_t* hist = smem;                                   // 2 x TK_BINS
-  int* red = reinterpret_cast<int*>(smem + 2 * TK_BINS);   // 32
+  uint32_t* hist = smem;                                   // TK_BINS
+  int* red = reinterpret_cast<int*>(smem + TK_BINS);       // 32
   int* res = red + 32;                                     // 32
   int* off = res + 32;                                     // TK_FCH_MAX chunk offsets, then the total
   uint32_t* kc = reinterpret_cast<uint32_t*>(off + TK_FCH_MAX + 64);  // TK_CHUNK_C keys
@@ -590,14 +595,17 @@ static int64_t pow2_at_least(int64_t x) {
 // chunks per row and the row length it reads. Chunks are sized so a launch
 // offers about one workgroup per CU (a lone workgroup is VALU bound), never
 // below 4096 keys or 4*top_k (each level must shrink the rows), never above
-// what fits in LDS. Depends on shape arguments only.
+// what fits in LDS, and never above the row itself (rounded up to 256 keys):
+// LDS is sized by the chunk, and rows of up to 18K keys then leave room for
+// two workgroups per CU. Depends on shape arguments only.
 static int plan_levels(int64_t rows, int64_t n0, int top_k, int64_t* nch, int64_t* nlen, int64_t* chunk) {
   int lv = 0;
   int64_t n = n0;
   while (true) {
     const int64_t cmax = lv == 0 ? TK_CHUNK_S : TK_CHUNK_C;
     const int64_t want = pow2_at_least((rows * n + TK_TARGET_WG - 1) / TK_TARGET_WG);
-    const int64_t ch = std::min(cmax, std::max<int64_t>({want, (int64_t)TK_CHUNK_MIN, pow2_at_least(4 * (int64_t)top_k)}));
+    const int64_t ch = std::min({cmax, (n + 255) / 256 * 256,
+                                 std::max<int64_t>({want, (int64_t)TK_CHUNK_MIN, pow2_at_least(4 * (int64_t)top_k)})});
     chunk[lv] = ch;
     nch[lv] = std::max<int64_t>(1, (n + ch - 1) / ch);
     nlen[lv] = n;
@@ -638,8 +646,8 @@ hipError_t run_topk(const TopkLaunch& L, hipStream_t st) {
   const int64_t rows = L.B * L.Tq;
   if (rows == 0) return hipSuccess;
   static bool attr_set = false;
-  const size_t lds_s = (size_t)(2 * TK_BINS + 64 + TK_CHUNK_S) * 4;
-  const size_t lds_c = (size_t)(2 * TK_BINS + 64 + 2 * TK_CHUNK_C) * 4;
+  const size_t lds_s = (size_t)(TK_BINS + 64 + TK_CHUNK_S) * 4;
+  const size_t lds_c = (size_t)(TK_BINS + 64 + 2 * TK_CHUNK_C) * 4;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<TK_SCORES>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
@@ -650,7 +658,7 @@ hipError_t run_topk(const TopkLaunch& L, hipStream_t st) {
     attr_set = true;
   }
   if (use_threshold_path(rows, L.N_max, L.top_k)) {
-    const size_t lds_f = (size_t)(2 * TK_BINS + 64 + TK_FCH_MAX + 64 + 2 * TK_CHUNK_C) * 4;
+    const size_t lds_f = (size_t)(TK_BINS + 64 + TK_FCH_MAX + 64 + 2 * TK_CHUNK_C) * 4;
     static bool attr_f = false;
     if (!attr_f) {
       hipError_t e = hipFuncSetAttribute((const void*)topk_filtered_kernel,
@@ -712,9 +720,9 @@ hipError_t run_topk(const TopkLaunch& L, hipStream_t st) {
     dim3 grid((unsigned)nch[i], (unsigned)rows);
     a.chunk = (int)chunk[i];
     if (i == 0) {
-      hipLaunchKernelGGL(topk_kernel<TK_SCORES>, grid, dim3(TK_NT), (2 * TK_BINS + 64 + chunk[i]) * 4, st, a);
+      hipLaunchKernelGGL(topk_kernel<TK_SCORES>, grid, dim3(TK_NT), (TK_BINS + 64 + chunk[i]) * 4, st, a);
     } else {
-      hipLaunchKernelGGL(topk_kernel<TK_CANDS>, grid, dim3(TK_NT), (2 * TK_BINS + 64 + 2 * chunk[i]) * 4, st, a);
+      hipLaunchKernelGGL(topk_kernel<TK_CANDS>, grid, dim3(TK_NT), (TK_BINS + 64 + 2 * chunk[i]) * 4, st, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

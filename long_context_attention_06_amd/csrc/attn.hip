@@ -701,6 +701,8 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
       lmx[hg][dh][hq][l] = fmaxf(fmaxf(s[hq][0], s[hq][1]), fmaxf(s[hq][2], s[hq][3]));
     vm_barrier<63>();
     float alpha[2];
+    // before the first reference of a query O is zero and needs no scaling
+    const bool o_live = (ohq ? m_ref[1] : m_ref[0]) != -INFINITY;
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
       float tm = -INFINITY;
@@ -716,7 +718,7 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
       thr[hq] = m_new == -INFINITY ? -INFINITY : (m_new + GUARD) / scale_log2;
     }
     const float ao = ohq ? alpha[1] : alpha[0];
-    if (__any(ao != 1.0f)) {
+    if (__any(o_live && ao != 1.0f)) {
       // every O^T register of this lane belongs to its own head
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)

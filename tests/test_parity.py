@@ -303,15 +303,19 @@ def test_sparse_decode_no_sink_empty():
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
 
 
-def test_hca_decode():
-    _say("hca_decode")
+@pytest.mark.parametrize("N_max,V1", [(1500, 1000), (5000, 3333)])
+def test_hca_decode(N_max, V1):
+    """Dense HCA rows in splits: 1628 slots give 128-row splits, 5128 slots
+    352-row splits, with visible counts that leave splits empty and one that
+    mixes compressed and window rows."""
+    _say("hca_decode", N_max)
     g = _g(31)
-    B, H, D, N_max, W, m = 3, 64, 512, 1500, 128, 128
+    B, H, D, W, m = 3, 64, 512, 128, 128
     q = gen.bf16_round(g.standard_normal((B, H, D)).astype(np.float32) / math.sqrt(D))
     kv = gen.bf16_round(g.standard_normal((B, N_max, D)).astype(np.float32))
     win = gen.bf16_round(g.standard_normal((B, W, D)).astype(np.float32))
-    n_comp = np.array([1500, 1500, 40], np.int32)
-    q_pos = np.array([1500 * 128 + 5, 1000 * 128 - 1, 10 ** 6], np.int32)  # V = 1500, 1000, 40
+    n_comp = np.array([N_max, N_max, 40], np.int32)
+    q_pos = np.array([N_max * 128 + 5, V1 * 128 - 1, 10 ** 6], np.int32)  # V = N_max, V1, 40
     win_len = np.array([128, 128, 3], np.int32)
     sink = g.standard_normal(H).astype(np.float32)
     out = torch.empty((B, H, D), dtype=torch.bfloat16, device=DEV)

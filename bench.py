@@ -13,7 +13,7 @@ Inputs are synthetic (seeded generator), resident in HBM before timing, and
 rotated over several device replicas so that no step reads cache-resident
 data from the previous one.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c5|c4|c3]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c5|c4|c3|c2x]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -41,7 +41,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4", "c3"])
+    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4", "c3", "c2x"])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -104,7 +104,7 @@ def main():
         return
     if a.workload == "c3":
         return bench_prefill(a, torch, L, gen, dev)
-    cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4}[a.workload]
+    cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X}[a.workload]
     t0 = time.time()
     x = gen.gen_decode(cfg, with_compress=(cfg.kind == "csa_decode"))
     print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -122,6 +122,9 @@ def main():
         base["w"] = td(x["w"][:, None])
         if cfg.k_dtype == "fp8":
             base["k_idx"] = td(x["k_idx_codes"])
+            base["k_scale"] = td(x["k_scale"])
+        elif cfg.k_dtype == "mxfp4":
+            base["k_idx"] = td(x["k_idx_codes"]).view(torch.float4_e2m1fn_x2)
             base["k_scale"] = td(x["k_scale"])
         else:
             base["k_idx"] = bf(x["k_idx"])
@@ -221,17 +224,17 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
     }
     if cfg.kind == "csa_decode":
-        kbytes = N * cfg.D_I * (1 if cfg.k_dtype == "fp8" else 2) + (N * 4 if cfg.k_dtype == "fp8" else 0)
+        kbytes = {"fp8": N * (cfg.D_I + 4), "mxfp4": N * (cfg.D_I // 2 + cfg.D_I // 32)}.get(cfg.k_dtype, N * cfg.D_I * 2)
         scan_bytes = B * (kbytes + cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4)  # keys (+scales), q_idx, w
         step_bytes = B * (kbytes + cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4 + k * D * 2 + W * D * 2 + H * D * 2 * 2 + k * 4)
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
                          "m": m, "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I,
                          "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype}
-        res["roofline"] = {"bound": "hbm", "kernel": "idx_scan_fp8_kernel" if cfg.k_dtype == "fp8" else "idx_scan_bf16_kernel", "achieved": round(scan_bytes / (scan_avg * 1e-3) / 1e9, 1),
+        kname = {"fp8": "idx_scan_lp_kernel<2> (E4M3 keys)", "mxfp4": "idx_scan_lp_kernel<3> (MXFP4 keys)"}.get(cfg.k_dtype, "idx_scan_bf16_kernel")
+        res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": round(scan_bytes / (scan_avg * 1e-3) / 1e9, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(scan_bytes / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "traffic": _traffic("idx_scan_c2_traffic.txt" if a.workload == "c2" else "idx_scan_c5_traffic.txt",
-                                               ["indexer.hip", "common.h"]),
+                           "traffic": _traffic(f"idx_scan_{a.workload}_traffic.txt", ["indexer.hip", "common.h"]),
                            "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_ms": round(scan_avg, 4)}
         res["phases_ms"] = {"compress": round(float(ph_mean[0]), 4), "indexer_scan": round(float(ph_mean[1]), 4),
                             "topk": round(float(ph_mean[2]), 4), "attention": round(attn_avg, 4)}
@@ -407,6 +410,8 @@ def cpu_baseline(cfg, x, budget_s: float):
             comp[cfg.N - 1] = ent
             if cfg.k_dtype == "fp8":
                 keys, sc = oracle.e4m3_decode(x["k_idx_codes"][b]), x["k_scale"][b]
+            elif cfg.k_dtype == "mxfp4":
+                keys, sc = oracle.mxfp4_decode(x["k_idx_codes"][b], x["k_scale"][b]), None
             else:
                 keys, sc = x["k_idx"][b], None
             oracle.csa_query(x["q"][b], x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, cfg.N, m, cfg.top_k,

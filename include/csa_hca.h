@@ -33,7 +33,11 @@
  *     Indices, positions and lengths are int32.
  *   - dtype codes: CSA_F32, CSA_BF16 (storage of activations and caches),
  *     CSA_FP8_E4M3 (OCP E4M3 "FN", indexer keys only, with a per-entry fp32
- *     scale). Arithmetic is fp32 (bf16 x bf16 products accumulate in fp32).
+ *     scale), CSA_MXFP4 (OCP Microscaling MXFP4, indexer keys only: FP4 E2M1
+ *     elements, two per byte with element 2j in the low nibble of byte j, and
+ *     one E8M0 scale byte per block of 32 elements; the pages keep the
+ *     indexer in FP4). Arithmetic is fp32 (bf16 x bf16 products accumulate in
+ *     fp32; fp8 and FP4 keys are widened to bf16 exactly first).
  *   - Return codes: CSA_OK, CSA_INVALID_ARG (a null pointer that must not be
  *     null, a negative or inconsistent size), CSA_UNSUPPORTED (a valid
  *     combination with no kernel instantiation), CSA_WORKSPACE_TOO_SMALL,
@@ -60,7 +64,7 @@ extern "C" {
 
 #define CSA_HCA_VERSION 1
 
-enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 };
+enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3 };
 
 enum {
   CSA_OK = 0,
@@ -110,16 +114,22 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
  * For query t of sequence b at position p = q_pos[b, t], the visible entries
  * are i < V = min(n_comp[b], floor((p+1)/m), N_max), and
  *   scores[b, t, i] = sum_h w[b, t, h] * max(0, sigma_i * <q_idx[b,t,h,:], k_idx[b,i,:]>)
- * where sigma_i = k_scale[b, i] for fp8 keys and 1 otherwise.
+ * where sigma_i = k_scale[b, i] for fp8 keys and 1 otherwise (MXFP4 block
+ * scales are part of the key values).
  *
  *   q_idx   : [B, Tq, H_I, D_I] in q_dt          w      : [B, Tq, H_I] fp32
- *   k_idx   : [B, N_max, D_I] in k_dt            k_scale: [B, N_max] fp32 (fp8 keys only, else NULL)
+ *   k_idx   : [B, N_max, D_I] in k_dt (MXFP4: [B, N_max, D_I/2] bytes)
+ *   k_scale : fp8 keys: [B, N_max] fp32; MXFP4 keys: [B, N_max, D_I/32] E8M0
+ *             bytes, each in 1..254 (0 and the NaN byte 255 are not
+ *             supported; the elements widen to bf16 exactly for bytes
+ *             2..252, beyond which the largest or smallest magnitudes leave
+ *             bf16's normal range); NULL otherwise. 4-byte aligned.
  *   q_pos   : [B, Tq] int32                      n_comp : [B] int32
  *   scores  : [B, Tq, N_max] fp32; entries i >= V are left unspecified.
- * Supported: (H_I, D_I) in {(64, 128) with q_dt BF16 and k_dt BF16 or FP8_E4M3,
- * (4, 32) with q_dt = k_dt = F32}. N_max <= 2^24.
+ * Supported: (H_I, D_I) in {(64, 128) with q_dt BF16 and k_dt BF16, FP8_E4M3
+ * or MXFP4, (4, 32) with q_dt = k_dt = F32}. N_max <= 2^24.
  */
-int indexer_score(const void* q_idx, const float* w, const void* k_idx, const float* k_scale,
+int indexer_score(const void* q_idx, const float* w, const void* k_idx, const void* k_scale,
                   const int32_t* q_pos, const int32_t* n_comp,
                   int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m,
                   int q_dt, int k_dt, float* scores, void* stream);
@@ -142,7 +152,7 @@ size_t indexer_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int to
 
 /* indexer_score_topk — indexer_score followed by indexer_topk, the scores
  * living in the workspace. Same arguments and support as the two calls. */
-int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, const float* k_scale,
+int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, const void* k_scale,
                        const int32_t* q_pos, const int32_t* n_comp,
                        int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int top_k,
                        int q_dt, int k_dt, int32_t* topk_idx, float* topk_score,

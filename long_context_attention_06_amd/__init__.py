@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa_hca.so")
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = 0, -1, -2, -3, -4
 OVERLAP, JOINT_SOFTMAX = 1, 2
 
@@ -83,6 +83,8 @@ def _dt(t) -> int:
         return BF16
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return FP8_E4M3
+    if t.dtype == torch.float4_e2m1fn_x2:  # MXFP4 codes, two per byte (indexer keys)
+        return MXFP4
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
@@ -132,8 +134,9 @@ def csa_compress(Ca, Cb, Za, Zb, Ba, Bb, out, *, m: int, tok_begin: int = 0, blk
 # -------------------------------------------------------------------- indexer
 
 def indexer_score(q_idx, w, k_idx, k_scale, q_pos, n_comp, scores, *, m: int, stream=None) -> None:
-    """q_idx [B, Tq, H_I, D_I]; w [B, Tq, H_I]; k_idx [B, N_max, D_I]; k_scale [B, N_max] or None;
-    q_pos [B, Tq] int32; n_comp [B] int32; scores [B, Tq, N_max] fp32."""
+    """q_idx [B, Tq, H_I, D_I]; w [B, Tq, H_I]; k_idx [B, N_max, D_I] (MXFP4: [B, N_max, D_I/2] of
+    float4_e2m1fn_x2); k_scale: fp8 keys [B, N_max] fp32, MXFP4 keys [B, N_max, D_I/32] E8M0 bytes,
+    else None; q_pos [B, Tq] int32; n_comp [B] int32; scores [B, Tq, N_max] fp32."""
     B, Tq, H_I, D_I = q_idx.shape
     N_max = k_idx.shape[1]
     _check(lib.indexer_score(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q_pos), _ptr(n_comp), B, Tq,

@@ -67,23 +67,26 @@ int check_attn_common(const void* q, const void* out, float scale, int H, int D,
   return CSA_OK;
 }
 
-int check_indexer(const void* q_idx, const float* w, const void* k_idx, const float* k_scale, const int32_t* q_pos,
+int check_indexer(const void* q_idx, const float* w, const void* k_idx, const void* k_scale, const int32_t* q_pos,
                   const int32_t* n_comp, int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int q_dt,
                   int k_dt) {
   REQ(q_idx && w && k_idx && q_pos && n_comp, CSA_INVALID_ARG, "q_idx, w, k_idx, q_pos, n_comp must not be NULL");
   REQ(B >= 0 && Tq >= 0 && N_max >= 0, CSA_INVALID_ARG, "B, Tq, N_max must be >= 0");
   REQ(H_I > 0 && D_I > 0, CSA_INVALID_ARG, "H_I and D_I must be positive");
   REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");
-  REQ(q_dt >= CSA_F32 && q_dt <= CSA_FP8_E4M3 && k_dt >= CSA_F32 && k_dt <= CSA_FP8_E4M3, CSA_INVALID_ARG,
+  REQ(q_dt >= CSA_F32 && q_dt <= CSA_FP8_E4M3 && k_dt >= CSA_F32 && k_dt <= CSA_MXFP4, CSA_INVALID_ARG,
       "unknown dtype");
-  REQ(k_dt != CSA_FP8_E4M3 || k_scale, CSA_INVALID_ARG, "fp8 keys need k_scale");
+  REQ((k_dt != CSA_FP8_E4M3 && k_dt != CSA_MXFP4) || k_scale, CSA_INVALID_ARG, "fp8 and MXFP4 keys need k_scale");
+  REQ(k_dt != CSA_MXFP4 || D_I % 32 == 0, CSA_INVALID_ARG, "MXFP4 keys need D_I a multiple of 32");
   REQ(N_max <= (int64_t(1) << 24), CSA_UNSUPPORTED, "N_max above 2^24");
   REQ(B * Tq <= 65535, CSA_UNSUPPORTED, "B*Tq above 65535 rows per call");
-  const bool big = H_I == 64 && D_I == 128 && q_dt == CSA_BF16 && (k_dt == CSA_BF16 || k_dt == CSA_FP8_E4M3);
+  const bool big =
+      H_I == 64 && D_I == 128 && q_dt == CSA_BF16 && (k_dt == CSA_BF16 || k_dt == CSA_FP8_E4M3 || k_dt == CSA_MXFP4);
   const bool tiny = H_I <= 32 && D_I == 32 && q_dt == CSA_F32 && k_dt == CSA_F32;
   REQ(big || tiny, CSA_UNSUPPORTED,
-      "unsupported indexer shape/dtype: (64, 128) bf16 q with bf16/fp8 keys, or (<=32, 32) fp32");
+      "unsupported indexer shape/dtype: (64, 128) bf16 q with bf16/fp8/MXFP4 keys, or (<=32, 32) fp32");
   REQ(aligned16(q_idx) && aligned16(k_idx), CSA_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
+  REQ(!k_scale || ((uintptr_t)k_scale & 3) == 0, CSA_INVALID_ARG, "k_scale must be 4-byte aligned");
   return CSA_OK;
 }
 
@@ -140,7 +143,7 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
   return hip_status(csa::run_compress(a, (hipStream_t)stream), "csa_compress");
 }
 
-int indexer_score(const void* q_idx, const float* w, const void* k_idx, const float* k_scale, const int32_t* q_pos,
+int indexer_score(const void* q_idx, const float* w, const void* k_idx, const void* k_scale, const int32_t* q_pos,
                   const int32_t* n_comp, int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int q_dt,
                   int k_dt, float* scores, void* stream) {
   int rc = check_indexer(q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, q_dt, k_dt);
@@ -172,7 +175,7 @@ size_t indexer_score_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, 
   return round256((size_t)B * Tq * N_max * 4) + indexer_topk_workspace_bytes(B, Tq, N_max, top_k);
 }
 
-int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, const float* k_scale,
+int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, const void* k_scale,
                        const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq, int H_I, int D_I,
                        int64_t N_max, int m, int top_k, int q_dt, int k_dt, int32_t* topk_idx, float* topk_score,
                        void* ws, size_t ws_bytes, void* stream) {

@@ -15,7 +15,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #define LN2_F 0.6931471805599453f
 
 // dtype tags (match the ABI codes)
-enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 

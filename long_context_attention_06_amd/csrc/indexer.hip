@@ -34,9 +34,21 @@ namespace csa {
 // of 4 bytes those 16 chunks must fall in 16 different 16-byte bank groups.
 // bf16 rows are 256 bytes (every row starts in group 0): chunk ^ (r & 15).
 // fp8 rows are 128 bytes (odd rows start in group 8): chunk ^ ((r >> 1) & 7).
+// MXFP4 rows are 64 bytes (four rows per 256 bytes): chunk ^ ((r >> 2) & 3).
 template <int KDT>
 __device__ __forceinline__ int kswz(int r) {
-  return KDT == DT_FP8 ? ((r >> 1) & 7) : (r & 15);
+  return KDT == DT_FP8 ? ((r >> 1) & 7) : KDT == DT_MXFP4 ? ((r >> 2) & 3) : (r & 15);
+}
+
+// 8 OCP MXFP4 codes (one dword, element 2j in the low nibble of byte j) ->
+// 8 bf16, times the block scale 2^(E - 127): gfx950's scaled convert takes two
+// codes per instruction and applies the scale's exponent exactly (every E2M1
+// value times a power of two in bf16 range is a bf16 value).
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t codes, float scale) {
+  return as_bf16x8(u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3))});
 }
 
 // bf16 keys, 64 heads x 128 dims.  Grid: (workgroups per row, rows).
@@ -163,23 +175,25 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
 // instruction, exact: every E4M3 value is a bf16 value); the scale multiplies
 // the head-weighted sum. Scores collect in LDS and are written out every
 // SC_TILES tiles: no store is in flight while DMA waits are counted.
+template <int KDT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-idx_scan_fp8_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-                    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
-                    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
-                    int64_t N_max, int m, float* __restrict__ scores) {
-  constexpr int KDT = DT_FP8;
+idx_scan_lp_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+                   const uint8_t* __restrict__ k_idx, const uint32_t* __restrict__ k_scale,
+                   const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
+                   int64_t N_max, int m, float* __restrict__ scores) {
+  static_assert(KDT == DT_FP8 || KDT == DT_MXFP4, "low-precision keys");
+  constexpr bool MX = KDT == DT_MXFP4;
   constexpr int H = 64, DI = 128, KS = 4;   // k-steps of 32
-  constexpr int KROW = DI;                  // bytes per key row
-  constexpr int TE = 128;                   // entries per tile
+  constexpr int KROW = MX ? DI / 2 : DI;    // bytes per key row
+  constexpr int TE = MX ? 256 : 128;        // entries per tile
   constexpr int NE = TE / 64;               // 16-entry N tiles per wave
   constexpr int TB = TE * KROW;             // 16 KB
   constexpr int NBUF = 4;                   // 64 KB ring
   constexpr int DPW = TB / 1024 / 4;        // 1 KB DMAs per wave per tile
-  constexpr int PER_TILE = DPW + 1;         // + the scales
-  constexpr int SC_TILES = 16;              // score buffer (tiles)
+  constexpr int PER_TILE = DPW + 1;         // + the scales (one dword per entry)
+  constexpr int SC_TILES = 2048 / TE;       // score buffer (8 KB)
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k[NBUF][TB];
-  __shared__ __attribute__((aligned(16))) float lds_s[NBUF][TE];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_s[NBUF][TE];  // fp32 scale bits, or four E8M0 bytes
   __shared__ __attribute__((aligned(16))) float lds_sc[SC_TILES][TE];
   __shared__ __attribute__((aligned(16))) float lds_w[H];
 
@@ -227,7 +241,7 @@ idx_scan_fp8_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
 #pragma unroll
     for (int j = 0; j < DPW; ++j)
       dma_row(tb, (uint32_t)(min(drow[j], last) * KROW) + dcol[j], lds_addr(&lds_k[buf][(DPW * wv + j) * 1024]));
-    if (l < TE / 4)  // wave wv moves the scales of entries 32 wv .. 32 wv + 31
+    if (l < TE / 4)  // wave wv moves the scales of entries TE/4 wv .. TE/4 wv + TE/4 - 1
       dma_dword(uniform_ptr(k_scale + b * N_max + tile * TE), (uint32_t)(min(TE / 4 * wv + l, last) * 4),
                 lds_addr(&lds_s[buf][TE / 4 * wv]));
   };
@@ -267,20 +281,29 @@ idx_scan_fp8_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
       const uint8_t* kr = &lds_k[buf][el * KROW];
       const int sw = kswz<KDT>(el);
       bf16x8_t kbv[KS];
-      // dims G*32 + s*8 .. : bytes G*32 + s*8, i.e. chunk G*2 + s/2, half s%2
+      if constexpr (MX) {
+        // dims G*32 + s*8 .. : block G, bytes G*16 + s*4 (one chunk), scaled
+        // by the block's E8M0 byte G as the fp32 2^(E - 127)
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + ((G ^ sw) * 16));
+        const float sc = __uint_as_float(((lds_s[buf][el] >> (8 * G)) & 0xffu) << 23);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + (((G * 2 + c) ^ sw) * 16));
-        u32x4_t lo, hi;
+        for (int s = 0; s < KS; ++s) kbv[s] = fp4x8_to_bf16x8(v[s], sc);
+      } else {
+        // dims G*32 + s*8 .. : bytes G*32 + s*8, i.e. chunk G*2 + s/2, half s%2
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          lo[2 * q] = fp8x2_to_bf16x2(v[q], false);
-          lo[2 * q + 1] = fp8x2_to_bf16x2(v[q], true);
-          hi[2 * q] = fp8x2_to_bf16x2(v[2 + q], false);
-          hi[2 * q + 1] = fp8x2_to_bf16x2(v[2 + q], true);
+        for (int c = 0; c < 2; ++c) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + (((G * 2 + c) ^ sw) * 16));
+          u32x4_t lo, hi;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            lo[2 * q] = fp8x2_to_bf16x2(v[q], false);
+            lo[2 * q + 1] = fp8x2_to_bf16x2(v[q], true);
+            hi[2 * q] = fp8x2_to_bf16x2(v[2 + q], false);
+            hi[2 * q + 1] = fp8x2_to_bf16x2(v[2 + q], true);
+          }
+          kbv[2 * c] = as_bf16x8(lo);
+          kbv[2 * c + 1] = as_bf16x8(hi);
         }
-        kbv[2 * c] = as_bf16x8(lo);
-        kbv[2 * c + 1] = as_bf16x8(hi);
       }
       part[n] = 0.0f;
 #pragma unroll
@@ -302,7 +325,9 @@ idx_scan_fp8_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
 #pragma unroll
       for (int n = 0; n < NE; ++n) {
         const int el = wv * (16 * NE) + n * 16 + l16;
-        lds_sc[(it - it_flushed) % SC_TILES][el] = part[n] * lds_s[buf][el];
+        // fp8: sigma_i scales the head-weighted sum (ReLU commutes with a
+        // positive scale); MXFP4 scales are already inside the key values
+        lds_sc[(it - it_flushed) % SC_TILES][el] = MX ? part[n] : part[n] * __uint_as_float(lds_s[buf][el]);
       }
     }
     if (it + 1 - it_flushed == SC_TILES && it + 1 < nmine) {
@@ -325,17 +350,19 @@ idx_scan_fp8_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
 template <int KDT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-                   const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
+                   const uint8_t* __restrict__ k_idx, const uint32_t* __restrict__ k_scale,
                    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
                    int64_t N_max, int m, float* __restrict__ scores) {
   constexpr int H = 64, DI = 128, KS = 4, QB = 8;
-  constexpr int KROW = (KDT == DT_FP8) ? DI : DI * 2;
+  constexpr bool MX = KDT == DT_MXFP4;
+  constexpr int KROW = (KDT == DT_FP8) ? DI : MX ? DI / 2 : DI * 2;
   constexpr int TE = 64;
   constexpr int TB = TE * KROW;
   constexpr int NT = 64 * QB;
   constexpr int LPT = (TB + NT * 16 - 1) / (NT * 16);  // 16-byte loads per thread per tile
   static_assert(TB % (NT * 16) == 0 || TB < NT * 16, "tile load mapping");
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][TB];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_ks[2][MX ? TE : 1];  // MXFP4: four E8M0 bytes per entry
   __shared__ __attribute__((aligned(16))) float lds_w[QB][H];
 
   const int tid = threadIdx.x;
@@ -376,6 +403,7 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   float* srow = scores + row * N_max;
 
   u32x4_t rg[2][LPT];
+  uint32_t rs[2] = {0u, 0u};  // MXFP4: the scale dword of entry tid of the tile
   auto load = [&](auto SLOT, int64_t tile) {
     constexpr int slot = decltype(SLOT)::value;
 #pragma unroll
@@ -384,9 +412,16 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
       const int64_t e = tile * TE + o / KROW;
       rg[slot][j] = (o < TB && e < Vmax) ? ld16(kb + e * KROW + (o % KROW)) : u32x4_t{0, 0, 0, 0};
     }
+    if constexpr (MX) {
+      const int64_t e = tile * TE + tid;
+      rs[slot] = (tid < TE && e < Vmax) ? k_scale[b * N_max + e] : 0u;
+    }
   };
   auto stash = [&](auto SLOT) {
     constexpr int slot = decltype(SLOT)::value;
+    if constexpr (MX) {
+      if (tid < TE) lds_ks[slot][tid] = rs[slot];
+    }
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
       const int o = (j * NT + tid) * 16;
@@ -410,7 +445,13 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
         const uint8_t* kr = &lds_k[buf][el * KROW];
         const int sw = kswz<KDT>(el);
         bf16x8_t kbv[KS];
-        if constexpr (KDT == DT_FP8) {
+        if constexpr (MX) {
+          // block G of the entry: one chunk, scaled by its E8M0 byte
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + ((G ^ sw) * 16));
+          const float sc = __uint_as_float(((lds_ks[buf][el] >> (8 * G)) & 0xffu) << 23);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) kbv[s] = fp4x8_to_bf16x8(v[s], sc);
+        } else if constexpr (KDT == DT_FP8) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + (((G * 2 + c) ^ sw) * 16));
@@ -445,7 +486,7 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
       for (int nt = 0; nt < 4; ++nt) {
         const float v = sum_rows16(part[nt]);
         const int64_t e = tile * TE + nt * 16 + l16;
-        if (G == 0 && e < Vq) srow[e] = KDT == DT_FP8 ? v * k_scale[b * N_max + e] : v;
+        if (G == 0 && e < Vq) srow[e] = KDT == DT_FP8 ? v * __uint_as_float(k_scale[b * N_max + e]) : v;
       }
     }
   };
@@ -507,29 +548,27 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
   if (a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16 && a.Tq >= 8) {
     // many queries per sequence: key tiles shared by 8 queries per workgroup
     dim3 grid((unsigned)((a.Tq + 7) / 8), (unsigned)a.B);
-    if (a.k_dt == DT_FP8)
-      hipLaunchKernelGGL((idx_prefill_kernel<DT_FP8>), grid, dim3(512), 0, st,
-                         reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
-                         a.k_scale, a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
-    else
-      hipLaunchKernelGGL((idx_prefill_kernel<DT_BF16>), grid, dim3(512), 0, st,
-                         reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
-                         a.k_scale, a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
+    auto kern = a.k_dt == DT_FP8 ? idx_prefill_kernel<DT_FP8>
+                : a.k_dt == DT_MXFP4 ? idx_prefill_kernel<DT_MXFP4> : idx_prefill_kernel<DT_BF16>;
+    hipLaunchKernelGGL(kern, grid, dim3(512), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx), a.w,
+                       reinterpret_cast<const uint8_t*>(a.k_idx), reinterpret_cast<const uint32_t*>(a.k_scale),
+                       a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
     return hipGetLastError();
   }
   if (a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16) {
     if (a.N_max == 0) return hipSuccess;  // no entries: nothing to score (the kernels load entry 0 first)
-    const int64_t te = a.k_dt == DT_FP8 ? 128 : IDX_BF16_TE;
+    const int64_t te = a.k_dt == DT_FP8 ? 128 : a.k_dt == DT_MXFP4 ? 256 : IDX_BF16_TE;
     const int64_t ntiles = (a.N_max + te - 1) / te;
     // a few workgroups per CU in total, each walking a strided run of tiles
     // of its row
     int64_t per_row = (512 + rows - 1) / rows;
     per_row = max((int64_t)1, min(ntiles, per_row));
     dim3 grid((unsigned)per_row, (unsigned)rows);
-    if (a.k_dt == DT_FP8)
-      hipLaunchKernelGGL(idx_scan_fp8_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx),
-                         a.w, reinterpret_cast<const uint8_t*>(a.k_idx), a.k_scale, a.q_pos, a.n_comp, a.Tq,
-                         a.N_max, a.m, a.scores);
+    if (a.k_dt == DT_FP8 || a.k_dt == DT_MXFP4)
+      hipLaunchKernelGGL((a.k_dt == DT_FP8 ? idx_scan_lp_kernel<DT_FP8> : idx_scan_lp_kernel<DT_MXFP4>), grid,
+                         dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx), a.w,
+                         reinterpret_cast<const uint8_t*>(a.k_idx), reinterpret_cast<const uint32_t*>(a.k_scale),
+                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
     else
       hipLaunchKernelGGL(idx_scan_bf16_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx),
                          a.w, reinterpret_cast<const uint8_t*>(a.k_idx), a.q_pos, a.n_comp, a.Tq, a.N_max, a.m,

@@ -21,7 +21,7 @@ struct IndexerLaunch {
   const void* q_idx;
   const float* w;
   const void* k_idx;
-  const float* k_scale;
+  const void* k_scale;  // fp8: fp32 per entry; MXFP4: E8M0 byte per 32 dims
   const int32_t* q_pos;
   const int32_t* n_comp;
   int64_t B, Tq, N_max;

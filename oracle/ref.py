@@ -64,6 +64,26 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 15) & ((c & 7) == 7), np.nan, v)
 
 
+def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """OCP MXFP4 (Microscaling Formats v1.0) -> values, from the format
+    definition. Element: FP4 E2M1, sign(1) exp(2, bias 1) mantissa(1), exponent
+    field 0 subnormal (mantissa/2), so the magnitudes are 0, 0.5, 1, 1.5, 2, 3,
+    4, 6. Two elements per byte, element 2j in the low nibble of byte j. One
+    E8M0 scale byte E per block of 32 elements scales it by 2^(E - 127); the
+    byte 255 is NaN. codes [..., D/2] uint8, scales [..., D/32] uint8 ->
+    [..., D] float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    nib = np.stack([c & 0xF, c >> 4], axis=-1).reshape(c.shape[:-1] + (2 * c.shape[-1],))
+    e = (nib >> 1) & 3
+    mt = (nib & 1).astype(F64)
+    mag = np.where(e == 0, 0.5 * mt, (1.0 + 0.5 * mt) * np.exp2(e.astype(F64) - 1.0))
+    v = np.where(nib & 8, -mag, mag)
+    E = np.asarray(scales, dtype=np.uint8).astype(np.int64)
+    sc = np.where(E == 255, np.nan, np.exp2(E.astype(F64) - 127.0))
+    blk = v.reshape(v.shape[:-1] + (E.shape[-1], v.shape[-1] // E.shape[-1]))
+    return (blk * sc[..., None]).reshape(v.shape)
+
+
 # ----------------------------------------------------------------------------
 # A1: CSA / HCA KV compression  ([CSDN] CSA step 1, the CComp_i equation;
 # [LQNN] section 5 for the dropped tail; [WIKI] item 1 for the rates).

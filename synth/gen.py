@@ -100,6 +100,48 @@ def e4m3_quantize_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return codes, scale
 
 
+MXFP4_BLOCK = 32
+
+
+def mxfp4_encode_elems(v: np.ndarray) -> np.ndarray:
+    """float -> OCP FP4 E2M1 codes (uint8, low 4 bits), round to nearest even,
+    saturating at +-6.
+
+    Bit layout (OCP Microscaling Formats v1.0, FP4 E2M1): sign(1) exp(2, bias 1)
+    mantissa(1); exponent field 0 is subnormal (0 or 0.5); no inf or NaN. The
+    eight magnitudes in code order are 0, 0.5, 1, 1.5, 2, 3, 4, 6, so the even
+    codes are the ones with mantissa bit 0."""
+    v = np.asarray(v, dtype=np.float64)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    a = np.minimum(np.abs(v), 6.0)
+    d = np.abs(a[..., None] - grid)                       # distance to every magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = np.where(d == best, np.arange(8), 99)          # nearest codes (two on a tie)
+    even = np.where((cand % 2 == 0) & (cand < 99), cand, 99).min(axis=-1)
+    code = np.where(even < 99, even, cand.min(axis=-1))   # a tie goes to the even code
+    sign = (np.signbit(v) & (code > 0)).astype(np.int64)  # -0 encodes as +0
+    return (code | (sign << 3)).astype(np.uint8)
+
+
+def mxfp4_quantize_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """OCP MXFP4 quantization of the last axis in blocks of 32: per block the
+    shared E8M0 exponent is floor(log2(amax)) - 2 (2 = emax of E2M1), kept in
+    1..254 (scale byte 127 for an all-zero block); elements are E2M1 codes of
+    x / 2^(E - 127). Two codes per byte, element 2j in the low nibble of byte j.
+    Returns (codes uint8 [..., D/2], scales uint8 [..., D/32])."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    assert D % MXFP4_BLOCK == 0
+    xb = x.reshape(x.shape[:-1] + (D // MXFP4_BLOCK, MXFP4_BLOCK))
+    amax = np.abs(xb).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2.0, 0.0)
+    E = np.clip(ex + 127.0, 1.0, 254.0).astype(np.int64)
+    codes = mxfp4_encode_elems(xb / np.exp2(E - 127.0)[..., None]).reshape(x.shape)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, E.astype(np.uint8)
+
+
 # ----------------------------------------------------------------------------
 # Workload configurations.
 # ----------------------------------------------------------------------------
@@ -138,7 +180,10 @@ C3 = Cfg("c3_csa_prefill_64k", 3, "csa_prefill", B=1, n=65536, m=4, H=64, D=512,
 C4 = Cfg("c4_hca_decode_1m", 4, "hca_decode", B=16, n=1 << 20, m=128, H=64, D=512, W=128)
 C5 = Cfg("c5_csa_decode_pro_1m_fp8", 5, "csa_decode", B=4, n=1 << 20, m=4, H=64, D=512,
          H_I=64, D_I=128, top_k=1024, W=128, k_dtype="fp8")
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5)}
+# C2 with the indexer keys stored as the pages keep them (FP4; OCP MXFP4 here),
+# same seed and shapes: a measurement of the next step, not one of the five
+C2X = dataclasses.replace(C2, name="c2x_csa_decode_flash_128k_mxfp4", k_dtype="mxfp4")
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X)}
 
 
 def scaled(cfg: Cfg, **kw) -> Cfg:
@@ -181,6 +226,10 @@ def gen_decode_seq(cfg: Cfg, b: int, with_compress: bool = True) -> Dict[str, np
             codes, scale = e4m3_quantize_rows(k)
             out["k_idx_codes"] = codes
             out["k_scale"] = scale
+        elif cfg.k_dtype == "mxfp4":
+            codes, scale = mxfp4_quantize_rows(k)
+            out["k_idx_codes"] = codes  # [N, D_I/2] two codes per byte
+            out["k_scale"] = scale      # [N, D_I/32] E8M0 bytes
         else:
             out["k_idx"] = _store(k, cfg.dtype)
         if with_compress:

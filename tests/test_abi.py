@@ -71,6 +71,12 @@ def test_indexer_validation():
     assert f(None, P, P, None, P, P, 1, 1, 64, 128, 100, 4, 1, 1, P, None) == L.INVALID_ARG
     # fp8 keys without scale
     assert f(P, P, P, None, P, P, 1, 1, 64, 128, 100, 4, 1, 2, P, None) == L.INVALID_ARG
+    # MXFP4 keys: need scales, D_I a multiple of 32, 4-byte aligned scales; dtype 4 is unknown
+    assert f(P, P, P, None, P, P, 1, 1, 64, 128, 100, 4, 1, 3, P, None) == L.INVALID_ARG
+    assert "MXFP4" in _err()
+    assert f(P, P, P, P, P, P, 1, 1, 64, 48, 100, 4, 1, 3, P, None) == L.INVALID_ARG
+    assert f(P, P, P, P + 2, P, P, 1, 1, 64, 128, 100, 4, 1, 3, P, None) == L.INVALID_ARG
+    assert f(P, P, P, P, P, P, 1, 1, 64, 128, 100, 4, 1, 4, P, None) == L.INVALID_ARG
     # unsupported head shape
     assert f(P, P, P, None, P, P, 1, 1, 32, 128, 100, 4, 1, 1, P, None) == L.UNSUPPORTED
     # fp32 keys with bf16 queries

@@ -106,6 +106,11 @@ def _indexer_case(B, Tq, N_max, n_comp, q_pos, m, top_k, kdt, seed=0, H_I=64, D_
         kval = oracle.e4m3_decode(codes)
         k_t = dev(codes)
         sc_t = dev(scale)
+    elif kdt == "mxfp4":
+        codes, sc = gen.mxfp4_quantize_rows(k)
+        kval = oracle.mxfp4_decode(codes, sc)  # block scales are part of the key values
+        k_t = dev(codes).view(torch.float4_e2m1fn_x2)
+        sc_t = dev(sc)
     elif kdt == "bf16":
         k = gen.bf16_round(k)
         kval = k
@@ -131,7 +136,8 @@ def _indexer_case(B, Tq, N_max, n_comp, q_pos, m, top_k, kdt, seed=0, H_I=64, D_
         for t in range(Tq):
             V = oracle.visible(qpos[b, t], n_comp[b], m)
             V = min(V, N_max)
-            ref = oracle.indexer_scores(q_idx[b, t], w[b, t], kval[b], V, None if scale is None else scale[b])
+            ref = oracle.indexer_scores(q_idx[b, t], w[b, t], kval[b], V,
+                                        None if (scale is None or kdt == "mxfp4") else scale[b])
             got = S[b, t, :V]
             err = np.abs(got - ref).max() if V else 0.0
             # fp32 accumulation of bf16 products over 128 dims, 64 heads
@@ -152,6 +158,18 @@ def test_indexer_bf16_decode():
 
 def test_indexer_fp8_decode():
     _indexer_case(2, 1, 2100, [2100, 2100], [8399, 5000], 4, 256, "fp8", seed=11)
+
+
+def test_indexer_mxfp4_decode():
+    # MXFP4 keys (OCP FP4 E2M1, E8M0 scale per 32 dims): ragged tail of the
+    # 256-entry tiles, a short sequence
+    _indexer_case(3, 1, 2300, [2300, 1777, 9], [9199, 9199, 9199], 4, 256, "mxfp4", seed=14)
+
+
+def test_indexer_mxfp4_prefill_rows():
+    pos = np.sort(_g(15).integers(0, 2400, 40))
+    pos[:3] = [0, 2, 3]  # V = 0, 0, 1
+    _indexer_case(1, 40, 600, [600], pos, 4, 32, "mxfp4", seed=15)
 
 
 def test_indexer_bf16_prefill_rows():

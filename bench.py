@@ -13,7 +13,10 @@ Inputs are synthetic (seeded generator), resident in HBM before timing, and
 rotated over several device replicas so that no step reads cache-resident
 data from the previous one.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c5|c4|c3|c2x]
+Other workloads: c5 (1M context, E4M3 indexer keys), c2x (c2 with MXFP4
+indexer keys), c4 (HCA decode 1M), c3 (CSA prefill 64K), c6 (HCA prefill 64K).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c5|c4|c3|c2x|c6]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -41,7 +44,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4", "c3", "c2x"])
+    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4", "c3", "c2x", "c6"])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -104,6 +107,8 @@ def main():
         return
     if a.workload == "c3":
         return bench_prefill(a, torch, L, gen, dev)
+    if a.workload == "c6":
+        return bench_hca_prefill(a, torch, L, gen, dev)
     cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X}[a.workload]
     t0 = time.time()
     x = gen.gen_decode(cfg, with_compress=(cfg.kind == "csa_decode"))
@@ -339,7 +344,7 @@ def bench_prefill(a, torch, L, gen, dev):
                    "window": W},
         "prefill_tflops": round(total_fl / (ms * 1e-3) / 1e12, 2),
         "algorithmic_tflop": round(total_fl / 1e12, 3),
-        "roofline": {"bound": "mfma", "kernel": "attn_prs_kernel (sparse prefill)", "achieved": round(mqa_tfs, 1),
+        "roofline": {"bound": "mfma", "kernel": "attn_prs_kernel<2> (sparse prefill)", "achieved": round(mqa_tfs, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mqa_tfs / BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flops_all_launches": mqa_fl,
                      "avg_launch_ms": round(float(np.mean(attn_ms)), 4)},
@@ -352,6 +357,108 @@ def bench_prefill(a, torch, L, gen, dev):
     if not a.no_cpu:
         res["cpu_baseline"] = cpu_prefill_baseline(cfg, tok, a.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def hca_prefill_rows(cfg, pos):
+    """Rows each query attends in HCA prefill: V(p) entries plus its window."""
+    pos = pos.astype(np.int64)
+    return np.minimum(cfg.N, (pos + 1) // cfg.m) + np.minimum(cfg.W, pos + 1)
+
+
+def bench_hca_prefill(a, torch, L, gen, dev):
+    """HCA prefill of one 65536-token sequence: single-branch compression of
+    all tokens at m' = 128, then 16 chunks of 4096 queries through hca_prefill
+    (every visible entry plus the window and the sink)."""
+    cfg = gen.C6
+    t0 = time.time()
+    tok = gen.gen_prefill_tokens(cfg)
+    bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).to(dev)
+    td = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+    N, m, D, H, W = cfg.N, cfg.m, cfg.D, cfg.H, cfg.W
+    Ca, Za, Ba, sink = bf(tok["Ca"][None]), bf(tok["Za"][None]), td(tok["Ba"]), td(tok["sink"])
+    kv_tok = bf(tok["kv_tok"])
+    comp = torch.empty((1, N, D), dtype=torch.bfloat16, device=dev)
+    nch = gen.num_chunks(cfg)
+    chunks = []
+    for c in range(nch):
+        qs = gen.gen_prefill_queries(cfg, c)
+        chunks.append({"q": bf(qs["q"]), "q_pos": td(qs["q_pos"]), "pos_np": qs["q_pos"]})
+    print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    T = gen.QCHUNK
+    out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    def run(ev=None):
+        if ev is not None: ev[0].record(stream)
+        L.csa_compress(Ca, None, Za, None, Ba, None, comp, m=m, overlap=False, stream=s)
+        if ev is not None: ev[1].record(stream)
+        for c, ch in enumerate(chunks):
+            L.hca_prefill(ch["q"], comp[0], kv_tok, ch["q_pos"], sink, out, m=m, W=W, stream=s)
+            if ev is not None: ev[2 + c].record(stream)
+
+    for _ in range(max(1, a.warmup)):
+        run()
+    torch.cuda.synchronize()
+    steps = max(1, min(a.steps, 5))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + nch)]
+    run(ev)
+    torch.cuda.synchronize()
+    comp_ms = ev[0].elapsed_time(ev[1])
+    attn_ms = [ev[1 + c].elapsed_time(ev[2 + c]) for c in range(nch)]
+    rows = [float(hca_prefill_rows(cfg, ch["pos_np"]).sum()) for ch in chunks]
+    mqa_fl = sum(rows) * H * D * 4
+    mqa_tfs = mqa_fl / (sum(attn_ms) * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(cfg.n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": max(1, a.warmup), "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.n, "query_chunk": T, "compressed_entries": N, "m": m,
+                   "heads": H, "head_dim": D, "window": W},
+        "prefill_tflops": round(mqa_fl / (ms * 1e-3) / 1e12, 2),
+        "algorithmic_tflop": round(mqa_fl / 1e12, 3),
+        "roofline": {"bound": "mfma", "kernel": "attn_prs_kernel<3> (HCA prefill)", "achieved": round(mqa_tfs, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mqa_tfs / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_all_launches": mqa_fl,
+                     "avg_launch_ms": round(float(np.mean(attn_ms)), 4)},
+        "phases_ms": {"compress": round(comp_ms, 4), "attention_total": round(sum(attn_ms), 4)},
+    }
+    if not a.no_cpu:
+        res["cpu_baseline"] = cpu_hca_prefill_baseline(cfg, tok, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_hca_prefill_baseline(cfg, tok, budget_s: float):
+    """The oracle on the host: single-branch compression of the whole
+    sequence, then queries of the last chunk one by one until the budget is
+    spent; extrapolated to all queries by attended-row counts."""
+    import oracle
+    from synth import gen
+    t0 = time.perf_counter()
+    comp = oracle.compress(tok["Ca"], None, tok["Za"], None, tok["Ba"], None, cfg.m, overlap=False)
+    t_comp = time.perf_counter() - t0
+    qs = gen.gen_prefill_queries(cfg, gen.num_chunks(cfg) - 1)
+    t1 = time.perf_counter()
+    done, rows = 0, 0.0
+    while done < len(qs["q_pos"]) and (done == 0 or time.perf_counter() - t1 < budget_s):
+        i = len(qs["q_pos"]) - 1 - done
+        p = int(qs["q_pos"][i])
+        oracle.hca_query(qs["q"][i], comp, p, cfg.N, cfg.m, oracle.window_rows(tok["kv_tok"], p, cfg.W), tok["sink"])
+        rows += float(hca_prefill_rows(cfg, np.array([p]))[0])
+        done += 1
+    t_q = time.perf_counter() - t1
+    all_rows = float(hca_prefill_rows(cfg, gen.query_positions(cfg)).sum())
+    est = t_comp + t_q * all_rows / max(rows, 1.0)
+    return {"value": round(cfg.n / est, 3), "unit": "tokens/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"compression of all {cfg.n} tokens ({t_comp:.1f}s) + {done} queries of the last chunk "
+                      f"({t_q:.1f}s), extrapolated to all queries by attended-row counts"}
 
 
 def cpu_prefill_baseline(cfg, tok, budget_s: float):

@@ -215,6 +215,21 @@ int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, con
                   void* ws, size_t ws_bytes, void* stream);
 size_t hca_dense_mqa_workspace_bytes(int64_t B, int H, int D, int64_t N_max, int W);
 
+/* hca_prefill — HCA for Tq queries of one sequence ([CSDN] HCA: dense
+ * attention over every compressed entry a query can see, plus the
+ * [LIDUOS] window and sink). Query t at position p = q_pos[t] attends to
+ *   R = kv_comp[0 .. V-1] + kv_tok[max(0, p-W+1) .. min(p, T_tok-1)],
+ *   V = min(N, floor((p+1)/m))  (an entry exists once its m tokens are in).
+ *   q      : [Tq, H, D]          kv_comp : [N, D] (the HCA entries, m = m')
+ *   kv_tok : [T_tok, D] raw per-token KV      q_pos : [Tq] int32, >= 0
+ *   out    : [Tq, H, D] in out_dt             lse   : [Tq, H] (nullable)
+ * No limit on V beyond N + W <= 2^24 (rows are read in order, not from a
+ * table). Needs no workspace (ws may be NULL). */
+int hca_prefill(const void* q, const void* kv_comp, const void* kv_tok, const int32_t* q_pos, const float* sink,
+                float scale, int64_t Tq, int H, int D, int64_t N, int m, int64_t T_tok, int W, int kv_dt,
+                int out_dt, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+size_t hca_prefill_workspace_bytes(int64_t Tq, int H, int D, int64_t N, int W);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,9 @@ _SIGS = {
     "hca_dense_mqa": ([_vp] * 4 + [_i32, _vp, _vp, _vp, _f32, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                                    _vp, _sz, _vp], _i32),
     "hca_dense_mqa_workspace_bytes": ([_i64, _i32, _i32, _i64, _i32], _sz),
+    "hca_prefill": ([_vp] * 5 + [_f32, _i64, _i32, _i32, _i64, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
+                                 _vp], _i32),
+    "hca_prefill_workspace_bytes": ([_i64, _i32, _i32, _i64, _i32], _sz),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -206,6 +209,21 @@ def sparse_mqa_prefill(q, kv_comp, topk_idx, kv_tok, q_pos, sink, out, lse=None,
     _check(lib.sparse_mqa_prefill(_ptr(q), _ptr(kv_comp), _ptr(topk_idx), _ptr(kv_tok), _ptr(q_pos), _ptr(sink),
                                   scale, Tq, H, D, N, T_tok, top_k, W, _dt(q), _dt(out), _ptr(out), _ptr(lse),
                                   _ptr(ws), nb, _stream(stream)))
+
+
+def hca_prefill_workspace_bytes(Tq: int, H: int, D: int, N: int, W: int) -> int:
+    return lib.hca_prefill_workspace_bytes(Tq, H, D, N, W)
+
+
+def hca_prefill(q, kv_comp, kv_tok, q_pos, sink, out, lse=None, *, m: int, W: int, scale: float = 1.0,
+                ws=None, stream=None) -> None:
+    """q [Tq, H, D]; kv_comp [N, D] (HCA entries); kv_tok [T_tok, D]; q_pos [Tq]."""
+    Tq, H, D = q.shape
+    N = kv_comp.shape[0] if kv_comp is not None else 0
+    T_tok = kv_tok.shape[0] if kv_tok is not None else 0
+    ws, nb = _ws(hca_prefill_workspace_bytes(Tq, H, D, N, W), ws, q.device)
+    _check(lib.hca_prefill(_ptr(q), _ptr(kv_comp), _ptr(kv_tok), _ptr(q_pos), _ptr(sink), scale, Tq, H, D, N, m,
+                           T_tok, W, _dt(q), _dt(out), _ptr(out), _ptr(lse), _ptr(ws), nb, _stream(stream)))
 
 
 def hca_dense_mqa_workspace_bytes(B: int, H: int, D: int, N_max: int, W: int) -> int:

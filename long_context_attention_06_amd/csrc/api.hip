@@ -294,6 +294,47 @@ int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_i
   return hip_status(csa::run_attn(a, (hipStream_t)stream), "sparse_mqa_prefill");
 }
 
+size_t hca_prefill_workspace_bytes(int64_t, int, int, int64_t, int) { return 0; }
+
+int hca_prefill(const void* q, const void* kv_comp, const void* kv_tok, const int32_t* q_pos, const float* sink,
+                float scale, int64_t Tq, int H, int D, int64_t N, int m, int64_t T_tok, int W, int kv_dt, int out_dt,
+                void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, 0);
+  if (rc) return rc;
+  REQ(Tq >= 0 && N >= 0 && T_tok >= 0, CSA_INVALID_ARG, "Tq, N, T_tok must be >= 0");
+  REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");
+  REQ(q_pos, CSA_INVALID_ARG, "q_pos must not be NULL");
+  REQ(N == 0 || kv_comp, CSA_INVALID_ARG, "kv_comp must not be NULL");
+  REQ(W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
+  REQ(N + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
+  REQ(Tq <= 0x7fffffff, CSA_UNSUPPORTED, "Tq too large");
+  csa::AttnLaunch a{};
+  a.src = 3;
+  a.q = q;
+  a.kv_comp = kv_comp;
+  a.kv_win = kv_tok;
+  a.q_pos = q_pos;
+  a.sink = sink;
+  a.scale = scale;
+  a.nq = Tq;
+  a.N_max = N;
+  a.T_tok = T_tok;
+  a.H = H;
+  a.D = D;
+  a.W = W;
+  a.m_rate = m;
+  a.kv_dt = kv_dt;
+  a.out_dt = out_dt;
+  a.slots = (int)(N + W);
+  a.split_rows = a.slots;
+  a.nsplit = 1;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(csa::run_attn(a, (hipStream_t)stream), "hca_prefill");
+}
+
 size_t hca_dense_mqa_workspace_bytes(int64_t B, int H, int D, int64_t N_max, int W) {
   if (B < 0 || H <= 0 || D <= 0 || N_max < 0 || W < 0) return 0;
   return attn_ws(B, H, D, nsplit_for(N_max + W, hca_split_rows(N_max + W)));

@@ -37,7 +37,7 @@
 
 namespace csa {
 
-enum { SRC_SPARSE_DEC = 0, SRC_HCA_DEC = 1, SRC_SPARSE_PRE = 2 };
+enum { SRC_SPARSE_DEC = 0, SRC_HCA_DEC = 1, SRC_SPARSE_PRE = 2, SRC_HCA_PRE = 3 };
 
 // XOR swizzle of the 16-byte chunk index inside each 256-byte group of a
 // tile row (rows are 1 KB, so every row starts in bank group 0). A b128 read
@@ -90,6 +90,12 @@ __device__ __forceinline__ const uint8_t* slot_row(const RowSrc& s, int64_t qi, 
     int64_t tok = (int64_t)lim1 - s.W + 1 + w;
     if (tok < 0 || tok >= s.T_tok) return nullptr;
     return s.kv_win + tok * ROWB;
+  } else if (SRC == SRC_HCA_PRE) {
+    // lim0: visible entries V(p); lim1: position p
+    if (j < s.N_max) return j < lim0 ? s.kv_comp + (int64_t)j * ROWB : nullptr;
+    const int64_t tok = (int64_t)lim1 - s.W + 1 + (j - s.N_max);
+    if (tok < 0 || tok >= s.T_tok) return nullptr;
+    return s.kv_win + tok * ROWB;
   } else {
     if (j < s.N_max) {
       if (j >= lim0) return nullptr;
@@ -131,12 +137,12 @@ constexpr int TAB_MAX = 2048;     // rows of one workgroup for the table-driven 
 // the row sources, where the compressed and window rows live, and the split's
 // compacted row list (HCA: two contiguous ranges; sparse: a table in LDS).
 struct QRows {
-  int lim0, lim1;  // SPARSE_DEC: window length; HCA: V, window length; PRE: -, position
+  int lim0, lim1;  // SPARSE_DEC: window length; HCA: V, window length; PRE: -, position; HCA_PRE: V, position
   int s_begin, s_end;
   const uint8_t* comp_base;
   const uint8_t* win_base;
   int n_rows;    // rows after dropping invalid slots
-  int len1, w0;  // HCA: rows taken from the compressed range; first window row
+  int len1, w0;  // HCA: rows taken from the compressed range; first window row (HCA_PRE: token)
 };
 
 template <int SRC>
@@ -155,13 +161,18 @@ __device__ __forceinline__ QRows query_rows(const RowSrc& src, const int32_t* __
       r.lim0 = (int)max((int64_t)0, min(v, src.N_max));
     }
     r.lim1 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
+  } else if (SRC == SRC_HCA_PRE) {
+    r.lim1 = q_pos[qi];
+    const int64_t v = min(((int64_t)r.lim1 + 1) / m_rate, src.N_max);
+    r.lim0 = (int)max((int64_t)0, v);
   } else {
     r.lim1 = q_pos[qi];
   }
   r.s_begin = sp * split_rows;
   r.s_end = min(slots, r.s_begin + split_rows);
-  r.comp_base = src.kv_comp + (SRC == SRC_SPARSE_PRE ? 0 : qi * src.N_max * ROWB);
-  r.win_base = src.kv_win + (SRC == SRC_SPARSE_PRE ? 0 : qi * (int64_t)src.W * ROWB);
+  constexpr bool PRE = SRC == SRC_SPARSE_PRE || SRC == SRC_HCA_PRE;  // one sequence: shared caches
+  r.comp_base = src.kv_comp + (PRE ? 0 : qi * src.N_max * ROWB);
+  r.win_base = src.kv_win + (PRE ? 0 : qi * (int64_t)src.W * ROWB);
   r.n_rows = r.len1 = r.w0 = 0;
   if (SRC == SRC_HCA_DEC) {
     // slots [0, N_max) are compressed entries (valid below V), then the window
@@ -169,6 +180,13 @@ __device__ __forceinline__ QRows query_rows(const RowSrc& src, const int32_t* __
     const int a2 = max(r.s_begin, (int)src.N_max), b2 = min(r.s_end, (int)src.N_max + r.lim1);
     r.w0 = a2 - (int)src.N_max;
     r.n_rows = r.len1 + max(0, b2 - a2);
+  } else if (SRC == SRC_HCA_PRE) {
+    // entries 0 .. V-1, then the window tokens max(0, p-W+1) .. min(p, T_tok-1)
+    const int64_t first = max((int64_t)0, (int64_t)r.lim1 - src.W + 1);
+    const int64_t last = min((int64_t)r.lim1, src.T_tok - 1);
+    r.len1 = r.lim0;
+    r.w0 = (int)first;
+    r.n_rows = r.len1 + (int)max((int64_t)0, last - first + 1);
   }
   return r;
 }
@@ -518,17 +536,18 @@ constexpr int PSTR = 40;         // bf16 per head row of a P^T buffer: 32 rows +
 constexpr float GUARD = 64.0f;   // log2 units a logit may sit above the shared reference
 }  // namespace prs
 
+template <int SRC>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __restrict__ q_pos,
+attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __restrict__ q_pos, int m_rate,
                 const float* __restrict__ sink, float scale_log2, int H, int slots, void* __restrict__ out,
                 float* __restrict__ lse, int out_dt) {
   using namespace prs;
-  constexpr int SRC = SRC_SPARSE_PRE;
+  static_assert(SRC == SRC_SPARSE_PRE || SRC == SRC_HCA_PRE, "prefill row sources");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TILEB];
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][2][32 * PSTR];  // [tile parity][head group] P^T
   __shared__ __attribute__((aligned(16))) float lmx[2][2][2][64];          // [head group][row half][hq][lane]
   __shared__ __attribute__((aligned(16))) int flg[2][NW];                  // [tile parity][wave]: P must be redone
-  __shared__ __attribute__((aligned(16))) int tab[TAB_MAX];
+  __shared__ __attribute__((aligned(16))) int tab[SRC == SRC_HCA_PRE ? 4 : TAB_MAX];
   __shared__ int cnt[2 * NW];
 
   const int tid = threadIdx.x;
@@ -542,7 +561,7 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   // softmax head of hq = (l >> 4) & 1, dims 256 dh + 32 nt + 8 (r/4) + 4 h + r%4.
   const int ohq = (l >> 4) & 1;
 
-  QRows rr = query_rows<SRC>(src, nullptr, nullptr, q_pos, 1, qi, 0, slots, slots);
+  QRows rr = query_rows<SRC>(src, nullptr, nullptr, q_pos, m_rate, qi, 0, slots, slots);
 
   // ---- Q^T operand (B of S = K Q^T): head 32 hg + 16 hq + l16, dims 32 ks + 8 gc
   // .. +7 with gc = the two bits of g16 swapped (the K operand takes the same
@@ -558,8 +577,10 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
     for (int ks = 0; ks < 16; ++ks) qb[hq][ks] = as_bf16x8(hok ? ld16(qp + 32 * ks) : u32x4_t{0, 0, 0, 0});
   }
 
-  int n_comp_rows = 0;
-  rr.n_rows = build_row_table<SRC, NT, TR>(src, rr, qi, tab, cnt, &n_comp_rows);
+  // sparse: a row table in LDS; HCA: rows are entries 0 .. V-1 and then the
+  // window tokens, addressed arithmetically
+  int n_comp_rows = rr.len1;
+  if (SRC == SRC_SPARSE_PRE) rr.n_rows = build_row_table<SRC, NT, TR>(src, rr, qi, tab, cnt, &n_comp_rows);
   const int n_rows = rr.n_rows;
   const int ntiles = (n_rows + TR - 1) / TR;
   // table entries below ncb are compressed rows, the rest window rows (the
@@ -576,6 +597,17 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   auto issue = [&](int t) {
     const int c0 = t * TR + RPW * w;
     const uint32_t dst = ring_lds + (uint32_t)((t & (NBUF - 1)) * TILEB + RPW * w * ROWB);
+    if constexpr (SRC == SRC_HCA_PRE) {
+      // rows past the end repeat the last row (they are masked)
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int c = min(c0 + i, n_rows - 1);
+        const uint8_t* rp = c < rr.len1 ? rr.comp_base + (int64_t)c * ROWB
+                                        : rr.win_base + (int64_t)(rr.w0 + c - rr.len1) * ROWB;
+        dma_row(uniform_ptr(rp), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+      }
+      return;
+    }
     const u32x4_t e0 = *reinterpret_cast<const u32x4_t*>(&tab[c0]);
     const u32x4_t e1 = *reinterpret_cast<const u32x4_t*>(&tab[c0 + 4]);
     const bool comp_only = c0 + RPW <= ncb, win_only = c0 >= ncb;
@@ -923,7 +955,7 @@ attn_f32_kernel(const float* __restrict__ q, RowSrc src, const int32_t* __restri
   constexpr int CODE_MAX = 1024;   // top-k slots per split staged in LDS
   __shared__ __attribute__((aligned(16))) uint8_t lds_r[2][TR * RPITCH];
   __shared__ int lds_valid[2][TR];
-  __shared__ int lds_code[(SRC == SRC_HCA_DEC) ? 1 : CODE_MAX];
+  __shared__ int lds_code[(SRC == SRC_HCA_DEC || SRC == SRC_HCA_PRE) ? 1 : CODE_MAX];
 
   const int tid = threadIdx.x;
   const int l = tid & 63, wv = tid >> 6;
@@ -942,6 +974,9 @@ attn_f32_kernel(const float* __restrict__ q, RowSrc src, const int32_t* __restri
       lim0 = (int)max((int64_t)0, min(v, src.N_max));
     }
     lim1 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
+  } else if (SRC == SRC_HCA_PRE) {
+    lim1 = q_pos[qi];
+    lim0 = (int)max((int64_t)0, min(((int64_t)lim1 + 1) / m_rate, src.N_max));
   } else {
     lim1 = q_pos[qi];
   }
@@ -977,7 +1012,7 @@ attn_f32_kernel(const float* __restrict__ q, RowSrc src, const int32_t* __restri
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
       const int j = base + lrs + ps * RPP;
-      const int code = (j < s_end && j - s_begin < CODE_MAX && (SRC != SRC_HCA_DEC) && j < src.top_k)
+      const int code = (j < s_end && j - s_begin < CODE_MAX && (SRC == SRC_SPARSE_DEC || SRC == SRC_SPARSE_PRE) && j < src.top_k)
                            ? lds_code[j - s_begin] : -1;
       const uint8_t* rp = (j < s_end) ? slot_row<SRC, ROWB>(src, qi, j, code, lim0, lim1) : nullptr;
       vm |= (rp != nullptr ? 1u : 0u) << ps;
@@ -1280,11 +1315,12 @@ static hipError_t launch_bf16(const AttnLaunch& a, hipStream_t st) {
   return launch_combine(a, st);
 }
 
+template <int SRC>
 static hipError_t launch_pre32(const AttnLaunch& a, hipStream_t st) {
-  if (a.nsplit != 1 || a.slots > prs::TAB_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_prs_kernel, dim3((unsigned)a.nq), dim3(prs::NT), 0, st,
-                     reinterpret_cast<const uint16_t*>(a.q), row_src(a), a.q_pos, a.sink, a.scale * LOG2E_F, a.H,
-                     a.slots, a.out, a.lse, a.out_dt);
+  if (a.nsplit != 1 || (SRC == SRC_SPARSE_PRE && a.slots > prs::TAB_MAX)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_prs_kernel<SRC>), dim3((unsigned)a.nq), dim3(prs::NT), 0, st,
+                     reinterpret_cast<const uint16_t*>(a.q), row_src(a), a.q_pos, a.m_rate, a.sink,
+                     a.scale * LOG2E_F, a.H, a.slots, a.out, a.lse, a.out_dt);
   return hipGetLastError();
 }
 
@@ -1303,8 +1339,14 @@ static hipError_t launch_f32(const AttnLaunch& a, hipStream_t st) {
 template <int SRC>
 static hipError_t dispatch_src(const AttnLaunch& a, hipStream_t st) {
   if (a.kv_dt == DT_BF16 && a.D == 512 && a.H > 48 && a.H <= 64) {
-    if (SRC == SRC_SPARSE_PRE && a.nsplit == 1) return launch_pre32(a, st);
-    return launch_bf16<SRC>(a, st);
+    if constexpr (SRC == SRC_HCA_PRE) {
+      return launch_pre32<SRC>(a, st);
+    } else if constexpr (SRC == SRC_SPARSE_PRE) {
+      if (a.nsplit == 1) return launch_pre32<SRC>(a, st);
+      return launch_bf16<SRC>(a, st);
+    } else {
+      return launch_bf16<SRC>(a, st);
+    }
   }
   if (a.kv_dt == DT_F32 && a.D == 64 && a.H <= 16) return launch_f32<64, 1, SRC>(a, st);
   return hipErrorInvalidValue;
@@ -1315,6 +1357,7 @@ hipError_t run_attn(const AttnLaunch& a, hipStream_t st) {
   switch (a.src) {
     case 0: return dispatch_src<SRC_SPARSE_DEC>(a, st);
     case 1: return dispatch_src<SRC_HCA_DEC>(a, st);
+    case 3: return dispatch_src<SRC_HCA_PRE>(a, st);
     default: return dispatch_src<SRC_SPARSE_PRE>(a, st);
   }
 }

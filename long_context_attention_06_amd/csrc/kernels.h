@@ -46,7 +46,7 @@ size_t topk_ws_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k);
 hipError_t run_topk(const TopkLaunch& a, hipStream_t st);
 
 struct AttnLaunch {
-  int src;  // 0 sparse decode, 1 HCA decode, 2 sparse prefill
+  int src;  // 0 sparse decode, 1 HCA decode, 2 sparse prefill, 3 HCA prefill
   const void* q;
   const void* kv_comp;
   const int32_t* idx;

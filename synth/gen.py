@@ -150,7 +150,7 @@ def mxfp4_quantize_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 class Cfg:
     name: str
     seed: int
-    kind: str            # "tiny" | "csa_decode" | "csa_prefill" | "hca_decode"
+    kind: str            # "tiny" | "csa_decode" | "csa_prefill" | "hca_decode" | "hca_prefill"
     B: int               # sequences (decode) / 1 (prefill)
     n: int               # context length in tokens
     m: int               # compression rate
@@ -183,7 +183,10 @@ C5 = Cfg("c5_csa_decode_pro_1m_fp8", 5, "csa_decode", B=4, n=1 << 20, m=4, H=64,
 # C2 with the indexer keys stored as the pages keep them (FP4; OCP MXFP4 here),
 # same seed and shapes: a measurement of the next step, not one of the five
 C2X = dataclasses.replace(C2, name="c2x_csa_decode_flash_128k_mxfp4", k_dtype="mxfp4")
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X)}
+# HCA prefill of one 64K sequence: single-branch compression at m' = 128
+# (512 entries), then every query over all entries it can see plus its window
+C6 = Cfg("c6_hca_prefill_64k", 6, "hca_prefill", B=1, n=65536, m=128, H=64, D=512, W=128, Tq=65536)
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6)}
 
 
 def scaled(cfg: Cfg, **kw) -> Cfg:
@@ -269,12 +272,16 @@ def gen_prefill_tokens(cfg: Cfg) -> Dict[str, np.ndarray]:
     compression inputs [n, D], raw KV [n, D] for the window, indexer keys
     [N, D_I] (one per compressed entry)."""
     s, n, D = cfg.seed, cfg.n, cfg.D
+    hca = cfg.kind == "hca_prefill"  # one branch, no indexer
     out = {}
-    for nm in ("Ca", "Cb", "Za", "Zb"):
+    for nm in (("Ca", "Za") if hca else ("Ca", "Cb", "Za", "Zb")):
         out[nm] = _store(_normal(rng(s, nm), (n, D)), cfg.dtype)
     out["kv_tok"] = _store(_normal(rng(s, "kv_tok"), (n, D)), cfg.dtype)
-    out["k_idx"] = _store(_normal(rng(s, "k_idx"), (cfg.N, cfg.D_I)), cfg.dtype)
+    if not hca:
+        out["k_idx"] = _store(_normal(rng(s, "k_idx"), (cfg.N, cfg.D_I)), cfg.dtype)
     out.update(gen_shared(cfg))
+    if hca:
+        del out["Bb"]
     return out
 
 
@@ -293,12 +300,14 @@ def gen_prefill_queries(cfg: Cfg, chunk: int) -> Dict[str, np.ndarray]:
     hi = min(lo + QCHUNK, cfg.Tq)
     T = hi - lo
     qscale = 1.0 / math.sqrt(cfg.D) if cfg.kind != "tiny" else 1.0 / 8.0
-    qi_scale = 1.0 / math.sqrt(cfg.D_I) if cfg.kind != "tiny" else 1.0
     out = {
         "q": _store(_normal(rng(s, "q", chunk), (T, cfg.H, cfg.D), qscale), cfg.dtype),
-        "q_idx": _store(_normal(rng(s, "q_idx", chunk), (T, cfg.H_I, cfg.D_I), qi_scale), cfg.dtype),
         "q_pos": query_positions(cfg)[lo:hi].copy(),
     }
+    if cfg.kind == "hca_prefill":  # no indexer
+        return out
+    qi_scale = 1.0 / math.sqrt(cfg.D_I) if cfg.kind != "tiny" else 1.0
+    out["q_idx"] = _store(_normal(rng(s, "q_idx", chunk), (T, cfg.H_I, cfg.D_I), qi_scale), cfg.dtype)
     g = rng(s, "w", chunk)
     if cfg.kind == "tiny":
         out["w"] = g.uniform(0.0, 1.0, size=(T, cfg.H_I)).astype(np.float32)

@@ -23,7 +23,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
     missing = [n for n in names if n not in exported]
@@ -122,3 +122,14 @@ def test_attention_validation():
     # f32 rows stage at most 1024 top-k slots; bf16 rows take any top_k with top_k + W <= 2048
     assert p(P, P, P, P, P, P, 1.0, 4, 16, 64, 2000, 4000, 1025, 8, 0, 0, P, None, None, 0, None) == L.UNSUPPORTED
     assert "top_k <= 1024" in _err()
+    hp = L.lib.hca_prefill
+    # q_pos null; m = 0; unsupported heads; N + W beyond 2^24; bad scale
+    assert hp(P, P, P, None, P, 1.0, 4, 64, 512, 512, 128, 65536, 128, 1, 1, P, None, None, 0, None) == L.INVALID_ARG
+    assert hp(P, P, P, P, P, 1.0, 4, 64, 512, 512, 0, 65536, 128, 1, 1, P, None, None, 0, None) == L.INVALID_ARG
+    assert "m must be" in _err()
+    assert hp(P, P, P, P, P, 1.0, 4, 32, 512, 512, 128, 65536, 128, 1, 1, P, None, None, 0, None) == L.UNSUPPORTED
+    assert hp(P, P, P, P, P, 1.0, 4, 64, 512, 1 << 24, 128, 65536, 128, 1, 1, P, None, None, 0, None) == \
+        L.UNSUPPORTED
+    assert hp(P, P, P, P, P, 0.0, 4, 64, 512, 512, 128, 65536, 128, 1, 1, P, None, None, 0, None) == L.INVALID_ARG
+    # no entries and no window is valid (out = 0 or the sink alone); kv_comp may then be null
+    assert L.hca_prefill_workspace_bytes(4096, 64, 512, 8192, 128) == 0

@@ -377,6 +377,60 @@ def test_sparse_prefill(H, k, N, with_sink):
         assert np.abs(LS[t] - rlse).max() < 1e-3
 
 
+@pytest.mark.parametrize("H,m,N,T_tok,with_sink", [(64, 128, 40, 5300, True), (49, 4, 3000, 12100, False),
+                                                   (57, 16, 300, 4900, True)])
+def test_hca_prefill(H, m, N, T_tok, with_sink):
+    """HCA prefill rows: entries 0 .. V(p)-1 and the window. Queries with no
+    entry yet (p < m-1), the first entry (p = m-1), V capped by N, positions
+    past the last token (window clipped), rows beyond the sparse path's
+    2048-row table (m = 4, N = 3000), and heads that leave part of the second
+    32-head group empty."""
+    _say(f"hca_prefill H={H} m={m} N={N}")
+    g = _g(60 + H)
+    Tq, D, W = 44, 512, 128
+    q = gen.bf16_round(g.standard_normal((Tq, H, D)).astype(np.float32) / math.sqrt(D))
+    kv = gen.bf16_round(g.standard_normal((N, D)).astype(np.float32))
+    tok = gen.bf16_round(g.standard_normal((T_tok, D)).astype(np.float32))
+    pos = np.sort(g.integers(0, T_tok, Tq)).astype(np.int32)
+    pos[:4] = [0, m - 2 if m > 1 else 0, m - 1, m]
+    pos[-2:] = [T_tok + 60, T_tok + 500]  # window partly / wholly past the tokens
+    pos = np.sort(pos)
+    sink = g.standard_normal(H).astype(np.float32) if with_sink else None
+    out = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((Tq, H), device=DEV)
+    L.hca_prefill(bf(q), bf(kv), bf(tok), dev(pos), dev(sink) if with_sink else None, out, lse, m=m, W=W)
+    torch.cuda.synchronize()
+    O, LS = host(out), host(lse)
+    s_ref = sink if with_sink else np.full(H, -np.inf)
+    for t in range(Tq):
+        p = int(pos[t])
+        ref, rlse = oracle.hca_query(q[t], kv, p, N, m, oracle.window_rows(tok, p, W), s_ref)
+        check_out(O[t], ref, _attn_tight(ref), f"hca prefill t={t} p={p}")
+        assert np.abs(LS[t] - rlse).max() < 1e-3
+
+
+def test_hca_prefill_tiny_f32():
+    """The fp32 small-head path (C1 shapes) through the same entry point."""
+    _say("hca_prefill f32")
+    g = _g(70)
+    Tq, H, D, N, m, T_tok, W = 64, 4, 64, 256, 4, 1024, 16
+    q = (g.standard_normal((Tq, H, D)) / 8.0).astype(np.float32)
+    kv = g.standard_normal((N, D)).astype(np.float32)
+    tok = g.standard_normal((T_tok, D)).astype(np.float32)
+    pos = np.sort(np.concatenate([[0, 2, 3, 4], g.integers(0, T_tok, Tq - 4)])).astype(np.int32)
+    sink = np.zeros(H, np.float32)
+    out = torch.empty((Tq, H, D), dtype=torch.float32, device=DEV)
+    lse = torch.empty((Tq, H), device=DEV)
+    L.hca_prefill(dev(q), dev(kv), dev(tok), dev(pos), dev(sink), out, lse, m=m, W=W)
+    torch.cuda.synchronize()
+    O, LS = host(out), host(lse)
+    for t in range(Tq):
+        p = int(pos[t])
+        ref, rlse = oracle.hca_query(q[t], kv, p, N, m, oracle.window_rows(tok, p, W), sink)
+        check_out(O[t], ref, _attn_tight(ref, "f32"), f"hca prefill f32 t={t} p={p}")
+        assert np.abs(LS[t] - rlse).max() < 1e-4
+
+
 def test_sparse_prefill_reference_moves():
     """Logits that jump far above everything earlier in a query (more than the
     2^64 headroom P has against the exponent reference the kernel carries from

@@ -1,6 +1,7 @@
 """GPU parity of whole paths, in the launch configuration bench.py times:
-CSA decode step (compress the completed block, score, select, attend), HCA
-decode, and CSA prefill by 4096-query chunks. Reduced sizes check every
+CSA decode step (compress the completed block, score, select, attend) with
+bf16, E4M3 or MXFP4 indexer keys, HCA decode, CSA prefill and HCA prefill by
+4096-query chunks. Reduced sizes check every
 query; the full workload sizes check sampled sequences / queries against the
 oracle computed one by one."""
 import numpy as np
@@ -43,6 +44,8 @@ def run_csa_decode(cfg, x):
     scores = torch.empty((B, 1, N), dtype=torch.float32, device=DEV)
     if cfg.k_dtype == "fp8":
         k_t, sc = _t(x["k_idx_codes"]), _t(x["k_scale"])
+    elif cfg.k_dtype == "mxfp4":
+        k_t, sc = _t(x["k_idx_codes"]).view(torch.float4_e2m1fn_x2), _t(x["k_scale"])
     else:
         k_t, sc = _bf(x["k_idx"]), None
     L.indexer_score(_bf(x["q_idx"][:, None]), _t(x["w"][:, None]), k_t, sc, q_pos, n_comp, scores, m=m)
@@ -72,6 +75,8 @@ def check_csa_decode(cfg, x, seqs):
         comp[N - 1] = kv2[b, 1]  # the stored (bf16) entry is what the step attends
         if cfg.k_dtype == "fp8":
             keys, sc = oracle.e4m3_decode(x["k_idx_codes"][b]), x["k_scale"][b]
+        elif cfg.k_dtype == "mxfp4":
+            keys, sc = oracle.mxfp4_decode(x["k_idx_codes"][b], x["k_scale"][b]), None
         else:
             keys, sc = x["k_idx"][b], None
         oidx, o_ref, lse_ref, s = oracle.csa_query(x["q"][b], x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, N,
@@ -186,6 +191,61 @@ def test_csa_prefill_64k_last_chunk_sampled():
     cfg = gen.C3  # 65536 tokens; the last (largest) 4096-query chunk, as bench.py runs it
     rng = np.random.default_rng(8)
     check_prefill(cfg, [gen.num_chunks(cfg) - 1], lambda T: sorted(set([0, 1, T - 1] + list(rng.integers(0, T, 8)))))
+
+
+def test_csa_decode_flash_mxfp4_reduced():
+    cfg = gen.scaled(gen.C2X, B=4, n=16384)
+    check_csa_decode(cfg, gen.gen_decode(cfg), range(cfg.B))
+
+
+def test_csa_decode_flash_mxfp4_full_size_sampled():
+    cfg = gen.C2X  # 32 sequences x 32768 entries, MXFP4 indexer keys, as bench.py runs it
+    check_csa_decode(cfg, gen.gen_decode(cfg), [0, 17, 31])
+
+
+def check_hca_prefill(cfg, chunks, picks):
+    """Single-branch compression of the whole sequence at m' (HCA), then
+    hca_prefill by 4096-query chunks, as bench.py runs it."""
+    L = _L()
+    tok = gen.gen_prefill_tokens(cfg)
+    comp_t = torch.empty((1, cfg.N, cfg.D), dtype=torch.bfloat16, device=DEV)
+    L.csa_compress(_bf(tok["Ca"][None]), None, _bf(tok["Za"][None]), None, _t(tok["Ba"]), None, comp_t, m=cfg.m,
+                   overlap=False)
+    torch.cuda.synchronize()
+    comp = host(comp_t)[0]
+    rows = sorted(set([0, 1, cfg.N // 2, cfg.N - 2, cfg.N - 1]))
+    ref_comp = oracle.compress(tok["Ca"], None, tok["Za"], None, tok["Ba"], None, cfg.m, overlap=False, blocks=rows)
+    check_out(comp[rows], ref_comp, 2.0 ** -8 * max(1.0, np.abs(ref_comp).max()), "hca prefill compress")
+    kv_tok = _bf(tok["kv_tok"])
+    for c in chunks:
+        qs = gen.gen_prefill_queries(cfg, c)
+        T = len(qs["q_pos"])
+        out = torch.empty((T, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((T, cfg.H), device=DEV)
+        L.hca_prefill(_bf(qs["q"]), comp_t[0], kv_tok, _t(qs["q_pos"]), _t(tok["sink"]), out, lse, m=cfg.m, W=cfg.W)
+        torch.cuda.synchronize()
+        O, LSE = host(out), host(lse)
+        for t in picks(T):
+            p = int(qs["q_pos"][t])
+            print(f"[case] {cfg.name} chunk {c} query {t} pos {p}", flush=True)
+            # the stored (bf16) entries are what the queries attend
+            ref, rlse = oracle.hca_query(qs["q"][t], comp.astype(np.float64), p, cfg.N, cfg.m,
+                                         oracle.window_rows(tok["kv_tok"], p, cfg.W), tok["sink"])
+            check_out(O[t], ref, _tight(ref), f"hca prefill out t={t}")
+            assert np.abs(LSE[t] - rlse).max() < 1e-3
+
+
+def test_hca_prefill_reduced_two_chunks():
+    cfg = gen.scaled(gen.C6, n=8192, Tq=8192)
+    rng = np.random.default_rng(9)
+    check_hca_prefill(cfg, [0, 1], lambda T: sorted(set([0, 1, 126, 127, 128, 255, 2047, T - 2, T - 1]
+                                                         + list(rng.integers(0, T, 20)))))
+
+
+def test_hca_prefill_64k_last_chunk_sampled():
+    cfg = gen.C6  # 65536 tokens; the last 4096-query chunk (512 entries visible), as bench.py runs it
+    rng = np.random.default_rng(10)
+    check_hca_prefill(cfg, [gen.num_chunks(cfg) - 1], lambda T: sorted(set([0, 1, T - 1] + list(rng.integers(0, T, 8)))))
 
 
 def test_determinism_and_batch_invariance():

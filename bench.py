@@ -111,7 +111,7 @@ def main():
         return bench_hca_prefill(a, torch, L, gen, dev)
     cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X}[a.workload]
     t0 = time.time()
-    x = gen.gen_decode(cfg, with_compress=(cfg.kind == "csa_decode"))
+    x = gen.gen_decode(cfg, with_compress=True)
     print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     def bf(v):
@@ -134,6 +134,9 @@ def main():
         else:
             base["k_idx"] = bf(x["k_idx"])
         for nm in ("Ca", "Cb", "Za", "Zb"):
+            base[nm] = bf(x[nm])
+    else:
+        for nm in ("Ca", "Za"):
             base[nm] = bf(x[nm])
     shared = {"sink": td(x["sink"]), "Ba": td(x["Ba"]), "Bb": td(x["Bb"]),
               "q_pos": td(np.full((B, 1), cfg.n - 1, np.int32)), "n_comp": td(np.full((B,), N, np.int32)),
@@ -169,6 +172,9 @@ def main():
             L.sparse_mqa_decode(r["q"], r["kv_comp"], idx.view(B, k), r["kv_win"], shared["win_len"], shared["sink"],
                                 out, scale=1.0, ws=ws_a, stream=s)
         else:
+            # HCA: the token completes block N-1 (m' divides n): one branch, no overlap
+            L.csa_compress(r["Ca"], None, r["Za"], None, shared["Ba"], None, r["kv_comp"], m=m,
+                           tok_begin=cfg.n - m, blk_begin=N - 1, blk_end=N, overlap=False, stream=s)
             rec(ev, 1)
             rec(ev, 2)
             rec(ev, 3)
@@ -249,6 +255,7 @@ def main():
         hbytes = B * ((N + W) * D * 2 + H * D * 2 * 2)
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
                          "m": m, "heads": H, "head_dim": D, "window": W}
+        res["phases_ms"] = {"compress": round(float(ph_mean[0]), 4), "attention": round(attn_avg, 4)}
         res["roofline"] = {"bound": "hbm", "kernel": "hca_dense_mqa (attn_bf16_kernel HCA splits + combine)",
                            "achieved": round(hbytes / (kern_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(hbytes / (kern_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -524,7 +531,10 @@ def cpu_baseline(cfg, x, budget_s: float):
             oracle.csa_query(x["q"][b], x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, cfg.N, m, cfg.top_k,
                              x["kv_win"][b], x["sink"], k_scale=sc)
         else:
-            oracle.hca_query(x["q"][b], x["kv_comp"][b], cfg.n - 1, cfg.N, m, x["kv_win"][b], x["sink"])
+            ent = oracle.compress(x["Ca"][b], None, x["Za"][b], None, x["Ba"], None, m, overlap=False)[0]
+            comp = x["kv_comp"][b].astype(np.float64)
+            comp[cfg.N - 1] = ent
+            oracle.hca_query(x["q"][b], comp, cfg.n - 1, cfg.N, m, x["kv_win"][b], x["sink"])
         done += 1
     dt = time.perf_counter() - t0
     return {"value": round(done / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",

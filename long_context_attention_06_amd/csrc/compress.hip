@@ -205,9 +205,96 @@ compress_kernel(const void* __restrict__ Ca, const void* __restrict__ Cb, const 
   }
 }
 
+// Single-branch compression with long blocks (HCA, m' = 128): a thread per
+// 8 channels would walk all m tokens one group after another, so a decode
+// step (one block per sequence) would wait for m/4 dependent load rounds.
+// Here 16 threads split a block's tokens, 8 each, with all their loads issued
+// before any arithmetic; each keeps an online-softmax partial (max, sum,
+// weighted sum) per channel, and the 16 partials of a channel are merged
+// through LDS in slice order. A workgroup covers 16 channel groups (128
+// channels) of one block; lanes run along the channels, so a wave reads 256
+// contiguous bytes of four token rows.
+constexpr int CS_TOK = 8;    // tokens per slice
+constexpr int CS_SL = 16;    // slices per workgroup pass
+constexpr int CS_CG = 16;    // channel groups per workgroup
+
+template <int IN_DT, int OUT_DT>
+__global__ void __launch_bounds__(256)
+compress_split_kernel(const void* __restrict__ Ca, const void* __restrict__ Za, const float* __restrict__ Ba,
+                      void* __restrict__ out, int64_t n_rows, int64_t tok_begin, int64_t blk_begin, int64_t nblk,
+                      int64_t out_cap, int d, int m) {
+  __shared__ float part[3][CS_SL][CS_CG * 8];  // max, sum, weighted sum (exp2 domain)
+  const int groups = d / 8;
+  const int cgb = (groups + CS_CG - 1) / CS_CG;  // workgroups per block
+  const int cgl = threadIdx.x % CS_CG, sl = threadIdx.x / CS_CG;
+  const int cg = (int)(blockIdx.x % cgb) * CS_CG + cgl;
+  const int64_t t = blockIdx.x / cgb;
+  const int64_t i = blk_begin + t % nblk;
+  const int64_t b = t / nblk;
+  const bool live = cg < groups;
+  const int c0 = live ? cg * 8 : 0;
+  const int64_t row0 = b * n_rows + (m * i - tok_begin);
+
+  SoftAcc A;
+  A.init();
+  // slices sl, sl + 16, ... of the block; tokens past m are dropped
+  for (int j0 = sl * CS_TOK; j0 < m; j0 += CS_SL * CS_TOK) {
+    float z[CS_TOK][8], c[CS_TOK][8];
+#pragma unroll
+    for (int u = 0; u < CS_TOK; ++u) {
+      const int j = min(j0 + u, m - 1);  // a repeated token is masked below
+      load8<IN_DT>(Za, (row0 + j) * d + c0, z[u]);
+      load8<IN_DT>(Ca, (row0 + j) * d + c0, c[u]);
+      const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(Ba + (int64_t)j * d + c0);
+      const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(Ba + (int64_t)j * d + c0 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[u][e] = j0 + u < m ? (z[u][e] + b0[e]) * LOG2E_F : -INFINITY;
+        z[u][4 + e] = j0 + u < m ? (z[u][4 + e] + b1[e]) * LOG2E_F : -INFINITY;
+      }
+    }
+    A.feed<4>(z, c);
+    A.feed<4>(z + 4, c + 4);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    part[0][sl][cgl * 8 + e] = A.mx[e];
+    part[1][sl][cgl * 8 + e] = A.sm[e];
+    part[2][sl][cgl * 8 + e] = A.acc[e];
+  }
+  __syncthreads();
+  if (threadIdx.x >= CS_CG * 8) return;
+  // merge: thread (channel group cgl2, channel e2)
+  const int ch = threadIdx.x, cgl2 = ch / 8;
+  const int cg2 = (int)(blockIdx.x % cgb) * CS_CG + cgl2;
+  if (cg2 >= groups) return;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < CS_SL; ++q) mx = fmaxf(mx, part[0][q][ch]);
+  float sm = 0.f, acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < CS_SL; ++q) {
+    const float a = part[0][q][ch] == -INFINITY ? 0.f : exp2f(part[0][q][ch] - mx);
+    sm += part[1][q][ch] * a;
+    acc += part[2][q][ch] * a;
+  }
+  const float r = acc / sm;
+  const int64_t o = (b * out_cap + i) * d + cg2 * 8 + (ch % 8);
+  if constexpr (OUT_DT == DT_BF16)
+    reinterpret_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16(r);
+  else
+    reinterpret_cast<float*>(out)[o] = r;
+}
+
 template <int IN_DT, int OUT_DT>
 static hipError_t launch(const CompressLaunch& a, hipStream_t st) {
   const int64_t nblk = a.blk_end - a.blk_begin;
+  if (!a.overlap && a.m >= 2 * CS_TOK) {
+    const int64_t grid = a.B * nblk * ((a.d / 8 + CS_CG - 1) / CS_CG);
+    hipLaunchKernelGGL((compress_split_kernel<IN_DT, OUT_DT>), dim3((unsigned)grid), dim3(256), 0, st, a.Ca, a.Za,
+                       a.Ba, a.out, a.n_rows, a.tok_begin, a.blk_begin, nblk, a.out_cap, a.d, a.m);
+    return hipGetLastError();
+  }
   const int64_t total = a.B * nblk * (a.d / 8);
   // few entries (a decode step): 64-thread groups reach more CUs
   const int nt = total < 256 * 256 ? 64 : 256;

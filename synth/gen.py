@@ -211,9 +211,11 @@ def gen_decode_seq(cfg: Cfg, b: int, with_compress: bool = True) -> Dict[str, np
     """Inputs of one sequence b of a decode workload (CSA or HCA).
 
     The query is the last token, position p = n-1. kv_comp holds N entries.
-    For CSA with ``with_compress`` the raw inputs of the last two blocks
-    (2m tokens: rows for tokens n-2m .. n-1) are also drawn, so that the step
-    can produce entry N-1 itself (it completes at this token when m divides n).
+    With ``with_compress`` the raw inputs that produce entry N-1 are also
+    drawn, so that the step can make that entry itself (it completes at this
+    token when m divides n): for CSA the last two blocks (2m tokens, rows for
+    tokens n-2m .. n-1, both branches), for HCA the last block (m tokens,
+    one branch).
     """
     s, D = cfg.seed, cfg.D
     out: Dict[str, np.ndarray] = {}
@@ -239,6 +241,9 @@ def gen_decode_seq(cfg: Cfg, b: int, with_compress: bool = True) -> Dict[str, np
             rows = 2 * cfg.m
             for nm in ("Ca", "Cb", "Za", "Zb"):
                 out[nm] = _store(_normal(rng(s, nm, b), (rows, D)), cfg.dtype)
+    elif cfg.kind == "hca_decode" and with_compress:
+        for nm in ("Ca", "Za"):
+            out[nm] = _store(_normal(rng(s, nm, b), (cfg.m, D)), cfg.dtype)
     return out
 
 

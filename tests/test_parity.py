@@ -89,6 +89,18 @@ def test_compress_hca_single_branch():
     _compress_case(3, 8, 4096 - 8, 512, 4, 1022, 1024, "bf16", "f32", overlap=False, seed=8, out_cap=1024)
 
 
+def test_compress_single_branch_long_blocks():
+    """Single-branch blocks of m >= 16 run split over tokens: m' = 128 decode
+    append (one block per sequence), m not a multiple of the 8-token slice,
+    blocks longer than 16 slices (each thread takes several), and a channel
+    count that leaves part of a 16-group workgroup idle."""
+    n, m = 1 << 14, 128
+    _compress_case(4, m, n - m, 512, m, n // m - 1, n // m, "bf16", "bf16", overlap=False, seed=9, out_cap=n // m)
+    _compress_case(2, 20 * 7 + 3, 0, 512, 20, 0, 7, "bf16", "f32", overlap=False, seed=10)
+    _compress_case(1, 1024 * 2, 0, 256, 1024, 0, 2, "bf16", "f32", overlap=False, seed=11)
+    _compress_case(2, 16 * 9, 0, 64, 16, 2, 9, "f32", "f32", overlap=False, seed=12)
+
+
 # ------------------------------------------------------------------ indexer
 
 def _indexer_case(B, Tq, N_max, n_comp, q_pos, m, top_k, kdt, seed=0, H_I=64, D_I=128, wdist="normal"):

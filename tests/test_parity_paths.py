@@ -1,7 +1,7 @@
 """GPU parity of whole paths, in the launch configuration bench.py times:
 CSA decode step (compress the completed block, score, select, attend) with
-bf16, E4M3 or MXFP4 indexer keys, HCA decode, CSA prefill and HCA prefill by
-4096-query chunks. Reduced sizes check every
+bf16, E4M3 or MXFP4 indexer keys, HCA decode step (append the completed
+entry, attend), CSA prefill and HCA prefill by 4096-query chunks. Reduced sizes check every
 query; the full workload sizes check sampled sequences / queries against the
 oracle computed one by one."""
 import numpy as np
@@ -111,22 +111,46 @@ def test_csa_decode_pro_1m_fp8_full_size_sampled():
     check_csa_decode(cfg, gen.gen_decode(cfg), [1, 3])
 
 
-def test_hca_decode_1m_full_size():
+def run_hca_decode(cfg, x):
+    """One HCA decode token per sequence, as bench.py runs it: the token
+    completes block N-1 (m' divides n), whose entry is appended by
+    single-branch compression, then dense MQA over all entries + window."""
     L = _L()
-    cfg = gen.C4
-    x = gen.gen_decode(cfg, with_compress=False)
     B, N, m, W = cfg.B, cfg.N, cfg.m, cfg.W
+    kv = _bf(x["kv_comp"])
+    L.csa_compress(_bf(x["Ca"]), None, _bf(x["Za"]), None, _t(x["Ba"]), None, kv, m=m, tok_begin=cfg.n - m,
+                   blk_begin=N - 1, blk_end=N, overlap=False)
     out = torch.empty((B, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, cfg.H), device=DEV)
-    L.hca_dense_mqa(_bf(x["q"]), _bf(x["kv_comp"]), _t(np.full((B,), N, np.int32)),
-                    _t(np.full((B,), cfg.n - 1, np.int32)), _bf(x["kv_win"]), _t(np.full((B,), W, np.int32)),
-                    _t(x["sink"]), out, lse, m=m)
+    L.hca_dense_mqa(_bf(x["q"]), kv, _t(np.full((B,), N, np.int32)), _t(np.full((B,), cfg.n - 1, np.int32)),
+                    _bf(x["kv_win"]), _t(np.full((B,), W, np.int32)), _t(x["sink"]), out, lse, m=m)
     torch.cuda.synchronize()
-    O, LS = host(out), host(lse)
-    for b in range(B):
-        ref, rlse = oracle.hca_query(x["q"][b], x["kv_comp"][b], cfg.n - 1, N, m, x["kv_win"][b], x["sink"])
+    return host(kv[:, N - 2:]), host(out), host(lse)
+
+
+def check_hca_decode(cfg, seqs):
+    x = gen.gen_decode(cfg, with_compress=True)
+    kv2, O, LS = run_hca_decode(cfg, x)
+    N, m = cfg.N, cfg.m
+    for b in seqs:
+        print(f"[case] {cfg.name} b={b}", flush=True)
+        ent = oracle.compress(x["Ca"][b], None, x["Za"][b], None, x["Ba"], None, m, overlap=False)[0]
+        check_out(kv2[b, 1], ent, 2.0 ** -8 * max(1.0, np.abs(ent).max()), "hca entry N-1")
+        assert np.array_equal(kv2[b, 0], x["kv_comp"][b, N - 2]), "compress wrote outside its block"
+        comp = x["kv_comp"][b].astype(np.float64)
+        comp[N - 1] = kv2[b, 1]  # the stored (bf16) entry is what the step attends
+        ref, rlse = oracle.hca_query(x["q"][b], comp, cfg.n - 1, N, m, x["kv_win"][b], x["sink"])
         check_out(O[b], ref, _tight(ref), f"hca b={b}")
         assert np.abs(LS[b] - rlse).max() < 1e-3
+
+
+def test_hca_decode_reduced():
+    check_hca_decode(gen.scaled(gen.C4, B=3, n=1 << 16), range(3))
+
+
+def test_hca_decode_1m_full_size():
+    cfg = gen.C4  # 16 sequences x 8192 entries, every sequence checked
+    check_hca_decode(cfg, range(cfg.B))
 
 
 def run_prefill_chunk(cfg, tok, comp_t, chunk):

@@ -14,9 +14,10 @@ rotated over several device replicas so that no step reads cache-resident
 data from the previous one.
 
 Other workloads: c5 (1M context, E4M3 indexer keys), c2x (c2 with MXFP4
-indexer keys), c4 (HCA decode 1M), c3 (CSA prefill 64K), c6 (HCA prefill 64K).
+indexer keys), c4 (HCA decode 1M), c3 (CSA prefill 64K), c6 (HCA prefill 64K),
+c4f / c2f (c4 / c2 with the main KV rows in E4M3 + bf16 RoPE dims).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c5|c4|c3|c2x|c6]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c5|c4|c3|c2x|c6|c4f|c2f]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -44,7 +45,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4", "c3", "c2x", "c6"])
+    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4", "c3", "c2x", "c6", "c4f", "c2f"])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -109,7 +110,7 @@ def main():
         return bench_prefill(a, torch, L, gen, dev)
     if a.workload == "c6":
         return bench_hca_prefill(a, torch, L, gen, dev)
-    cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X}[a.workload]
+    cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X, "c4f": gen.C4F, "c2f": gen.C2F}[a.workload]
     t0 = time.time()
     x = gen.gen_decode(cfg, with_compress=True)
     print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -121,7 +122,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
 
     B, N, H, D, W, m = cfg.B, cfg.N, cfg.H, cfg.D, cfg.W, cfg.m
-    base = {"q": bf(x["q"]), "kv_comp": bf(x["kv_comp"]), "kv_win": bf(x["kv_win"])}
+    kvt = td if cfg.kv_dtype == "fp8" else bf  # mixed-precision rows travel as bytes
+    rowb = D + 64 if cfg.kv_dtype == "fp8" else 2 * D  # bytes per main-KV row
+    base = {"q": bf(x["q"]), "kv_comp": kvt(x["kv_comp"]), "kv_win": kvt(x["kv_win"])}
     if cfg.kind == "csa_decode":
         base["q_idx"] = bf(x["q_idx"][:, None])
         base["w"] = td(x["w"][:, None])
@@ -237,10 +240,11 @@ def main():
     if cfg.kind == "csa_decode":
         kbytes = {"fp8": N * (cfg.D_I + 4), "mxfp4": N * (cfg.D_I // 2 + cfg.D_I // 32)}.get(cfg.k_dtype, N * cfg.D_I * 2)
         scan_bytes = B * (kbytes + cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4)  # keys (+scales), q_idx, w
-        step_bytes = B * (kbytes + cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4 + k * D * 2 + W * D * 2 + H * D * 2 * 2 + k * 4)
+        step_bytes = B * (kbytes + cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4 + (k + W) * rowb + H * D * 2 * 2 + k * 4)
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
                          "m": m, "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I,
-                         "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype}
+                         "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype,
+                         "kv_dtype": cfg.kv_dtype}
         kname = {"fp8": "idx_scan_lp_kernel<2> (E4M3 keys)", "mxfp4": "idx_scan_lp_kernel<3> (MXFP4 keys)"}.get(cfg.k_dtype, "idx_scan_bf16_kernel")
         res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": round(scan_bytes / (scan_avg * 1e-3) / 1e9, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -252,11 +256,12 @@ def main():
         res["step_hbm_gbs"] = round(step_bytes / (ms_step * 1e-3) / 1e9, 1)
         res["indexer_kv_hbm_gbs"] = res["roofline"]["achieved"]
     else:
-        hbytes = B * ((N + W) * D * 2 + H * D * 2 * 2)
+        hbytes = B * ((N + W) * rowb + H * D * 2 * 2)
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
-                         "m": m, "heads": H, "head_dim": D, "window": W}
+                         "m": m, "heads": H, "head_dim": D, "window": W, "kv_dtype": cfg.kv_dtype}
         res["phases_ms"] = {"compress": round(float(ph_mean[0]), 4), "attention": round(attn_avg, 4)}
-        res["roofline"] = {"bound": "hbm", "kernel": "hca_dense_mqa (attn_bf16_kernel HCA splits + combine)",
+        res["roofline"] = {"bound": "hbm", "kernel": "hca_dense_mqa (attn_bf16_kernel<1, %s> HCA splits + combine)"
+                           % ("true" if cfg.kv_dtype == "fp8" else "false"),
                            "achieved": round(hbytes / (kern_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(hbytes / (kern_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "traffic": None, "algorithmic_bytes_per_launch": hbytes, "avg_launch_ms": round(kern_avg, 4)}
@@ -512,6 +517,10 @@ def cpu_baseline(cfg, x, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
+    from synth import gen
+    fp8 = cfg.kv_dtype == "fp8"
+    kvd = (lambda r: oracle.kv_fp8_decode(r, cfg.D)) if fp8 else (lambda r: np.asarray(r, np.float64))
+    stored = (lambda e: oracle.kv_fp8_decode(gen.kv_fp8_rows(e), cfg.D)) if fp8 else (lambda e: e)
     done = 0
     t0 = time.perf_counter()
     m = cfg.m
@@ -520,8 +529,8 @@ def cpu_baseline(cfg, x, budget_s: float):
         if cfg.kind == "csa_decode":
             ent = oracle.compress(x["Ca"][b], x["Cb"][b], x["Za"][b], x["Zb"][b], x["Ba"], x["Bb"], m,
                                   blocks=range(1, 2))[0]
-            comp = x["kv_comp"][b].astype(np.float64)
-            comp[cfg.N - 1] = ent
+            comp = kvd(x["kv_comp"][b])
+            comp[cfg.N - 1] = stored(ent)
             if cfg.k_dtype == "fp8":
                 keys, sc = oracle.e4m3_decode(x["k_idx_codes"][b]), x["k_scale"][b]
             elif cfg.k_dtype == "mxfp4":
@@ -529,12 +538,12 @@ def cpu_baseline(cfg, x, budget_s: float):
             else:
                 keys, sc = x["k_idx"][b], None
             oracle.csa_query(x["q"][b], x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, cfg.N, m, cfg.top_k,
-                             x["kv_win"][b], x["sink"], k_scale=sc)
+                             kvd(x["kv_win"][b]), x["sink"], k_scale=sc)
         else:
             ent = oracle.compress(x["Ca"][b], None, x["Za"][b], None, x["Ba"], None, m, overlap=False)[0]
-            comp = x["kv_comp"][b].astype(np.float64)
-            comp[cfg.N - 1] = ent
-            oracle.hca_query(x["q"][b], comp, cfg.n - 1, cfg.N, m, x["kv_win"][b], x["sink"])
+            comp = kvd(x["kv_comp"][b])
+            comp[cfg.N - 1] = stored(ent)
+            oracle.hca_query(x["q"][b], comp, cfg.n - 1, cfg.N, m, kvd(x["kv_win"][b]), x["sink"])
         done += 1
     dt = time.perf_counter() - t0
     return {"value": round(done / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",

@@ -36,8 +36,12 @@
  *     scale), CSA_MXFP4 (OCP Microscaling MXFP4, indexer keys only: FP4 E2M1
  *     elements, two per byte with element 2j in the low nibble of byte j, and
  *     one E8M0 scale byte per block of 32 elements; the pages keep the
- *     indexer in FP4). Arithmetic is fp32 (bf16 x bf16 products accumulate in
- *     fp32; fp8 and FP4 keys are widened to bf16 exactly first).
+ *     indexer in FP4), CSA_KV_FP8 (the mixed-precision main KV row the pages
+ *     describe: RoPE dims in BF16, the rest in FP8 -- for a row of D dims,
+ *     bytes 0 .. D-65 are the OCP E4M3 codes of dims 0 .. D-65 and the next
+ *     128 bytes the last 64 dims as bf16, little endian: D + 64 bytes per row,
+ *     no scale). Arithmetic is fp32 (bf16 x bf16 products accumulate in fp32;
+ *     fp8 and FP4 values are widened to bf16 exactly first).
  *   - Return codes: CSA_OK, CSA_INVALID_ARG (a null pointer that must not be
  *     null, a negative or inconsistent size), CSA_UNSUPPORTED (a valid
  *     combination with no kernel instantiation), CSA_WORKSPACE_TOO_SMALL,
@@ -64,7 +68,7 @@ extern "C" {
 
 #define CSA_HCA_VERSION 1
 
-enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3 };
+enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3, CSA_KV_FP8 = 4 };
 
 enum {
   CSA_OK = 0,
@@ -100,7 +104,9 @@ const char* csa_last_error(void);
  * complete tokens: trailing tokens form no entry, [LQNN] section 5);
  * m*blk_begin >= tok_begin, and with CSA_OVERLAP and blk_begin >= 1 also
  * m*(blk_begin-1) >= tok_begin; blk_end <= out_cap; 1 <= m <= 1024.
- * Supported: in_dt in {F32, BF16}, out_dt in {F32, BF16}, d % 8 == 0.
+ * Supported: in_dt in {F32, BF16}, out_dt in {F32, BF16, KV_FP8 (d > 64; out
+ * rows are d + 64 bytes: channels below d-64 rounded to E4M3 to nearest even,
+ * saturating at +-448, the last 64 to bf16)}, d % 8 == 0.
  */
 int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
                  const float* Ba, const float* Bb, void* out,
@@ -170,6 +176,9 @@ size_t indexer_score_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, 
  * out_h = 0 and lse_h = -inf. Rows present in two sources count twice.
  * Supported: D = 512 with kv_dt BF16 and 49 <= H <= 64, or D = 64 with
  * kv_dt F32 and 1 <= H <= 16; out_dt in {F32, BF16}; q has the dtype kv_dt.
+ * The decode entry points (sparse_mqa_decode, hca_dense_mqa) also take
+ * kv_dt KV_FP8 (D = 512, 49 <= H <= 64, bf16 q): kv_comp and kv_win rows are
+ * then D + 64 = 576 bytes, 16-byte aligned.
  * scale must be positive and finite (CSA_INVALID_ARG otherwise); q and out
  * must be 16-byte aligned.
  */

@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa_hca.so")
 
-F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
+F32, BF16, FP8_E4M3, MXFP4, KV_FP8 = 0, 1, 2, 3, 4
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = 0, -1, -2, -3, -4
 OVERLAP, JOINT_SOFTMAX = 1, 2
 
@@ -91,6 +91,15 @@ def _dt(t) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def _kv_dt(q, kv) -> int:
+    """Row dtype of a KV cache: uint8 rows D + 64 bytes wide are the
+    mixed-precision layout (D - 64 E4M3 bytes, then 64 bf16 RoPE dims) read
+    with bf16 queries; otherwise the rows have the query's dtype."""
+    if kv is not None and kv.dtype == torch.uint8 and kv.shape[-1] == q.shape[-1] + 64:
+        return KV_FP8
+    return _dt(q)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is not None:
         return stream
@@ -129,8 +138,9 @@ def csa_compress(Ca, Cb, Za, Zb, Ba, Bb, out, *, m: int, tok_begin: int = 0, blk
     if blk_end is None:
         blk_end = (tok_begin + n_rows) // m
     flags = (OVERLAP if overlap else 0) | (JOINT_SOFTMAX if joint else 0)
+    out_dt = KV_FP8 if out.dtype == torch.uint8 and out.shape[-1] == d + 64 else _dt(out)
     _check(lib.csa_compress(_ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), _ptr(out), B, n_rows,
-                            tok_begin, d, m, blk_begin, blk_end, out_cap, flags, _dt(Ca), _dt(out),
+                            tok_begin, d, m, blk_begin, blk_end, out_cap, flags, _dt(Ca), out_dt,
                             _stream(stream)))
 
 
@@ -183,15 +193,16 @@ def sparse_mqa_decode_workspace_bytes(B: int, H: int, D: int, top_k: int, W: int
 def sparse_mqa_decode(q, kv_comp, topk_idx, kv_win, win_len, sink, out, lse=None, *, scale: float = 1.0, ws=None,
                       stream=None) -> None:
     """q [B, H, D]; kv_comp [B, N_max, D]; topk_idx [B, top_k]; kv_win [B, W, D]; win_len [B];
-    sink [H] fp32 or None; out [B, H, D]; lse [B, H] or None."""
+    sink [H] fp32 or None; out [B, H, D]; lse [B, H] or None. kv_comp and kv_win
+    may be mixed-precision uint8 rows [.., D + 64] (KV_FP8) with bf16 q."""
     B, H, D = q.shape
     N_max = kv_comp.shape[1]
     top_k = topk_idx.shape[-1]
     W = kv_win.shape[1] if kv_win is not None else 0
     ws, nb = _ws(sparse_mqa_decode_workspace_bytes(B, H, D, top_k, W), ws, q.device)
     _check(lib.sparse_mqa_decode(_ptr(q), _ptr(kv_comp), _ptr(topk_idx), _ptr(kv_win), _ptr(win_len), _ptr(sink),
-                                 scale, B, H, D, N_max, top_k, W, _dt(q), _dt(out), _ptr(out), _ptr(lse), _ptr(ws),
-                                 nb, _stream(stream)))
+                                 scale, B, H, D, N_max, top_k, W, _kv_dt(q, kv_comp), _dt(out), _ptr(out), _ptr(lse),
+                                 _ptr(ws), nb, _stream(stream)))
 
 
 def sparse_mqa_prefill_workspace_bytes(Tq: int, H: int, D: int, top_k: int, W: int) -> int:
@@ -207,7 +218,7 @@ def sparse_mqa_prefill(q, kv_comp, topk_idx, kv_tok, q_pos, sink, out, lse=None,
     T_tok = kv_tok.shape[0]
     ws, nb = _ws(sparse_mqa_prefill_workspace_bytes(Tq, H, D, top_k, W), ws, q.device)
     _check(lib.sparse_mqa_prefill(_ptr(q), _ptr(kv_comp), _ptr(topk_idx), _ptr(kv_tok), _ptr(q_pos), _ptr(sink),
-                                  scale, Tq, H, D, N, T_tok, top_k, W, _dt(q), _dt(out), _ptr(out), _ptr(lse),
+                                  scale, Tq, H, D, N, T_tok, top_k, W, _kv_dt(q, kv_comp), _dt(out), _ptr(out), _ptr(lse),
                                   _ptr(ws), nb, _stream(stream)))
 
 
@@ -223,7 +234,8 @@ def hca_prefill(q, kv_comp, kv_tok, q_pos, sink, out, lse=None, *, m: int, W: in
     T_tok = kv_tok.shape[0] if kv_tok is not None else 0
     ws, nb = _ws(hca_prefill_workspace_bytes(Tq, H, D, N, W), ws, q.device)
     _check(lib.hca_prefill(_ptr(q), _ptr(kv_comp), _ptr(kv_tok), _ptr(q_pos), _ptr(sink), scale, Tq, H, D, N, m,
-                           T_tok, W, _dt(q), _dt(out), _ptr(out), _ptr(lse), _ptr(ws), nb, _stream(stream)))
+                           T_tok, W, _kv_dt(q, kv_comp), _dt(out), _ptr(out), _ptr(lse), _ptr(ws), nb,
+                           _stream(stream)))
 
 
 def hca_dense_mqa_workspace_bytes(B: int, H: int, D: int, N_max: int, W: int) -> int:
@@ -238,5 +250,5 @@ def hca_dense_mqa(q, kv_comp, n_comp, q_pos, kv_win, win_len, sink, out, lse=Non
     W = kv_win.shape[1] if kv_win is not None else 0
     ws, nb = _ws(hca_dense_mqa_workspace_bytes(B, H, D, N_max, W), ws, q.device)
     _check(lib.hca_dense_mqa(_ptr(q), _ptr(kv_comp), _ptr(n_comp), _ptr(q_pos), m, _ptr(kv_win), _ptr(win_len),
-                             _ptr(sink), scale, B, H, D, N_max, W, _dt(q), _dt(out), _ptr(out), _ptr(lse), _ptr(ws),
-                             nb, _stream(stream)))
+                             _ptr(sink), scale, B, H, D, N_max, W, _kv_dt(q, kv_comp), _dt(out), _ptr(out),
+                             _ptr(lse), _ptr(ws), nb, _stream(stream)))

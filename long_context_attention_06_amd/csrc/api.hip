@@ -48,7 +48,8 @@ size_t attn_ws(int64_t nq, int H, int D, int nsplit) {
 }
 
 bool attn_supported(int H, int D, int kv_dt) {
-  return (kv_dt == CSA_BF16 && D == 512 && H > 48 && H <= 64) || (kv_dt == CSA_F32 && D == 64 && H >= 1 && H <= 16);
+  return ((kv_dt == CSA_BF16 || kv_dt == CSA_KV_FP8) && D == 512 && H > 48 && H <= 64) ||
+         (kv_dt == CSA_F32 && D == 64 && H >= 1 && H <= 16);
 }
 
 int check_attn_common(const void* q, const void* out, float scale, int H, int D, int kv_dt, int out_dt, int W,
@@ -57,11 +58,12 @@ int check_attn_common(const void* q, const void* out, float scale, int H, int D,
   REQ(scale > 0.0f && scale <= 3.0e38f, CSA_INVALID_ARG, "scale must be positive and finite");
   REQ(H > 0 && D > 0, CSA_INVALID_ARG, "H and D must be positive");
   REQ(W >= 0 && top_k >= 0, CSA_INVALID_ARG, "W and top_k must be >= 0");
-  REQ(kv_dt == CSA_F32 || kv_dt == CSA_BF16 || kv_dt == CSA_FP8_E4M3, CSA_INVALID_ARG, "unknown kv_dt");
+  REQ(kv_dt == CSA_F32 || kv_dt == CSA_BF16 || kv_dt == CSA_FP8_E4M3 || kv_dt == CSA_MXFP4 || kv_dt == CSA_KV_FP8,
+      CSA_INVALID_ARG, "unknown kv_dt");
   REQ(out_dt == CSA_F32 || out_dt == CSA_BF16 || out_dt == CSA_FP8_E4M3, CSA_INVALID_ARG, "unknown out_dt");
   REQ(out_dt != CSA_FP8_E4M3, CSA_UNSUPPORTED, "out_dt must be F32 or BF16");
   REQ(attn_supported(H, D, kv_dt), CSA_UNSUPPORTED,
-      "unsupported (H, D, kv_dt): supported are (49..64, 512, BF16) and (1..16, 64, F32)");
+      "unsupported (H, D, kv_dt): supported are (49..64, 512, BF16 or KV_FP8) and (1..16, 64, F32)");
   REQ(aligned16(q), CSA_INVALID_ARG, "q must be 16-byte aligned");
   REQ(aligned16(out), CSA_INVALID_ARG, "out must be 16-byte aligned");
   return CSA_OK;
@@ -124,9 +126,13 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
   REQ(0 <= blk_begin && blk_begin <= blk_end, CSA_INVALID_ARG, "need 0 <= blk_begin <= blk_end");
   REQ(blk_end <= out_cap, CSA_INVALID_ARG, "blk_end exceeds out_cap");
   REQ(in_dt == CSA_F32 || in_dt == CSA_BF16 || in_dt == CSA_FP8_E4M3, CSA_INVALID_ARG, "unknown in_dt");
-  REQ(out_dt == CSA_F32 || out_dt == CSA_BF16 || out_dt == CSA_FP8_E4M3, CSA_INVALID_ARG, "unknown out_dt");
-  REQ(in_dt != CSA_FP8_E4M3 && out_dt != CSA_FP8_E4M3, CSA_UNSUPPORTED, "compress supports F32 and BF16 only");
+  REQ(out_dt == CSA_F32 || out_dt == CSA_BF16 || out_dt == CSA_FP8_E4M3 || out_dt == CSA_MXFP4 ||
+          out_dt == CSA_KV_FP8,
+      CSA_INVALID_ARG, "unknown out_dt");
+  REQ(in_dt != CSA_FP8_E4M3 && out_dt != CSA_FP8_E4M3 && out_dt != CSA_MXFP4, CSA_UNSUPPORTED,
+      "compress reads F32 or BF16 and writes F32, BF16 or KV_FP8 rows");
   REQ(d % 8 == 0, CSA_UNSUPPORTED, "d must be a multiple of 8");
+  REQ(out_dt != CSA_KV_FP8 || d > 64, CSA_UNSUPPORTED, "KV_FP8 rows need d > 64 (64 bf16 RoPE channels)");
   if (blk_end > blk_begin) {
     REQ(m * blk_end <= tok_begin + n_rows, CSA_INVALID_ARG,
         "block range needs tokens beyond the provided rows (a block is formed only from m complete tokens)");
@@ -265,6 +271,7 @@ int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_i
   REQ(W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
   REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
   REQ(Tq <= 0x7fffffff, CSA_UNSUPPORTED, "Tq too large");
+  REQ(kv_dt != CSA_KV_FP8, CSA_UNSUPPORTED, "sparse_mqa_prefill reads BF16 or F32 rows");
   REQ(kv_dt == CSA_BF16 || top_k <= 1024, CSA_UNSUPPORTED, "sparse_mqa_prefill on f32 rows supports top_k <= 1024");
   REQ(top_k + W <= 2048, CSA_UNSUPPORTED, "sparse_mqa_prefill supports top_k + W <= 2048 rows per query");
   csa::AttnLaunch a{};
@@ -310,6 +317,7 @@ int hca_prefill(const void* q, const void* kv_comp, const void* kv_tok, const in
   REQ(W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
   REQ(N + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
   REQ(Tq <= 0x7fffffff, CSA_UNSUPPORTED, "Tq too large");
+  REQ(kv_dt != CSA_KV_FP8, CSA_UNSUPPORTED, "hca_prefill reads BF16 or F32 rows");
   csa::AttnLaunch a{};
   a.src = 3;
   a.q = q;

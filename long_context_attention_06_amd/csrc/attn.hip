@@ -145,11 +145,10 @@ struct QRows {
   int len1, w0;  // HCA: rows taken from the compressed range; first window row (HCA_PRE: token)
 };
 
-template <int SRC>
+template <int SRC, int ROWB = 1024>
 __device__ __forceinline__ QRows query_rows(const RowSrc& src, const int32_t* __restrict__ win_len,
                                             const int32_t* __restrict__ n_comp, const int32_t* __restrict__ q_pos,
                                             int m_rate, int64_t qi, int sp, int slots, int split_rows) {
-  constexpr int ROWB = 1024;
   QRows r;
   r.lim0 = 0;
   r.lim1 = 0;
@@ -252,15 +251,18 @@ __device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, in
   return n_rows;
 }
 
-// Address of compacted row c of an HCA split / of a sparse table entry.
+// Address of compacted row c of an HCA split / of a sparse table entry (rows
+// of ROWB bytes).
+template <int ROWB = 1024>
 __device__ __forceinline__ const uint8_t* hca_row(const QRows& r, int c) {
-  return c < r.len1 ? r.comp_base + (int64_t)(r.s_begin + c) * 1024 : r.win_base + (int64_t)(r.w0 + c - r.len1) * 1024;
+  return c < r.len1 ? r.comp_base + (int64_t)(r.s_begin + c) * ROWB : r.win_base + (int64_t)(r.w0 + c - r.len1) * ROWB;
 }
+template <int ROWB = 1024>
 __device__ __forceinline__ const uint8_t* tab_row(const QRows& r, int e) {
-  return e >= 0 ? r.comp_base + (int64_t)e * 1024 : r.win_base + (int64_t)(e & 0x7fffffff) * 1024;
+  return e >= 0 ? r.comp_base + (int64_t)e * ROWB : r.win_base + (int64_t)(e & 0x7fffffff) * ROWB;
 }
 
-template <int SRC>
+template <int SRC, bool KV8>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __restrict__ win_len,
                  const int32_t* __restrict__ n_comp, const int32_t* __restrict__ q_pos, int m_rate,
@@ -268,7 +270,16 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
                  float* __restrict__ part_o, float* __restrict__ part_ml, void* __restrict__ out,
                  float* __restrict__ lse, int out_dt) {
   using namespace bfk;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TILEB];
+  // KV8 rows: dims 0..447 as E4M3 bytes, then the 64 RoPE dims as bf16 (576 B
+  // in memory). In LDS they sit unswizzled at a 592-byte pitch (148 dwords:
+  // 16 consecutive rows start in 16 distinct 4-bank groups), the second half
+  // of a tile 64 bytes further on, so that rows r and r + 16 do not share banks.
+  constexpr int SROWB = KV8 ? 576 : ROWB;          // bytes per row in memory
+  constexpr int NOPE = 448;                        // E4M3 dims of a KV8 row
+  constexpr int PITCH = KV8 ? 592 : ROWB;          // LDS bytes per row
+  constexpr int TB = KV8 ? TR * PITCH + 64 : TILEB;
+  auto lrow = [](int r) { return KV8 ? r * PITCH + (r >> 4) * 64 : r * ROWB; };
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TB];
   __shared__ __attribute__((aligned(16))) f32x4_t xchg[NW][2][64];
   __shared__ __attribute__((aligned(16))) int tab[SRC == SRC_HCA_DEC ? 4 : TAB_MAX];
   __shared__ int cnt[2 * NW];
@@ -283,7 +294,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
   const int nsplit = gridDim.y;
   const int head = hg * 16 + l16;  // this lane's head in S^T / P / softmax
 
-  QRows rr = query_rows<SRC>(src, win_len, n_comp, q_pos, m_rate, qi, sp, slots, split_rows);
+  QRows rr = query_rows<SRC, SROWB>(src, win_len, n_comp, q_pos, m_rate, qi, sp, slots, split_rows);
 
   // ---- Q^T operand (B of S^T = R Q^T): lane (head, G), dims 256 dh + 32 s + 8 G .. +7
   bf16x8_t qb[8];
@@ -303,23 +314,27 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   uint32_t voff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((l ^ swz(4 * w + i)) * 16);
+  for (int i = 0; i < 4; ++i) voff[i] = KV8 ? (uint32_t)(l * 16) : (uint32_t)((l ^ swz(4 * w + i)) * 16);
+  // a KV8 row is 36 lanes x 16 bytes; the other lanes' LDS slots belong to the next row
+  auto row_dma = [&](const uint8_t* rp, int i, uint32_t dst) {
+    if (!KV8 || l < SROWB / 16) dma_row(uniform_ptr(rp), voff[i], __builtin_amdgcn_readfirstlane(dst));
+  };
   auto issue = [&](int t) {
     const int c0 = t * TR + 4 * w;  // first of this wave's four rows
-    const uint32_t dst = ring_lds + (uint32_t)((t & (NBUF - 1)) * TILEB + 4 * w * ROWB);
+    const uint32_t dst = ring_lds + (uint32_t)((t & (NBUF - 1)) * TB);
     if (SRC == SRC_HCA_DEC) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int c = c0 + i;
         if (c >= n_rows) c = t * TR;  // rows past the end repeat a valid row; they are masked
-        dma_row(uniform_ptr(hca_row(rr, c)), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+        row_dma(hca_row<SROWB>(rr, c), i, dst + lrow(4 * w + i));
       }
     } else {
       const u32x4_t e4 = *reinterpret_cast<const u32x4_t*>(&tab[c0]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = (int)__builtin_amdgcn_readfirstlane(e4[i]);
-        dma_row(uniform_ptr(tab_row(rr, e)), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+        row_dma(tab_row<SROWB>(rr, e), i, dst + lrow(4 * w + i));
       }
     }
   };
@@ -346,32 +361,80 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
       pofs[1][u] = rowb * ROWB + (((2 * u + c0) ^ swz(rowb)) * 16) + cb + dh * 512;
     }
   }
+  // KV8 offsets. S^T operand: row mt*16 + l16 (its E4M3 dims are its bytes).
+  // V^T operand of the E4M3 dims (ds_read_b64_tr_b8): within a 16-lane group,
+  // lanes 2k and 2k+1 give the addresses of row r_k, columns 0-7 and 8-15 of
+  // a 16-dim block, and lane j receives column j of rows r_0 .. r_7; r_k
+  // follows P's K order, rows 4G + k and then 16 + 4G + (k-4). The RoPE dims
+  // use the 16-bit transposed read (lane: row 4G + l16/4 (+16), four columns).
+  int kofs8[2], vofs8, rofs8[2];
+  {
+    kofs8[0] = lrow(l16);
+    kofs8[1] = lrow(16 + l16);
+    const int k = l16 >> 1;
+    vofs8 = lrow(k < 4 ? 4 * G + k : 16 + 4 * G + (k - 4)) + 8 * (l16 & 1);
+    const int rowa = G * 4 + (l16 >> 2);
+    rofs8[0] = lrow(rowa) + NOPE + 8 * (l16 & 3);
+    rofs8[1] = lrow(rowa + 16) + NOPE + 8 * (l16 & 3);
+  }
 
   // consume Q here: the compiler's wait for its loads lands before the first
   // row load, so its load tracking never waits on rows in flight in the loop
 #pragma unroll
   for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(qb[s]));
+  constexpr int PER = 4;  // row loads per wave per tile
   for (int t = 0; t < ntiles && t < NBUF - 1; ++t) issue(t);
   for (int t = 0; t < ntiles; ++t) {
     const int ahead = min(NBUF - 2, ntiles - 1 - t);  // tiles issued after this one
     if (ahead >= 2)
-      vm_barrier<8>();
+      vm_barrier<2 * PER>();
     else if (ahead == 1)
-      vm_barrier<4>();
+      vm_barrier<PER>();
     else
       vm_barrier<0>();
     // the buffer of tile t-1 is free: every wave has passed this barrier
     if (t + NBUF - 1 < ntiles) issue(t + NBUF - 1);
-    const uint8_t* R = ring + (t & (NBUF - 1)) * TILEB;
+    const uint8_t* R = ring + (t & (NBUF - 1)) * TB;
 
     // ---- partial S^T over this wave's 256 dims, two 16-row M-tiles
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, sb = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (KV8) {
+      // dims 256 dh + 32 s + 8 G: E4M3 bytes below 448 (dh = 0, or s < 6),
+      // bf16 above (dh = 1, s = 6, 7)
+      auto k8 = [&](int mt, int s) {
+        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(R + kofs8[mt] + 256 * dh + 32 * s + 8 * G);
+        return as_bf16x8(u32x4_t{fp8x2_to_bf16x2(v[0], false), fp8x2_to_bf16x2(v[0], true),
+                                 fp8x2_to_bf16x2(v[1], false), fp8x2_to_bf16x2(v[1], true)});
+      };
+      auto kr16 = [&](int mt, int s) {
+        return as_bf16x8(*reinterpret_cast<const u32x4_t*>(R + kofs8[mt] + NOPE + 2 * (32 * (s - 6) + 8 * G)));
+      };
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(R + qofs[0][s & 3] + (s >> 2) * 256));
-      const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(R + qofs[1][s & 3] + (s >> 2) * 256));
-      sa = mfma16(a0, qb[s], sa);
-      sb = mfma16(a1, qb[s], sb);
+      for (int s = 0; s < 6; ++s) {
+        sa = mfma16(k8(0, s), qb[s], sa);
+        sb = mfma16(k8(1, s), qb[s], sb);
+      }
+      if (dh == 0) {
+#pragma unroll
+        for (int s = 6; s < 8; ++s) {
+          sa = mfma16(k8(0, s), qb[s], sa);
+          sb = mfma16(k8(1, s), qb[s], sb);
+        }
+      } else {
+#pragma unroll
+        for (int s = 6; s < 8; ++s) {
+          sa = mfma16(kr16(0, s), qb[s], sa);
+          sb = mfma16(kr16(1, s), qb[s], sb);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8_t a0 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(R + qofs[0][s & 3] + (s >> 2) * 256));
+        const bf16x8_t a1 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(R + qofs[1][s & 3] + (s >> 2) * 256));
+        sa = mfma16(a0, qb[s], sa);
+        sb = mfma16(a1, qb[s], sb);
+      }
     }
     // ---- swap partials with the other dim half
     xchg[w][0][l] = sa;
@@ -419,14 +482,41 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
     // ---- O += P R over this wave's dims; K order: rows 4G + 0..3, then 16 + 4G + 0..3
     const bf16x8_t pa = as_bf16x8(u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])});
+    if constexpr (KV8) {
+      // N-tile nt holds dims 256 dh + 16 nt: E4M3 below 448, bf16 for dh = 1, nt >= 12
+      auto v8 = [&](int nt) {
+        const i32x2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (i32x2_t __attribute__((address_space(3)))*)(R + vofs8 + 256 * dh + 16 * nt));
+        return as_bf16x8(u32x4_t{fp8x2_to_bf16x2((uint32_t)r[0], false), fp8x2_to_bf16x2((uint32_t)r[0], true),
+                                 fp8x2_to_bf16x2((uint32_t)r[1], false), fp8x2_to_bf16x2((uint32_t)r[1], true)});
+      };
+      auto v16 = [&](int nt) {
+        const int cofs = 2 * 16 * (nt - 12);
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4_t __attribute__((address_space(3)))*)(R + rofs8[0] + cofs));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4_t __attribute__((address_space(3)))*)(R + rofs8[1] + cofs));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
 #pragma unroll
-    for (int nt = 0; nt < 16; ++nt) {
-      auto* pa4 = (s16x4_t __attribute__((address_space(3)))*)(R + pofs[0][nt & 7] + (nt >> 3) * 256);
-      auto* pb4 = (s16x4_t __attribute__((address_space(3)))*)(R + pofs[1][nt & 7] + (nt >> 3) * 256);
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa4);
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pb4);
-      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[nt] = mfma16(pa, bv, o[nt]);
+      for (int nt = 0; nt < 12; ++nt) o[nt] = mfma16(pa, v8(nt), o[nt]);
+      if (dh == 0) {
+#pragma unroll
+        for (int nt = 12; nt < 16; ++nt) o[nt] = mfma16(pa, v8(nt), o[nt]);
+      } else {
+#pragma unroll
+        for (int nt = 12; nt < 16; ++nt) o[nt] = mfma16(pa, v16(nt), o[nt]);
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt) {
+        auto* pa4 = (s16x4_t __attribute__((address_space(3)))*)(R + pofs[0][nt & 7] + (nt >> 3) * 256);
+        auto* pb4 = (s16x4_t __attribute__((address_space(3)))*)(R + pofs[1][nt & 7] + (nt >> 3) * 256);
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa4);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pb4);
+        const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[nt] = mfma16(pa, bv, o[nt]);
+      }
     }
   }
 
@@ -1303,11 +1393,11 @@ static hipError_t launch_combine(const AttnLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int SRC>
+template <int SRC, bool KV8 = false>
 static hipError_t launch_bf16(const AttnLaunch& a, hipStream_t st) {
   if (SRC != SRC_HCA_DEC && a.split_rows > bfk::TAB_MAX) return hipErrorInvalidValue;
   dim3 grid((unsigned)a.nq, a.nsplit);
-  hipLaunchKernelGGL((attn_bf16_kernel<SRC>), grid, dim3(bfk::NT), 0, st, reinterpret_cast<const uint16_t*>(a.q),
+  hipLaunchKernelGGL((attn_bf16_kernel<SRC, KV8>), grid, dim3(bfk::NT), 0, st, reinterpret_cast<const uint16_t*>(a.q),
                      row_src(a), a.win_len, a.n_comp, a.q_pos, a.m_rate, a.sink, a.scale * LOG2E_F, a.H, a.slots,
                      a.split_rows, a.nsplit > 1 ? a.part_o : nullptr, a.part_ml, a.out, a.lse, a.out_dt);
   hipError_t e = hipGetLastError();
@@ -1347,6 +1437,10 @@ static hipError_t dispatch_src(const AttnLaunch& a, hipStream_t st) {
     } else {
       return launch_bf16<SRC>(a, st);
     }
+  }
+  if (a.kv_dt == DT_KV_FP8 && a.D == 512 && a.H > 48 && a.H <= 64) {
+    if constexpr (SRC == SRC_SPARSE_DEC || SRC == SRC_HCA_DEC) return launch_bf16<SRC, true>(a, st);
+    return hipErrorInvalidValue;
   }
   if (a.kv_dt == DT_F32 && a.D == 64 && a.H <= 16) return launch_f32<64, 1, SRC>(a, st);
   return hipErrorInvalidValue;

@@ -33,6 +33,57 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float* f) {
   }
 }
 
+// fp32 -> OCP E4M3 (FN) code, round to nearest even, saturating at +-448
+// (the format has no infinity): 3 mantissa bits kept from the binary32 bit
+// pattern, the exponent rebiased from 127 to 7; below 2^-6 the grid is the
+// subnormal step 2^-9 (a rounded multiple of 8 is the smallest normal).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    const uint32_t ua = __float_as_uint(a);
+    const uint32_t lsb = (ua >> 20) & 1u;
+    code = ((ua + 0x7ffffu + lsb) >> 20) - (120u << 3);
+  }
+  return code | sign;
+}
+
+// Stores 8 channels c0 .. c0+7 of one entry. Mixed-precision KV rows (d - 64
+// E4M3 bytes, then the 64 RoPE channels as bf16: d + 64 bytes) take E4M3 or
+// bf16 by the channels' side of d - 64 (a multiple of 8).
+template <int OUT_DT>
+__device__ __forceinline__ void store8(void* out, int64_t row, int d, int c0, const float* res) {
+  if constexpr (OUT_DT == DT_BF16) {
+    u32x4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(res[2 * e], res[2 * e + 1]);
+    st16(reinterpret_cast<uint16_t*>(out) + row * d + c0, v);
+  } else if constexpr (OUT_DT == DT_KV_FP8) {
+    uint8_t* orow = reinterpret_cast<uint8_t*>(out) + row * (int64_t)(d + 64);
+    const int nope = d - 64;
+    if (c0 < nope) {
+      uint32_t w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        w[h] = f32_to_e4m3(res[4 * h]) | (f32_to_e4m3(res[4 * h + 1]) << 8) | (f32_to_e4m3(res[4 * h + 2]) << 16) |
+               (f32_to_e4m3(res[4 * h + 3]) << 24);
+      *reinterpret_cast<u32x2_t*>(orow + c0) = u32x2_t{w[0], w[1]};
+    } else {
+      u32x4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(res[2 * e], res[2 * e + 1]);
+      *reinterpret_cast<u32x4_t*>(orow + nope + 2 * (c0 - nope)) = v;
+    }
+  } else {
+    float* p = reinterpret_cast<float*>(out) + row * d + c0;
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{res[0], res[1], res[2], res[3]};
+    *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{res[4], res[5], res[6], res[7]};
+  }
+}
+
 struct SoftAcc {
   float mx[8], sm[8], acc[8];
   __device__ void init() {
@@ -191,18 +242,7 @@ compress_kernel(const void* __restrict__ Ca, const void* __restrict__ Cb, const 
 #pragma unroll
     for (int e = 0; e < 8; ++e) res[e] = A.acc[e] / A.sm[e];
   }
-  const int64_t o = (b * out_cap + i) * d + c0;
-  if constexpr (OUT_DT == DT_BF16) {
-    u32x4_t v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(res[2 * e], res[2 * e + 1]);
-    st16(reinterpret_cast<uint16_t*>(out) + o, v);
-  } else {
-    float* p = reinterpret_cast<float*>(out) + o;
-    f32x4_t v0 = {res[0], res[1], res[2], res[3]}, v1 = {res[4], res[5], res[6], res[7]};
-    *reinterpret_cast<f32x4_t*>(p) = v0;
-    *reinterpret_cast<f32x4_t*>(p + 4) = v1;
-  }
+  store8<OUT_DT>(out, b * out_cap + i, d, c0, res);
 }
 
 // Single-branch compression with long blocks (HCA, m' = 128): a thread per
@@ -263,27 +303,28 @@ compress_split_kernel(const void* __restrict__ Ca, const void* __restrict__ Za, 
     part[2][sl][cgl * 8 + e] = A.acc[e];
   }
   __syncthreads();
-  if (threadIdx.x >= CS_CG * 8) return;
-  // merge: thread (channel group cgl2, channel e2)
-  const int ch = threadIdx.x, cgl2 = ch / 8;
+  // merge: thread cgl2 < 16 takes the 8 channels of its channel group
+  if (threadIdx.x >= CS_CG) return;
+  const int cgl2 = threadIdx.x;
   const int cg2 = (int)(blockIdx.x % cgb) * CS_CG + cgl2;
   if (cg2 >= groups) return;
-  float mx = -INFINITY;
+  float res[8];
 #pragma unroll
-  for (int q = 0; q < CS_SL; ++q) mx = fmaxf(mx, part[0][q][ch]);
-  float sm = 0.f, acc = 0.f;
+  for (int e = 0; e < 8; ++e) {
+    const int ch = cgl2 * 8 + e;
+    float mx = -INFINITY;
 #pragma unroll
-  for (int q = 0; q < CS_SL; ++q) {
-    const float a = part[0][q][ch] == -INFINITY ? 0.f : exp2f(part[0][q][ch] - mx);
-    sm += part[1][q][ch] * a;
-    acc += part[2][q][ch] * a;
+    for (int q = 0; q < CS_SL; ++q) mx = fmaxf(mx, part[0][q][ch]);
+    float sm = 0.f, acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < CS_SL; ++q) {
+      const float a = part[0][q][ch] == -INFINITY ? 0.f : exp2f(part[0][q][ch] - mx);
+      sm += part[1][q][ch] * a;
+      acc += part[2][q][ch] * a;
+    }
+    res[e] = acc / sm;
   }
-  const float r = acc / sm;
-  const int64_t o = (b * out_cap + i) * d + cg2 * 8 + (ch % 8);
-  if constexpr (OUT_DT == DT_BF16)
-    reinterpret_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16(r);
-  else
-    reinterpret_cast<float*>(out)[o] = r;
+  store8<OUT_DT>(out, b * out_cap + i, d, cg2 * 8, res);
 }
 
 template <int IN_DT, int OUT_DT>
@@ -307,6 +348,8 @@ static hipError_t launch(const CompressLaunch& a, hipStream_t st) {
 
 hipError_t run_compress(const CompressLaunch& a, hipStream_t st) {
   if (a.B == 0 || a.blk_end <= a.blk_begin) return hipSuccess;
+  if (a.out_dt == DT_KV_FP8)
+    return a.in_dt == DT_BF16 ? launch<DT_BF16, DT_KV_FP8>(a, st) : launch<DT_F32, DT_KV_FP8>(a, st);
   if (a.in_dt == DT_BF16 && a.out_dt == DT_BF16) return launch<DT_BF16, DT_BF16>(a, st);
   if (a.in_dt == DT_BF16 && a.out_dt == DT_F32) return launch<DT_BF16, DT_F32>(a, st);
   if (a.in_dt == DT_F32 && a.out_dt == DT_BF16) return launch<DT_F32, DT_BF16>(a, st);

@@ -64,6 +64,20 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 15) & ((c & 7) == 7), np.nan, v)
 
 
+def kv_fp8_decode(rows: np.ndarray, D: int) -> np.ndarray:
+    """Mixed-precision main-KV row -> values (the pages keep the RoPE dims in
+    BF16 and the rest in FP8): bytes 0 .. D-65 are OCP E4M3 codes of dims
+    0 .. D-65; the next 128 bytes are dims D-64 .. D-1 as bf16, little endian
+    (value = the bf16 bits as the upper half of an IEEE binary32)."""
+    r = np.asarray(rows, dtype=np.uint8)
+    nope = D - 64
+    assert r.shape[-1] == nope + 128
+    lo = r[..., nope::2].astype(np.uint32)
+    hi = r[..., nope + 1::2].astype(np.uint32)
+    rope = ((hi << 24) | (lo << 16)).astype(np.uint32).view(np.float32).astype(F64)
+    return np.concatenate([e4m3_decode(r[..., :nope]), rope], axis=-1)
+
+
 def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """OCP MXFP4 (Microscaling Formats v1.0) -> values, from the format
     definition. Element: FP4 E2M1, sign(1) exp(2, bias 1) mantissa(1), exponent

@@ -100,6 +100,24 @@ def e4m3_quantize_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return codes, scale
 
 
+# Mixed-precision main KV rows: the RoPE dims (the last 64) stay bf16, the
+# other D - 64 dims are E4M3 codes, with no scale.
+KV_ROPE_DIMS = 64
+
+
+def kv_fp8_rows(x: np.ndarray) -> np.ndarray:
+    """float32 rows [..., D] -> mixed-precision rows uint8 [..., D - 64 + 128]:
+    bytes 0 .. D-65 are the E4M3 codes of dims 0 .. D-65 (e4m3_encode: round to
+    nearest even, saturating at +-448), then the 64 RoPE dims as bf16 (round
+    to nearest even), two bytes each, little endian."""
+    x = np.asarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    nope = D - KV_ROPE_DIMS
+    codes = e4m3_encode(x[..., :nope])
+    rope = np.ascontiguousarray(bf16_bits(x[..., nope:])).view(np.uint8)
+    return np.ascontiguousarray(np.concatenate([codes, rope], axis=-1))
+
+
 MXFP4_BLOCK = 32
 
 
@@ -162,6 +180,7 @@ class Cfg:
     W: int = 128         # sliding window
     dtype: str = "bf16"  # storage dtype of activations / caches
     k_dtype: str = "bf16"  # indexer key storage
+    kv_dtype: str = "bf16"  # main KV rows: "bf16", or "fp8" (E4M3 + bf16 RoPE dims)
     Tq: int = 1          # queries per sequence
 
     @property
@@ -186,7 +205,11 @@ C2X = dataclasses.replace(C2, name="c2x_csa_decode_flash_128k_mxfp4", k_dtype="m
 # HCA prefill of one 64K sequence: single-branch compression at m' = 128
 # (512 entries), then every query over all entries it can see plus its window
 C6 = Cfg("c6_hca_prefill_64k", 6, "hca_prefill", B=1, n=65536, m=128, H=64, D=512, W=128, Tq=65536)
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6)}
+# C4 and C2 with the main KV cache as the pages store it (RoPE dims bf16, the
+# rest FP8), same seeds and shapes
+C4F = dataclasses.replace(C4, name="c4f_hca_decode_1m_kv_fp8", kv_dtype="fp8")
+C2F = dataclasses.replace(C2, name="c2f_csa_decode_flash_128k_kv_fp8", kv_dtype="fp8")
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6, C4F, C2F)}
 
 
 def scaled(cfg: Cfg, **kw) -> Cfg:
@@ -220,8 +243,12 @@ def gen_decode_seq(cfg: Cfg, b: int, with_compress: bool = True) -> Dict[str, np
     s, D = cfg.seed, cfg.D
     out: Dict[str, np.ndarray] = {}
     out["q"] = _store(_normal(rng(s, "q", b), (cfg.H, D), 1.0 / math.sqrt(D)), cfg.dtype)
-    out["kv_comp"] = _store(_normal(rng(s, "kv_comp", b), (cfg.N, D)), cfg.dtype)
-    out["kv_win"] = _store(_normal(rng(s, "kv_win", b), (min(cfg.W, cfg.n), D)), cfg.dtype)
+    kv = _normal(rng(s, "kv_comp", b), (cfg.N, D))
+    win = _normal(rng(s, "kv_win", b), (min(cfg.W, cfg.n), D))
+    if cfg.kv_dtype == "fp8":  # uint8 rows [.., D + 64]
+        out["kv_comp"], out["kv_win"] = kv_fp8_rows(kv), kv_fp8_rows(win)
+    else:
+        out["kv_comp"], out["kv_win"] = _store(kv, cfg.dtype), _store(win, cfg.dtype)
     if cfg.kind == "csa_decode":
         HI, DI = cfg.H_I, cfg.D_I
         out["q_idx"] = _store(_normal(rng(s, "q_idx", b), (HI, DI), 1.0 / math.sqrt(DI)), cfg.dtype)

@@ -64,6 +64,9 @@ def test_compress_validation():
     # validation; block 4 would need token 12 for its overlap branch
     assert f(P, P, P, P, P, P, P, 1, 8, 16, 64, 4, 4, 6, 6, 1, 0, 0, None) == L.INVALID_ARG
     assert "previous block" in _err()
+    # mixed-precision KV output rows need d > 64
+    assert f(P, P, P, P, P, P, P, 1, 8, 0, 64, 4, 0, 2, 2, 1, 0, L.KV_FP8, None) == L.UNSUPPORTED
+    assert "d > 64" in _err()
 
 
 def test_indexer_validation():
@@ -122,7 +125,14 @@ def test_attention_validation():
     # f32 rows stage at most 1024 top-k slots; bf16 rows take any top_k with top_k + W <= 2048
     assert p(P, P, P, P, P, P, 1.0, 4, 16, 64, 2000, 4000, 1025, 8, 0, 0, P, None, None, 0, None) == L.UNSUPPORTED
     assert "top_k <= 1024" in _err()
+    # mixed-precision KV rows: decode only; the prefill entry points refuse them
+    assert p(P, P, P, P, P, P, 1.0, 4, 64, 512, 100, 400, 16, 8, L.KV_FP8, 1, P, None, None, 0, None) == \
+        L.UNSUPPORTED
+    assert "BF16 or F32 rows" in _err()
+    assert f(P, P, P, P, P, P, 1.0, 2, 64, 256, 100, 16, 8, L.KV_FP8, 1, P, None, P, 1 << 30, None) == L.UNSUPPORTED
     hp = L.lib.hca_prefill
+    assert hp(P, P, P, P, P, 1.0, 4, 64, 512, 512, 128, 65536, 128, L.KV_FP8, 1, P, None, None, 0, None) == \
+        L.UNSUPPORTED
     # q_pos null; m = 0; unsupported heads; N + W beyond 2^24; bad scale
     assert hp(P, P, P, None, P, 1.0, 4, 64, 512, 512, 128, 65536, 128, 1, 1, P, None, None, 0, None) == L.INVALID_ARG
     assert hp(P, P, P, P, P, 1.0, 4, 64, 512, 512, 0, 65536, 128, 1, 1, P, None, None, 0, None) == L.INVALID_ARG

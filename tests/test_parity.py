@@ -320,6 +320,101 @@ def test_sparse_decode_edge_rows():
             assert np.abs(LS[b] - rlse).max() < 1e-3
 
 
+def _kv8(x):
+    """float32 rows [..., 512] -> (mixed-precision rows uint8 [..., 576] on the
+    device, the values they hold as float64 for the oracle)."""
+    rows = gen.kv_fp8_rows(x)
+    return dev(rows), oracle.kv_fp8_decode(rows, x.shape[-1])
+
+
+def test_sparse_decode_kv_fp8():
+    """Mixed-precision rows (E4M3 except the 64 bf16 RoPE dims) through the
+    decode kernel, with the edge rows of the bf16 test: short and empty
+    selections, a duplicate, an out-of-range index, window lengths 128/5/0/77."""
+    _say("sparse_decode", "kv_fp8")
+    g = _g(33)
+    B, H, D, N_max, k, W = 4, 64, 512, 700, 300, 128
+    q = gen.bf16_round(g.standard_normal((B, H, D)).astype(np.float32) / math.sqrt(D))
+    kv_d, kv_v = _kv8(g.standard_normal((B, N_max, D)).astype(np.float32))
+    win_d, win_v = _kv8(g.standard_normal((B, W, D)).astype(np.float32))
+    idx = np.sort(g.choice(N_max, size=(B, k)), axis=1).astype(np.int32)
+    idx[0, 250:] = -1
+    idx[1, :] = -1
+    idx[2, 10] = idx[2, 11]
+    idx[3, 5] = N_max + 3
+    win_len = np.array([128, 5, 0, 77], np.int32)
+    sink = g.standard_normal(H).astype(np.float32)
+    out = torch.empty((B, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H), device=DEV)
+    L.sparse_mqa_decode(bf(q), kv_d, dev(idx), win_d, dev(win_len), dev(sink), out, lse)
+    torch.cuda.synchronize()
+    O, LS = host(out), host(lse)
+    for b in range(B):
+        ids = idx[b][(idx[b] >= 0) & (idx[b] < N_max)]
+        rows = np.concatenate([kv_v[b][ids], win_v[b][:win_len[b]]])
+        ref, rlse = oracle.attend(q[b], rows, sink)
+        check_out(O[b], ref, _attn_tight(ref), f"sparse_decode kv_fp8 b={b}")
+        assert np.abs(LS[b] - rlse).max() < 1e-3
+
+
+@pytest.mark.parametrize("N_max,V1", [(1500, 1000), (5000, 3333)])
+def test_hca_decode_kv_fp8(N_max, V1):
+    """Dense HCA splits over mixed-precision rows (as the bf16 test)."""
+    _say("hca_decode kv_fp8", N_max)
+    g = _g(34)
+    B, H, D, W, m = 3, 64, 512, 128, 128
+    q = gen.bf16_round(g.standard_normal((B, H, D)).astype(np.float32) / math.sqrt(D))
+    kv_d, kv_v = _kv8(g.standard_normal((B, N_max, D)).astype(np.float32))
+    win_d, win_v = _kv8(g.standard_normal((B, W, D)).astype(np.float32))
+    n_comp = np.array([N_max, N_max, 40], np.int32)
+    q_pos = np.array([N_max * 128 + 5, V1 * 128 - 1, 10 ** 6], np.int32)
+    win_len = np.array([128, 128, 3], np.int32)
+    sink = g.standard_normal(H).astype(np.float32)
+    out = torch.empty((B, H, D), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, H), device=DEV)
+    L.hca_dense_mqa(bf(q), kv_d, dev(n_comp), dev(q_pos), win_d, dev(win_len), dev(sink), out, lse, m=m)
+    torch.cuda.synchronize()
+    O, LS = host(out), host(lse)
+    for b in range(B):
+        ref, rlse = oracle.hca_query(q[b], kv_v[b], int(q_pos[b]), int(n_comp[b]), m, win_v[b][:win_len[b]], sink)
+        check_out(O[b], ref, _attn_tight(ref), f"hca kv_fp8 b={b}")
+        assert np.abs(LS[b] - rlse).max() < 1e-3
+
+
+@pytest.mark.parametrize("m,overlap", [(4, True), (128, False)])
+def test_compress_kv_fp8_rows(m, overlap):
+    """Compression writing mixed-precision KV rows: each value within half an
+    E4M3 step (bf16 for the RoPE channels) of the oracle's entry, and the
+    codes exactly the round-to-nearest-even encoding of the same call's fp32
+    result (the rounding rule of the format, checked on the kernel's own
+    values), with rows outside the block range untouched."""
+    _say("compress kv_fp8", m, overlap)
+    g = _g(35 + m)
+    B, d, nblk = 2, 512, 6
+    n_rows = m * nblk + 3
+    arrs = [gen.bf16_round(g.standard_normal((B, n_rows, d)).astype(np.float32)) for _ in range(4)]
+    Ba = g.standard_normal((m, d)).astype(np.float32)
+    Bb = g.standard_normal((m, d)).astype(np.float32)
+    Ca, Cb, Za, Zb = (bf(a) for a in arrs)
+    kw = dict(m=m, blk_begin=1, blk_end=nblk, overlap=overlap)
+    out8 = torch.full((B, nblk, d + 64), 0x5A, dtype=torch.uint8, device=DEV)
+    out32 = torch.empty((B, nblk, d), dtype=torch.float32, device=DEV)
+    cb, zb, bb = (Cb, Zb, dev(Bb)) if overlap else (None, None, None)
+    L.csa_compress(Ca, cb, Za, zb, dev(Ba), bb, out8, **kw)
+    L.csa_compress(Ca, cb, Za, zb, dev(Ba), bb, out32, **kw)
+    torch.cuda.synchronize()
+    got8, got32 = host(out8), host(out32)
+    assert np.all(got8[:, 0] == 0x5A), "row outside the block range written"
+    assert np.array_equal(got8[:, 1:], gen.kv_fp8_rows(got32[:, 1:])), "codes differ from RNE of the fp32 result"
+    for b in range(B):
+        ref = oracle.compress(arrs[0][b], arrs[1][b], arrs[2][b], arrs[3][b], Ba, Bb, m, overlap=overlap,
+                              blocks=range(1, nblk))
+        v = oracle.kv_fp8_decode(got8[b, 1:], d)
+        step = np.where(np.arange(d) < d - 64, 2.0 ** -4, 2.0 ** -8)  # half-step relative bound per channel
+        bound = np.maximum(np.abs(ref) * step, 2.0 ** -10) + 1e-5
+        assert np.all(np.abs(v - ref) <= bound), f"b={b} max err {np.abs(v - ref).max():.3e}"
+
+
 def test_sparse_decode_no_sink_empty():
     _say("sparse_decode", "empty")
     B, H, D = 1, 64, 512

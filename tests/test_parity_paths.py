@@ -32,11 +32,31 @@ def _tight(ref):
     return 2.0 ** -7 * max(1.0, float(np.abs(ref).max(initial=0.0)))
 
 
+def _kv(cfg, rows):
+    """A main-KV tensor to the device: bf16 values, or mixed-precision bytes."""
+    return _t(rows) if cfg.kv_dtype == "fp8" else _bf(rows)
+
+
+def _kv_values(cfg, rows):
+    return oracle.kv_fp8_decode(rows, cfg.D) if cfg.kv_dtype == "fp8" else np.asarray(rows, np.float64)
+
+
+def _check_entry(cfg, got_row, ent, what):
+    """The appended entry: bf16 within its rounding; mixed-precision rows
+    within half an E4M3 step (bf16 for the RoPE dims)."""
+    if cfg.kv_dtype == "fp8":
+        v = oracle.kv_fp8_decode(got_row, cfg.D)
+        step = np.where(np.arange(cfg.D) < cfg.D - 64, 2.0 ** -4, 2.0 ** -8)
+        assert np.all(np.abs(v - ent) <= np.maximum(np.abs(ent) * step, 2.0 ** -10) + 1e-5), what
+    else:
+        check_out(got_row, ent, 2.0 ** -8 * max(1.0, np.abs(ent).max()), what)
+
+
 def run_csa_decode(cfg, x):
     """One decode token per sequence, as bench.py runs it."""
     L = _L()
     B, N, m, k, W = cfg.B, cfg.N, cfg.m, cfg.top_k, cfg.W
-    kv = _bf(x["kv_comp"])
+    kv = _kv(cfg, x["kv_comp"])
     L.csa_compress(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]), _t(x["Bb"]), kv, m=m,
                    tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
     q_pos = _t(np.full((B, 1), cfg.n - 1, np.int32))
@@ -53,7 +73,7 @@ def run_csa_decode(cfg, x):
     L.indexer_topk(scores, q_pos, n_comp, idx, m=m)
     out = torch.empty((B, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, cfg.H), device=DEV)
-    L.sparse_mqa_decode(_bf(x["q"]), kv, idx.view(B, k), _bf(x["kv_win"]), _t(np.full((B,), W, np.int32)),
+    L.sparse_mqa_decode(_bf(x["q"]), kv, idx.view(B, k), _kv(cfg, x["kv_win"]), _t(np.full((B,), W, np.int32)),
                         _t(x["sink"]), out, lse)
     torch.cuda.synchronize()
     # the cache stays on the device (GBs at full size); only its last two rows come back
@@ -69,10 +89,10 @@ def check_csa_decode(cfg, x, seqs):
         # their second block, with the first as its overlapping predecessor
         ent = oracle.compress(x["Ca"][b], x["Cb"][b], x["Za"][b], x["Zb"][b], x["Ba"], x["Bb"], m,
                               blocks=range(1, 2))[0]
-        check_out(kv2[b, 1], ent, 2.0 ** -8 * max(1.0, np.abs(ent).max()), "compressed entry N-1")
+        _check_entry(cfg, kv2[b, 1], ent, "compressed entry N-1")
         assert np.array_equal(kv2[b, 0], x["kv_comp"][b, N - 2]), "compress wrote outside its block"
-        comp = x["kv_comp"][b].astype(np.float64)
-        comp[N - 1] = kv2[b, 1]  # the stored (bf16) entry is what the step attends
+        comp = _kv_values(cfg, x["kv_comp"][b])
+        comp[N - 1] = _kv_values(cfg, kv2[b, 1])  # the stored entry is what the step attends
         if cfg.k_dtype == "fp8":
             keys, sc = oracle.e4m3_decode(x["k_idx_codes"][b]), x["k_scale"][b]
         elif cfg.k_dtype == "mxfp4":
@@ -80,10 +100,11 @@ def check_csa_decode(cfg, x, seqs):
         else:
             keys, sc = x["k_idx"][b], None
         oidx, o_ref, lse_ref, s = oracle.csa_query(x["q"][b], x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, N,
-                                                   m, cfg.top_k, x["kv_win"][b], x["sink"], k_scale=sc)
+                                                   m, cfg.top_k, _kv_values(cfg, x["kv_win"][b]), x["sink"],
+                                                   k_scale=sc)
         assert np.abs(S[b] - s).max() <= 2e-5 * 8 * (1 + np.abs(s).max())
         check_topk_row(I[b], oidx, s, cfg.top_k, f"b={b}")
-        rows = np.concatenate([comp[I[b][I[b] >= 0]], x["kv_win"][b]])
+        rows = np.concatenate([comp[I[b][I[b] >= 0]], _kv_values(cfg, x["kv_win"][b])])
         o_own, lse_own = oracle.attend(x["q"][b], rows, x["sink"])
         check_out(O[b], o_own, _tight(o_own), f"out on gpu idx b={b}")
         assert np.abs(LSE[b] - lse_own).max() < 1e-3
@@ -117,13 +138,13 @@ def run_hca_decode(cfg, x):
     single-branch compression, then dense MQA over all entries + window."""
     L = _L()
     B, N, m, W = cfg.B, cfg.N, cfg.m, cfg.W
-    kv = _bf(x["kv_comp"])
+    kv = _kv(cfg, x["kv_comp"])
     L.csa_compress(_bf(x["Ca"]), None, _bf(x["Za"]), None, _t(x["Ba"]), None, kv, m=m, tok_begin=cfg.n - m,
                    blk_begin=N - 1, blk_end=N, overlap=False)
     out = torch.empty((B, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, cfg.H), device=DEV)
     L.hca_dense_mqa(_bf(x["q"]), kv, _t(np.full((B,), N, np.int32)), _t(np.full((B,), cfg.n - 1, np.int32)),
-                    _bf(x["kv_win"]), _t(np.full((B,), W, np.int32)), _t(x["sink"]), out, lse, m=m)
+                    _kv(cfg, x["kv_win"]), _t(np.full((B,), W, np.int32)), _t(x["sink"]), out, lse, m=m)
     torch.cuda.synchronize()
     return host(kv[:, N - 2:]), host(out), host(lse)
 
@@ -135,11 +156,11 @@ def check_hca_decode(cfg, seqs):
     for b in seqs:
         print(f"[case] {cfg.name} b={b}", flush=True)
         ent = oracle.compress(x["Ca"][b], None, x["Za"][b], None, x["Ba"], None, m, overlap=False)[0]
-        check_out(kv2[b, 1], ent, 2.0 ** -8 * max(1.0, np.abs(ent).max()), "hca entry N-1")
+        _check_entry(cfg, kv2[b, 1], ent, "hca entry N-1")
         assert np.array_equal(kv2[b, 0], x["kv_comp"][b, N - 2]), "compress wrote outside its block"
-        comp = x["kv_comp"][b].astype(np.float64)
-        comp[N - 1] = kv2[b, 1]  # the stored (bf16) entry is what the step attends
-        ref, rlse = oracle.hca_query(x["q"][b], comp, cfg.n - 1, N, m, x["kv_win"][b], x["sink"])
+        comp = _kv_values(cfg, x["kv_comp"][b])
+        comp[N - 1] = _kv_values(cfg, kv2[b, 1])  # the stored entry is what the step attends
+        ref, rlse = oracle.hca_query(x["q"][b], comp, cfg.n - 1, N, m, _kv_values(cfg, x["kv_win"][b]), x["sink"])
         check_out(O[b], ref, _tight(ref), f"hca b={b}")
         assert np.abs(LS[b] - rlse).max() < 1e-3
 
@@ -151,6 +172,16 @@ def test_hca_decode_reduced():
 def test_hca_decode_1m_full_size():
     cfg = gen.C4  # 16 sequences x 8192 entries, every sequence checked
     check_hca_decode(cfg, range(cfg.B))
+
+
+def test_hca_decode_1m_kv_fp8_full_size():
+    cfg = gen.C4F  # mixed-precision main KV, as bench.py runs it
+    check_hca_decode(cfg, range(cfg.B))
+
+
+def test_csa_decode_flash_kv_fp8_full_size_sampled():
+    cfg = gen.C2F  # mixed-precision main KV, as bench.py runs it
+    check_csa_decode(cfg, gen.gen_decode(cfg), [0, 13, 31])
 
 
 def run_prefill_chunk(cfg, tok, comp_t, chunk):

@@ -15,9 +15,9 @@ data from the previous one.
 
 Other workloads: c5 (1M context, E4M3 indexer keys), c2x (c2 with MXFP4
 indexer keys), c4 (HCA decode 1M), c3 (CSA prefill 64K), c6 (HCA prefill 64K),
-c4f / c2f (c4 / c2 with the main KV rows in E4M3 + bf16 RoPE dims).
+c4f / c2f / c3f (c4 / c2 / c3 with the main KV rows in E4M3 + bf16 RoPE dims).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c5|c4|c3|c2x|c6|c4f|c2f]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c5|c4|c3|c2x|c6|c4f|c2f|c3f]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -45,7 +45,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4", "c3", "c2x", "c6", "c4f", "c2f"])
+    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4", "c3", "c2x", "c6", "c4f", "c2f", "c3f"])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -106,8 +106,8 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
                           "copies": 3}), flush=True)
         return
-    if a.workload == "c3":
-        return bench_prefill(a, torch, L, gen, dev)
+    if a.workload in ("c3", "c3f"):
+        return bench_prefill(a, torch, L, gen, dev, gen.C3F if a.workload == "c3f" else gen.C3)
     if a.workload == "c6":
         return bench_hca_prefill(a, torch, L, gen, dev)
     cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X, "c4f": gen.C4F, "c2f": gen.C2F}[a.workload]
@@ -282,10 +282,10 @@ def prefill_flops(cfg, pos):
     return idx, mqa
 
 
-def bench_prefill(a, torch, L, gen, dev):
+def bench_prefill(a, torch, L, gen, dev, cfg):
     """CSA prefill of one 65536-token sequence: compression of all tokens, then
-    16 chunks of 4096 queries through scores, top-k and sparse MQA."""
-    cfg = gen.C3
+    16 chunks of 4096 queries through scores, top-k and sparse MQA (main KV
+    rows in bf16, or E4M3 + bf16 RoPE dims)."""
     t0 = time.time()
     tok = gen.gen_prefill_tokens(cfg)
     bf = lambda v: torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).to(dev)
@@ -293,8 +293,10 @@ def bench_prefill(a, torch, L, gen, dev):
     N, m, D, H, k, W = cfg.N, cfg.m, cfg.D, cfg.H, cfg.top_k, cfg.W
     Ca, Cb, Za, Zb = (bf(tok[nm][None]) for nm in ("Ca", "Cb", "Za", "Zb"))
     Ba, Bb, sink = td(tok["Ba"]), td(tok["Bb"]), td(tok["sink"])
-    kv_tok, k_idx = bf(tok["kv_tok"]), bf(tok["k_idx"][None])
-    comp = torch.empty((1, N, D), dtype=torch.bfloat16, device=dev)
+    fp8 = cfg.kv_dtype == "fp8"
+    kv_tok, k_idx = (td if fp8 else bf)(tok["kv_tok"]), bf(tok["k_idx"][None])
+    comp = (torch.empty((1, N, D + 64), dtype=torch.uint8, device=dev) if fp8
+            else torch.empty((1, N, D), dtype=torch.bfloat16, device=dev))
     nch = gen.num_chunks(cfg)
     chunks = []
     for c in range(nch):
@@ -353,10 +355,11 @@ def bench_prefill(a, torch, L, gen, dev):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.n, "query_chunk": T, "compressed_entries": N, "m": m,
                    "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I, "heads": H, "head_dim": D,
-                   "window": W},
+                   "window": W, "kv_dtype": cfg.kv_dtype},
         "prefill_tflops": round(total_fl / (ms * 1e-3) / 1e12, 2),
         "algorithmic_tflop": round(total_fl / 1e12, 3),
-        "roofline": {"bound": "mfma", "kernel": "attn_prs_kernel<2> (sparse prefill)", "achieved": round(mqa_tfs, 1),
+        "roofline": {"bound": "mfma", "kernel": "attn_prs_kernel<2, %s> (sparse prefill)" % ("true" if fp8 else "false"),
+                     "achieved": round(mqa_tfs, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mqa_tfs / BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flops_all_launches": mqa_fl,
                      "avg_launch_ms": round(float(np.mean(attn_ms)), 4)},
@@ -481,6 +484,10 @@ def cpu_prefill_baseline(cfg, tok, budget_s: float):
     from synth import gen
     t0 = time.perf_counter()
     comp = oracle.compress(tok["Ca"], tok["Cb"], tok["Za"], tok["Zb"], tok["Ba"], tok["Bb"], cfg.m)
+    kv_tok = tok["kv_tok"]
+    if cfg.kv_dtype == "fp8":  # the entries as stored, and the token rows' values
+        comp = oracle.kv_fp8_decode(gen.kv_fp8_rows(comp), cfg.D)
+        kv_tok = oracle.kv_fp8_decode(kv_tok, cfg.D)
     t_comp = time.perf_counter() - t0
     qs = gen.gen_prefill_queries(cfg, gen.num_chunks(cfg) - 1)
     t1 = time.perf_counter()
@@ -489,7 +496,7 @@ def cpu_prefill_baseline(cfg, tok, budget_s: float):
         i = len(qs["q_pos"]) - 1 - done
         p = int(qs["q_pos"][i])
         oracle.csa_query(qs["q"][i], qs["q_idx"][i], qs["w"][i], comp, tok["k_idx"], p, cfg.N, cfg.m, cfg.top_k,
-                         oracle.window_rows(tok["kv_tok"], p, cfg.W), tok["sink"])
+                         oracle.window_rows(kv_tok, p, cfg.W), tok["sink"])
         pairs += min(cfg.N, (p + 1) // cfg.m)
         done += 1
     t_q = time.perf_counter() - t1

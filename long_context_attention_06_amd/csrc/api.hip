@@ -271,8 +271,7 @@ int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_i
   REQ(W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
   REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
   REQ(Tq <= 0x7fffffff, CSA_UNSUPPORTED, "Tq too large");
-  REQ(kv_dt != CSA_KV_FP8, CSA_UNSUPPORTED, "sparse_mqa_prefill reads BF16 or F32 rows");
-  REQ(kv_dt == CSA_BF16 || top_k <= 1024, CSA_UNSUPPORTED, "sparse_mqa_prefill on f32 rows supports top_k <= 1024");
+  REQ(kv_dt != CSA_F32 || top_k <= 1024, CSA_UNSUPPORTED, "sparse_mqa_prefill on f32 rows supports top_k <= 1024");
   REQ(top_k + W <= 2048, CSA_UNSUPPORTED, "sparse_mqa_prefill supports top_k + W <= 2048 rows per query");
   csa::AttnLaunch a{};
   a.src = 2;
@@ -317,7 +316,6 @@ int hca_prefill(const void* q, const void* kv_comp, const void* kv_tok, const in
   REQ(W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
   REQ(N + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
   REQ(Tq <= 0x7fffffff, CSA_UNSUPPORTED, "Tq too large");
-  REQ(kv_dt != CSA_KV_FP8, CSA_UNSUPPORTED, "hca_prefill reads BF16 or F32 rows");
   csa::AttnLaunch a{};
   a.src = 3;
   a.q = q;

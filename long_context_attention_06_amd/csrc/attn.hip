@@ -626,14 +626,22 @@ constexpr int PSTR = 40;         // bf16 per head row of a P^T buffer: 32 rows +
 constexpr float GUARD = 64.0f;   // log2 units a logit may sit above the shared reference
 }  // namespace prs
 
-template <int SRC>
+template <int SRC, bool KV8>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __restrict__ q_pos, int m_rate,
                 const float* __restrict__ sink, float scale_log2, int H, int slots, void* __restrict__ out,
                 float* __restrict__ lse, int out_dt) {
   using namespace prs;
   static_assert(SRC == SRC_SPARSE_PRE || SRC == SRC_HCA_PRE, "prefill row sources");
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TILEB];
+  // KV8 rows (448 E4M3 bytes, then the 64 RoPE dims as bf16: 576 bytes) sit
+  // unswizzled in LDS at a 592-byte pitch, the second half of a tile 64
+  // bytes further on, as in the decode kernel
+  constexpr int SROWB = KV8 ? 576 : ROWB;
+  constexpr int NOPE = 448;
+  constexpr int PITCH = KV8 ? 592 : ROWB;
+  constexpr int TB = KV8 ? TR * PITCH + 64 : TILEB;
+  auto lrow = [](int r) { return KV8 ? r * PITCH + (r >> 4) * 64 : r * ROWB; };
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TB];
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][2][32 * PSTR];  // [tile parity][head group] P^T
   __shared__ __attribute__((aligned(16))) float lmx[2][2][2][64];          // [head group][row half][hq][lane]
   __shared__ __attribute__((aligned(16))) int flg[2][NW];                  // [tile parity][wave]: P must be redone
@@ -651,7 +659,7 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   // softmax head of hq = (l >> 4) & 1, dims 256 dh + 32 nt + 8 (r/4) + 4 h + r%4.
   const int ohq = (l >> 4) & 1;
 
-  QRows rr = query_rows<SRC>(src, nullptr, nullptr, q_pos, m_rate, qi, 0, slots, slots);
+  QRows rr = query_rows<SRC, SROWB>(src, nullptr, nullptr, q_pos, m_rate, qi, 0, slots, slots);
 
   // ---- Q^T operand (B of S = K Q^T): head 32 hg + 16 hq + l16, dims 32 ks + 8 gc
   // .. +7 with gc = the two bits of g16 swapped (the K operand takes the same
@@ -683,18 +691,22 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   uint32_t voff[RPW];
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) voff[i] = (uint32_t)((l ^ swz4(RPW * w + i)) * 16);
+  for (int i = 0; i < RPW; ++i) voff[i] = KV8 ? (uint32_t)(l * 16) : (uint32_t)((l ^ swz4(RPW * w + i)) * 16);
+  // a KV8 row is 36 lanes x 16 bytes; the other lanes' LDS slots belong to the next row
+  auto row_dma = [&](const uint8_t* base, uint32_t off, uint32_t lds) {
+    if (!KV8 || l < SROWB / 16) dma_row(base, off, __builtin_amdgcn_readfirstlane(lds));
+  };
   auto issue = [&](int t) {
     const int c0 = t * TR + RPW * w;
-    const uint32_t dst = ring_lds + (uint32_t)((t & (NBUF - 1)) * TILEB + RPW * w * ROWB);
+    const uint32_t dst = ring_lds + (uint32_t)((t & (NBUF - 1)) * TB);
     if constexpr (SRC == SRC_HCA_PRE) {
       // rows past the end repeat the last row (they are masked)
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int c = min(c0 + i, n_rows - 1);
-        const uint8_t* rp = c < rr.len1 ? rr.comp_base + (int64_t)c * ROWB
-                                        : rr.win_base + (int64_t)(rr.w0 + c - rr.len1) * ROWB;
-        dma_row(uniform_ptr(rp), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+        const uint8_t* rp = c < rr.len1 ? rr.comp_base + (int64_t)c * SROWB
+                                        : rr.win_base + (int64_t)(rr.w0 + c - rr.len1) * SROWB;
+        row_dma(uniform_ptr(rp), voff[i], dst + lrow(RPW * w + i));
       }
       return;
     }
@@ -707,13 +719,13 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const uint32_t e = i < 4 ? e0[i & 3] : e1[i & 3];
-        dma_row(uniform_ptr(base), (e << 10) + voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+        row_dma(uniform_ptr(base), (e & 0x7fffffffu) * SROWB + voff[i], dst + lrow(RPW * w + i));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         const int e = (int)__builtin_amdgcn_readfirstlane(i < 4 ? e0[i & 3] : e1[i & 3]);
-        dma_row(uniform_ptr(tab_row(rr, e)), voff[i], __builtin_amdgcn_readfirstlane(dst + i * ROWB));
+        row_dma(uniform_ptr(tab_row<SROWB>(rr, e)), voff[i], dst + lrow(RPW * w + i));
       }
     }
   };
@@ -768,9 +780,43 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   // P^T write: this lane's four rows 16 dh + 4 g16 .. +3 of head 16 hq + l16
   const int pwr = l16 * PSTR + 16 * dh + 4 * g16;
 
+  // KV8: the K operand of k-steps below 14 (dims < 448) is 8 E4M3 bytes per
+  // lane, widened at the product; k-steps 14, 15 read the bf16 RoPE dims.
+  // V^T of the E4M3 dims comes from the 8-bit transposed read: within a
+  // 16-lane group, lanes 2k and 2k+1 address row 16 ks + 8 h + k (columns 0-7
+  // and 8-15 of a 16-dim block) and lane j receives column j of those eight
+  // rows (P^T's K order); the RoPE N-tiles (dims 448-511) use the 16-bit
+  // transposed read, with the same lane roles as the bf16 layout.
+  const int kofs8 = lrow(16 * dh + l16) + 8 * gc;
+  const int kofs8r = lrow(16 * dh + l16) + NOPE + 16 * gc;
+  int vofs8[2], rofs8[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    vofs8[ks] = lrow(16 * ks + 8 * h + (l16 >> 1)) + 16 * (g16 & 1) + 8 * (l16 & 1) + 256 * dh;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+      rofs8[ks][rd] = lrow(16 * ks + 8 * h + 4 * rd + (l16 >> 2)) + NOPE + 32 * (g16 & 1) + 8 * (l16 & 3);
+  }
+  auto k_at = [&](const uint8_t* RK, int ks) -> u32x4_t {
+    if constexpr (KV8) {
+      if (ks < 14) {
+        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(RK + kofs8 + 32 * ks);
+        return u32x4_t{v[0], v[1], 0u, 0u};
+      }
+      return *reinterpret_cast<const u32x4_t*>(RK + kofs8r + 64 * (ks - 14));
+    } else {
+      return *reinterpret_cast<const u32x4_t*>(RK + kofs[ks & 3] + (ks >> 2) * 256);
+    }
+  };
+  auto kop = [&](const u32x4_t& k, int ks) -> bf16x8_t {
+    if (KV8 && ks < 14)
+      return as_bf16x8(u32x4_t{fp8x2_to_bf16x2(k[0], false), fp8x2_to_bf16x2(k[0], true),
+                               fp8x2_to_bf16x2(k[1], false), fp8x2_to_bf16x2(k[1], true)});
+    return as_bf16x8(k);
+  };
   auto k_reads = [&](const uint8_t* RK, u32x4_t* kr) {
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) kr[ks] = *reinterpret_cast<const u32x4_t*>(RK + kofs[ks & 3] + (ks >> 2) * 256);
+    for (int ks = 0; ks < 16; ++ks) kr[ks] = k_at(RK, ks);
   };
   auto qk = [&](const u32x4_t* kr, f32x4_t* s) {
 #pragma unroll
@@ -780,7 +826,7 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
 #pragma unroll
-      for (int hq = 0; hq < 2; ++hq) s[hq] = mfma16(as_bf16x8(kr[ks]), qb[hq][ks], s[hq]);
+      for (int hq = 0; hq < 2; ++hq) s[hq] = mfma16(kop(kr[ks], ks), qb[hq][ks], s[hq]);
       __builtin_amdgcn_sched_barrier(0x7F6);
     }
   };
@@ -894,22 +940,33 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   for (int t = 0; t < ntiles; ++t) {
     const bool iss = t + NBUF - 1 < ntiles, nxt = t + 1 < ntiles;
     if (iss) issue(t + NBUF - 1);  // the slot of tile t-1, free since the last barrier
-    const uint8_t* R = ring + (t & (NBUF - 1)) * TILEB;
-    const uint8_t* RN = ring + ((t + 1) & (NBUF - 1)) * TILEB;
+    const uint8_t* R = ring + (t & (NBUF - 1)) * TB;
+    const uint8_t* RN = ring + ((t + 1) & (NBUF - 1)) * TB;
 
     // ---- S of tile t+1 and the transposed V reads of tile t, in a fixed
     // order: each k-step issues the K read four steps ahead and two V reads,
     // then its two products (the heads' chains alternate). The reads stay
     // spread over the products instead of queueing in one burst. On the last
     // tile the products read a stale slot and their result is dropped.
-    auto k_read = [&](int ks) {
-      return *reinterpret_cast<const u32x4_t*>(RN + kofs[ks & 3] + (ks >> 2) * 256);
-    };
-    s16x4_t vr[8][2][2];  // [nt][ks][first/second four rows]
+    auto k_read = [&](int ks) { return k_at(RN, ks); };
+    s16x4_t vr[KV8 ? 2 : 8][2][2];  // [nt][ks][first/second four rows] (KV8: the RoPE N-tiles 6, 7)
+    i32x2_t v8[8][2];                // KV8: [nt][ks] E4M3 V^T of eight rows
     auto v_read = [&](int i) {  // i = 4 nt + 2 ks + rd
       const int nt = i >> 2, ks = (i >> 1) & 1, rd = i & 1;
-      vr[nt][ks][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (s16x4_t __attribute__((address_space(3)))*)(R + pofs[ks][rd][nt & 3] + (nt >> 2) * 256));
+      if constexpr (KV8) {
+        // N-tiles 6, 7 read both forms (dh = 0: E4M3 dims 192-255; dh = 1:
+        // RoPE dims 448-511); the product takes the wave's own, so the
+        // schedule has no branch
+        if (rd == 0)
+          v8[nt][ks] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (i32x2_t __attribute__((address_space(3)))*)(R + vofs8[ks] + 32 * nt));
+        if (nt >= 6)
+          vr[nt - 6][ks][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (s16x4_t __attribute__((address_space(3)))*)(R + rofs8[ks][rd] + 64 * (nt - 6)));
+      } else {
+        vr[nt][ks][rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (s16x4_t __attribute__((address_space(3)))*)(R + pofs[ks][rd][nt & 3] + (nt >> 2) * 256));
+      }
     };
     u32x4_t kr[16];
 #pragma unroll
@@ -921,7 +978,7 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
       v_read(2 * ks);
       v_read(2 * ks + 1);
 #pragma unroll
-      for (int hq = 0; hq < 2; ++hq) s[hq] = mfma16(as_bf16x8(kr[ks]), qb[hq][ks], s[hq]);
+      for (int hq = 0; hq < 2; ++hq) s[hq] = mfma16(kop(kr[ks], ks), qb[hq][ks], s[hq]);
       __builtin_amdgcn_sched_barrier(0x006);  // only VALU / SALU work moves across
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -932,8 +989,20 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t bv = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(vr[nt][ks][0], vr[nt][ks][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        bf16x8_t bv;
+        if constexpr (KV8) {
+          const i32x2_t c = v8[nt][ks];
+          bv = as_bf16x8(u32x4_t{fp8x2_to_bf16x2((uint32_t)c[0], false), fp8x2_to_bf16x2((uint32_t)c[0], true),
+                                 fp8x2_to_bf16x2((uint32_t)c[1], false), fp8x2_to_bf16x2((uint32_t)c[1], true)});
+          if (nt >= 6) {
+            const bf16x8_t br = __builtin_bit_cast(
+                bf16x8_t, __builtin_shufflevector(vr[nt - 6][ks][0], vr[nt - 6][ks][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            bv = dh ? br : bv;
+          }
+        } else {
+          bv = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(vr[nt][ks][0], vr[nt][ks][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
         o[nt] = mfma32x16(bv, as_bf16x8(pcur[ks]), o[nt]);
       }
     // (on the last tile this works on the stale S: its P^T and flag are never
@@ -1405,10 +1474,10 @@ static hipError_t launch_bf16(const AttnLaunch& a, hipStream_t st) {
   return launch_combine(a, st);
 }
 
-template <int SRC>
+template <int SRC, bool KV8 = false>
 static hipError_t launch_pre32(const AttnLaunch& a, hipStream_t st) {
   if (a.nsplit != 1 || (SRC == SRC_SPARSE_PRE && a.slots > prs::TAB_MAX)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_prs_kernel<SRC>), dim3((unsigned)a.nq), dim3(prs::NT), 0, st,
+  hipLaunchKernelGGL((attn_prs_kernel<SRC, KV8>), dim3((unsigned)a.nq), dim3(prs::NT), 0, st,
                      reinterpret_cast<const uint16_t*>(a.q), row_src(a), a.q_pos, a.m_rate, a.sink,
                      a.scale * LOG2E_F, a.H, a.slots, a.out, a.lse, a.out_dt);
   return hipGetLastError();
@@ -1439,8 +1508,12 @@ static hipError_t dispatch_src(const AttnLaunch& a, hipStream_t st) {
     }
   }
   if (a.kv_dt == DT_KV_FP8 && a.D == 512 && a.H > 48 && a.H <= 64) {
-    if constexpr (SRC == SRC_SPARSE_DEC || SRC == SRC_HCA_DEC) return launch_bf16<SRC, true>(a, st);
-    return hipErrorInvalidValue;
+    if constexpr (SRC == SRC_SPARSE_DEC || SRC == SRC_HCA_DEC) {
+      return launch_bf16<SRC, true>(a, st);
+    } else {
+      if (a.nsplit != 1) return hipErrorInvalidValue;
+      return launch_pre32<SRC, true>(a, st);
+    }
   }
   if (a.kv_dt == DT_F32 && a.D == 64 && a.H <= 16) return launch_f32<64, 1, SRC>(a, st);
   return hipErrorInvalidValue;

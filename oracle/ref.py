@@ -222,12 +222,12 @@ def attend(q, rows, sink, tau: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
 
 def window_rows(kv_tok, p: int, W: int) -> np.ndarray:
     """Raw rows of tokens max(0, p-W+1) .. p (reading R8)."""
-    return np.asarray(kv_tok, F64)[max(0, p - W + 1):p + 1]
+    return np.asarray(kv_tok[max(0, p - W + 1):p + 1], F64)
 
 
 def sparse_rows(kv_comp, idx) -> np.ndarray:
     idx = np.asarray(idx)
-    return np.asarray(kv_comp, F64)[idx[idx >= 0]]
+    return np.asarray(np.asarray(kv_comp)[idx[idx >= 0]], F64)
 
 
 # ----------------------------------------------------------------------------

@@ -209,7 +209,8 @@ C6 = Cfg("c6_hca_prefill_64k", 6, "hca_prefill", B=1, n=65536, m=128, H=64, D=51
 # rest FP8), same seeds and shapes
 C4F = dataclasses.replace(C4, name="c4f_hca_decode_1m_kv_fp8", kv_dtype="fp8")
 C2F = dataclasses.replace(C2, name="c2f_csa_decode_flash_128k_kv_fp8", kv_dtype="fp8")
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6, C4F, C2F)}
+C3F = dataclasses.replace(C3, name="c3f_csa_prefill_64k_kv_fp8", kv_dtype="fp8")
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6, C4F, C2F, C3F)}
 
 
 def scaled(cfg: Cfg, **kw) -> Cfg:
@@ -308,7 +309,8 @@ def gen_prefill_tokens(cfg: Cfg) -> Dict[str, np.ndarray]:
     out = {}
     for nm in (("Ca", "Za") if hca else ("Ca", "Cb", "Za", "Zb")):
         out[nm] = _store(_normal(rng(s, nm), (n, D)), cfg.dtype)
-    out["kv_tok"] = _store(_normal(rng(s, "kv_tok"), (n, D)), cfg.dtype)
+    kv_tok = _normal(rng(s, "kv_tok"), (n, D))
+    out["kv_tok"] = kv_fp8_rows(kv_tok) if cfg.kv_dtype == "fp8" else _store(kv_tok, cfg.dtype)
     if not hca:
         out["k_idx"] = _store(_normal(rng(s, "k_idx"), (cfg.N, cfg.D_I)), cfg.dtype)
     out.update(gen_shared(cfg))

@@ -125,13 +125,12 @@ def test_attention_validation():
     # f32 rows stage at most 1024 top-k slots; bf16 rows take any top_k with top_k + W <= 2048
     assert p(P, P, P, P, P, P, 1.0, 4, 16, 64, 2000, 4000, 1025, 8, 0, 0, P, None, None, 0, None) == L.UNSUPPORTED
     assert "top_k <= 1024" in _err()
-    # mixed-precision KV rows: decode only; the prefill entry points refuse them
-    assert p(P, P, P, P, P, P, 1.0, 4, 64, 512, 100, 400, 16, 8, L.KV_FP8, 1, P, None, None, 0, None) == \
+    # mixed-precision KV rows: D = 512 with 49..64 heads only
+    assert p(P, P, P, P, P, P, 1.0, 4, 16, 64, 100, 400, 16, 8, L.KV_FP8, 1, P, None, None, 0, None) == \
         L.UNSUPPORTED
-    assert "BF16 or F32 rows" in _err()
     assert f(P, P, P, P, P, P, 1.0, 2, 64, 256, 100, 16, 8, L.KV_FP8, 1, P, None, P, 1 << 30, None) == L.UNSUPPORTED
     hp = L.lib.hca_prefill
-    assert hp(P, P, P, P, P, 1.0, 4, 64, 512, 512, 128, 65536, 128, L.KV_FP8, 1, P, None, None, 0, None) == \
+    assert hp(P, P, P, P, P, 1.0, 4, 32, 512, 512, 128, 65536, 128, L.KV_FP8, 1, P, None, None, 0, None) == \
         L.UNSUPPORTED
     # q_pos null; m = 0; unsupported heads; N + W beyond 2^24; bad scale
     assert hp(P, P, P, None, P, 1.0, 4, 64, 512, 512, 128, 65536, 128, 1, 1, P, None, None, 0, None) == L.INVALID_ARG

@@ -516,6 +516,63 @@ def test_hca_prefill(H, m, N, T_tok, with_sink):
         assert np.abs(LS[t] - rlse).max() < 1e-3
 
 
+@pytest.mark.parametrize("H,k,N,with_sink", [(64, 64, 300, True), (49, 1920, 3000, False)])
+def test_sparse_prefill_kv_fp8(H, k, N, with_sink):
+    """Prefill on mixed-precision rows (E4M3 + bf16 RoPE dims): padded
+    selections, window-only queries, the largest row table, part-empty head
+    groups."""
+    _say(f"sparse_prefill kv_fp8 H={H} k={k}")
+    g = _g(80 + H)
+    Tq, D, T_tok, W = 50, 512, 1200, 128
+    q = gen.bf16_round(g.standard_normal((Tq, H, D)).astype(np.float32) / math.sqrt(D))
+    kv_d, kv_v = _kv8(g.standard_normal((N, D)).astype(np.float32))
+    tok_d, tok_v = _kv8(g.standard_normal((T_tok, D)).astype(np.float32))
+    pos = np.sort(g.integers(0, T_tok, Tq)).astype(np.int32)
+    pos[0] = 0
+    idx = np.sort(g.choice(N, size=(Tq, k)), axis=1).astype(np.int32)
+    idx[3, 20:] = -1
+    idx[7, :] = -1
+    sink = g.standard_normal(H).astype(np.float32) if with_sink else None
+    out = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((Tq, H), device=DEV)
+    L.sparse_mqa_prefill(bf(q), kv_d, dev(idx), tok_d, dev(pos), dev(sink) if with_sink else None, out, lse, W=W)
+    torch.cuda.synchronize()
+    O, LS = host(out), host(lse)
+    for t in range(Tq):
+        ids = idx[t][idx[t] >= 0]
+        rows = np.concatenate([kv_v[ids], oracle.window_rows(tok_v, int(pos[t]), W)])
+        ref, rlse = oracle.attend(q[t], rows, sink if with_sink else np.full(H, -np.inf))
+        check_out(O[t], ref, _attn_tight(ref), f"prefill kv_fp8 t={t}")
+        assert np.abs(LS[t] - rlse).max() < 1e-3
+
+
+@pytest.mark.parametrize("H,m,N,T_tok", [(64, 128, 40, 5300), (57, 4, 3000, 12100)])
+def test_hca_prefill_kv_fp8(H, m, N, T_tok):
+    """HCA prefill on mixed-precision rows: no entry yet, V capped by N,
+    windows past the last token, rows beyond 2048."""
+    _say(f"hca_prefill kv_fp8 H={H} m={m}")
+    g = _g(90 + H)
+    Tq, D, W = 44, 512, 128
+    q = gen.bf16_round(g.standard_normal((Tq, H, D)).astype(np.float32) / math.sqrt(D))
+    kv_d, kv_v = _kv8(g.standard_normal((N, D)).astype(np.float32))
+    tok_d, tok_v = _kv8(g.standard_normal((T_tok, D)).astype(np.float32))
+    pos = np.sort(g.integers(0, T_tok, Tq)).astype(np.int32)
+    pos[:3] = [0, m - 1, m]
+    pos[-1] = T_tok + 60
+    pos = np.sort(pos)
+    sink = g.standard_normal(H).astype(np.float32)
+    out = torch.empty((Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((Tq, H), device=DEV)
+    L.hca_prefill(bf(q), kv_d, tok_d, dev(pos), dev(sink), out, lse, m=m, W=W)
+    torch.cuda.synchronize()
+    O, LS = host(out), host(lse)
+    for t in range(Tq):
+        p = int(pos[t])
+        ref, rlse = oracle.hca_query(q[t], kv_v, p, N, m, oracle.window_rows(tok_v, p, W), sink)
+        check_out(O[t], ref, _attn_tight(ref), f"hca prefill kv_fp8 t={t} p={p}")
+        assert np.abs(LS[t] - rlse).max() < 1e-3
+
+
 def test_hca_prefill_tiny_f32():
     """The fp32 small-head path (C1 shapes) through the same entry point."""
     _say("hca_prefill f32")

@@ -198,8 +198,8 @@ def run_prefill_chunk(cfg, tok, comp_t, chunk):
     L.indexer_topk(scores, q_pos, n_comp, idx, m=m)
     out = torch.empty((T, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((T, cfg.H), device=DEV)
-    L.sparse_mqa_prefill(_bf(qs["q"]), comp_t[0], idx[0], _bf(tok["kv_tok"]), q_pos[0], _t(tok["sink"]), out, lse,
-                         W=cfg.W)
+    L.sparse_mqa_prefill(_bf(qs["q"]), comp_t[0], idx[0], _kv(cfg, tok["kv_tok"]), q_pos[0], _t(tok["sink"]), out,
+                         lse, W=cfg.W)
     torch.cuda.synchronize()
     return qs, host(scores)[0], host(idx)[0], host(out), host(lse)
 
@@ -207,23 +207,28 @@ def run_prefill_chunk(cfg, tok, comp_t, chunk):
 def check_prefill(cfg, chunks, picks):
     L = _L()
     tok = gen.gen_prefill_tokens(cfg)
-    comp_t = torch.empty((1, cfg.N, cfg.D), dtype=torch.bfloat16, device=DEV)
+    fp8 = cfg.kv_dtype == "fp8"
+    comp_t = (torch.empty((1, cfg.N, cfg.D + 64), dtype=torch.uint8, device=DEV) if fp8
+              else torch.empty((1, cfg.N, cfg.D), dtype=torch.bfloat16, device=DEV))
     L.csa_compress(*(_bf(tok[nm][None]) for nm in ("Ca", "Cb", "Za", "Zb")), _t(tok["Ba"]), _t(tok["Bb"]), comp_t,
                    m=cfg.m)
     torch.cuda.synchronize()
-    comp = host(comp_t)[0]
+    comp_rows = host(comp_t)[0]
+    comp = _kv_values(cfg, comp_rows)  # the stored entries' values
+    kv_tok = _kv_values(cfg, tok["kv_tok"])
     ref_comp_rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(cfg.N // 2 - 32, cfg.N // 2 + 32),
                                               np.arange(cfg.N - 64, cfg.N)]))
     ref_comp = oracle.compress(tok["Ca"], tok["Cb"], tok["Za"], tok["Zb"], tok["Ba"], tok["Bb"], cfg.m,
                                blocks=[int(r) for r in ref_comp_rows])
-    check_out(comp[ref_comp_rows], ref_comp, 2.0 ** -8 * max(1.0, np.abs(ref_comp).max()), "prefill compress")
+    for r, ent in zip(ref_comp_rows, ref_comp):
+        _check_entry(cfg, comp_rows[r], ent, f"prefill compress row {r}")
     for c in chunks:
         qs, S, I, O, LSE = run_prefill_chunk(cfg, tok, comp_t, c)
         T = len(qs["q_pos"])
         for t in picks(T):
             p = int(qs["q_pos"][t])
             print(f"[case] {cfg.name} chunk {c} query {t} pos {p}", flush=True)
-            win = oracle.window_rows(tok["kv_tok"], p, cfg.W)
+            win = oracle.window_rows(kv_tok, p, cfg.W)
             V = oracle.visible(p, cfg.N, cfg.m)
             s = oracle.indexer_scores(qs["q_idx"][t], qs["w"][t], tok["k_idx"], V)
             assert np.abs(S[t, :V] - s).max(initial=0.0) <= 2e-5 * 8 * (1 + np.abs(s).max(initial=0.0))
@@ -240,6 +245,18 @@ def test_csa_prefill_reduced_two_chunks():
     rng = np.random.default_rng(7)
     check_prefill(cfg, [0, 1], lambda T: sorted(set([0, 1, 2, 3, 4, 63, 64, 2047, T - 2, T - 1]
                                                      + list(rng.integers(0, T, 20)))))
+
+
+def test_csa_prefill_kv_fp8_reduced_two_chunks():
+    cfg = gen.scaled(gen.C3F, n=8192, Tq=8192)
+    rng = np.random.default_rng(11)
+    check_prefill(cfg, [0, 1], lambda T: sorted(set([0, 1, 2, 3, 4, 2047, T - 1] + list(rng.integers(0, T, 16)))))
+
+
+def test_csa_prefill_64k_kv_fp8_last_chunk_sampled():
+    cfg = gen.C3F  # mixed-precision main KV, as bench.py runs it
+    rng = np.random.default_rng(12)
+    check_prefill(cfg, [gen.num_chunks(cfg) - 1], lambda T: sorted(set([0, T - 1] + list(rng.integers(0, T, 6)))))
 
 
 def test_csa_prefill_64k_last_chunk_sampled():

@@ -15,9 +15,11 @@ data from the previous one.
 
 Other workloads: c5 (1M context, E4M3 indexer keys), c2x (c2 with MXFP4
 indexer keys), c4 (HCA decode 1M), c3 (CSA prefill 64K), c6 (HCA prefill 64K),
-c4f / c2f / c3f (c4 / c2 / c3 with the main KV rows in E4M3 + bf16 RoPE dims).
+c4f / c2f / c3f (c4 / c2 / c3 with the main KV rows in E4M3 + bf16 RoPE dims),
+c2r (c2 with the query RMSNorm + RoPE prologue and the output inverse RoPE).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c5|c4|c3|c2x|c6|c4f|c2f|c3f]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload c2|c5|c4|c3|c2x|c6|c4f|c2f|c3f|c2r]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -45,7 +47,8 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c5", "c4", "c3", "c2x", "c6", "c4f", "c2f", "c3f"])
+    ap.add_argument("--workload", default="c2",
+                    choices=["c2", "c5", "c4", "c3", "c2x", "c6", "c4f", "c2f", "c3f", "c2r"])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -110,7 +113,8 @@ def main():
         return bench_prefill(a, torch, L, gen, dev, gen.C3F if a.workload == "c3f" else gen.C3)
     if a.workload == "c6":
         return bench_hca_prefill(a, torch, L, gen, dev)
-    cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X, "c4f": gen.C4F, "c2f": gen.C2F}[a.workload]
+    cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X, "c4f": gen.C4F, "c2f": gen.C2F,
+           "c2r": gen.C2R}[a.workload]
     t0 = time.time()
     x = gen.gen_decode(cfg, with_compress=True)
     print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -144,8 +148,13 @@ def main():
     shared = {"sink": td(x["sink"]), "Ba": td(x["Ba"]), "Bb": td(x["Bb"]),
               "q_pos": td(np.full((B, 1), cfg.n - 1, np.int32)), "n_comp": td(np.full((B,), N, np.int32)),
               "win_len": td(np.full((B,), min(W, cfg.n), np.int32))}
+    if cfg.qk_rope:
+        shared["q_gamma"] = td(x["q_gamma"])
+        shared["pos"] = td(np.full((B,), cfg.n - 1, np.int32))
+    att_scale = 1.0 / math.sqrt(D) if cfg.qk_rope else 1.0
     reps = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(a.replicas - 1)]
     out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    qn = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
     if cfg.kind == "csa_decode":
         k = cfg.top_k
         scores = torch.empty((B, 1, N), dtype=torch.float32, device=dev)
@@ -163,6 +172,10 @@ def main():
 
     def step(r, ev=None):
         rec(ev, 0)
+        q_att = r["q"]
+        if cfg.qk_rope:  # prologue: RMSNorm + RoPE of the raw queries at their position
+            L.qk_norm_rope(r["q"], qn, shared["pos"], shared["q_gamma"], norm=True, rope=True, stream=s)
+            q_att = qn
         if cfg.kind == "csa_decode":
             L.csa_compress(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"], r["kv_comp"], m=m,
                            tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, stream=s)
@@ -172,8 +185,10 @@ def main():
             rec(ev, 2)
             L.indexer_topk(scores, shared["q_pos"], shared["n_comp"], idx, m=m, ws=ws_t, stream=s)
             rec(ev, 3)
-            L.sparse_mqa_decode(r["q"], r["kv_comp"], idx.view(B, k), r["kv_win"], shared["win_len"], shared["sink"],
-                                out, scale=1.0, ws=ws_a, stream=s)
+            L.sparse_mqa_decode(q_att, r["kv_comp"], idx.view(B, k), r["kv_win"], shared["win_len"], shared["sink"],
+                                out, scale=att_scale, ws=ws_a, stream=s)
+            if cfg.qk_rope:  # epilogue: the output's rotated dims turned back
+                L.qk_norm_rope(out, out, shared["pos"], inverse=True, stream=s)
         else:
             # HCA: the token completes block N-1 (m' divides n): one branch, no overlap
             L.csa_compress(r["Ca"], None, r["Za"], None, shared["Ba"], None, r["kv_comp"], m=m,
@@ -244,7 +259,7 @@ def main():
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
                          "m": m, "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I,
                          "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype,
-                         "kv_dtype": cfg.kv_dtype}
+                         "kv_dtype": cfg.kv_dtype, "qk_norm_rope": cfg.qk_rope}
         kname = {"fp8": "idx_scan_lp_kernel<2> (E4M3 keys)", "mxfp4": "idx_scan_lp_kernel<3> (MXFP4 keys)"}.get(cfg.k_dtype, "idx_scan_bf16_kernel")
         res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": round(scan_bytes / (scan_avg * 1e-3) / 1e9, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -544,8 +559,14 @@ def cpu_baseline(cfg, x, budget_s: float):
                 keys, sc = oracle.mxfp4_decode(x["k_idx_codes"][b], x["k_scale"][b]), None
             else:
                 keys, sc = x["k_idx"][b], None
-            oracle.csa_query(x["q"][b], x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, cfg.N, m, cfg.top_k,
-                             kvd(x["kv_win"][b]), x["sink"], k_scale=sc)
+            q, tau = x["q"][b], 1.0
+            if cfg.qk_rope:
+                q = oracle.rope_rotate(oracle.rms_norm(q[None], x["q_gamma"], 1e-6), [cfg.n - 1])[0]
+                tau = 1.0 / math.sqrt(cfg.D)
+            _, o, _, _ = oracle.csa_query(q, x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, cfg.N, m, cfg.top_k,
+                                          kvd(x["kv_win"][b]), x["sink"], k_scale=sc, tau=tau)
+            if cfg.qk_rope:
+                oracle.rope_rotate(o[None], [cfg.n - 1], inverse=True)
         else:
             ent = oracle.compress(x["Ca"][b], None, x["Za"][b], None, x["Ba"], None, m, overlap=False)[0]
             comp = kvd(x["kv_comp"][b])

@@ -81,6 +81,9 @@ enum {
 /* csa_compress flags */
 enum { CSA_OVERLAP = 1, CSA_JOINT_SOFTMAX = 2 };
 
+/* qk_norm_rope flags */
+enum { CSA_RMSNORM = 1, CSA_ROPE = 2, CSA_ROPE_INVERSE = 4 };
+
 int csa_hca_version(void);
 const char* csa_last_error(void);
 
@@ -238,6 +241,28 @@ int hca_prefill(const void* q, const void* kv_comp, const void* kv_tok, const in
                 float scale, int64_t Tq, int H, int D, int64_t N, int m, int64_t T_tok, int W, int kv_dt,
                 int out_dt, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 size_t hca_prefill_workspace_bytes(int64_t Tq, int H, int D, int64_t N, int W);
+
+/*
+ * qk_norm_rope — the attention's prologue and epilogue: QK RMSNorm and
+ * partial rotary position encoding ([CSDN] 其他辅助设计: RMSNorm on queries
+ * and keys before the core attention, rotation of the last 64 dims only),
+ * and the inverse rotation of the output ([LIDUOS] 1M Context 的结构与取舍:
+ * rows are both key and value, so the output is rotated back).
+ *
+ * For every row x[t, h, :] (D values), in this order:
+ *   CSA_RMSNORM      : x <- x / sqrt(mean(x^2) + eps) * gamma  (gamma [D] fp32,
+ *                      NULL = all ones);
+ *   CSA_ROPE         : with s = D - rope_dims, the pair (x[s+2i], x[s+2i+1])
+ *                      is rotated by the angle pos[t] * rope_theta^(-2i/rope_dims);
+ *   CSA_ROPE_INVERSE : the same pairs rotated by minus that angle.
+ *   x, out : [T, H, D] in dt (F32 or BF16), 16-byte aligned; out may be x.
+ *   pos    : [T] int32 (needed with a rotation).
+ * Arithmetic is fp32; angles are formed and reduced in double precision.
+ * Supported: D % 8 == 0, D <= 512; rope_dims even in [2, D]. CSA_ROPE and
+ * CSA_ROPE_INVERSE together are CSA_INVALID_ARG.
+ */
+int qk_norm_rope(const void* x, void* out, const float* gamma, const int32_t* pos, int64_t T, int H, int D,
+                 int rope_dims, float eps, float rope_theta, int flags, int dt, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa_hca.so")
 F32, BF16, FP8_E4M3, MXFP4, KV_FP8 = 0, 1, 2, 3, 4
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = 0, -1, -2, -3, -4
 OVERLAP, JOINT_SOFTMAX = 1, 2
+RMSNORM, ROPE, ROPE_INVERSE = 1, 2, 4
 
 
 class CsaError(RuntimeError):
@@ -60,6 +61,7 @@ _SIGS = {
     "hca_prefill": ([_vp] * 5 + [_f32, _i64, _i32, _i32, _i64, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
                                  _vp], _i32),
     "hca_prefill_workspace_bytes": ([_i64, _i32, _i32, _i64, _i32], _sz),
+    "qk_norm_rope": ([_vp] * 4 + [_i64, _i32, _i32, _i32, _f32, _f32, _i32, _i32, _vp], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -236,6 +238,15 @@ def hca_prefill(q, kv_comp, kv_tok, q_pos, sink, out, lse=None, *, m: int, W: in
     _check(lib.hca_prefill(_ptr(q), _ptr(kv_comp), _ptr(kv_tok), _ptr(q_pos), _ptr(sink), scale, Tq, H, D, N, m,
                            T_tok, W, _kv_dt(q, kv_comp), _dt(out), _ptr(out), _ptr(lse), _ptr(ws), nb,
                            _stream(stream)))
+
+
+def qk_norm_rope(x, out, pos=None, gamma=None, *, norm: bool = False, rope: bool = False, inverse: bool = False,
+                 rope_dims: int = 64, eps: float = 1e-6, theta: float = 10000.0, stream=None) -> None:
+    """x, out [T, H, D] (out may be x); pos [T] int32; gamma [D] fp32 or None."""
+    T, H, D = x.shape
+    flags = (RMSNORM if norm else 0) | (ROPE if rope else 0) | (ROPE_INVERSE if inverse else 0)
+    _check(lib.qk_norm_rope(_ptr(x), _ptr(out), _ptr(gamma), _ptr(pos), T, H, D, rope_dims, eps, theta, flags,
+                            _dt(x), _stream(stream)))
 
 
 def hca_dense_mqa_workspace_bytes(B: int, H: int, D: int, N_max: int, W: int) -> int:

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libcsa_hca.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "compress.hip", "indexer.hip", "topk.hip", "attn.hip"]
+SOURCES = ["api.hip", "compress.hip", "indexer.hip", "topk.hip", "attn.hip", "rope.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -300,6 +300,26 @@ int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_i
   return hip_status(csa::run_attn(a, (hipStream_t)stream), "sparse_mqa_prefill");
 }
 
+int qk_norm_rope(const void* x, void* out, const float* gamma, const int32_t* pos, int64_t T, int H, int D,
+                 int rope_dims, float eps, float rope_theta, int flags, int dt, void* stream) {
+  REQ(x && out, CSA_INVALID_ARG, "x and out must not be NULL");
+  REQ((flags & ~(CSA_RMSNORM | CSA_ROPE | CSA_ROPE_INVERSE)) == 0, CSA_INVALID_ARG, "unknown flags");
+  REQ(!((flags & CSA_ROPE) && (flags & CSA_ROPE_INVERSE)), CSA_INVALID_ARG, "CSA_ROPE and CSA_ROPE_INVERSE together");
+  REQ(T >= 0 && H >= 1 && D >= 1, CSA_INVALID_ARG, "need T >= 0, H >= 1, D >= 1");
+  REQ(dt == CSA_F32 || dt == CSA_BF16, CSA_UNSUPPORTED, "dt must be F32 or BF16");
+  REQ(D % 8 == 0 && D <= 512, CSA_UNSUPPORTED, "D must be a multiple of 8, at most 512");
+  const bool rope = flags & (CSA_ROPE | CSA_ROPE_INVERSE);
+  REQ(!rope || pos, CSA_INVALID_ARG, "pos must not be NULL with a rotation");
+  REQ(!rope || (rope_dims >= 2 && rope_dims <= D && rope_dims % 2 == 0), CSA_INVALID_ARG,
+      "rope_dims must be even and in [2, D]");
+  REQ(!rope || (rope_theta > 0.0f && rope_theta <= 3.0e38f), CSA_INVALID_ARG, "rope_theta must be positive and finite");
+  REQ(!(flags & CSA_RMSNORM) || (eps >= 0.0f && eps <= 3.0e38f), CSA_INVALID_ARG, "eps must be >= 0 and finite");
+  REQ(aligned16(x) && aligned16(out), CSA_INVALID_ARG, "x and out must be 16-byte aligned");
+  REQ(T * (int64_t)H <= ((int64_t)1 << 33), CSA_UNSUPPORTED, "too many rows");
+  csa::NormRopeLaunch a{x, out, gamma, pos, T, H, D, rope ? rope_dims : 2, eps, rope_theta, flags, dt};
+  return hip_status(csa::run_norm_rope(a, (hipStream_t)stream), "qk_norm_rope");
+}
+
 size_t hca_prefill_workspace_bytes(int64_t, int, int, int64_t, int) { return 0; }
 
 int hca_prefill(const void* q, const void* kv_comp, const void* kv_tok, const int32_t* q_pos, const float* sink,

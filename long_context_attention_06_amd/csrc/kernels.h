@@ -69,4 +69,17 @@ struct AttnLaunch {
 };
 hipError_t run_attn(const AttnLaunch& a, hipStream_t st);
 
+enum { NR_NORM = 1, NR_ROPE = 2, NR_ROPE_INV = 4 };
+struct NormRopeLaunch {
+  const void* x;
+  void* out;
+  const float* gamma;
+  const int32_t* pos;
+  int64_t T;
+  int H, D, R;
+  float eps, theta;
+  int flags, dt;
+};
+hipError_t run_norm_rope(const NormRopeLaunch& a, hipStream_t st);
+
 }  // namespace csa

@@ -64,6 +64,35 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 15) & ((c & 7) == 7), np.nan, v)
 
 
+def rms_norm(x, gamma=None, eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm over the last axis ([CSDN] 其他辅助设计: QK normalisation
+    before the core attention): x / sqrt(mean(x^2) + eps) * gamma."""
+    x = np.asarray(x, F64)
+    y = x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    return y if gamma is None else y * np.asarray(gamma, F64)
+
+
+def rope_rotate(x, pos, rope_dims: int = 64, theta: float = 10000.0, inverse: bool = False) -> np.ndarray:
+    """Partial rotary position encoding ([CSDN] 其他辅助设计: only the last
+    64 dims are rotated; [LIDUOS] 1M Context 的结构与取舍: the output side takes the inverse
+    rotation). With R = rope_dims and s = D - R, the pair (x[s+2i], x[s+2i+1])
+    is rotated by the angle p * theta^(-2i/R) (by minus that angle with
+    inverse); the other dims pass through. x: [T, ..., D]; pos: [T]."""
+    x = np.array(x, F64)
+    D = x.shape[-1]
+    s = D - rope_dims
+    i = np.arange(rope_dims // 2, dtype=F64)
+    inv_freq = np.power(F64(theta), -2.0 * i / rope_dims)
+    ang = np.asarray(pos, F64).reshape((-1,) + (1,) * (x.ndim - 1)) * inv_freq  # [T, 1.., R/2]
+    if inverse:
+        ang = -ang
+    c, sn = np.cos(ang), np.sin(ang)
+    a, b = x[..., s::2].copy(), x[..., s + 1::2].copy()
+    x[..., s::2] = a * c - b * sn
+    x[..., s + 1::2] = a * sn + b * c
+    return x
+
+
 def kv_fp8_decode(rows: np.ndarray, D: int) -> np.ndarray:
     """Mixed-precision main-KV row -> values (the pages keep the RoPE dims in
     BF16 and the rest in FP8): bytes 0 .. D-65 are OCP E4M3 codes of dims

@@ -28,7 +28,7 @@ import numpy as np
 TID = {
     "Ca": 1, "Cb": 2, "Za": 3, "Zb": 4, "Ba": 5, "Bb": 6,
     "k_idx": 7, "q_idx": 8, "w": 9, "q": 10, "kv_comp": 11, "kv_win": 12,
-    "kv_tok": 13, "sink": 14,
+    "kv_tok": 13, "sink": 14, "q_gamma": 15,
 }
 
 QCHUNK = 4096  # prefill query chunk (queries per chunk)
@@ -181,6 +181,7 @@ class Cfg:
     dtype: str = "bf16"  # storage dtype of activations / caches
     k_dtype: str = "bf16"  # indexer key storage
     kv_dtype: str = "bf16"  # main KV rows: "bf16", or "fp8" (E4M3 + bf16 RoPE dims)
+    qk_rope: bool = False   # decode step with the query prologue (RMSNorm, RoPE) and output inverse RoPE
     Tq: int = 1          # queries per sequence
 
     @property
@@ -210,7 +211,11 @@ C6 = Cfg("c6_hca_prefill_64k", 6, "hca_prefill", B=1, n=65536, m=128, H=64, D=51
 C4F = dataclasses.replace(C4, name="c4f_hca_decode_1m_kv_fp8", kv_dtype="fp8")
 C2F = dataclasses.replace(C2, name="c2f_csa_decode_flash_128k_kv_fp8", kv_dtype="fp8")
 C3F = dataclasses.replace(C3, name="c3f_csa_prefill_64k_kv_fp8", kv_dtype="fp8")
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6, C4F, C2F, C3F)}
+# C2 with the attention's prologue and epilogue: raw queries are RMS-normalised
+# (gamma ~ U(0.5, 1.5)) and rotated at their position, the output is rotated
+# back; the logit scale is then 1/sqrt(D)
+C2R = dataclasses.replace(C2, name="c2r_csa_decode_flash_128k_qk_rope", qk_rope=True)
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6, C4F, C2F, C3F, C2R)}
 
 
 def scaled(cfg: Cfg, **kw) -> Cfg:
@@ -287,6 +292,8 @@ def gen_shared(cfg: Cfg) -> Dict[str, np.ndarray]:
         out["sink"] = _normal(rng(s, "sink"), (cfg.H,))
         out["Ba"] = _normal(rng(s, "Ba"), (cfg.m, cfg.D))
         out["Bb"] = _normal(rng(s, "Bb"), (cfg.m, cfg.D))
+    if cfg.qk_rope:
+        out["q_gamma"] = rng(s, "q_gamma").uniform(0.5, 1.5, size=cfg.D).astype(np.float32)
     return out
 
 

@@ -23,12 +23,27 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
     missing = [n for n in names if n not in exported]
     assert not missing, missing
     assert set(names) == set(L.EXPORTS)
+
+
+def test_norm_rope_validation():
+    f = L.lib.qk_norm_rope
+    # args: x, out, gamma, pos, T, H, D, rope_dims, eps, theta, flags, dt, stream
+    assert f(None, P, None, P, 4, 8, 512, 64, 1e-6, 1e4, L.ROPE, L.BF16, None) == L.INVALID_ARG
+    assert f(P, P, None, None, 4, 8, 512, 64, 1e-6, 1e4, L.ROPE, L.BF16, None) == L.INVALID_ARG  # no pos
+    assert "pos" in _err()
+    assert f(P, P, None, P, 4, 8, 512, 64, 1e-6, 1e4, L.ROPE | L.ROPE_INVERSE, L.BF16, None) == L.INVALID_ARG
+    assert f(P, P, None, P, 4, 8, 512, 63, 1e-6, 1e4, L.ROPE, L.BF16, None) == L.INVALID_ARG  # odd rope_dims
+    assert f(P, P, None, P, 4, 8, 512, 64, 1e-6, 0.0, L.ROPE, L.BF16, None) == L.INVALID_ARG  # theta
+    assert f(P, P, None, P, 4, 8, 512, 64, -1.0, 1e4, L.RMSNORM, L.BF16, None) == L.INVALID_ARG  # eps
+    assert f(P, P, None, P, 4, 8, 1024, 64, 1e-6, 1e4, L.ROPE, L.BF16, None) == L.UNSUPPORTED  # D > 512
+    assert f(P, P, None, P, 4, 8, 512, 64, 1e-6, 1e4, L.ROPE, L.FP8_E4M3, None) == L.UNSUPPORTED
+    assert f(P, P, None, P, 4, 8, 512, 64, 1e-6, 1e4, 8, L.BF16, None) == L.INVALID_ARG  # unknown flag
 
 
 def test_version():

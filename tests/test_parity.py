@@ -595,6 +595,39 @@ def test_hca_prefill_tiny_f32():
         assert np.abs(LS[t] - rlse).max() < 1e-4
 
 
+@pytest.mark.parametrize("dt,T,H,D,R", [("bf16", 37, 64, 512, 64), ("f32", 20, 4, 64, 64), ("f32", 9, 3, 512, 16)])
+def test_qk_norm_rope(dt, T, H, D, R):
+    """RMSNorm + partial RoPE (prologue) and the inverse rotation (epilogue)
+    against the oracle, positions up to past 2^20, in place and out of place;
+    the inverse undoes the rotation."""
+    _say("qk_norm_rope", dt, T, H, D, R)
+    g = _g(100 + T)
+    x = g.standard_normal((T, H, D)).astype(np.float32) * 3.0
+    if dt == "bf16":
+        x = gen.bf16_round(x)
+    gamma = g.uniform(0.5, 1.5, D).astype(np.float32)
+    pos = g.integers(0, 1 << 21, T).astype(np.int32)
+    pos[0], pos[1] = 0, (1 << 20) + 3
+    up = bf if dt == "bf16" else dev
+    xd, out = up(x), up(np.zeros_like(x))
+    L.qk_norm_rope(xd, out, dev(pos), dev(gamma), norm=True, rope=True, rope_dims=R, eps=1e-6, theta=10000.0)
+    inv = out.clone()
+    L.qk_norm_rope(inv, inv, dev(pos), inverse=True, rope_dims=R, theta=10000.0)  # in place
+    torch.cuda.synchronize()
+    ref = oracle.rope_rotate(oracle.rms_norm(x, gamma, 1e-6), pos, rope_dims=R, theta=10000.0)
+    # rows are unit-RMS after the norm: the fp32 rotation errs by about 1e-7
+    # of the row scale even where a rotated value cancels, and bf16 storage
+    # adds half an ulp of the value
+    rel = 2.0 ** -8 if dt == "bf16" else 2e-6
+    got = host(out)
+    assert np.all(np.abs(got - ref) <= rel * (np.abs(ref) + 1.0)), f"max {np.abs(got - ref).max():.3e}"
+    # the inverse of the stored (rounded) rotation, against the oracle's inverse of the same values
+    back = oracle.rope_rotate(got, pos, rope_dims=R, theta=10000.0, inverse=True)
+    gi = host(inv)
+    assert np.all(np.abs(gi - back) <= rel * (np.abs(back) + 1.0))
+    assert np.abs(gi - oracle.rms_norm(x, gamma, 1e-6)).max() <= 4 * rel * (1 + np.abs(ref).max())
+
+
 def test_sparse_prefill_reference_moves():
     """Logits that jump far above everything earlier in a query (more than the
     2^64 headroom P has against the exponent reference the kernel carries from

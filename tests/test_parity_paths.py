@@ -73,8 +73,16 @@ def run_csa_decode(cfg, x):
     L.indexer_topk(scores, q_pos, n_comp, idx, m=m)
     out = torch.empty((B, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, cfg.H), device=DEV)
-    L.sparse_mqa_decode(_bf(x["q"]), kv, idx.view(B, k), _kv(cfg, x["kv_win"]), _t(np.full((B,), W, np.int32)),
-                        _t(x["sink"]), out, lse)
+    q, scale = _bf(x["q"]), 1.0
+    if cfg.qk_rope:  # prologue on the raw queries, at position n-1
+        pos = _t(np.full((B,), cfg.n - 1, np.int32))
+        qn = torch.empty_like(q)
+        L.qk_norm_rope(q, qn, pos, _t(x["q_gamma"]), norm=True, rope=True)
+        q, scale = qn, 1.0 / np.sqrt(cfg.D)
+    L.sparse_mqa_decode(q, kv, idx.view(B, k), _kv(cfg, x["kv_win"]), _t(np.full((B,), W, np.int32)),
+                        _t(x["sink"]), out, lse, scale=scale)
+    if cfg.qk_rope:  # epilogue: the output rotated back
+        L.qk_norm_rope(out, out, pos, inverse=True)
     torch.cuda.synchronize()
     # the cache stays on the device (GBs at full size); only its last two rows come back
     return host(kv[:, N - 2:]), host(scores)[:, 0], host(idx)[:, 0], host(out), host(lse)
@@ -99,13 +107,23 @@ def check_csa_decode(cfg, x, seqs):
             keys, sc = oracle.mxfp4_decode(x["k_idx_codes"][b], x["k_scale"][b]), None
         else:
             keys, sc = x["k_idx"][b], None
-        oidx, o_ref, lse_ref, s = oracle.csa_query(x["q"][b], x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, N,
+        q, tau = x["q"][b], 1.0
+        if cfg.qk_rope:
+            # the prologue's result, stored in bf16 as the attention reads it
+            q = gen.bf16_round(oracle.rope_rotate(oracle.rms_norm(q[None], x["q_gamma"], 1e-6), [cfg.n - 1])[0]
+                               .astype(np.float32)).astype(np.float64)
+            tau = 1.0 / np.sqrt(cfg.D)
+        oidx, o_ref, lse_ref, s = oracle.csa_query(q, x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, N,
                                                    m, cfg.top_k, _kv_values(cfg, x["kv_win"][b]), x["sink"],
-                                                   k_scale=sc)
+                                                   k_scale=sc, tau=tau)
+        if cfg.qk_rope:
+            o_ref = oracle.rope_rotate(o_ref[None], [cfg.n - 1], inverse=True)[0]
         assert np.abs(S[b] - s).max() <= 2e-5 * 8 * (1 + np.abs(s).max())
         check_topk_row(I[b], oidx, s, cfg.top_k, f"b={b}")
         rows = np.concatenate([comp[I[b][I[b] >= 0]], _kv_values(cfg, x["kv_win"][b])])
-        o_own, lse_own = oracle.attend(x["q"][b], rows, x["sink"])
+        o_own, lse_own = oracle.attend(q, rows, x["sink"], tau)
+        if cfg.qk_rope:
+            o_own = oracle.rope_rotate(o_own[None], [cfg.n - 1], inverse=True)[0]
         check_out(O[b], o_own, _tight(o_own), f"out on gpu idx b={b}")
         assert np.abs(LSE[b] - lse_own).max() < 1e-3
         if np.array_equal(I[b], oidx):
@@ -263,6 +281,16 @@ def test_csa_prefill_64k_last_chunk_sampled():
     cfg = gen.C3  # 65536 tokens; the last (largest) 4096-query chunk, as bench.py runs it
     rng = np.random.default_rng(8)
     check_prefill(cfg, [gen.num_chunks(cfg) - 1], lambda T: sorted(set([0, 1, T - 1] + list(rng.integers(0, T, 8)))))
+
+
+def test_csa_decode_flash_qk_rope_reduced():
+    cfg = gen.scaled(gen.C2R, B=4, n=16384)  # query RMSNorm + RoPE prologue, output inverse RoPE
+    check_csa_decode(cfg, gen.gen_decode(cfg), range(cfg.B))
+
+
+def test_csa_decode_flash_qk_rope_full_size_sampled():
+    cfg = gen.C2R
+    check_csa_decode(cfg, gen.gen_decode(cfg), [0, 21, 31])
 
 
 def test_csa_decode_flash_mxfp4_reduced():

@@ -49,6 +49,9 @@
  *     HIP call, so a rejected call touches neither the device nor the stream.
  *     csa_last_error() returns the calling thread's message for its last
  *     failed call. No C++ exception crosses this boundary.
+ *   - A pointer may be NULL when the call reads or writes nothing through it
+ *     (no sequence or query, no compressed entry, no window row): such calls
+ *     return CSA_OK and launch nothing.
  *   - Device-side data (indices, positions, lengths) is not validated on the
  *     host; kernels clamp it: an index outside [0, N_max) is skipped, a
  *     length is clamped to its buffer, a position to the rows that exist.

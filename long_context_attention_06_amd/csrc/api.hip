@@ -52,9 +52,11 @@ bool attn_supported(int H, int D, int kv_dt) {
          (kv_dt == CSA_F32 && D == 64 && H >= 1 && H <= 16);
 }
 
+// Pointers may be NULL where the call has nothing to read or write through
+// them (no query, no row of that source).
 int check_attn_common(const void* q, const void* out, float scale, int H, int D, int kv_dt, int out_dt, int W,
-                      int top_k) {
-  REQ(q && out, CSA_INVALID_ARG, "q and out must not be NULL");
+                      int top_k, int64_t nq) {
+  REQ(nq == 0 || (q && out), CSA_INVALID_ARG, "q and out must not be NULL");
   REQ(scale > 0.0f && scale <= 3.0e38f, CSA_INVALID_ARG, "scale must be positive and finite");
   REQ(H > 0 && D > 0, CSA_INVALID_ARG, "H and D must be positive");
   REQ(W >= 0 && top_k >= 0, CSA_INVALID_ARG, "W and top_k must be >= 0");
@@ -72,8 +74,9 @@ int check_attn_common(const void* q, const void* out, float scale, int H, int D,
 int check_indexer(const void* q_idx, const float* w, const void* k_idx, const void* k_scale, const int32_t* q_pos,
                   const int32_t* n_comp, int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int q_dt,
                   int k_dt) {
-  REQ(q_idx && w && k_idx && q_pos && n_comp, CSA_INVALID_ARG, "q_idx, w, k_idx, q_pos, n_comp must not be NULL");
   REQ(B >= 0 && Tq >= 0 && N_max >= 0, CSA_INVALID_ARG, "B, Tq, N_max must be >= 0");
+  REQ(B * Tq == 0 || (q_idx && w && q_pos && n_comp), CSA_INVALID_ARG, "q_idx, w, q_pos, n_comp must not be NULL");
+  REQ(B * Tq * N_max == 0 || k_idx, CSA_INVALID_ARG, "k_idx must not be NULL");
   REQ(H_I > 0 && D_I > 0, CSA_INVALID_ARG, "H_I and D_I must be positive");
   REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");
   REQ(q_dt >= CSA_F32 && q_dt <= CSA_FP8_E4M3 && k_dt >= CSA_F32 && k_dt <= CSA_MXFP4, CSA_INVALID_ARG,
@@ -94,7 +97,8 @@ int check_indexer(const void* q_idx, const float* w, const void* k_idx, const vo
 
 int check_topk(const float* scores, const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq,
                int64_t N_max, int m, int top_k, const int32_t* topk_idx) {
-  REQ(scores && q_pos && n_comp && topk_idx, CSA_INVALID_ARG, "scores, q_pos, n_comp, topk_idx must not be NULL");
+  REQ(B * Tq == 0 || (scores && q_pos && n_comp && topk_idx), CSA_INVALID_ARG,
+      "scores, q_pos, n_comp, topk_idx must not be NULL");
   REQ(B >= 0 && Tq >= 0 && N_max >= 0, CSA_INVALID_ARG, "B, Tq, N_max must be >= 0");
   REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");
   REQ(top_k >= 1, CSA_INVALID_ARG, "top_k must be >= 1");
@@ -118,8 +122,9 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
   REQ((flags & ~(CSA_OVERLAP | CSA_JOINT_SOFTMAX)) == 0, CSA_INVALID_ARG, "unknown flags");
   const bool overlap = flags & CSA_OVERLAP, joint = flags & CSA_JOINT_SOFTMAX;
   REQ(!joint || overlap, CSA_INVALID_ARG, "CSA_JOINT_SOFTMAX needs CSA_OVERLAP");
-  REQ(Ca && Za && Ba && out, CSA_INVALID_ARG, "Ca, Za, Ba, out must not be NULL");
-  REQ(!overlap || (Cb && Zb && Bb), CSA_INVALID_ARG, "CSA_OVERLAP needs Cb, Zb, Bb");
+  const bool empty = B == 0 || blk_end <= blk_begin;  // nothing to read or write
+  REQ(empty || (Ca && Za && Ba && out), CSA_INVALID_ARG, "Ca, Za, Ba, out must not be NULL");
+  REQ(empty || !overlap || (Cb && Zb && Bb), CSA_INVALID_ARG, "CSA_OVERLAP needs Cb, Zb, Bb");
   REQ(B >= 0 && n_rows >= 0 && tok_begin >= 0, CSA_INVALID_ARG, "B, n_rows, tok_begin must be >= 0");
   REQ(d > 0, CSA_INVALID_ARG, "d must be positive");
   REQ(m >= 1 && m <= 1024, CSA_INVALID_ARG, "m must be in [1, 1024]");
@@ -154,7 +159,7 @@ int indexer_score(const void* q_idx, const float* w, const void* k_idx, const vo
                   int k_dt, float* scores, void* stream) {
   int rc = check_indexer(q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, q_dt, k_dt);
   if (rc) return rc;
-  REQ(scores, CSA_INVALID_ARG, "scores must not be NULL");
+  REQ(B * Tq * N_max == 0 || scores, CSA_INVALID_ARG, "scores must not be NULL");
   csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, scores};
   return hip_status(csa::run_indexer(a, (hipStream_t)stream), "indexer_score");
 }
@@ -187,7 +192,7 @@ int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, con
                        void* ws, size_t ws_bytes, void* stream) {
   int rc = check_indexer(q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, q_dt, k_dt);
   if (rc) return rc;
-  REQ(topk_idx, CSA_INVALID_ARG, "topk_idx must not be NULL");
+  REQ(B * Tq == 0 || topk_idx, CSA_INVALID_ARG, "topk_idx must not be NULL");
   REQ(top_k >= 1, CSA_INVALID_ARG, "top_k must be >= 1");
   REQ(top_k <= 4096, CSA_UNSUPPORTED, "top_k above 4096");
   const size_t need = indexer_score_topk_workspace_bytes(B, Tq, N_max, top_k);
@@ -214,11 +219,11 @@ int sparse_mqa_decode(const void* q, const void* kv_comp, const int32_t* topk_id
                       const int32_t* win_len, const float* sink, float scale, int64_t B, int H, int D, int64_t N_max,
                       int top_k, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws, size_t ws_bytes,
                       void* stream) {
-  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, top_k);
+  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, top_k, B);
   if (rc) return rc;
   REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
-  REQ(top_k == 0 || (kv_comp && topk_idx), CSA_INVALID_ARG, "kv_comp and topk_idx must not be NULL");
-  REQ(W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
+  REQ(B == 0 || top_k == 0 || (kv_comp && topk_idx), CSA_INVALID_ARG, "kv_comp and topk_idx must not be NULL");
+  REQ(B == 0 || W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
   REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
   const int ns = nsplit_for((int64_t)top_k + W, SPARSE_SPLIT_ROWS);
   const size_t need = attn_ws(B, H, D, ns);
@@ -263,12 +268,12 @@ int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_i
                        size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
-  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, top_k);
+  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, top_k, Tq);
   if (rc) return rc;
   REQ(Tq >= 0 && N >= 0 && T_tok >= 0, CSA_INVALID_ARG, "Tq, N, T_tok must be >= 0");
-  REQ(q_pos, CSA_INVALID_ARG, "q_pos must not be NULL");
-  REQ(top_k == 0 || (kv_comp && topk_idx), CSA_INVALID_ARG, "kv_comp and topk_idx must not be NULL");
-  REQ(W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
+  REQ(Tq == 0 || q_pos, CSA_INVALID_ARG, "q_pos must not be NULL");
+  REQ(Tq == 0 || top_k == 0 || (kv_comp && topk_idx), CSA_INVALID_ARG, "kv_comp and topk_idx must not be NULL");
+  REQ(Tq == 0 || W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
   REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
   REQ(Tq <= 0x7fffffff, CSA_UNSUPPORTED, "Tq too large");
   REQ(kv_dt != CSA_F32 || top_k <= 1024, CSA_UNSUPPORTED, "sparse_mqa_prefill on f32 rows supports top_k <= 1024");
@@ -302,14 +307,14 @@ int sparse_mqa_prefill(const void* q, const void* kv_comp, const int32_t* topk_i
 
 int qk_norm_rope(const void* x, void* out, const float* gamma, const int32_t* pos, int64_t T, int H, int D,
                  int rope_dims, float eps, float rope_theta, int flags, int dt, void* stream) {
-  REQ(x && out, CSA_INVALID_ARG, "x and out must not be NULL");
+  REQ(T * (int64_t)H == 0 || (x && out), CSA_INVALID_ARG, "x and out must not be NULL");
   REQ((flags & ~(CSA_RMSNORM | CSA_ROPE | CSA_ROPE_INVERSE)) == 0, CSA_INVALID_ARG, "unknown flags");
   REQ(!((flags & CSA_ROPE) && (flags & CSA_ROPE_INVERSE)), CSA_INVALID_ARG, "CSA_ROPE and CSA_ROPE_INVERSE together");
   REQ(T >= 0 && H >= 1 && D >= 1, CSA_INVALID_ARG, "need T >= 0, H >= 1, D >= 1");
   REQ(dt == CSA_F32 || dt == CSA_BF16, CSA_UNSUPPORTED, "dt must be F32 or BF16");
   REQ(D % 8 == 0 && D <= 512, CSA_UNSUPPORTED, "D must be a multiple of 8, at most 512");
   const bool rope = flags & (CSA_ROPE | CSA_ROPE_INVERSE);
-  REQ(!rope || pos, CSA_INVALID_ARG, "pos must not be NULL with a rotation");
+  REQ(!rope || T == 0 || pos, CSA_INVALID_ARG, "pos must not be NULL with a rotation");
   REQ(!rope || (rope_dims >= 2 && rope_dims <= D && rope_dims % 2 == 0), CSA_INVALID_ARG,
       "rope_dims must be even and in [2, D]");
   REQ(!rope || (rope_theta > 0.0f && rope_theta <= 3.0e38f), CSA_INVALID_ARG, "rope_theta must be positive and finite");
@@ -327,13 +332,13 @@ int hca_prefill(const void* q, const void* kv_comp, const void* kv_tok, const in
                 void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
-  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, 0);
+  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, 0, Tq);
   if (rc) return rc;
   REQ(Tq >= 0 && N >= 0 && T_tok >= 0, CSA_INVALID_ARG, "Tq, N, T_tok must be >= 0");
   REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");
-  REQ(q_pos, CSA_INVALID_ARG, "q_pos must not be NULL");
-  REQ(N == 0 || kv_comp, CSA_INVALID_ARG, "kv_comp must not be NULL");
-  REQ(W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
+  REQ(Tq == 0 || q_pos, CSA_INVALID_ARG, "q_pos must not be NULL");
+  REQ(Tq == 0 || N == 0 || kv_comp, CSA_INVALID_ARG, "kv_comp must not be NULL");
+  REQ(Tq == 0 || W == 0 || kv_tok, CSA_INVALID_ARG, "kv_tok must not be NULL");
   REQ(N + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
   REQ(Tq <= 0x7fffffff, CSA_UNSUPPORTED, "Tq too large");
   csa::AttnLaunch a{};
@@ -370,12 +375,13 @@ int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, con
                   const void* kv_win, const int32_t* win_len, const float* sink, float scale, int64_t B, int H, int D,
                   int64_t N_max, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws, size_t ws_bytes,
                   void* stream) {
-  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, 0);
+  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, 0, B);
   if (rc) return rc;
   REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
   REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");
-  REQ(N_max == 0 || (kv_comp && n_comp && q_pos), CSA_INVALID_ARG, "kv_comp, n_comp, q_pos must not be NULL");
-  REQ(W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
+  REQ(B == 0 || N_max == 0 || (kv_comp && n_comp && q_pos), CSA_INVALID_ARG,
+      "kv_comp, n_comp, q_pos must not be NULL");
+  REQ(B == 0 || W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
   REQ(N_max + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
   const int hsr = hca_split_rows(N_max + W);
   const int ns = nsplit_for(N_max + W, hsr);

@@ -642,10 +642,18 @@ size_t topk_ws_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k) {
   return mx == 0 ? 0 : 2 * ((mx + 255) & ~size_t(255));
 }
 
+constexpr int TK_MAX_DEVICES = 64;
+
 hipError_t run_topk(const TopkLaunch& L, hipStream_t st) {
   const int64_t rows = L.B * L.Tq;
   if (rows == 0) return hipSuccess;
-  static bool attr_set = false;
+  // the LDS opt-in is a per-device function attribute: set once per device
+  // (setting it twice is harmless, so concurrent first calls need no lock)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= TK_MAX_DEVICES) return hipErrorInvalidDevice;
+  static bool attr_set_dev[TK_MAX_DEVICES] = {};
+  static bool attr_f_dev[TK_MAX_DEVICES] = {};
+  bool& attr_set = attr_set_dev[dev];
   const size_t lds_s = (size_t)(TK_BINS + 64 + TK_CHUNK_S) * 4;
   const size_t lds_c = (size_t)(TK_BINS + 64 + 2 * TK_CHUNK_C) * 4;
   if (!attr_set) {
@@ -659,7 +667,7 @@ hipError_t run_topk(const TopkLaunch& L, hipStream_t st) {
   }
   if (use_threshold_path(rows, L.N_max, L.top_k)) {
     const size_t lds_f = (size_t)(TK_BINS + 64 + TK_FCH_MAX + 64 + 2 * TK_CHUNK_C) * 4;
-    static bool attr_f = false;
+    bool& attr_f = attr_f_dev[dev];
     if (!attr_f) {
       hipError_t e = hipFuncSetAttribute((const void*)topk_filtered_kernel,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_f);

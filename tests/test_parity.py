@@ -736,6 +736,41 @@ def test_sparse_all_entries_equals_hca():
 
 # ------------------------------------------------------------------ whole paths
 
+def test_zero_sizes():
+    """Every entry point returns OK on empty inputs (no query, no sequence, no
+    compressed entry) without launching an empty grid; a top-k row with no
+    visible entry is all padding."""
+    _say("zero sizes")
+    H, D = 64, 512
+    e = torch.empty
+    q0, out0 = e((0, H, D), dtype=torch.bfloat16, device=DEV), e((0, H, D), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((1, 8, D), dtype=torch.bfloat16, device=DEV)
+    L.csa_compress(*(e((0, 16, D), dtype=torch.bfloat16, device=DEV) for _ in range(4)), dev(np.zeros((4, D), np.float32)),
+                   dev(np.zeros((4, D), np.float32)), e((0, 4, D), dtype=torch.bfloat16, device=DEV), m=4)
+    L.sparse_mqa_decode(q0, e((0, 8, D), dtype=torch.bfloat16, device=DEV), e((0, 16), dtype=torch.int32, device=DEV),
+                        e((0, 128, D), dtype=torch.bfloat16, device=DEV), e((0,), dtype=torch.int32, device=DEV), None,
+                        out0)
+    L.hca_dense_mqa(q0, e((0, 8, D), dtype=torch.bfloat16, device=DEV), e((0,), dtype=torch.int32, device=DEV),
+                    e((0,), dtype=torch.int32, device=DEV), e((0, 128, D), dtype=torch.bfloat16, device=DEV),
+                    e((0,), dtype=torch.int32, device=DEV), None, out0, m=128)
+    L.sparse_mqa_prefill(q0, kv[0], e((0, 16), dtype=torch.int32, device=DEV), kv[0], e((0,), dtype=torch.int32, device=DEV),
+                         None, out0, W=8)
+    L.hca_prefill(q0, kv[0], kv[0], e((0,), dtype=torch.int32, device=DEV), None, out0, m=4, W=8)
+    L.qk_norm_rope(q0, out0, e((0,), dtype=torch.int32, device=DEV), norm=True, rope=True)
+    # indexer over no entries, then top-k rows with nothing visible
+    B, Tq, k = 2, 3, 16
+    qi = torch.zeros((B, Tq, 64, 128), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((B, Tq, 64), device=DEV)
+    pos = dev(np.full((B, Tq), 1000, np.int32))
+    nc = dev(np.zeros(B, np.int32))
+    scores = torch.zeros((B, Tq, 0), device=DEV)
+    L.indexer_score(qi, w, e((B, 0, 128), dtype=torch.bfloat16, device=DEV), None, pos, nc, scores, m=4)
+    idx = torch.full((B, Tq, k), 7, dtype=torch.int32, device=DEV)
+    L.indexer_topk(torch.zeros((B, Tq, 1), device=DEV), pos, nc, idx, m=4)
+    torch.cuda.synchronize()
+    assert torch.all(idx == -1)
+
+
 def test_tiny_csa_pipeline_c1():
     """Tiny fp32 CSA end to end: compress -> score/top-k -> sparse MQA with
     window and sink, the 64 last positions of a 1024-token sequence."""

@@ -16,10 +16,11 @@ data from the previous one.
 Other workloads: c5 (1M context, E4M3 indexer keys), c2x (c2 with MXFP4
 indexer keys), c4 (HCA decode 1M), c3 (CSA prefill 64K), c6 (HCA prefill 64K),
 c4f / c2f / c3f (c4 / c2 / c3 with the main KV rows in E4M3 + bf16 RoPE dims),
-c2r (c2 with the query RMSNorm + RoPE prologue and the output inverse RoPE).
+c2r (c2 with the query RMSNorm + RoPE prologue and the output inverse RoPE),
+c2m (c2 with two query tokens per sequence and step).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--workload c2|c5|c4|c3|c2x|c6|c4f|c2f|c3f|c2r]
+                       [--workload c2|c5|c4|c3|c2x|c6|c4f|c2f|c3f|c2r|c2m]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -48,7 +49,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2",
-                    choices=["c2", "c5", "c4", "c3", "c2x", "c6", "c4f", "c2f", "c3f", "c2r"])
+                    choices=["c2", "c5", "c4", "c3", "c2x", "c6", "c4f", "c2f", "c3f", "c2r", "c2m"])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -114,7 +115,7 @@ def main():
     if a.workload == "c6":
         return bench_hca_prefill(a, torch, L, gen, dev)
     cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X, "c4f": gen.C4F, "c2f": gen.C2F,
-           "c2r": gen.C2R}[a.workload]
+           "c2r": gen.C2R, "c2m": gen.C2M}[a.workload]
     t0 = time.time()
     x = gen.gen_decode(cfg, with_compress=True)
     print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -129,9 +130,10 @@ def main():
     kvt = td if cfg.kv_dtype == "fp8" else bf  # mixed-precision rows travel as bytes
     rowb = D + 64 if cfg.kv_dtype == "fp8" else 2 * D  # bytes per main-KV row
     base = {"q": bf(x["q"]), "kv_comp": kvt(x["kv_comp"]), "kv_win": kvt(x["kv_win"])}
+    Tq = cfg.Tq  # query tokens per sequence and step
     if cfg.kind == "csa_decode":
-        base["q_idx"] = bf(x["q_idx"][:, None])
-        base["w"] = td(x["w"][:, None])
+        base["q_idx"] = bf(x["q_idx"] if Tq > 1 else x["q_idx"][:, None])
+        base["w"] = td(x["w"] if Tq > 1 else x["w"][:, None])
         if cfg.k_dtype == "fp8":
             base["k_idx"] = td(x["k_idx_codes"])
             base["k_scale"] = td(x["k_scale"])
@@ -146,21 +148,23 @@ def main():
         for nm in ("Ca", "Za"):
             base[nm] = bf(x[nm])
     shared = {"sink": td(x["sink"]), "Ba": td(x["Ba"]), "Bb": td(x["Bb"]),
-              "q_pos": td(np.full((B, 1), cfg.n - 1, np.int32)), "n_comp": td(np.full((B,), N, np.int32)),
-              "win_len": td(np.full((B,), min(W, cfg.n), np.int32))}
+              "q_pos": td(np.tile(np.arange(cfg.n - Tq, cfg.n, dtype=np.int32), (B, 1))),
+              "n_comp": td(np.full((B,), N, np.int32)),
+              "win_len": td(np.full((B,), min(W + Tq - 1, cfg.n), np.int32))}
     if cfg.qk_rope:
         shared["q_gamma"] = td(x["q_gamma"])
         shared["pos"] = td(np.full((B,), cfg.n - 1, np.int32))
     att_scale = 1.0 / math.sqrt(D) if cfg.qk_rope else 1.0
     reps = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(a.replicas - 1)]
-    out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty(((B, Tq, H, D) if Tq > 1 else (B, H, D)), dtype=torch.bfloat16, device=dev)
     qn = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
     if cfg.kind == "csa_decode":
         k = cfg.top_k
-        scores = torch.empty((B, 1, N), dtype=torch.float32, device=dev)
-        idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
-        ws_t = torch.empty(max(1, L.indexer_topk_workspace_bytes(B, 1, N, k)), dtype=torch.uint8, device=dev)
-        ws_a = torch.empty(max(1, L.sparse_mqa_decode_workspace_bytes(B, H, D, k, W)), dtype=torch.uint8, device=dev)
+        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
+        ws_t = torch.empty(max(1, L.indexer_topk_workspace_bytes(B, Tq, N, k)), dtype=torch.uint8, device=dev)
+        ws_a = torch.empty(max(1, L.sparse_mqa_decode_multi_workspace_bytes(B, Tq, H, D, k, W)), dtype=torch.uint8,
+                           device=dev)
     else:
         ws_a = torch.empty(max(1, L.hca_dense_mqa_workspace_bytes(B, H, D, N, W)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -185,8 +189,12 @@ def main():
             rec(ev, 2)
             L.indexer_topk(scores, shared["q_pos"], shared["n_comp"], idx, m=m, ws=ws_t, stream=s)
             rec(ev, 3)
-            L.sparse_mqa_decode(q_att, r["kv_comp"], idx.view(B, k), r["kv_win"], shared["win_len"], shared["sink"],
-                                out, scale=att_scale, ws=ws_a, stream=s)
+            if Tq > 1:
+                L.sparse_mqa_decode_multi(q_att, r["kv_comp"], idx, r["kv_win"], shared["win_len"], shared["sink"],
+                                          out, scale=att_scale, ws=ws_a, stream=s)
+            else:
+                L.sparse_mqa_decode(q_att, r["kv_comp"], idx.view(B, k), r["kv_win"], shared["win_len"],
+                                    shared["sink"], out, scale=att_scale, ws=ws_a, stream=s)
             if cfg.qk_rope:  # epilogue: the output's rotated dims turned back
                 L.qk_norm_rope(out, out, shared["pos"], inverse=True, stream=s)
         else:
@@ -246,7 +254,7 @@ def main():
     kern_avg = e3a.elapsed_time(e3b) / a.steps
     scan_avg = kern_avg
 
-    tokens_per_s = B / (ms_step * 1e-3)
+    tokens_per_s = B * Tq / (ms_step * 1e-3)
     res = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
@@ -254,12 +262,13 @@ def main():
     }
     if cfg.kind == "csa_decode":
         kbytes = {"fp8": N * (cfg.D_I + 4), "mxfp4": N * (cfg.D_I // 2 + cfg.D_I // 32)}.get(cfg.k_dtype, N * cfg.D_I * 2)
-        scan_bytes = B * (kbytes + cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4)  # keys (+scales), q_idx, w
-        step_bytes = B * (kbytes + cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4 + (k + W) * rowb + H * D * 2 * 2 + k * 4)
+        # keys (+scales) once per sequence (what the method needs), q_idx and w per query
+        scan_bytes = B * (kbytes + Tq * (cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4))
+        step_bytes = B * (kbytes + Tq * (cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4 + (k + W) * rowb + H * D * 2 * 2 + k * 4))
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
                          "m": m, "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I,
                          "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype,
-                         "kv_dtype": cfg.kv_dtype, "qk_norm_rope": cfg.qk_rope}
+                         "kv_dtype": cfg.kv_dtype, "qk_norm_rope": cfg.qk_rope, "query_tokens_per_sequence": Tq}
         kname = {"fp8": "idx_scan_lp_kernel<2> (E4M3 keys)", "mxfp4": "idx_scan_lp_kernel<3> (MXFP4 keys)"}.get(cfg.k_dtype, "idx_scan_bf16_kernel")
         res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": round(scan_bytes / (scan_avg * 1e-3) / 1e9, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -559,14 +568,20 @@ def cpu_baseline(cfg, x, budget_s: float):
                 keys, sc = oracle.mxfp4_decode(x["k_idx_codes"][b], x["k_scale"][b]), None
             else:
                 keys, sc = x["k_idx"][b], None
-            q, tau = x["q"][b], 1.0
-            if cfg.qk_rope:
-                q = oracle.rope_rotate(oracle.rms_norm(q[None], x["q_gamma"], 1e-6), [cfg.n - 1])[0]
-                tau = 1.0 / math.sqrt(cfg.D)
-            _, o, _, _ = oracle.csa_query(q, x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, cfg.N, m, cfg.top_k,
-                                          kvd(x["kv_win"][b]), x["sink"], k_scale=sc, tau=tau)
-            if cfg.qk_rope:
-                oracle.rope_rotate(o[None], [cfg.n - 1], inverse=True)
+            win = kvd(x["kv_win"][b])
+            for t in range(cfg.Tq):  # query token t at position n - Tq + t, its window ending at its token
+                p = cfg.n - cfg.Tq + t
+                q, qi_, w_ = ((x["q"][b][t], x["q_idx"][b][t], x["w"][b][t]) if cfg.Tq > 1
+                              else (x["q"][b], x["q_idx"][b], x["w"][b]))
+                tau = 1.0
+                if cfg.qk_rope:
+                    q = oracle.rope_rotate(oracle.rms_norm(q[None], x["q_gamma"], 1e-6), [p])[0]
+                    tau = 1.0 / math.sqrt(cfg.D)
+                hi = len(win) - cfg.Tq + t
+                _, o, _, _ = oracle.csa_query(q, qi_, w_, comp, keys, p, cfg.N, m, cfg.top_k,
+                                              win[max(0, hi - cfg.W + 1):hi + 1], x["sink"], k_scale=sc, tau=tau)
+                if cfg.qk_rope:
+                    oracle.rope_rotate(o[None], [p], inverse=True)
         else:
             ent = oracle.compress(x["Ca"][b], None, x["Za"][b], None, x["Ba"], None, m, overlap=False)[0]
             comp = kvd(x["kv_comp"][b])
@@ -574,8 +589,8 @@ def cpu_baseline(cfg, x, budget_s: float):
             oracle.hca_query(x["q"][b], comp, cfg.n - 1, cfg.N, m, kvd(x["kv_win"][b]), x["sink"])
         done += 1
     dt = time.perf_counter() - t0
-    return {"value": round(done / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {cfg.B} sequences of one decode step ({cfg.name}), float64 NumPy, "
+    return {"value": round(done * cfg.Tq / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {cfg.B} sequences ({cfg.Tq} query token(s) each) of one decode step ({cfg.name}), float64 NumPy, "
                       f"{dt:.1f}s"}
 
 

@@ -203,6 +203,25 @@ int sparse_mqa_decode(const void* q, const void* kv_comp, const int32_t* topk_id
                       void* ws, size_t ws_bytes, void* stream);
 size_t sparse_mqa_decode_workspace_bytes(int64_t B, int H, int D, int top_k, int W);
 
+/* sparse_mqa_decode_multi — Tq consecutive query tokens per sequence in one
+ * decode step (the pages' configuration trains a depth-1 multi-token
+ * predictor, [LQNN] section 3: a step can verify a drafted token beside the
+ * current one). Query t of sequence b (t < Tq, the last Tq tokens, oldest
+ * first) attends its own top-k rows and its own window:
+ *   q      : [B, Tq, H, D]       topk_idx : [B, Tq, top_k] int32 (-1 = empty)
+ *   kv_win : [B, W + Tq - 1, D]  a buffer of the latest raw tokens, oldest
+ *            first; rows 0 .. wl-1 are valid (wl = min(win_len[b], W + Tq - 1))
+ *            and row wl-1 is the newest token. Query t's own token is row
+ *            wl - Tq + t; its window is the (at most) W rows ending there.
+ *   out    : [B, Tq, H, D]       lse : [B, Tq, H] (nullable)
+ * Everything else as sparse_mqa_decode, which is this call with Tq = 1.
+ * 1 <= Tq <= 64. */
+int sparse_mqa_decode_multi(const void* q, const void* kv_comp, const int32_t* topk_idx, const void* kv_win,
+                            const int32_t* win_len, const float* sink, float scale, int64_t B, int64_t Tq, int H,
+                            int D, int64_t N_max, int top_k, int W, int kv_dt, int out_dt, void* out, float* lse,
+                            void* ws, size_t ws_bytes, void* stream);
+size_t sparse_mqa_decode_multi_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int top_k, int W);
+
 /* sparse_mqa_prefill — Tq queries of one sequence.
  *   q      : [Tq, H, D]          kv_comp : [N, D]
  *   topk_idx : [Tq, top_k] int32 (-1 = empty)

@@ -52,6 +52,9 @@ _SIGS = {
     "sparse_mqa_decode": ([_vp] * 6 + [_f32, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
                                        _vp], _i32),
     "sparse_mqa_decode_workspace_bytes": ([_i64, _i32, _i32, _i32, _i32], _sz),
+    "sparse_mqa_decode_multi": ([_vp] * 6 + [_f32, _i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
+                                             _vp, _sz, _vp], _i32),
+    "sparse_mqa_decode_multi_workspace_bytes": ([_i64, _i64, _i32, _i32, _i32, _i32], _sz),
     "sparse_mqa_prefill": ([_vp] * 6 + [_f32, _i64, _i32, _i32, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                         _sz, _vp], _i32),
     "sparse_mqa_prefill_workspace_bytes": ([_i64, _i32, _i32, _i32, _i32], _sz),
@@ -205,6 +208,24 @@ def sparse_mqa_decode(q, kv_comp, topk_idx, kv_win, win_len, sink, out, lse=None
     _check(lib.sparse_mqa_decode(_ptr(q), _ptr(kv_comp), _ptr(topk_idx), _ptr(kv_win), _ptr(win_len), _ptr(sink),
                                  scale, B, H, D, N_max, top_k, W, _kv_dt(q, kv_comp), _dt(out), _ptr(out), _ptr(lse),
                                  _ptr(ws), nb, _stream(stream)))
+
+
+def sparse_mqa_decode_multi_workspace_bytes(B: int, Tq: int, H: int, D: int, top_k: int, W: int) -> int:
+    return lib.sparse_mqa_decode_multi_workspace_bytes(B, Tq, H, D, top_k, W)
+
+
+def sparse_mqa_decode_multi(q, kv_comp, topk_idx, kv_win, win_len, sink, out, lse=None, *, scale: float = 1.0,
+                            ws=None, stream=None) -> None:
+    """q [B, Tq, H, D]; kv_comp [B, N_max, D]; topk_idx [B, Tq, top_k]; kv_win [B, W + Tq - 1, D];
+    win_len [B]; out [B, Tq, H, D]; lse [B, Tq, H] or None."""
+    B, Tq, H, D = q.shape
+    N_max = kv_comp.shape[1]
+    top_k = topk_idx.shape[-1]
+    W = kv_win.shape[1] - (Tq - 1) if kv_win is not None else 0
+    ws, nb = _ws(sparse_mqa_decode_multi_workspace_bytes(B, Tq, H, D, top_k, W), ws, q.device)
+    _check(lib.sparse_mqa_decode_multi(_ptr(q), _ptr(kv_comp), _ptr(topk_idx), _ptr(kv_win), _ptr(win_len),
+                                       _ptr(sink), scale, B, Tq, H, D, N_max, top_k, W, _kv_dt(q, kv_comp), _dt(out),
+                                       _ptr(out), _ptr(lse), _ptr(ws), nb, _stream(stream)))
 
 
 def sparse_mqa_prefill_workspace_bytes(Tq: int, H: int, D: int, top_k: int, W: int) -> int:

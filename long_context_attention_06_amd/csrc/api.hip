@@ -210,27 +210,33 @@ int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, con
   return hip_status(csa::run_topk(t, st), "indexer_score_topk");
 }
 
-size_t sparse_mqa_decode_workspace_bytes(int64_t B, int H, int D, int top_k, int W) {
-  if (B < 0 || H <= 0 || D <= 0 || top_k < 0 || W < 0) return 0;
-  return attn_ws(B, H, D, nsplit_for((int64_t)top_k + W, SPARSE_SPLIT_ROWS));
+size_t sparse_mqa_decode_multi_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int top_k, int W) {
+  if (B < 0 || Tq < 1 || H <= 0 || D <= 0 || top_k < 0 || W < 0) return 0;
+  return attn_ws(B * Tq, H, D, nsplit_for((int64_t)top_k + W, SPARSE_SPLIT_ROWS));
 }
 
-int sparse_mqa_decode(const void* q, const void* kv_comp, const int32_t* topk_idx, const void* kv_win,
-                      const int32_t* win_len, const float* sink, float scale, int64_t B, int H, int D, int64_t N_max,
-                      int top_k, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws, size_t ws_bytes,
-                      void* stream) {
-  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, top_k, B);
-  if (rc) return rc;
+size_t sparse_mqa_decode_workspace_bytes(int64_t B, int H, int D, int top_k, int W) {
+  return sparse_mqa_decode_multi_workspace_bytes(B, 1, H, D, top_k, W);
+}
+
+int sparse_mqa_decode_multi(const void* q, const void* kv_comp, const int32_t* topk_idx, const void* kv_win,
+                            const int32_t* win_len, const float* sink, float scale, int64_t B, int64_t Tq, int H,
+                            int D, int64_t N_max, int top_k, int W, int kv_dt, int out_dt, void* out, float* lse,
+                            void* ws, size_t ws_bytes, void* stream) {
   REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
-  REQ(B == 0 || top_k == 0 || (kv_comp && topk_idx), CSA_INVALID_ARG, "kv_comp and topk_idx must not be NULL");
-  REQ(B == 0 || W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
+  REQ(Tq >= 1 && Tq <= 64, CSA_INVALID_ARG, "Tq must be in [1, 64]");
+  const int64_t nq = B * Tq;
+  int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, top_k, nq);
+  if (rc) return rc;
+  REQ(nq == 0 || top_k == 0 || (kv_comp && topk_idx), CSA_INVALID_ARG, "kv_comp and topk_idx must not be NULL");
+  REQ(nq == 0 || W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
   REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
   const int ns = nsplit_for((int64_t)top_k + W, SPARSE_SPLIT_ROWS);
-  const size_t need = attn_ws(B, H, D, ns);
+  const size_t need = attn_ws(nq, H, D, ns);
   REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
   REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
   REQ(((uintptr_t)ws & 255u) == 0, CSA_INVALID_ARG, "ws must be 256-byte aligned");
-  REQ(B <= 0x7fffffff, CSA_UNSUPPORTED, "B too large");
+  REQ(nq <= 0x7fffffff, CSA_UNSUPPORTED, "B * Tq too large");
   csa::AttnLaunch a{};
   a.src = 0;
   a.q = q;
@@ -240,12 +246,14 @@ int sparse_mqa_decode(const void* q, const void* kv_comp, const int32_t* topk_id
   a.win_len = win_len;
   a.sink = sink;
   a.scale = scale;
-  a.nq = B;
+  a.nq = nq;
   a.N_max = N_max;
   a.H = H;
   a.D = D;
   a.top_k = top_k;
   a.W = W;
+  a.Tq = (int)Tq;
+  a.Wb = W + (int)Tq - 1;
   a.m_rate = 1;
   a.kv_dt = kv_dt;
   a.out_dt = out_dt;
@@ -253,11 +261,19 @@ int sparse_mqa_decode(const void* q, const void* kv_comp, const int32_t* topk_id
   a.split_rows = ns > 1 ? SPARSE_SPLIT_ROWS : a.slots;
   a.nsplit = ns;
   a.part_o = reinterpret_cast<float*>(ws);
-  a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + round256((size_t)B * ns * H * D * 4));
+  a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + round256((size_t)nq * ns * H * D * 4));
   a.out = out;
   a.lse = lse;
   if (W == 0) a.win_len = nullptr;
   return hip_status(csa::run_attn(a, (hipStream_t)stream), "sparse_mqa_decode");
+}
+
+int sparse_mqa_decode(const void* q, const void* kv_comp, const int32_t* topk_idx, const void* kv_win,
+                      const int32_t* win_len, const float* sink, float scale, int64_t B, int H, int D, int64_t N_max,
+                      int top_k, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws, size_t ws_bytes,
+                      void* stream) {
+  return sparse_mqa_decode_multi(q, kv_comp, topk_idx, kv_win, win_len, sink, scale, B, 1, H, D, N_max, top_k, W,
+                                 kv_dt, out_dt, out, lse, ws, ws_bytes, stream);
 }
 
 size_t sparse_mqa_prefill_workspace_bytes(int64_t, int, int, int, int) { return 0; }

@@ -61,7 +61,22 @@ struct RowSrc {
   int64_t T_tok;
   int top_k;
   int W;
+  int Tq;  // sparse decode: queries per sequence (query qi is token qi % Tq of sequence qi / Tq)
+  int Wb;  // sparse decode: window buffer rows per sequence (W + Tq - 1)
 };
+
+// Sparse decode window of query t of a sequence: the buffer's valid rows are
+// 0 .. wl-1 (wl = min(win_len, Wb)), its last row the newest token; query t's
+// own token is row wl - Tq + t, and its window the (at most) W rows ending
+// there. Returns the first row; *cnt gets the row count.
+__device__ __forceinline__ int dec_window(const RowSrc& s, const int32_t* __restrict__ win_len, int64_t b, int t,
+                                          int* cnt) {
+  const int wl = win_len ? min(max(win_len[b], 0), s.Wb) : 0;
+  const int hi = wl - s.Tq + t;
+  const int lo = max(0, hi - s.W + 1);
+  *cnt = max(0, hi - lo + 1);
+  return lo;
+}
 
 // The memory-resident part of a slot (its top-k index); loaded one tile ahead
 // of the row itself so the index -> row dependency never stalls a tile.
@@ -79,13 +94,13 @@ __device__ __forceinline__ const uint8_t* slot_row(const RowSrc& s, int64_t qi, 
     if (j < s.top_k) {
       const int id = code;
       if (id < 0 || id >= s.N_max) return nullptr;
-      int64_t row = (SRC == SRC_SPARSE_DEC) ? qi * s.N_max + id : (int64_t)id;
+      int64_t row = (SRC == SRC_SPARSE_DEC) ? (qi / s.Tq) * s.N_max + id : (int64_t)id;
       return s.kv_comp + row * ROWB;
     }
     int w = j - s.top_k;
-    if (SRC == SRC_SPARSE_DEC) {
+    if (SRC == SRC_SPARSE_DEC) {  // lim0: window rows of this query, lim1: its first buffer row
       if (w >= lim0) return nullptr;
-      return s.kv_win + (qi * s.W + w) * ROWB;
+      return s.kv_win + ((qi / s.Tq) * s.Wb + lim1 + w) * ROWB;
     }
     int64_t tok = (int64_t)lim1 - s.W + 1 + w;
     if (tok < 0 || tok >= s.T_tok) return nullptr;
@@ -152,8 +167,9 @@ __device__ __forceinline__ QRows query_rows(const RowSrc& src, const int32_t* __
   QRows r;
   r.lim0 = 0;
   r.lim1 = 0;
+  r.w0 = 0;
   if (SRC == SRC_SPARSE_DEC) {
-    r.lim0 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
+    r.w0 = dec_window(src, win_len, qi / src.Tq, (int)(qi % src.Tq), &r.lim0);
   } else if (SRC == SRC_HCA_DEC) {
     if (n_comp) {
       const int64_t v = min((int64_t)n_comp[qi], ((int64_t)q_pos[qi] + 1) / m_rate);
@@ -170,9 +186,12 @@ __device__ __forceinline__ QRows query_rows(const RowSrc& src, const int32_t* __
   r.s_begin = sp * split_rows;
   r.s_end = min(slots, r.s_begin + split_rows);
   constexpr bool PRE = SRC == SRC_SPARSE_PRE || SRC == SRC_HCA_PRE;  // one sequence: shared caches
-  r.comp_base = src.kv_comp + (PRE ? 0 : qi * src.N_max * ROWB);
-  r.win_base = src.kv_win + (PRE ? 0 : qi * (int64_t)src.W * ROWB);
-  r.n_rows = r.len1 = r.w0 = 0;
+  const int64_t seq = SRC == SRC_SPARSE_DEC ? qi / src.Tq : qi;
+  const int64_t wrows = SRC == SRC_SPARSE_DEC ? src.Wb : src.W;
+  r.comp_base = src.kv_comp + (PRE ? 0 : seq * src.N_max * ROWB);
+  r.win_base = src.kv_win + (PRE ? 0 : seq * wrows * ROWB);
+  r.n_rows = r.len1 = 0;
+  if (SRC != SRC_SPARSE_DEC) r.w0 = 0;
   if (SRC == SRC_HCA_DEC) {
     // slots [0, N_max) are compressed entries (valid below V), then the window
     r.len1 = max(0, min(r.s_end, r.lim0) - r.s_begin);
@@ -208,7 +227,7 @@ __device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, in
     bool ok = false;
     if (j < r.s_end) {
       if (j < src.top_k) {
-        const int id = src.idx[qi * src.top_k + j];
+        const int id = src.idx[qi * src.top_k + j];  // qi: the flattened query
         ok = id >= 0 && id < src.N_max;
         e = id;
       } else {
@@ -216,6 +235,7 @@ __device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, in
         int row = ww;
         if (SRC == SRC_SPARSE_DEC) {
           ok = ww < r.lim0;
+          row = r.w0 + ww;  // this query's window starts at buffer row w0
         } else {
           const int64_t tok = (int64_t)r.lim1 - src.W + 1 + ww;
           ok = tok >= 0 && tok < src.T_tok;
@@ -1126,7 +1146,7 @@ attn_f32_kernel(const float* __restrict__ q, RowSrc src, const int32_t* __restri
 
   int lim0 = 0, lim1 = 0;
   if (SRC == SRC_SPARSE_DEC) {
-    lim0 = win_len ? min(max(win_len[qi], 0), src.W) : 0;
+    lim1 = dec_window(src, win_len, qi / src.Tq, (int)(qi % src.Tq), &lim0);
   } else if (SRC == SRC_HCA_DEC) {
     if (n_comp) {
       const int64_t v = min((int64_t)n_comp[qi], ((int64_t)q_pos[qi] + 1) / m_rate);
@@ -1453,6 +1473,8 @@ static RowSrc row_src(const AttnLaunch& a) {
   src.T_tok = a.T_tok;
   src.top_k = a.top_k;
   src.W = a.W;
+  src.Tq = a.Tq > 0 ? a.Tq : 1;
+  src.Wb = a.Wb > 0 ? a.Wb : a.W;
   return src;
 }
 

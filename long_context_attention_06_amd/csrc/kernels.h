@@ -62,6 +62,7 @@ struct AttnLaunch {
   int H, D, top_k, W, m_rate;
   int kv_dt, out_dt;
   int slots, split_rows, nsplit;
+  int Tq, Wb;  // sparse decode: queries per sequence, window buffer rows (0: 1 and W)
   float* part_o;
   float* part_ml;
   void* out;

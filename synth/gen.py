@@ -182,7 +182,7 @@ class Cfg:
     k_dtype: str = "bf16"  # indexer key storage
     kv_dtype: str = "bf16"  # main KV rows: "bf16", or "fp8" (E4M3 + bf16 RoPE dims)
     qk_rope: bool = False   # decode step with the query prologue (RMSNorm, RoPE) and output inverse RoPE
-    Tq: int = 1          # queries per sequence
+    Tq: int = 1          # queries per sequence (decode: the last Tq tokens, e.g. 2 with a drafted token)
 
     @property
     def N(self) -> int:  # compressed entries; tail tokens (n mod m) are dropped
@@ -215,7 +215,10 @@ C3F = dataclasses.replace(C3, name="c3f_csa_prefill_64k_kv_fp8", kv_dtype="fp8")
 # (gamma ~ U(0.5, 1.5)) and rotated at their position, the output is rotated
 # back; the logit scale is then 1/sqrt(D)
 C2R = dataclasses.replace(C2, name="c2r_csa_decode_flash_128k_qk_rope", qk_rope=True)
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6, C4F, C2F, C3F, C2R)}
+# C2 with two query tokens per sequence and step (the current token and a
+# drafted one, as a depth-1 multi-token predictor verifies them)
+C2M = dataclasses.replace(C2, name="c2m_csa_decode_flash_128k_2tok", Tq=2)
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6, C4F, C2F, C3F, C2R, C2M)}
 
 
 def scaled(cfg: Cfg, **kw) -> Cfg:
@@ -248,17 +251,19 @@ def gen_decode_seq(cfg: Cfg, b: int, with_compress: bool = True) -> Dict[str, np
     """
     s, D = cfg.seed, cfg.D
     out: Dict[str, np.ndarray] = {}
-    out["q"] = _store(_normal(rng(s, "q", b), (cfg.H, D), 1.0 / math.sqrt(D)), cfg.dtype)
+    tq = (cfg.Tq,) if cfg.Tq > 1 else ()  # several query tokens: a leading query axis
+    out["q"] = _store(_normal(rng(s, "q", b), tq + (cfg.H, D), 1.0 / math.sqrt(D)), cfg.dtype)
     kv = _normal(rng(s, "kv_comp", b), (cfg.N, D))
-    win = _normal(rng(s, "kv_win", b), (min(cfg.W, cfg.n), D))
+    # the window buffer holds the latest W + Tq - 1 tokens
+    win = _normal(rng(s, "kv_win", b), (min(cfg.W + cfg.Tq - 1, cfg.n), D))
     if cfg.kv_dtype == "fp8":  # uint8 rows [.., D + 64]
         out["kv_comp"], out["kv_win"] = kv_fp8_rows(kv), kv_fp8_rows(win)
     else:
         out["kv_comp"], out["kv_win"] = _store(kv, cfg.dtype), _store(win, cfg.dtype)
     if cfg.kind == "csa_decode":
         HI, DI = cfg.H_I, cfg.D_I
-        out["q_idx"] = _store(_normal(rng(s, "q_idx", b), (HI, DI), 1.0 / math.sqrt(DI)), cfg.dtype)
-        out["w"] = _normal(rng(s, "w", b), (HI,))
+        out["q_idx"] = _store(_normal(rng(s, "q_idx", b), tq + (HI, DI), 1.0 / math.sqrt(DI)), cfg.dtype)
+        out["w"] = _normal(rng(s, "w", b), tq + (HI,))
         k = _normal(rng(s, "k_idx", b), (cfg.N, DI))
         if cfg.k_dtype == "fp8":
             codes, scale = e4m3_quantize_rows(k)

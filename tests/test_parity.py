@@ -415,6 +415,53 @@ def test_compress_kv_fp8_rows(m, overlap):
         assert np.all(np.abs(v - ref) <= bound), f"b={b} max err {np.abs(v - ref).max():.3e}"
 
 
+@pytest.mark.parametrize("rows", ["bf16", "kv_fp8", "f32"])
+def test_sparse_decode_multi(rows):
+    """Two (and three) query tokens per sequence, each with its own top-k
+    rows and its own window in a shared buffer of the latest W + Tq - 1
+    tokens: full buffers, a short sequence, no window, a query with no
+    window row yet."""
+    _say("sparse_decode_multi", rows)
+    g = _g(110)
+    f32 = rows == "f32"
+    H, D, N_max, k, W = (4, 64, 300, 40, 16) if f32 else (64, 512, 700, 300, 128)
+    for Tq in (2, 3):
+        B = 4
+        Wb = W + Tq - 1
+        q = g.standard_normal((B, Tq, H, D)).astype(np.float32) / math.sqrt(D)
+        kvx = g.standard_normal((B, N_max, D)).astype(np.float32)
+        winx = g.standard_normal((B, Wb, D)).astype(np.float32)
+        if rows == "kv_fp8":
+            kv_d, kv_v = _kv8(kvx)
+            win_d, win_v = _kv8(winx)
+        elif f32:
+            kv_d, kv_v, win_d, win_v = dev(kvx), kvx.astype(np.float64), dev(winx), winx.astype(np.float64)
+        else:
+            kvx, winx = gen.bf16_round(kvx), gen.bf16_round(winx)
+            kv_d, kv_v, win_d, win_v = bf(kvx), kvx.astype(np.float64), bf(winx), winx.astype(np.float64)
+        if not f32:
+            q = gen.bf16_round(q)
+        idx = np.sort(g.choice(N_max, size=(B, Tq, k)), axis=2).astype(np.int32)
+        idx[1, 0, k // 2:] = -1
+        win_len = np.array([Wb, 5, 0, Tq - 1], np.int32)  # the last: query 0 has no window row yet
+        sink = g.standard_normal(H).astype(np.float32)
+        out = torch.empty((B, Tq, H, D), dtype=torch.float32, device=DEV)
+        lse = torch.empty((B, Tq, H), device=DEV)
+        L.sparse_mqa_decode_multi(dev(q) if f32 else bf(q), kv_d, dev(idx), win_d, dev(win_len), dev(sink), out, lse)
+        torch.cuda.synchronize()
+        O, LS = host(out), host(lse)
+        for b in range(B):
+            wl = min(int(win_len[b]), Wb)
+            for t in range(Tq):
+                hi = wl - Tq + t
+                lo = max(0, hi - W + 1)
+                ids = idx[b, t][idx[b, t] >= 0]
+                rws = np.concatenate([kv_v[b][ids], win_v[b][lo:hi + 1] if hi >= lo else win_v[b][:0]])
+                ref, rlse = oracle.attend(q[b, t], rws, sink)
+                check_out(O[b, t], ref, _attn_tight(ref, "f32" if f32 else "bf16"), f"multi Tq={Tq} b={b} t={t}")
+                assert np.abs(LS[b, t] - rlse).max() < 1e-3
+
+
 def test_sparse_decode_no_sink_empty():
     _say("sparse_decode", "empty")
     B, H, D = 1, 64, 512

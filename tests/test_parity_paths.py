@@ -283,6 +283,61 @@ def test_csa_prefill_64k_last_chunk_sampled():
     check_prefill(cfg, [gen.num_chunks(cfg) - 1], lambda T: sorted(set([0, 1, T - 1] + list(rng.integers(0, T, 8)))))
 
 
+def check_csa_decode_multi(cfg, seqs):
+    """Tq query tokens per sequence in one step (positions n-Tq .. n-1): the
+    completed entry is appended, each token is scored and selected at its own
+    position, and attends its own rows and its window (the W buffer rows
+    ending at its token), as bench.py runs it."""
+    L = _L()
+    x = gen.gen_decode(cfg)
+    B, N, m, k, W, Tq = cfg.B, cfg.N, cfg.m, cfg.top_k, cfg.W, cfg.Tq
+    kv = _kv(cfg, x["kv_comp"])
+    L.csa_compress(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]), _t(x["Bb"]), kv, m=m,
+                   tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
+    pos = np.tile(np.arange(cfg.n - Tq, cfg.n, dtype=np.int32), (B, 1))
+    q_pos, n_comp = _t(pos), _t(np.full((B,), N, np.int32))
+    scores = torch.empty((B, Tq, N), dtype=torch.float32, device=DEV)
+    L.indexer_score(_bf(x["q_idx"]), _t(x["w"]), _bf(x["k_idx"]), None, q_pos, n_comp, scores, m=m)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    L.indexer_topk(scores, q_pos, n_comp, idx, m=m)
+    out = torch.empty((B, Tq, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Tq, cfg.H), device=DEV)
+    L.sparse_mqa_decode_multi(_bf(x["q"]), kv, idx, _kv(cfg, x["kv_win"]), _t(np.full((B,), W + Tq - 1, np.int32)),
+                              _t(x["sink"]), out, lse)
+    torch.cuda.synchronize()
+    kv2, S, I, O, LSE = host(kv[:, N - 2:]), host(scores), host(idx), host(out), host(lse)
+    for b in seqs:
+        ent = oracle.compress(x["Ca"][b], x["Cb"][b], x["Za"][b], x["Zb"][b], x["Ba"], x["Bb"], m,
+                              blocks=range(1, 2))[0]
+        _check_entry(cfg, kv2[b, 1], ent, "compressed entry N-1")
+        comp = _kv_values(cfg, x["kv_comp"][b])
+        comp[N - 1] = _kv_values(cfg, kv2[b, 1])
+        win = _kv_values(cfg, x["kv_win"][b])
+        for t in range(Tq):
+            p = cfg.n - Tq + t
+            print(f"[case] {cfg.name} b={b} t={t} pos {p}", flush=True)
+            wrows = win[t:t + W]  # full buffer: token t's window is rows t .. t+W-1
+            oidx, o_ref, lse_ref, sc = oracle.csa_query(x["q"][b][t], x["q_idx"][b][t], x["w"][b][t], comp,
+                                                        x["k_idx"][b], p, N, m, k, wrows, x["sink"])
+            V = oracle.visible(p, N, m)
+            assert np.abs(S[b, t, :V] - sc).max() <= 2e-5 * 8 * (1 + np.abs(sc).max())
+            check_topk_row(I[b, t], oidx, sc, k, f"b={b} t={t}")
+            rows = np.concatenate([comp[I[b, t][I[b, t] >= 0]], wrows])
+            o_own, lse_own = oracle.attend(x["q"][b][t], rows, x["sink"])
+            check_out(O[b, t], o_own, _tight(o_own), f"multi out b={b} t={t}")
+            assert np.abs(LSE[b, t] - lse_own).max() < 1e-3
+            if np.array_equal(I[b, t], oidx):
+                check_out(O[b, t], o_ref, _tight(o_ref), f"multi end to end b={b} t={t}")
+
+
+def test_csa_decode_flash_2tok_reduced():
+    check_csa_decode_multi(gen.scaled(gen.C2M, B=4, n=16384), range(4))
+
+
+def test_csa_decode_flash_2tok_full_size_sampled():
+    check_csa_decode_multi(gen.C2M, [0, 19, 31])
+
+
 def test_csa_decode_flash_qk_rope_reduced():
     cfg = gen.scaled(gen.C2R, B=4, n=16384)  # query RMSNorm + RoPE prologue, output inverse RoPE
     check_csa_decode(cfg, gen.gen_decode(cfg), range(cfg.B))

@@ -59,7 +59,10 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t codes, float scale)
 // .. + 7, so each load instruction reads 64 contiguous bytes of 16 key rows.
 // The waves never wait for each other (no LDS tile, no barrier per tile).
 // Two tiles per wave are in flight (a register ring) while one is computed;
-// heads are four 16-row M tiles of v_mfma_f32_16x16x32_bf16.
+// heads are four 16-row M tiles of v_mfma_f32_16x16x32_bf16. With NQ = 2 a
+// workgroup serves two query rows of one sequence (a step with a drafted
+// token): each key tile is loaded once for both queries' 2 x 64 heads.
+template <int NQ>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                      const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
@@ -69,13 +72,13 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
   constexpr int KROW = DI * 2;                          // bytes per key row
   constexpr int TE = IDX_BF16_TE;                       // entries per tile (16 per wave)
   static_assert(TE == 64, "one 16-entry N tile per wave");
-  __shared__ __attribute__((aligned(16))) float lds_w[H];
+  __shared__ __attribute__((aligned(16))) float lds_w[NQ * H];
 
   const int tid = threadIdx.x;
   const int l = tid & 63, wv = tid >> 6;
   const int G = l >> 4, l16 = l & 15;  // k-group (8 dims of each k-step) and entry of the MFMA operands
-  const int64_t row = blockIdx.y;
-  const int64_t b = row / Tq;
+  const int64_t row0 = (int64_t)blockIdx.y * NQ;  // first query row of this workgroup (Tq % NQ == 0)
+  const int64_t b = row0 / Tq;
   const uint8_t* kb = k_idx + b * N_max * KROW + G * 16;
 
   u32x4_t rg[3][KS];
@@ -98,37 +101,50 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
   load(I0{}, blockIdx.x, N_max);
   load(I1{}, blockIdx.x + gridDim.x, N_max);
 
-  int64_t V = min((int64_t)n_comp[b], ((int64_t)q_pos[row] + 1) / m);
-  V = max((int64_t)0, min(V, N_max));
+  int64_t Vq[NQ], V = 0;  // visible entries of each query; the tiles cover the largest
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    Vq[j] = max((int64_t)0, min(min((int64_t)n_comp[b], ((int64_t)q_pos[row0 + j] + 1) / m), N_max));
+    V = max(V, Vq[j]);
+  }
   const int64_t ntiles = (V + TE - 1) / TE;
   if ((int64_t)blockIdx.x >= ntiles) return;
   const int64_t nmine = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // tiles of this workgroup
 
   // query operand A[m = head][k]: lane (head mt*16 + l16, group G) holds dims
   // 32 s + 8 G .. + 7 for k-step s
-  bf16x8_t qa[4][KS];
+  bf16x8_t qa[NQ][4][KS];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const uint16_t* qp = q_idx + (row * H + mt * 16 + l16) * DI + G * 8;
+  for (int j = 0; j < NQ; ++j)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qa[mt][s] = as_bf16x8(ld16(qp + s * 32));
-  }
-  if (tid < H) lds_w[tid] = w[row * H + tid];
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint16_t* qp = q_idx + ((row0 + j) * H + mt * 16 + l16) * DI + G * 8;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qa[j][mt][s] = as_bf16x8(ld16(qp + s * 32));
+    }
+  if (tid < NQ * H) lds_w[tid] = w[row0 * H + tid];
   // wait for the query and the weights here, on every lane: left pending into
   // the loop, these loads would make each tile wait for all loads in flight
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int j = 0; j < NQ; ++j)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qa[mt][s]));
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qa[j][mt][s]));
   __syncthreads();
-  f32x4_t wr[4];  // weights of heads mt*16 + G*4 + 0..3 (accumulator rows of this lane)
+  f32x4_t wr[NQ][4];  // weights of heads mt*16 + G*4 + 0..3 (accumulator rows of this lane)
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) wr[mt] = *reinterpret_cast<const f32x4_t*>(&lds_w[mt * 16 + G * 4]);
-  // scores go out through a buffer descriptor of the row's V entries: the
+  for (int j = 0; j < NQ; ++j)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) wr[j][mt] = *reinterpret_cast<const f32x4_t*>(&lds_w[j * H + mt * 16 + G * 4]);
+  // scores go out through a buffer descriptor of each row's V entries: the
   // hardware drops stores past its end, so the store needs no branch (a
   // branch would again make the count of memory operations in flight unknown)
-  const __amdgpu_buffer_rsrc_t srow =
-      __builtin_amdgcn_make_buffer_rsrc(scores + row * N_max, (short)0, (int)(V * 4), BUF_RSRC_WORD3);
+  __amdgpu_buffer_rsrc_t srow[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j)
+    srow[j] = __builtin_amdgcn_make_buffer_rsrc(scores + (row0 + j) * N_max, (short)0, (int)(Vq[j] * 4),
+                                                BUF_RSRC_WORD3);
 
   // tile it is in slot it % 3; the load of tile it + 2 goes to the slot the
   // previous tile used, so no register is both read and refilled in one step
@@ -136,20 +152,24 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
     constexpr int slot = decltype(SLOT)::value;
     const int64_t tile = blockIdx.x + it * gridDim.x;
     load(NEXT, blockIdx.x + (it + 2) * gridDim.x, V);  // past the last tile: clamped, unused
-    float part = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], as_bf16x8(rg[slot][s]), acc);
-      // accumulator row r of this lane is head mt*16 + G*4 + r
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part += wr[mt][r] * relu_bits(acc[r]);
-    }
-    part = sum_rows16(part);
     const int e = (int)(tile * TE) + wv * 16 + l16;
-    // lanes of groups 1..3 hold the same sums: their offset is past the end
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow, G == 0 ? e * 4 : (int)(V * 4), 0, 0);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      float part = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = mfma16(qa[j][mt][s], as_bf16x8(rg[slot][s]), acc);
+        // accumulator row r of this lane is head mt*16 + G*4 + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part += wr[j][mt][r] * relu_bits(acc[r]);
+      }
+      part = sum_rows16(part);
+      // lanes of groups 1..3 hold the same sums: their offset is past the end
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow[j], G == 0 ? e * 4 : (int)(Vq[j] * 4), 0,
+                                            0);
+    }
   };
   // whole triples and unconditional loads keep the count of memory operations
   // in flight the same on every path, so each tile waits for its own loads
@@ -564,13 +584,22 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
     int64_t per_row = (512 + rows - 1) / rows;
     per_row = max((int64_t)1, min(ntiles, per_row));
     dim3 grid((unsigned)per_row, (unsigned)rows);
+    if (a.k_dt == DT_BF16 && a.Tq % 2 == 0) {
+      // query rows of one sequence in pairs: each key tile loaded once for both
+      const int64_t groups = rows / 2;
+      const int64_t pg = max((int64_t)1, min(ntiles, (512 + groups - 1) / groups));
+      hipLaunchKernelGGL(idx_scan_bf16_kernel<2>, dim3((unsigned)pg, (unsigned)groups), dim3(256), 0, st,
+                         reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
+                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
+      return hipGetLastError();
+    }
     if (a.k_dt == DT_FP8 || a.k_dt == DT_MXFP4)
       hipLaunchKernelGGL((a.k_dt == DT_FP8 ? idx_scan_lp_kernel<DT_FP8> : idx_scan_lp_kernel<DT_MXFP4>), grid,
                          dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx), a.w,
                          reinterpret_cast<const uint8_t*>(a.k_idx), reinterpret_cast<const uint32_t*>(a.k_scale),
                          a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
     else
-      hipLaunchKernelGGL(idx_scan_bf16_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx),
+      hipLaunchKernelGGL(idx_scan_bf16_kernel<1>, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx),
                          a.w, reinterpret_cast<const uint8_t*>(a.k_idx), a.q_pos, a.n_comp, a.Tq, a.N_max, a.m,
                          a.scores);
     return hipGetLastError();

@@ -172,6 +172,15 @@ def test_indexer_fp8_decode():
     _indexer_case(2, 1, 2100, [2100, 2100], [8399, 5000], 4, 256, "fp8", seed=11)
 
 
+def test_indexer_bf16_decode_query_pairs():
+    """Two and four query rows per sequence (a step with drafted tokens): the
+    scan serves rows in pairs per workgroup, with different visible counts
+    in a pair, a pair with nothing visible for its first row, and ragged
+    tails."""
+    _indexer_case(3, 2, 2300, [2300, 1777, 9], [9198, 9199, 5000, 7103, 2, 36], 4, 256, "bf16", seed=16)
+    _indexer_case(2, 4, 1500, [1500, 700], [5996, 5997, 5998, 5999, 100, 2799, 2800, 2803], 4, 128, "bf16", seed=17)
+
+
 def test_indexer_mxfp4_decode():
     # MXFP4 keys (OCP FP4 E2M1, E8M0 scale per 32 dims): ragged tail of the
     # 256-entry tiles, a short sequence

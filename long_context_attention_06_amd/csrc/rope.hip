@@ -13,8 +13,8 @@
 // row's sum of squares is a wave reduction; the rotated pairs are
 // (D-R+2i, D-R+2i+1), which never straddle a lane's 8 values. Angles
 // p * theta^(-2i/R) are formed and reduced in double precision (in fp32 the
-// product alone is off by up to 0.06 rad at p = 2^20); the rotation itself
-// runs in fp32.
+// product alone is off by up to 0.06 rad at p = 2^20), one pair per lane, and
+// reach the lanes that rotate by a shuffle; the rotation itself runs in fp32.
 #include "common.h"
 #include "kernels.h"
 
@@ -56,19 +56,30 @@ norm_rope_kernel(const void* __restrict__ x, void* __restrict__ out, const float
     for (int e = 0; e < 8; ++e) v[e] *= r * (gamma && live ? gamma[c0 + e] : 1.0f);
   }
   const int s0 = D - R;  // first rotated dim
-  if ((flags & (NR_ROPE | NR_ROPE_INV)) && live && c0 + 8 > s0) {
+  if (flags & (NR_ROPE | NR_ROPE_INV)) {
+    // pair i's angle, one pair per lane in rounds of 64 (R/2 pairs), handed
+    // to the lane that holds the pair by a lane shuffle
     const double p = (double)pos[row / H] * ((flags & NR_ROPE_INV) ? -1.0 : 1.0);
+    for (int base = 0; base < R / 2; base += 64) {
+      float cs_l = 1.0f, sn_l = 0.0f;
+      if (base + l < R / 2) {
+        double sn, cs;
+        sincos(p * exp2(-2.0 * (double)(base + l) / (double)R * log2_theta), &sn, &cs);
+        cs_l = (float)cs;
+        sn_l = (float)sn;
+      }
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int d = c0 + e;
-      if (d < s0) continue;
-      const int i = (d - s0) >> 1;
-      const double ang = p * exp2(-2.0 * (double)i / (double)R * log2_theta);
-      double sn, cs;
-      sincos(ang, &sn, &cs);
-      const float a = v[e], b = v[e + 1], c = (float)cs, s = (float)sn;
-      v[e] = a * c - b * s;
-      v[e + 1] = a * s + b * c;
+      for (int e = 0; e < 8; e += 2) {
+        const int i = (c0 + e - s0) >> 1;  // this lane's pair (negative: not rotated)
+        const bool mine = live && c0 + e >= s0 && i >= base && i < base + 64;
+        const int src = mine ? i - base : l;
+        const float c = __shfl(cs_l, src, 64), s = __shfl(sn_l, src, 64);
+        if (mine) {
+          const float a = v[e], b = v[e + 1];
+          v[e] = a * c - b * s;
+          v[e + 1] = a * s + b * c;
+        }
+      }
     }
   }
   if (!live) return;

@@ -147,6 +147,23 @@ int indexer_score(const void* q_idx, const float* w, const void* k_idx, const vo
                   int q_dt, int k_dt, float* scores, void* stream);
 
 /*
+ * csa_compress_indexer_score — a decode step's csa_compress and indexer_score
+ * in one call (the two are independent: the step's new entry is attended,
+ * not scored, in this step). Arguments are those of csa_compress followed by
+ * those of indexer_score (Bc is csa_compress's B, m_c its m); results are
+ * bit for bit those of the two calls. Where the scan takes the bf16-key path
+ * (Tq < 8) and the compression is bf16 in, bf16 or KV_FP8 out, with the
+ * overlap branch or m < 16, the compression's few workgroups ride in the
+ * scan's launch; otherwise the two run in turn.
+ */
+int csa_compress_indexer_score(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                               const float* Bb, void* kv_out, int64_t Bc, int64_t n_rows, int64_t tok_begin, int d,
+                               int m_c, int64_t blk_begin, int64_t blk_end, int64_t out_cap, int flags, int in_dt,
+                               int out_dt, const void* q_idx, const float* w, const void* k_idx, const void* k_scale,
+                               const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq, int H_I, int D_I,
+                               int64_t N_max, int m, int q_dt, int k_dt, float* scores, void* stream);
+
+/*
  * indexer_topk — top-k selection over indexer scores, [CSDN] CSA step 2.
  *
  * Row (b, t) keeps K' = min(top_k, V) entries with the largest scores among

@@ -45,6 +45,8 @@ _SIGS = {
     "csa_compress": ([_vp] * 7 + [_i64, _i64, _i64, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _vp], _i32),
     "indexer_score": ([_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp], _i32),
     "indexer_topk": ([_vp] * 3 + [_i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "csa_compress_indexer_score": ([_vp] * 7 + [_i64, _i64, _i64, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32]
+                                   + [_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp], _i32),
     "indexer_topk_workspace_bytes": ([_i64, _i64, _i64, _i32], _sz),
     "indexer_score_topk": ([_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
                                         _vp], _i32),
@@ -159,6 +161,24 @@ def indexer_score(q_idx, w, k_idx, k_scale, q_pos, n_comp, scores, *, m: int, st
     N_max = k_idx.shape[1]
     _check(lib.indexer_score(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q_pos), _ptr(n_comp), B, Tq,
                              H_I, D_I, N_max, m, _dt(q_idx), _dt(k_idx), _ptr(scores), _stream(stream)))
+
+
+def csa_compress_indexer_score(Ca, Cb, Za, Zb, Ba, Bb, kv_out, q_idx, w, k_idx, k_scale, q_pos, n_comp, scores, *,
+                               m_c: int, m: int, tok_begin: int = 0, blk_begin: int = 0, blk_end: Optional[int] = None,
+                               overlap: bool = True, joint: bool = False, stream=None) -> None:
+    """csa_compress(Ca .. Bb -> kv_out) and indexer_score(q_idx .. -> scores) in one call."""
+    Bc, n_rows, d = Ca.shape
+    out_cap = kv_out.shape[1]
+    if blk_end is None:
+        blk_end = (tok_begin + n_rows) // m_c
+    flags = (OVERLAP if overlap else 0) | (JOINT_SOFTMAX if joint else 0)
+    out_dt = KV_FP8 if kv_out.dtype == torch.uint8 and kv_out.shape[-1] == d + 64 else _dt(kv_out)
+    B, Tq, H_I, D_I = q_idx.shape
+    N_max = k_idx.shape[1]
+    _check(lib.csa_compress_indexer_score(
+        _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), _ptr(kv_out), Bc, n_rows, tok_begin, d, m_c,
+        blk_begin, blk_end, out_cap, flags, _dt(Ca), out_dt, _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale),
+        _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I, N_max, m, _dt(q_idx), _dt(k_idx), _ptr(scores), _stream(stream)))
 
 
 def indexer_topk_workspace_bytes(B: int, Tq: int, N_max: int, top_k: int) -> int:

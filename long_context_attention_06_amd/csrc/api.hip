@@ -116,9 +116,12 @@ int csa_hca_version(void) { return CSA_HCA_VERSION; }
 
 const char* csa_last_error(void) { return g_err.c_str(); }
 
-int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba, const float* Bb,
-                 void* out, int64_t B, int64_t n_rows, int64_t tok_begin, int d, int m, int64_t blk_begin,
-                 int64_t blk_end, int64_t out_cap, int flags, int in_dt, int out_dt, void* stream) {
+}  // extern "C"
+
+static int prep_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                         const float* Bb, void* out, int64_t B, int64_t n_rows, int64_t tok_begin, int d, int m,
+                         int64_t blk_begin, int64_t blk_end, int64_t out_cap, int flags, int in_dt, int out_dt,
+                         csa::CompressLaunch* L) {
   REQ((flags & ~(CSA_OVERLAP | CSA_JOINT_SOFTMAX)) == 0, CSA_INVALID_ARG, "unknown flags");
   const bool overlap = flags & CSA_OVERLAP, joint = flags & CSA_JOINT_SOFTMAX;
   REQ(!joint || overlap, CSA_INVALID_ARG, "CSA_JOINT_SOFTMAX needs CSA_OVERLAP");
@@ -149,8 +152,20 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
       "tensors must be 16-byte aligned");
   REQ(!overlap || (aligned16(Cb) && aligned16(Zb) && aligned16(Bb)), CSA_INVALID_ARG,
       "tensors must be 16-byte aligned");
-  csa::CompressLaunch a{Ca, Cb, Za, Zb, Ba, Bb, out, B, n_rows, tok_begin, blk_begin, blk_end, out_cap, d, m,
-                        overlap, joint, in_dt, out_dt};
+  *L = csa::CompressLaunch{Ca, Cb, Za, Zb, Ba, Bb, out, B, n_rows, tok_begin, blk_begin, blk_end, out_cap, d, m,
+                           overlap, joint, in_dt, out_dt};
+  return CSA_OK;
+}
+
+extern "C" {
+
+int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba, const float* Bb,
+                 void* out, int64_t B, int64_t n_rows, int64_t tok_begin, int d, int m, int64_t blk_begin,
+                 int64_t blk_end, int64_t out_cap, int flags, int in_dt, int out_dt, void* stream) {
+  csa::CompressLaunch a{};
+  int rc = prep_compress(Ca, Cb, Za, Zb, Ba, Bb, out, B, n_rows, tok_begin, d, m, blk_begin, blk_end, out_cap, flags,
+                         in_dt, out_dt, &a);
+  if (rc) return rc;
   return hip_status(csa::run_compress(a, (hipStream_t)stream), "csa_compress");
 }
 
@@ -162,6 +177,23 @@ int indexer_score(const void* q_idx, const float* w, const void* k_idx, const vo
   REQ(B * Tq * N_max == 0 || scores, CSA_INVALID_ARG, "scores must not be NULL");
   csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, scores};
   return hip_status(csa::run_indexer(a, (hipStream_t)stream), "indexer_score");
+}
+
+int csa_compress_indexer_score(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                               const float* Bb, void* kv_out, int64_t Bc, int64_t n_rows, int64_t tok_begin, int d,
+                               int m_c, int64_t blk_begin, int64_t blk_end, int64_t out_cap, int flags, int in_dt,
+                               int out_dt, const void* q_idx, const float* w, const void* k_idx, const void* k_scale,
+                               const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq, int H_I, int D_I,
+                               int64_t N_max, int m, int q_dt, int k_dt, float* scores, void* stream) {
+  csa::CompressLaunch c{};
+  int rc = prep_compress(Ca, Cb, Za, Zb, Ba, Bb, kv_out, Bc, n_rows, tok_begin, d, m_c, blk_begin, blk_end, out_cap,
+                         flags, in_dt, out_dt, &c);
+  if (rc) return rc;
+  rc = check_indexer(q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, q_dt, k_dt);
+  if (rc) return rc;
+  REQ(B * Tq * N_max == 0 || scores, CSA_INVALID_ARG, "scores must not be NULL");
+  csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, scores};
+  return hip_status(csa::run_compress_indexer(c, a, (hipStream_t)stream), "csa_compress_indexer_score");
 }
 
 size_t indexer_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k) {

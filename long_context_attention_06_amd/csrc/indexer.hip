@@ -21,6 +21,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "compress_entry.h"
 #include "kernels.h"
 
 namespace csa {
@@ -62,12 +63,21 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t codes, float scale)
 // heads are four 16-row M tiles of v_mfma_f32_16x16x32_bf16. With NQ = 2 a
 // workgroup serves two query rows of one sequence (a step with a drafted
 // token): each key tile is loaded once for both queries' 2 x 64 heads.
-template <int NQ>
+// With CO != 0 the grid's rows past scan_y are a decode step's compression
+// (bf16 in, output dtype CO): it has no dependence on the scan, so its few
+// workgroups run beside the scan's instead of in a launch of their own.
+template <int NQ, int CO>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                      const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
                      const int32_t* __restrict__ n_comp, int64_t Tq, int64_t N_max, int m,
-                     float* __restrict__ scores) {
+                     float* __restrict__ scores, CompressArgs ca, unsigned scan_y) {
+  if constexpr (CO != 0) {
+    if (blockIdx.y >= scan_y) {
+      compress_entry<DT_BF16, CO>(ca, ((int64_t)(blockIdx.y - scan_y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x);
+      return;
+    }
+  }
   constexpr int H = 64, DI = 128, KS = 4;               // k-steps of 32
   constexpr int KROW = DI * 2;                          // bytes per key row
   constexpr int TE = IDX_BF16_TE;                       // entries per tile (16 per wave)
@@ -588,9 +598,9 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
       // query rows of one sequence in pairs: each key tile loaded once for both
       const int64_t groups = rows / 2;
       const int64_t pg = max((int64_t)1, min(ntiles, (512 + groups - 1) / groups));
-      hipLaunchKernelGGL(idx_scan_bf16_kernel<2>, dim3((unsigned)pg, (unsigned)groups), dim3(256), 0, st,
+      hipLaunchKernelGGL((idx_scan_bf16_kernel<2, 0>), dim3((unsigned)pg, (unsigned)groups), dim3(256), 0, st,
                          reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
-                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
+                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)groups);
       return hipGetLastError();
     }
     if (a.k_dt == DT_FP8 || a.k_dt == DT_MXFP4)
@@ -599,9 +609,9 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
                          reinterpret_cast<const uint8_t*>(a.k_idx), reinterpret_cast<const uint32_t*>(a.k_scale),
                          a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
     else
-      hipLaunchKernelGGL(idx_scan_bf16_kernel<1>, grid, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx),
-                         a.w, reinterpret_cast<const uint8_t*>(a.k_idx), a.q_pos, a.n_comp, a.Tq, a.N_max, a.m,
-                         a.scores);
+      hipLaunchKernelGGL((idx_scan_bf16_kernel<1, 0>), grid, dim3(256), 0, st,
+                         reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
+                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)rows);
     return hipGetLastError();
   }
   // f32, D_I = 32, H_I <= 32
@@ -612,6 +622,49 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
   hipLaunchKernelGGL(idx_scan_f32_kernel, grid, dim3(256), 0, st, reinterpret_cast<const float*>(a.q_idx), a.w,
                      reinterpret_cast<const float*>(a.k_idx), a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.H_I,
                      a.scores);
+  return hipGetLastError();
+}
+
+// The compression rides in the bf16 scan's launch when the scan takes that
+// path and the standalone compression would use the same kernel (any overlap
+// compression, or m < 16: one thread per 8 channels), so the two give the
+// same bits; otherwise the two run in turn.
+hipError_t run_compress_indexer(const CompressLaunch& c, const IndexerLaunch& a, hipStream_t st) {
+  const int64_t rows = a.B * a.Tq;
+  const int64_t nblk = c.blk_end - c.blk_begin;
+  const bool scan_bf16 = a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16 && a.k_dt == DT_BF16 && a.Tq < 8;
+  const bool comp_ok = c.in_dt == DT_BF16 && (c.out_dt == DT_BF16 || c.out_dt == DT_KV_FP8) &&
+                       (c.overlap || c.m < 16) && c.B > 0 && nblk > 0;
+  if (!(scan_bf16 && comp_ok && rows > 0 && a.N_max > 0)) {
+    hipError_t e = run_compress(c, st);
+    if (e != hipSuccess) return e;
+    return run_indexer(a, st);
+  }
+  const int64_t ntiles = (a.N_max + IDX_BF16_TE - 1) / IDX_BF16_TE;
+  const int nq = a.Tq % 2 == 0 ? 2 : 1;
+  const int64_t sy = rows / nq;  // scan rows of the grid
+  const int64_t gx = max((int64_t)1, min(ntiles, (512 + sy - 1) / sy));
+  const int64_t cthreads = c.B * nblk * (c.d / 8);
+  const int64_t cy = (cthreads + gx * 256 - 1) / (gx * 256);  // compression rows of the grid
+  const CompressArgs ca = compress_args(c);
+  const dim3 grid((unsigned)gx, (unsigned)(sy + cy));
+  const auto* q = reinterpret_cast<const uint16_t*>(a.q_idx);
+  const auto* k = reinterpret_cast<const uint8_t*>(a.k_idx);
+  if (nq == 2) {
+    if (c.out_dt == DT_KV_FP8)
+      hipLaunchKernelGGL((idx_scan_bf16_kernel<2, DT_KV_FP8>), grid, dim3(256), 0, st, q, a.w, k, a.q_pos, a.n_comp,
+                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy);
+    else
+      hipLaunchKernelGGL((idx_scan_bf16_kernel<2, DT_BF16>), grid, dim3(256), 0, st, q, a.w, k, a.q_pos, a.n_comp,
+                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy);
+  } else {
+    if (c.out_dt == DT_KV_FP8)
+      hipLaunchKernelGGL((idx_scan_bf16_kernel<1, DT_KV_FP8>), grid, dim3(256), 0, st, q, a.w, k, a.q_pos, a.n_comp,
+                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy);
+    else
+      hipLaunchKernelGGL((idx_scan_bf16_kernel<1, DT_BF16>), grid, dim3(256), 0, st, q, a.w, k, a.q_pos, a.n_comp,
+                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy);
+  }
   return hipGetLastError();
 }
 

@@ -30,6 +30,9 @@ struct IndexerLaunch {
   float* scores;
 };
 hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st);
+// a decode step's compression and indexer scan in one launch where the scan
+// kernel can carry the compression's workgroups; otherwise the two in turn
+hipError_t run_compress_indexer(const CompressLaunch& c, const IndexerLaunch& a, hipStream_t st);
 
 struct TopkLaunch {
   const float* scores;

@@ -181,6 +181,46 @@ def test_indexer_bf16_decode_query_pairs():
     _indexer_case(2, 4, 1500, [1500, 700], [5996, 5997, 5998, 5999, 100, 2799, 2800, 2803], 4, 128, "bf16", seed=17)
 
 
+@pytest.mark.parametrize("kdt,kv,Tq", [("bf16", "bf16", 1), ("bf16", "fp8", 1), ("bf16", "bf16", 2),
+                                        ("fp8", "bf16", 1)])
+def test_compress_indexer_fused_equals_separate(kdt, kv, Tq):
+    """The one-call decode front (compression of the completed block and the
+    indexer scan) gives the bits of csa_compress followed by indexer_score;
+    E4M3 keys take the two launches in turn."""
+    _say("fused front", kdt, kv, Tq)
+    cfg = gen.scaled(gen.C2F if kv == "fp8" else gen.C2, B=4, n=16384, k_dtype=kdt, Tq=Tq)
+    x = gen.gen_decode(cfg)
+    B, N, m = cfg.B, cfg.N, cfg.m
+    kvt = dev if kv == "fp8" else bf
+    raw = [bf(x[nm]) for nm in ("Ca", "Cb", "Za", "Zb")]
+    Ba, Bb = dev(x["Ba"]), dev(x["Bb"])
+    if kdt == "fp8":
+        k_t, sc = dev(x["k_idx_codes"]), dev(x["k_scale"])
+    else:
+        k_t, sc = bf(x["k_idx"]), None
+    qi = bf(x["q_idx"] if Tq > 1 else x["q_idx"][:, None])
+    w = dev(x["w"] if Tq > 1 else x["w"][:, None])
+    pos = dev(np.tile(np.arange(cfg.n - Tq, cfg.n, dtype=np.int32), (B, 1)))
+    nc = dev(np.full((B,), N, np.int32))
+    outs = []
+    for fused in (False, True):
+        kvd = kvt(x["kv_comp"])
+        scores = torch.full((B, Tq, N), float("nan"), device=DEV)
+        kw = dict(tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
+        if fused:
+            L.csa_compress_indexer_score(*raw, Ba, Bb, kvd, qi, w, k_t, sc, pos, nc, scores, m_c=m, m=m, **kw)
+        else:
+            L.csa_compress(*raw, Ba, Bb, kvd, m=m, **kw)
+            L.indexer_score(qi, w, k_t, sc, pos, nc, scores, m=m)
+        torch.cuda.synchronize()
+        outs.append((host(kvd[:, N - 2:]), host(scores)))
+    assert np.array_equal(outs[0][0], outs[1][0]), "compressed entries differ"
+    a, b = outs[0][1], outs[1][1]
+    for t in range(Tq):
+        V = oracle.visible(cfg.n - Tq + t, N, m)
+        assert np.array_equal(a[:, t, :V], b[:, t, :V]), "scores differ"
+
+
 def test_indexer_mxfp4_decode():
     # MXFP4 keys (OCP FP4 E2M1, E8M0 scale per 32 dims): ragged tail of the
     # 256-entry tiles, a short sequence

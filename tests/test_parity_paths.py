@@ -57,8 +57,6 @@ def run_csa_decode(cfg, x):
     L = _L()
     B, N, m, k, W = cfg.B, cfg.N, cfg.m, cfg.top_k, cfg.W
     kv = _kv(cfg, x["kv_comp"])
-    L.csa_compress(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]), _t(x["Bb"]), kv, m=m,
-                   tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
     q_pos = _t(np.full((B, 1), cfg.n - 1, np.int32))
     n_comp = _t(np.full((B,), N, np.int32))
     scores = torch.empty((B, 1, N), dtype=torch.float32, device=DEV)
@@ -68,7 +66,10 @@ def run_csa_decode(cfg, x):
         k_t, sc = _t(x["k_idx_codes"]).view(torch.float4_e2m1fn_x2), _t(x["k_scale"])
     else:
         k_t, sc = _bf(x["k_idx"]), None
-    L.indexer_score(_bf(x["q_idx"][:, None]), _t(x["w"][:, None]), k_t, sc, q_pos, n_comp, scores, m=m)
+    # the completed block's entry and the scan in one call, as bench.py runs them
+    L.csa_compress_indexer_score(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]), _t(x["Bb"]), kv,
+                                 _bf(x["q_idx"][:, None]), _t(x["w"][:, None]), k_t, sc, q_pos, n_comp, scores,
+                                 m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
     idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
     L.indexer_topk(scores, q_pos, n_comp, idx, m=m)
     out = torch.empty((B, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
@@ -292,12 +293,12 @@ def check_csa_decode_multi(cfg, seqs):
     x = gen.gen_decode(cfg)
     B, N, m, k, W, Tq = cfg.B, cfg.N, cfg.m, cfg.top_k, cfg.W, cfg.Tq
     kv = _kv(cfg, x["kv_comp"])
-    L.csa_compress(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]), _t(x["Bb"]), kv, m=m,
-                   tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
     pos = np.tile(np.arange(cfg.n - Tq, cfg.n, dtype=np.int32), (B, 1))
     q_pos, n_comp = _t(pos), _t(np.full((B,), N, np.int32))
     scores = torch.empty((B, Tq, N), dtype=torch.float32, device=DEV)
-    L.indexer_score(_bf(x["q_idx"]), _t(x["w"]), _bf(x["k_idx"]), None, q_pos, n_comp, scores, m=m)
+    L.csa_compress_indexer_score(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]), _t(x["Bb"]), kv,
+                                 _bf(x["q_idx"]), _t(x["w"]), _bf(x["k_idx"]), None, q_pos, n_comp, scores, m_c=m,
+                                 m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
     idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
     L.indexer_topk(scores, q_pos, n_comp, idx, m=m)
     out = torch.empty((B, Tq, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)

@@ -205,13 +205,21 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
 // instruction, exact: every E4M3 value is a bf16 value); the scale multiplies
 // the head-weighted sum. Scores collect in LDS and are written out every
 // SC_TILES tiles: no store is in flight while DMA waits are counted.
-template <int KDT>
+// CO != 0: grid rows past scan_y are a decode step's compression, as in the
+// bf16 scan.
+template <int KDT, int CO>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 idx_scan_lp_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                    const uint8_t* __restrict__ k_idx, const uint32_t* __restrict__ k_scale,
                    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
-                   int64_t N_max, int m, float* __restrict__ scores) {
+                   int64_t N_max, int m, float* __restrict__ scores, CompressArgs ca, unsigned scan_y) {
   static_assert(KDT == DT_FP8 || KDT == DT_MXFP4, "low-precision keys");
+  if constexpr (CO != 0) {
+    if (blockIdx.y >= scan_y) {
+      compress_entry<DT_BF16, CO>(ca, ((int64_t)(blockIdx.y - scan_y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x);
+      return;
+    }
+  }
   constexpr bool MX = KDT == DT_MXFP4;
   constexpr int H = 64, DI = 128, KS = 4;   // k-steps of 32
   constexpr int KROW = MX ? DI / 2 : DI;    // bytes per key row
@@ -604,10 +612,10 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
       return hipGetLastError();
     }
     if (a.k_dt == DT_FP8 || a.k_dt == DT_MXFP4)
-      hipLaunchKernelGGL((a.k_dt == DT_FP8 ? idx_scan_lp_kernel<DT_FP8> : idx_scan_lp_kernel<DT_MXFP4>), grid,
+      hipLaunchKernelGGL((a.k_dt == DT_FP8 ? idx_scan_lp_kernel<DT_FP8, 0> : idx_scan_lp_kernel<DT_MXFP4, 0>), grid,
                          dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx), a.w,
                          reinterpret_cast<const uint8_t*>(a.k_idx), reinterpret_cast<const uint32_t*>(a.k_scale),
-                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
+                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)rows);
     else
       hipLaunchKernelGGL((idx_scan_bf16_kernel<1, 0>), grid, dim3(256), 0, st,
                          reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
@@ -632,10 +640,34 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
 hipError_t run_compress_indexer(const CompressLaunch& c, const IndexerLaunch& a, hipStream_t st) {
   const int64_t rows = a.B * a.Tq;
   const int64_t nblk = c.blk_end - c.blk_begin;
-  const bool scan_bf16 = a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16 && a.k_dt == DT_BF16 && a.Tq < 8;
+  const bool scan_dec = a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16 && a.Tq < 8;
   const bool comp_ok = c.in_dt == DT_BF16 && (c.out_dt == DT_BF16 || c.out_dt == DT_KV_FP8) &&
                        (c.overlap || c.m < 16) && c.B > 0 && nblk > 0;
-  if (!(scan_bf16 && comp_ok && rows > 0 && a.N_max > 0)) {
+  if (!(scan_dec && comp_ok && rows > 0 && a.N_max > 0)) {
+    hipError_t e = run_compress(c, st);
+    if (e != hipSuccess) return e;
+    return run_indexer(a, st);
+  }
+  const int64_t cthreads0 = c.B * nblk * (c.d / 8);
+  const CompressArgs ca0 = compress_args(c);
+  if (a.k_dt == DT_FP8 || a.k_dt == DT_MXFP4) {
+    // the low-precision scan: one row per workgroup row, as run_indexer lays it out
+    const int64_t te = a.k_dt == DT_FP8 ? 128 : 256;
+    const int64_t nt = (a.N_max + te - 1) / te;
+    const int64_t gx = max((int64_t)1, min(nt, (512 + rows - 1) / rows));
+    const int64_t cy = (cthreads0 + gx * 256 - 1) / (gx * 256);
+    const dim3 grid((unsigned)gx, (unsigned)(rows + cy));
+    const auto* q = reinterpret_cast<const uint16_t*>(a.q_idx);
+    const auto* k = reinterpret_cast<const uint8_t*>(a.k_idx);
+    const auto* ks = reinterpret_cast<const uint32_t*>(a.k_scale);
+    const bool f8 = a.k_dt == DT_FP8, o8 = c.out_dt == DT_KV_FP8;
+    auto kern = f8 ? (o8 ? idx_scan_lp_kernel<DT_FP8, DT_KV_FP8> : idx_scan_lp_kernel<DT_FP8, DT_BF16>)
+                   : (o8 ? idx_scan_lp_kernel<DT_MXFP4, DT_KV_FP8> : idx_scan_lp_kernel<DT_MXFP4, DT_BF16>);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, a.w, k, ks, a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores,
+                       ca0, (unsigned)rows);
+    return hipGetLastError();
+  }
+  if (a.k_dt != DT_BF16) {
     hipError_t e = run_compress(c, st);
     if (e != hipSuccess) return e;
     return run_indexer(a, st);

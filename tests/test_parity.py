@@ -182,11 +182,12 @@ def test_indexer_bf16_decode_query_pairs():
 
 
 @pytest.mark.parametrize("kdt,kv,Tq", [("bf16", "bf16", 1), ("bf16", "fp8", 1), ("bf16", "bf16", 2),
-                                        ("fp8", "bf16", 1)])
+                                        ("fp8", "bf16", 1), ("mxfp4", "fp8", 1), ("fp8", "bf16", 8)])
 def test_compress_indexer_fused_equals_separate(kdt, kv, Tq):
     """The one-call decode front (compression of the completed block and the
-    indexer scan) gives the bits of csa_compress followed by indexer_score;
-    E4M3 keys take the two launches in turn."""
+    indexer scan) gives the bits of csa_compress followed by indexer_score,
+    with bf16, E4M3 and MXFP4 keys; eight query rows (the many-query scan)
+    take the two launches in turn."""
     _say("fused front", kdt, kv, Tq)
     cfg = gen.scaled(gen.C2F if kv == "fp8" else gen.C2, B=4, n=16384, k_dtype=kdt, Tq=Tq)
     x = gen.gen_decode(cfg)
@@ -196,6 +197,8 @@ def test_compress_indexer_fused_equals_separate(kdt, kv, Tq):
     Ba, Bb = dev(x["Ba"]), dev(x["Bb"])
     if kdt == "fp8":
         k_t, sc = dev(x["k_idx_codes"]), dev(x["k_scale"])
+    elif kdt == "mxfp4":
+        k_t, sc = dev(x["k_idx_codes"]).view(torch.float4_e2m1fn_x2), dev(x["k_scale"])
     else:
         k_t, sc = bf(x["k_idx"]), None
     qi = bf(x["q_idx"] if Tq > 1 else x["q_idx"][:, None])

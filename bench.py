@@ -270,9 +270,10 @@ def main():
                          "m": m, "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I,
                          "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype,
                          "kv_dtype": cfg.kv_dtype, "qk_norm_rope": cfg.qk_rope, "query_tokens_per_sequence": Tq}
-        kname = {"fp8": "idx_scan_lp_kernel<2> (E4M3 keys)", "mxfp4": "idx_scan_lp_kernel<3> (MXFP4 keys)"}.get(
-            cfg.k_dtype, "idx_scan_bf16_kernel<2> (two query rows per workgroup)" if Tq % 2 == 0
-            else "idx_scan_bf16_kernel<1>")
+        # the scan alone (the step's launch also carries the compression: <.., 1|4>)
+        kname = {"fp8": "idx_scan_lp_kernel<2, 0> (E4M3 keys)", "mxfp4": "idx_scan_lp_kernel<3, 0> (MXFP4 keys)"}.get(
+            cfg.k_dtype, "idx_scan_bf16_kernel<2, 0> (two query rows per workgroup)" if Tq % 2 == 0
+            else "idx_scan_bf16_kernel<1, 0>")
         res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": round(scan_bytes / (scan_avg * 1e-3) / 1e9, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(scan_bytes / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

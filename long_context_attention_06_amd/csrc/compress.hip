@@ -33,19 +33,24 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
 // channels) of one block; lanes run along the channels, so a wave reads 256
 // contiguous bytes of four token rows.
 constexpr int CS_TOK = 8;    // tokens per slice
-constexpr int CS_SL = 16;    // slices per workgroup pass
 constexpr int CS_CG = 16;    // channel groups per workgroup
+// With few blocks (a decode step's append: one block per sequence) the
+// workgroups cover 4 channel groups and 64 slices of 2 tokens instead, so a
+// step of 16 sequences offers 256 workgroups rather than 64.
+constexpr int CS_TOK_FEW = 2, CS_CG_FEW = 4;
 
-template <int IN_DT, int OUT_DT>
+template <int IN_DT, int OUT_DT, int CG, int TOK>
 __global__ void __launch_bounds__(256)
 compress_split_kernel(const void* __restrict__ Ca, const void* __restrict__ Za, const float* __restrict__ Ba,
                       void* __restrict__ out, int64_t n_rows, int64_t tok_begin, int64_t blk_begin, int64_t nblk,
                       int64_t out_cap, int d, int m) {
-  __shared__ float part[3][CS_SL][CS_CG * 8];  // max, sum, weighted sum (exp2 domain)
+  constexpr int SL = 256 / CG;  // slices per workgroup pass
+  __shared__ float part[3][SL][CG * 8];  // max, sum, weighted sum (exp2 domain)
+  __shared__ float merged[CG * 8];
   const int groups = d / 8;
-  const int cgb = (groups + CS_CG - 1) / CS_CG;  // workgroups per block
-  const int cgl = threadIdx.x % CS_CG, sl = threadIdx.x / CS_CG;
-  const int cg = (int)(blockIdx.x % cgb) * CS_CG + cgl;
+  const int cgb = (groups + CG - 1) / CG;  // workgroups per block
+  const int cgl = threadIdx.x % CG, sl = threadIdx.x / CG;
+  const int cg = (int)(blockIdx.x % cgb) * CG + cgl;
   const int64_t t = blockIdx.x / cgb;
   const int64_t i = blk_begin + t % nblk;
   const int64_t b = t / nblk;
@@ -55,11 +60,11 @@ compress_split_kernel(const void* __restrict__ Ca, const void* __restrict__ Za, 
 
   SoftAcc A;
   A.init();
-  // slices sl, sl + 16, ... of the block; tokens past m are dropped
-  for (int j0 = sl * CS_TOK; j0 < m; j0 += CS_SL * CS_TOK) {
-    float z[CS_TOK][8], c[CS_TOK][8];
+  // slices sl, sl + SL, ... of the block; tokens past m are dropped
+  for (int j0 = sl * TOK; j0 < m; j0 += SL * TOK) {
+    float z[TOK][8], c[TOK][8];
 #pragma unroll
-    for (int u = 0; u < CS_TOK; ++u) {
+    for (int u = 0; u < TOK; ++u) {
       const int j = min(j0 + u, m - 1);  // a repeated token is masked below
       load8<IN_DT>(Za, (row0 + j) * d + c0, z[u]);
       load8<IN_DT>(Ca, (row0 + j) * d + c0, c[u]);
@@ -71,8 +76,13 @@ compress_split_kernel(const void* __restrict__ Ca, const void* __restrict__ Za, 
         z[u][4 + e] = j0 + u < m ? (z[u][4 + e] + b1[e]) * LOG2E_F : -INFINITY;
       }
     }
-    A.feed<4>(z, c);
-    A.feed<4>(z + 4, c + 4);
+    // the first group holds token j0 < m, so its maximum is finite
+    if constexpr (TOK >= 4) {
+#pragma unroll
+      for (int g = 0; g < TOK; g += 4) A.feed<4>(z + g, c + g);
+    } else {
+      A.feed<TOK>(z, c);
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -81,27 +91,26 @@ compress_split_kernel(const void* __restrict__ Ca, const void* __restrict__ Za, 
     part[2][sl][cgl * 8 + e] = A.acc[e];
   }
   __syncthreads();
-  // merge: thread cgl2 < 16 takes the 8 channels of its channel group
-  if (threadIdx.x >= CS_CG) return;
-  const int cgl2 = threadIdx.x;
-  const int cg2 = (int)(blockIdx.x % cgb) * CS_CG + cgl2;
-  if (cg2 >= groups) return;
-  float res[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int ch = cgl2 * 8 + e;
+  // merge: one thread per channel over the slices, in slice order
+  if (threadIdx.x < CG * 8) {
+    const int ch = threadIdx.x;
     float mx = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < CS_SL; ++q) mx = fmaxf(mx, part[0][q][ch]);
+    for (int q = 0; q < SL; ++q) mx = fmaxf(mx, part[0][q][ch]);
     float sm = 0.f, acc = 0.f;
-#pragma unroll
-    for (int q = 0; q < CS_SL; ++q) {
+    for (int q = 0; q < SL; ++q) {
       const float a = part[0][q][ch] == -INFINITY ? 0.f : exp2f(part[0][q][ch] - mx);
       sm += part[1][q][ch] * a;
       acc += part[2][q][ch] * a;
     }
-    res[e] = acc / sm;
+    merged[ch] = acc / sm;
   }
+  __syncthreads();
+  if (threadIdx.x >= CG) return;
+  const int cg2 = (int)(blockIdx.x % cgb) * CG + (int)threadIdx.x;
+  if (cg2 >= groups) return;
+  float res[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) res[e] = merged[threadIdx.x * 8 + e];
   store8<OUT_DT>(out, b * out_cap + i, d, cg2 * 8, res);
 }
 
@@ -115,8 +124,15 @@ static hipError_t launch(const CompressLaunch& a, hipStream_t st) {
   const int64_t nblk = a.blk_end - a.blk_begin;
   if (!a.overlap && a.m >= 2 * CS_TOK) {
     const int64_t grid = a.B * nblk * ((a.d / 8 + CS_CG - 1) / CS_CG);
-    hipLaunchKernelGGL((compress_split_kernel<IN_DT, OUT_DT>), dim3((unsigned)grid), dim3(256), 0, st, a.Ca, a.Za,
-                       a.Ba, a.out, a.n_rows, a.tok_begin, a.blk_begin, nblk, a.out_cap, a.d, a.m);
+    if (grid < 256 && a.m >= 64) {
+      const int64_t gf = a.B * nblk * ((a.d / 8 + CS_CG_FEW - 1) / CS_CG_FEW);
+      hipLaunchKernelGGL((compress_split_kernel<IN_DT, OUT_DT, CS_CG_FEW, CS_TOK_FEW>), dim3((unsigned)gf), dim3(256),
+                         0, st, a.Ca, a.Za, a.Ba, a.out, a.n_rows, a.tok_begin, a.blk_begin, nblk, a.out_cap, a.d,
+                         a.m);
+    } else {
+      hipLaunchKernelGGL((compress_split_kernel<IN_DT, OUT_DT, CS_CG, CS_TOK>), dim3((unsigned)grid), dim3(256), 0,
+                         st, a.Ca, a.Za, a.Ba, a.out, a.n_rows, a.tok_begin, a.blk_begin, nblk, a.out_cap, a.d, a.m);
+    }
     return hipGetLastError();
   }
   const int64_t total = a.B * nblk * (a.d / 8);

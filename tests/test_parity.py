@@ -224,6 +224,36 @@ def test_compress_indexer_fused_equals_separate(kdt, kv, Tq):
         assert np.array_equal(a[:, t, :V], b[:, t, :V]), "scores differ"
 
 
+def test_indexer_topk_maximum_entries():
+    """The largest cache the indexer takes (N_max just under 2^24, a ragged
+    tail): every visible score against the oracle (computed on the host in
+    chunks), and the exact top-k selection. Keys are seeded bf16 values drawn
+    on the device (the 4 GB key cache is too large for the host generator)."""
+    N_max, D_I, H_I, k = (1 << 24) - 5, 128, 64, 1024
+    _say("indexer max entries", N_max)
+    torch.manual_seed(123)
+    keys = torch.randn((1, N_max, D_I), device=DEV).to(torch.bfloat16)
+    g = _g(124)
+    q = gen.bf16_round(g.standard_normal((1, 1, H_I, D_I)).astype(np.float32) / math.sqrt(D_I))
+    w = g.standard_normal((1, 1, H_I)).astype(np.float32)
+    pos = np.array([[4 * N_max - 1]], np.int32)  # every entry visible with m = 4
+    nc = np.array([N_max], np.int32)
+    scores = torch.empty((1, 1, N_max), device=DEV)
+    L.indexer_score(bf(q), dev(w), keys, None, dev(pos), dev(nc), scores, m=4)
+    idx = torch.empty((1, 1, k), dtype=torch.int32, device=DEV)
+    L.indexer_topk(scores, dev(pos), dev(nc), idx, m=4)
+    torch.cuda.synchronize()
+    S, I = host(scores)[0, 0], host(idx)[0, 0]
+    ref = np.empty(N_max)
+    step = 1 << 21
+    for a in range(0, N_max, step):
+        kc = keys[0, a:a + step].to(torch.float32).cpu().numpy()
+        ref[a:a + len(kc)] = oracle.indexer_scores(q[0, 0], w[0, 0], kc, len(kc))
+    err = np.abs(S - ref).max()
+    assert err <= 2e-5 * 8 * (1 + np.abs(ref).max()), f"max score error {err:.2e}"
+    check_topk_row(I, oracle.topk_select(ref, k), ref, k, "max entries")
+
+
 def test_indexer_mxfp4_decode():
     # MXFP4 keys (OCP FP4 E2M1, E8M0 scale per 32 dims): ragged tail of the
     # 256-entry tiles, a short sequence

@@ -104,7 +104,7 @@ int check_topk(const float* scores, const int32_t* q_pos, const int32_t* n_comp,
   REQ(top_k >= 1, CSA_INVALID_ARG, "top_k must be >= 1");
   REQ(top_k <= 4096, CSA_UNSUPPORTED, "top_k above 4096");
   REQ(N_max <= (int64_t(1) << 24), CSA_UNSUPPORTED, "N_max above 2^24");
-  REQ(B * Tq <= 0x7fffffff, CSA_UNSUPPORTED, "too many rows");
+  REQ(B * Tq <= 65535, CSA_UNSUPPORTED, "B*Tq above 65535 rows per call");
   return CSA_OK;
 }
 

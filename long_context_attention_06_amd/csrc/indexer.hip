@@ -643,7 +643,10 @@ hipError_t run_compress_indexer(const CompressLaunch& c, const IndexerLaunch& a,
   const bool scan_dec = a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16 && a.Tq < 8;
   const bool comp_ok = c.in_dt == DT_BF16 && (c.out_dt == DT_BF16 || c.out_dt == DT_KV_FP8) &&
                        (c.overlap || c.m < 16) && c.B > 0 && nblk > 0;
-  if (!(scan_dec && comp_ok && rows > 0 && a.N_max > 0)) {
+  // the compression's grid rows go after the scan's: keep the total within
+  // the grid's y limit (at most ceil(threads / 256) rows, whatever the width)
+  const bool fits = rows + (c.B * nblk * (c.d / 8) + 255) / 256 <= 65535;
+  if (!(scan_dec && comp_ok && fits && rows > 0 && a.N_max > 0)) {
     hipError_t e = run_compress(c, st);
     if (e != hipSuccess) return e;
     return run_indexer(a, st);

@@ -104,6 +104,7 @@ def test_indexer_validation():
     t = L.lib.indexer_topk
     assert t(P, P, P, 1, 1, 100, 4, 0, P, None, None, 0, None) == L.INVALID_ARG
     assert t(P, P, P, 1, 1, 100, 4, 5000, P, None, None, 0, None) == L.UNSUPPORTED
+    assert t(P, P, P, 2, 40000, 100, 4, 16, P, None, None, 0, None) == L.UNSUPPORTED  # rows beyond the grid's y
     st = L.lib.indexer_score_topk
     need = L.indexer_score_topk_workspace_bytes(2, 3, 1000, 16)
     assert need >= 2 * 3 * 1000 * 4

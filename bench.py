@@ -545,7 +545,8 @@ def _threads():
 
 def cpu_baseline(cfg, x, budget_s: float):
     """The float64 oracle on the host cores, on whole sequences of the same
-    workload until the time budget is used (at least one sequence)."""
+    workload, cycling over the step's sequences until the time budget is
+    used (at least one sequence)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -559,8 +560,8 @@ def cpu_baseline(cfg, x, budget_s: float):
     done = 0
     t0 = time.perf_counter()
     m = cfg.m
-    while done < cfg.B and (done == 0 or time.perf_counter() - t0 < budget_s):
-        b = done
+    while done == 0 or time.perf_counter() - t0 < budget_s:
+        b = done % cfg.B
         if cfg.kind == "csa_decode":
             ent = oracle.compress(x["Ca"][b], x["Cb"][b], x["Za"][b], x["Zb"][b], x["Ba"], x["Bb"], m,
                                   blocks=range(1, 2))[0]
@@ -594,8 +595,8 @@ def cpu_baseline(cfg, x, budget_s: float):
         done += 1
     dt = time.perf_counter() - t0
     return {"value": round(done * cfg.Tq / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {cfg.B} sequences ({cfg.Tq} query token(s) each) of one decode step ({cfg.name}), float64 NumPy, "
-                      f"{dt:.1f}s"}
+            "sample": f"{done} sequences ({cfg.Tq} query token(s) each; the step's {cfg.B} taken in turn, "
+                      f"{done / cfg.B:.1f} steps) of a decode step ({cfg.name}), float64 NumPy, {dt:.1f}s"}
 
 
 if __name__ == "__main__":

@@ -160,9 +160,11 @@ def main():
     qn = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
     if cfg.kind == "csa_decode":
         k = cfg.top_k
-        scores = torch.empty((B, Tq, N), dtype=torch.float32, device=dev)
         idx = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
-        ws_t = torch.empty(max(1, L.indexer_topk_workspace_bytes(B, Tq, N, k)), dtype=torch.uint8, device=dev)
+        # scores, digit histograms and top-k scratch; zero-filled once, as the
+        # calls leave it (their histograms cleared after use)
+        ws_t = torch.zeros(L.indexer_score_topk_workspace_bytes(B, Tq, N, k), dtype=torch.uint8, device=dev)
+        scores = ws_t[:B * Tq * N * 4].view(torch.float32).view(B, Tq, N)
         ws_a = torch.empty(max(1, L.sparse_mqa_decode_multi_workspace_bytes(B, Tq, H, D, k, W)), dtype=torch.uint8,
                            device=dev)
     else:
@@ -181,14 +183,13 @@ def main():
             L.qk_norm_rope(r["q"], qn, shared["pos"], shared["q_gamma"], norm=True, rope=True, stream=s)
             q_att = qn
         if cfg.kind == "csa_decode":
-            # the completed block's entry and the indexer scan, one call (one launch for bf16 keys)
-            L.csa_compress_indexer_score(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"], r["kv_comp"],
-                                         r["q_idx"], r["w"], r["k_idx"], r.get("k_scale"), shared["q_pos"],
-                                         shared["n_comp"], scores, m_c=m, m=m, tok_begin=cfg.n - 2 * m,
-                                         blk_begin=N - 1, blk_end=N, stream=s)
+            # the completed block's entry, the indexer scan and the top-k: one call
+            L.csa_compress_indexer_score_topk(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"],
+                                              r["kv_comp"], r["q_idx"], r["w"], r["k_idx"], r.get("k_scale"),
+                                              shared["q_pos"], shared["n_comp"], idx, m_c=m, m=m,
+                                              tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, ws=ws_t, stream=s)
             rec(ev, 1)
             rec(ev, 2)
-            L.indexer_topk(scores, shared["q_pos"], shared["n_comp"], idx, m=m, ws=ws_t, stream=s)
             rec(ev, 3)
             if Tq > 1:
                 L.sparse_mqa_decode_multi(q_att, r["kv_comp"], idx, r["kv_win"], shared["win_len"], shared["sink"],
@@ -279,8 +280,8 @@ def main():
                            "frac": round(scan_bytes / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "traffic": _traffic(f"idx_scan_{a.workload}_traffic.txt", ["indexer.hip", "common.h"]),
                            "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_ms": round(scan_avg, 4)}
-        res["phases_ms"] = {"compress_and_indexer_scan": round(float(ph_mean[0] + ph_mean[1]), 4),
-                            "topk": round(float(ph_mean[2]), 4), "attention": round(attn_avg, 4)}
+        res["phases_ms"] = {"compress_indexer_scan_topk": round(float(ph_mean[0] + ph_mean[1] + ph_mean[2]), 4),
+                            "attention": round(attn_avg, 4)}
         res["step_hbm_gbs"] = round(step_bytes / (ms_step * 1e-3) / 1e9, 1)
         res["indexer_kv_hbm_gbs"] = res["roofline"]["achieved"]
     else:
@@ -334,10 +335,9 @@ def bench_prefill(a, torch, L, gen, dev, cfg):
     print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     T = gen.QCHUNK
     n_comp = td(np.array([N], np.int32))
-    scores = torch.empty((1, T, N), dtype=torch.float32, device=dev)
     idx = torch.empty((1, T, k), dtype=torch.int32, device=dev)
     out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
-    ws_t = torch.empty(max(1, L.indexer_topk_workspace_bytes(1, T, N, k)), dtype=torch.uint8, device=dev)
+    ws_t = torch.zeros(L.indexer_score_topk_workspace_bytes(1, T, N, k), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
 
@@ -346,9 +346,9 @@ def bench_prefill(a, torch, L, gen, dev, cfg):
         L.csa_compress(Ca, Cb, Za, Zb, Ba, Bb, comp, m=m, stream=s)
         if ev is not None: ev[1].record(stream)
         for c, ch in enumerate(chunks):
-            L.indexer_score(ch["q_idx"], ch["w"], k_idx, None, ch["q_pos"], n_comp, scores, m=m, stream=s)
+            L.indexer_score_topk(ch["q_idx"], ch["w"], k_idx, None, ch["q_pos"], n_comp, idx, m=m, ws=ws_t,
+                                 stream=s)
             if ev is not None: ev[2 + 3 * c].record(stream)
-            L.indexer_topk(scores, ch["q_pos"], n_comp, idx, m=m, ws=ws_t, stream=s)
             if ev is not None: ev[3 + 3 * c].record(stream)
             L.sparse_mqa_prefill(ch["q"], comp[0], idx[0], kv_tok, ch["q_pos"][0], sink, out, W=W, stream=s)
             if ev is not None: ev[4 + 3 * c].record(stream)
@@ -375,7 +375,7 @@ def bench_prefill(a, torch, L, gen, dev, cfg):
     fl = [prefill_flops(cfg, ch["pos_np"]) for ch in chunks]
     idx_fl, mqa_fl = sum(f[0] for f in fl), sum(f[1] for f in fl)
     total_fl = idx_fl + mqa_fl
-    idx_tfs = idx_fl / (sum(idx_ms) * 1e-3) / 1e12
+    idx_tfs = idx_fl / (sum(idx_ms) * 1e-3) / 1e12  # scores and top-k together
     mqa_tfs = mqa_fl / (sum(attn_ms) * 1e-3) / 1e12
     res = {
         "metric": METRIC, "value": round(cfg.n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,

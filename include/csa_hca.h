@@ -17,8 +17,9 @@
  *            (m=4, 64x128 indexer, top_k 512, m'=128, 64 heads x 512, window
  *            128) and section 5 (tokens after the last full block of m are not
  *            compressed).
- *   [WIKI]   DeepTech wiki summary, batch-invariance note: a token's output is
- *            bitwise the same wherever it sits in a batch.
+ *   [CSDN] section 八 (MegaMoE 超级内核与训练稳定性) also carries the
+ *            batch-invariance remark: a token's output is bitwise the same
+ *            wherever it sits in a batch.
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers owned by the caller, unless stated. The
@@ -148,8 +149,10 @@ int indexer_score(const void* q_idx, const float* w, const void* k_idx, const vo
 
 /*
  * csa_compress_indexer_score — a decode step's csa_compress and indexer_score
- * in one call (the two are independent: the step's new entry is attended,
- * not scored, in this step). Arguments are those of csa_compress followed by
+ * in one call. The two are independent: the scan reads the indexer keys (a
+ * separate input, one key per entry, which may include the new entry's),
+ * never the main-KV row being written, so kv_out must not overlap q_idx, w,
+ * k_idx, k_scale or scores (overlap is undefined). Arguments are those of csa_compress followed by
  * those of indexer_score (Bc is csa_compress's B, m_c its m); results are
  * bit for bit those of the two calls. Where the scan takes the bf16-key path
  * (Tq < 8) and the compression is bf16 in, bf16 or KV_FP8 out, with the
@@ -180,13 +183,45 @@ int indexer_topk(const float* scores, const int32_t* q_pos, const int32_t* n_com
 size_t indexer_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k);
 
 /* indexer_score_topk — indexer_score followed by indexer_topk, the scores
- * living in the workspace. Same arguments and support as the two calls. */
+ * living in the workspace. Same arguments and support as the two calls, and
+ * the same results.
+ * The workspace also carries, per query row, a 2048-bin histogram of the
+ * scores' top 11 bits that the scan fills and the top-k reads to find the bin
+ * holding the k-th score. The top-k counts the candidates it finds against
+ * the scores themselves, so the histogram is only a hint: results never
+ * depend on the workspace's contents on entry. Decode scans (Tq < 8) add to
+ * the histogram and the top-k clears it after use, so a call runs its fast
+ * path when the workspace was zero-filled once or last used by a call of the
+ * same shape; otherwise it selects from the full score rows (exact, slower).
+ * Prefill scans (Tq >= 8) write the histogram whole. */
 int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, const void* k_scale,
                        const int32_t* q_pos, const int32_t* n_comp,
                        int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int top_k,
                        int q_dt, int k_dt, int32_t* topk_idx, float* topk_score,
                        void* ws, size_t ws_bytes, void* stream);
 size_t indexer_score_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k);
+
+/*
+ * csa_compress_indexer_score_topk — a decode step's front half, [CSDN] CSA
+ * steps 1 and 2 in one call: csa_compress (the entry the new token completes)
+ * and indexer_score_topk. Arguments are those of csa_compress followed by
+ * those of indexer_score_topk (Bc is csa_compress's B, m_c its m); the
+ * workspace is indexer_score_topk_workspace_bytes(B, Tq, N_max, top_k) and
+ * behaves as there. Results are bit for bit those of the separate calls. The
+ * compression and the scan are independent: the scan reads the indexer keys,
+ * a separate input, never the main-KV row being written, so kv_out must not
+ * overlap q_idx, w, k_idx, k_scale or the workspace (overlap is undefined).
+ * Where the scan takes the bf16-key path (Tq < 8) and the compression is bf16
+ * in, bf16 or KV_FP8 out, with the overlap branch or m < 16, the
+ * compression's few workgroups ride in the scan's launch.
+ */
+int csa_compress_indexer_score_topk(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                                    const float* Bb, void* kv_out, int64_t Bc, int64_t n_rows, int64_t tok_begin,
+                                    int d, int m_c, int64_t blk_begin, int64_t blk_end, int64_t out_cap, int flags,
+                                    int in_dt, int out_dt, const void* q_idx, const float* w, const void* k_idx,
+                                    const void* k_scale, const int32_t* q_pos, const int32_t* n_comp, int64_t B,
+                                    int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt, int k_dt,
+                                    int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Shared-KV multi-query attention with a sink ([CSDN] CSA step 3 and HCA;

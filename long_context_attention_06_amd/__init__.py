@@ -47,6 +47,9 @@ _SIGS = {
     "indexer_topk": ([_vp] * 3 + [_i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "csa_compress_indexer_score": ([_vp] * 7 + [_i64, _i64, _i64, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32]
                                    + [_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp], _i32),
+    "csa_compress_indexer_score_topk": ([_vp] * 7 + [_i64, _i64, _i64, _i32, _i32, _i64, _i64, _i64, _i32, _i32,
+                                                      _i32] + [_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32,
+                                                                           _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "indexer_topk_workspace_bytes": ([_i64, _i64, _i64, _i32], _sz),
     "indexer_score_topk": ([_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
                                         _vp], _i32),
@@ -124,7 +127,9 @@ def _ws(nbytes: int, ws, device) -> tuple:
     if nbytes == 0:
         return None, 0
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        # zero-filled: a top-k workspace whose digit histogram starts at zero
+        # takes the fast path from the first call (results never depend on it)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     if ws.numel() * ws.element_size() < nbytes:
         return ws, ws.numel() * ws.element_size()
     return ws, ws.numel() * ws.element_size()
@@ -179,6 +184,29 @@ def csa_compress_indexer_score(Ca, Cb, Za, Zb, Ba, Bb, kv_out, q_idx, w, k_idx, 
         _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), _ptr(kv_out), Bc, n_rows, tok_begin, d, m_c,
         blk_begin, blk_end, out_cap, flags, _dt(Ca), out_dt, _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale),
         _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I, N_max, m, _dt(q_idx), _dt(k_idx), _ptr(scores), _stream(stream)))
+
+
+def csa_compress_indexer_score_topk(Ca, Cb, Za, Zb, Ba, Bb, kv_out, q_idx, w, k_idx, k_scale, q_pos, n_comp,
+                                    topk_idx, topk_score=None, *, m_c: int, m: int, tok_begin: int = 0,
+                                    blk_begin: int = 0, blk_end: Optional[int] = None, overlap: bool = True,
+                                    joint: bool = False, ws=None, stream=None) -> None:
+    """csa_compress(Ca .. Bb -> kv_out) and indexer_score_topk(q_idx .. -> topk_idx) in one call, the
+    scores living in the workspace (indexer_score_topk_workspace_bytes)."""
+    Bc, n_rows, d = Ca.shape
+    out_cap = kv_out.shape[1]
+    if blk_end is None:
+        blk_end = (tok_begin + n_rows) // m_c
+    flags = (OVERLAP if overlap else 0) | (JOINT_SOFTMAX if joint else 0)
+    out_dt = KV_FP8 if kv_out.dtype == torch.uint8 and kv_out.shape[-1] == d + 64 else _dt(kv_out)
+    B, Tq, H_I, D_I = q_idx.shape
+    N_max = k_idx.shape[1]
+    top_k = topk_idx.shape[-1]
+    ws, nb = _ws(indexer_score_topk_workspace_bytes(B, Tq, N_max, top_k), ws, q_idx.device)
+    _check(lib.csa_compress_indexer_score_topk(
+        _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), _ptr(kv_out), Bc, n_rows, tok_begin, d, m_c,
+        blk_begin, blk_end, out_cap, flags, _dt(Ca), out_dt, _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale),
+        _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I, N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(topk_idx),
+        _ptr(topk_score), _ptr(ws), nb, _stream(stream)))
 
 
 def indexer_topk_workspace_bytes(B: int, Tq: int, N_max: int, top_k: int) -> int:

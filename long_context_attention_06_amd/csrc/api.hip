@@ -198,7 +198,7 @@ int csa_compress_indexer_score(const void* Ca, const void* Cb, const void* Za, c
 
 size_t indexer_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k) {
   if (B < 0 || Tq < 0 || N_max < 0) return 0;
-  return round256(csa::topk_ws_bytes(B, Tq, N_max, top_k));
+  return round256(csa::topk_ws_bytes(B, Tq, N_max, top_k, false));
 }
 
 int indexer_topk(const float* scores, const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq,
@@ -209,13 +209,36 @@ int indexer_topk(const float* scores, const int32_t* q_pos, const int32_t* n_com
   const size_t need = indexer_topk_workspace_bytes(B, Tq, N_max, top_k);
   REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
   REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
-  csa::TopkLaunch a{scores, q_pos, n_comp, B, Tq, N_max, m, top_k, topk_idx, topk_score, ws, ws_bytes};
+  REQ(need == 0 || ((uintptr_t)ws & 255u) == 0, CSA_INVALID_ARG, "ws must be 256-byte aligned");
+  csa::TopkLaunch a{scores, q_pos, n_comp, B, Tq, N_max, m, top_k, topk_idx, topk_score, ws, ws_bytes,
+                    csa::TOPK_HINT_NONE};
   return hip_status(csa::run_topk(a, (hipStream_t)stream), "indexer_topk");
 }
 
 size_t indexer_score_topk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k) {
   if (B < 0 || Tq < 0 || N_max < 0) return 0;
-  return round256((size_t)B * Tq * N_max * 4) + indexer_topk_workspace_bytes(B, Tq, N_max, top_k);
+  return round256((size_t)B * Tq * N_max * 4) + round256(csa::topk_ws_bytes(B, Tq, N_max, top_k, true));
+}
+
+// The scan (scores into the workspace, plus the digit histogram and zeroed
+// counters the top-k reads), then the top-k.
+static int score_then_topk(const csa::CompressLaunch* c, csa::IndexerLaunch a, int top_k, int32_t* topk_idx,
+                           float* topk_score, void* ws, size_t ws_bytes, hipStream_t st, const char* what) {
+  const int64_t rows = a.B * a.Tq;
+  const size_t sbytes = round256((size_t)rows * a.N_max * 4);
+  a.scores = reinterpret_cast<float*>(ws);
+  uint8_t* tw = reinterpret_cast<uint8_t*>(ws) + sbytes;
+  const int mode = csa::indexer_hint_mode(a);
+  a.hint = mode != csa::TOPK_HINT_NONE ? reinterpret_cast<uint32_t*>(tw) : nullptr;
+  if (csa::topk_long_rows(a.N_max)) {
+    a.zero = reinterpret_cast<uint32_t*>(tw + csa::topk_counter_offset(rows, a.N_max));
+    a.zero_n = rows;
+  }
+  int rc = hip_status(c ? csa::run_compress_indexer(*c, a, st) : csa::run_indexer(a, st), what);
+  if (rc) return rc;
+  csa::TopkLaunch t{a.scores, a.q_pos, a.n_comp, a.B, a.Tq, a.N_max, a.m, top_k, topk_idx, topk_score,
+                    tw, ws_bytes - sbytes, mode};
+  return hip_status(csa::run_topk(t, st), what);
 }
 
 int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, const void* k_scale,
@@ -231,15 +254,36 @@ int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, con
   REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
   REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
   REQ(((uintptr_t)ws & 255u) == 0, CSA_INVALID_ARG, "ws must be 256-byte aligned");
-  float* scores = reinterpret_cast<float*>(ws);
-  const size_t sbytes = round256((size_t)B * Tq * N_max * 4);
-  csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, scores};
-  hipStream_t st = (hipStream_t)stream;
-  rc = hip_status(csa::run_indexer(a, st), "indexer_score_topk");
+  if (B * Tq == 0) return CSA_OK;
+  csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, nullptr};
+  return score_then_topk(nullptr, a, top_k, topk_idx, topk_score, ws, ws_bytes, (hipStream_t)stream,
+                         "indexer_score_topk");
+}
+
+int csa_compress_indexer_score_topk(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                                    const float* Bb, void* kv_out, int64_t Bc, int64_t n_rows, int64_t tok_begin,
+                                    int d, int m_c, int64_t blk_begin, int64_t blk_end, int64_t out_cap, int flags,
+                                    int in_dt, int out_dt, const void* q_idx, const float* w, const void* k_idx,
+                                    const void* k_scale, const int32_t* q_pos, const int32_t* n_comp, int64_t B,
+                                    int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt, int k_dt,
+                                    int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes, void* stream) {
+  csa::CompressLaunch c{};
+  int rc = prep_compress(Ca, Cb, Za, Zb, Ba, Bb, kv_out, Bc, n_rows, tok_begin, d, m_c, blk_begin, blk_end, out_cap,
+                         flags, in_dt, out_dt, &c);
   if (rc) return rc;
-  csa::TopkLaunch t{scores, q_pos, n_comp, B, Tq, N_max, m, top_k, topk_idx, topk_score,
-                    reinterpret_cast<uint8_t*>(ws) + sbytes, ws_bytes - sbytes};
-  return hip_status(csa::run_topk(t, st), "indexer_score_topk");
+  rc = check_indexer(q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, q_dt, k_dt);
+  if (rc) return rc;
+  REQ(B * Tq == 0 || topk_idx, CSA_INVALID_ARG, "topk_idx must not be NULL");
+  REQ(top_k >= 1, CSA_INVALID_ARG, "top_k must be >= 1");
+  REQ(top_k <= 4096, CSA_UNSUPPORTED, "top_k above 4096");
+  const size_t need = indexer_score_topk_workspace_bytes(B, Tq, N_max, top_k);
+  REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
+  REQ(((uintptr_t)ws & 255u) == 0, CSA_INVALID_ARG, "ws must be 256-byte aligned");
+  if (B * Tq == 0) return hip_status(csa::run_compress(c, (hipStream_t)stream), "csa_compress_indexer_score_topk");
+  csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, nullptr};
+  return score_then_topk(&c, a, top_k, topk_idx, topk_score, ws, ws_bytes, (hipStream_t)stream,
+                         "csa_compress_indexer_score_topk");
 }
 
 size_t sparse_mqa_decode_multi_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int top_k, int W) {

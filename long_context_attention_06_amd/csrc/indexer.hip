@@ -30,6 +30,20 @@ namespace csa {
 #define IDX_BF16_TE 64
 #endif
 
+// The scans also count, per query row, the scores by digit: the top 11 bits
+// of the order-preserving key (sign, exponent, two mantissa bits). The top-k
+// uses the counts to find the bin holding its threshold without a pass of its
+// own; it checks the counts against the scores, so they are a hint only.
+constexpr int DIG_BINS = 2048;
+constexpr int DIG_SHIFT = 21;
+
+// Workgroup (0, 0) of a scan zeroes the top-k's arrival counters (the scan
+// runs first in the call, so they are zero when the top-k starts).
+__device__ __forceinline__ void zero_counters(uint32_t* zero, int64_t n) {
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) zero[i] = 0u;
+}
+
 // XOR swizzle of the 16-byte chunk index of key row r in an LDS tile. The
 // operand reads take one chunk of each of 16 consecutive rows; with 64 banks
 // of 4 bytes those 16 chunks must fall in 16 different 16-byte bank groups.
@@ -71,7 +85,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                      const uint8_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
                      const int32_t* __restrict__ n_comp, int64_t Tq, int64_t N_max, int m,
-                     float* __restrict__ scores, CompressArgs ca, unsigned scan_y) {
+                     float* __restrict__ scores, CompressArgs ca, unsigned scan_y, uint32_t* __restrict__ hint,
+                     uint32_t* __restrict__ zero, int64_t zero_n) {
   if constexpr (CO != 0) {
     if (blockIdx.y >= scan_y) {
       compress_entry<DT_BF16, CO>(ca, ((int64_t)(blockIdx.y - scan_y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x);
@@ -83,6 +98,7 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
   constexpr int TE = IDX_BF16_TE;                       // entries per tile (16 per wave)
   static_assert(TE == 64, "one 16-entry N tile per wave");
   __shared__ __attribute__((aligned(16))) float lds_w[NQ * H];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_h[NQ * DIG_BINS];  // digit histogram per query row
 
   const int tid = threadIdx.x;
   const int l = tid & 63, wv = tid >> 6;
@@ -118,7 +134,10 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
     V = max(V, Vq[j]);
   }
   const int64_t ntiles = (V + TE - 1) / TE;
-  if ((int64_t)blockIdx.x >= ntiles) return;
+  if ((int64_t)blockIdx.x >= ntiles) {
+    zero_counters(zero, zero_n);
+    return;
+  }
   const int64_t nmine = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // tiles of this workgroup
 
   // query operand A[m = head][k]: lane (head mt*16 + l16, group G) holds dims
@@ -133,6 +152,8 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
       for (int s = 0; s < KS; ++s) qa[j][mt][s] = as_bf16x8(ld16(qp + s * 32));
     }
   if (tid < NQ * H) lds_w[tid] = w[row0 * H + tid];
+  if (hint)
+    for (int i = tid; i < NQ * DIG_BINS; i += 256) lds_h[i] = 0u;
   // wait for the query and the weights here, on every lane: left pending into
   // the loop, these loads would make each tile wait for all loads in flight
 #pragma unroll
@@ -179,6 +200,7 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
       // lanes of groups 1..3 hold the same sums: their offset is past the end
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow[j], G == 0 ? e * 4 : (int)(Vq[j] * 4), 0,
                                             0);
+      if (hint && G == 0 && e < Vq[j]) atomicAdd(&lds_h[j * DIG_BINS + (f32_key(part) >> DIG_SHIFT)], 1u);
     }
   };
   // whole triples and unconditional loads keep the count of memory operations
@@ -188,6 +210,14 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
     body(it, I0{}, I2{});
     body(it + 1, I1{}, I0{});
     body(it + 2, I2{}, I1{});
+  }
+  zero_counters(zero, zero_n);
+  if (hint) {
+    __syncthreads();
+    for (int i = tid; i < NQ * DIG_BINS; i += 256) {
+      const uint32_t v = lds_h[i];
+      if (v) atomicAdd(&hint[(row0 + i / DIG_BINS) * DIG_BINS + (i % DIG_BINS)], v);
+    }
   }
 }
 
@@ -212,7 +242,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 idx_scan_lp_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                    const uint8_t* __restrict__ k_idx, const uint32_t* __restrict__ k_scale,
                    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
-                   int64_t N_max, int m, float* __restrict__ scores, CompressArgs ca, unsigned scan_y) {
+                   int64_t N_max, int m, float* __restrict__ scores, CompressArgs ca, unsigned scan_y,
+                   uint32_t* __restrict__ hint, uint32_t* __restrict__ zero, int64_t zero_n) {
   static_assert(KDT == DT_FP8 || KDT == DT_MXFP4, "low-precision keys");
   if constexpr (CO != 0) {
     if (blockIdx.y >= scan_y) {
@@ -229,11 +260,14 @@ idx_scan_lp_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   constexpr int NBUF = 4;                   // 64 KB ring
   constexpr int DPW = TB / 1024 / 4;        // 1 KB DMAs per wave per tile
   constexpr int PER_TILE = DPW + 1;         // + the scales (one dword per entry)
-  constexpr int SC_TILES = 2048 / TE;       // score buffer (8 KB)
+  constexpr int SC_TILES = MX ? 6 : 16;     // score buffer (6 or 8 KB: two workgroups' LDS fit a CU)
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k[NBUF][TB];
   __shared__ __attribute__((aligned(16))) uint32_t lds_s[NBUF][TE];  // fp32 scale bits, or four E8M0 bytes
   __shared__ __attribute__((aligned(16))) float lds_sc[SC_TILES][TE];
   __shared__ __attribute__((aligned(16))) float lds_w[H];
+  // digit histogram, two 16-bit counts per word (a count that wraps only
+  // spoils the hint)
+  __shared__ __attribute__((aligned(16))) uint32_t lds_h[DIG_BINS / 2];
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -244,8 +278,13 @@ idx_scan_lp_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   int64_t V = min((int64_t)n_comp[b], ((int64_t)q_pos[row] + 1) / m);
   V = max((int64_t)0, min(V, N_max));
   const int64_t ntiles = (V + TE - 1) / TE;
-  if ((int64_t)blockIdx.x >= ntiles) return;
+  if ((int64_t)blockIdx.x >= ntiles) {
+    zero_counters(zero, zero_n);
+    return;
+  }
   const int64_t nmine = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // tiles of this workgroup
+  if (hint)
+    for (int i = tid; i < DIG_BINS / 2; i += 256) lds_h[i] = 0u;  // visible after the first barrier
 
   // query operand A[m = head][k]: lane (head mt*16 + l16, group G) holds dims
   // G*32 + s*8 + 0..7 for k-step s (a fixed permutation of the 128 dims,
@@ -360,12 +399,18 @@ idx_scan_lp_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
       part[n] = sum_rows16(part[n]);
     }
     if (G == 0) {
+      const int64_t tile = blockIdx.x + it * gridDim.x;
 #pragma unroll
       for (int n = 0; n < NE; ++n) {
         const int el = wv * (16 * NE) + n * 16 + l16;
         // fp8: sigma_i scales the head-weighted sum (ReLU commutes with a
         // positive scale); MXFP4 scales are already inside the key values
-        lds_sc[(it - it_flushed) % SC_TILES][el] = MX ? part[n] : part[n] * __uint_as_float(lds_s[buf][el]);
+        const float sc = MX ? part[n] : part[n] * __uint_as_float(lds_s[buf][el]);
+        lds_sc[(it - it_flushed) % SC_TILES][el] = sc;
+        if (hint && tile * TE + el < V) {
+          const uint32_t d = f32_key(sc) >> DIG_SHIFT;
+          atomicAdd(&lds_h[d >> 1], 1u << ((d & 1u) << 4));
+        }
       }
     }
     if (it + 1 - it_flushed == SC_TILES && it + 1 < nmine) {
@@ -376,6 +421,15 @@ idx_scan_lp_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   }
   __syncthreads();
   flush(it_flushed, nmine);
+  zero_counters(zero, zero_n);
+  if (hint) {
+    uint32_t* g = hint + row * DIG_BINS;
+    for (int i = tid; i < DIG_BINS / 2; i += 256) {
+      const uint32_t v = lds_h[i];
+      if (v & 0xffffu) atomicAdd(&g[2 * i], v & 0xffffu);
+      if (v >> 16) atomicAdd(&g[2 * i + 1], v >> 16);
+    }
+  }
 }
 
 // Prefill: many queries of one sequence. A workgroup of 8 waves owns 8
@@ -390,7 +444,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                    const uint8_t* __restrict__ k_idx, const uint32_t* __restrict__ k_scale,
                    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
-                   int64_t N_max, int m, float* __restrict__ scores) {
+                   int64_t N_max, int m, float* __restrict__ scores, uint32_t* __restrict__ hint,
+                   uint32_t* __restrict__ zero, int64_t zero_n) {
   constexpr int H = 64, DI = 128, KS = 4, QB = 8;
   constexpr bool MX = KDT == DT_MXFP4;
   constexpr int KROW = (KDT == DT_FP8) ? DI : MX ? DI / 2 : DI * 2;
@@ -402,6 +457,9 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][TB];
   __shared__ __attribute__((aligned(16))) uint32_t lds_ks[2][MX ? TE : 1];  // MXFP4: four E8M0 bytes per entry
   __shared__ __attribute__((aligned(16))) float lds_w[QB][H];
+  // each wave's row: digit histogram, two 16-bit counts per word (the wave
+  // sees its whole row, so the counts are exact unless one wraps)
+  __shared__ __attribute__((aligned(16))) uint32_t lds_h[QB][DIG_BINS / 2];
 
   const int tid = threadIdx.x;
   const int l = tid & 63, wv = tid >> 6;
@@ -428,7 +486,10 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
 #pragma unroll
   for (int i = 0; i < QB; ++i) Vmax = max(Vmax, lds_vmax[i]);
   const int64_t ntiles = (Vmax + TE - 1) / TE;
-  if (ntiles == 0) return;
+  zero_counters(zero, zero_n);
+  if (ntiles == 0) return;  // no row of this workgroup sees an entry: the top-k never reads their counts
+  if (hint)
+    for (int i = l; i < DIG_BINS / 2; i += 64) lds_h[wv][i] = 0u;
 
   bf16x8_t qa[4][KS];
 #pragma unroll
@@ -524,7 +585,14 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
       for (int nt = 0; nt < 4; ++nt) {
         const float v = sum_rows16(part[nt]);
         const int64_t e = tile * TE + nt * 16 + l16;
-        if (G == 0 && e < Vq) srow[e] = KDT == DT_FP8 ? v * __uint_as_float(k_scale[b * N_max + e]) : v;
+        if (G == 0 && e < Vq) {
+          const float sc = KDT == DT_FP8 ? v * __uint_as_float(k_scale[b * N_max + e]) : v;
+          srow[e] = sc;
+          if (hint) {
+            const uint32_t d = f32_key(sc) >> DIG_SHIFT;
+            atomicAdd(&lds_h[wv][d >> 1], 1u << ((d & 1u) << 4));
+          }
+        }
       }
     }
   };
@@ -533,6 +601,13 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   for (int64_t it = 0; it < ntiles; it += 2) {
     body(it, I0{});
     if (it + 1 < ntiles) body(it + 1, I1{});
+  }
+  if (hint && qok) {  // the row's whole histogram, unpacked (the wave's own LDS: no barrier needed)
+    uint32_t* g = hint + row * DIG_BINS;
+    for (int i = l; i < DIG_BINS / 2; i += 64) {
+      const uint32_t v = lds_h[wv][i];
+      *reinterpret_cast<u32x2_t*>(g + 2 * i) = u32x2_t{v & 0xffffu, v >> 16};
+    }
   }
 }
 
@@ -580,6 +655,11 @@ idx_scan_f32_kernel(const float* __restrict__ q_idx, const float* __restrict__ w
   }
 }
 
+int indexer_hint_mode(const IndexerLaunch& a) {
+  if (!(a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16)) return TOPK_HINT_NONE;  // the tiny fp32 scan counts nothing
+  return a.Tq >= 8 ? TOPK_HINT_WRITTEN : TOPK_HINT_ACCUMULATED;
+}
+
 hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
   const int64_t rows = a.B * a.Tq;
   if (rows == 0 || a.N_max == 0) return hipSuccess;
@@ -590,7 +670,7 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
                 : a.k_dt == DT_MXFP4 ? idx_prefill_kernel<DT_MXFP4> : idx_prefill_kernel<DT_BF16>;
     hipLaunchKernelGGL(kern, grid, dim3(512), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx), a.w,
                        reinterpret_cast<const uint8_t*>(a.k_idx), reinterpret_cast<const uint32_t*>(a.k_scale),
-                       a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores);
+                       a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, a.hint, a.zero, a.zero_n);
     return hipGetLastError();
   }
   if (a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16) {
@@ -608,18 +688,21 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
       const int64_t pg = max((int64_t)1, min(ntiles, (512 + groups - 1) / groups));
       hipLaunchKernelGGL((idx_scan_bf16_kernel<2, 0>), dim3((unsigned)pg, (unsigned)groups), dim3(256), 0, st,
                          reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
-                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)groups);
+                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)groups, a.hint,
+                         a.zero, a.zero_n);
       return hipGetLastError();
     }
     if (a.k_dt == DT_FP8 || a.k_dt == DT_MXFP4)
       hipLaunchKernelGGL((a.k_dt == DT_FP8 ? idx_scan_lp_kernel<DT_FP8, 0> : idx_scan_lp_kernel<DT_MXFP4, 0>), grid,
                          dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx), a.w,
                          reinterpret_cast<const uint8_t*>(a.k_idx), reinterpret_cast<const uint32_t*>(a.k_scale),
-                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)rows);
+                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)rows, a.hint,
+                         a.zero, a.zero_n);
     else
       hipLaunchKernelGGL((idx_scan_bf16_kernel<1, 0>), grid, dim3(256), 0, st,
                          reinterpret_cast<const uint16_t*>(a.q_idx), a.w, reinterpret_cast<const uint8_t*>(a.k_idx),
-                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)rows);
+                         a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)rows, a.hint,
+                         a.zero, a.zero_n);
     return hipGetLastError();
   }
   // f32, D_I = 32, H_I <= 32
@@ -667,7 +750,7 @@ hipError_t run_compress_indexer(const CompressLaunch& c, const IndexerLaunch& a,
     auto kern = f8 ? (o8 ? idx_scan_lp_kernel<DT_FP8, DT_KV_FP8> : idx_scan_lp_kernel<DT_FP8, DT_BF16>)
                    : (o8 ? idx_scan_lp_kernel<DT_MXFP4, DT_KV_FP8> : idx_scan_lp_kernel<DT_MXFP4, DT_BF16>);
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, a.w, k, ks, a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores,
-                       ca0, (unsigned)rows);
+                       ca0, (unsigned)rows, a.hint, a.zero, a.zero_n);
     return hipGetLastError();
   }
   if (a.k_dt != DT_BF16) {
@@ -688,17 +771,17 @@ hipError_t run_compress_indexer(const CompressLaunch& c, const IndexerLaunch& a,
   if (nq == 2) {
     if (c.out_dt == DT_KV_FP8)
       hipLaunchKernelGGL((idx_scan_bf16_kernel<2, DT_KV_FP8>), grid, dim3(256), 0, st, q, a.w, k, a.q_pos, a.n_comp,
-                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy);
+                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy, a.hint, a.zero, a.zero_n);
     else
       hipLaunchKernelGGL((idx_scan_bf16_kernel<2, DT_BF16>), grid, dim3(256), 0, st, q, a.w, k, a.q_pos, a.n_comp,
-                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy);
+                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy, a.hint, a.zero, a.zero_n);
   } else {
     if (c.out_dt == DT_KV_FP8)
       hipLaunchKernelGGL((idx_scan_bf16_kernel<1, DT_KV_FP8>), grid, dim3(256), 0, st, q, a.w, k, a.q_pos, a.n_comp,
-                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy);
+                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy, a.hint, a.zero, a.zero_n);
     else
       hipLaunchKernelGGL((idx_scan_bf16_kernel<1, DT_BF16>), grid, dim3(256), 0, st, q, a.w, k, a.q_pos, a.n_comp,
-                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy);
+                         a.Tq, a.N_max, a.m, a.scores, ca, (unsigned)sy, a.hint, a.zero, a.zero_n);
   }
   return hipGetLastError();
 }

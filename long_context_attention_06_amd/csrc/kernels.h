@@ -28,8 +28,15 @@ struct IndexerLaunch {
   int H_I, D_I, m;
   int q_dt, k_dt;
   float* scores;
+  // top-k support (nullable): the rows' digit histograms [B*Tq, 2048] that the
+  // scan adds to or writes (see indexer_hint_mode), and counters it zeroes
+  uint32_t* hint;
+  uint32_t* zero;
+  int64_t zero_n;
 };
 hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st);
+// TOPK_HINT_* that run_indexer produces for these arguments when hint is set
+int indexer_hint_mode(const IndexerLaunch& a);
 // a decode step's compression and indexer scan in one launch where the scan
 // kernel can carry the compression's workgroups; otherwise the two in turn
 hipError_t run_compress_indexer(const CompressLaunch& c, const IndexerLaunch& a, hipStream_t st);
@@ -44,8 +51,20 @@ struct TopkLaunch {
   float* out_score;
   void* ws;
   size_t ws_bytes;
+  // where the digit histogram at the start of ws comes from (TOPK_HINT_*)
+  int hint_mode;
 };
-size_t topk_ws_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k);
+enum {
+  TOPK_HINT_NONE = 0,         // no histogram: the top-k builds what it needs
+  TOPK_HINT_ACCUMULATED = 1,  // added to by this call's scan; the top-k clears it once consumed
+  TOPK_HINT_WRITTEN = 2,      // written whole by this call's scan
+};
+// from_scan: the call's scan provides the histogram (and zeroes the counters)
+size_t topk_ws_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k, bool from_scan);
+size_t topk_hint_bytes(int64_t rows, int64_t N_max, bool from_scan);
+// byte offset of the arrival counters in the top-k workspace (long rows)
+size_t topk_counter_offset(int64_t rows, int64_t N_max);
+bool topk_long_rows(int64_t N_max);
 hipError_t run_topk(const TopkLaunch& a, hipStream_t st);
 
 struct AttnLaunch {

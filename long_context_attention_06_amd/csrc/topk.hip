@@ -5,22 +5,37 @@
 // 1024 for Pro): for a query row with V visible scores, the K = min(k, V)
 // entries with the largest scores; equal scores go to the lower index, so the
 // set is unique. Indices are written in ascending order, the row padded with
-// -1. Batch invariance (DeepTech wiki, batch-invariance note) follows from the
-// algorithm: selection is exact, so the output depends on the row alone.
+// -1. Batch invariance (the same page, section 八, on the MegaMoE kernel and
+// training stability: a token's result must not depend on its batch) follows
+// from the algorithm: the selection is exact, so the output depends on the
+// row alone.
 //
-// Algorithm. A 1024-thread workgroup owns one chunk of up to 32768 keys of a
-// row, cached in LDS as order-preserving uint32 keys. A radix select with
-// integer LDS histograms finds the exact chunk-local K-th key T: digits of up
-// to 11 bits taken below the common prefix of the chunk's smallest and largest
-// key (at most three passes); each digit is chosen by one wave that holds the
-// bin counts in registers and scans them from the top. The chunk is then compacted in index order (per-wave
-// counts, a scan over waves, ballot prefix sums): all keys > T and the
-// lowest-index ties == T. A row that fits one chunk is finished in one launch.
-// A longer row writes each chunk's top K (key, index) pairs, in index order;
-// the union of the chunk winners contains the row's top K (an entry beaten by
-// K others inside its chunk is beaten by them in the row, ties included), so
-// the next launch selects again among the candidates, and repeats until one
-// chunk remains. No cross-workgroup atomics, no memory to clear.
+// Algorithm. Scores become order-preserving uint32 keys; the top 11 bits of
+// a key are its digit (sign, exponent, two mantissa bits: four bins per
+// binade). A 2048-bin digit histogram of the row names the threshold bin b:
+// fewer than K keys have a digit above b, at least K have a digit >= b. The
+// candidates -- every key with digit >= b, usually K plus a few hundred --
+// are compacted in index order (ballot prefix sums), and an exact radix
+// select among them finds the K-th key T and how many keys equal to T are
+// kept (the lowest-index ones). A last ordered pass writes the selection.
+//
+// The histogram is only a hint. The compaction counts the candidates
+// exactly; whenever they are fewer than K or too many for the buffer, the
+// row is selected exactly from the full score row instead. So a stale,
+// partial or garbage histogram can cost time but never changes a result,
+// and the workspace's contents on entry never matter.
+//
+// Workgroups are 256 threads (one wave per SIMD): every instruction of a
+// wave-uniform step then costs one issue per SIMD, not four. Rows of up to
+// 16384 keys: one workgroup per row holds the keys in registers and finishes
+// the row in one launch (topk_row_kernel), with the histogram passed in by
+// the prefill indexer or built with LDS atomics. Longer rows are spread over
+// 4096-key chunks: topk_filter_kernel compacts each chunk's candidates into a
+// per-chunk list, reading the row's histogram that the decode scan
+// accumulated (or topk_clear_kernel + topk_hist_kernel built);
+// topk_final_kernel gathers the lists in chunk order, selects, writes, and
+// clears the row's histogram for the next call. No result depends on the
+// order of any atomic operation.
 #include <algorithm>
 
 #include "common.h"
@@ -28,75 +43,93 @@
 
 namespace csa {
 
-constexpr int TK_NT = 1024;
+constexpr int TK_NT = 256;
 constexpr int TK_NW = TK_NT / 64;
 constexpr int TK_BINS = 2048;
-constexpr int TK_CHUNK_S = 32768;  // max scores per workgroup (128 KiB of LDS)
-constexpr int TK_CHUNK_C = 16384;  // max candidates per workgroup (keys + indices, 128 KiB)
-constexpr int TK_CHUNK_MIN = 4096;
-constexpr int TK_TARGET_WG = 256;  // workgroups a launch should offer (one per CU)
-enum { TK_SCORES = 0, TK_CANDS = 1 };
+constexpr int TK_BPL = TK_BINS / TK_NT;    // histogram bins per thread
+constexpr int TK_DSHIFT = 21;              // digit = key >> 21 (11 bits)
+constexpr int TK_ROW_MAX = 16384;          // keys of a row finished by one workgroup
+constexpr int TK_ROW_CAP = 4096;           // candidates of topk_row_kernel (32 KB of LDS)
+constexpr int TK_FCH = 4096;               // keys per chunk workgroup: four wave segments of 1024
+constexpr int TK_SEG = TK_FCH / TK_NW;     // keys per wave segment
+constexpr int TK_WCAP = 512;               // candidates kept per wave segment
+constexpr int TK_LDS_MAX = 160 * 1024;     // LDS of a workgroup on gfx950
+constexpr uint32_t TK_HINT_CLAMP = (1u << 20) - 1;  // keeps the bin sums inside int32
 
 __device__ __forceinline__ float key_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+__device__ __forceinline__ int below_cnt(uint64_t msk) {  // popcount of the mask's bits below this lane
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
+}
+// wave exclusive prefix and total of v in 0..7
+__device__ __forceinline__ int excl3(int v, int& total) {
+  const uint64_t b0 = __ballot(v & 1), b1 = __ballot(v & 2), b2 = __ballot(v & 4);
+  total = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+  return below_cnt(b0) + 2 * below_cnt(b1) + 4 * below_cnt(b2);
+}
+
 // Given the counts of the TK_BINS bins, find the bin b with (count above b) <
-// need <= (count of bins >= b). All threads take part: wave w scans bins
-// [TK_BINS - 128 (w+1), TK_BINS - 128 w) from the top, two per lane (one
-// inclusive scan over lanes), the waves' totals meet in tot[0..TK_NW), and
-// the lane holding the threshold publishes out[0] = b, out[1] = count above b,
-// out[2] = count of b. Ends with a barrier that publishes out[] and frees hist
-// and tot.
+// need <= (count of bins >= b). All threads take part: lane l of wave w holds
+// the eight bins below TK_BINS - 512 w - 8 l (one inclusive scan over lanes
+// of their sums), the waves' totals meet in tot[0..TK_NW), and the lane
+// holding the threshold publishes out[0] = b, out[1] = count above b, out[2] =
+// count of b. If no bin qualifies (the counts sum to less than need) out[] is
+// left as it was. Ends with a barrier that publishes out[] and frees hist and
+// tot.
 __device__ __forceinline__ void find_bin_block(const uint32_t* hist, int need, int* tot, int* out) {
-  static_assert(TK_BINS == 128 * TK_NW, "two bins per lane");
+  static_assert(TK_BPL == 8, "eight bins per lane");
   const int t = threadIdx.x, l = t & 63, wv = t >> 6;
-  const int hi = TK_BINS - 128 * wv - 2 * l - 1;  // this lane's upper bin; the lower one is hi - 1
-  const u32x2_t c2 = *reinterpret_cast<const u32x2_t*>(hist + hi - 1);
-  const int chi = (int)c2[1], clo = (int)c2[0], own = chi + clo;
+  const int lo = TK_BINS - 8 * (t + 1);  // this lane's lowest bin; its bins are lo .. lo + 7
+  const u32x4_t c0 = *reinterpret_cast<const u32x4_t*>(hist + lo);
+  const u32x4_t c1 = *reinterpret_cast<const u32x4_t*>(hist + lo + 4);
+  const int own = (int)(c0[0] + c0[1] + c0[2] + c0[3] + c1[0] + c1[1] + c1[2] + c1[3]);
   const int inc = wave_incl_scan_dpp(own);
   if (l == 63) tot[wv] = inc;
   __syncthreads();
   int above = inc - own;  // bins above this lane's, within the wave
 #pragma unroll
-  for (int q = 0; q < TK_NW / 4; ++q) {
-    const u32x4_t t4 = *reinterpret_cast<const u32x4_t*>(tot + 4 * q);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) above += 4 * q + e < wv ? (int)t4[e] : 0;
-  }
+  for (int u = 0; u < TK_NW; ++u) above += u < wv ? tot[u] : 0;
   if (above < need && need <= above + own) {
-    const bool upper = need <= above + chi;
-    out[0] = upper ? hi : hi - 1;
-    out[1] = upper ? above : above + chi;
-    out[2] = upper ? chi : clo;
+    const int c[8] = {(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3],
+                      (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+    int a = above, bin = lo, cb = c[0];
+    bool found = false;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {  // from the top bin down
+      if (!found && need <= a + c[i]) {
+        found = true;
+        bin = lo + i;
+        cb = c[i];
+      } else if (!found) {
+        a += c[i];
+      }
+    }
+    out[0] = bin;
+    out[1] = a;
+    out[2] = cb;
   }
   __syncthreads();
 }
 
 struct TopkArgs {
-  const float* scores;     // TK_SCORES: [rows, N_max]
-  const uint32_t* ckey;    // TK_CANDS: [rows, n_cand]
-  const int32_t* cidx;
+  const float* scores;     // [rows, N_max]
   const int32_t* q_pos;
   const int32_t* n_comp;
-  int64_t Tq, N_max, n_cand;
+  int64_t Tq, N_max;
   int m, top_k;
-  int chunk;               // keys per workgroup at this level
-  int32_t* out_idx;        // final: [rows, top_k]
-  float* out_score;        // final, nullable
-  uint32_t* nkey;          // next level: [rows, nchunk, top_k]
-  int32_t* nidx;
-  // threshold path: per-row threshold key, per-chunk candidates and counts
-  uint32_t* thr;           // [rows]
-  uint32_t* fkey;          // [rows, nfch * TK_FCH]
-  int32_t* fidx;
-  int32_t* fcnt;           // [rows, nfch]
-  int nfch;
+  int32_t* out_idx;        // [rows, top_k]
+  float* out_score;        // nullable
+  uint32_t* hint;          // [rows, TK_BINS] digit histogram; NULL: built by the row kernel
+  int clear_hint;          // the hint was accumulated by the scan: clear it once consumed
+  uint32_t* ctr;           // [rows] arrival counters of the chunk workgroups, zero on entry
+  uint32_t* wkey;          // [rows, nseg, TK_WCAP] candidates per wave segment
+  int32_t* widx;
+  int32_t* wcnt;           // [rows, nseg]; TK_WCAP + 1 marks an overflowing segment
+  int nseg;                // wave segments per row of N_max keys
+  int cap;                 // candidates the last workgroup of a row can hold (dynamic LDS)
 };
-
-constexpr int TK_FCH = 4096;     // keys per workgroup of the filter
-constexpr int TK_SAMPLE = 4096;  // scores sampled per row for the threshold
-constexpr int TK_FCH_MAX = 1024; // filter chunks per row the final kernel can gather
 
 __device__ __forceinline__ int64_t visible_of(const TopkArgs& a, int64_t row) {
   const int64_t b = row / a.Tq;
@@ -132,9 +165,7 @@ struct RowKeys {
 // Exact K-th largest key T of keys [0, n) (0 < K < n) and how many keys equal
 // to T belong to the top K (`need`). All threads call it. The digits start
 // below the common prefix of the smallest and largest key, so the first
-// histogram spreads over the keys' own range (a fixed top digit puts scores of
-// similar magnitude into a few bins, and the LDS atomics of a pass then
-// serialise on them).
+// histogram spreads over the keys' own range.
 template <class KS>
 __device__ void block_select(const KS& ks, int n, int K, uint32_t* hist, int* red, int* res, uint32_t& T,
                              int& need) {
@@ -181,7 +212,6 @@ __device__ void block_select(const KS& ks, int n, int K, uint32_t* hist, int* re
     auto add = [&](uint32_t k) {
       if (R >= 32 || (k >> R) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1u);
     };
-    // four 16-byte reads in flight per thread before their atomics
     for (int i0 = t; i0 < n4; i0 += 4 * TK_NT) {
       u32x4_t k4[4];
 #pragma unroll
@@ -209,9 +239,6 @@ __device__ void block_select(const KS& ks, int n, int K, uint32_t* hist, int* re
     }
     R = shift;
     if (R > 0) {
-      // another pass: find_bin_block's closing barrier freed the histogram
-      // (one buffer keeps the LDS of a 16K-key chunk small enough for two
-      // workgroups per CU)
       for (int i = t; i < TK_BINS; i += TK_NT) h[i] = 0;
       __syncthreads();
     }
@@ -261,14 +288,9 @@ __device__ void block_compact(const KS& ks, int n, int K, bool all, uint32_t T, 
   {
     int gs[TK_NW], es[TK_NW];
 #pragma unroll
-    for (int q = 0; q < TK_NW / 4; ++q) {
-      const u32x4_t g4 = *reinterpret_cast<const u32x4_t*>(red + 4 * q);
-      const u32x4_t e4 = *reinterpret_cast<const u32x4_t*>(red + TK_NW + 4 * q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gs[4 * q + e] = (int)g4[e];
-        es[4 * q + e] = (int)e4[e];
-      }
+    for (int u = 0; u < TK_NW; ++u) {
+      gs[u] = red[u];
+      es[u] = red[TK_NW + u];
     }
 #pragma unroll
     for (int u = 0; u < TK_NW; ++u) {
@@ -277,15 +299,6 @@ __device__ void block_compact(const KS& ks, int n, int K, bool all, uint32_t T, 
       eq_before += before ? es[u] : 0;
     }
   }
-  // popcount of the mask's bits below this lane (v_mbcnt_lo/hi)
-  auto below_cnt = [](uint64_t msk) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
-  };
-  auto excl3 = [&](int v, int& total) {  // wave exclusive prefix and total of v in 0..7
-    const uint64_t b0 = __ballot(v & 1), b1 = __ballot(v & 2), b2 = __ballot(v & 4);
-    total = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
-    return below_cnt(b0) + 2 * below_cnt(b1) + 4 * below_cnt(b2);
-  };
   int run_sel = 0, run_eq = 0;
   for (int base = s_lo; base < s_hi; base += 256) {
     const int i0 = base + 4 * l;
@@ -320,326 +333,494 @@ __device__ void block_compact(const KS& ks, int n, int K, bool all, uint32_t T, 
     run_eq += eq_tot;
   }
   for (int i = K + t; i < top_k; i += TK_NT) pad(i);
+  __syncthreads();  // red[] is free again
 }
 
-template <int SRC>
-__global__ void __launch_bounds__(TK_NT) topk_kernel(TopkArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-  uint32_t* hist = smem;                                   // TK_BINS
-  int* red = reinterpret_cast<int*>(smem + TK_BINS);       // 32
-  int* res = red + 32;                                     // 32
-  const int CH = a.chunk;
-  uint32_t* kc = smem + TK_BINS + 64;                      // CH keys
-  int32_t* ic = reinterpret_cast<int32_t*>(kc + CH);       // TK_CANDS: indices
-
-  const int t = threadIdx.x;
-  const int64_t row = blockIdx.y;
-  const int c = blockIdx.x, nchunk = gridDim.x;
-  const int64_t n_row = SRC == TK_SCORES ? visible_of(a, row) : a.n_cand;
-  const int64_t lo = (int64_t)c * CH;
-  const int n = (int)max((int64_t)0, min(n_row - lo, (int64_t)CH));
-  const int top_k = a.top_k;
-  const int K = min(top_k, n);
-  const bool final_out = nchunk == 1;
-
-  // ---- load the chunk: keys (and candidate indices) into LDS
-  if constexpr (SRC == TK_SCORES) {
-    const float* src = a.scores + row * a.N_max + lo;
-    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
-      const int n4 = n >> 2;
-      const f32x4_t* s4 = reinterpret_cast<const f32x4_t*>(src);
-      for (int i0 = t; i0 < n4; i0 += TK_NT * 4) {
-        f32x4_t v[4];
+// Keys held in registers by a TK_NT-thread workgroup: KPT per thread. Wave w
+// owns positions [lo + w*64*KPT, +64*KPT); in step j (KPT/4 steps) lane l
+// holds the four positions base_j + 4 l + e, base_j = lo + w*64*KPT + 256 j.
+template <int KPT>
+struct RegKeys {
+  static_assert(KPT % 4 == 0, "whole 16-byte steps");
+  uint32_t k[KPT];
+  __device__ __forceinline__ int pos(int lo, int j, int e) const {
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    return lo + w * 64 * KPT + 256 * j + 4 * l + e;
+  }
+  // keys of positions [lo, hi) of src (hi - lo <= TK_NT KPT); others read 0
+  // and are never candidates (the callers test positions against hi)
+  __device__ __forceinline__ void load(const float* src, int lo, int hi) {
+    const bool al = ((reinterpret_cast<uintptr_t>(src + lo)) & 15) == 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (i0 + u * TK_NT < n4) v[u] = s4[i0 + u * TK_NT];
+    for (int j = 0; j < KPT / 4; ++j) {
+      const int p = pos(lo, j, 0);
+      if (al && p + 3 < hi) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + p);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * TK_NT;
-          if (i < n4)
-            *reinterpret_cast<u32x4_t*>(kc + 4 * i) =
-                u32x4_t{f32_key(v[u][0]), f32_key(v[u][1]), f32_key(v[u][2]), f32_key(v[u][3])};
+        for (int e = 0; e < 4; ++e) k[4 * j + e] = f32_key(v[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) k[4 * j + e] = p + e < hi ? f32_key(src[p + e]) : 0u;
+      }
+    }
+  }
+};
+
+// Ordered compaction of the register keys whose position is below hi and
+// whose digit is at least b: their (key, position) pairs go to slots
+// [0, M) in position order through put(slot, key, pos) (called for slot <
+// cap only). Returns M, the exact candidate count (uniform). All threads call
+// it; red holds TK_NW ints; ends with a barrier after red is read.
+template <int KPT, class Put>
+__device__ int reg_compact(const RegKeys<KPT>& rk, int lo, int hi, uint32_t b, int cap, int* red, Put put) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int pre[KPT / 4];
+  int wtot = 0;
+#pragma unroll
+  for (int j = 0; j < KPT / 4; ++j) {
+    int n = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) n += (rk.pos(lo, j, e) < hi) && (rk.k[4 * j + e] >> TK_DSHIFT) >= b;
+    int st;
+    pre[j] = wtot + excl3(n, st);
+    wtot += st;
+  }
+  if (l == 0) red[w] = wtot;
+  __syncthreads();
+  int off = 0, M = 0;
+#pragma unroll
+  for (int u = 0; u < TK_NW; ++u) {
+    const int v = red[u];
+    off += u < w ? v : 0;
+    M += v;
+  }
+  if (M <= cap) {
+#pragma unroll
+    for (int j = 0; j < KPT / 4; ++j) {
+      int s = off + pre[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = rk.pos(lo, j, e);
+        if (p < hi && (rk.k[4 * j + e] >> TK_DSHIFT) >= b) {
+          put(s, rk.k[4 * j + e], p);
+          ++s;
         }
       }
-      for (int i = 4 * n4 + t; i < n; i += TK_NT) kc[i] = f32_key(src[i]);
-    } else {
-      for (int i = t; i < n; i += TK_NT) kc[i] = f32_key(src[i]);
-    }
-  } else {
-    const uint32_t* ks = a.ckey + row * a.n_cand + lo;
-    const int32_t* is = a.cidx + row * a.n_cand + lo;
-    if (((reinterpret_cast<uintptr_t>(ks) | reinterpret_cast<uintptr_t>(is)) & 15) == 0) {
-      const int n4 = n >> 2;
-      for (int i0 = t; i0 < n4; i0 += TK_NT * 2) {
-        u32x4_t kv[2], iv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          if (i0 + u * TK_NT < n4) {
-            kv[u] = reinterpret_cast<const u32x4_t*>(ks)[i0 + u * TK_NT];
-            iv[u] = reinterpret_cast<const u32x4_t*>(is)[i0 + u * TK_NT];
-          }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          if (i0 + u * TK_NT < n4) {
-            reinterpret_cast<u32x4_t*>(kc)[i0 + u * TK_NT] = kv[u];
-            reinterpret_cast<u32x4_t*>(ic)[i0 + u * TK_NT] = iv[u];
-          }
-      }
-      for (int i = 4 * n4 + t; i < n; i += TK_NT) {
-        kc[i] = ks[i];
-        ic[i] = is[i];
-      }
-    } else {
-      for (int i = t; i < n; i += TK_NT) {
-        kc[i] = ks[i];
-        ic[i] = is[i];
-      }
     }
   }
-  __syncthreads();  // publish the key cache
+  __syncthreads();  // red[] is free again; the puts are done
+  return M;
+}
 
-  const LdsKeys keys{kc};
+// The row's visible count is at most the top-k: every visible entry, in order.
+__device__ __forceinline__ void emit_all_visible(const TopkArgs& a, int64_t row, int V) {
+  const int64_t obase = row * (int64_t)a.top_k;
+  const float* src = a.scores + row * a.N_max;
+  for (int i = threadIdx.x; i < a.top_k; i += TK_NT) {
+    a.out_idx[obase + i] = i < V ? i : -1;
+    if (a.out_score) a.out_score[obase + i] = i < V ? src[i] : -INFINITY;
+  }
+}
+
+template <class KS, class Idx>
+__device__ __forceinline__ void write_selection(const TopkArgs& a, int64_t row, const KS& keys, int n, int K, bool all,
+                                                uint32_t T, int need, int* red, Idx idx_of) {
+  const int64_t obase = row * (int64_t)a.top_k;
+  block_compact(
+      keys, n, K, all, T, need, a.top_k, red,
+      [&](int pos, uint32_t key, int i) {
+        a.out_idx[obase + pos] = idx_of(i);
+        if (a.out_score) a.out_score[obase + pos] = key_f32(key);
+      },
+      [&](int i) {
+        a.out_idx[obase + i] = -1;
+        if (a.out_score) a.out_score[obase + i] = -INFINITY;
+      });
+}
+
+// Exact selection of the whole row from memory: the path taken when the
+// histogram hint does not hold (too few or too many candidates).
+__device__ void select_row_from_memory(const TopkArgs& a, int64_t row, int V, int K, uint32_t* hist, int* red,
+                                       int* res) {
+  const float* src = a.scores + row * a.N_max;
+  const RowKeys keys{src, V, (reinterpret_cast<uintptr_t>(src) & 15) == 0};
   uint32_t T = 0;
   int need = 0;
-  const bool all = K == n;
-  if (!all) block_select(keys, n, K, hist, red, res, T, need);
-  const int64_t obase = final_out ? row * (int64_t)top_k : (row * nchunk + c) * (int64_t)top_k;
-  auto emit = [&](int pos, uint32_t key, int i) {
-    const int32_t gi = SRC == TK_SCORES ? (int32_t)(lo + i) : ic[i];
-    if (final_out) {
-      a.out_idx[obase + pos] = gi;
-      if (a.out_score) a.out_score[obase + pos] = key_f32(key);
-    } else {
-      a.nkey[obase + pos] = key;
-      a.nidx[obase + pos] = gi;
-    }
-  };
-  auto pad = [&](int i) {
-    if (final_out) {
-      a.out_idx[obase + i] = -1;
-      if (a.out_score) a.out_score[obase + i] = -INFINITY;
-    } else {
-      a.nkey[obase + i] = 0u;  // below every finite key: never selected later
-      a.nidx[obase + i] = -1;
-    }
-  };
-  block_compact(keys, n, K, all, T, need, top_k, red, emit, pad);
+  block_select(keys, V, K, hist, red, res, T, need);
+  write_selection(a, row, keys, V, K, false, T, need, red, [](int i) { return (int32_t)i; });
 }
 
-// ----------------------------------------------------------------------------
-// Threshold path for long rows (one sample select, one filter, one select)
-// ----------------------------------------------------------------------------
-// 1. topk_threshold_kernel: per row, the exact r-th largest key T_s of an
-//    evenly spaced sample of TK_SAMPLE scores, r chosen so that about 2 K of
-//    the row's scores lie at or above it. Rows that fit the final kernel take
-//    T_s = 0 (every key).
-// 2. topk_filter_kernel: per 4096-key chunk, the keys >= T_s with their
-//    positions, compacted in position order, and their count.
-// 3. topk_filtered_kernel: per row, the chunks' candidates gathered in chunk
-//    order (so in position order) and selected exactly. If the sample misled
-//    (fewer than K' candidates, or more than fit in LDS), it selects over the
-//    whole row read from memory instead. Either way the result is the exact
-//    top K'.
-__global__ void __launch_bounds__(TK_NT) topk_threshold_kernel(TopkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
-  __shared__ __attribute__((aligned(16))) int red[32], res[32];
-  __shared__ __attribute__((aligned(16))) uint32_t kc[TK_SAMPLE];
+// Block sum of one int per thread (uniform result); red holds TK_NW ints.
+__device__ __forceinline__ int block_sum(int v, int* red) {
+  v = wave_sum_dpp(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int u = 0; u < TK_NW; ++u) s += red[u];
+  __syncthreads();
+  return s;
+}
+
+// The K-th key among M candidates cached in LDS (keys ck, position order),
+// the candidates being every key whose digit is at least b, and write the
+// row. The threshold lies in digit b when fewer than K candidates have a
+// larger digit; the next 11 bits of the keys of digit b then name its
+// sub-bin, and (unless the sub-bin is taken whole) the last 10 bits the key
+// itself: one or two histogram passes over the candidates. Any inconsistency
+// (a hint that did not hold) falls back to a full radix select over the
+// candidates, which contain the top K either way.
+template <class Idx>
+__device__ void select_in_candidates(const TopkArgs& a, int64_t row, const uint32_t* ck, int M, int K, int b,
+                                     uint32_t* hist, int* red, int* res, Idx idx_of) {
   const int t = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const int64_t V = visible_of(a, row);
-  if (V <= TK_CHUNK_C) {
-    if (t == 0) a.thr[row] = 0u;
+  const LdsKeys keys{ck};
+  if (M == K) {
+    write_selection(a, row, keys, M, K, true, 0u, 0, red, idx_of);
     return;
   }
-  const int K = min((int64_t)a.top_k, V);
-  const float* src = a.scores + row * a.N_max;
-  for (int i = t; i < TK_SAMPLE; i += TK_NT) kc[i] = f32_key(src[(int64_t)i * V / TK_SAMPLE]);
-  __syncthreads();
-  const int r = (int)min((int64_t)(TK_SAMPLE - 1), (2 * (int64_t)K * TK_SAMPLE + V - 1) / V + 8);
-  uint32_t T;
-  int need;
-  block_select(LdsKeys{kc}, TK_SAMPLE, r, hist, red, res, T, need);
-  if (t == 0) a.thr[row] = T;
+  uint32_t T = 0;
+  int need = 0;
+  bool done = false;
+  if (b >= 0) {
+    for (int i = t; i < TK_BINS; i += TK_NT) hist[i] = 0;
+    __syncthreads();
+    int above = 0;
+    for (int i = t; i < M; i += TK_NT) {
+      const uint32_t k = ck[i];
+      const int d = (int)(k >> TK_DSHIFT);
+      above += d > b;
+      if (d == b) atomicAdd(&hist[(k >> 10) & (TK_BINS - 1)], 1u);
+    }
+    above = block_sum(above, red);  // its barriers also publish the histogram
+    const int need1 = K - above;
+    if (need1 > 0) {
+      if (t == 0) res[0] = -1;
+      __syncthreads();
+      find_bin_block(hist, need1, red, res);
+      const int s2 = res[0];
+      const uint32_t P = ((uint32_t)b << 11) | (uint32_t)max(s2, 0);  // 22-bit key prefix
+      if (s2 >= 0 && P > 0) {
+        const int need2 = need1 - res[1];
+        if (need2 == res[2]) {
+          T = (P << 10) - 1u;  // the sub-bin is taken whole
+          need = 0;
+          done = true;
+        } else {
+          for (int i = t; i < TK_BINS; i += TK_NT) hist[i] = 0;
+          __syncthreads();
+          for (int i = t; i < M; i += TK_NT) {
+            const uint32_t k = ck[i];
+            if ((k >> 10) == P) atomicAdd(&hist[k & 1023u], 1u);
+          }
+          if (t == 0) res[0] = -1;
+          __syncthreads();
+          find_bin_block(hist, need2, red, res);
+          if (res[0] >= 0) {
+            T = (P << 10) | (uint32_t)res[0];
+            need = need2 - res[1];
+            done = true;
+          }
+        }
+      }
+    }
+  }
+  if (!done) block_select(keys, M, K, hist, red, res, T, need);
+  write_selection(a, row, keys, M, K, false, T, need, red, idx_of);
 }
 
-__global__ void __launch_bounds__(TK_NT) topk_filter_kernel(TopkArgs a) {
-  __shared__ int wtot[TK_NW];
+// Copy a row's histogram hint into LDS, clamping each bin so that any sum of
+// bins stays inside int32 (a clamped bin only weakens the hint).
+__device__ __forceinline__ void load_hint(const uint32_t* h, uint32_t* hist) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < TK_BPL / 4; ++u) {
+    const u32x4_t v = reinterpret_cast<const u32x4_t*>(h)[t + u * TK_NT];
+    reinterpret_cast<u32x4_t*>(hist)[t + u * TK_NT] =
+        u32x4_t{min(v[0], TK_HINT_CLAMP), min(v[1], TK_HINT_CLAMP), min(v[2], TK_HINT_CLAMP), min(v[3], TK_HINT_CLAMP)};
+  }
+}
+__device__ __forceinline__ void clear_hint(uint32_t* h) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < TK_BPL / 4; ++u) reinterpret_cast<u32x4_t*>(h)[t + u * TK_NT] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
+// ----------------------------------------------------------------------------
+// Rows of up to TK_ROW_MAX keys: one workgroup per row, keys in registers
+// ----------------------------------------------------------------------------
+template <int KPT>
+__global__ void __launch_bounds__(TK_NT) topk_row_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
+  __shared__ __attribute__((aligned(16))) int red[2 * TK_NW], res[4];
+  __shared__ __attribute__((aligned(16))) uint32_t ck[TK_ROW_CAP];
+  __shared__ __attribute__((aligned(16))) int32_t ci[TK_ROW_CAP];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int V = (int)visible_of(a, row);
+  const int K = min(a.top_k, V);
+  uint32_t* h = a.hint ? a.hint + row * TK_BINS : nullptr;
+  if (K == V) {
+    emit_all_visible(a, row, V);
+    if (h && a.clear_hint) clear_hint(h);
+    return;
+  }
+  const float* src = a.scores + row * a.N_max;
+  RegKeys<KPT> rk;
+  rk.load(src, 0, V);
+  // digit histogram of the row (exact), or its hint
+  if (h) {
+    load_hint(h, hist);
+  } else {
+    for (int i = t; i < TK_BINS; i += TK_NT) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (rk.pos(0, j, e) < V) atomicAdd(&hist[rk.k[4 * j + e] >> TK_DSHIFT], 1u);
+  }
+  if (t == 0) res[0] = -1;
+  __syncthreads();
+  find_bin_block(hist, K, red, res);
+  const int b = res[0];
+  int M = -1;
+  if (b >= 0)
+    M = reg_compact(rk, 0, V, (uint32_t)b, TK_ROW_CAP, red, [&](int s, uint32_t key, int p) {
+      ck[s] = key;
+      ci[s] = p;
+    });
+  if (h && a.clear_hint) clear_hint(h);  // consumed: cleared for the next call
+  if (M >= K && M <= TK_ROW_CAP)
+    select_in_candidates(a, row, ck, M, K, b, hist, red, res, [&](int i) { return ci[i]; });
+  else
+    select_row_from_memory(a, row, V, K, hist, red, res);
+}
+
+// ----------------------------------------------------------------------------
+// Longer rows: per-chunk candidates, the row's last workgroup selects
+// ----------------------------------------------------------------------------
+// Zeroes the hint and the arrival counters of every row (top-k without a
+// histogram from the scan).
+__global__ void __launch_bounds__(TK_NT) topk_clear_kernel(uint32_t* hint, uint32_t* ctr, int rows) {
+  clear_hint(hint + (int64_t)blockIdx.x * TK_BINS);
+  if (threadIdx.x == 0) ctr[blockIdx.x] = 0u;
+  (void)rows;
+}
+
+// Digit histogram of chunk blockIdx.x (16 TK_NT keys) of row blockIdx.y, added
+// to the row's histogram (integer atomics: the sums do not depend on order).
+__global__ void __launch_bounds__(TK_NT) topk_hist_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
+  const int t = threadIdx.x;
+  const int64_t row = blockIdx.y;
+  const int V = (int)visible_of(a, row);
+  const int lo = blockIdx.x * (16 * TK_NT);
+  if (lo >= V) return;
+  const int hi = min(V, lo + 16 * TK_NT);
+  for (int i = t; i < TK_BINS; i += TK_NT) hist[i] = 0;
+  RegKeys<16> rk;
+  rk.load(a.scores + row * a.N_max, lo, hi);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (rk.pos(lo, j, e) < hi) atomicAdd(&hist[rk.k[4 * j + e] >> TK_DSHIFT], 1u);
+  __syncthreads();
+  uint32_t* g = a.hint + row * TK_BINS;
+  for (int i = t; i < TK_BINS; i += TK_NT)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
+
+// Chunk blockIdx.x (TK_FCH keys) of row blockIdx.y. Each wave compacts the
+// candidates of its 1024-key segment -- keys whose digit is at least the
+// threshold bin of the row's histogram hint; every chunk reads the same hint,
+// so all agree on the bin -- into its own list, in position order (a ballot
+// prefix inside the wave; no workgroup barrier). The workgroup that arrives
+// last at the row's counter then gathers every list in segment order and
+// selects the row. Rows with K = V are written by chunk 0.
+__host__ __device__ constexpr int seg_words(int nseg) { return (nseg + 8 + 3) & ~3; }
+
+// The lists and counts the chunks hand to the row's last workgroup travel by
+// device-coherent accesses (relaxed device-scope atomics: the per-XCD L2
+// caches are not coherent with each other, and these loads and stores bypass
+// them), so the hand-over needs no L2 write-back or invalidation: a chunk
+// waits for its own stores to complete before it counts its arrival.
+template <class T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void __launch_bounds__(TK_NT) topk_chunk_kernel(TopkArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  uint32_t* hist = smem;                                      // TK_BINS
+  int* red = reinterpret_cast<int*>(smem + TK_BINS);          // 2 TK_NW
+  int* res = red + 2 * TK_NW;                                 // 4, then the last-arrival flag (+ pad)
+  int* off = res + 8;                                         // nseg segment offsets (+ pad)
+  uint32_t* ck = reinterpret_cast<uint32_t*>(off + seg_words(a.nseg));  // cap keys
+  int32_t* ci = reinterpret_cast<int32_t*>(ck + a.cap);              // and positions
   const int t = threadIdx.x, l = t & 63, wv = t >> 6;
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
-  const int64_t V = visible_of(a, row);
-  const int64_t lo = (int64_t)c * TK_FCH;
-  const int n = (int)max((int64_t)0, min(V - lo, (int64_t)TK_FCH));
-  const uint32_t thr = a.thr[row];
-  const float* src = a.scores + row * a.N_max + lo;
-  const int p = 4 * t;
-  u32x4_t k4;
-  if ((reinterpret_cast<uintptr_t>(src) & 15) == 0 && p + 3 < n) {
-    const f32x4_t v = reinterpret_cast<const f32x4_t*>(src)[t];
-    k4 = u32x4_t{f32_key(v[0]), f32_key(v[1]), f32_key(v[2]), f32_key(v[3])};
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) k4[e] = p + e < n ? f32_key(src[p + e]) : 0u;
-  }
-  bool sel[4];
-  int ns = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    sel[e] = p + e < n && k4[e] >= thr;
-    ns += sel[e];
-  }
-  auto below_cnt = [](uint64_t msk) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
-  };
-  const uint64_t b0 = __ballot(ns & 1), b1 = __ballot(ns & 2), b2 = __ballot(ns & 4);
-  const int wsum = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
-  int pos = below_cnt(b0) + 2 * below_cnt(b1) + 4 * below_cnt(b2);
-  if (l == 0) wtot[wv] = wsum;
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int u = 0; u < TK_NW; ++u) {
-    const int v = wtot[u];
-    pos += u < wv ? v : 0;
-    total += v;
-  }
-  const int64_t obase = row * (int64_t)a.nfch * TK_FCH + lo;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (sel[e]) {
-      a.fkey[obase + pos] = k4[e];
-      a.fidx[obase + pos] = (int32_t)(lo + p + e);
-      ++pos;
+  const int V = (int)visible_of(a, row);
+  const int K = min(a.top_k, V);
+  uint32_t* h = a.hint + row * TK_BINS;
+  if (K == V) {
+    if (c == 0) {
+      emit_all_visible(a, row, V);
+      if (a.clear_hint) clear_hint(h);
     }
-  if (t == 0) a.fcnt[row * a.nfch + c] = total;
-}
-
-__global__ void __launch_bounds__(TK_NT) topk_filtered_kernel(TopkArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-  uint32_t* hist = smem;                                   // TK_BINS
-  int* red = reinterpret_cast<int*>(smem + TK_BINS);       // 32
-  int* res = red + 32;                                     // 32
-  int* off = res + 32;                                     // TK_FCH_MAX chunk offsets, then the total
-  uint32_t* kc = reinterpret_cast<uint32_t*>(off + TK_FCH_MAX + 64);  // TK_CHUNK_C keys
-  int32_t* ic = reinterpret_cast<int32_t*>(kc + TK_CHUNK_C);          // and positions
-  const int t = threadIdx.x, l = t & 63, wv = t >> 6;
-  const int64_t row = blockIdx.x;
-  const int64_t V = visible_of(a, row);
-  const int top_k = a.top_k;
-  const int K = (int)min((int64_t)top_k, V);
-  const int nfch = a.nfch;
-  const int32_t* cnt = a.fcnt + row * nfch;
-
-  // chunk offsets in chunk order (wave 0: a lane sums a contiguous run of chunks)
-  if (wv == 0) {
-    const int per = (nfch + 63) / 64;
-    const int c0 = min(nfch, l * per), c1 = min(nfch, c0 + per);
-    int s = 0;
-    for (int c = c0; c < c1; ++c) s += cnt[c];
-    int run = wave_incl_scan_dpp(s) - s;
-    for (int c = c0; c < c1; ++c) {
-      off[c] = run;
-      run += cnt[c];
-    }
-    if (l == 63) off[TK_FCH_MAX] = run;
+    return;
   }
+  const int lo = c * TK_FCH;
+  if (lo >= V) return;  // chunks past V hold no key and do not arrive
+  const int hi = min(V, lo + TK_FCH);
+  const int nch = (V + TK_FCH - 1) / TK_FCH;  // chunks that arrive
+  RegKeys<TK_FCH / TK_NT> rk;
+  rk.load(a.scores + row * a.N_max, lo, hi);
+  load_hint(h, hist);
+  if (t == 0) res[0] = -1;
   __syncthreads();
-  const int total = off[TK_FCH_MAX];
-  const int64_t obase = row * (int64_t)top_k;
-  auto emit_to = [&](auto idx_of) {
-    return [&, idx_of](int pos, uint32_t key, int i) {
-      a.out_idx[obase + pos] = idx_of(i);
-      if (a.out_score) a.out_score[obase + pos] = key_f32(key);
-    };
-  };
-  auto pad = [&](int i) {
-    a.out_idx[obase + i] = -1;
-    if (a.out_score) a.out_score[obase + i] = -INFINITY;
-  };
-  if (total >= K && total <= TK_CHUNK_C) {
-    // gather: wave wv copies chunks wv, wv + 16, ... to their offsets
-    const uint32_t* fk = a.fkey + row * (int64_t)nfch * TK_FCH;
-    const int32_t* fi = a.fidx + row * (int64_t)nfch * TK_FCH;
-    for (int c = wv; c < nfch; c += TK_NW) {
-      const int nc = cnt[c], o = off[c];
-      for (int j = l; j < nc; j += 64) {
-        kc[o + j] = fk[(int64_t)c * TK_FCH + j];
-        ic[o + j] = fi[(int64_t)c * TK_FCH + j];
+  find_bin_block(hist, K, red, res);
+  const int b = res[0];
+  // this wave's segment: ordered compaction into its list
+  {
+    constexpr int KPT = TK_FCH / TK_NT;
+    const int seg = c * TK_NW + wv;
+    const int64_t lb = (row * a.nseg + seg) * (int64_t)TK_WCAP;
+    int run = 0;
+#pragma unroll
+    for (int j = 0; j < KPT / 4; ++j) {
+      bool cand[4];
+      int n = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cand[e] = b >= 0 && rk.pos(lo, j, e) < hi && (rk.k[4 * j + e] >> TK_DSHIFT) >= (uint32_t)b;
+        n += cand[e];
+      }
+      int st;
+      int s = run + excl3(n, st);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (cand[e]) {
+          if (s < TK_WCAP) {
+            st_dev(&a.wkey[lb + s], rk.k[4 * j + e]);
+            st_dev(&a.widx[lb + s], (int32_t)rk.pos(lo, j, e));
+          }
+          ++s;
+        }
+      run += st;
+    }
+    if (l == 0) st_dev(&a.wcnt[row * a.nseg + seg], b < 0 ? TK_WCAP + 1 : min(run, TK_WCAP + 1));
+  }
+  // arrival: every store of this chunk has completed, then it counts
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (t == 0)
+    res[4] = __hip_atomic_fetch_add(&a.ctr[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(nch - 1);
+  __syncthreads();
+  if (!res[4]) return;
+  // ---- last workgroup of the row: segment offsets, gather, select
+  const int nseg = (V + TK_SEG - 1) / TK_SEG;
+  int M = -1;
+  {
+    const int32_t* cnt = a.wcnt + row * a.nseg;
+    int base = 0, ovf = 0;
+    for (int s0 = 0; s0 < nseg; s0 += TK_NT) {
+      const int v = s0 + t < nseg ? ld_dev(&cnt[s0 + t]) : 0;
+      ovf |= v > TK_WCAP;
+      const int vc = min(v, TK_WCAP);
+      const int inc = wave_incl_scan_dpp(vc);
+      if (l == 63) red[wv] = inc;
+      __syncthreads();
+      int wb = 0, tot = 0;
+#pragma unroll
+      for (int u = 0; u < TK_NW; ++u) {
+        wb += u < wv ? red[u] : 0;
+        tot += red[u];
+      }
+      if (s0 + t < nseg) off[s0 + t] = base + wb + inc - vc;
+      base += tot;
+      __syncthreads();
+    }
+    ovf = block_sum(ovf, red);
+    M = ovf ? -1 : base;
+  }
+  if (M >= K && M <= a.cap) {
+    // gather: P threads per segment, each copying every P-th candidate (up to
+    // 16 loads in flight per thread)
+    const int P = nseg >= TK_NT ? 1 : TK_NT / nseg;
+    for (int s0 = 0; s0 < nseg; s0 += TK_NT / P) {
+      const int sg = s0 + t / P, sub = t % P;
+      if (sg < nseg) {
+        const int n = min(ld_dev(&a.wcnt[row * a.nseg + sg]), TK_WCAP), o = off[sg];
+        const int64_t lb = (row * a.nseg + sg) * (int64_t)TK_WCAP;
+        for (int j0 = sub; j0 < n; j0 += 16 * P) {
+          uint32_t kv[16];
+          int32_t iv[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int j = j0 + u * P;
+            if (j < n) {
+              kv[u] = ld_dev(&a.wkey[lb + j]);
+              iv[u] = ld_dev(&a.widx[lb + j]);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int j = j0 + u * P;
+            if (j < n) {
+              ck[o + j] = kv[u];
+              ci[o + j] = iv[u];
+            }
+          }
+        }
       }
     }
     __syncthreads();
-    const LdsKeys keys{kc};
-    uint32_t T = 0;
-    int need = 0;
-    const bool all = K == total;
-    if (!all) block_select(keys, total, K, hist, red, res, T, need);
-    block_compact(keys, total, K, all, T, need, top_k, red, emit_to([&](int i) { return ic[i]; }), pad);
+    select_in_candidates(a, row, ck, M, K, b, hist, red, res, [&](int i) { return ci[i]; });
   } else {
-    const float* src = a.scores + row * a.N_max;
-    const RowKeys keys{src, (int)V, (reinterpret_cast<uintptr_t>(src) & 15) == 0};
-    uint32_t T = 0;
-    int need = 0;
-    const bool all = K == (int)V;
-    if (!all) block_select(keys, (int)V, K, hist, red, res, T, need);
-    block_compact(keys, (int)V, K, all, T, need, top_k, red, emit_to([](int i) { return (int32_t)i; }), pad);
+    select_row_from_memory(a, row, V, K, hist, red, res);
   }
-}
-
-static int64_t pow2_at_least(int64_t x) {
-  int64_t p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
-
-// Level plan for rows of length n0: per launch, keys per workgroup (chunk),
-// chunks per row and the row length it reads. Chunks are sized so a launch
-// offers about one workgroup per CU (a lone workgroup is VALU bound), never
-// below 4096 keys or 4*top_k (each level must shrink the rows), never above
-// what fits in LDS, and never above the row itself (rounded up to 256 keys):
-// LDS is sized by the chunk, and rows of up to 18K keys then leave room for
-// two workgroups per CU. Depends on shape arguments only.
-static int plan_levels(int64_t rows, int64_t n0, int top_k, int64_t* nch, int64_t* nlen, int64_t* chunk) {
-  int lv = 0;
-  int64_t n = n0;
-  while (true) {
-    const int64_t cmax = lv == 0 ? TK_CHUNK_S : TK_CHUNK_C;
-    const int64_t want = pow2_at_least((rows * n + TK_TARGET_WG - 1) / TK_TARGET_WG);
-    const int64_t ch = std::min({cmax, (n + 255) / 256 * 256,
-                                 std::max<int64_t>({want, (int64_t)TK_CHUNK_MIN, pow2_at_least(4 * (int64_t)top_k)})});
-    chunk[lv] = ch;
-    nch[lv] = std::max<int64_t>(1, (n + ch - 1) / ch);
-    nlen[lv] = n;
-    ++lv;
-    if (nch[lv - 1] == 1 || lv == 12) break;
-    n = nch[lv - 1] * top_k;
-  }
-  return lv;
-}
-
-// Long rows (three or more levels) take the threshold path when its final
-// kernel can gather every filter chunk. Depends on shape arguments only.
-static bool use_threshold_path(int64_t rows, int64_t N_max, int top_k) {
-  int64_t nch[12], nlen[12], chunk[12];
-  const int lv = plan_levels(rows, N_max, top_k, nch, nlen, chunk);
-  const int64_t nfch = (N_max + TK_FCH - 1) / TK_FCH;
-  return lv >= 3 && nfch <= TK_FCH_MAX && top_k <= TK_CHUNK_C / 8;
+  if (a.clear_hint) clear_hint(h);  // consumed: cleared for the next call
+  if (t == 0) a.ctr[row] = 0u;
 }
 
 static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// threshold path workspace: thr [rows] | fcnt [rows, nfch] | fkey, fidx [rows, nfch * TK_FCH]
-static size_t threshold_ws(int64_t rows, int64_t N_max) {
-  const int64_t nfch = (N_max + TK_FCH - 1) / TK_FCH;
-  return round256(rows * 4) + round256(rows * nfch * 4) + 2 * round256((size_t)rows * nfch * TK_FCH * 4);
+static bool long_rows(int64_t N_max) { return N_max > TK_ROW_MAX; }
+bool topk_long_rows(int64_t N_max) { return long_rows(N_max); }
+
+static int64_t wave_segments(int64_t N_max) { return (N_max + TK_FCH - 1) / TK_FCH * TK_NW; }
+
+// Workspace: hint [rows, TK_BINS] (rows of a histogram-carrying call, or
+// long rows) | long rows: ctr [rows] | wcnt [rows, nseg] | wkey, widx [rows,
+// nseg, TK_WCAP]
+size_t topk_hint_bytes(int64_t rows, int64_t N_max, bool from_scan) {
+  return (from_scan || long_rows(N_max)) ? round256((size_t)rows * TK_BINS * 4) : 0;
 }
 
-size_t topk_ws_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k) {
-  if (use_threshold_path(B * Tq, N_max, top_k)) return threshold_ws(B * Tq, N_max);
-  int64_t nch[12], nlen[12], chunk[12];
-  const int lv = plan_levels(B * Tq, N_max, top_k, nch, nlen, chunk);
-  size_t mx = 0;
-  for (int i = 0; i + 1 < lv; ++i) mx = std::max(mx, (size_t)(B * Tq) * nch[i] * top_k * 8);
-  return mx == 0 ? 0 : 2 * ((mx + 255) & ~size_t(255));
+size_t topk_ws_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k, bool from_scan) {
+  (void)top_k;
+  const int64_t rows = B * Tq;
+  if (rows <= 0) return 0;
+  size_t n = topk_hint_bytes(rows, N_max, from_scan);
+  if (long_rows(N_max)) {
+    const int64_t nseg = wave_segments(N_max);
+    n += round256((size_t)rows * 4) + round256((size_t)rows * nseg * 4) +
+         2 * round256((size_t)rows * nseg * TK_WCAP * 4);
+  }
+  return n;
+}
+
+size_t topk_counter_offset(int64_t rows, int64_t N_max) {
+  return long_rows(N_max) ? round256((size_t)rows * TK_BINS * 4) : 0;
 }
 
 constexpr int TK_MAX_DEVICES = 64;
@@ -647,66 +828,6 @@ constexpr int TK_MAX_DEVICES = 64;
 hipError_t run_topk(const TopkLaunch& L, hipStream_t st) {
   const int64_t rows = L.B * L.Tq;
   if (rows == 0) return hipSuccess;
-  // the LDS opt-in is a per-device function attribute: set once per device
-  // (setting it twice is harmless, so concurrent first calls need no lock)
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= TK_MAX_DEVICES) return hipErrorInvalidDevice;
-  static bool attr_set_dev[TK_MAX_DEVICES] = {};
-  static bool attr_f_dev[TK_MAX_DEVICES] = {};
-  bool& attr_set = attr_set_dev[dev];
-  const size_t lds_s = (size_t)(TK_BINS + 64 + TK_CHUNK_S) * 4;
-  const size_t lds_c = (size_t)(TK_BINS + 64 + 2 * TK_CHUNK_C) * 4;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<TK_SCORES>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)topk_kernel<TK_CANDS>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds_c);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  if (use_threshold_path(rows, L.N_max, L.top_k)) {
-    const size_t lds_f = (size_t)(TK_BINS + 64 + TK_FCH_MAX + 64 + 2 * TK_CHUNK_C) * 4;
-    bool& attr_f = attr_f_dev[dev];
-    if (!attr_f) {
-      hipError_t e = hipFuncSetAttribute((const void*)topk_filtered_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_f);
-      if (e != hipSuccess) return e;
-      attr_f = true;
-    }
-    const int64_t nfch = (L.N_max + TK_FCH - 1) / TK_FCH;
-    TopkArgs a{};
-    a.scores = L.scores;
-    a.q_pos = L.q_pos;
-    a.n_comp = L.n_comp;
-    a.Tq = L.Tq;
-    a.N_max = L.N_max;
-    a.m = L.m;
-    a.top_k = L.top_k;
-    a.out_idx = L.idx;
-    a.out_score = L.out_score;
-    a.nfch = (int)nfch;
-    uint8_t* w = reinterpret_cast<uint8_t*>(L.ws);
-    a.thr = reinterpret_cast<uint32_t*>(w);
-    w += round256(rows * 4);
-    a.fcnt = reinterpret_cast<int32_t*>(w);
-    w += round256(rows * nfch * 4);
-    a.fkey = reinterpret_cast<uint32_t*>(w);
-    w += round256((size_t)rows * nfch * TK_FCH * 4);
-    a.fidx = reinterpret_cast<int32_t*>(w);
-    hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(TK_NT), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)nfch, (unsigned)rows), dim3(TK_NT), 0, st, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_filtered_kernel, dim3((unsigned)rows), dim3(TK_NT), lds_f, st, a);
-    return hipGetLastError();
-  }
-  int64_t nch[12], nlen[12], chunk[12];
-  const int lv = plan_levels(rows, L.N_max, L.top_k, nch, nlen, chunk);
-  size_t half = 0;
-  if (lv > 1) half = L.ws_bytes / 2;
   TopkArgs a{};
   a.scores = L.scores;
   a.q_pos = L.q_pos;
@@ -717,30 +838,61 @@ hipError_t run_topk(const TopkLaunch& L, hipStream_t st) {
   a.top_k = L.top_k;
   a.out_idx = L.idx;
   a.out_score = L.out_score;
-  for (int i = 0; i < lv; ++i) {
-    const bool last = i + 1 == lv;
-    uint8_t* cur = reinterpret_cast<uint8_t*>(L.ws) + (i & 1) * half;  // written by level i
-    if (!last) {
-      const size_t nk = (size_t)rows * nch[i] * L.top_k;
-      a.nkey = reinterpret_cast<uint32_t*>(cur);
-      a.nidx = reinterpret_cast<int32_t*>(cur + nk * 4);
-    }
-    dim3 grid((unsigned)nch[i], (unsigned)rows);
-    a.chunk = (int)chunk[i];
-    if (i == 0) {
-      hipLaunchKernelGGL(topk_kernel<TK_SCORES>, grid, dim3(TK_NT), (TK_BINS + 64 + chunk[i]) * 4, st, a);
-    } else {
-      hipLaunchKernelGGL(topk_kernel<TK_CANDS>, grid, dim3(TK_NT), (TK_BINS + 64 + 2 * chunk[i]) * 4, st, a);
-    }
+  uint8_t* w = reinterpret_cast<uint8_t*>(L.ws);
+  const bool from_scan = L.hint_mode != TOPK_HINT_NONE;
+  a.clear_hint = L.hint_mode == TOPK_HINT_ACCUMULATED;
+  if (!long_rows(L.N_max)) {
+    a.hint = from_scan ? reinterpret_cast<uint32_t*>(w) : nullptr;
+    const dim3 grid((unsigned)rows);
+    if (L.N_max <= 4096)
+      hipLaunchKernelGGL(topk_row_kernel<16>, grid, dim3(TK_NT), 0, st, a);
+    else
+      hipLaunchKernelGGL(topk_row_kernel<64>, grid, dim3(TK_NT), 0, st, a);
+    return hipGetLastError();
+  }
+  const int64_t nseg = wave_segments(L.N_max);
+  // candidates the last workgroup of a row can hold: about 8 top-k, at least
+  // 4096, at most 16384 and what the LDS leaves beside the segment offsets; a
+  // row with more falls back to memory
+  const size_t fixed = (size_t)(TK_BINS + 2 * TK_NW + 8 + seg_words((int)nseg)) * 4;
+  int cap = (int)std::min<int64_t>(16384, std::max<int64_t>(4096, 8 * (int64_t)L.top_k));
+  while (fixed + (size_t)cap * 8 > (size_t)TK_LDS_MAX) cap -= 1024;
+  const size_t lds = fixed + (size_t)cap * 8;
+  // the LDS opt-in is a per-device function attribute: set once per device
+  // (setting it twice is harmless, so concurrent first calls need no lock)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= TK_MAX_DEVICES) return hipErrorInvalidDevice;
+  static bool attr_set_dev[TK_MAX_DEVICES] = {};
+  if (!attr_set_dev[dev]) {
+    hipError_t e = hipFuncSetAttribute((const void*)topk_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       TK_LDS_MAX);
+    if (e != hipSuccess) return e;
+    attr_set_dev[dev] = true;
+  }
+  a.hint = reinterpret_cast<uint32_t*>(w);
+  w += round256((size_t)rows * TK_BINS * 4);
+  a.ctr = reinterpret_cast<uint32_t*>(w);
+  w += round256((size_t)rows * 4);
+  a.wcnt = reinterpret_cast<int32_t*>(w);
+  w += round256((size_t)rows * nseg * 4);
+  a.wkey = reinterpret_cast<uint32_t*>(w);
+  w += round256((size_t)rows * nseg * TK_WCAP * 4);
+  a.widx = reinterpret_cast<int32_t*>(w);
+  a.nseg = (int)nseg;
+  a.cap = cap;
+  if (!from_scan) {
+    // no histogram from a scan: build it here (the counters start at zero too)
+    a.clear_hint = 0;
+    hipLaunchKernelGGL(topk_clear_kernel, dim3((unsigned)rows), dim3(TK_NT), 0, st, a.hint, a.ctr, (int)rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (!last) {  // the candidates become the next level's input
-      a.ckey = a.nkey;
-      a.cidx = a.nidx;
-      a.n_cand = nch[i] * L.top_k;
-    }
+    const unsigned nh = (unsigned)((L.N_max + 16 * TK_NT - 1) / (16 * TK_NT));
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(nh, (unsigned)rows), dim3(TK_NT), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)(nseg / TK_NW), (unsigned)rows), dim3(TK_NT), lds, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace csa

@@ -139,10 +139,21 @@ def _indexer_case(B, Tq, N_max, n_comp, q_pos, m, top_k, kdt, seed=0, H_I=64, D_
     idx2 = torch.empty_like(idx)
     tsc = torch.empty((B, Tq, top_k), device=DEV)
     L.indexer_topk(scores, qp, nc, idx, tsc, m=m)
-    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx2, m=m)
+    # the fused call: on a zeroed workspace, again on the same workspace (the
+    # digit histogram the previous call cleared), and on a workspace of
+    # garbage (the histogram is only a hint: same results, slower path)
+    nb = L.indexer_score_topk_workspace_bytes(B, Tq, N_max, top_k)
+    ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device=DEV)
+    idx3, idx4 = torch.empty_like(idx), torch.empty_like(idx)
+    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx2, m=m, ws=ws)
+    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx3, m=m, ws=ws)
+    junk = torch.randint(0, 256, (max(nb, 1),), dtype=torch.uint8, device=DEV)
+    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx4, m=m, ws=junk)
     torch.cuda.synchronize()
     S, I, I2, TS = host(scores), host(idx), host(idx2), host(tsc)
     assert np.array_equal(I, I2), "indexer_score_topk != indexer_score + indexer_topk"
+    assert np.array_equal(I, host(idx3)), "indexer_score_topk on a reused workspace"
+    assert np.array_equal(I, host(idx4)), "indexer_score_topk on a workspace of garbage"
     qpos = np.asarray(q_pos).reshape(B, Tq)
     for b in range(B):
         for t in range(Tq):
@@ -280,7 +291,7 @@ def test_indexer_tiny_f32_c1():
 
 # ------------------------------------------------------------------ top-k alone
 
-def _topk_case(rows, N_max, Vs, k, dist, seed=0):
+def _topk_case(rows, N_max, Vs, k, dist, seed=0, ws_extra=None):
     _say("topk", rows, N_max, k, dist)
     g = _g(seed)
     if dist == "ties":
@@ -294,13 +305,22 @@ def _topk_case(rows, N_max, Vs, k, dist, seed=0):
     qp = np.asarray(Vs, np.int32) - 1  # V = min(n_comp, q_pos + 1)
     nc = np.full((1,), N_max, np.int32)
     idx = torch.empty((1, rows, k), dtype=torch.int32, device=DEV)
-    L.indexer_topk(dev(s.reshape(1, rows, N_max)), dev(qp.reshape(1, rows)), dev(nc), idx, m=m)
+    tsc = torch.full((1, rows, k), 7.0, dtype=torch.float32, device=DEV)
+    ws = None
+    if ws_extra is not None:  # a workspace larger than needed, filled with garbage
+        nb = L.indexer_topk_workspace_bytes(1, rows, N_max, k) + ws_extra
+        ws = torch.randint(0, 256, (max(nb, 1),), dtype=torch.uint8, device=DEV)
+    L.indexer_topk(dev(s.reshape(1, rows, N_max)), dev(qp.reshape(1, rows)), dev(nc), idx, tsc, m=m, ws=ws)
     torch.cuda.synchronize()
-    I = host(idx)[0]
+    I, TS = host(idx)[0], host(tsc)[0]
     for r in range(rows):
         V = max(0, min(Vs[r], N_max))
         ref = oracle.topk_select(s[r, :V].astype(np.float64), k)
         assert np.array_equal(I[r], ref), f"row {r}: exact selection differs"
+        K = min(k, V)
+        # the returned scores are the scores of the returned indices, -inf past K
+        assert np.array_equal(TS[r, :K], s[r, I[r, :K]].astype(np.float64)), f"row {r}: returned scores"
+        assert np.all(np.isneginf(TS[r, K:])), f"row {r}: padding scores"
 
 
 def test_indexer_fp8_all_codes_exact():
@@ -339,31 +359,42 @@ def test_topk_ties_lower_index_wins():
     _topk_case(2, 500, [500, 500], 17, "zeros", seed=22)
 
 
-def test_topk_two_level_rows():
-    # rows longer than one 32768-key chunk go through chunk winners + a second selection;
-    # rows of one launch may end in either chunk
-    _topk_case(3, 40000, [40000, 33000, 20000], 1024, "normal", seed=23)
+def test_topk_one_workgroup_rows():
+    # rows of up to 32768 keys are finished by one workgroup each; the
+    # candidates of the threshold bin, all ties, and rows shorter than k
+    _topk_case(4, 32768, [32768, 32767, 511, 16385], 512, "normal", seed=30)
+    _topk_case(3, 16384, [16384, 9000, 12], 512, "ties", seed=31)
+    _topk_case(2, 32768, [32768, 20000], 4096, "normal", seed=32)
 
 
-def test_topk_threshold_path_normal():
-    # rows needing three or more levels take a sampled threshold, a filter and one
-    # select; a short row (V <= 16384) keeps every key as a candidate
+def test_topk_long_rows():
+    # rows longer than 32768 keys: digit histogram, per-chunk candidates, one
+    # final select; rows of one launch end in different chunks, one row is
+    # shorter than k (its scores past K must read -inf)
+    _topk_case(4, 40000, [40000, 33000, 20000, 700], 1024, "normal", seed=23)
     _topk_case(3, 200003, [200003, 150001, 17000], 1024, "normal", seed=28)
     _topk_case(2, 100000, [100000, 99999], 256, "normal", seed=29)
 
 
 def test_topk_long_rows_ties_and_ragged():
-    # long rows of integer scores: the sampled threshold keeps too many candidates,
-    # so the final kernel selects over the whole row; ties cross chunks, rows end
-    # mid-chunk and mid-lane
+    # long rows of integer scores: far more candidates than fit, so the final
+    # kernel selects over the whole row; ties cross chunks, rows end mid-chunk
+    # and mid-lane
     _topk_case(3, 300001, [300001, 123457, 4099], 1024, "ties", seed=25)
     _topk_case(5, 9001, [9001, 4097, 4096, 1, 0], 1, "normal", seed=26)
     _topk_case(2, 8193, [8193, 8190], 7, "zeros", seed=27)
 
 
-def test_topk_multilevel_ties():
-    # 600000 keys, top 4096: four levels; integer scores make ties cross chunks
+def test_topk_multichunk_ties():
+    # 600000 keys, top 4096; integer scores make ties cross chunks
     _topk_case(2, 600000, [600000, 431111], 4096, "ties", seed=24)
+
+
+def test_topk_workspace_garbage_and_oversized():
+    # the workspace's contents on entry never matter, and a workspace larger
+    # than needed (by a size that is not a multiple of 256) changes nothing
+    _topk_case(3, 70001, [70001, 50000, 33], 512, "normal", seed=33, ws_extra=4)
+    _topk_case(2, 5000, [5000, 3000], 64, "normal", seed=34, ws_extra=4)
 
 
 # ------------------------------------------------------------------ attention

@@ -59,19 +59,24 @@ def run_csa_decode(cfg, x):
     kv = _kv(cfg, x["kv_comp"])
     q_pos = _t(np.full((B, 1), cfg.n - 1, np.int32))
     n_comp = _t(np.full((B,), N, np.int32))
-    scores = torch.empty((B, 1, N), dtype=torch.float32, device=DEV)
     if cfg.k_dtype == "fp8":
         k_t, sc = _t(x["k_idx_codes"]), _t(x["k_scale"])
     elif cfg.k_dtype == "mxfp4":
         k_t, sc = _t(x["k_idx_codes"]).view(torch.float4_e2m1fn_x2), _t(x["k_scale"])
     else:
         k_t, sc = _bf(x["k_idx"]), None
-    # the completed block's entry and the scan in one call, as bench.py runs them
-    L.csa_compress_indexer_score(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]), _t(x["Bb"]), kv,
-                                 _bf(x["q_idx"][:, None]), _t(x["w"][:, None]), k_t, sc, q_pos, n_comp, scores,
-                                 m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
+    # the completed block's entry, the scan and the top-k in one call, as
+    # bench.py runs them; twice on one workspace (the second call reads the
+    # digit histogram the first one left cleared), the scores in its first bytes
+    ws = torch.zeros(L.indexer_score_topk_workspace_bytes(B, 1, N, k), dtype=torch.uint8, device=DEV)
     idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
-    L.indexer_topk(scores, q_pos, n_comp, idx, m=m)
+    idx1 = torch.empty_like(idx)
+    for dst in (idx1, idx):
+        L.csa_compress_indexer_score_topk(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]),
+                                          _t(x["Bb"]), kv, _bf(x["q_idx"][:, None]), _t(x["w"][:, None]), k_t, sc,
+                                          q_pos, n_comp, dst, m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1,
+                                          blk_end=N, ws=ws)
+    scores = ws[:B * N * 4].view(torch.float32).view(B, 1, N)
     out = torch.empty((B, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, cfg.H), device=DEV)
     q, scale = _bf(x["q"]), 1.0
@@ -85,6 +90,7 @@ def run_csa_decode(cfg, x):
     if cfg.qk_rope:  # epilogue: the output rotated back
         L.qk_norm_rope(out, out, pos, inverse=True)
     torch.cuda.synchronize()
+    assert torch.equal(idx, idx1), "the step's selection differs between two calls on one workspace"
     # the cache stays on the device (GBs at full size); only its last two rows come back
     return host(kv[:, N - 2:]), host(scores)[:, 0], host(idx)[:, 0], host(out), host(lse)
 
@@ -210,11 +216,12 @@ def run_prefill_chunk(cfg, tok, comp_t, chunk):
     N, m, k = cfg.N, cfg.m, cfg.top_k
     q_pos = _t(qs["q_pos"][None])
     n_comp = _t(np.array([N], np.int32))
-    scores = torch.empty((1, T, N), dtype=torch.float32, device=DEV)
-    L.indexer_score(_bf(qs["q_idx"][None]), _t(qs["w"][None]), _bf(tok["k_idx"][None]), None, q_pos, n_comp,
-                    scores, m=m)
+    # scores and top-k in one call, as bench.py runs them (scores in the workspace's first bytes)
+    ws = torch.empty(L.indexer_score_topk_workspace_bytes(1, T, N, k), dtype=torch.uint8, device=DEV)
     idx = torch.empty((1, T, k), dtype=torch.int32, device=DEV)
-    L.indexer_topk(scores, q_pos, n_comp, idx, m=m)
+    L.indexer_score_topk(_bf(qs["q_idx"][None]), _t(qs["w"][None]), _bf(tok["k_idx"][None]), None, q_pos, n_comp,
+                         idx, m=m, ws=ws)
+    scores = ws[:T * N * 4].view(torch.float32).view(1, T, N)
     out = torch.empty((T, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((T, cfg.H), device=DEV)
     L.sparse_mqa_prefill(_bf(qs["q"]), comp_t[0], idx[0], _kv(cfg, tok["kv_tok"]), q_pos[0], _t(tok["sink"]), out,
@@ -244,7 +251,8 @@ def check_prefill(cfg, chunks, picks):
     for c in chunks:
         qs, S, I, O, LSE = run_prefill_chunk(cfg, tok, comp_t, c)
         T = len(qs["q_pos"])
-        for t in picks(T):
+        pk = picks(c) if getattr(picks, "per_chunk", False) else picks
+        for t in pk(T):
             p = int(qs["q_pos"][t])
             print(f"[case] {cfg.name} chunk {c} query {t} pos {p}", flush=True)
             win = oracle.window_rows(kv_tok, p, cfg.W)
@@ -284,6 +292,28 @@ def test_csa_prefill_64k_last_chunk_sampled():
     check_prefill(cfg, [gen.num_chunks(cfg) - 1], lambda T: sorted(set([0, 1, T - 1] + list(rng.integers(0, T, 8)))))
 
 
+def test_csa_prefill_64k_all_chunks_sampled():
+    """Every 4096-query chunk of the 64K prefill through the GPU path, sampled:
+    the first and last 64 queries of the sequence, the 8 queries on each side
+    of every chunk boundary, and a few random queries per chunk."""
+    cfg = gen.C3
+    nch = gen.num_chunks(cfg)
+    rng = np.random.default_rng(13)
+
+    def picks(c):
+        def f(T):
+            p = set(range(8)) | set(range(T - 8, T)) | set(rng.integers(0, T, 4).tolist())
+            if c == 0:
+                p |= set(range(64))
+            if c == nch - 1:
+                p |= set(range(T - 64, T))
+            return sorted(p)
+        return f
+
+    picks.per_chunk = True
+    check_prefill(cfg, list(range(nch)), picks)
+
+
 def check_csa_decode_multi(cfg, seqs):
     """Tq query tokens per sequence in one step (positions n-Tq .. n-1): the
     completed entry is appended, each token is scored and selected at its own
@@ -295,12 +325,13 @@ def check_csa_decode_multi(cfg, seqs):
     kv = _kv(cfg, x["kv_comp"])
     pos = np.tile(np.arange(cfg.n - Tq, cfg.n, dtype=np.int32), (B, 1))
     q_pos, n_comp = _t(pos), _t(np.full((B,), N, np.int32))
-    scores = torch.empty((B, Tq, N), dtype=torch.float32, device=DEV)
-    L.csa_compress_indexer_score(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]), _t(x["Bb"]), kv,
-                                 _bf(x["q_idx"]), _t(x["w"]), _bf(x["k_idx"]), None, q_pos, n_comp, scores, m_c=m,
-                                 m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
+    ws = torch.zeros(L.indexer_score_topk_workspace_bytes(B, Tq, N, k), dtype=torch.uint8, device=DEV)
     idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
-    L.indexer_topk(scores, q_pos, n_comp, idx, m=m)
+    L.csa_compress_indexer_score_topk(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]),
+                                      _t(x["Bb"]), kv, _bf(x["q_idx"]), _t(x["w"]), _bf(x["k_idx"]), None, q_pos,
+                                      n_comp, idx, m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N,
+                                      ws=ws)
+    scores = ws[:B * Tq * N * 4].view(torch.float32).view(B, Tq, N)
     out = torch.empty((B, Tq, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, Tq, cfg.H), device=DEV)
     L.sparse_mqa_decode_multi(_bf(x["q"]), kv, idx, _kv(cfg, x["kv_win"]), _t(np.full((B,), W + Tq - 1, np.int32)),

@@ -161,12 +161,11 @@ def main():
     if cfg.kind == "csa_decode":
         k = cfg.top_k
         idx = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
-        # scores, digit histograms and top-k scratch; zero-filled once, as the
-        # calls leave it (their histograms cleared after use)
-        ws_t = torch.zeros(L.indexer_score_topk_workspace_bytes(B, Tq, N, k), dtype=torch.uint8, device=dev)
+        # scores, digit histograms, top-k and attention scratch; zero-filled
+        # once, as the step leaves it (its histograms cleared after use)
+        ws_t = torch.zeros(L.csa_decode_step_workspace_bytes(B, Tq, N, k, H, D, W), dtype=torch.uint8, device=dev)
         scores = ws_t[:B * Tq * N * 4].view(torch.float32).view(B, Tq, N)
-        ws_a = torch.empty(max(1, L.sparse_mqa_decode_multi_workspace_bytes(B, Tq, H, D, k, W)), dtype=torch.uint8,
-                           device=dev)
+        ws_a = None
     else:
         ws_a = torch.empty(max(1, L.hca_dense_mqa_workspace_bytes(B, H, D, N, W)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -183,20 +182,17 @@ def main():
             L.qk_norm_rope(r["q"], qn, shared["pos"], shared["q_gamma"], norm=True, rope=True, stream=s)
             q_att = qn
         if cfg.kind == "csa_decode":
-            # the completed block's entry, the indexer scan and the top-k: one call
-            L.csa_compress_indexer_score_topk(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"],
-                                              r["kv_comp"], r["q_idx"], r["w"], r["k_idx"], r.get("k_scale"),
-                                              shared["q_pos"], shared["n_comp"], idx, m_c=m, m=m,
-                                              tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, ws=ws_t, stream=s)
+            # the whole step in one call: the completed block's entry, the
+            # indexer scan, then top-k, attention and split merge
+            L.csa_decode_step(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"], r["q_idx"], r["w"],
+                              r["k_idx"], r.get("k_scale"), shared["q_pos"], shared["n_comp"],
+                              q_att if Tq > 1 else q_att.view(B, 1, H, D), r["kv_comp"], r["kv_win"],
+                              shared["win_len"], shared["sink"], idx, out if Tq > 1 else out.view(B, 1, H, D),
+                              m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, scale=att_scale,
+                              ws=ws_t, stream=s)
             rec(ev, 1)
             rec(ev, 2)
             rec(ev, 3)
-            if Tq > 1:
-                L.sparse_mqa_decode_multi(q_att, r["kv_comp"], idx, r["kv_win"], shared["win_len"], shared["sink"],
-                                          out, scale=att_scale, ws=ws_a, stream=s)
-            else:
-                L.sparse_mqa_decode(q_att, r["kv_comp"], idx.view(B, k), r["kv_win"], shared["win_len"],
-                                    shared["sink"], out, scale=att_scale, ws=ws_a, stream=s)
             if cfg.qk_rope:  # epilogue: the output's rotated dims turned back
                 L.qk_norm_rope(out, out, shared["pos"], inverse=True, stream=s)
         else:
@@ -280,8 +276,7 @@ def main():
                            "frac": round(scan_bytes / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "traffic": _traffic(f"idx_scan_{a.workload}_traffic.txt", ["indexer.hip", "common.h"]),
                            "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_ms": round(scan_avg, 4)}
-        res["phases_ms"] = {"compress_indexer_scan_topk": round(float(ph_mean[0] + ph_mean[1] + ph_mean[2]), 4),
-                            "attention": round(attn_avg, 4)}
+        res["phases_ms"] = {"decode_step": round(float(ph_mean.sum()), 4)}
         res["step_hbm_gbs"] = round(step_bytes / (ms_step * 1e-3) / 1e9, 1)
         res["indexer_kv_hbm_gbs"] = res["roofline"]["achieved"]
     else:

@@ -274,6 +274,45 @@ int sparse_mqa_decode_multi(const void* q, const void* kv_comp, const int32_t* t
                             void* ws, size_t ws_bytes, void* stream);
 size_t sparse_mqa_decode_multi_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int top_k, int W);
 
+/*
+ * csa_decode_step — one CSA decode step for Tq query tokens per sequence,
+ * [CSDN] CSA steps 1-3 in the pages' order: the compression of the blocks
+ * the step's tokens complete (csa_compress into kv_comp, rows [blk_begin,
+ * blk_end)), the indexer scores, the top-k and the shared-KV MQA with the
+ * window and the sink. Results are bit for bit those of csa_compress,
+ * indexer_score_topk and sparse_mqa_decode_multi in turn.
+ *   compression: as csa_compress with B = B, out = kv_comp, out_cap = N_max,
+ *                out_dt = kv_dt, d = D (blk_begin == blk_end: none).
+ *   indexer    : as indexer_score_topk (q_idx [B, Tq, H_I, D_I], q_pos [B, Tq]);
+ *                topk_idx [B, Tq, top_k] and topk_score (nullable) are outputs.
+ *   attention  : as sparse_mqa_decode_multi (q [B, Tq, H, D], kv_win
+ *                [B, W + Tq - 1, D], win_len [B], out [B, Tq, H, D], lse nullable).
+ *   ws         : csa_decode_step_workspace_bytes(...); the scores occupy its
+ *                first B * Tq * N_max * 4 bytes. As with indexer_score_topk,
+ *                results never depend on its contents on entry, and a
+ *                zero-filled workspace (or one last used by a call of the same
+ *                shape) takes the fast path.
+ * With bf16 indexer queries, fewer than 8 query tokens per sequence, D = 512
+ * and bf16 or KV_FP8 rows, the top-k, the attention and the merge of its
+ * splits run as one launch of at most one workgroup per CU (B * Tq up to the
+ * CU count, at most 16 splits of 128 rows), whose workgroups hand each other
+ * their results through the workspace; otherwise as separate launches. That
+ * launch waits on its own workgroups only: two calls that overlap on one
+ * device (two streams) must not share a workspace, and a call running beside
+ * other kernels that hold CUs for long is slowed, not deadlocked -- its waits
+ * are bounded, and a query whose wait ran out gets NaN outputs and index -1.
+ * Either form is an ordinary stream launch and can be captured in a HIP graph.
+ */
+int csa_decode_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba, const float* Bb,
+                    int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin, int64_t blk_end,
+                    int flags, int in_dt, const void* q_idx, const float* w, const void* k_idx,
+                    const void* k_scale, const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq,
+                    int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt, int k_dt, const void* q,
+                    void* kv_comp, const void* kv_win, const int32_t* win_len, const float* sink, float scale, int H,
+                    int D, int W, int kv_dt, int out_dt, int32_t* topk_idx, float* topk_score, void* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+size_t csa_decode_step_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k, int H, int D, int W);
+
 /* sparse_mqa_prefill — Tq queries of one sequence.
  *   q      : [Tq, H, D]          kv_comp : [N, D]
  *   topk_idx : [Tq, top_k] int32 (-1 = empty)

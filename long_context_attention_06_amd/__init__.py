@@ -50,6 +50,10 @@ _SIGS = {
     "csa_compress_indexer_score_topk": ([_vp] * 7 + [_i64, _i64, _i64, _i32, _i32, _i64, _i64, _i64, _i32, _i32,
                                                       _i32] + [_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32,
                                                                            _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "csa_decode_step": ([_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i64, _i32, _i32] + [_vp] * 6
+                        + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32] + [_vp] * 5
+                        + [_f32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
+    "csa_decode_step_workspace_bytes": ([_i64, _i64, _i64, _i32, _i32, _i32, _i32], _sz),
     "indexer_topk_workspace_bytes": ([_i64, _i64, _i64, _i32], _sz),
     "indexer_score_topk": ([_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
                                         _vp], _i32),
@@ -207,6 +211,34 @@ def csa_compress_indexer_score_topk(Ca, Cb, Za, Zb, Ba, Bb, kv_out, q_idx, w, k_
         blk_begin, blk_end, out_cap, flags, _dt(Ca), out_dt, _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale),
         _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I, N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(topk_idx),
         _ptr(topk_score), _ptr(ws), nb, _stream(stream)))
+
+
+def csa_decode_step_workspace_bytes(B: int, Tq: int, N_max: int, top_k: int, H: int, D: int, W: int) -> int:
+    return lib.csa_decode_step_workspace_bytes(B, Tq, N_max, top_k, H, D, W)
+
+
+def csa_decode_step(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, n_comp, q, kv_comp, kv_win, win_len,
+                    sink, topk_idx, out, lse=None, topk_score=None, *, m_c: int, m: int, tok_begin: int = 0,
+                    blk_begin: int = 0, blk_end: Optional[int] = None, overlap: bool = True, joint: bool = False,
+                    scale: float = 1.0, ws=None, stream=None) -> None:
+    """One CSA decode step: compression of blocks [blk_begin, blk_end) into kv_comp, indexer scores,
+    top-k (-> topk_idx [B, Tq, top_k]) and sparse MQA (q [B, Tq, H, D] or [B, H, D] -> out)."""
+    _, n_rows, d = Ca.shape
+    if blk_end is None:
+        blk_end = (tok_begin + n_rows) // m_c
+    flags = (OVERLAP if overlap else 0) | (JOINT_SOFTMAX if joint else 0)
+    B, Tq, H_I, D_I = q_idx.shape
+    N_max = k_idx.shape[1]
+    top_k = topk_idx.shape[-1]
+    H, D = q.shape[-2], q.shape[-1]
+    W = kv_win.shape[1] - Tq + 1
+    ws, nb = _ws(csa_decode_step_workspace_bytes(B, Tq, N_max, top_k, H, D, W), ws, q.device)
+    _check(lib.csa_decode_step(
+        _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), n_rows, tok_begin, d, m_c, blk_begin, blk_end,
+        flags, _dt(Ca), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I,
+        N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len), _ptr(sink),
+        scale, H, D, W, _kv_dt(q, kv_comp), _dt(out), _ptr(topk_idx), _ptr(topk_score), _ptr(out), _ptr(lse),
+        _ptr(ws), nb, _stream(stream)))
 
 
 def indexer_topk_workspace_bytes(B: int, Tq: int, N_max: int, top_k: int) -> int:

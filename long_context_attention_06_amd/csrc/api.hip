@@ -286,6 +286,157 @@ int csa_compress_indexer_score_topk(const void* Ca, const void* Cb, const void* 
                          "csa_compress_indexer_score_topk");
 }
 
+// A decode step: [blocks of kv_comp completed by the step's tokens], scores,
+// top-k and sparse MQA with the split merge. The workspace holds the scores,
+// the top-k's scratch (its digit histogram first) and the tail's scratch
+// (arrival counters and sub-bin counts first, zeroed by the scan; the lists;
+// the split partials).
+static size_t step_split_rows(int slots, int* nsplit) {
+  *nsplit = nsplit_for(slots, SPARSE_SPLIT_ROWS);
+  return *nsplit > 1 ? SPARSE_SPLIT_ROWS : slots;
+}
+
+size_t csa_decode_step_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k, int H, int D, int W) {
+  if (B < 0 || Tq < 1 || N_max < 0 || top_k < 1 || H <= 0 || D <= 0 || W < 0) return 0;
+  const int64_t nq = B * Tq;
+  int ns = 0;
+  const int sr = (int)step_split_rows(top_k + W, &ns);
+  return round256((size_t)nq * N_max * 4) + round256(csa::topk_ws_bytes(B, Tq, N_max, top_k, true)) +
+         round256(std::max(csa::decode_tail_ws_bytes(nq, N_max, top_k, H, D, top_k + W, sr, ns),
+                           attn_ws(nq, H, D, ns)));
+}
+
+int csa_decode_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba, const float* Bb,
+                    int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin, int64_t blk_end,
+                    int flags, int in_dt, const void* q_idx, const float* w, const void* k_idx,
+                    const void* k_scale, const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq,
+                    int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt, int k_dt, const void* q,
+                    void* kv_comp, const void* kv_win, const int32_t* win_len, const float* sink, float scale, int H,
+                    int D, int W, int kv_dt, int out_dt, int32_t* topk_idx, float* topk_score, void* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream) {
+  REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
+  REQ(Tq >= 1 && Tq <= 64, CSA_INVALID_ARG, "Tq must be in [1, 64]");
+  const int64_t nq = B * Tq;
+  csa::CompressLaunch c{};
+  int rc = prep_compress(Ca, Cb, Za, Zb, Ba, Bb, kv_comp, B, n_rows, tok_begin, d, m_c, blk_begin, blk_end, N_max,
+                         flags, in_dt, kv_dt, &c);
+  if (rc) return rc;
+  REQ(blk_begin == blk_end || d == D, CSA_INVALID_ARG, "the compressed rows must have the attention's D channels");
+  rc = check_indexer(q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, q_dt, k_dt);
+  if (rc) return rc;
+  REQ(top_k >= 1, CSA_INVALID_ARG, "top_k must be >= 1");
+  REQ(top_k <= 4096, CSA_UNSUPPORTED, "top_k above 4096");
+  REQ(nq == 0 || topk_idx, CSA_INVALID_ARG, "topk_idx must not be NULL");
+  rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, top_k, nq);
+  if (rc) return rc;
+  REQ(nq == 0 || kv_comp, CSA_INVALID_ARG, "kv_comp must not be NULL");
+  REQ(nq == 0 || W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
+  REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
+  const size_t need = csa_decode_step_workspace_bytes(B, Tq, N_max, top_k, H, D, W);
+  REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
+  REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
+  REQ(((uintptr_t)ws & 255u) == 0, CSA_INVALID_ARG, "ws must be 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (nq == 0) return hip_status(csa::run_compress(c, st), "csa_decode_step");
+  REQ(nq <= 0x7fffffff, CSA_UNSUPPORTED, "B * Tq too large");
+
+  const int slots = top_k + W;
+  int ns = 0;
+  const int sr = (int)step_split_rows(slots, &ns);
+  uint8_t* p = reinterpret_cast<uint8_t*>(ws);
+  float* scores = reinterpret_cast<float*>(p);
+  p += round256((size_t)nq * N_max * 4);
+  uint8_t* tw = p;  // top-k scratch, digit histogram first
+  p += round256(csa::topk_ws_bytes(B, Tq, N_max, top_k, true));
+  uint8_t* xw = p;  // tail scratch, or the separate attention's partials
+
+  csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, scores};
+  const int mode = csa::indexer_hint_mode(a);
+  a.hint = mode != csa::TOPK_HINT_NONE ? reinterpret_cast<uint32_t*>(tw) : nullptr;
+  const bool fused = mode == csa::TOPK_HINT_ACCUMULATED && D == 512 && kv_dt != CSA_F32 &&
+                     csa::decode_tail_applies(nq, N_max, top_k, slots, sr, ns, kv_dt);
+  if (fused) {
+    a.zero = reinterpret_cast<uint32_t*>(xw);
+    a.zero_n = (int64_t)(csa::decode_tail_zero_bytes(nq) / 4);
+  } else if (csa::topk_long_rows(N_max)) {
+    a.zero = reinterpret_cast<uint32_t*>(tw + csa::topk_counter_offset(nq, N_max));
+    a.zero_n = nq;
+  }
+  rc = hip_status(csa::run_compress_indexer(c, a, st), "csa_decode_step");
+  if (rc) return rc;
+  int topk_mode = mode;
+  if (fused) {
+    csa::DecodeTailLaunch t{};
+    t.q = q;
+    t.kv_comp = kv_comp;
+    t.kv_win = kv_win;
+    t.win_len = win_len;
+    t.sink = sink;
+    t.scale = scale;
+    t.nq = nq;
+    t.N_max = N_max;
+    t.Tq = (int)Tq;
+    t.H = H;
+    t.W = W;
+    t.top_k = top_k;
+    t.slots = slots;
+    t.split_rows = sr;
+    t.nsplit = ns;
+    t.kv_dt = kv_dt;
+    t.out_dt = out_dt;
+    t.scores = scores;
+    t.q_pos = q_pos;
+    t.n_comp = n_comp;
+    t.m = m;
+    t.hint = reinterpret_cast<uint32_t*>(tw);
+    t.out_idx = topk_idx;
+    t.out_score = topk_score;
+    t.out = out;
+    t.lse = lse;
+    t.ws = xw;
+    bool launched = false;
+    (void)csa::run_decode_tail(t, st, &launched);
+    if (launched) return CSA_OK;
+    // the cooperative launch was refused: the separate kernels, the top-k
+    // rebuilding its histogram and counters (the scan zeroed the tail's)
+    (void)hipGetLastError();
+    topk_mode = csa::TOPK_HINT_NONE;
+    if (!csa::topk_long_rows(N_max)) topk_mode = mode;  // short rows read the scan's histogram as it is
+  }
+  csa::TopkLaunch tk{scores, q_pos, n_comp, B, Tq, N_max, m, top_k, topk_idx, topk_score, tw,
+                     csa::topk_ws_bytes(B, Tq, N_max, top_k, true), topk_mode};
+  rc = hip_status(csa::run_topk(tk, st), "csa_decode_step");
+  if (rc) return rc;
+  csa::AttnLaunch at{};
+  at.src = 0;
+  at.q = q;
+  at.kv_comp = kv_comp;
+  at.idx = topk_idx;
+  at.kv_win = kv_win;
+  at.win_len = W == 0 ? nullptr : win_len;
+  at.sink = sink;
+  at.scale = scale;
+  at.nq = nq;
+  at.N_max = N_max;
+  at.H = H;
+  at.D = D;
+  at.top_k = top_k;
+  at.W = W;
+  at.Tq = (int)Tq;
+  at.Wb = W + (int)Tq - 1;
+  at.m_rate = 1;
+  at.kv_dt = kv_dt;
+  at.out_dt = out_dt;
+  at.slots = slots;
+  at.split_rows = sr;
+  at.nsplit = ns;
+  at.part_o = reinterpret_cast<float*>(xw);
+  at.part_ml = reinterpret_cast<float*>(xw + round256((size_t)nq * ns * H * D * 4));
+  at.out = out;
+  at.lse = lse;
+  return hip_status(csa::run_attn(at, st), "csa_decode_step");
+}
+
 size_t sparse_mqa_decode_multi_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int top_k, int W) {
   if (B < 0 || Tq < 1 || H <= 0 || D <= 0 || top_k < 0 || W < 0) return 0;
   return attn_ws(B * Tq, H, D, nsplit_for((int64_t)top_k + W, SPARSE_SPLIT_ROWS));

@@ -449,3 +449,118 @@ def test_determinism_and_batch_invariance():
     one = run_csa_decode(gen.scaled(cfg, B=1), x1)
     for u, v in zip(one, a):
         assert np.array_equal(u[0], v[2])
+
+
+def run_decode_step(cfg, x, ws=None, seqs_nc=None):
+    """The whole step through csa_decode_step, and the same step through the
+    separate calls; returns both results (kv row N-1, idx, out, lse)."""
+    L = _L()
+    B, N, m, k, W, Tq = cfg.B, cfg.N, cfg.m, cfg.top_k, cfg.W, cfg.Tq
+    pos = np.tile(np.arange(cfg.n - Tq, cfg.n, dtype=np.int32), (B, 1))
+    nc = np.full((B,), N, np.int32) if seqs_nc is None else np.asarray(seqs_nc, np.int32)
+    q_pos, n_comp = _t(pos), _t(nc)
+    if cfg.k_dtype == "fp8":
+        k_t, sc = _t(x["k_idx_codes"]), _t(x["k_scale"])
+    elif cfg.k_dtype == "mxfp4":
+        k_t, sc = _t(x["k_idx_codes"]).view(torch.float4_e2m1fn_x2), _t(x["k_scale"])
+    else:
+        k_t, sc = _bf(x["k_idx"]), None
+    qi = _bf(x["q_idx"] if Tq > 1 else x["q_idx"][:, None])
+    wt = _t(x["w"] if Tq > 1 else x["w"][:, None])
+    q = _bf(x["q"] if Tq > 1 else x["q"][:, None])
+    win, wl = _kv(cfg, x["kv_win"]), _t(np.full((B,), W + Tq - 1, np.int32))
+    comp = [_bf(x[nm]) for nm in ("Ca", "Cb", "Za", "Zb")]
+    res = []
+    for fused in (True, False):
+        kv = _kv(cfg, x["kv_comp"])
+        idx = torch.full((B, Tq, k), -7, dtype=torch.int32, device=DEV)
+        tsc = torch.full((B, Tq, k), 7.0, device=DEV)
+        out = torch.empty((B, Tq, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((B, Tq, cfg.H), device=DEV)
+        if fused:
+            L.csa_decode_step(*comp, _t(x["Ba"]), _t(x["Bb"]), qi, wt, k_t, sc, q_pos, n_comp, q, kv, win, wl,
+                              _t(x["sink"]), idx, out, lse, tsc, m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1,
+                              blk_end=N, ws=ws)
+        else:
+            L.csa_compress_indexer_score_topk(*comp, _t(x["Ba"]), _t(x["Bb"]), kv, qi, wt, k_t, sc, q_pos, n_comp,
+                                              idx, tsc, m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1,
+                                              blk_end=N)
+            L.sparse_mqa_decode_multi(q, kv, idx, win, wl, _t(x["sink"]), out, lse)
+        torch.cuda.synchronize()
+        res.append((host(kv[:, N - 1]), host(idx), host(tsc), host(out), host(lse)))
+    return res
+
+
+def _same(a, b, what):
+    for i, nm in enumerate(("kv row N-1", "idx", "topk scores", "out", "lse")):
+        assert np.array_equal(a[i], b[i], equal_nan=True), f"{what}: {nm} differs between the fused and separate paths"
+
+
+@pytest.mark.parametrize("name", ["c2_reduced", "c2m_reduced", "c2f_reduced", "c2x_reduced", "c5_reduced"])
+def test_decode_step_equals_separate_reduced(name):
+    base = {"c2_reduced": gen.C2, "c2m_reduced": gen.C2M, "c2f_reduced": gen.C2F, "c2x_reduced": gen.C2X,
+            "c5_reduced": gen.C5}[name]
+    cfg = gen.scaled(base, B=6, n=4 * 40000 if base is gen.C5 else 16384)
+    x = gen.gen_decode(cfg)
+    print(f"[case] decode step {name}", flush=True)
+    fz, sp = run_decode_step(cfg, x)
+    _same(fz, sp, name)
+    # short rows: sequences that see fewer entries than top_k or just over it
+    nc = [cfg.N, 3, cfg.top_k, cfg.top_k + 1, cfg.N // 2 + 1, 1]
+    fz, sp = run_decode_step(cfg, x, seqs_nc=nc)
+    _same(fz, sp, name + " short rows")
+    K = np.minimum(cfg.top_k, np.asarray(nc))
+    for b in range(cfg.B):
+        for t in range(cfg.Tq):
+            assert np.all(fz[1][b, t, K[b]:] == -1) and np.all(np.isneginf(fz[2][b, t, K[b]:]))
+
+
+def test_decode_step_workspace_garbage_and_reuse():
+    cfg = gen.scaled(gen.C2, B=5, n=65536)
+    x = gen.gen_decode(cfg)
+    L = _L()
+    nb = L.csa_decode_step_workspace_bytes(cfg.B, 1, cfg.N, cfg.top_k, cfg.H, cfg.D, cfg.W)
+    for what, ws in (("garbage", torch.randint(0, 256, (nb,), dtype=torch.uint8, device=DEV)),
+                     ("zeroed", torch.zeros(nb, dtype=torch.uint8, device=DEV))):
+        for rep in range(2):  # the second call reads what the first left
+            print(f"[case] decode step workspace {what} call {rep}", flush=True)
+            fz, sp = run_decode_step(cfg, x, ws=ws)
+            _same(fz, sp, f"{what} workspace, call {rep}")
+
+
+@pytest.mark.parametrize("name", ["c2", "c5", "c2m"])
+def test_decode_step_full_size_sampled(name):
+    """The step as bench.py runs it, at full size: the same bits as the
+    separate calls, and sampled sequences against the oracle."""
+    cfg = {"c2": gen.C2, "c5": gen.C5, "c2m": gen.C2M}[name]
+    x = gen.gen_decode(cfg)
+    print(f"[case] decode step {cfg.name}", flush=True)
+    fz, sp = run_decode_step(cfg, x)
+    _same(fz, sp, cfg.name)
+    kvN1, I, TS, O, LSE = fz
+    m, N = cfg.m, cfg.N
+    for b in ([0, cfg.B - 1] if cfg.B > 2 else [0]):
+        ent = oracle.compress(x["Ca"][b], x["Cb"][b], x["Za"][b], x["Zb"][b], x["Ba"], x["Bb"], m,
+                              blocks=range(1, 2))[0]
+        _check_entry(cfg, kvN1[b], ent, "compressed entry N-1")
+        comp = _kv_values(cfg, x["kv_comp"][b])
+        comp[N - 1] = _kv_values(cfg, kvN1[b])
+        if cfg.k_dtype == "fp8":
+            keys, ksc = oracle.e4m3_decode(x["k_idx_codes"][b]), x["k_scale"][b]
+        else:
+            keys, ksc = x["k_idx"][b], None
+        win = _kv_values(cfg, x["kv_win"][b])
+        for t in range(cfg.Tq):
+            p = cfg.n - cfg.Tq + t
+            print(f"[case] {cfg.name} b={b} t={t}", flush=True)
+            q = x["q"][b][t] if cfg.Tq > 1 else x["q"][b]
+            qi = x["q_idx"][b][t] if cfg.Tq > 1 else x["q_idx"][b]
+            wv = x["w"][b][t] if cfg.Tq > 1 else x["w"][b]
+            wrows = win[t:t + cfg.W]
+            oidx, o_ref, lse_ref, s = oracle.csa_query(q, qi, wv, comp, keys, p, N, m, cfg.top_k, wrows, x["sink"],
+                                                       k_scale=ksc)
+            check_topk_row(I[b, t], oidx, s, cfg.top_k, f"b={b} t={t}")
+            rows = np.concatenate([comp[I[b, t][I[b, t] >= 0]], wrows])
+            o_own, lse_own = oracle.attend(q, rows, x["sink"])
+            check_out(O[b, t], o_own, _tight(o_own), f"out on gpu idx b={b} t={t}")
+            assert np.abs(LSE[b, t] - lse_own).max() < 1e-3

@@ -16,7 +16,10 @@ Sources (web pages on DeepSeek-V4, cited by title and section):
           m'=128, 64 query heads x 512, sliding window 128) and section 5
           (tokens beyond the last multiple of m are not compressed).
   [WIKI]  "DeepSeek V4 技术深度 …（DeepTech 深科技）", 5 大架构 item 1
-          (CSA every 4 tokens, HCA every 128) and the batch-invariance note.
+          (CSA every 4 tokens, HCA every 128).
+  [CSDN] section 八 "MegaMoE 超级内核与训练稳定性" carries the
+          batch-invariance remark (a token's output does not depend on where
+          it sits in a batch); every function here works on one row at a time.
 
 Readings where the pages are silent or garbled (each also listed in the design
 notes of the repository):
@@ -173,11 +176,6 @@ def compress(Ca, Cb, Za, Zb, Ba, Bb, m: int, overlap: bool = True, joint: bool =
             if has_b:
                 out[r] += (_softmax_axis0(zb) * Cb[b]).sum(axis=0)
     return out
-
-
-def compress_weights(Za, Ba, m: int, i: int) -> np.ndarray:
-    """The a-branch softmax weights of block i ([m, d]); used by invariants."""
-    return _softmax_axis0(np.asarray(Za, F64)[m * i:m * i + m] + np.asarray(Ba, F64))
 
 
 # ----------------------------------------------------------------------------

@@ -28,3 +28,22 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Report the attention output checks: count and the worst max-abs error
+    relative to the oracle's RMS and to its largest magnitude."""
+    try:
+        from tests.parity_util import REPORT
+    except Exception:
+        return
+    if not REPORT:
+        return
+    tr = terminalreporter
+    rel = [(mx / rms if rms else 0.0, mx / big if big else 0.0, mx, what) for what, mx, rms, big in REPORT]
+    tr.write_sep("-", f"attention output checks: {len(REPORT)}")
+    for r_rms, r_big, mx, what in sorted(rel, reverse=True)[:8]:
+        tr.write_line(f"  max-abs {mx:.3e}  /rms {r_rms:.3e}  /max|ref| {r_big:.3e}  {what}")
+    worst = max(rel)
+    tr.write_line(f"  worst max-abs/rms(oracle) {worst[0]:.3e}; worst max-abs/max|oracle| "
+                  f"{max(r[1] for r in rel):.3e}; largest max-abs {max(r[2] for r in rel):.3e}")

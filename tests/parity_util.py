@@ -7,8 +7,10 @@ Comparison contract:
     1e-6 max|s|). Outside the band the GPU and oracle sets must be equal, and
     both must hold K' = min(k, V) entries, in ascending order, -1 padded.
   * attention outputs: max-abs <= 2e-2 against the float64 oracle, plus a
-    tighter bound derived from the arithmetic (bf16 storage of P and of the
-    output: relative 2^-8 of the output scale) reported and asserted.
+    tighter bound derived from the arithmetic, scaled with the output
+    (out_bound), both asserted. Every check is recorded with its max-abs and
+    the oracle's RMS and largest magnitude; the session prints the worst
+    ratios at its end (tests/conftest.py).
 """
 from __future__ import annotations
 
@@ -17,6 +19,22 @@ import torch
 
 DEV = "cuda:0"
 OUT_TOL = 2e-2
+# (what, max-abs error, rms of the oracle output, max |oracle output|) of every output check
+REPORT = []
+
+
+def out_bound(ref, exact: bool = False) -> float:
+    """The bound the arithmetic allows, proportional to the output's size.
+
+    bf16 paths round each softmax weight P to bf16 for the PV product and the
+    output to bf16 once more: each rounding errs by at most 2^-9 relative, and
+    the P roundings enter as a weighted sum of independent errors, so the
+    error stays a small multiple of 2^-9 max|o|; 2^-7 max|o| leaves a factor 4.
+    fp32 rows and outputs (exact=True) keep every value in fp32: 1e-5 max|o|.
+    There is no absolute floor: an all-zero output must come out exactly zero.
+    """
+    mx = float(np.abs(np.asarray(ref, np.float64)).max(initial=0.0))
+    return (1e-5 if exact else 2.0 ** -7) * mx
 
 
 def dev(x: np.ndarray, dtype=None) -> torch.Tensor:
@@ -65,10 +83,14 @@ def check_topk_row(gpu_idx: np.ndarray, oracle_idx: np.ndarray, oracle_scores: n
 
 
 def check_out(gpu: np.ndarray, ref: np.ndarray, tight: float, what=""):
+    ref = np.asarray(ref, np.float64)
     err = np.abs(np.asarray(gpu, np.float64) - ref)
     mx = float(err.max()) if err.size else 0.0
     rms = float(np.sqrt((ref ** 2).mean())) if ref.size else 0.0
+    big = float(np.abs(ref).max(initial=0.0))
+    REPORT.append((what, mx, rms, big))
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
     assert mx <= OUT_TOL, f"{what}: max-abs {mx:.3e} > {OUT_TOL}"
-    assert mx <= tight, f"{what}: max-abs {mx:.3e} > derived bound {tight:.1e} (rms ref {rms:.3e})"
+    assert mx <= tight, (f"{what}: max-abs {mx:.3e} > derived bound {tight:.2e} "
+                         f"(max-abs/rms {mx / rms if rms else 0:.3e}, max|ref| {big:.3e})")
     return mx, rms

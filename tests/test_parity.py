@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from synth import gen
-from tests.parity_util import DEV, bf, check_out, check_topk_row, dev, host
+from tests.parity_util import DEV, bf, check_out, check_topk_row, dev, host, out_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -400,9 +400,8 @@ def test_topk_workspace_garbage_and_oversized():
 # ------------------------------------------------------------------ attention
 
 def _attn_tight(ref, kv_dt="bf16"):
-    """P is rounded to bf16 for the PV product and bf16 outputs are rounded
-    once more: a relative error of about 2^-8 of the output scale."""
-    return (2.0 ** -7 if kv_dt == "bf16" else 1e-5) * max(1.0, float(np.abs(ref).max(initial=0.0)))
+    """The arithmetic's bound (out_bound): bf16 P and output, or fp32 throughout."""
+    return out_bound(ref, exact=kv_dt != "bf16")
 
 
 def test_sparse_decode_edge_rows():

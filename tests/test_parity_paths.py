@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from synth import gen
-from tests.parity_util import DEV, check_out, check_topk_row, host
+from tests.parity_util import DEV, check_out, check_topk_row, host, out_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +29,7 @@ def _t(v):
 
 
 def _tight(ref):
-    return 2.0 ** -7 * max(1.0, float(np.abs(ref).max(initial=0.0)))
+    return out_bound(ref)
 
 
 def _kv(cfg, rows):
@@ -149,12 +149,12 @@ def test_csa_decode_pro_fp8_reduced():
 
 def test_csa_decode_flash_full_size_sampled():
     cfg = gen.C2  # 32 sequences x 128K tokens, as bench.py
-    check_csa_decode(cfg, gen.gen_decode(cfg), [0, 13, 31])
+    check_csa_decode(cfg, gen.gen_decode(cfg), [0, 1, 7, 8, 13, 20, 30, 31])
 
 
 def test_csa_decode_pro_1m_fp8_full_size_sampled():
     cfg = gen.C5  # 4 sequences x 1M tokens, fp8 indexer keys
-    check_csa_decode(cfg, gen.gen_decode(cfg), [1, 3])
+    check_csa_decode(cfg, gen.gen_decode(cfg), range(cfg.B))
 
 
 def run_hca_decode(cfg, x):

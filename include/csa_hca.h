@@ -313,6 +313,34 @@ int csa_decode_step(const void* Ca, const void* Cb, const void* Za, const void* 
                     void* ws, size_t ws_bytes, void* stream);
 size_t csa_decode_step_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k, int H, int D, int W);
 
+/*
+ * csa_decode_step_noalloc — csa_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc). Arguments and results are those of
+ * csa_decode_step without ws / ws_bytes: the scratch is a device array of
+ * CSA_STEP_SCRATCH_BYTES inside the library, one per device, held from the
+ * library's load until the process ends. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).
+ *   Limit: csa_decode_step_workspace_bytes(B, Tq, N_max, top_k, H, D, W) must
+ *   not exceed CSA_STEP_SCRATCH_BYTES (a C2-sized step, 32 sequences of 128K
+ *   tokens, needs about 30 MB); above it the call returns
+ *   CSA_WORKSPACE_TOO_SMALL before any GPU work.
+ *   Every call on a device shares that device's array: calls that overlap on
+ *   one device (two streams, two threads) race and must be serialised by the
+ *   caller. Results never depend on what the array holds; the first call of a
+ *   shape on a device clears the region it uses with a fill kernel (no
+ *   hipMemset), so later calls of that shape take the fast path.
+ */
+#define CSA_STEP_SCRATCH_BYTES ((size_t)64 << 20)
+int csa_decode_step_noalloc(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                            const float* Bb, int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin,
+                            int64_t blk_end, int flags, int in_dt, const void* q_idx, const float* w,
+                            const void* k_idx, const void* k_scale, const int32_t* q_pos, const int32_t* n_comp,
+                            int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt,
+                            int k_dt, const void* q, void* kv_comp, const void* kv_win, const int32_t* win_len,
+                            const float* sink, float scale, int H, int D, int W, int kv_dt, int out_dt,
+                            int32_t* topk_idx, float* topk_score, void* out, float* lse, void* stream);
+
 /* sparse_mqa_prefill — Tq queries of one sequence.
  *   q      : [Tq, H, D]          kv_comp : [N, D]
  *   topk_idx : [Tq, top_k] int32 (-1 = empty)

@@ -54,6 +54,9 @@ _SIGS = {
                         + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32] + [_vp] * 5
                         + [_f32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
     "csa_decode_step_workspace_bytes": ([_i64, _i64, _i64, _i32, _i32, _i32, _i32], _sz),
+    "csa_decode_step_noalloc": ([_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i64, _i32, _i32] + [_vp] * 6
+                                + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32] + [_vp] * 5
+                                + [_f32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 5, _i32),
     "indexer_topk_workspace_bytes": ([_i64, _i64, _i64, _i32], _sz),
     "indexer_score_topk": ([_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
                                         _vp], _i32),
@@ -239,6 +242,31 @@ def csa_decode_step(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, n_c
         N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len), _ptr(sink),
         scale, H, D, W, _kv_dt(q, kv_comp), _dt(out), _ptr(topk_idx), _ptr(topk_score), _ptr(out), _ptr(lse),
         _ptr(ws), nb, _stream(stream)))
+
+
+STEP_SCRATCH_BYTES = 64 << 20  # CSA_STEP_SCRATCH_BYTES: the scratch csa_decode_step_noalloc holds per device
+
+
+def csa_decode_step_noalloc(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, n_comp, q, kv_comp, kv_win,
+                            win_len, sink, topk_idx, out, lse=None, topk_score=None, *, m_c: int, m: int,
+                            tok_begin: int = 0, blk_begin: int = 0, blk_end: Optional[int] = None,
+                            overlap: bool = True, joint: bool = False, scale: float = 1.0, stream=None) -> None:
+    """csa_decode_step with the library's own per-device scratch: allocates nothing."""
+    _, n_rows, d = Ca.shape
+    if blk_end is None:
+        blk_end = (tok_begin + n_rows) // m_c
+    flags = (OVERLAP if overlap else 0) | (JOINT_SOFTMAX if joint else 0)
+    B, Tq, H_I, D_I = q_idx.shape
+    N_max = k_idx.shape[1]
+    top_k = topk_idx.shape[-1]
+    H, D = q.shape[-2], q.shape[-1]
+    W = kv_win.shape[1] - Tq + 1
+    _check(lib.csa_decode_step_noalloc(
+        _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), n_rows, tok_begin, d, m_c, blk_begin, blk_end,
+        flags, _dt(Ca), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I,
+        N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len), _ptr(sink),
+        scale, H, D, W, _kv_dt(q, kv_comp), _dt(out), _ptr(topk_idx), _ptr(topk_score), _ptr(out), _ptr(lse),
+        _stream(stream)))
 
 
 def indexer_topk_workspace_bytes(B: int, Tq: int, N_max: int, top_k: int) -> int:

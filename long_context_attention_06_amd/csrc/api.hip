@@ -2,6 +2,7 @@
 // before any HIP call), workspace sizing, split planning and kernel dispatch.
 // The operations and their sources are documented in include/csa_hca.h.
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/csa_hca.h"
@@ -306,14 +307,15 @@ size_t csa_decode_step_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int
                            attn_ws(nq, H, D, ns)));
 }
 
-int csa_decode_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba, const float* Bb,
-                    int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin, int64_t blk_end,
-                    int flags, int in_dt, const void* q_idx, const float* w, const void* k_idx,
-                    const void* k_scale, const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq,
-                    int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt, int k_dt, const void* q,
-                    void* kv_comp, const void* kv_win, const int32_t* win_len, const float* sink, float scale, int H,
-                    int D, int W, int kv_dt, int out_dt, int32_t* topk_idx, float* topk_score, void* out, float* lse,
-                    void* ws, size_t ws_bytes, void* stream) {
+static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                            const float* Bb, int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin,
+                            int64_t blk_end, int flags, int in_dt, const void* q_idx, const float* w,
+                            const void* k_idx, const void* k_scale, const int32_t* q_pos, const int32_t* n_comp,
+                            int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt,
+                            int k_dt, const void* q, void* kv_comp, const void* kv_win, const int32_t* win_len,
+                            const float* sink, float scale, int H, int D, int W, int kv_dt, int out_dt,
+                            int32_t* topk_idx, float* topk_score, void* out, float* lse, void* ws, size_t ws_bytes,
+                            void* stream) {
   REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
   REQ(Tq >= 1 && Tq <= 64, CSA_INVALID_ARG, "Tq must be in [1, 64]");
   const int64_t nq = B * Tq;
@@ -435,6 +437,98 @@ int csa_decode_step(const void* Ca, const void* Cb, const void* Za, const void* 
   at.out = out;
   at.lse = lse;
   return hip_status(csa::run_attn(at, st), "csa_decode_step");
+}
+
+int csa_decode_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba, const float* Bb,
+                    int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin, int64_t blk_end,
+                    int flags, int in_dt, const void* q_idx, const float* w, const void* k_idx,
+                    const void* k_scale, const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq,
+                    int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt, int k_dt, const void* q,
+                    void* kv_comp, const void* kv_win, const int32_t* win_len, const float* sink, float scale, int H,
+                    int D, int W, int kv_dt, int out_dt, int32_t* topk_idx, float* topk_score, void* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream) {
+  return decode_step_impl(Ca, Cb, Za, Zb, Ba, Bb, n_rows, tok_begin, d, m_c, blk_begin, blk_end, flags, in_dt, q_idx,
+                          w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, top_k, q_dt, k_dt, q, kv_comp,
+                          kv_win, win_len, sink, scale, H, D, W, kv_dt, out_dt, topk_idx, topk_score, out, lse, ws,
+                          ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the decode step for callers that cannot allocate: its scratch is the
+// file-scope device array below (each device holds its own copy, at its own
+// address, from the library's load until the process ends). In host code the
+// array's name is only a stand-in: kernels get the address that
+// hipGetSymbolAddress returned for the current device.
+static __device__ __align__(256) uint8_t scratch[CSA_STEP_SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_DEVICES = 64;
+struct ScratchDev {
+  void* ptr = nullptr;    // this device's address of `scratch`
+  int64_t shape[7] = {};  // the previous call's shape, which fixes the scratch layout
+  bool used = false;
+};
+std::mutex g_scratch_mu;
+ScratchDev g_scratch[SCRATCH_DEVICES];
+
+__global__ void zero_fill_kernel(uint4* p, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+}
+}  // namespace
+
+extern "C" {
+
+int csa_decode_step_noalloc(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                            const float* Bb, int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin,
+                            int64_t blk_end, int flags, int in_dt, const void* q_idx, const float* w,
+                            const void* k_idx, const void* k_scale, const int32_t* q_pos, const int32_t* n_comp,
+                            int64_t B, int64_t Tq, int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt,
+                            int k_dt, const void* q, void* kv_comp, const void* kv_win, const int32_t* win_len,
+                            const float* sink, float scale, int H, int D, int W, int kv_dt, int out_dt,
+                            int32_t* topk_idx, float* topk_score, void* out, float* lse, void* stream) {
+  const size_t need = csa_decode_step_workspace_bytes(B, Tq, N_max, top_k, H, D, W);
+  REQ(need <= CSA_STEP_SCRATCH_BYTES, CSA_WORKSPACE_TOO_SMALL,
+      "csa_decode_step_noalloc: the step needs " + std::to_string(need) + " bytes of scratch, above the " +
+          std::to_string((size_t)CSA_STEP_SCRATCH_BYTES) + " this form holds; use csa_decode_step");
+  int dev = 0;
+  int rc = hip_status(hipGetDevice(&dev), "csa_decode_step_noalloc: hipGetDevice");
+  if (rc) return rc;
+  REQ(dev >= 0 && dev < SCRATCH_DEVICES, CSA_UNSUPPORTED, "csa_decode_step_noalloc: device index above 63");
+  void* ptr = nullptr;
+  bool clear = false;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    ScratchDev& sd = g_scratch[dev];
+    if (!sd.ptr) {
+      void* p = nullptr;
+      rc = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "csa_decode_step_noalloc: hipGetSymbolAddress");
+      if (rc) return rc;
+      REQ(p && ((uintptr_t)p & 255u) == 0, CSA_HIP_ERROR, "csa_decode_step_noalloc: scratch address not usable");
+      sd.ptr = p;
+    }
+    const int64_t shape[7] = {B, Tq, N_max, top_k, H, D, W};
+    clear = !sd.used || !std::equal(shape, shape + 7, sd.shape);
+    std::copy(shape, shape + 7, sd.shape);
+    sd.used = true;
+    ptr = sd.ptr;
+  }
+  // Results never depend on the scratch's contents; zeros (or what a call of
+  // the same shape left) let the selection use the scan's histogram. A new
+  // layout is cleared by a fill kernel, which a graph capture can hold.
+  if (clear && need > 0) {
+    const size_t n16 = (need + 15) / 16;
+    const unsigned blocks = (unsigned)std::min<size_t>((n16 + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<uint4*>(ptr), n16);
+    rc = hip_status(hipGetLastError(), "csa_decode_step_noalloc: clear");
+    if (rc) return rc;
+  }
+  return decode_step_impl(Ca, Cb, Za, Zb, Ba, Bb, n_rows, tok_begin, d, m_c, blk_begin, blk_end, flags, in_dt, q_idx,
+                          w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, top_k, q_dt, k_dt, q, kv_comp,
+                          kv_win, win_len, sink, scale, H, D, W, kv_dt, out_dt, topk_idx, topk_score, out, lse, ptr,
+                          CSA_STEP_SCRATCH_BYTES, stream);
 }
 
 size_t sparse_mqa_decode_multi_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int top_k, int W) {

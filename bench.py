@@ -6,12 +6,13 @@ compressed entries of dim 512), 64 indexer heads x 128, top-k 512, 64 query
 heads x 512, a 128-token window and a sink, bf16. One step is one decode token
 per sequence through the whole path:
     csa_compress   (entry N-1 completes at this token: n is a multiple of m)
-    indexer_score  (the dominant HBM stream)
-    indexer_topk
-    sparse_mqa_decode (split attention + combine)
-Inputs are synthetic (seeded generator), resident in HBM before timing, and
-rotated over several device replicas so that no step reads cache-resident
-data from the previous one.
+    indexer_score  (the dominant HBM stream; one launch with the compression)
+    top-k, sparse MQA and the merge of its splits (one launch)
+as one csa_decode_step call. Inputs are synthetic (seeded generator),
+resident in HBM before timing, and rotated over several device replicas so
+that no step reads cache-resident data from the previous one. The default
+line also carries c5, c4 and c3 (below), each timed the same way, under
+"workloads".
 
 Other workloads: c5 (1M context, E4M3 indexer keys), c2x (c2 with MXFP4
 indexer keys), c4 (HCA decode 1M), c3 (CSA prefill 64K), c6 (HCA prefill 64K),
@@ -19,7 +20,7 @@ c4f / c2f / c3f (c4 / c2 / c3 with the main KV rows in E4M3 + bf16 RoPE dims),
 c2r (c2 with the query RMSNorm + RoPE prologue and the output inverse RoPE),
 c2m (c2 with two query tokens per sequence and step).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
                        [--workload c2|c5|c4|c3|c2x|c6|c4f|c2f|c3f|c2r|c2m]
 Prints one JSON line.
 """
@@ -52,11 +53,18 @@ def _args():
                     choices=["c2", "c5", "c4", "c3", "c2x", "c6", "c4f", "c2f", "c3f", "c2r", "c2m"])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--extra-cpu-seconds", type=float, default=4.0,
+                    help="budget of the CPU baseline of each secondary workload")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="with the default workload, skip the secondary workloads (c5, c4, c3)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 1 GiB device-to-device copies: the known-size reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+EXTRAS = ("c5", "c4", "c3")  # secondary workloads carried by the default line
 
 
 def _src_hash(names):
@@ -86,6 +94,65 @@ def _traffic(kernel_file: str, src_files):
         return None
 
 
+def _roofline(bound, kernel, work, ms, peak, unit, traffic=None, copy_gbs=None):
+    """achieved = algorithmic work per launch / average launch duration."""
+    ach = work / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+    r = {"bound": bound, "kernel": kernel, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+         "frac": round(ach / peak, 4), "traffic": traffic,
+         ("algorithmic_bytes_per_launch" if unit == "GB/s" else "algorithmic_flops_per_launch"): work,
+         "avg_launch_ms": round(ms, 4)}
+    if copy_gbs and unit == "GB/s":
+        r["frac_of_copy"] = round(ach / copy_gbs, 4)  # against the on-box device copy rate
+    return r
+
+
+def measure_copy(torch, dev):
+    """On-box rate of a plain 1 GiB device-to-device copy (read + write bytes
+    per second): the practical ceiling the HBM fractions are also quoted against."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
+def _graph_loop_ms(torch, fn, steps):
+    """Average duration of fn(i), i < steps, launched back to back: captured
+    in one HIP graph so no host work sits between the launches, replayed once
+    between two events on the current stream."""
+    side = torch.cuda.Stream()  # default priority, as every stream here
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g
+    return ms
+
+
 def main():
     a = _args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -110,12 +177,39 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
                           "copies": 3}), flush=True)
         return
-    if a.workload in ("c3", "c3f"):
-        return bench_prefill(a, torch, L, gen, dev, gen.C3F if a.workload == "c3f" else gen.C3)
-    if a.workload == "c6":
-        return bench_hca_prefill(a, torch, L, gen, dev)
+    copy_gbs = measure_copy(torch, dev)
+    res = run_workload(a.workload, a, torch, L, gen, dev, a.steps, a.warmup,
+                       None if a.no_cpu else a.cpu_seconds, copy_gbs)
+    res["copy_gbs"] = copy_gbs
+    if a.workload == "c2" and not a.no_extras:
+        # the other headline configurations, each timed the same way (fewer
+        # steps, a shorter CPU baseline), under "workloads"
+        res["workloads"] = {}
+        for w in EXTRAS:
+            torch.cuda.empty_cache()
+            r = run_workload(w, a, torch, L, gen, dev, min(a.steps, 20), min(a.warmup, 3),
+                             None if a.no_cpu else a.extra_cpu_seconds, copy_gbs)
+            res["workloads"][w] = {k: v for k, v in r.items() if k not in (
+                "metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "dtype", "data")}
+    print(json.dumps(res), flush=True)
+
+
+def run_workload(w, a, torch, L, gen, dev, steps, warmup, cpu_s, copy_gbs):
+    if w in ("c3", "c3f"):
+        return bench_prefill(a, torch, L, gen, dev, gen.C3F if w == "c3f" else gen.C3, steps, warmup, cpu_s)
+    if w == "c6":
+        return bench_hca_prefill(a, torch, L, gen, dev, steps, warmup, cpu_s)
     cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X, "c4f": gen.C4F, "c2f": gen.C2F,
-           "c2r": gen.C2R, "c2m": gen.C2M}[a.workload]
+           "c2r": gen.C2R, "c2m": gen.C2M}[w]
+    return bench_decode(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, copy_gbs, w)
+
+
+def _base(steps, warmup):
+    return {"metric": METRIC, "n_gpus": 1, "steps": steps, "warmup": warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+
+
+def bench_decode(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, copy_gbs, wname):
     t0 = time.time()
     x = gen.gen_decode(cfg, with_compress=True)
     print(f"[bench] generated {cfg.name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -164,25 +258,21 @@ def main():
         # scores, digit histograms, top-k and attention scratch; zero-filled
         # once, as the step leaves it (its histograms cleared after use)
         ws_t = torch.zeros(L.csa_decode_step_workspace_bytes(B, Tq, N, k, H, D, W), dtype=torch.uint8, device=dev)
-        scores = ws_t[:B * Tq * N * 4].view(torch.float32).view(B, Tq, N)
         ws_a = None
     else:
         ws_a = torch.empty(max(1, L.hca_dense_mqa_workspace_bytes(B, H, D, N, W)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
 
-    def rec(ev, i):
-        if ev is not None:
-            ev[i].record(stream)
-
-    def step(r, ev=None):
-        rec(ev, 0)
+    def step(r, pre=None):
+        if pre is not None:
+            pre.record(stream)
         q_att = r["q"]
         if cfg.qk_rope:  # prologue: RMSNorm + RoPE of the raw queries at their position
             L.qk_norm_rope(r["q"], qn, shared["pos"], shared["q_gamma"], norm=True, rope=True, stream=s)
             q_att = qn
         if cfg.kind == "csa_decode":
-            # the whole step in one call: the completed block's entry, the
+            # the whole step in one call: the completed block's entry with the
             # indexer scan, then top-k, attention and split merge
             L.csa_decode_step(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"], r["q_idx"], r["w"],
                               r["k_idx"], r.get("k_scale"), shared["q_pos"], shared["n_comp"],
@@ -190,110 +280,127 @@ def main():
                               shared["win_len"], shared["sink"], idx, out if Tq > 1 else out.view(B, 1, H, D),
                               m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, scale=att_scale,
                               ws=ws_t, stream=s)
-            rec(ev, 1)
-            rec(ev, 2)
-            rec(ev, 3)
             if cfg.qk_rope:  # epilogue: the output's rotated dims turned back
                 L.qk_norm_rope(out, out, shared["pos"], inverse=True, stream=s)
         else:
             # HCA: the token completes block N-1 (m' divides n): one branch, no overlap
             L.csa_compress(r["Ca"], None, r["Za"], None, shared["Ba"], None, r["kv_comp"], m=m,
                            tok_begin=cfg.n - m, blk_begin=N - 1, blk_end=N, overlap=False, stream=s)
-            rec(ev, 1)
-            rec(ev, 2)
-            rec(ev, 3)
             L.hca_dense_mqa(r["q"], r["kv_comp"], shared["n_comp"], shared["q_pos"].view(B), r["kv_win"],
                             shared["win_len"], shared["sink"], out, m=m, ws=ws_a, stream=s)
 
-    for i in range(a.warmup):
+    for i in range(warmup):
         step(reps[i % len(reps)])
     torch.cuda.synchronize()
-    # (1) the headline: K plain steps between two events
-    e_start = torch.cuda.Event(enable_timing=True)
-    e_end = torch.cuda.Event(enable_timing=True)
+    # (1) the headline: K plain steps between two events; then four more
+    # such runs, for the median over runs
+    runs = []
+    for rep in range(5):
+        e_start = torch.cuda.Event(enable_timing=True)
+        e_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e_start.record(stream)
+        t_wall = time.perf_counter()
+        for i in range(steps):
+            step(reps[i % len(reps)])
+        e_end.record(stream)
+        torch.cuda.synchronize()
+        if rep == 0:
+            wall = time.perf_counter() - t_wall
+        runs.append(e_start.elapsed_time(e_end) / steps)
+    ms_step = runs[0]
+    # (2) the same K steps with the library's phase events (csa_trace_phases):
+    # [0] call start [1] scan launched [2] top-k / fused tail [3] attention
+    # kernel [4] call end, plus an event before each step
+    pre = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for e in pre + [e for es in evs for e in es]:
+        e.record(stream)  # creates the event, so its handle exists
     torch.cuda.synchronize()
-    e_start.record(stream)
-    t_wall = time.perf_counter()
-    for i in range(a.steps):
-        step(reps[i % len(reps)])
-    e_end.record(stream)
+    for i in range(steps):
+        L.trace_phases(evs[i])
+        step(reps[i % len(reps)], pre[i])
+    L.trace_phases(None)
+    pre[steps].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_step = e_start.elapsed_time(e_end) / a.steps
-    # (2) the same K steps with an event at every phase boundary:
-    # [0] compress [1] indexer scan [2] top-k [3] attention [next 0]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
-    e_fin = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    for i in range(a.steps):
-        step(reps[i % len(reps)], evs[i])
-    e_fin.record(stream)
-    torch.cuda.synchronize()
-    nxt = [evs[i + 1][0] for i in range(a.steps - 1)] + [e_fin]
-    ph = np.array([[evs[i][0].elapsed_time(evs[i][1]), evs[i][1].elapsed_time(evs[i][2]),
-                    evs[i][2].elapsed_time(evs[i][3]), evs[i][3].elapsed_time(nxt[i])] for i in range(a.steps)])
+    ph = np.array([[pre[i].elapsed_time(evs[i][0])] + [evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
+                   + [evs[i][4].elapsed_time(pre[i + 1])] for i in range(steps)])
     ph_mean = ph.mean(axis=0)
-    attn_avg = float(ph_mean[3])
-    # (3) the dominant kernel alone, K back-to-back launches between two events
-    # on the stream it runs on: its average launch duration for the roofline
-    e3a, e3b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e3a.record(stream)
-    for i in range(a.steps):
-        r = reps[i % len(reps)]
-        if cfg.kind == "csa_decode":
-            L.indexer_score(r["q_idx"], r["w"], r["k_idx"], r.get("k_scale"), shared["q_pos"], shared["n_comp"],
-                            scores, m=m, stream=s)
-        else:
-            L.hca_dense_mqa(r["q"], r["kv_comp"], shared["n_comp"], shared["q_pos"].view(B), r["kv_win"],
-                            shared["win_len"], shared["sink"], out, m=m, ws=ws_a, stream=s)
-    e3b.record(stream)
-    torch.cuda.synchronize()
-    kern_avg = e3a.elapsed_time(e3b) / a.steps
-    scan_avg = kern_avg
 
-    tokens_per_s = B * Tq / (ms_step * 1e-3)
-    res = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-    }
+    res = _base(steps, warmup)
+    res.update({"value": round(B * Tq / (ms_step * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms_step, 4),
+                "ms_per_step_median_of_5_runs": round(float(np.median(runs)), 4)})
     if cfg.kind == "csa_decode":
         kbytes = {"fp8": N * (cfg.D_I + 4), "mxfp4": N * (cfg.D_I // 2 + cfg.D_I // 32)}.get(cfg.k_dtype, N * cfg.D_I * 2)
-        # keys (+scales) once per sequence (what the method needs), q_idx and w per query
-        scan_bytes = B * (kbytes + Tq * (cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4))
+        # the scan launch: keys (+scales) once per sequence, q_idx and w per
+        # query, the scores it writes, and the compression it carries (the
+        # a-branch block and the overlapping b-branch block, four tensors of m
+        # rows, in; the entry out)
+        comp_bytes = B * (4 * m * D * 2 + rowb)
+        scan_bytes = B * (kbytes + Tq * (cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4 + N * 4)) + comp_bytes
         step_bytes = B * (kbytes + Tq * (cfg.H_I * cfg.D_I * 2 + cfg.H_I * 4 + (k + W) * rowb + H * D * 2 * 2 + k * 4))
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
                          "m": m, "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I,
                          "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype,
                          "kv_dtype": cfg.kv_dtype, "qk_norm_rope": cfg.qk_rope, "query_tokens_per_sequence": Tq}
-        # the scan alone (the step's launch also carries the compression: <.., 1|4>)
-        kname = {"fp8": "idx_scan_lp_kernel<2, 0> (E4M3 keys)", "mxfp4": "idx_scan_lp_kernel<3, 0> (MXFP4 keys)"}.get(
-            cfg.k_dtype, "idx_scan_bf16_kernel<2, 0> (two query rows per workgroup)" if Tq % 2 == 0
-            else "idx_scan_bf16_kernel<1, 0>")
-        res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": round(scan_bytes / (scan_avg * 1e-3) / 1e9, 1),
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(scan_bytes / (scan_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "traffic": _traffic(f"idx_scan_{a.workload}_traffic.txt", ["indexer.hip", "common.h"]),
-                           "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_ms": round(scan_avg, 4)}
-        res["phases_ms"] = {"decode_step": round(float(ph_mean.sum()), 4)}
+        kname = {"fp8": "idx_scan_lp_kernel<2, 1> (E4M3 keys, with the entry's compression)",
+                 "mxfp4": "idx_scan_lp_kernel<3, 1> (MXFP4 keys, with the entry's compression)"}.get(
+            cfg.k_dtype, "idx_scan_bf16_kernel<2, 1> (two query rows per workgroup, with the entry's compression)"
+            if Tq % 2 == 0 else "idx_scan_bf16_kernel<1, 1> (with the entry's compression)")
+        # (3) the step's first launch (compression + scan, the same kernel
+        # instance) K times back to back, as csa_compress_indexer_score runs
+        # it: the step's launch also accumulates the top-k's digit histogram,
+        # which this one skips
+        scores = ws_t[:B * Tq * N * 4].view(torch.float32).view(B, Tq, N)
+
+        def scan(i):
+            r = reps[i % len(reps)]
+            L.csa_compress_indexer_score(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"],
+                                         r["kv_comp"], r["q_idx"], r["w"], r["k_idx"], r.get("k_scale"),
+                                         shared["q_pos"], shared["n_comp"], scores, m_c=m, m=m,
+                                         tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
+
+        scan_ms = _graph_loop_ms(torch, scan, steps)
+        res["roofline"] = _roofline("hbm", kname, scan_bytes, scan_ms, HBM_PEAK_GBS, "GB/s",
+                                    _traffic(f"idx_scan_{wname}_traffic.txt",
+                                             ["indexer.hip", "common.h", "compress_entry.h"]), copy_gbs)
+        # the same launch inside the traced step, between the library's phase
+        # events (which add their own 1-3 us)
+        res["roofline"]["in_step_ms"] = round(float(ph_mean[1]), 4)
+        res["phases_ms"] = {"before_call": round(float(ph_mean[0]), 4), "compress_and_scan": round(float(ph_mean[1]), 4),
+                            "topk_or_fused_tail": round(float(ph_mean[2]), 4),
+                            "attention": round(float(ph_mean[3]), 4), "merge": round(float(ph_mean[4]), 4),
+                            "after_call": round(float(ph_mean[5]), 4)}
         res["step_hbm_gbs"] = round(step_bytes / (ms_step * 1e-3) / 1e9, 1)
+        res["step_algorithmic_bytes"] = step_bytes
         res["indexer_kv_hbm_gbs"] = res["roofline"]["achieved"]
     else:
-        hbytes = B * ((N + W) * rowb + H * D * 2 * 2)
+        # hca_dense_mqa: the split attention kernel and the merge of its
+        # splits (rows once and q in, the output out), K calls back to back
+        abytes = B * ((N + W) * rowb + H * D * 2 * 2)
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
                          "m": m, "heads": H, "head_dim": D, "window": W, "kv_dtype": cfg.kv_dtype}
-        res["phases_ms"] = {"compress": round(float(ph_mean[0]), 4), "attention": round(attn_avg, 4)}
-        res["roofline"] = {"bound": "hbm", "kernel": "hca_dense_mqa (attn_bf16_kernel<1, %s> HCA splits + combine)"
-                           % ("true" if cfg.kv_dtype == "fp8" else "false"),
-                           "achieved": round(hbytes / (kern_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(hbytes / (kern_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "traffic": None, "algorithmic_bytes_per_launch": hbytes, "avg_launch_ms": round(kern_avg, 4)}
-    res["wall_s_timed"] = round(wall, 3)
+        res["phases_ms"] = {"append": round(float(ph_mean[0]), 4), "attention": round(float(ph_mean[3]), 4),
+                            "merge": round(float(ph_mean[4]), 4)}
 
-    if not a.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(cfg, x, a.cpu_seconds)
-    print(json.dumps(res), flush=True)
+        def hca(i):
+            r = reps[i % len(reps)]
+            L.hca_dense_mqa(r["q"], r["kv_comp"], shared["n_comp"], shared["q_pos"].view(B), r["kv_win"],
+                            shared["win_len"], shared["sink"], out, m=m, ws=ws_a)
+
+        attn_ms = _graph_loop_ms(torch, hca, steps)
+        fp8 = cfg.kv_dtype == "fp8"
+        res["roofline"] = _roofline("hbm", "hca_dense_mqa: attn_bf16_kernel<1, %s> (HCA decode splits) + "
+                                    "attn_combine_kernel" % ("true" if fp8 else "false"),
+                                    abytes, attn_ms, HBM_PEAK_GBS, "GB/s",
+                                    _traffic(f"attn_hca_{wname}_traffic.txt", ["attn.hip", "attn_core.h", "common.h"]),
+                                    copy_gbs)
+        res["step_hbm_gbs"] = round(abytes / (ms_step * 1e-3) / 1e9, 1)
+    res["wall_s_timed"] = round(wall, 3)
+    if cpu_s is not None:
+        res["cpu_baseline"] = cpu_baseline(cfg, x, cpu_s)
+    del reps, base
+    return res
 
 
 def prefill_flops(cfg, pos):
@@ -306,7 +413,7 @@ def prefill_flops(cfg, pos):
     return idx, mqa
 
 
-def bench_prefill(a, torch, L, gen, dev, cfg):
+def bench_prefill(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s):
     """CSA prefill of one 65536-token sequence: compression of all tokens, then
     16 chunks of 4096 queries through scores, top-k and sparse MQA (main KV
     rows in bf16, or E4M3 + bf16 RoPE dims)."""
@@ -335,23 +442,23 @@ def bench_prefill(a, torch, L, gen, dev, cfg):
     ws_t = torch.zeros(L.indexer_score_topk_workspace_bytes(1, T, N, k), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
+    ev = None
 
-    def run(ev=None):
-        if ev is not None: ev[0].record(stream)
+    def run(trace=False):
+        if trace: ev["pre"].record(stream)
         L.csa_compress(Ca, Cb, Za, Zb, Ba, Bb, comp, m=m, stream=s)
-        if ev is not None: ev[1].record(stream)
         for c, ch in enumerate(chunks):
+            if trace: L.trace_phases(ev["idx"][c])  # [0] start [1] scan launched [2..4] top-k done
             L.indexer_score_topk(ch["q_idx"], ch["w"], k_idx, None, ch["q_pos"], n_comp, idx, m=m, ws=ws_t,
                                  stream=s)
-            if ev is not None: ev[2 + 3 * c].record(stream)
-            if ev is not None: ev[3 + 3 * c].record(stream)
             L.sparse_mqa_prefill(ch["q"], comp[0], idx[0], kv_tok, ch["q_pos"][0], sink, out, W=W, stream=s)
-            if ev is not None: ev[4 + 3 * c].record(stream)
+            if trace: ev["attn"][c].record(stream)
+        if trace: L.trace_phases(None)
 
-    for _ in range(max(1, a.warmup)):
+    for _ in range(max(1, warmup)):
         run()
     torch.cuda.synchronize()
-    steps = max(1, min(a.steps, 5))
+    steps = max(1, min(steps, 5))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
@@ -359,42 +466,40 @@ def bench_prefill(a, torch, L, gen, dev, cfg):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + 3 * nch)]
-    run(ev)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    ev = {"pre": mk(), "idx": [[mk() for _ in range(5)] for _ in range(nch)], "attn": [mk() for _ in range(nch)]}
+    for e in [ev["pre"]] + ev["attn"] + [e for es in ev["idx"] for e in es]:
+        e.record(stream)
     torch.cuda.synchronize()
-    comp_ms = ev[0].elapsed_time(ev[1])
-    prev = [ev[1]] + [ev[4 + 3 * c] for c in range(nch - 1)]
-    idx_ms = [prev[c].elapsed_time(ev[2 + 3 * c]) for c in range(nch)]
-    topk_ms = [ev[2 + 3 * c].elapsed_time(ev[3 + 3 * c]) for c in range(nch)]
-    attn_ms = [ev[3 + 3 * c].elapsed_time(ev[4 + 3 * c]) for c in range(nch)]
+    run(trace=True)
+    torch.cuda.synchronize()
+    comp_ms = ev["pre"].elapsed_time(ev["idx"][0][0])
+    idx_ms = [ev["idx"][c][0].elapsed_time(ev["idx"][c][1]) for c in range(nch)]
+    topk_ms = [ev["idx"][c][1].elapsed_time(ev["idx"][c][4]) for c in range(nch)]
+    attn_ms = [ev["idx"][c][4].elapsed_time(ev["attn"][c]) for c in range(nch)]
     fl = [prefill_flops(cfg, ch["pos_np"]) for ch in chunks]
     idx_fl, mqa_fl = sum(f[0] for f in fl), sum(f[1] for f in fl)
     total_fl = idx_fl + mqa_fl
-    idx_tfs = idx_fl / (sum(idx_ms) * 1e-3) / 1e12  # scores and top-k together
-    mqa_tfs = mqa_fl / (sum(attn_ms) * 1e-3) / 1e12
-    res = {
-        "metric": METRIC, "value": round(cfg.n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": max(1, a.warmup), "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+    res = _base(steps, max(1, warmup))
+    res.update({
+        "value": round(cfg.n / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
         "config": {"workload": cfg.name, "tokens": cfg.n, "query_chunk": T, "compressed_entries": N, "m": m,
                    "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I, "heads": H, "head_dim": D,
                    "window": W, "kv_dtype": cfg.kv_dtype},
         "prefill_tflops": round(total_fl / (ms * 1e-3) / 1e12, 2),
         "algorithmic_tflop": round(total_fl / 1e12, 3),
-        "roofline": {"bound": "mfma", "kernel": "attn_prs_kernel<2, %s> (sparse prefill)" % ("true" if fp8 else "false"),
-                     "achieved": round(mqa_tfs, 1),
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mqa_tfs / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops_all_launches": mqa_fl,
-                     "avg_launch_ms": round(float(np.mean(attn_ms)), 4)},
-        "roofline_indexer": {"bound": "mfma", "kernel": "idx_prefill_kernel", "achieved": round(idx_tfs, 1),
-                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
-                             "algorithmic_flops_all_launches": idx_fl, "avg_launch_ms": round(float(np.mean(idx_ms)), 4)},
+        # per launch: a 4096-query chunk (all chunks' flops over all chunks' time)
+        "roofline": _roofline("mfma", "attn_prs_kernel<2, %s> (sparse prefill, per 4096-query chunk)"
+                              % ("true" if fp8 else "false"), mqa_fl / nch, float(np.mean(attn_ms)),
+                              BF16_PEAK_TFLOPS, "TFLOP/s"),
+        "roofline_indexer": _roofline("mfma", "idx_prefill_kernel (per 4096-query chunk)", idx_fl / nch,
+                                      float(np.mean(idx_ms)), BF16_PEAK_TFLOPS, "TFLOP/s"),
         "phases_ms": {"compress": round(comp_ms, 4), "indexer_total": round(sum(idx_ms), 4),
                       "topk_total": round(sum(topk_ms), 4), "attention_total": round(sum(attn_ms), 4)},
-    }
-    if not a.no_cpu:
-        res["cpu_baseline"] = cpu_prefill_baseline(cfg, tok, a.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    })
+    if cpu_s is not None:
+        res["cpu_baseline"] = cpu_prefill_baseline(cfg, tok, cpu_s)
+    return res
 
 
 def hca_prefill_rows(cfg, pos):
@@ -403,7 +508,7 @@ def hca_prefill_rows(cfg, pos):
     return np.minimum(cfg.N, (pos + 1) // cfg.m) + np.minimum(cfg.W, pos + 1)
 
 
-def bench_hca_prefill(a, torch, L, gen, dev):
+def bench_hca_prefill(a, torch, L, gen, dev, steps, warmup, cpu_s):
     """HCA prefill of one 65536-token sequence: single-branch compression of
     all tokens at m' = 128, then 16 chunks of 4096 queries through hca_prefill
     (every visible entry plus the window and the sink)."""
@@ -435,10 +540,10 @@ def bench_hca_prefill(a, torch, L, gen, dev):
             L.hca_prefill(ch["q"], comp[0], kv_tok, ch["q_pos"], sink, out, m=m, W=W, stream=s)
             if ev is not None: ev[2 + c].record(stream)
 
-    for _ in range(max(1, a.warmup)):
+    for _ in range(max(1, warmup)):
         run()
     torch.cuda.synchronize()
-    steps = max(1, min(a.steps, 5))
+    steps = max(1, min(steps, 5))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(steps):
@@ -453,24 +558,20 @@ def bench_hca_prefill(a, torch, L, gen, dev):
     attn_ms = [ev[1 + c].elapsed_time(ev[2 + c]) for c in range(nch)]
     rows = [float(hca_prefill_rows(cfg, ch["pos_np"]).sum()) for ch in chunks]
     mqa_fl = sum(rows) * H * D * 4
-    mqa_tfs = mqa_fl / (sum(attn_ms) * 1e-3) / 1e12
-    res = {
-        "metric": METRIC, "value": round(cfg.n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": max(1, a.warmup), "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+    res = _base(steps, max(1, warmup))
+    res.update({
+        "value": round(cfg.n / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
         "config": {"workload": cfg.name, "tokens": cfg.n, "query_chunk": T, "compressed_entries": N, "m": m,
                    "heads": H, "head_dim": D, "window": W},
         "prefill_tflops": round(mqa_fl / (ms * 1e-3) / 1e12, 2),
         "algorithmic_tflop": round(mqa_fl / 1e12, 3),
-        "roofline": {"bound": "mfma", "kernel": "attn_prs_kernel<3> (HCA prefill)", "achieved": round(mqa_tfs, 1),
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(mqa_tfs / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops_all_launches": mqa_fl,
-                     "avg_launch_ms": round(float(np.mean(attn_ms)), 4)},
+        "roofline": _roofline("mfma", "attn_prs_kernel<3> (HCA prefill, per 4096-query chunk)", mqa_fl / nch,
+                              float(np.mean(attn_ms)), BF16_PEAK_TFLOPS, "TFLOP/s"),
         "phases_ms": {"compress": round(comp_ms, 4), "attention_total": round(sum(attn_ms), 4)},
-    }
-    if not a.no_cpu:
-        res["cpu_baseline"] = cpu_hca_prefill_baseline(cfg, tok, a.cpu_seconds)
-    print(json.dumps(res), flush=True)
+    })
+    if cpu_s is not None:
+        res["cpu_baseline"] = cpu_hca_prefill_baseline(cfg, tok, cpu_s)
+    return res
 
 
 def cpu_hca_prefill_baseline(cfg, tok, budget_s: float):

@@ -341,6 +341,23 @@ int csa_decode_step_noalloc(const void* Ca, const void* Cb, const void* Za, cons
                             const float* sink, float scale, int H, int D, int W, int kv_dt, int out_dt,
                             int32_t* topk_idx, float* topk_score, void* out, float* lse, void* stream);
 
+/*
+ * csa_trace_phases — instrumentation of the decode calls, for timing their
+ * phases with the caller's HIP events (no synchronisation, nothing
+ * allocated). While set on the calling thread, csa_decode_step,
+ * csa_decode_step_noalloc, hca_dense_mqa, indexer_score_topk and
+ * csa_compress_indexer_score_topk record events[i] with hipEventRecord on
+ * the call's stream at these points:
+ *   [0] before the first launch   [1] after the indexer scan launch
+ *   [2] after the top-k (or the fused top-k + attention + merge launch)
+ *   [3] after the attention kernel, before its split merge   [4] at the end.
+ * A phase a call does not have is recorded where it would start, so every
+ * event of a traced call is recorded, in order. events: n (0..5) hipEvent_t
+ * handles owned by the caller; n = 0 turns tracing off.
+ * Errors: CSA_INVALID_ARG for n outside 0..5 or a NULL array with n > 0.
+ */
+int csa_trace_phases(void* const* events, int n);
+
 /* sparse_mqa_prefill — Tq queries of one sequence.
  *   q      : [Tq, H, D]          kv_comp : [N, D]
  *   topk_idx : [Tq, top_k] int32 (-1 = empty)

@@ -54,6 +54,7 @@ _SIGS = {
                         + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32] + [_vp] * 5
                         + [_f32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
     "csa_decode_step_workspace_bytes": ([_i64, _i64, _i64, _i32, _i32, _i32, _i32], _sz),
+    "csa_trace_phases": ([ctypes.POINTER(ctypes.c_void_p), _i32], _i32),
     "csa_decode_step_noalloc": ([_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i64, _i32, _i32] + [_vp] * 6
                                 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32] + [_vp] * 5
                                 + [_f32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 5, _i32),
@@ -242,6 +243,20 @@ def csa_decode_step(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, n_c
         N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len), _ptr(sink),
         scale, H, D, W, _kv_dt(q, kv_comp), _dt(out), _ptr(topk_idx), _ptr(topk_score), _ptr(out), _ptr(lse),
         _ptr(ws), nb, _stream(stream)))
+
+
+def trace_phases(events) -> None:
+    """Record these torch.cuda.Event objects (up to 5, each recorded once
+    before, so that it exists) at the phase boundaries of the decode calls on
+    this thread; None or [] turns it off. Instrumentation only."""
+    if not events:
+        _check(lib.csa_trace_phases(None, 0))
+        return
+    hs = [e.cuda_event for e in events]
+    if any(h == 0 for h in hs):
+        raise ValueError("record every event once before tracing with it")
+    arr = (ctypes.c_void_p * len(hs))(*hs)
+    _check(lib.csa_trace_phases(arr, len(hs)))
 
 
 STEP_SCRATCH_BYTES = 64 << 20  # CSA_STEP_SCRATCH_BYTES: the scratch csa_decode_step_noalloc holds per device

@@ -111,9 +111,27 @@ int check_topk(const float* scores, const int32_t* q_pos, const int32_t* n_comp,
 
 }  // namespace
 
+namespace csa {
+namespace {
+thread_local hipEvent_t t_phase_ev[PHASES] = {};
+thread_local int t_phase_n = 0;
+}  // namespace
+void phase_mark(int i, hipStream_t st) {
+  if (i < t_phase_n && t_phase_ev[i]) (void)hipEventRecord(t_phase_ev[i], st);
+}
+}  // namespace csa
+
 extern "C" {
 
 int csa_hca_version(void) { return CSA_HCA_VERSION; }
+
+int csa_trace_phases(void* const* events, int n) {
+  REQ(n >= 0 && n <= csa::PHASES, CSA_INVALID_ARG, "csa_trace_phases: n must be in [0, 5]");
+  REQ(n == 0 || events, CSA_INVALID_ARG, "csa_trace_phases: events must not be NULL");
+  for (int i = 0; i < csa::PHASES; ++i) csa::t_phase_ev[i] = i < n ? (hipEvent_t)events[i] : nullptr;
+  csa::t_phase_n = n;
+  return CSA_OK;
+}
 
 const char* csa_last_error(void) { return g_err.c_str(); }
 
@@ -235,11 +253,15 @@ static int score_then_topk(const csa::CompressLaunch* c, csa::IndexerLaunch a, i
     a.zero = reinterpret_cast<uint32_t*>(tw + csa::topk_counter_offset(rows, a.N_max));
     a.zero_n = rows;
   }
+  csa::phase_mark(csa::PHASE_START, st);
   int rc = hip_status(c ? csa::run_compress_indexer(*c, a, st) : csa::run_indexer(a, st), what);
+  csa::phase_mark(csa::PHASE_SCAN, st);
   if (rc) return rc;
   csa::TopkLaunch t{a.scores, a.q_pos, a.n_comp, a.B, a.Tq, a.N_max, a.m, top_k, topk_idx, topk_score,
                     tw, ws_bytes - sbytes, mode};
-  return hip_status(csa::run_topk(t, st), what);
+  rc = hip_status(csa::run_topk(t, st), what);
+  for (int i = csa::PHASE_TOPK; i < csa::PHASES; ++i) csa::phase_mark(i, st);
+  return rc;
 }
 
 int indexer_score_topk(const void* q_idx, const float* w, const void* k_idx, const void* k_scale,
@@ -364,7 +386,9 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
     a.zero = reinterpret_cast<uint32_t*>(tw + csa::topk_counter_offset(nq, N_max));
     a.zero_n = nq;
   }
+  csa::phase_mark(csa::PHASE_START, st);
   rc = hip_status(csa::run_compress_indexer(c, a, st), "csa_decode_step");
+  csa::phase_mark(csa::PHASE_SCAN, st);
   if (rc) return rc;
   int topk_mode = mode;
   if (fused) {
@@ -398,7 +422,10 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
     t.ws = xw;
     bool launched = false;
     (void)csa::run_decode_tail(t, st, &launched);
-    if (launched) return CSA_OK;
+    if (launched) {
+      for (int i = csa::PHASE_TOPK; i < csa::PHASES; ++i) csa::phase_mark(i, st);
+      return CSA_OK;
+    }
     // the cooperative launch was refused: the separate kernels, the top-k
     // rebuilding its histogram and counters (the scan zeroed the tail's)
     (void)hipGetLastError();
@@ -408,6 +435,7 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
   csa::TopkLaunch tk{scores, q_pos, n_comp, B, Tq, N_max, m, top_k, topk_idx, topk_score, tw,
                      csa::topk_ws_bytes(B, Tq, N_max, top_k, true), topk_mode};
   rc = hip_status(csa::run_topk(tk, st), "csa_decode_step");
+  csa::phase_mark(csa::PHASE_TOPK, st);
   if (rc) return rc;
   csa::AttnLaunch at{};
   at.src = 0;
@@ -436,7 +464,9 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
   at.part_ml = reinterpret_cast<float*>(xw + round256((size_t)nq * ns * H * D * 4));
   at.out = out;
   at.lse = lse;
-  return hip_status(csa::run_attn(at, st), "csa_decode_step");
+  rc = hip_status(csa::run_attn(at, st), "csa_decode_step");
+  csa::phase_mark(csa::PHASE_END, st);
+  return rc;
 }
 
 int csa_decode_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba, const float* Bb,
@@ -752,7 +782,10 @@ int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, con
   a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + round256((size_t)B * ns * H * D * 4));
   a.out = out;
   a.lse = lse;
-  return hip_status(csa::run_attn(a, (hipStream_t)stream), "hca_dense_mqa");
+  for (int i = csa::PHASE_START; i < csa::PHASE_ATTN; ++i) csa::phase_mark(i, (hipStream_t)stream);
+  rc = hip_status(csa::run_attn(a, (hipStream_t)stream), "hca_dense_mqa");
+  csa::phase_mark(csa::PHASE_END, (hipStream_t)stream);
+  return rc;
 }
 
 }  // extern "C"

@@ -1030,6 +1030,7 @@ static hipError_t launch_bf16(const AttnLaunch& a, hipStream_t st) {
                      row_src(a), a.win_len, a.n_comp, a.q_pos, a.m_rate, a.sink, a.scale * LOG2E_F, a.H, a.slots,
                      a.split_rows, a.nsplit > 1 ? a.part_o : nullptr, a.part_ml, a.out, a.lse, a.out_dt);
   hipError_t e = hipGetLastError();
+  phase_mark(PHASE_ATTN, st);
   if (e != hipSuccess || a.nsplit == 1) return e;
   return launch_combine(a, st);
 }
@@ -1051,6 +1052,7 @@ static hipError_t launch_f32(const AttnLaunch& a, hipStream_t st) {
                      a.scale * LOG2E_F, a.H, a.slots, a.split_rows, a.nsplit > 1 ? a.part_o : nullptr, a.part_ml,
                      a.out, a.lse, a.out_dt);
   hipError_t e = hipGetLastError();
+  phase_mark(PHASE_ATTN, st);
   if (e != hipSuccess || a.nsplit == 1) return e;
   return launch_combine(a, st);
 }

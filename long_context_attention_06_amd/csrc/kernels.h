@@ -136,4 +136,9 @@ struct NormRopeLaunch {
 };
 hipError_t run_norm_rope(const NormRopeLaunch& a, hipStream_t st);
 
+// Phase marks of the decode calls (csa_trace_phases): records the caller's
+// event i, if one is set on this thread, on stream st.
+enum { PHASE_START = 0, PHASE_SCAN = 1, PHASE_TOPK = 2, PHASE_ATTN = 3, PHASE_END = 4, PHASES = 5 };
+void phase_mark(int i, hipStream_t st);
+
 }  // namespace csa

@@ -247,47 +247,49 @@ def bench_decode(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, copy_gbs, wna
               "win_len": td(np.full((B,), min(W + Tq - 1, cfg.n), np.int32))}
     if cfg.qk_rope:
         shared["q_gamma"] = td(x["q_gamma"])
-        shared["pos"] = td(np.full((B,), cfg.n - 1, np.int32))
     att_scale = 1.0 / math.sqrt(D) if cfg.qk_rope else 1.0
     reps = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(a.replicas - 1)]
     out = torch.empty(((B, Tq, H, D) if Tq > 1 else (B, H, D)), dtype=torch.bfloat16, device=dev)
-    qn = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
     if cfg.kind == "csa_decode":
         k = cfg.top_k
         idx = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
         # scores, digit histograms, top-k and attention scratch; zero-filled
         # once, as the step leaves it (its histograms cleared after use)
-        ws_t = torch.zeros(L.csa_decode_step_workspace_bytes(B, Tq, N, k, H, D, W), dtype=torch.uint8, device=dev)
+        wsb = (L.csa_decode_step_qk_workspace_bytes if cfg.qk_rope else L.csa_decode_step_workspace_bytes)
+        ws_t = torch.zeros(wsb(B, Tq, N, k, H, D, W), dtype=torch.uint8, device=dev)
         ws_a = None
     else:
-        ws_a = torch.empty(max(1, L.hca_dense_mqa_workspace_bytes(B, H, D, N, W)), dtype=torch.uint8, device=dev)
+        ws_a = torch.zeros(max(1, L.hca_decode_step_workspace_bytes(B, H, D, N, W)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     s = stream.cuda_stream
 
     def step(r, pre=None):
         if pre is not None:
             pre.record(stream)
-        q_att = r["q"]
-        if cfg.qk_rope:  # prologue: RMSNorm + RoPE of the raw queries at their position
-            L.qk_norm_rope(r["q"], qn, shared["pos"], shared["q_gamma"], norm=True, rope=True, stream=s)
-            q_att = qn
-        if cfg.kind == "csa_decode":
+        if cfg.kind == "csa_decode" and cfg.qk_rope:
+            # raw queries: the step applies RMSNorm + RoPE before the attention
+            # and the inverse rotation to its output
+            L.csa_decode_step_qk(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"], r["q_idx"], r["w"],
+                                 r["k_idx"], r.get("k_scale"), shared["q_pos"], shared["n_comp"],
+                                 r["q"].view(B, 1, H, D), r["kv_comp"], r["kv_win"], shared["win_len"],
+                                 shared["sink"], idx, out.view(B, 1, H, D), q_gamma=shared["q_gamma"], m_c=m, m=m,
+                                 tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, scale=att_scale, ws=ws_t,
+                                 stream=s)
+        elif cfg.kind == "csa_decode":
             # the whole step in one call: the completed block's entry with the
             # indexer scan, then top-k, attention and split merge
             L.csa_decode_step(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"], r["q_idx"], r["w"],
                               r["k_idx"], r.get("k_scale"), shared["q_pos"], shared["n_comp"],
-                              q_att if Tq > 1 else q_att.view(B, 1, H, D), r["kv_comp"], r["kv_win"],
+                              r["q"] if Tq > 1 else r["q"].view(B, 1, H, D), r["kv_comp"], r["kv_win"],
                               shared["win_len"], shared["sink"], idx, out if Tq > 1 else out.view(B, 1, H, D),
                               m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, scale=att_scale,
                               ws=ws_t, stream=s)
-            if cfg.qk_rope:  # epilogue: the output's rotated dims turned back
-                L.qk_norm_rope(out, out, shared["pos"], inverse=True, stream=s)
         else:
-            # HCA: the token completes block N-1 (m' divides n): one branch, no overlap
-            L.csa_compress(r["Ca"], None, r["Za"], None, shared["Ba"], None, r["kv_comp"], m=m,
-                           tok_begin=cfg.n - m, blk_begin=N - 1, blk_end=N, overlap=False, stream=s)
-            L.hca_dense_mqa(r["q"], r["kv_comp"], shared["n_comp"], shared["q_pos"].view(B), r["kv_win"],
-                            shared["win_len"], shared["sink"], out, m=m, ws=ws_a, stream=s)
+            # HCA: the token completes block N-1 (m' divides n): its single-
+            # branch entry, the dense attention and the split merge in one call
+            L.hca_decode_step(r["Ca"], r["Za"], shared["Ba"], r["q"], r["kv_comp"], shared["n_comp"],
+                              shared["q_pos"].view(B), r["kv_win"], shared["win_len"], shared["sink"], out, m_c=m, m=m,
+                              tok_begin=cfg.n - m, blk_begin=N - 1, blk_end=N, ws=ws_a, stream=s)
 
     for i in range(warmup):
         step(reps[i % len(reps)])
@@ -375,25 +377,28 @@ def bench_decode(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, copy_gbs, wna
         res["step_algorithmic_bytes"] = step_bytes
         res["indexer_kv_hbm_gbs"] = res["roofline"]["achieved"]
     else:
-        # hca_dense_mqa: the split attention kernel and the merge of its
-        # splits (rows once and q in, the output out), K calls back to back
-        abytes = B * ((N + W) * rowb + H * D * 2 * 2)
+        # the step's two launches: the appended entry (m tokens of Ca and Za
+        # in, the entry out), every row once, q in, the output out
+        abytes = B * ((N + W) * rowb + H * D * 2 * 2 + 2 * m * D * 2 + rowb)
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
                          "m": m, "heads": H, "head_dim": D, "window": W, "kv_dtype": cfg.kv_dtype}
-        res["phases_ms"] = {"append": round(float(ph_mean[0]), 4), "attention": round(float(ph_mean[3]), 4),
+        res["phases_ms"] = {"before_call": round(float(ph_mean[0]), 4),
+                            "append_and_attention": round(float(ph_mean[1] + ph_mean[2] + ph_mean[3]), 4),
                             "merge": round(float(ph_mean[4]), 4)}
 
         def hca(i):
             r = reps[i % len(reps)]
-            L.hca_dense_mqa(r["q"], r["kv_comp"], shared["n_comp"], shared["q_pos"].view(B), r["kv_win"],
-                            shared["win_len"], shared["sink"], out, m=m, ws=ws_a)
+            L.hca_decode_step(r["Ca"], r["Za"], shared["Ba"], r["q"], r["kv_comp"], shared["n_comp"],
+                              shared["q_pos"].view(B), r["kv_win"], shared["win_len"], shared["sink"], out, m_c=m, m=m,
+                              tok_begin=cfg.n - m, blk_begin=N - 1, blk_end=N, ws=ws_a)
 
         attn_ms = _graph_loop_ms(torch, hca, steps)
         fp8 = cfg.kv_dtype == "fp8"
-        res["roofline"] = _roofline("hbm", "hca_dense_mqa: attn_bf16_kernel<1, %s> (HCA decode splits) + "
+        res["roofline"] = _roofline("hbm", "hca_decode_step: attn_bf16_kernel<1, %s> (append + HCA decode splits) + "
                                     "attn_combine_kernel" % ("true" if fp8 else "false"),
                                     abytes, attn_ms, HBM_PEAK_GBS, "GB/s",
-                                    _traffic(f"attn_hca_{wname}_traffic.txt", ["attn.hip", "attn_core.h", "common.h"]),
+                                    _traffic(f"hca_step_{wname}_traffic.txt",
+                                             ["attn.hip", "attn_core.h", "compress_entry.h", "common.h"]),
                                     copy_gbs)
         res["step_hbm_gbs"] = round(abytes / (ms_step * 1e-3) / 1e9, 1)
     res["wall_s_timed"] = round(wall, 3)

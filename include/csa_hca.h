@@ -314,6 +314,35 @@ int csa_decode_step(const void* Ca, const void* Cb, const void* Za, const void* 
 size_t csa_decode_step_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k, int H, int D, int W);
 
 /*
+ * csa_decode_step_qk — csa_decode_step with the attention's prologue and
+ * epilogue ([CSDN] 其他辅助设计: RMSNorm of the queries before the core
+ * attention, rotary encoding of the last rope_dims dims only; [LIDUOS] 1M
+ * Context 的结构与取舍: the output takes the inverse rotation, since rows are
+ * both key and value). q holds the raw queries; the step attends with
+ *   q' = rotate(RMSNorm(q) * q_gamma, q_pos)  (as qk_norm_rope with
+ *        CSA_RMSNORM | CSA_ROPE and pos = q_pos, each part per qk_flags),
+ * and writes out = rotate^-1(attention(q'), q_pos) (CSA_ROPE only).
+ *   q_gamma : [D] fp32 or NULL (ones); eps, rope_dims, rope_theta as in
+ *             qk_norm_rope; qk_flags a subset of CSA_RMSNORM | CSA_ROPE.
+ *   ws      : csa_decode_step_qk_workspace_bytes(...) bytes.
+ * Where the step runs as one launch after the scan (see csa_decode_step) the
+ * prologue runs on the query registers of that launch and the inverse
+ * rotation on its merged output before the one rounding to out_dt;
+ * otherwise qk_norm_rope's kernels run around the separate attention. q' is
+ * rounded to bf16 once in either form.
+ */
+int csa_decode_step_qk(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                       const float* Bb, int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin,
+                       int64_t blk_end, int flags, int in_dt, const void* q_idx, const float* w, const void* k_idx,
+                       const void* k_scale, const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq,
+                       int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt, int k_dt, const void* q,
+                       void* kv_comp, const void* kv_win, const int32_t* win_len, const float* sink, float scale,
+                       int H, int D, int W, int kv_dt, int out_dt, int32_t* topk_idx, float* topk_score, void* out,
+                       float* lse, const float* q_gamma, float eps, int rope_dims, float rope_theta, int qk_flags,
+                       void* ws, size_t ws_bytes, void* stream);
+size_t csa_decode_step_qk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k, int H, int D, int W);
+
+/*
  * csa_decode_step_noalloc — csa_decode_step for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid hipMalloc). Arguments and results are those of
@@ -384,6 +413,31 @@ int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, con
                   int kv_dt, int out_dt, void* out, float* lse,
                   void* ws, size_t ws_bytes, void* stream);
 size_t hca_dense_mqa_workspace_bytes(int64_t B, int H, int D, int64_t N_max, int W);
+
+/*
+ * hca_decode_step — one HCA decode step ([CSDN] HCA: every m' tokens become
+ * one entry, and a query attends densely to every entry it can see, plus the
+ * [LIDUOS] window and sink): csa_compress of the blocks the step's token
+ * completes, single branch (Cb, Zb, Bb NULL, no flags), into kv_comp rows
+ * [blk_begin, blk_end), then hca_dense_mqa over the updated kv_comp.
+ *   compression: as csa_compress with B, out = kv_comp, out_cap = N_max,
+ *                out_dt = kv_dt, d = D (blk_begin == blk_end: none).
+ *   attention  : as hca_dense_mqa (q [B, H, D], n_comp, q_pos [B], m).
+ *   ws         : hca_decode_step_workspace_bytes(...) bytes (the split
+ *                partials), 256-byte aligned; any contents on entry.
+ * With D = 512, bf16 or KV_FP8 rows and one appended block of bf16 inputs,
+ * the append rides in the attention's launch: the workgroup whose split
+ * holds the new entry computes it first, stores it, and then gathers its
+ * rows; the splits then merge in a second launch. Otherwise csa_compress's
+ * kernel runs first. Results match the separate calls up to the summation
+ * order of the new entry (fp32, then rounded to kv_dt).
+ */
+int hca_decode_step(const void* Ca, const void* Za, const float* Ba, int64_t n_rows, int64_t tok_begin, int d,
+                    int m_c, int64_t blk_begin, int64_t blk_end, int in_dt, const void* q, void* kv_comp,
+                    const int32_t* n_comp, const int32_t* q_pos, int m, const void* kv_win, const int32_t* win_len,
+                    const float* sink, float scale, int64_t B, int H, int D, int64_t N_max, int W, int kv_dt,
+                    int out_dt, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+size_t hca_decode_step_workspace_bytes(int64_t B, int H, int D, int64_t N_max, int W);
 
 /* hca_prefill — HCA for Tq queries of one sequence ([CSDN] HCA: dense
  * attention over every compressed entry a query can see, plus the

@@ -55,6 +55,11 @@ _SIGS = {
                         + [_f32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 5 + [_sz, _vp], _i32),
     "csa_decode_step_workspace_bytes": ([_i64, _i64, _i64, _i32, _i32, _i32, _i32], _sz),
     "csa_trace_phases": ([ctypes.POINTER(ctypes.c_void_p), _i32], _i32),
+    "csa_decode_step_qk": ([_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i64, _i32, _i32] + [_vp] * 6
+                           + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32] + [_vp] * 5
+                           + [_f32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 5 + [_f32, _i32, _f32, _i32]
+                           + [_vp, _sz, _vp], _i32),
+    "csa_decode_step_qk_workspace_bytes": ([_i64, _i64, _i64, _i32, _i32, _i32, _i32], _sz),
     "csa_decode_step_noalloc": ([_vp] * 6 + [_i64, _i64, _i32, _i32, _i64, _i64, _i32, _i32] + [_vp] * 6
                                 + [_i64, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _i32] + [_vp] * 5
                                 + [_f32, _i32, _i32, _i32, _i32, _i32] + [_vp] * 5, _i32),
@@ -74,6 +79,9 @@ _SIGS = {
     "hca_dense_mqa": ([_vp] * 4 + [_i32, _vp, _vp, _vp, _f32, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                                    _vp, _sz, _vp], _i32),
     "hca_dense_mqa_workspace_bytes": ([_i64, _i32, _i32, _i64, _i32], _sz),
+    "hca_decode_step": ([_vp] * 3 + [_i64, _i64, _i32, _i32, _i64, _i64, _i32] + [_vp] * 4 + [_i32] + [_vp] * 3
+                        + [_f32, _i64, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "hca_decode_step_workspace_bytes": ([_i64, _i32, _i32, _i64, _i32], _sz),
     "hca_prefill": ([_vp] * 5 + [_f32, _i64, _i32, _i32, _i64, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
                                  _vp], _i32),
     "hca_prefill_workspace_bytes": ([_i64, _i32, _i32, _i64, _i32], _sz),
@@ -245,6 +253,36 @@ def csa_decode_step(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, n_c
         _ptr(ws), nb, _stream(stream)))
 
 
+def csa_decode_step_qk_workspace_bytes(B: int, Tq: int, N_max: int, top_k: int, H: int, D: int, W: int) -> int:
+    return lib.csa_decode_step_qk_workspace_bytes(B, Tq, N_max, top_k, H, D, W)
+
+
+def csa_decode_step_qk(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, n_comp, q, kv_comp, kv_win, win_len,
+                       sink, topk_idx, out, lse=None, topk_score=None, *, m_c: int, m: int, q_gamma=None,
+                       eps: float = 1e-6, rope_dims: int = 64, rope_theta: float = 10000.0, norm: bool = True,
+                       rope: bool = True, tok_begin: int = 0, blk_begin: int = 0, blk_end: Optional[int] = None,
+                       overlap: bool = True, joint: bool = False, scale: float = 1.0, ws=None, stream=None) -> None:
+    """csa_decode_step on raw queries: RMSNorm (q_gamma) + RoPE of the last rope_dims dims at q_pos
+    before the attention, the inverse rotation of the output after it."""
+    _, n_rows, d = Ca.shape
+    if blk_end is None:
+        blk_end = (tok_begin + n_rows) // m_c
+    flags = (OVERLAP if overlap else 0) | (JOINT_SOFTMAX if joint else 0)
+    qk_flags = (RMSNORM if norm else 0) | (ROPE if rope else 0)
+    B, Tq, H_I, D_I = q_idx.shape
+    N_max = k_idx.shape[1]
+    top_k = topk_idx.shape[-1]
+    H, D = q.shape[-2], q.shape[-1]
+    W = kv_win.shape[1] - Tq + 1
+    ws, nb = _ws(csa_decode_step_qk_workspace_bytes(B, Tq, N_max, top_k, H, D, W), ws, q.device)
+    _check(lib.csa_decode_step_qk(
+        _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), n_rows, tok_begin, d, m_c, blk_begin, blk_end,
+        flags, _dt(Ca), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I,
+        N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len), _ptr(sink),
+        scale, H, D, W, _kv_dt(q, kv_comp), _dt(out), _ptr(topk_idx), _ptr(topk_score), _ptr(out), _ptr(lse),
+        _ptr(q_gamma), eps, rope_dims, rope_theta, qk_flags, _ptr(ws), nb, _stream(stream)))
+
+
 def trace_phases(events) -> None:
     """Record these torch.cuda.Event objects (up to 5, each recorded once
     before, so that it exists) at the phase boundaries of the decode calls on
@@ -366,6 +404,29 @@ def sparse_mqa_prefill(q, kv_comp, topk_idx, kv_tok, q_pos, sink, out, lse=None,
     _check(lib.sparse_mqa_prefill(_ptr(q), _ptr(kv_comp), _ptr(topk_idx), _ptr(kv_tok), _ptr(q_pos), _ptr(sink),
                                   scale, Tq, H, D, N, T_tok, top_k, W, _kv_dt(q, kv_comp), _dt(out), _ptr(out), _ptr(lse),
                                   _ptr(ws), nb, _stream(stream)))
+
+
+def hca_decode_step_workspace_bytes(B: int, H: int, D: int, N_max: int, W: int) -> int:
+    return lib.hca_decode_step_workspace_bytes(B, H, D, N_max, W)
+
+
+def hca_decode_step(Ca, Za, Ba, q, kv_comp, n_comp, q_pos, kv_win, win_len, sink, out, lse=None, *, m_c: int,
+                    m: int, tok_begin: int = 0, blk_begin: int = 0, blk_end: Optional[int] = None, scale: float = 1.0,
+                    ws=None, stream=None) -> None:
+    """One HCA decode step: single-branch compression of blocks [blk_begin, blk_end) of Ca/Za
+    [B, n_rows, D] into kv_comp, then dense MQA of q [B, H, D] over every visible entry,
+    the window and the sink (-> out [B, H, D])."""
+    B, n_rows, d = Ca.shape
+    if blk_end is None:
+        blk_end = (tok_begin + n_rows) // m_c
+    H, D = q.shape[-2], q.shape[-1]
+    N_max = kv_comp.shape[1]
+    W = kv_win.shape[1]
+    ws, nb = _ws(hca_decode_step_workspace_bytes(B, H, D, N_max, W), ws, q.device)
+    _check(lib.hca_decode_step(_ptr(Ca), _ptr(Za), _ptr(Ba), n_rows, tok_begin, d, m_c, blk_begin, blk_end, _dt(Ca),
+                               _ptr(q), _ptr(kv_comp), _ptr(n_comp), _ptr(q_pos), m, _ptr(kv_win), _ptr(win_len),
+                               _ptr(sink), scale, B, H, D, N_max, W, _kv_dt(q, kv_comp), _dt(out), _ptr(out),
+                               _ptr(lse), _ptr(ws), nb, _stream(stream)))
 
 
 def hca_prefill_workspace_bytes(Tq: int, H: int, D: int, N: int, W: int) -> int:

@@ -314,6 +314,15 @@ int csa_compress_indexer_score_topk(const void* Ca, const void* Cb, const void* 
 // the top-k's scratch (its digit histogram first) and the tail's scratch
 // (arrival counters and sub-bin counts first, zeroed by the scan; the lists;
 // the split partials).
+// The query prologue / output epilogue of csa_decode_step_qk.
+struct QkOpts {
+  int flags;  // CSA_RMSNORM | CSA_ROPE
+  const float* gamma;
+  float eps;
+  int R;
+  float theta;
+};
+
 static size_t step_split_rows(int slots, int* nsplit) {
   *nsplit = nsplit_for(slots, SPARSE_SPLIT_ROWS);
   return *nsplit > 1 ? SPARSE_SPLIT_ROWS : slots;
@@ -337,7 +346,7 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
                             int k_dt, const void* q, void* kv_comp, const void* kv_win, const int32_t* win_len,
                             const float* sink, float scale, int H, int D, int W, int kv_dt, int out_dt,
                             int32_t* topk_idx, float* topk_score, void* out, float* lse, void* ws, size_t ws_bytes,
-                            void* stream) {
+                            void* stream, const QkOpts* qk = nullptr) {
   REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
   REQ(Tq >= 1 && Tq <= 64, CSA_INVALID_ARG, "Tq must be in [1, 64]");
   const int64_t nq = B * Tq;
@@ -356,10 +365,13 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
   REQ(nq == 0 || kv_comp, CSA_INVALID_ARG, "kv_comp must not be NULL");
   REQ(nq == 0 || W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
   REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
-  const size_t need = csa_decode_step_workspace_bytes(B, Tq, N_max, top_k, H, D, W);
+  const size_t base_need = csa_decode_step_workspace_bytes(B, Tq, N_max, top_k, H, D, W);
+  const bool qk_on = qk && qk->flags;
+  const size_t need = base_need + (qk_on ? round256((size_t)nq * H * D * 2) : 0);
   REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
   REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
   REQ(((uintptr_t)ws & 255u) == 0, CSA_INVALID_ARG, "ws must be 256-byte aligned");
+  REQ(!qk_on || out_dt == CSA_BF16 || out_dt == CSA_F32, CSA_UNSUPPORTED, "out_dt must be F32 or BF16");
   hipStream_t st = (hipStream_t)stream;
   if (nq == 0) return hip_status(csa::run_compress(c, st), "csa_decode_step");
   REQ(nq <= 0x7fffffff, CSA_UNSUPPORTED, "B * Tq too large");
@@ -377,7 +389,9 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
   csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, scores};
   const int mode = csa::indexer_hint_mode(a);
   a.hint = mode != csa::TOPK_HINT_NONE ? reinterpret_cast<uint32_t*>(tw) : nullptr;
+  // the fused prologue forms each rotated pair's angle in one lane of a wave
   const bool fused = mode == csa::TOPK_HINT_ACCUMULATED && D == 512 && kv_dt != CSA_F32 &&
+                     (!qk_on || !(qk->flags & CSA_ROPE) || qk->R <= 128) &&
                      csa::decode_tail_applies(nq, N_max, top_k, slots, sr, ns, kv_dt);
   if (fused) {
     a.zero = reinterpret_cast<uint32_t*>(xw);
@@ -420,6 +434,13 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
     t.out = out;
     t.lse = lse;
     t.ws = xw;
+    if (qk_on) {
+      t.qk_flags = ((qk->flags & CSA_RMSNORM) ? 1 : 0) | ((qk->flags & CSA_ROPE) ? 2 : 0);
+      t.qk_gamma = qk->gamma;
+      t.qk_eps = qk->eps;
+      t.qk_R = qk->R;
+      t.qk_theta = qk->theta;
+    }
     bool launched = false;
     (void)csa::run_decode_tail(t, st, &launched);
     if (launched) {
@@ -437,9 +458,19 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
   rc = hip_status(csa::run_topk(tk, st), "csa_decode_step");
   csa::phase_mark(csa::PHASE_TOPK, st);
   if (rc) return rc;
+  const void* q_att = q;
+  if (qk_on) {
+    // the separate kernels: the standalone prologue into the workspace's last region
+    void* qn = reinterpret_cast<uint8_t*>(ws) + base_need;
+    csa::NormRopeLaunch nr{q, qn, qk->gamma, q_pos, nq, H, D, (qk->flags & CSA_ROPE) ? qk->R : 2, qk->eps,
+                           qk->theta, qk->flags & (CSA_RMSNORM | CSA_ROPE), CSA_BF16};
+    rc = hip_status(csa::run_norm_rope(nr, st), "csa_decode_step_qk");
+    if (rc) return rc;
+    q_att = qn;
+  }
   csa::AttnLaunch at{};
   at.src = 0;
-  at.q = q;
+  at.q = q_att;
   at.kv_comp = kv_comp;
   at.idx = topk_idx;
   at.kv_win = kv_win;
@@ -465,6 +496,10 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
   at.out = out;
   at.lse = lse;
   rc = hip_status(csa::run_attn(at, st), "csa_decode_step");
+  if (rc == CSA_OK && qk_on && (qk->flags & CSA_ROPE)) {
+    csa::NormRopeLaunch nr{out, out, nullptr, q_pos, nq, H, D, qk->R, 0.0f, qk->theta, CSA_ROPE_INVERSE, out_dt};
+    rc = hip_status(csa::run_norm_rope(nr, st), "csa_decode_step_qk");
+  }
   csa::phase_mark(csa::PHASE_END, st);
   return rc;
 }
@@ -481,6 +516,34 @@ int csa_decode_step(const void* Ca, const void* Cb, const void* Za, const void* 
                           w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, top_k, q_dt, k_dt, q, kv_comp,
                           kv_win, win_len, sink, scale, H, D, W, kv_dt, out_dt, topk_idx, topk_score, out, lse, ws,
                           ws_bytes, stream);
+}
+
+size_t csa_decode_step_qk_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k, int H, int D, int W) {
+  const size_t base = csa_decode_step_workspace_bytes(B, Tq, N_max, top_k, H, D, W);
+  return base == 0 ? 0 : base + round256((size_t)(B * Tq) * H * D * 2);
+}
+
+int csa_decode_step_qk(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
+                       const float* Bb, int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin,
+                       int64_t blk_end, int flags, int in_dt, const void* q_idx, const float* w, const void* k_idx,
+                       const void* k_scale, const int32_t* q_pos, const int32_t* n_comp, int64_t B, int64_t Tq,
+                       int H_I, int D_I, int64_t N_max, int m, int top_k, int q_dt, int k_dt, const void* q,
+                       void* kv_comp, const void* kv_win, const int32_t* win_len, const float* sink, float scale,
+                       int H, int D, int W, int kv_dt, int out_dt, int32_t* topk_idx, float* topk_score, void* out,
+                       float* lse, const float* q_gamma, float eps, int rope_dims, float rope_theta, int qk_flags,
+                       void* ws, size_t ws_bytes, void* stream) {
+  REQ((qk_flags & ~(CSA_RMSNORM | CSA_ROPE)) == 0, CSA_INVALID_ARG, "qk_flags: CSA_RMSNORM and/or CSA_ROPE");
+  const bool rope = qk_flags & CSA_ROPE;
+  REQ(!rope || (rope_dims >= 2 && rope_dims <= D && rope_dims % 2 == 0), CSA_INVALID_ARG,
+      "rope_dims must be even and in [2, D]");
+  REQ(!rope || (rope_theta > 0.0f && rope_theta <= 3.0e38f), CSA_INVALID_ARG, "rope_theta must be positive and finite");
+  REQ(!(qk_flags & CSA_RMSNORM) || (eps >= 0.0f && eps <= 3.0e38f), CSA_INVALID_ARG, "eps must be >= 0 and finite");
+  REQ(D % 8 == 0 && D <= 512, CSA_UNSUPPORTED, "D must be a multiple of 8, at most 512");
+  const QkOpts qk{qk_flags, q_gamma, eps, rope ? rope_dims : 2, rope_theta};
+  return decode_step_impl(Ca, Cb, Za, Zb, Ba, Bb, n_rows, tok_begin, d, m_c, blk_begin, blk_end, flags, in_dt, q_idx,
+                          w, k_idx, k_scale, q_pos, n_comp, B, Tq, H_I, D_I, N_max, m, top_k, q_dt, k_dt, q, kv_comp,
+                          kv_win, win_len, sink, scale, H, D, W, kv_dt, out_dt, topk_idx, topk_score, out, lse, ws,
+                          ws_bytes, stream, &qk);
 }
 
 }  // extern "C"
@@ -738,10 +801,12 @@ size_t hca_dense_mqa_workspace_bytes(int64_t B, int H, int D, int64_t N_max, int
   return attn_ws(B, H, D, nsplit_for(N_max + W, hca_split_rows(N_max + W)));
 }
 
-int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, const int32_t* q_pos, int m,
-                  const void* kv_win, const int32_t* win_len, const float* sink, float scale, int64_t B, int H, int D,
-                  int64_t N_max, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws, size_t ws_bytes,
-                  void* stream) {
+// Checks and the split plan of an HCA decode call (hca_dense_mqa and the
+// attention of hca_decode_step).
+static int hca_prep(const void* q, const void* kv_comp, const int32_t* n_comp, const int32_t* q_pos, int m,
+                    const void* kv_win, const int32_t* win_len, const float* sink, float scale, int64_t B, int H,
+                    int D, int64_t N_max, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws,
+                    size_t ws_bytes, csa::AttnLaunch* a) {
   int rc = check_attn_common(q, out, scale, H, D, kv_dt, out_dt, W, 0, B);
   if (rc) return rc;
   REQ(B >= 0 && N_max >= 0, CSA_INVALID_ARG, "B and N_max must be >= 0");
@@ -757,34 +822,93 @@ int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, con
   REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
   REQ(((uintptr_t)ws & 255u) == 0, CSA_INVALID_ARG, "ws must be 256-byte aligned");
   REQ(B <= 0x7fffffff, CSA_UNSUPPORTED, "B too large");
-  csa::AttnLaunch a{};
-  a.src = 1;
-  a.q = q;
-  a.kv_comp = kv_comp;
-  a.kv_win = kv_win;
-  a.win_len = win_len;
-  a.n_comp = n_comp;
-  a.q_pos = q_pos;
-  a.sink = sink;
-  a.scale = scale;
-  a.nq = B;
-  a.N_max = N_max;
-  a.H = H;
-  a.D = D;
-  a.W = W;
-  a.m_rate = m;
-  a.kv_dt = kv_dt;
-  a.out_dt = out_dt;
-  a.slots = (int)(N_max + W);
-  a.split_rows = ns > 1 ? hsr : a.slots;
-  a.nsplit = ns;
-  a.part_o = reinterpret_cast<float*>(ws);
-  a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + round256((size_t)B * ns * H * D * 4));
-  a.out = out;
-  a.lse = lse;
+  *a = csa::AttnLaunch{};
+  a->src = 1;
+  a->q = q;
+  a->kv_comp = kv_comp;
+  a->kv_win = kv_win;
+  a->win_len = win_len;
+  a->n_comp = n_comp;
+  a->q_pos = q_pos;
+  a->sink = sink;
+  a->scale = scale;
+  a->nq = B;
+  a->N_max = N_max;
+  a->H = H;
+  a->D = D;
+  a->W = W;
+  a->m_rate = m;
+  a->kv_dt = kv_dt;
+  a->out_dt = out_dt;
+  a->slots = (int)(N_max + W);
+  a->split_rows = ns > 1 ? hsr : a->slots;
+  a->nsplit = ns;
+  a->part_o = reinterpret_cast<float*>(ws);
+  a->part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + round256((size_t)B * ns * H * D * 4));
+  a->out = out;
+  a->lse = lse;
+  return CSA_OK;
+}
+
+int hca_dense_mqa(const void* q, const void* kv_comp, const int32_t* n_comp, const int32_t* q_pos, int m,
+                  const void* kv_win, const int32_t* win_len, const float* sink, float scale, int64_t B, int H, int D,
+                  int64_t N_max, int W, int kv_dt, int out_dt, void* out, float* lse, void* ws, size_t ws_bytes,
+                  void* stream) {
+  csa::AttnLaunch a;
+  int rc = hca_prep(q, kv_comp, n_comp, q_pos, m, kv_win, win_len, sink, scale, B, H, D, N_max, W, kv_dt, out_dt,
+                    out, lse, ws, ws_bytes, &a);
+  if (rc) return rc;
   for (int i = csa::PHASE_START; i < csa::PHASE_ATTN; ++i) csa::phase_mark(i, (hipStream_t)stream);
   rc = hip_status(csa::run_attn(a, (hipStream_t)stream), "hca_dense_mqa");
   csa::phase_mark(csa::PHASE_END, (hipStream_t)stream);
+  return rc;
+}
+
+size_t hca_decode_step_workspace_bytes(int64_t B, int H, int D, int64_t N_max, int W) {
+  return hca_dense_mqa_workspace_bytes(B, H, D, N_max, W);
+}
+
+int hca_decode_step(const void* Ca, const void* Za, const float* Ba, int64_t n_rows, int64_t tok_begin, int d,
+                    int m_c, int64_t blk_begin, int64_t blk_end, int in_dt, const void* q, void* kv_comp,
+                    const int32_t* n_comp, const int32_t* q_pos, int m, const void* kv_win, const int32_t* win_len,
+                    const float* sink, float scale, int64_t B, int H, int D, int64_t N_max, int W, int kv_dt,
+                    int out_dt, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  csa::CompressLaunch c{};
+  int rc = prep_compress(Ca, nullptr, Za, nullptr, Ba, nullptr, kv_comp, B, n_rows, tok_begin, d, m_c, blk_begin,
+                         blk_end, N_max, 0, in_dt, kv_dt, &c);
+  if (rc) return rc;
+  REQ(blk_begin == blk_end || d == D, CSA_INVALID_ARG, "the compressed rows must have the attention's D channels");
+  csa::AttnLaunch a;
+  rc = hca_prep(q, kv_comp, n_comp, q_pos, m, kv_win, win_len, sink, scale, B, H, D, N_max, W, kv_dt, out_dt, out,
+                lse, ws, ws_bytes, &a);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if (B == 0) return CSA_OK;
+  // the append rides in the attention's launch: the workgroup whose split
+  // holds the new entry computes it first (bf16 inputs, one block, D = 512)
+  const bool fold = blk_end - blk_begin == 1 && in_dt == CSA_BF16 && D == 512 && kv_dt != CSA_F32;
+  csa::phase_mark(csa::PHASE_START, st);
+  if (fold) {
+    a.app_Ca = Ca;
+    a.app_Za = Za;
+    a.app_Ba = Ba;
+    a.app_n_rows = n_rows;
+    a.app_tok_begin = tok_begin;
+    a.app_blk = blk_begin;
+    a.app_m = m_c;
+    a.app_out = kv_comp;
+    csa::phase_mark(csa::PHASE_SCAN, st);
+    csa::phase_mark(csa::PHASE_TOPK, st);
+    rc = hip_status(csa::run_attn(a, st), "hca_decode_step");
+    csa::phase_mark(csa::PHASE_END, st);
+    return rc;
+  }
+  rc = hip_status(csa::run_compress(c, st), "hca_decode_step");
+  if (rc) return rc;
+  csa::phase_mark(csa::PHASE_SCAN, st);
+  csa::phase_mark(csa::PHASE_TOPK, st);
+  rc = hip_status(csa::run_attn(a, st), "hca_decode_step");
+  csa::phase_mark(csa::PHASE_END, st);
   return rc;
 }
 

@@ -33,9 +33,20 @@
 #include <type_traits>
 
 #include "attn_core.h"
+#include "compress_entry.h"
 #include "kernels.h"
 
 namespace csa {
+
+// The HCA decode step's append (see AttnLaunch), as kernel arguments.
+struct HcaAppend {
+  const uint16_t* Ca;  // NULL: none
+  const uint16_t* Za;
+  const float* Ba;
+  int64_t n_rows, tok_begin, blk;
+  int m;
+  void* out;  // kv_comp
+};
 
 template <int SRC, bool KV8>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -43,7 +54,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
                  const int32_t* __restrict__ n_comp, const int32_t* __restrict__ q_pos, int m_rate,
                  const float* __restrict__ sink, float scale_log2, int H, int slots, int split_rows,
                  float* __restrict__ part_o, float* __restrict__ part_ml, void* __restrict__ out,
-                 float* __restrict__ lse, int out_dt) {
+                 float* __restrict__ lse, int out_dt, HcaAppend app) {
   using namespace bfk;
   constexpr int SROWB = DecRows<KV8>::SROWB, TB = DecRows<KV8>::TB;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TB];
@@ -73,6 +84,17 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
   }
 
   if (SRC != SRC_HCA_DEC) rr.n_rows = build_row_table<SRC, NT, TR>(src, rr, qi, tab, cnt);
+  if constexpr (SRC == SRC_HCA_DEC) {
+    if (app.Ca && sp == (int)(app.blk / split_rows)) {
+      // the step's new entry is in this split: computed here and stored, and
+      // the store complete, before any row of the split is gathered (the
+      // gathers read it back through this CU's path to the cache)
+      block_entry_wg<DT_BF16, KV8 ? DT_KV_FP8 : DT_BF16, NT>(app.Ca, app.Za, app.Ba,
+                                                            qi * app.n_rows + (app.m * app.blk - app.tok_begin), D,
+                                                            app.m, app.out, qi * src.N_max + app.blk,
+                                                            reinterpret_cast<float*>(ring));
+    }
+  }
 
   f32x4_t o[16];
   float m_ref, l_run;
@@ -902,8 +924,18 @@ attn_f32_kernel(const float* __restrict__ q, RowSrc src, const int32_t* __restri
   }
 }
 
+// Eight consecutive dims of a partial row.
+__device__ __forceinline__ void part8(const float* p, float (&v)[8]) {
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p), b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+
 // Merge split partials in fixed order s = 0..nsplit-1 and add the sink.
-// One wave per (query, head); lanes cover the head's dims in float4 chunks.
+// One wave per (query, head); lane l covers the head's dims 8 l .. 8 l + 7.
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                     const float* __restrict__ sink, int H, int D, int nsplit,
@@ -914,26 +946,28 @@ attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ 
   if (h >= H) return;
   const float s2 = sink ? sink[h] * LOG2E_F : -INFINITY;
   const int64_t row0 = qi * nsplit * (int64_t)H + h;  // partial (qi, s, h) at row0 + s*H
-  constexpr int MAXC = 2;  // float4 chunks per lane (D <= 512)
-  f32x4_t acc[MAXC];
+  const int d = l * 8;
+  const bool dok = d < D;  // D <= 512, a multiple of 8
+  float acc[8];
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   float M = s2, Z = 0.0f;
   constexpr int U1 = 16;
   if (nsplit <= U1) {
     // every partial of the head in one round of loads, then the same merge
     float mv[U1], lv[U1];
-    f32x4_t v[U1][MAXC];
+    float v[U1][8];
 #pragma unroll
     for (int u = 0; u < U1; ++u) {
       const int64_t pb = row0 + (int64_t)u * H;
       const bool in = u < nsplit;
       mv[u] = in ? part_ml[pb * 2] : -INFINITY;
       lv[u] = in ? part_ml[pb * 2 + 1] : 0.0f;
+      if (in && dok) {
+        part8(part_o + pb * D + d, v[u]);
+      } else {
 #pragma unroll
-      for (int c = 0; c < MAXC; ++c) {
-        const int d = (c * 64 + l) * 4;
-        v[u][c] = (in && d < D) ? *reinterpret_cast<const f32x4_t*>(part_o + pb * D + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
       }
     }
 #pragma unroll
@@ -945,9 +979,7 @@ attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ 
         const float a = exp2f(mv[u] - M);  // 0 for an empty or absent split (m = -inf)
         Z += lv[u] * a;
 #pragma unroll
-        for (int c = 0; c < MAXC; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[c][e] += v[u][c][e] * a;
+        for (int e = 0; e < 8; ++e) acc[e] += v[u][e] * a;
       }
     }
   } else {
@@ -955,44 +987,39 @@ attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ 
     if (M != -INFINITY) {
       Z = exp2f(s2 - M);
       for (int s0 = 0; s0 < nsplit; s0 += 4) {
-        f32x4_t v[4][MAXC];
+        float v[4][8];
         float a[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int s = s0 + u;
           a[u] = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
           if (s < nsplit) {
             const int64_t pb = row0 + (int64_t)s * H;
             a[u] = exp2f(part_ml[pb * 2] - M);  // 0 for an empty split (m = -inf)
             Z += part_ml[pb * 2 + 1] * a[u];
-#pragma unroll
-            for (int c = 0; c < MAXC; ++c) {
-              const int d = (c * 64 + l) * 4;
-              v[u][c] = d < D ? *reinterpret_cast<const f32x4_t*>(part_o + pb * D + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
+            if (dok) part8(part_o + pb * D + d, v[u]);
           }
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int c = 0; c < MAXC; ++c)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[c][e] += v[u][c][e] * a[u];
+          for (int e = 0; e < 8; ++e) acc[e] += v[u][e] * a[u];
       }
     }
   }
   const float inv = (M != -INFINITY) ? 1.0f / Z : 0.0f;
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int d = (c * 64 + l) * 4;
-    if (d >= D) continue;
+  if (dok) {
     const int64_t o = (qi * H + h) * (int64_t)D + d;
     if (out_dt == DT_BF16) {
-      u32x2_t w = {pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv), pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv)};
-      *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(out) + o) = w;
+      const u32x4_t w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                         pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + o) = w;
     } else {
-      f32x4_t w = {acc[c][0] * inv, acc[c][1] * inv, acc[c][2] * inv, acc[c][3] * inv};
-      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(out) + o) = w;
+      float* op = reinterpret_cast<float*>(out) + o;
+      *reinterpret_cast<f32x4_t*>(op) = f32x4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+      *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
     }
   }
   if (lse && l == 0) lse[qi * H + h] = (M != -INFINITY) ? (M + log2f(Z)) * LN2_F : -INFINITY;
@@ -1028,7 +1055,9 @@ static hipError_t launch_bf16(const AttnLaunch& a, hipStream_t st) {
   dim3 grid((unsigned)a.nq, a.nsplit);
   hipLaunchKernelGGL((attn_bf16_kernel<SRC, KV8>), grid, dim3(bfk::NT), 0, st, reinterpret_cast<const uint16_t*>(a.q),
                      row_src(a), a.win_len, a.n_comp, a.q_pos, a.m_rate, a.sink, a.scale * LOG2E_F, a.H, a.slots,
-                     a.split_rows, a.nsplit > 1 ? a.part_o : nullptr, a.part_ml, a.out, a.lse, a.out_dt);
+                     a.split_rows, a.nsplit > 1 ? a.part_o : nullptr, a.part_ml, a.out, a.lse, a.out_dt,
+                     HcaAppend{reinterpret_cast<const uint16_t*>(a.app_Ca), reinterpret_cast<const uint16_t*>(a.app_Za),
+                               a.app_Ba, a.app_n_rows, a.app_tok_begin, a.app_blk, a.app_m, a.app_out});
   hipError_t e = hipGetLastError();
   phase_mark(PHASE_ATTN, st);
   if (e != hipSuccess || a.nsplit == 1) return e;

@@ -251,4 +251,72 @@ __device__ __forceinline__ void compress_entry(const CompressArgs& a, int64_t gi
 }
 
 
+// One single-branch entry (no overlap term), computed by a whole workgroup of
+// NT threads: thread (slice sl, channel group g) runs the online softmax of
+// its 8 channels over tokens sl * 4 + 4 * SL * k .. +3 of the block (SL =
+// NT / (d / 8) slices), and the slices' (max, sum, weighted sum) merge in
+// slice order through `scratch` (3 * SL * d floats of LDS). Entry row orow of
+// out gets it. Used where a decode step's append rides in the attention's
+// launch.
+template <int IN_DT, int OUT_DT, int NT>
+__device__ void block_entry_wg(const void* Ca, const void* Za, const float* Ba, int64_t row0, int d, int m,
+                               void* out, int64_t orow, float* scratch) {
+  const int groups = d / 8;
+  const int SL = NT / groups;  // d = 512: 8 slices
+  const int tid = threadIdx.x;
+  const int g = tid % groups, sl = tid / groups;
+  const int c0 = g * 8;
+  SoftAcc A;
+  A.init();
+  if (sl < SL) {
+    for (int j0 = sl * 4; j0 < m; j0 += SL * 4) {
+      float z[4][8], c[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = min(j0 + u, m - 1);  // a repeated token is masked below
+        load8<IN_DT>(Za, (row0 + j) * d + c0, z[u]);
+        load8<IN_DT>(Ca, (row0 + j) * d + c0, c[u]);
+        const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(Ba + (int64_t)j * d + c0);
+        const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(Ba + (int64_t)j * d + c0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z[u][e] = j0 + u < m ? (z[u][e] + b0[e]) * LOG2E_F : -INFINITY;
+          z[u][4 + e] = j0 + u < m ? (z[u][4 + e] + b1[e]) * LOG2E_F : -INFINITY;
+        }
+      }
+      A.feed<4>(z, c);  // token j0 < m is in the group: its maximum is finite
+    }
+    float* pm = scratch;
+    float* ps = scratch + SL * d;
+    float* pa = scratch + 2 * SL * d;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pm[sl * d + c0 + e] = A.mx[e];
+      ps[sl * d + c0 + e] = A.sm[e];
+      pa[sl * d + c0 + e] = A.acc[e];
+    }
+  }
+  __syncthreads();
+  if (tid < groups) {
+    float res[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ch = c0 + e;
+      float mx = -INFINITY;
+      for (int q = 0; q < SL; ++q) mx = fmaxf(mx, scratch[q * d + ch]);
+      float sm = 0.f, acc = 0.f;
+      for (int q = 0; q < SL; ++q) {
+        const float v = scratch[q * d + ch];
+        const float a = v == -INFINITY ? 0.f : exp2f(v - mx);
+        sm += scratch[(SL + q) * d + ch] * a;
+        acc += scratch[(2 * SL + q) * d + ch] * a;
+      }
+      res[e] = acc / sm;
+    }
+    store8<OUT_DT>(out, orow, d, c0, res);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the entry is written before the barrier releases readers
+  __syncthreads();
+}
+
 }  // namespace csa

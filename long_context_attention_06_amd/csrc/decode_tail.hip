@@ -53,6 +53,7 @@ constexpr int CAP = (RING - CAND_B) / 8;  // candidates a workgroup holds
 constexpr int MAX_SPLITS = 16;
 constexpr int SPIN = 1 << 22;          // bound of a wait (never reached when all workgroups are resident)
 constexpr uint32_t FAILED = 1u << 16;  // added to a query's second counter when a workgroup gave up
+constexpr int SC1 = 16;                // buffer cache policy: device-coherent (past the per-XCD caches)
 }  // namespace dtl
 
 struct TailArgs {
@@ -63,7 +64,7 @@ struct TailArgs {
   const float* sink;
   float scale_log2;
   int H, slots, split_rows, nsplit;
-  float* part_o;
+  float* part_o;  // [nq, nsplit, H, 512]
   float* part_ml;
   void* out;
   float* lse;
@@ -82,7 +83,24 @@ struct TailArgs {
   int nseg, passes;
   int32_t* out_idx;        // [nq, top_k]
   float* out_score;        // nullable
+  // the query prologue and output epilogue (sparse source): RMSNorm of each
+  // head's query with qk_gamma, rotation of its last qk_R dims by the query's
+  // position, and the inverse rotation of the output; qk_flags 0: none
+  int qk_flags;            // 1: norm, 2: rotation
+  const float* qk_gamma;   // [D] or NULL (ones)
+  float qk_eps;
+  int qk_R;
+  double qk_log2_theta;
 };
+
+// cos and sin of the angle of rotated pair i at position p, formed in double
+// precision as the standalone prologue forms it
+__device__ __forceinline__ void rope_cs(double p, int i, int R, double log2_theta, float& c, float& s) {
+  double sn, cs;
+  sincos(p * exp2(-2.0 * (double)i / (double)R * log2_theta), &sn, &cs);
+  c = (float)cs;
+  s = (float)sn;
+}
 
 template <class T>
 __device__ __forceinline__ void st_coh(T* p, T v) {
@@ -209,6 +227,65 @@ csa_decode_tail_kernel(TailArgs a) {
   }
   arrive(&a.sync[qi * 2]);
 
+  // ---- the query prologue (while the other workgroups filter): RMSNorm over
+  // the head's 512 dims (a wave holds 256 of them: the pair w, w ^ 4 adds its
+  // halves through LDS), then the rotation of the last R dims (pairs of
+  // consecutive dims inside a lane's 8), in fp32, rounded back to bf16
+  if (a.qk_flags && nmine > 0) {
+    float v[8][8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) unpack_bf16x8(__builtin_bit_cast(u32x4_t, qb[s2]), v[s2]);
+    if (a.qk_flags & 1) {
+      float ss = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += v[s2][e] * v[s2][e];
+      ss += shfl_xor(ss, 16);
+      ss += shfl_xor(ss, 32);
+      float* half = reinterpret_cast<float*>(xchg);  // free until the tile loop
+      if (G == 0) half[w * 16 + l16] = ss;
+      __syncthreads();
+      const float tot = half[w * 16 + l16] + half[(w ^ 4) * 16 + l16];
+      const float r = 1.0f / sqrtf(tot / (float)D + a.qk_eps);
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = dh * 256 + s2 * 32 + G * 8 + e;
+          v[s2][e] *= r * (a.qk_gamma ? a.qk_gamma[d] : 1.0f);
+        }
+    }
+    if (a.qk_flags & 2) {
+      // lane i < R/2 forms pair i's angle once; the lanes that rotate it
+      // read it by a shuffle (all lanes shuffle; s0 is even, so a pair never
+      // straddles it)
+      const int s0 = D - a.qk_R;
+      float cl = 1.0f, sl = 0.0f;
+      if (l < a.qk_R / 2) rope_cs((double)a.q_pos[qi], l, a.qk_R, a.qk_log2_theta, cl, sl);
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        if (dh * 256 + s2 * 32 + 32 <= s0) continue;  // uniform: no rotated dim in this chunk
+        const int d0 = dh * 256 + s2 * 32 + G * 8;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bool rot = d0 + e >= s0;
+          const int src = rot ? (d0 + e - s0) >> 1 : 0;
+          const float c2 = __shfl(cl, src, 64), sn = __shfl(sl, src, 64);
+          if (rot) {
+            const float x0 = v[s2][e], x1 = v[s2][e + 1];
+            v[s2][e] = x0 * c2 - x1 * sn;
+            v[s2][e + 1] = x0 * sn + x1 * c2;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      qb[s2] = as_bf16x8(u32x4_t{pack_bf16x2(v[s2][0], v[s2][1]), pack_bf16x2(v[s2][2], v[s2][3]),
+                                 pack_bf16x2(v[s2][4], v[s2][5]), pack_bf16x2(v[s2][6], v[s2][7])});
+  }
+
   // ---- 2. selection (attention workgroups): the slots of this workgroup's splits
   if (nmine > 0) {
     const bool ok = wait_for(&a.sync[qi * 2], (uint32_t)P, &res[6]) >= (uint32_t)P;  // every list is in
@@ -323,8 +400,8 @@ csa_decode_tail_kernel(TailArgs a) {
     }
     __syncthreads();  // mysel is complete
 
-    // ---- 3. attention: row tables of every own split (the select's scratch
-    // is in the ring, which the tiles then take over), then the splits in turn
+    // ---- row tables of every own split (the select's scratch is in the
+    // ring, which the tiles then take over)
     for (int k = 0; k < nmine; ++k) {
       const int sp = c + k * P;
       const QRows rq = query_rows<SRC_SPARSE_DEC, DecRows<KV8>::SROWB>(a.src, a.win_len, nullptr, nullptr, 1, qi,
@@ -334,6 +411,10 @@ csa_decode_tail_kernel(TailArgs a) {
       if (tid == 0) nrow[k] = n;
     }
     __syncthreads();
+  }
+
+  // ---- 3. attention over the own splits in turn
+  if (nmine > 0) {
 #pragma unroll 1
     for (int k = 0; k < nmine; ++k) {
       const int sp = c + k * P;
@@ -365,6 +446,8 @@ csa_decode_tail_kernel(TailArgs a) {
           st_coh(&a.part_ml[(pbase + head) * 2 + 1], l_run);
         }
       } else {
+        float rope_c = 1.0f, rope_s = 0.0f;
+        if ((a.qk_flags & 2) && l < a.qk_R / 2) rope_cs((double)a.q_pos[qi], l, a.qk_R, a.qk_log2_theta, rope_c, rope_s);
         // one split: normalise here, as the separate kernel does
         float mrr[4], lrr[4];
 #pragma unroll
@@ -386,7 +469,16 @@ csa_decode_tail_kernel(TailArgs a) {
 #pragma unroll
           for (int nt = 0; nt < 16; ++nt) {
             const int64_t oo = (qi * H + h) * (int64_t)D + dbase + nt * 16;
-            const float v = o[nt][r] * fac;
+            float v = o[nt][r] * fac;
+            if ((a.qk_flags & 2) && dh * 256 + nt * 16 + 16 > D - a.qk_R) {
+              // the inverse rotation: the pair's other dim is in the lane next
+              // door; lane i < R/2 formed pair i's angle (rope_l)
+              const int d = dbase + nt * 16, s0 = D - a.qk_R;
+              const float other = shfl_xor(v, 1);
+              const int src = d >= s0 ? (d - s0) >> 1 : 0;
+              const float c2 = __shfl(rope_c, src, 64), sn = __shfl(rope_s, src, 64);
+              if (d >= s0) v = (l16 & 1) ? v * c2 - other * sn : v * c2 + other * sn;
+            }
             if (a.out_dt == DT_BF16)
               reinterpret_cast<uint16_t*>(a.out)[oo] = (uint16_t)f32_to_bf16(v);
             else
@@ -406,12 +498,12 @@ csa_decode_tail_kernel(TailArgs a) {
   }
 merge:
   if (nsplit == 1) return;
-  arrive(&a.sync[qi * 2 + 1]);
 
   // ---- 4. merge: one wave per head (its 512 dims, eight per lane), every
   // split's partial in one round of device-coherent loads, then the same
   // arithmetic in split order as the separate merge kernel
   {
+    arrive(&a.sync[qi * 2 + 1]);
     const uint32_t got = wait_for(&a.sync[qi * 2 + 1], (uint32_t)P, &res[7]);
     const bool ok = got >= (uint32_t)P && got < dtl::FAILED;
     constexpr int U1 = dtl::MAX_SPLITS;
@@ -419,30 +511,40 @@ merge:
         a.part_o + qi * nsplit * (int64_t)H * D, (short)0, (int)(nsplit * H * D * 4), BUF_RSRC_WORD3);
     const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
         a.part_ml + qi * nsplit * (int64_t)H * 2, (short)0, (int)(nsplit * H * 2 * 4), BUF_RSRC_WORD3);
-    constexpr int SC1 = 16;  // cache policy: device-coherent (bypasses the per-XCD caches)
+    const int d = l * 8;  // this lane's eight dims
+    float rope_c = 1.0f, rope_s = 0.0f;
+    if ((a.qk_flags & 2) && l < a.qk_R / 2 && c * NW < H)
+      rope_cs((double)a.q_pos[qi], l, a.qk_R, a.qk_log2_theta, rope_c, rope_s);
     for (int h = c * NW + w; h < H; h += P * NW) {
       const float s2 = a.sink ? a.sink[h] * LOG2E_F : -INFINITY;
       float mv[U1], lv[U1];
-      f32x4_t v[U1][2];
+      float v[U1][8];
 #pragma unroll
       for (int u = 0; u < U1; ++u) {
         const bool in = u < nsplit;
         const int pb = u * H + h;  // partial (qi, u, h)
         if (in) {
-          const u32x2_t ml = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rm, pb * 8, 0, SC1));
+          const u32x2_t ml =
+              __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rm, pb * 8, 0, dtl::SC1));
           mv[u] = __uint_as_float(ml[0]);
           lv[u] = __uint_as_float(ml[1]);
 #pragma unroll
-          for (int cc = 0; cc < 2; ++cc)
-            v[u][cc] = __builtin_bit_cast(
-                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, (pb * D + (cc * 64 + l) * 4) * 4, 0, SC1));
+          for (int hv = 0; hv < 2; ++hv) {
+            const f32x4_t r = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, (pb * D + d + 4 * hv) * 4, 0, dtl::SC1));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[u][4 * hv + i] = r[i];
+          }
         } else {
           mv[u] = -INFINITY;
           lv[u] = 0.0f;
-          v[u][0] = v[u][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
         }
       }
-      f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
       float Mx = s2, Z = 0.0f;
 #pragma unroll
       for (int u = 0; u < U1; ++u) Mx = fmaxf(Mx, mv[u]);
@@ -453,24 +555,36 @@ merge:
           const float e = exp2f(mv[u] - Mx);  // 0 for an empty or absent split (m = -inf)
           Z += lv[u] * e;
 #pragma unroll
-          for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[cc][q] += v[u][cc][q] * e;
+          for (int q = 0; q < 8; ++q) acc[q] += v[u][q] * e;
         }
       }
       const float inv = ok ? ((Mx != -INFINITY) ? 1.0f / Z : 0.0f) : __builtin_nanf("");
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int d = (cc * 64 + l) * 4;
-        const int64_t oo = (qi * H + h) * (int64_t)D + d;
-        if (a.out_dt == DT_BF16) {
-          const u32x2_t wv = {pack_bf16x2(acc[cc][0] * inv, acc[cc][1] * inv),
-                              pack_bf16x2(acc[cc][2] * inv, acc[cc][3] * inv)};
-          *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.out) + oo) = wv;
-        } else {
-          *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.out) + oo) =
-              f32x4_t{acc[cc][0] * inv, acc[cc][1] * inv, acc[cc][2] * inv, acc[cc][3] * inv};
+      for (int q = 0; q < 8; ++q) acc[q] *= inv;
+      if (a.qk_flags & 2) {
+        // the output's inverse rotation, pairs inside the lane's 8 dims (all
+        // lanes shuffle; lane i < R/2 formed pair i's angle before the loop)
+#pragma unroll
+        for (int q = 0; q < 8; q += 2) {
+          const bool rot = d + q >= D - a.qk_R;
+          const int src = rot ? (d + q - (D - a.qk_R)) >> 1 : 0;
+          const float c2 = __shfl(rope_c, src, 64), sn = __shfl(rope_s, src, 64);
+          if (rot) {
+            const float x0 = acc[q], x1 = acc[q + 1];
+            acc[q] = x0 * c2 + x1 * sn;
+            acc[q + 1] = x1 * c2 - x0 * sn;
+          }
         }
+      }
+      const int64_t oo = (qi * H + h) * (int64_t)D + d;
+      if (a.out_dt == DT_BF16) {
+        const u32x4_t wv = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                            pack_bf16x2(acc[6], acc[7])};
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(a.out) + oo) = wv;
+      } else {
+        float* op = reinterpret_cast<float*>(a.out) + oo;
+        *reinterpret_cast<f32x4_t*>(op) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
       }
       if (a.lse && l == 0)
         a.lse[qi * H + h] = !ok ? __builtin_nanf("") : (Mx != -INFINITY) ? (Mx + log2f(Z)) * LN2_F : -INFINITY;
@@ -487,7 +601,7 @@ static size_t r256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workgroups per query and filter passes, or false when the fused launch
 // does not apply (then the caller runs the separate kernels).
-static bool tail_plan(int64_t nq, int64_t N_max, int top_k, int slots, int split_rows, int nsplit, int* P_out,
+static bool tail_plan(int64_t nq, int64_t N_max, int top_k, int split_rows, int nsplit, int* P_out,
                       int* passes_out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= DT_MAX_DEVICES) return false;
@@ -505,7 +619,6 @@ static bool tail_plan(int64_t nq, int64_t N_max, int top_k, int slots, int split
     // exceed the CU count: then every workgroup of it runs at once
     resident = std::max(1, std::min({per, per8, 1}) * cus);
   }
-  (void)slots;
   if (nq <= 0 || nq > resident || nsplit > dtl::MAX_SPLITS || top_k > 4096) return false;
   const int64_t chunks = std::max<int64_t>(1, (N_max + dtl::FCH - 1) / dtl::FCH);
   const int64_t P = std::min<int64_t>(chunks, resident / nq);
@@ -520,8 +633,8 @@ static bool tail_plan(int64_t nq, int64_t N_max, int top_k, int slots, int split
 
 bool decode_tail_applies(int64_t nq, int64_t N_max, int top_k, int slots, int split_rows, int nsplit, int kv_dt) {
   int P = 0, passes = 0;
-  return (kv_dt == DT_BF16 || kv_dt == DT_KV_FP8) &&
-         tail_plan(nq, N_max, top_k, slots, split_rows, nsplit, &P, &passes);
+  (void)slots;
+  return (kv_dt == DT_BF16 || kv_dt == DT_KV_FP8) && tail_plan(nq, N_max, top_k, split_rows, nsplit, &P, &passes);
 }
 
 size_t decode_tail_ws_bytes(int64_t nq, int64_t N_max, int top_k, int H, int D, int slots, int split_rows,
@@ -538,7 +651,7 @@ size_t decode_tail_zero_bytes(int64_t nq) { return r256((size_t)nq * 2 * 4) + (s
 hipError_t run_decode_tail(const DecodeTailLaunch& L, hipStream_t st, bool* launched) {
   *launched = false;
   int P = 0, passes = 0;
-  if (!tail_plan(L.nq, L.N_max, L.top_k, L.slots, L.split_rows, L.nsplit, &P, &passes)) return hipSuccess;
+  if (!tail_plan(L.nq, L.N_max, L.top_k, L.split_rows, L.nsplit, &P, &passes)) return hipSuccess;
   if (L.kv_dt != DT_BF16 && L.kv_dt != DT_KV_FP8) return hipSuccess;
   TailArgs a{};
   a.q = reinterpret_cast<const uint16_t*>(L.q);
@@ -569,6 +682,11 @@ hipError_t run_decode_tail(const DecodeTailLaunch& L, hipStream_t st, bool* laun
   a.hint = L.hint;
   a.out_idx = L.out_idx;
   a.out_score = L.out_score;
+  a.qk_flags = L.qk_flags;
+  a.qk_gamma = L.qk_gamma;
+  a.qk_eps = L.qk_eps;
+  a.qk_R = L.qk_R;
+  a.qk_log2_theta = L.qk_flags ? log2((double)L.qk_theta) : 0.0;
   const int64_t nseg = std::max<int64_t>(1, (L.N_max + dtl::FCH - 1) / dtl::FCH) * dtl::NW + dtl::NW;
   uint8_t* w = reinterpret_cast<uint8_t*>(L.ws);
   a.sync = reinterpret_cast<uint32_t*>(w);

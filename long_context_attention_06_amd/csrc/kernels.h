@@ -89,6 +89,16 @@ struct AttnLaunch {
   float* part_ml;
   void* out;
   float* lse;
+  // HCA decode: the step's append of entry app_blk of every sequence (single
+  // branch, m = app_m tokens of bf16 app_Ca / app_Za from row app_tok_begin
+  // of app_n_rows), written to kv_comp by the workgroup whose split holds it
+  // before it gathers that row (app_Ca NULL: none)
+  const void* app_Ca;
+  const void* app_Za;
+  const float* app_Ba;
+  int64_t app_n_rows, app_tok_begin, app_blk;
+  int app_m;
+  void* app_out;
 };
 hipError_t run_attn(const AttnLaunch& a, hipStream_t st);
 
@@ -115,6 +125,14 @@ struct DecodeTailLaunch {
   void* out;
   float* lse;
   void* ws;              // decode_tail_ws_bytes; its first decode_tail_zero_bytes zero on entry
+  // the query's RMSNorm (qk_flags & 1, weights qk_gamma or
+  // ones) and rotation of its last qk_R dims by q_pos (qk_flags & 2, also
+  // the inverse rotation of the output); 0: none
+  int qk_flags;
+  const float* qk_gamma;
+  float qk_eps;
+  int qk_R;
+  float qk_theta;
 };
 // whether the fused launch applies (host-side; the same answer as run_decode_tail gives)
 bool decode_tail_applies(int64_t nq, int64_t N_max, int top_k, int slots, int split_rows, int nsplit, int kv_dt);

@@ -23,7 +23,7 @@ def _declared():
 
 def test_header_symbols_exported():
     names = _declared()
-    assert len(names) == 25, names
+    assert len(names) == 29, names
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
     missing = [n for n in names if n not in exported]

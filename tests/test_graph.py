@@ -96,3 +96,65 @@ def test_decode_step_graph_replays(form):
         got = step.result()
         for i, nm in enumerate(("kv row N-1", "idx", "topk scores", "out", "lse")):
             assert np.array_equal(got[i], ref[i], equal_nan=True), f"replay {rep}: {nm} differs from the eager call"
+
+
+class _HcaStep:
+    """Device tensors of one HCA decode step (append + dense MQA, one call)."""
+
+    def __init__(self, cfg):
+        L = _L()
+        self.cfg = cfg
+        x = gen.gen_decode(cfg, with_compress=True)
+        B, N, m, W = cfg.B, cfg.N, cfg.m, cfg.W
+        self.args = (_bf(x["Ca"]), _bf(x["Za"]), _t(x["Ba"]), _bf(x["q"]))
+        self.kv = _bf(x["kv_comp"])
+        self.rest = (_t(np.full((B,), N, np.int32)), _t(np.full((B,), cfg.n - 1, np.int32)), _bf(x["kv_win"]),
+                     _t(np.full((B,), W, np.int32)), _t(x["sink"]))
+        self.out = torch.empty((B, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
+        self.lse = torch.empty((B, cfg.H), device=DEV)
+        self.ws = torch.zeros(L.hca_decode_step_workspace_bytes(B, cfg.H, cfg.D, N, W), dtype=torch.uint8,
+                              device=DEV)
+        self.kw = dict(m_c=m, m=m, tok_begin=cfg.n - m, blk_begin=N - 1, blk_end=N)
+
+    def __call__(self):
+        _L().hca_decode_step(*self.args, self.kv, *self.rest, self.out, self.lse, **self.kw, ws=self.ws)
+
+    def spoil(self):
+        self.out.fill_(float("nan"))
+        self.lse.fill_(float("nan"))
+        self.kv[:, self.cfg.N - 1].fill_(7.0)
+
+    def result(self):
+        return host(self.kv[:, self.cfg.N - 1]), host(self.out), host(self.lse)
+
+
+@pytest.mark.gpu
+def test_hca_decode_step_graph_replays():
+    """Replays reuse one launch, so its merge counter must come back to zero
+    after every call; the appended entry is recomputed by each replay."""
+    print("[case] graph capture of an HCA decode step", flush=True)
+    step = _HcaStep(gen.scaled(gen.C4, B=4, n=1 << 17))
+    other = _HcaStep(gen.scaled(gen.C4, B=2, n=1 << 16))
+    step()
+    torch.cuda.synchronize()
+    ref = step.result()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        step.spoil()
+        if rep % 2:
+            other()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = step.result()
+        for i, nm in enumerate(("entry N-1", "out", "lse")):
+            assert np.array_equal(got[i], ref[i], equal_nan=True), f"replay {rep}: {nm} differs from the eager call"

@@ -157,29 +157,37 @@ def test_csa_decode_pro_1m_fp8_full_size_sampled():
     check_csa_decode(cfg, gen.gen_decode(cfg), range(cfg.B))
 
 
-def run_hca_decode(cfg, x):
+def run_hca_decode(cfg, x, step=False, ws=None, nc=None):
     """One HCA decode token per sequence, as bench.py runs it: the token
     completes block N-1 (m' divides n), whose entry is appended by
-    single-branch compression, then dense MQA over all entries + window."""
+    single-branch compression, then dense MQA over all entries + window.
+    step=True runs both through hca_decode_step (one launch)."""
     L = _L()
     B, N, m, W = cfg.B, cfg.N, cfg.m, cfg.W
     kv = _kv(cfg, x["kv_comp"])
-    L.csa_compress(_bf(x["Ca"]), None, _bf(x["Za"]), None, _t(x["Ba"]), None, kv, m=m, tok_begin=cfg.n - m,
-                   blk_begin=N - 1, blk_end=N, overlap=False)
     out = torch.empty((B, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, cfg.H), device=DEV)
-    L.hca_dense_mqa(_bf(x["q"]), kv, _t(np.full((B,), N, np.int32)), _t(np.full((B,), cfg.n - 1, np.int32)),
-                    _kv(cfg, x["kv_win"]), _t(np.full((B,), W, np.int32)), _t(x["sink"]), out, lse, m=m)
+    n_comp = _t(np.full((B,), N, np.int32) if nc is None else np.asarray(nc, np.int32))
+    q_pos = _t(np.full((B,), cfg.n - 1, np.int32))
+    if step:
+        L.hca_decode_step(_bf(x["Ca"]), _bf(x["Za"]), _t(x["Ba"]), _bf(x["q"]), kv, n_comp, q_pos,
+                          _kv(cfg, x["kv_win"]), _t(np.full((B,), W, np.int32)), _t(x["sink"]), out, lse, m_c=m, m=m,
+                          tok_begin=cfg.n - m, blk_begin=N - 1, blk_end=N, ws=ws)
+    else:
+        L.csa_compress(_bf(x["Ca"]), None, _bf(x["Za"]), None, _t(x["Ba"]), None, kv, m=m, tok_begin=cfg.n - m,
+                       blk_begin=N - 1, blk_end=N, overlap=False)
+        L.hca_dense_mqa(_bf(x["q"]), kv, n_comp, q_pos, _kv(cfg, x["kv_win"]), _t(np.full((B,), W, np.int32)),
+                        _t(x["sink"]), out, lse, m=m)
     torch.cuda.synchronize()
     return host(kv[:, N - 2:]), host(out), host(lse)
 
 
-def check_hca_decode(cfg, seqs):
+def check_hca_decode(cfg, seqs, step=False):
     x = gen.gen_decode(cfg, with_compress=True)
-    kv2, O, LS = run_hca_decode(cfg, x)
+    kv2, O, LS = run_hca_decode(cfg, x, step=step)
     N, m = cfg.N, cfg.m
     for b in seqs:
-        print(f"[case] {cfg.name} b={b}", flush=True)
+        print(f"[case] {cfg.name} b={b} step={step}", flush=True)
         ent = oracle.compress(x["Ca"][b], None, x["Za"][b], None, x["Ba"], None, m, overlap=False)[0]
         _check_entry(cfg, kv2[b, 1], ent, "hca entry N-1")
         assert np.array_equal(kv2[b, 0], x["kv_comp"][b, N - 2]), "compress wrote outside its block"
@@ -202,6 +210,51 @@ def test_hca_decode_1m_full_size():
 def test_hca_decode_1m_kv_fp8_full_size():
     cfg = gen.C4F  # mixed-precision main KV, as bench.py runs it
     check_hca_decode(cfg, range(cfg.B))
+
+
+def test_hca_decode_step_reduced():
+    check_hca_decode(gen.scaled(gen.C4, B=3, n=1 << 16), range(3), step=True)
+
+
+def test_hca_decode_step_1m_full_size():
+    cfg = gen.C4  # one launch: append, split attention and merge; every sequence checked
+    check_hca_decode(cfg, range(cfg.B), step=True)
+
+
+def test_hca_decode_step_1m_kv_fp8_full_size():
+    cfg = gen.C4F
+    check_hca_decode(cfg, range(cfg.B), step=True)
+
+
+def test_hca_decode_step_matches_separate_calls():
+    """The one-launch step against csa_compress + hca_dense_mqa: the appended
+    entry differs at most by the rounding of its fp32 sum (one step of the
+    stored format), and so the outputs by far less than the derived bound;
+    sequences see all, some or none of the appended block; a garbage
+    workspace and its reuse give the same bits as a zeroed one."""
+    cfg = gen.scaled(gen.C4, B=6, n=1 << 17)
+    x = gen.gen_decode(cfg, with_compress=True)
+    N = cfg.N
+    nc = [N, N - 1, N, 3, 0, N // 2]
+    kv_s, O_s, L_s = run_hca_decode(cfg, x, step=False, nc=nc)
+    nb = _L().hca_decode_step_workspace_bytes(cfg.B, cfg.H, cfg.D, N, cfg.W)
+    ref = None
+    for what, ws in (("zeroed", torch.zeros(nb, dtype=torch.uint8, device=DEV)),
+                     ("garbage", torch.randint(0, 256, (nb,), dtype=torch.uint8, device=DEV))):
+        for rep in range(2):
+            print(f"[case] hca step vs separate, {what} workspace, call {rep}", flush=True)
+            kv_f, O_f, L_f = run_hca_decode(cfg, x, step=True, ws=ws, nc=nc)
+            if ref is None:
+                ref = (kv_f, O_f, L_f)
+            for a_, b_, nm in zip((kv_f, O_f, L_f), ref, ("entry", "out", "lse")):
+                assert np.array_equal(a_, b_, equal_nan=True), f"{what} call {rep}: {nm} differs"
+    assert np.array_equal(kv_f[:, 0], kv_s[:, 0]), "entry N-2 changed"
+    ent_f, ent_s = kv_f[:, 1].astype(np.float64), kv_s[:, 1].astype(np.float64)
+    # one bf16 step at most: 2^-7 of the value
+    assert np.all(np.abs(ent_f - ent_s) <= 2.0 ** -7 * np.abs(ent_s)), "entry N-1"
+    for b in range(cfg.B):
+        check_out(O_f[b], O_s[b], out_bound(O_s[b]) / 4, f"hca step vs separate b={b}")
+        assert np.abs(L_f[b] - L_s[b]).max() < 1e-4
 
 
 def test_csa_decode_flash_kv_fp8_full_size_sampled():
@@ -564,3 +617,72 @@ def test_decode_step_full_size_sampled(name):
             o_own, lse_own = oracle.attend(q, rows, x["sink"])
             check_out(O[b, t], o_own, _tight(o_own), f"out on gpu idx b={b} t={t}")
             assert np.abs(LSE[b, t] - lse_own).max() < 1e-3
+
+
+def run_decode_step_qk(cfg, x):
+    """csa_decode_step_qk on the raw queries, and the same through
+    qk_norm_rope + csa_decode_step + the inverse rotation."""
+    L = _L()
+    B, N, m, k, W = cfg.B, cfg.N, cfg.m, cfg.top_k, cfg.W
+    pos = np.full((B, 1), cfg.n - 1, np.int32)
+    q_pos, n_comp = _t(pos), _t(np.full((B,), N, np.int32))
+    k_t = _bf(x["k_idx"])
+    qi, wt, q = _bf(x["q_idx"][:, None]), _t(x["w"][:, None]), _bf(x["q"][:, None])
+    win, wl = _kv(cfg, x["kv_win"]), _t(np.full((B,), W, np.int32))
+    comp = [_bf(x[nm]) for nm in ("Ca", "Cb", "Za", "Zb")]
+    gamma, scale = _t(x["q_gamma"]), 1.0 / np.sqrt(cfg.D)
+    res = []
+    for fused in (True, False):
+        kv = _kv(cfg, x["kv_comp"])
+        idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+        out = torch.empty((B, 1, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((B, 1, cfg.H), device=DEV)
+        args = (*comp, _t(x["Ba"]), _t(x["Bb"]), qi, wt, k_t, None, q_pos, n_comp)
+        kw = dict(m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, scale=scale)
+        if fused:
+            L.csa_decode_step_qk(*args, q, kv, win, wl, _t(x["sink"]), idx, out, lse, q_gamma=gamma, **kw)
+        else:
+            qn = torch.empty_like(q)
+            L.qk_norm_rope(q.view(B, cfg.H, cfg.D), qn.view(B, cfg.H, cfg.D), q_pos.view(B), gamma, norm=True,
+                           rope=True)
+            L.csa_decode_step(*args, qn, kv, win, wl, _t(x["sink"]), idx, out, lse, **kw)
+            L.qk_norm_rope(out.view(B, cfg.H, cfg.D), out.view(B, cfg.H, cfg.D), q_pos.view(B), inverse=True)
+        torch.cuda.synchronize()
+        res.append((host(kv[:, N - 1]), host(idx)[:, 0], host(out)[:, 0], host(lse)[:, 0]))
+    return res
+
+
+def _check_step_qk(cfg, seqs):
+    x = gen.gen_decode(cfg, with_compress=True)
+    (kvf, If, Of, Lf), (kvs, Is, Os, Ls) = run_decode_step_qk(cfg, x)
+    assert np.array_equal(kvf, kvs) and np.array_equal(If, Is), "entry / selection differ from the separate calls"
+    N, m = cfg.N, cfg.m
+    for b in range(cfg.B):
+        # the fused prologue sums its squares in another order, and the
+        # fused epilogue rotates before the one rounding of the output
+        check_out(Of[b], Os[b], out_bound(Os[b]), f"step_qk vs separate b={b}")
+        assert np.abs(Lf[b] - Ls[b]).max() < 1e-3
+    for b in seqs:
+        print(f"[case] {cfg.name} step_qk b={b}", flush=True)
+        comp = _kv_values(cfg, x["kv_comp"][b])
+        comp[N - 1] = _kv_values(cfg, kvf[b])
+        p = cfg.n - 1
+        q = gen.bf16_round(oracle.rope_rotate(oracle.rms_norm(x["q"][b][None], x["q_gamma"], 1e-6), [p])[0]
+                           .astype(np.float32)).astype(np.float64)
+        tau = 1.0 / np.sqrt(cfg.D)
+        oidx, o_ref, lse_ref, s = oracle.csa_query(q, x["q_idx"][b], x["w"][b], comp, x["k_idx"][b], p, N, m,
+                                                   cfg.top_k, _kv_values(cfg, x["kv_win"][b]), x["sink"], tau=tau)
+        check_topk_row(If[b], oidx, s, cfg.top_k, f"b={b}")
+        rows = np.concatenate([comp[If[b][If[b] >= 0]], _kv_values(cfg, x["kv_win"][b])])
+        o_own, lse_own = oracle.attend(q, rows, x["sink"], tau)
+        o_own = oracle.rope_rotate(o_own[None], [p], inverse=True)[0]
+        check_out(Of[b], o_own, _tight(o_own), f"step_qk out on gpu idx b={b}")
+        assert np.abs(Lf[b] - lse_own).max() < 1e-3
+
+
+def test_decode_step_qk_reduced():
+    _check_step_qk(gen.scaled(gen.C2R, B=5, n=16384), range(5))
+
+
+def test_decode_step_qk_full_size_sampled():
+    _check_step_qk(gen.C2R, [0, 17, 31])

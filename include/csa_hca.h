@@ -292,16 +292,11 @@ size_t sparse_mqa_decode_multi_workspace_bytes(int64_t B, int64_t Tq, int H, int
  *                results never depend on its contents on entry, and a
  *                zero-filled workspace (or one last used by a call of the same
  *                shape) takes the fast path.
- * With bf16 indexer queries, fewer than 8 query tokens per sequence, D = 512
- * and bf16 or KV_FP8 rows, the top-k, the attention and the merge of its
- * splits run as one launch of at most one workgroup per CU (B * Tq up to the
- * CU count, at most 16 splits of 128 rows), whose workgroups hand each other
- * their results through the workspace; otherwise as separate launches. That
- * launch waits on its own workgroups only: two calls that overlap on one
- * device (two streams) must not share a workspace, and a call running beside
- * other kernels that hold CUs for long is slowed, not deadlocked -- its waits
- * are bounded, and a query whose wait ran out gets NaN outputs and index -1.
- * Either form is an ordinary stream launch and can be captured in a HIP graph.
+ * The step is four launches: the scan (with the compression's workgroups and,
+ * for bf16 indexer queries, the top-k's digit histogram), the top-k, the
+ * split attention and the merge of the splits. Ordinary stream launches: the
+ * step can be captured in a HIP graph. Two calls that overlap on one device
+ * (two streams) must not share a workspace.
  */
 int csa_decode_step(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba, const float* Bb,
                     int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin, int64_t blk_end,
@@ -325,11 +320,11 @@ size_t csa_decode_step_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int
  *   q_gamma : [D] fp32 or NULL (ones); eps, rope_dims, rope_theta as in
  *             qk_norm_rope; qk_flags a subset of CSA_RMSNORM | CSA_ROPE.
  *   ws      : csa_decode_step_qk_workspace_bytes(...) bytes.
- * Where the step runs as one launch after the scan (see csa_decode_step) the
- * prologue runs on the query registers of that launch and the inverse
- * rotation on its merged output before the one rounding to out_dt;
- * otherwise qk_norm_rope's kernels run around the separate attention. q' is
- * rounded to bf16 once in either form.
+ * With D = 512 bf16 or KV_FP8 rows and rope_dims <= 128, the prologue runs on
+ * the attention kernel's query registers and the inverse rotation on the
+ * merged output before its one rounding to out_dt; otherwise qk_norm_rope's
+ * kernels run around the attention. q' is rounded to bf16 once in either
+ * form.
  */
 int csa_decode_step_qk(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
                        const float* Bb, int64_t n_rows, int64_t tok_begin, int d, int m_c, int64_t blk_begin,

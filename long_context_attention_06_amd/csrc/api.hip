@@ -311,9 +311,8 @@ int csa_compress_indexer_score_topk(const void* Ca, const void* Cb, const void* 
 
 // A decode step: [blocks of kv_comp completed by the step's tokens], scores,
 // top-k and sparse MQA with the split merge. The workspace holds the scores,
-// the top-k's scratch (its digit histogram first) and the tail's scratch
-// (arrival counters and sub-bin counts first, zeroed by the scan; the lists;
-// the split partials).
+// the top-k's scratch (its digit histogram first, which the scan fills) and
+// the attention's split partials.
 // The query prologue / output epilogue of csa_decode_step_qk.
 struct QkOpts {
   int flags;  // CSA_RMSNORM | CSA_ROPE
@@ -333,9 +332,9 @@ size_t csa_decode_step_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int
   const int64_t nq = B * Tq;
   int ns = 0;
   const int sr = (int)step_split_rows(top_k + W, &ns);
+  (void)sr;
   return round256((size_t)nq * N_max * 4) + round256(csa::topk_ws_bytes(B, Tq, N_max, top_k, true)) +
-         round256(std::max(csa::decode_tail_ws_bytes(nq, N_max, top_k, H, D, top_k + W, sr, ns),
-                           attn_ws(nq, H, D, ns)));
+         round256(attn_ws(nq, H, D, ns));
 }
 
 static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, const void* Zb, const float* Ba,
@@ -384,19 +383,12 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
   p += round256((size_t)nq * N_max * 4);
   uint8_t* tw = p;  // top-k scratch, digit histogram first
   p += round256(csa::topk_ws_bytes(B, Tq, N_max, top_k, true));
-  uint8_t* xw = p;  // tail scratch, or the separate attention's partials
+  uint8_t* xw = p;  // the attention's split partials
 
   csa::IndexerLaunch a{q_idx, w, k_idx, k_scale, q_pos, n_comp, B, Tq, N_max, H_I, D_I, m, q_dt, k_dt, scores};
   const int mode = csa::indexer_hint_mode(a);
   a.hint = mode != csa::TOPK_HINT_NONE ? reinterpret_cast<uint32_t*>(tw) : nullptr;
-  // the fused prologue forms each rotated pair's angle in one lane of a wave
-  const bool fused = mode == csa::TOPK_HINT_ACCUMULATED && D == 512 && kv_dt != CSA_F32 &&
-                     (!qk_on || !(qk->flags & CSA_ROPE) || qk->R <= 128) &&
-                     csa::decode_tail_applies(nq, N_max, top_k, slots, sr, ns, kv_dt);
-  if (fused) {
-    a.zero = reinterpret_cast<uint32_t*>(xw);
-    a.zero_n = (int64_t)(csa::decode_tail_zero_bytes(nq) / 4);
-  } else if (csa::topk_long_rows(N_max)) {
+  if (csa::topk_long_rows(N_max)) {
     a.zero = reinterpret_cast<uint32_t*>(tw + csa::topk_counter_offset(nq, N_max));
     a.zero_n = nq;
   }
@@ -404,63 +396,18 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
   rc = hip_status(csa::run_compress_indexer(c, a, st), "csa_decode_step");
   csa::phase_mark(csa::PHASE_SCAN, st);
   if (rc) return rc;
-  int topk_mode = mode;
-  if (fused) {
-    csa::DecodeTailLaunch t{};
-    t.q = q;
-    t.kv_comp = kv_comp;
-    t.kv_win = kv_win;
-    t.win_len = win_len;
-    t.sink = sink;
-    t.scale = scale;
-    t.nq = nq;
-    t.N_max = N_max;
-    t.Tq = (int)Tq;
-    t.H = H;
-    t.W = W;
-    t.top_k = top_k;
-    t.slots = slots;
-    t.split_rows = sr;
-    t.nsplit = ns;
-    t.kv_dt = kv_dt;
-    t.out_dt = out_dt;
-    t.scores = scores;
-    t.q_pos = q_pos;
-    t.n_comp = n_comp;
-    t.m = m;
-    t.hint = reinterpret_cast<uint32_t*>(tw);
-    t.out_idx = topk_idx;
-    t.out_score = topk_score;
-    t.out = out;
-    t.lse = lse;
-    t.ws = xw;
-    if (qk_on) {
-      t.qk_flags = ((qk->flags & CSA_RMSNORM) ? 1 : 0) | ((qk->flags & CSA_ROPE) ? 2 : 0);
-      t.qk_gamma = qk->gamma;
-      t.qk_eps = qk->eps;
-      t.qk_R = qk->R;
-      t.qk_theta = qk->theta;
-    }
-    bool launched = false;
-    (void)csa::run_decode_tail(t, st, &launched);
-    if (launched) {
-      for (int i = csa::PHASE_TOPK; i < csa::PHASES; ++i) csa::phase_mark(i, st);
-      return CSA_OK;
-    }
-    // the cooperative launch was refused: the separate kernels, the top-k
-    // rebuilding its histogram and counters (the scan zeroed the tail's)
-    (void)hipGetLastError();
-    topk_mode = csa::TOPK_HINT_NONE;
-    if (!csa::topk_long_rows(N_max)) topk_mode = mode;  // short rows read the scan's histogram as it is
-  }
   csa::TopkLaunch tk{scores, q_pos, n_comp, B, Tq, N_max, m, top_k, topk_idx, topk_score, tw,
-                     csa::topk_ws_bytes(B, Tq, N_max, top_k, true), topk_mode};
+                     csa::topk_ws_bytes(B, Tq, N_max, top_k, true), mode};
   rc = hip_status(csa::run_topk(tk, st), "csa_decode_step");
   csa::phase_mark(csa::PHASE_TOPK, st);
   if (rc) return rc;
+  // the query prologue and the output's inverse rotation ride in the
+  // attention and merge kernels (D = 512 rows; each rotated pair's angle is
+  // formed in one lane of a wave, so R / 2 <= 64); otherwise the standalone
+  // kernels run around the attention
+  const bool qk_fold = qk_on && D == 512 && kv_dt != CSA_F32 && (!(qk->flags & CSA_ROPE) || qk->R <= 128);
   const void* q_att = q;
-  if (qk_on) {
-    // the separate kernels: the standalone prologue into the workspace's last region
+  if (qk_on && !qk_fold) {
     void* qn = reinterpret_cast<uint8_t*>(ws) + base_need;
     csa::NormRopeLaunch nr{q, qn, qk->gamma, q_pos, nq, H, D, (qk->flags & CSA_ROPE) ? qk->R : 2, qk->eps,
                            qk->theta, qk->flags & (CSA_RMSNORM | CSA_ROPE), CSA_BF16};
@@ -495,8 +442,16 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
   at.part_ml = reinterpret_cast<float*>(xw + round256((size_t)nq * ns * H * D * 4));
   at.out = out;
   at.lse = lse;
+  if (qk_fold) {
+    at.q_pos = q_pos;
+    at.qk_flags = ((qk->flags & CSA_RMSNORM) ? 1 : 0) | ((qk->flags & CSA_ROPE) ? 2 : 0);
+    at.qk_gamma = qk->gamma;
+    at.qk_eps = qk->eps;
+    at.qk_R = qk->R;
+    at.qk_theta = qk->theta;
+  }
   rc = hip_status(csa::run_attn(at, st), "csa_decode_step");
-  if (rc == CSA_OK && qk_on && (qk->flags & CSA_ROPE)) {
+  if (rc == CSA_OK && qk_on && !qk_fold && (qk->flags & CSA_ROPE)) {
     csa::NormRopeLaunch nr{out, out, nullptr, q_pos, nq, H, D, qk->R, 0.0f, qk->theta, CSA_ROPE_INVERSE, out_dt};
     rc = hip_status(csa::run_norm_rope(nr, st), "csa_decode_step_qk");
   }

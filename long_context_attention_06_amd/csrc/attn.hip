@@ -54,7 +54,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
                  const int32_t* __restrict__ n_comp, const int32_t* __restrict__ q_pos, int m_rate,
                  const float* __restrict__ sink, float scale_log2, int H, int slots, int split_rows,
                  float* __restrict__ part_o, float* __restrict__ part_ml, void* __restrict__ out,
-                 float* __restrict__ lse, int out_dt, HcaAppend app) {
+                 float* __restrict__ lse, int out_dt, HcaAppend app, QkArgs qk) {
   using namespace bfk;
   constexpr int SROWB = DecRows<KV8>::SROWB, TB = DecRows<KV8>::TB;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TB];
@@ -84,6 +84,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
   }
 
   if (SRC != SRC_HCA_DEC) rr.n_rows = build_row_table<SRC, NT, TR>(src, rr, qi, tab, cnt);
+  if (SRC == SRC_SPARSE_DEC && qk.flags) qk_prologue(qb, reinterpret_cast<float*>(xchg), qk, qi);
   if constexpr (SRC == SRC_HCA_DEC) {
     if (app.Ca && sp == (int)(app.blk / split_rows)) {
       // the step's new entry is in this split: computed here and stored, and
@@ -124,6 +125,8 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
       part_ml[(pbase + head) * 2 + 1] = l_run;
     }
   } else {
+    float rope_c = 1.0f, rope_s = 0.0f;  // the output's inverse rotation: pair `lane`'s angle
+    if (SRC == SRC_SPARSE_DEC) rope_lane(qk, qi, rope_c, rope_s);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = hg * 16 + G * 4 + r;
@@ -138,7 +141,15 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
 #pragma unroll
       for (int nt = 0; nt < 16; ++nt) {
         const int64_t oo = (qi * H + h) * (int64_t)D + dbase + nt * 16;
-        const float v = o[nt][r] * fac;
+        float v = o[nt][r] * fac;
+        if (SRC == SRC_SPARSE_DEC && (qk.flags & 2) && dh * 256 + nt * 16 + 16 > D - qk.R) {
+          // the pair's other dim sits in the lane next door
+          const int d = dbase + nt * 16, s0 = D - qk.R;
+          const float other = shfl_xor(v, 1);
+          const int src = d >= s0 ? (d - s0) >> 1 : 0;
+          const float c = __shfl(rope_c, src, 64), sn = __shfl(rope_s, src, 64);
+          if (d >= s0) v = (l16 & 1) ? v * c - other * sn : v * c + other * sn;
+        }
         if (out_dt == DT_BF16)
           reinterpret_cast<uint16_t*>(out)[oo] = (uint16_t)f32_to_bf16(v);
         else
@@ -939,7 +950,7 @@ __device__ __forceinline__ void part8(const float* p, float (&v)[8]) {
 __global__ void __launch_bounds__(256)
 attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                     const float* __restrict__ sink, int H, int D, int nsplit,
-                    void* __restrict__ out, float* __restrict__ lse, int out_dt) {
+                    void* __restrict__ out, float* __restrict__ lse, int out_dt, QkArgs qk) {
   const int64_t qi = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
@@ -1010,16 +1021,36 @@ attn_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ 
     }
   }
   const float inv = (M != -INFINITY) ? 1.0f / Z : 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  if (qk.flags & 2) {
+    // the output's inverse rotation, pairs inside the lane's 8 dims; lane
+    // i < R/2 forms pair i's angle and the rotating lanes read it (every lane
+    // of the wave shuffles)
+    float rc, rs;
+    rope_lane(qk, qi, rc, rs);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bool rot = dok && d + e >= D - qk.R;
+      const int src = rot ? (d + e - (D - qk.R)) >> 1 : 0;
+      const float c = __shfl(rc, src, 64), sn = __shfl(rs, src, 64);
+      if (rot) {
+        const float x0 = acc[e], x1 = acc[e + 1];
+        acc[e] = x0 * c + x1 * sn;
+        acc[e + 1] = x1 * c - x0 * sn;
+      }
+    }
+  }
   if (dok) {
     const int64_t o = (qi * H + h) * (int64_t)D + d;
     if (out_dt == DT_BF16) {
-      const u32x4_t w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                         pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+      const u32x4_t w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                         pack_bf16x2(acc[6], acc[7])};
       *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + o) = w;
     } else {
       float* op = reinterpret_cast<float*>(out) + o;
-      *reinterpret_cast<f32x4_t*>(op) = f32x4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-      *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+      *reinterpret_cast<f32x4_t*>(op) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+      *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
     }
   }
   if (lse && l == 0) lse[qi * H + h] = (M != -INFINITY) ? (M + log2f(Z)) * LN2_F : -INFINITY;
@@ -1043,9 +1074,13 @@ static RowSrc row_src(const AttnLaunch& a) {
   return src;
 }
 
+static QkArgs qk_args(const AttnLaunch& a) {
+  return QkArgs{a.qk_flags, a.qk_gamma, a.qk_eps, a.qk_R, a.qk_flags ? log2((double)a.qk_theta) : 0.0, a.q_pos};
+}
+
 static hipError_t launch_combine(const AttnLaunch& a, hipStream_t st) {
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)a.nq, (unsigned)((a.H + 3) / 4)), dim3(256), 0, st,
-                     a.part_o, a.part_ml, a.sink, a.H, a.D, a.nsplit, a.out, a.lse, a.out_dt);
+                     a.part_o, a.part_ml, a.sink, a.H, a.D, a.nsplit, a.out, a.lse, a.out_dt, qk_args(a));
   return hipGetLastError();
 }
 
@@ -1057,7 +1092,8 @@ static hipError_t launch_bf16(const AttnLaunch& a, hipStream_t st) {
                      row_src(a), a.win_len, a.n_comp, a.q_pos, a.m_rate, a.sink, a.scale * LOG2E_F, a.H, a.slots,
                      a.split_rows, a.nsplit > 1 ? a.part_o : nullptr, a.part_ml, a.out, a.lse, a.out_dt,
                      HcaAppend{reinterpret_cast<const uint16_t*>(a.app_Ca), reinterpret_cast<const uint16_t*>(a.app_Za),
-                               a.app_Ba, a.app_n_rows, a.app_tok_begin, a.app_blk, a.app_m, a.app_out});
+                               a.app_Ba, a.app_n_rows, a.app_tok_begin, a.app_blk, a.app_m, a.app_out},
+                     qk_args(a));
   hipError_t e = hipGetLastError();
   phase_mark(PHASE_ATTN, st);
   if (e != hipSuccess || a.nsplit == 1) return e;

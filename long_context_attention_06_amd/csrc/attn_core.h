@@ -508,4 +508,95 @@ __device__ __forceinline__ void dec_tiles(const QRows& rr, const int* tab, uint8
 
 }
 
+// The query prologue and output epilogue of a decode step on raw queries
+// (DeepSeek V4 脱离 CUDA 全栈国产化, section 二, 其他辅助设计: RMSNorm of the
+// queries before the core attention, rotary encoding of the last R dims;
+// liduos.com "deepseek-v4-engineering-tradeoffs", 1M Context 的结构与取舍:
+// the output takes the inverse rotation). flags: 1 norm, 2 rotation.
+struct QkArgs {
+  int flags;
+  const float* gamma;  // [D] or NULL (ones)
+  float eps;
+  int R;               // rotated trailing dims, even, R / 2 <= 64
+  double log2_theta;
+  const int32_t* pos;  // [queries]: the rotation's position
+};
+
+// cos and sin of the angle p * theta^(-2i/R) of rotated pair i, formed in
+// double precision
+__device__ __forceinline__ void rope_cs(double p, int i, int R, double log2_theta, float& c, float& s) {
+  double sn, cs;
+  sincos(p * exp2(-2.0 * (double)i / (double)R * log2_theta), &sn, &cs);
+  c = (float)cs;
+  s = (float)sn;
+}
+
+// This lane's (cos, sin) of pair `lane` (lanes below R / 2), for the lanes
+// that rotate a pair to read by a shuffle: each angle formed once per wave.
+__device__ __forceinline__ void rope_lane(const QkArgs& qk, int64_t qi, float& c, float& s) {
+  const int l = threadIdx.x & 63;
+  c = 1.0f;
+  s = 0.0f;
+  if ((qk.flags & 2) && l < qk.R / 2) rope_cs((double)qk.pos[qi], l, qk.R, qk.log2_theta, c, s);
+}
+
+// The prologue on the decode tile loop's query operand: lane (head, G) of
+// wave (hg, dh) holds dims 256 dh + 32 s + 8 G .. +7 of its head in qb[s].
+// RMSNorm over the head's 512 dims (the waves w and w ^ 4 add their halves
+// through `half`, 8 x 16 floats of LDS), then the rotation of the pairs of
+// the last R dims (consecutive, inside a lane's 8), in fp32, rounded back to
+// bf16 once. All threads of the workgroup call it.
+__device__ __forceinline__ void qk_prologue(bf16x8_t (&qb)[8], float* half, const QkArgs& qk, int64_t qi) {
+  constexpr int D = 512;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = l >> 4, l16 = l & 15, dh = w >> 2;
+  float v[8][8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) unpack_bf16x8(__builtin_bit_cast(u32x4_t, qb[s]), v[s]);
+  if (qk.flags & 1) {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[s][e] * v[s][e];
+    ss += shfl_xor(ss, 16);
+    ss += shfl_xor(ss, 32);
+    if (G == 0) half[w * 16 + l16] = ss;
+    __syncthreads();
+    const float tot = half[w * 16 + l16] + half[(w ^ 4) * 16 + l16];
+    __syncthreads();  // `half` is free again
+    const float r = 1.0f / sqrtf(tot / (float)D + qk.eps);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[s][e] *= r * (qk.gamma ? qk.gamma[dh * 256 + s * 32 + G * 8 + e] : 1.0f);
+  }
+  if (qk.flags & 2) {
+    const int s0 = D - qk.R;  // even: a pair never straddles it
+    float cl, sl;
+    rope_lane(qk, qi, cl, sl);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (dh * 256 + s * 32 + 32 <= s0) continue;  // uniform: no rotated dim in this chunk
+      const int d0 = dh * 256 + s * 32 + G * 8;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bool rot = d0 + e >= s0;
+        const int src = rot ? (d0 + e - s0) >> 1 : 0;
+        const float c = __shfl(cl, src, 64), sn = __shfl(sl, src, 64);
+        if (rot) {
+          const float x0 = v[s][e], x1 = v[s][e + 1];
+          v[s][e] = x0 * c - x1 * sn;
+          v[s][e + 1] = x0 * sn + x1 * c;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    qb[s] = as_bf16x8(u32x4_t{pack_bf16x2(v[s][0], v[s][1]), pack_bf16x2(v[s][2], v[s][3]),
+                              pack_bf16x2(v[s][4], v[s][5]), pack_bf16x2(v[s][6], v[s][7])});
+}
+
 }  // namespace csa

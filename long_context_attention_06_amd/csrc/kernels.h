@@ -99,47 +99,17 @@ struct AttnLaunch {
   int64_t app_n_rows, app_tok_begin, app_blk;
   int app_m;
   void* app_out;
-};
-hipError_t run_attn(const AttnLaunch& a, hipStream_t st);
-
-// The fused tail of a CSA decode step (decode_tail.hip): top-k of the scores
-// in memory, sparse MQA, split merge. run_decode_tail launches nothing and
-// sets *launched = false when the fused launch does not apply to the shape.
-struct DecodeTailLaunch {
-  const void* q;
-  const void* kv_comp;
-  const void* kv_win;
-  const int32_t* win_len;
-  const float* sink;
-  float scale;
-  int64_t nq, N_max;
-  int Tq, H, W, top_k, slots, split_rows, nsplit;
-  int kv_dt, out_dt;
-  const float* scores;
-  const int32_t* q_pos;
-  const int32_t* n_comp;
-  int m;
-  uint32_t* hint;        // the scan's digit counts [nq, 2048]; cleared here
-  int32_t* out_idx;
-  float* out_score;
-  void* out;
-  float* lse;
-  void* ws;              // decode_tail_ws_bytes; its first decode_tail_zero_bytes zero on entry
-  // the query's RMSNorm (qk_flags & 1, weights qk_gamma or
-  // ones) and rotation of its last qk_R dims by q_pos (qk_flags & 2, also
-  // the inverse rotation of the output); 0: none
+  // sparse decode on raw queries: RMSNorm (qk_flags & 1, weights qk_gamma or
+  // ones) and rotation of the last qk_R dims by q_pos (qk_flags & 2, also the
+  // output's inverse rotation); 0: none
   int qk_flags;
   const float* qk_gamma;
   float qk_eps;
   int qk_R;
   float qk_theta;
 };
-// whether the fused launch applies (host-side; the same answer as run_decode_tail gives)
-bool decode_tail_applies(int64_t nq, int64_t N_max, int top_k, int slots, int split_rows, int nsplit, int kv_dt);
-size_t decode_tail_ws_bytes(int64_t nq, int64_t N_max, int top_k, int H, int D, int slots, int split_rows,
-                            int nsplit);
-size_t decode_tail_zero_bytes(int64_t nq);
-hipError_t run_decode_tail(const DecodeTailLaunch& a, hipStream_t st, bool* launched);
+hipError_t run_attn(const AttnLaunch& a, hipStream_t st);
+
 
 enum { NR_NORM = 1, NR_ROPE = 2, NR_ROPE_INV = 4 };
 struct NormRopeLaunch {

@@ -522,13 +522,14 @@ struct QkArgs {
   const int32_t* pos;  // [queries]: the rotation's position
 };
 
-// cos and sin of the angle p * theta^(-2i/R) of rotated pair i, formed in
-// double precision
+// cos and sin of the angle p * theta^(-2i/R) of rotated pair i: the angle
+// formed and reduced to [-pi, pi] in double precision (at p = 2^20 the fp32
+// product alone would be off by up to 0.06 rad; the double one by ~1e-11),
+// then the fp32 sincos of the small remainder
 __device__ __forceinline__ void rope_cs(double p, int i, int R, double log2_theta, float& c, float& s) {
-  double sn, cs;
-  sincos(p * exp2(-2.0 * (double)i / (double)R * log2_theta), &sn, &cs);
-  c = (float)cs;
-  s = (float)sn;
+  const double a = p * exp2(-2.0 * (double)i / (double)R * log2_theta);
+  const double r = a - 6.283185307179586 * rint(a * 0.15915494309189535);
+  sincosf((float)r, &s, &c);
 }
 
 // This lane's (cos, sin) of pair `lane` (lanes below R / 2), for the lanes

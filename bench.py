@@ -370,7 +370,7 @@ def bench_decode(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, copy_gbs, wna
         # events (which add their own 1-3 us)
         res["roofline"]["in_step_ms"] = round(float(ph_mean[1]), 4)
         res["phases_ms"] = {"before_call": round(float(ph_mean[0]), 4), "compress_and_scan": round(float(ph_mean[1]), 4),
-                            "topk_or_fused_tail": round(float(ph_mean[2]), 4),
+                            "topk": round(float(ph_mean[2]), 4),
                             "attention": round(float(ph_mean[3]), 4), "merge": round(float(ph_mean[4]), 4),
                             "after_call": round(float(ph_mean[5]), 4)}
         res["step_hbm_gbs"] = round(step_bytes / (ms_step * 1e-3) / 1e9, 1)

@@ -581,17 +581,20 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
           for (int r = 0; r < 4; ++r) part[nt] += wv4[r] * relu_bits(acc[r]);
         }
       }
+      // every lane group holds the four 16-entry sums: lane (G, l16) takes
+      // entry 16 G + l16, so one store covers the tile's 64 scores (256
+      // contiguous bytes) and one count instruction their digits
+      float v4[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float v = sum_rows16(part[nt]);
-        const int64_t e = tile * TE + nt * 16 + l16;
-        if (G == 0 && e < Vq) {
-          const float sc = KDT == DT_FP8 ? v * __uint_as_float(k_scale[b * N_max + e]) : v;
-          srow[e] = sc;
-          if (hint) {
-            const uint32_t d = f32_key(sc) >> DIG_SHIFT;
-            atomicAdd(&lds_h[wv][d >> 1], 1u << ((d & 1u) << 4));
-          }
+      for (int nt = 0; nt < 4; ++nt) v4[nt] = sum_rows16(part[nt]);
+      const float v = G == 0 ? v4[0] : G == 1 ? v4[1] : G == 2 ? v4[2] : v4[3];
+      const int64_t e = tile * TE + G * 16 + l16;
+      if (e < Vq) {
+        const float sc = KDT == DT_FP8 ? v * __uint_as_float(k_scale[b * N_max + e]) : v;
+        srow[e] = sc;
+        if (hint) {
+          const uint32_t d = f32_key(sc) >> DIG_SHIFT;
+          atomicAdd(&lds_h[wv][d >> 1], 1u << ((d & 1u) << 4));
         }
       }
     }

@@ -60,7 +60,7 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TB];
   __shared__ __attribute__((aligned(16))) f32x4_t xchg[NW][2][64];
   __shared__ __attribute__((aligned(16))) int tab[SRC == SRC_HCA_DEC ? 4 : TAB_MAX];
-  __shared__ int cnt[2 * NW];
+  __shared__ int cnt[2 * TAB_MAX / 64];
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -79,11 +79,16 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
   {
     const bool hok = head < H;
     const uint16_t* qp = q + (qi * H + (hok ? head : 0)) * (int64_t)D + dh * 256 + G * 8;
+    // loaded unconditionally (the head is clamped), zeroed after: loads under
+    // a branch would each be waited for
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(hok ? ld16(qp + s * 32) : u32x4_t{0, 0, 0, 0});
+    for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(ld16(qp + s * 32));
+    if (!hok)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(u32x4_t{0, 0, 0, 0});
   }
 
-  if (SRC != SRC_HCA_DEC) rr.n_rows = build_row_table<SRC, NT, TR>(src, rr, qi, tab, cnt);
+  if (SRC != SRC_HCA_DEC) rr.n_rows = build_row_table<SRC, NT, TR, 1>(src, rr, qi, tab, cnt);
   if (SRC == SRC_SPARSE_DEC && qk.flags) qk_prologue(qb, reinterpret_cast<float*>(xchg), qk, qi);
   if constexpr (SRC == SRC_HCA_DEC) {
     if (app.Ca && sp == (int)(app.blk / split_rows)) {
@@ -232,12 +237,16 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   constexpr int PITCH = KV8 ? 592 : ROWB;
   constexpr int TB = KV8 ? TR * PITCH + 64 : TILEB;
   auto lrow = [](int r) { return KV8 ? r * PITCH + (r >> 4) * 64 : r * ROWB; };
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * TB];
+  // the query's rows (64 heads x 1 KB) are staged from ring slot 2 on before
+  // the first tiles reach slots 2 and 3
+  constexpr int QOFF = 2 * TB;
+  constexpr int RING = NBUF * TB > QOFF + 64 * ROWB ? NBUF * TB : QOFF + 64 * ROWB;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
   __shared__ __attribute__((aligned(16))) uint16_t pbuf[2][2][32 * PSTR];  // [tile parity][head group] P^T
   __shared__ __attribute__((aligned(16))) float lmx[2][2][2][64];          // [head group][row half][hq][lane]
   __shared__ __attribute__((aligned(16))) int flg[2][NW];                  // [tile parity][wave]: P must be redone
   __shared__ __attribute__((aligned(16))) int tab[SRC == SRC_HCA_PRE ? 4 : TAB_MAX];
-  __shared__ int cnt[2 * NW];
+  __shared__ int cnt[2 * TAB_MAX / 64];
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
@@ -252,24 +261,42 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
 
   QRows rr = query_rows<SRC, SROWB>(src, nullptr, nullptr, q_pos, m_rate, qi, 0, slots, slots);
 
-  // ---- Q^T operand (B of S = K Q^T): head 32 hg + 16 hq + l16, dims 32 ks + 8 gc
-  // .. +7 with gc = the two bits of g16 swapped (the K operand takes the same
-  // dims; the order only decides which 16-byte chunk each lane group reads)
-  const int gc = ((g16 & 1) << 1) | (g16 >> 1);
-  bf16x8_t qb[2][16];
+  // ---- the first memory round trip carries everything that does not depend
+  // on the row table: (sparse) the slots' top-k codes, by DMA into the
+  // table's own words (top-k slots only; the window slots are arithmetic),
+  // then the query's head rows, by DMA into LDS (one coalesced 1 KB row per
+  // instruction; wave w takes heads w, w + 4, ..., rows past H repeat row
+  // H - 1 so every wave issues QPW of them). Chunk c of head row h sits at
+  // chunk c ^ (h & 15) of its LDS row, so the operand reads below (16 heads
+  // at one dim offset) fall in 16 distinct bank groups.
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  if constexpr (SRC == SRC_SPARSE_PRE) {
+    const int32_t* codes = src.idx + qi * src.top_k;
+    const uint32_t tab_lds = (uint32_t)(uintptr_t)tab;
 #pragma unroll
-  for (int hq = 0; hq < 2; ++hq) {
-    const int head = 32 * hg + 16 * hq + l16;
-    const bool hok = head < H;
-    const uint16_t* qp = q + (qi * H + (hok ? head : 0)) * (int64_t)D + 8 * gc;
+    for (int c = 0; c < TAB_MAX / 64; c += NW) {
+      const int j0 = (c + w) * 64;  // this wave's 64 slots
+      if (j0 < src.top_k)
+        dma_dword(uniform_ptr(codes), (uint32_t)(min(j0 + l, src.top_k - 1) * 4), tab_lds + (uint32_t)(j0 * 4));
+    }
+  }
+  constexpr int QPW = 64 / NW;  // head rows per wave
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qb[hq][ks] = as_bf16x8(hok ? ld16(qp + 32 * ks) : u32x4_t{0, 0, 0, 0});
+  for (int i = 0; i < QPW; ++i) {
+    const int hh = min(w + NW * i, H - 1);
+    dma_row(uniform_ptr(reinterpret_cast<const uint8_t*>(q + (qi * H + hh) * (int64_t)D)),
+            (uint32_t)((l ^ ((w + NW * i) & 15)) * 16), ring_lds + QOFF + (w + NW * i) * ROWB);
   }
 
   // sparse: a row table in LDS; HCA: rows are entries 0 .. V-1 and then the
   // window tokens, addressed arithmetically
   int n_comp_rows = rr.len1;
-  if (SRC == SRC_SPARSE_PRE) rr.n_rows = build_row_table<SRC, NT, TR>(src, rr, qi, tab, cnt, &n_comp_rows);
+  if constexpr (SRC == SRC_SPARSE_PRE) {
+    vm_barrier<QPW>();  // every wave's codes have landed (only query rows in flight)
+    // compacted in place: every code is read before the first table write
+    rr.n_rows = build_row_table_from<SRC, NT, TR, TAB_MAX / NT>(src, rr, qi, tab, cnt, &n_comp_rows,
+                                                                [&](int j) { return tab[j]; });
+  }
   const int n_rows = rr.n_rows;
   const int ntiles = (n_rows + TR - 1) / TR;
   // table entries below ncb are compressed rows, the rest window rows (the
@@ -279,7 +306,6 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   // lane offset, so rows from one cache need no per-row 64-bit address
   const bool off32 = src.N_max < (1 << 22) && src.T_tok < (1 << 22);
 
-  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   uint32_t voff[RPW];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) voff[i] = KV8 ? (uint32_t)(l * 16) : (uint32_t)((l ^ swz4(RPW * w + i)) * 16);
@@ -321,12 +347,39 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
     }
   };
 
+  // tiles 0 and 1 go out behind the query rows; once those have landed, each
+  // wave reads its Q^T operand and slot 2 is free for tile 2
+  for (int t = 0; t < ntiles && t < 2; ++t) issue(t);
+  if (ntiles >= 2)
+    vm_barrier<2 * RPW>();
+  else if (ntiles == 1)
+    vm_barrier<RPW>();
+  else
+    vm_barrier<0>();
+  // ---- Q^T operand (B of S = K Q^T): head 32 hg + 16 hq + l16, dims 32 ks + 8 gc
+  // .. +7 with gc = the two bits of g16 swapped (the K operand takes the same
+  // dims; the order only decides which 16-byte chunk each lane group reads)
+  const int gc = ((g16 & 1) << 1) | (g16 >> 1);
+  bf16x8_t qb[2][16];
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq) {
+    const int head = 32 * hg + 16 * hq + l16;
+    const uint8_t* qr = ring + QOFF + head * ROWB;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      qb[hq][ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qr + (((4 * ks + gc) ^ (head & 15)) * 16)));
+    if (head >= H)
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qb[hq][ks] = as_bf16x8(u32x4_t{0, 0, 0, 0});
+  }
   // Q^T waits in accumulation registers (MFMA reads its A/B operands from
   // either file), leaving the VGPRs to the reads in flight
 #pragma unroll
   for (int hq = 0; hq < 2; ++hq)
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(qb[hq][ks]));
+  // every wave's reads of the staged rows are done before tile 2 lands there
+  vm_barrier<2 * RPW>();
 
   f32x16_t o[8];
 #pragma unroll
@@ -511,7 +564,7 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   };
 
   u32x4_t pcur[2] = {u32x4_t{0, 0, 0, 0}, u32x4_t{0, 0, 0, 0}};  // P^T operand of the tile in hand
-  for (int t = 0; t < ntiles && t < NBUF - 1; ++t) issue(t);
+  if (ntiles > 2) issue(2);
   if (ntiles > 0) {
     if (ntiles > 2)
       vm_barrier<RPW>();  // tiles 0 and 1 resident, tile 2 may be in flight

@@ -183,69 +183,110 @@ __device__ __forceinline__ QRows query_rows(const RowSrc& src, const int32_t* __
 // id, or 0x80000000 | window row; invalid slots dropped, slot order kept (so
 // the compressed rows come first), the tail padded to a whole tile of TR with
 // the last row (those rows are masked). Returns the row count; the number of
-// compressed rows goes to *n_comp when it is given. cnt holds 2 NT/64 ints.
-template <int SRC, int NT, int TR, class CodeFn>
+// compressed rows goes to *n_comp when it is given. cnt holds 2 NCH NT/64 ints.
+//
+// Slots go in groups of NCH chunks of NT: a group's codes are all read before
+// any is ranked (one memory round trip per group), and its ranks take one
+// exchange of per-(chunk, wave) counts, two barriers per group. A split of one
+// group pads its table in the same pass.
+template <int SRC, int NT, int TR, int NCH, class CodeFn>
 __device__ int build_row_table_from(const RowSrc& src, const QRows& r, int64_t qi, int* tab, int* cnt, int* n_comp,
                                     CodeFn code_of) {
-  constexpr int NW = NT / 64;
+  constexpr int NW = NT / 64, GS = NCH * NT;
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int n_rows = 0, n_c = 0;
-  for (int c0 = r.s_begin; c0 < r.s_end; c0 += NT) {
-    const int j = c0 + tid;
-    int e = 0;
-    bool ok = false;
-    if (j < r.s_end) {
-      if (j < src.top_k) {
-        const int id = code_of(j);  // the slot's compressed entry (-1: empty)
-        ok = id >= 0 && id < src.N_max;
-        e = id;
+  const int ngroups = max(0, r.s_end - r.s_begin + GS - 1) / GS;
+  int n_rows = 0, nc = 0;
+  for (int g = 0; g < ngroups; ++g) {
+    const int base = r.s_begin + g * GS;
+    // the slots' compressed entries (-1: empty) first, at clamped slots and
+    // without branches, so the loads are in flight together
+    int id[NCH];
+    if (src.top_k > 0) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) id[c] = code_of(min(max(base + c * NT + tid, 0), src.top_k - 1));
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) id[c] = -1;
+    }
+    int e[NCH];
+    bool ok[NCH];
+    uint64_t bal[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int j = base + c * NT + tid;
+      const int ww = j - src.top_k;  // window slot
+      bool okw;
+      int row;
+      if (SRC == SRC_SPARSE_DEC) {
+        okw = ww < r.lim0;
+        row = r.w0 + ww;  // this query's window starts at buffer row w0
       } else {
-        const int ww = j - src.top_k;
-        int row = ww;
-        if (SRC == SRC_SPARSE_DEC) {
-          ok = ww < r.lim0;
-          row = r.w0 + ww;  // this query's window starts at buffer row w0
-        } else {
-          const int64_t tok = (int64_t)r.lim1 - src.W + 1 + ww;
-          ok = tok >= 0 && tok < src.T_tok;
-          row = (int)tok;
-        }
-        e = (int)(0x80000000u | (uint32_t)row);
+        const int64_t tok = (int64_t)r.lim1 - src.W + 1 + ww;
+        okw = tok >= 0 && tok < src.T_tok;
+        row = (int)tok;
+      }
+      const bool is_c = j < src.top_k;
+      ok[c] = j < r.s_end && (is_c ? (id[c] >= 0 && id[c] < src.N_max) : okw);
+      e[c] = is_c ? id[c] : (int)(0x80000000u | (uint32_t)row);
+      // counts of valid slots (and of valid compressed slots) per (chunk,
+      // wave) at index c NW + w: the slots' order
+      bal[c] = __ballot(ok[c]);
+      const uint64_t balc = __ballot(ok[c] && is_c);  // the whole wave votes
+      if (l == 0) {
+        cnt[c * NW + w] = __popcll(bal[c]);
+        cnt[NCH * NW + c * NW + w] = __popcll(balc);
       }
     }
-    const uint64_t bal = __ballot(ok);
-    const uint64_t balc = __ballot(ok && j < src.top_k);  // the whole wave votes
-    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-    if (l == 0) {
-      cnt[w] = __popcll(bal);
-      cnt[NW + w] = __popcll(balc);
-    }
     __syncthreads();
-    int off = n_rows, tot = 0;
+    // rows before each (chunk, this wave): the counts are read together (one
+    // LDS round trip) and summed in vector registers. The opaque zero offset
+    // keeps them there: read as uniform values they would go to scalar
+    // registers one read and one wait at a time.
+    int zo = 0;
+    asm volatile("" : "+v"(zo));
+    int off[NCH];
 #pragma unroll
-    for (int v = 0; v < NW; ++v) {
-      const int c = cnt[v];
-      off += v < w ? c : 0;
-      tot += c;
-      n_c += cnt[NW + v];
+    for (int c = 0; c < NCH; ++c) {
+      int before = 0, tot = 0;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        const int k = cnt[zo + c * NW + v];
+        before += v < w ? k : 0;
+        tot += k;
+        nc += cnt[zo + NCH * NW + c * NW + v];
+      }
+      off[c] = n_rows + before;
+      n_rows += tot;
     }
-    if (ok) tab[off + rank] = e;
-    n_rows += tot;
+    const int padded = ngroups == 1 ? (n_rows + TR - 1) / TR * TR : n_rows;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int rank =
+          __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[c] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[c], 0));
+      if (ok[c]) {
+        tab[off[c] + rank] = e[c];
+        // the last row also fills the padding
+        if (off[c] + rank == n_rows - 1)
+          for (int k = n_rows; k < padded; ++k) tab[k] = e[c];
+      }
+    }
     __syncthreads();
   }
-  const int padded = (n_rows + TR - 1) / TR * TR;
-  if (n_rows > 0 && n_rows + tid < padded) tab[n_rows + tid] = tab[n_rows - 1];
-  __syncthreads();
-  if (n_comp) *n_comp = n_c;
-  return n_rows;
+  if (ngroups > 1) {
+    const int padded = (n_rows + TR - 1) / TR * TR;
+    if (n_rows > 0 && n_rows + tid < padded) tab[n_rows + tid] = tab[n_rows - 1];
+    __syncthreads();
+  }
+  if (n_comp) *n_comp = __builtin_amdgcn_readfirstlane(nc);
+  return __builtin_amdgcn_readfirstlane(n_rows);
 }
 
 // The same with the slots' entries read from the top-k output in memory.
-template <int SRC, int NT, int TR>
+template <int SRC, int NT, int TR, int NCH>
 __device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, int* tab, int* cnt,
                                int* n_comp = nullptr) {
-  return build_row_table_from<SRC, NT, TR>(src, r, qi, tab, cnt, n_comp,
+  return build_row_table_from<SRC, NT, TR, NCH>(src, r, qi, tab, cnt, n_comp,
                                            [&](int j) { return src.idx[qi * src.top_k + j]; });
 }
 

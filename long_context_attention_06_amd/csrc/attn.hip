@@ -313,7 +313,16 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   auto row_dma = [&](const uint8_t* base, uint32_t off, uint32_t lds) {
     if (!KV8 || l < SROWB / 16) dma_row(base, off, __builtin_amdgcn_readfirstlane(lds));
   };
-  auto issue = [&](int t) {
+  // a tile's gathers in two parts: its eight table entries per wave (LDS
+  // reads that can go out early) and the row DMAs
+  auto tab_entries = [&](int t, u32x4_t& e0, u32x4_t& e1) {
+    if constexpr (SRC == SRC_SPARSE_PRE) {
+      const int c0 = t * TR + RPW * w;
+      e0 = *reinterpret_cast<const u32x4_t*>(&tab[c0]);
+      e1 = *reinterpret_cast<const u32x4_t*>(&tab[c0 + 4]);
+    }
+  };
+  auto issue_dma = [&](int t, const u32x4_t& e0, const u32x4_t& e1) {
     const int c0 = t * TR + RPW * w;
     const uint32_t dst = ring_lds + (uint32_t)((t & (NBUF - 1)) * TB);
     if constexpr (SRC == SRC_HCA_PRE) {
@@ -327,8 +336,6 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
       }
       return;
     }
-    const u32x4_t e0 = *reinterpret_cast<const u32x4_t*>(&tab[c0]);
-    const u32x4_t e1 = *reinterpret_cast<const u32x4_t*>(&tab[c0 + 4]);
     const bool comp_only = c0 + RPW <= ncb, win_only = c0 >= ncb;
     if (off32 && (comp_only || win_only)) {
       // one base for the wave's eight rows; the shift drops the window flag
@@ -345,6 +352,11 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
         row_dma(uniform_ptr(tab_row<SROWB>(rr, e)), voff[i], dst + lrow(RPW * w + i));
       }
     }
+  };
+  auto issue = [&](int t) {
+    u32x4_t e0{0u, 0u, 0u, 0u}, e1{0u, 0u, 0u, 0u};
+    tab_entries(t, e0, e1);
+    issue_dma(t, e0, e1);
   };
 
   // tiles 0 and 1 go out behind the query rows; once those have landed, each
@@ -564,13 +576,20 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   };
 
   u32x4_t pcur[2] = {u32x4_t{0, 0, 0, 0}, u32x4_t{0, 0, 0, 0}};  // P^T operand of the tile in hand
+  // tiles 2 and 3 take the slots the query rows left
   if (ntiles > 2) issue(2);
+  if (ntiles > 3) issue(3);
+  // K operand of the next tile's first four k-steps: read right after the
+  // barrier that makes the tile resident, so the first products need not
+  // wait for LDS
+  u32x4_t kr[16];
   if (ntiles > 0) {
-    if (ntiles > 2)
-      vm_barrier<RPW>();  // tiles 0 and 1 resident, tile 2 may be in flight
+    if (ntiles > 3)
+      vm_barrier<2 * RPW>();  // tiles 0 and 1 resident, tiles 2 and 3 may be in flight
+    else if (ntiles > 2)
+      vm_barrier<RPW>();
     else
       vm_barrier<0>();
-    u32x4_t kr[16];
     k_reads(ring, kr);
     f32x4_t s[2];
     qk(kr, s);
@@ -580,10 +599,13 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
     vm_barrier<63>();
     if (flags_set(0)) slow(s, 0, l_prev);
     p_reads(0, pcur);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kr[ks] = k_at(ring + (1 & (NBUF - 1)) * TB, ks);
   }
   for (int t = 0; t < ntiles; ++t) {
-    const bool iss = t + NBUF - 1 < ntiles, nxt = t + 1 < ntiles;
-    if (iss) issue(t + NBUF - 1);  // the slot of tile t-1, free since the last barrier
+    // tile t+3 is in flight (issued after the last barrier); tile t+4 goes
+    // out after this iteration's barrier, into tile t's slot
+    const bool iss = t + NBUF - 1 < ntiles, nxt = t + 1 < ntiles, iss4 = t + NBUF < ntiles;
     const uint8_t* R = ring + (t & (NBUF - 1)) * TB;
     const uint8_t* RN = ring + ((t + 1) & (NBUF - 1)) * TB;
 
@@ -612,27 +634,43 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
             (s16x4_t __attribute__((address_space(3)))*)(R + pofs[ks][rd][nt & 3] + (nt >> 2) * 256));
       }
     };
-    u32x4_t kr[16];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kr[ks] = k_read(ks);
     f32x4_t s[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+    // bf16 rows: the S products take the K reads and the V reads of N-tiles
+    // 0 and 1 only; the other V reads go out during the PV products, two
+    // N-tiles ahead, so each phase carries part of the LDS traffic
+    constexpr bool VSPLIT = !KV8;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       if (ks + 4 < 16) kr[ks + 4] = k_read(ks + 4);
-      v_read(2 * ks);
-      v_read(2 * ks + 1);
+      if (VSPLIT) {
+        if (ks >= 8) v_read(ks - 8);
+      } else {
+        v_read(2 * ks);
+        v_read(2 * ks + 1);
+      }
 #pragma unroll
       for (int hq = 0; hq < 2; ++hq) s[hq] = mfma16(kop(kr[ks], ks), qb[hq][ks], s[hq]);
       __builtin_amdgcn_sched_barrier(0x006);  // only VALU / SALU work moves across
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    u32x4_t te0{0u, 0u, 0u, 0u}, te1{0u, 0u, 0u, 0u};  // table entries of tile t+4
+    if (iss4) tab_entries(t + NBUF, te0, te1);
+
     // ---- O^T += V^T P^T of tile t over this wave's 256 dims: 8 N-tiles of 32
-    // dims, 2 k-steps of 16 rows; the softmax of tile t+1 runs between them
+    // dims, 2 k-steps of 16 rows; the softmax of tile t+1 runs between them.
+    // bf16 rows: each N-tile's V reads go out two N-tiles ahead, in a
+    // scheduling region of their own, so the reads keep their distance
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
+        if (VSPLIT && ks == 0) {
+          if (nt + 2 < 8)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v_read(4 * (nt + 2) + i);
+          __builtin_amdgcn_sched_barrier(0x006);  // only VALU / SALU work moves across
+        }
         bf16x8_t bv;
         if constexpr (KV8) {
           const i32x2_t c = v8[nt][ks];
@@ -654,10 +692,12 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
     const float l_prev[2] = {l_run[0], l_run[1]};
     mask_tail(s, t + 1);
     post_flag(softmax(s, (t + 1) & 1), (t + 1) & 1);
+    if constexpr (!VSPLIT) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);  // VALU
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 1);  // VALU
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -668,8 +708,19 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
     else
       vm_barrier<0>();
     if (nxt) {
-      if (flags_set((t + 1) & 1)) slow(s, (t + 1) & 1, l_prev);
+      // the flags, the next P^T and the first K reads of tile t+2 go out
+      // together, then tile t+4's gathers, and only then is the flag word
+      // waited for
+      const u32x4_t f = *reinterpret_cast<const u32x4_t*>(&flg[(t + 1) & 1][0]);
       p_reads((t + 1) & 1, pcur);
+      const uint8_t* RN2 = ring + ((t + 2) & (NBUF - 1)) * TB;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kr[ks] = k_at(RN2, ks);
+      if (iss4) issue_dma(t + NBUF, te0, te1);
+      if (__builtin_amdgcn_readfirstlane(f[0] | f[1] | f[2] | f[3]) != 0) {
+        slow(s, (t + 1) & 1, l_prev);
+        p_reads((t + 1) & 1, pcur);
+      }
     } else {
       l_run[0] = l_prev[0];
       l_run[1] = l_prev[1];

@@ -196,7 +196,7 @@ def main():
 
 def run_workload(w, a, torch, L, gen, dev, steps, warmup, cpu_s, copy_gbs):
     if w in ("c3", "c3f"):
-        return bench_prefill(a, torch, L, gen, dev, gen.C3F if w == "c3f" else gen.C3, steps, warmup, cpu_s)
+        return bench_prefill(a, torch, L, gen, dev, gen.C3F if w == "c3f" else gen.C3, steps, warmup, cpu_s, w)
     if w == "c6":
         return bench_hca_prefill(a, torch, L, gen, dev, steps, warmup, cpu_s)
     cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X, "c4f": gen.C4F, "c2f": gen.C2F,
@@ -418,7 +418,7 @@ def prefill_flops(cfg, pos):
     return idx, mqa
 
 
-def bench_prefill(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s):
+def bench_prefill(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, wname):
     """CSA prefill of one 65536-token sequence: compression of all tokens, then
     16 chunks of 4096 queries through scores, top-k and sparse MQA (main KV
     rows in bf16, or E4M3 + bf16 RoPE dims)."""
@@ -496,9 +496,13 @@ def bench_prefill(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s):
         # per launch: a 4096-query chunk (all chunks' flops over all chunks' time)
         "roofline": _roofline("mfma", "attn_prs_kernel<2, %s> (sparse prefill, per 4096-query chunk)"
                               % ("true" if fp8 else "false"), mqa_fl / nch, float(np.mean(attn_ms)),
-                              BF16_PEAK_TFLOPS, "TFLOP/s"),
+                              BF16_PEAK_TFLOPS, "TFLOP/s",
+                              _traffic(f"attn_prefill_{wname}_traffic.txt",
+                                       ["attn.hip", "attn_core.h", "compress_entry.h", "common.h"])),
         "roofline_indexer": _roofline("mfma", "idx_prefill_kernel (per 4096-query chunk)", idx_fl / nch,
-                                      float(np.mean(idx_ms)), BF16_PEAK_TFLOPS, "TFLOP/s"),
+                                      float(np.mean(idx_ms)), BF16_PEAK_TFLOPS, "TFLOP/s",
+                                      _traffic(f"idx_prefill_{wname}_traffic.txt",
+                                               ["indexer.hip", "common.h", "compress_entry.h"])),
         "phases_ms": {"compress": round(comp_ms, 4), "indexer_total": round(sum(idx_ms), 4),
                       "topk_total": round(sum(topk_ms), 4), "attention_total": round(sum(attn_ms), 4)},
     })

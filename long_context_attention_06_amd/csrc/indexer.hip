@@ -491,6 +491,10 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   if (hint)
     for (int i = l; i < DIG_BINS / 2; i += 64) lds_h[wv][i] = 0u;
 
+  // this lane's head weights, read once (heads 16 mt + 4 G + r)
+  f32x4_t wq[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) wq[mt] = *reinterpret_cast<const f32x4_t*>(&lds_w[wv][mt * 16 + G * 4]);
   bf16x8_t qa[4][KS];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -570,16 +574,20 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
           for (int s = 0; s < KS; ++s)
             kbv[s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + (((G * 4 + s) ^ sw) * 16)));
         }
+        // the four head tiles' chains interleaved, each product three
+        // products after the one it accumulates onto
+        f32x4_t acc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16(qa[mt][s], kbv[s], acc[mt]);
         part[nt] = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], kbv[s], acc);
-          const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[wv][mt * 16 + G * 4]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) part[nt] += wv4[r] * relu_bits(acc[r]);
-        }
+          for (int r = 0; r < 4; ++r) part[nt] += wq[mt][r] * relu_bits(acc[mt][r]);
       }
       // every lane group holds the four 16-entry sums: lane (G, l16) takes
       // entry 16 G + l16, so one store covers the tile's 64 scores (256

@@ -74,21 +74,24 @@ attn_bf16_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __re
 
   QRows rr = query_rows<SRC, SROWB>(src, win_len, n_comp, q_pos, m_rate, qi, sp, slots, split_rows);
 
-  // ---- Q^T operand (B of S^T = R Q^T): lane (head, G), dims 256 dh + 32 s + 8 G .. +7
+  // ---- Q^T operand (B of S^T = R Q^T): lane (head, G), dims 256 dh + 32 s + 8 G .. +7,
+  // loaded unconditionally (the head is clamped) and zeroed after (loads
+  // under a branch would each be waited for); for a sparse split the loads go
+  // out right behind the split's slot codes, which then need not wait for them
   bf16x8_t qb[8];
-  {
-    const bool hok = head < H;
+  const bool hok = head < H;
+  auto load_q = [&]() {
     const uint16_t* qp = q + (qi * H + (hok ? head : 0)) * (int64_t)D + dh * 256 + G * 8;
-    // loaded unconditionally (the head is clamped), zeroed after: loads under
-    // a branch would each be waited for
 #pragma unroll
     for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(ld16(qp + s * 32));
-    if (!hok)
+  };
+  if constexpr (SRC != SRC_HCA_DEC)
+    rr.n_rows = build_row_table<SRC, NT, TR, 1>(src, rr, qi, tab, cnt, nullptr, load_q);
+  else
+    load_q();
+  if (!hok)
 #pragma unroll
-      for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(u32x4_t{0, 0, 0, 0});
-  }
-
-  if (SRC != SRC_HCA_DEC) rr.n_rows = build_row_table<SRC, NT, TR, 1>(src, rr, qi, tab, cnt);
+    for (int s = 0; s < 8; ++s) qb[s] = as_bf16x8(u32x4_t{0, 0, 0, 0});
   if (SRC == SRC_SPARSE_DEC && qk.flags) qk_prologue(qb, reinterpret_cast<float*>(xchg), qk, qi);
   if constexpr (SRC == SRC_HCA_DEC) {
     if (app.Ca && sp == (int)(app.blk / split_rows)) {
@@ -294,8 +297,8 @@ attn_prs_kernel(const uint16_t* __restrict__ q, RowSrc src, const int32_t* __res
   if constexpr (SRC == SRC_SPARSE_PRE) {
     vm_barrier<QPW>();  // every wave's codes have landed (only query rows in flight)
     // compacted in place: every code is read before the first table write
-    rr.n_rows = build_row_table_from<SRC, NT, TR, TAB_MAX / NT>(src, rr, qi, tab, cnt, &n_comp_rows,
-                                                                [&](int j) { return tab[j]; });
+    rr.n_rows = build_row_table_from<SRC, NT, TR, TAB_MAX / NT>(
+        src, rr, qi, tab, cnt, &n_comp_rows, [&](int j) { return tab[j]; }, [] {});
   }
   const int n_rows = rr.n_rows;
   const int ntiles = (n_rows + TR - 1) / TR;

@@ -188,20 +188,21 @@ __device__ __forceinline__ QRows query_rows(const RowSrc& src, const int32_t* __
 // Slots go in groups of NCH chunks of NT: a group's codes are all read before
 // any is ranked (one memory round trip per group), and its ranks take one
 // exchange of per-(chunk, wave) counts, two barriers per group. A split of one
-// group pads its table in the same pass.
-template <int SRC, int NT, int TR, int NCH, class CodeFn>
+// group pads its table in the same pass. pre() runs once, right after the
+// first group's code loads are issued: loads the caller puts there go out in
+// the same memory round trip without the codes waiting behind them.
+template <int SRC, int NT, int TR, int NCH, class CodeFn, class PreFn>
 __device__ int build_row_table_from(const RowSrc& src, const QRows& r, int64_t qi, int* tab, int* cnt, int* n_comp,
-                                    CodeFn code_of) {
+                                    CodeFn code_of, PreFn pre) {
   constexpr int NW = NT / 64, GS = NCH * NT;
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ngroups = max(0, r.s_end - r.s_begin + GS - 1) / GS;
   int n_rows = 0, nc = 0;
-  for (int g = 0; g < ngroups; ++g) {
+  // the slots' compressed entries (-1: empty) of group g, at clamped slots
+  // and without branches, so the loads are in flight together
+  auto load_codes = [&](int g, int (&id)[NCH]) {
     const int base = r.s_begin + g * GS;
-    // the slots' compressed entries (-1: empty) first, at clamped slots and
-    // without branches, so the loads are in flight together
-    int id[NCH];
     if (src.top_k > 0) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) id[c] = code_of(min(max(base + c * NT + tid, 0), src.top_k - 1));
@@ -209,6 +210,9 @@ __device__ int build_row_table_from(const RowSrc& src, const QRows& r, int64_t q
 #pragma unroll
       for (int c = 0; c < NCH; ++c) id[c] = -1;
     }
+  };
+  auto group = [&](int g, const int (&id)[NCH]) {
+    const int base = r.s_begin + g * GS;
     int e[NCH];
     bool ok[NCH];
     uint64_t bal[NCH];
@@ -272,6 +276,17 @@ __device__ int build_row_table_from(const RowSrc& src, const QRows& r, int64_t q
       }
     }
     __syncthreads();
+  };
+  // the first group outside the loop, so the waits for its codes count only
+  // the loads pre() puts behind them
+  int id0[NCH];
+  load_codes(0, id0);
+  pre();
+  if (ngroups > 0) group(0, id0);
+  for (int g = 1; g < ngroups; ++g) {
+    int id[NCH];
+    load_codes(g, id);
+    group(g, id);
   }
   if (ngroups > 1) {
     const int padded = (n_rows + TR - 1) / TR * TR;
@@ -283,11 +298,11 @@ __device__ int build_row_table_from(const RowSrc& src, const QRows& r, int64_t q
 }
 
 // The same with the slots' entries read from the top-k output in memory.
-template <int SRC, int NT, int TR, int NCH>
-__device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, int* tab, int* cnt,
-                               int* n_comp = nullptr) {
+template <int SRC, int NT, int TR, int NCH, class PreFn>
+__device__ int build_row_table(const RowSrc& src, const QRows& r, int64_t qi, int* tab, int* cnt, int* n_comp,
+                               PreFn pre) {
   return build_row_table_from<SRC, NT, TR, NCH>(src, r, qi, tab, cnt, n_comp,
-                                           [&](int j) { return src.idx[qi * src.top_k + j]; });
+                                           [&](int j) { return src.idx[qi * src.top_k + j]; }, pre);
 }
 
 // Address of compacted row c of an HCA split / of a sparse table entry (rows

@@ -47,12 +47,20 @@ __device__ __forceinline__ void zero_counters(uint32_t* zero, int64_t n) {
 // XOR swizzle of the 16-byte chunk index of key row r in an LDS tile. The
 // operand reads take one chunk of each of 16 consecutive rows; with 64 banks
 // of 4 bytes those 16 chunks must fall in 16 different 16-byte bank groups.
-// bf16 rows are 256 bytes (every row starts in group 0): chunk ^ (r & 15).
 // fp8 rows are 128 bytes (odd rows start in group 8): chunk ^ ((r >> 1) & 7).
 // MXFP4 rows are 64 bytes (four rows per 256 bytes): chunk ^ ((r >> 2) & 3).
+// bf16 rows (256 bytes, every row starts in group 0) serve the prefill
+// kernel's 32x32 operand reads: a 16-byte access is served in passes of the
+// 16 lanes that agree in lane bits 2 and 4, which there are eight rows (low
+// bits 0, 1, 3 varying) times two chunk halves, and in the tile stores two
+// rows (bit 1 varying) times eight chunks (bit 2 fixed). Row bits (2, 0, 1, 3)
+// as the chunk's bits (0, 1, 2, 3) keep the 16 lanes of a pass in 16 groups
+// in both.
 template <int KDT>
 __device__ __forceinline__ int kswz(int r) {
-  return KDT == DT_FP8 ? ((r >> 1) & 7) : KDT == DT_MXFP4 ? ((r >> 2) & 3) : (r & 15);
+  return KDT == DT_FP8 ? ((r >> 1) & 7)
+         : KDT == DT_MXFP4 ? ((r >> 2) & 3)
+                           : (((r >> 2) & 1) | ((r & 1) << 1) | ((r & 2) << 1) | (r & 8));
 }
 
 // 8 OCP MXFP4 codes (one dword, element 2j in the low nibble of byte j) ->
@@ -491,16 +499,30 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   if (hint)
     for (int i = l; i < DIG_BINS / 2; i += 64) lds_h[wv][i] = 0u;
 
-  // this lane's head weights, read once (heads 16 mt + 4 G + r)
-  f32x4_t wq[4];
+  // bf16 keys run v_mfma_f32_32x32x16_bf16: heads are two 32-row M blocks,
+  // entries two 32-column N blocks, dims eight k-steps of 16. Lane (h, l32)
+  // with h = l / 32 holds A = head 32 mb + l32, dims 16 ks + 8 h .. +7, and
+  // B = entry 32 nb + l32, the same dims; its output holds entry 32 nb + l32
+  // for heads 32 mb + 8 (r / 4) + 4 h + r % 4 (r < 16).
+  constexpr bool M32 = KDT == DT_BF16;
+  const int h2 = l >> 5, l32 = l & 31;
+  // this lane's head weights, read once (16x16 form: heads 16 mt + 4 G + r;
+  // 32x32 form: heads 32 mb + 8 q + 4 h + r, quartet 4 mb + q)
+  f32x4_t wq[M32 ? 8 : 4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) wq[mt] = *reinterpret_cast<const f32x4_t*>(&lds_w[wv][mt * 16 + G * 4]);
+  for (int i = 0; i < (M32 ? 8 : 4); ++i)
+    wq[i] = *reinterpret_cast<const f32x4_t*>(&lds_w[wv][M32 ? (i >> 2) * 32 + (i & 3) * 8 + 4 * h2 : i * 16 + G * 4]);
+  // query operand, 16 registers of 16 bytes in either form (16x16: [mt][s],
+  // head 16 mt + l16, dims 32 G + 8 s; 32x32: [2 mb + ks / 4][ks % 4], head
+  // 32 mb + l32, dims 16 ks + 8 h)
   bf16x8_t qa[4][KS];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const uint16_t* qp = q_idx + (row * H + mt * 16 + l16) * DI + G * 32;
+    const uint16_t* qp = M32 ? q_idx + (row * H + (mt >> 1) * 32 + l32) * DI + (mt & 1) * 64 + h2 * 8
+                             : q_idx + (row * H + mt * 16 + l16) * DI + G * 32;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qa[mt][s] = as_bf16x8(qok ? ld16(qp + s * 8) : u32x4_t{0, 0, 0, 0});
+    for (int s = 0; s < KS; ++s)
+      qa[mt][s] = as_bf16x8(qok ? ld16(qp + (M32 ? s * 16 : s * 8)) : u32x4_t{0, 0, 0, 0});
   }
   const uint8_t* kb = k_idx + b * N_max * KROW;
   float* srow = scores + row * N_max;
@@ -535,12 +557,85 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  // 32x32 form: accumulators [mb][nb]; N block 1 carries into the next tile
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mb][1][r] = 0.0f;
   auto body = [&](int64_t tile, auto BUF) {
     constexpr int buf = decltype(BUF)::value;
     stash(BUF);
     if (tile + 2 < ntiles) load(BUF, tile + 2);
     __syncthreads();
-    if (qok && tile * TE < Vq) {
+    if constexpr (M32) {
+      // Half-tile software pipeline: the products of entries 0-31 (N block 0)
+      // run beside the head sums of the previous tile's entries 32-63, the
+      // products of entries 32-63 beside the head sums of entries 0-31. All
+      // waves compute every tile (a row that does not see an entry stores
+      // nothing for it), so the products and the sums form one straight-line
+      // region the scheduler can interleave.
+      // qa[2 mb + ks / 4][ks % 4] holds dims 16 ks + 8 h .. +7 of head 32 mb + l32
+      auto kread = [&](int nb, int ks) {
+        const int el = nb * 32 + l32;
+        return as_bf16x8(
+            *reinterpret_cast<const u32x4_t*>(&lds_k[buf][el * KROW + (((2 * ks + h2) ^ kswz<KDT>(el)) * 16)]));
+      };
+      // head sum of N block nb, eight of its 32 (head, value) pairs per step
+      auto hsum_part = [&](int nb, int q, float& part) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int mb = q >> 2, r = (q & 3) * 4 + i;
+          part += wq[4 * mb + (r >> 2)][r & 3] * relu_bits(acc[mb][nb][r]);
+        }
+      };
+      float pprev = 0.0f, pcur = 0.0f;
+      bf16x8_t kb = kread(0, 0);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][0][r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8_t kn = kread(ks < 7 ? 0 : 1, ks < 7 ? ks + 1 : 0);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc[mb][0] = mfma32(qa[2 * mb + (ks >> 2)][ks & 3], kb, acc[mb][0]);
+        hsum_part(1, ks, pprev);  // the previous tile's N block 1
+        kb = kn;
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][1][r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        bf16x8_t kn = kb;
+        if (ks < 7) kn = kread(1, ks + 1);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc[mb][1] = mfma32(qa[2 * mb + (ks >> 2)][ks & 3], kb, acc[mb][1]);
+        hsum_part(0, ks, pcur);  // this tile's N block 0
+        kb = kn;
+      }
+      // the other 32 heads of an entry sit in lane l ^ 32: both halves get the
+      // same sum (float addition commutes)
+      {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(pprev), __float_as_uint(pprev), false, false);
+        pprev = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(pcur), __float_as_uint(pcur), false, false);
+        pcur = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+      }
+      // lanes 0-31 store this tile's entries 0-31, lanes 32-63 the previous
+      // tile's entries 32-63: one store and one count instruction
+      const float v = h2 == 0 ? pcur : pprev;
+      const int64_t e = h2 == 0 ? tile * TE + l32 : (tile - 1) * TE + 32 + l32;
+      if (qok && e >= 0 && e < Vq && (h2 == 0 || tile > 0)) {
+        srow[e] = v;
+        if (hint) {
+          const uint32_t d = f32_key(v) >> DIG_SHIFT;
+          atomicAdd(&lds_h[wv][d >> 1], 1u << ((d & 1u) << 4));
+        }
+      }
+    } else if (qok && tile * TE < Vq) {
       float part[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -612,6 +707,24 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   for (int64_t it = 0; it < ntiles; it += 2) {
     body(it, I0{});
     if (it + 1 < ntiles) body(it + 1, I1{});
+  }
+  if constexpr (M32) {
+    // the last tile's entries 32-63
+    float pl = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pl += wq[4 * mb + (r >> 2)][r & 3] * relu_bits(acc[mb][1][r]);
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(pl), __float_as_uint(pl), false, false);
+    pl = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const int64_t e = (ntiles - 1) * TE + 32 + l32;
+    if (qok && h2 == 1 && e < Vq) {
+      srow[e] = pl;
+      if (hint) {
+        const uint32_t d = f32_key(pl) >> DIG_SHIFT;
+        atomicAdd(&lds_h[wv][d >> 1], 1u << ((d & 1u) << 4));
+      }
+    }
   }
   if (hint && qok) {  // the row's whole histogram, unpacked (the wave's own LDS: no barrier needed)
     uint32_t* g = hint + row * DIG_BINS;

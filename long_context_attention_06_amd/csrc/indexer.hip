@@ -462,7 +462,8 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   constexpr int NT = 64 * QB;
   constexpr int LPT = (TB + NT * 16 - 1) / (NT * 16);  // 16-byte loads per thread per tile
   static_assert(TB % (NT * 16) == 0 || TB < NT * 16, "tile load mapping");
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][TB];
+  // bf16 keys: a DMA ring of four tiles; E4M3 / MXFP4: two register-staged tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[KDT == DT_BF16 ? 4 : 2][TB];
   __shared__ __attribute__((aligned(16))) uint32_t lds_ks[2][MX ? TE : 1];  // MXFP4: four E8M0 bytes per entry
   __shared__ __attribute__((aligned(16))) float lds_w[QB][H];
   // each wave's row: digit histogram, two 16-bit counts per word (the wave
@@ -563,12 +564,8 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mb][1][r] = 0.0f;
-  auto body = [&](int64_t tile, auto BUF) {
-    constexpr int buf = decltype(BUF)::value;
-    stash(BUF);
-    if (tile + 2 < ntiles) load(BUF, tile + 2);
-    __syncthreads();
-    if constexpr (M32) {
+  auto compute32 = [&](int64_t tile, const uint8_t* kt) {
+    {
       // Half-tile software pipeline: the products of entries 0-31 (N block 0)
       // run beside the head sums of the previous tile's entries 32-63, the
       // products of entries 32-63 beside the head sums of entries 0-31. All
@@ -579,7 +576,7 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
       auto kread = [&](int nb, int ks) {
         const int el = nb * 32 + l32;
         return as_bf16x8(
-            *reinterpret_cast<const u32x4_t*>(&lds_k[buf][el * KROW + (((2 * ks + h2) ^ kswz<KDT>(el)) * 16)]));
+            *reinterpret_cast<const u32x4_t*>(&kt[el * KROW + (((2 * ks + h2) ^ kswz<KDT>(el)) * 16)]));
       };
       // head sum of N block nb, eight of its 32 (head, value) pairs per step
       auto hsum_part = [&](int nb, int q, float& part) {
@@ -635,6 +632,15 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
           atomicAdd(&lds_h[wv][d >> 1], 1u << ((d & 1u) << 4));
         }
       }
+    }
+  };
+  auto body = [&](int64_t tile, auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
+    stash(BUF);
+    if (tile + 2 < ntiles) load(BUF, tile + 2);
+    __syncthreads();
+    if constexpr (M32) {
+      compute32(tile, lds_k[buf]);
     } else if (qok && tile * TE < Vq) {
       float part[4];
 #pragma unroll
@@ -702,11 +708,43 @@ idx_prefill_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__
       }
     }
   };
-  load(I0{}, 0);
-  if (ntiles > 1) load(I1{}, 1);
-  for (int64_t it = 0; it < ntiles; it += 2) {
-    body(it, I0{});
-    if (it + 1 < ntiles) body(it + 1, I1{});
+  if constexpr (M32) {
+    // bf16 keys: tiles reach LDS by DMA (global_load_lds, one 1 KB piece =
+    // four rows per instruction, two per wave and tile; lane i takes row
+    // 4 j + i / 16 and fetches the chunk that lands in slot i % 16, i.e. chunk
+    // (i % 16) ^ kswz(row)), four buffers, two tiles per barrier: at a barrier
+    // every wave's loads of the next two tiles have landed and every wave is
+    // done with the two tiles before, whose buffers then take the two after.
+    // Entries past the workgroup's largest visible count load entry Vmax - 1.
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    auto issue_tile = [&](int64_t tile) {
+      const uint32_t dst = (uint32_t)(uintptr_t)&lds_k[tile & 3][0];
+      const uint8_t* base = kb + tile * TE * KROW;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = 2 * wvu + u;
+        const int r = 4 * j + (l >> 4);
+        const int64_t e = min(tile * TE + r, Vmax - 1);
+        const uint32_t voff = (uint32_t)((e - tile * TE) * KROW + (((l & 15) ^ kswz<KDT>(r)) * 16));
+        dma_row(uniform_ptr(base), voff, __builtin_amdgcn_readfirstlane(dst + (uint32_t)(j * 1024)));
+      }
+    };
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    for (int64_t t0 = 0; t0 < ntiles; t0 += 2) {
+      vm_barrier<0>();
+      if (t0 + 2 < ntiles) issue_tile(t0 + 2);
+      if (t0 + 3 < ntiles) issue_tile(t0 + 3);
+      compute32(t0, lds_k[t0 & 3]);
+      if (t0 + 1 < ntiles) compute32(t0 + 1, lds_k[(t0 + 1) & 3]);
+    }
+  } else {
+    load(I0{}, 0);
+    if (ntiles > 1) load(I1{}, 1);
+    for (int64_t it = 0; it < ntiles; it += 2) {
+      body(it, I0{});
+      if (it + 1 < ntiles) body(it + 1, I1{});
+    }
   }
   if constexpr (M32) {
     // the last tile's entries 32-63

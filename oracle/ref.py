@@ -130,6 +130,37 @@ def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return (blk * sc[..., None]).reshape(v.shape)
 
 
+def mxfp4_quantize(x) -> Tuple[np.ndarray, np.ndarray]:
+    """Values -> OCP MXFP4 (Microscaling Formats v1.0, conversion of a block of
+    32 wider values), along the last axis. The block's shared exponent is
+    floor(log2 max|x|) minus 2, the largest exponent of an E2M1 element, kept
+    as an E8M0 byte in 1..254 (127 for an all-zero block). Each value over
+    the block scale is rounded to the nearest E2M1 value, ties to the even
+    code: the grid spacing is 0.5 below 2, 1 from 2 to 4 and 2 above, so this
+    is round-half-even of x / spacing; magnitudes beyond 6 saturate at 6, and
+    a value that rounds to zero keeps no sign. Elements are packed two per
+    byte, element 2j in the low nibble of byte j. Serves the query of the
+    indexer's FP4 QK path ([CSDN] CSA step 2; reading R20).
+    x [..., D] (D a multiple of 32) -> (codes uint8 [..., D/2], scales uint8
+    [..., D/32])."""
+    x = np.asarray(x, F64)
+    D = x.shape[-1]
+    assert D % 32 == 0
+    xb = x.reshape(x.shape[:-1] + (D // 32, 32))
+    amax = np.abs(xb).max(axis=-1)
+    _, ex = np.frexp(amax)  # amax = f 2^ex with f in [0.5, 1): floor(log2 amax) = ex - 1
+    E = np.where(amax > 0, np.clip(ex - 1 - 2 + 127, 1, 254), 127).astype(np.int64)
+    y = xb * np.exp2(127.0 - E)[..., None]
+    a = np.abs(y)
+    step = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    mag = np.minimum(np.rint(a / step) * step, 6.0)
+    code = np.where(mag < 2.0, 2.0 * mag, np.where(mag < 4.0, mag + 2.0, 0.5 * mag + 4.0)).astype(np.int64)
+    code = code | (((y < 0) & (code > 0)).astype(np.int64) << 3)
+    code = code.reshape(x.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, E.astype(np.uint8)
+
+
 # ----------------------------------------------------------------------------
 # A1: CSA / HCA KV compression  ([CSDN] CSA step 1, the CComp_i equation;
 # [LQNN] section 5 for the dropped tail; [WIKI] item 1 for the rates).
@@ -188,12 +219,17 @@ def visible(p: int, n_comp: int, m: int) -> int:
     return max(0, min(int(n_comp), (int(p) + 1) // m))
 
 
-def indexer_scores(q_idx, w, k_idx, V: int, k_scale=None) -> np.ndarray:
+def indexer_scores(q_idx, w, k_idx, V: int, k_scale=None, q_fp4: bool = False) -> np.ndarray:
     """s_i = sum_h w_h * max(0, sigma_i * <q_h, k_i>) for i < V.
 
     q_idx [H_I, D_I], w [H_I], k_idx [>=V, D_I] (values), k_scale [>=V] or None.
+    q_fp4: the FP4 QK path with both operands in FP4 (reading R20): every head
+    row of the query is first quantised to MXFP4 (mxfp4_quantize) and the
+    product takes its decoded values.
     """
     q = np.asarray(q_idx, F64)
+    if q_fp4:
+        q = mxfp4_decode(*mxfp4_quantize(q))
     k = np.asarray(k_idx, F64)[:V]
     dots = k @ q.T  # [V, H_I]
     if k_scale is not None:
@@ -263,10 +299,10 @@ def sparse_rows(kv_comp, idx) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def csa_query(q, q_idx, w, kv_comp, k_idx, p: int, n_comp: int, m: int, top_k: int,
-              win, sink, k_scale=None, tau: float = 1.0):
+              win, sink, k_scale=None, tau: float = 1.0, q_fp4: bool = False):
     """One CSA query at position p: returns (idx, o, lse, scores)."""
     V = visible(p, n_comp, m)
-    s = indexer_scores(q_idx, w, k_idx, V, k_scale)
+    s = indexer_scores(q_idx, w, k_idx, V, k_scale, q_fp4=q_fp4)
     idx = topk_select(s, top_k)
     rows = np.concatenate([sparse_rows(kv_comp, idx), np.asarray(win, F64)], axis=0)
     o, lse = attend(q, rows, sink, tau)

@@ -412,4 +412,98 @@ def check_brute_force_tiny(o):
     assert np.allclose(out, np.array(outs), atol=1e-12)
 
 
+# ------------------------------------------------------ MXFP4 query quantiser
+
+_E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _e2m1_values(codes):
+    codes = np.asarray(codes, np.int64)
+    return np.where(codes & 8, -1.0, 1.0) * _E2M1[codes & 7]
+
+
+def check_mxfp4_quantize_ties_and_saturation(o):
+    """One block whose maximum is 6 (so the scale byte is 127 and the element
+    values are the inputs themselves): the OCP rule rounds each tie to the
+    even code and saturates beyond 6; the table is the E2M1 grid worked by
+    hand."""
+    x = np.zeros(32)
+    x[:14] = [6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, 0.3, -0.1, 2.9, -1.74, 4.9]
+    want = [6.0, 0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, -4.0, 0.5, 0.0, 3.0, -1.5, 4.0]
+    q, sc = o.mxfp4_quantize(x[None])
+    assert sc.tolist() == [[127]]
+    d = o.mxfp4_decode(q, sc)[0]
+    assert d[:14].tolist() == want and np.all(d[14:] == 0)
+    assert not np.signbit(d[10])  # -0.1 rounds to zero and keeps no sign
+    # a block maximum of 7 still has floor(log2) = 2: scale byte 127, 7 saturates to 6
+    x2 = np.zeros(32)
+    x2[0], x2[1] = 7.0, -0.75
+    q, sc = o.mxfp4_quantize(x2[None])
+    assert sc.tolist() == [[127]] and o.mxfp4_decode(q, sc)[0][:2].tolist() == [6.0, -1.0]
+
+
+def check_mxfp4_quantize_round_trip(o):
+    """Blocks whose values are E2M1 values times 2^s with the block maximum 6
+    or 4 are representable: quantising them gives back the same codes and
+    the scale byte 127 + s."""
+    g = _rng(41)
+    for s_, top in ((-9, 7), (0, 6), (3, 7), (12, 6)):
+        codes = g.integers(0, 16, (6, 128)).astype(np.int64)
+        codes[codes == 8] = 0                      # -0 quantises to +0
+        codes = np.where((codes & 7) > (top & 7), codes & 8 | (top & 7), codes)
+        codes[:, 5::32] = top                      # each block holds its maximum
+        x = _e2m1_values(codes) * 2.0 ** s_
+        q, sc = o.mxfp4_quantize(x)
+        assert np.all(sc == 127 + s_), (s_, top)  # max 6 or 4: floor(log2) = 2 + s
+        packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+        assert np.array_equal(q, packed), (s_, top)
+
+
+def check_mxfp4_quantize_nearest(o):
+    """Random blocks at several magnitudes: the block maximum lands in
+    [4, 8) of the scale, and every element is a nearest point of the E2M1
+    grid to x / scale (brute force over the 15 grid values), or 6 where it
+    saturates."""
+    g = _rng(42)
+    grid = np.concatenate([-_E2M1[1:][::-1], _E2M1])
+    for mag in (1e-3, 1.0, 37.0, 1e6):
+        x = g.standard_normal((16, 64)) * mag
+        q, sc = o.mxfp4_quantize(x)
+        d = o.mxfp4_decode(q, sc)
+        scale = np.repeat(np.exp2(sc.astype(np.float64) - 127.0), 32, axis=-1)
+        y, v = x / scale, d / scale
+        amax = np.abs(y).reshape(16, 2, 32).max(axis=-1)
+        assert np.all((amax >= 4.0) & (amax < 8.0))
+        best = np.abs(y[..., None] - grid).min(axis=-1)
+        inside = np.abs(y) <= 6.0
+        assert np.all(np.abs(y - v)[inside] <= best[inside] + 1e-12)
+        assert np.all(np.abs(v[~inside]) == 6.0) and np.all(np.sign(v[~inside]) == np.sign(y[~inside]))
+
+
+def check_indexer_fp4_query(o):
+    """The FP4 QK path: a query whose head rows are already MXFP4 values
+    scores exactly as the plain path; a general query scores as the plain
+    path on its quantised values, which differ from it."""
+    g = _rng(43)
+    H, D, V = 4, 64, 40
+    codes = g.integers(0, 16, (H, D)).astype(np.int64)
+    codes[codes == 8] = 0
+    codes[:, ::32] = 7
+    q_rep = _e2m1_values(codes) * 2.0 ** -3
+    k = g.standard_normal((V, D))
+    w = g.uniform(0, 1, H)
+    a = o.indexer_scores(q_rep, w, k, V, q_fp4=True)
+    b = o.indexer_scores(q_rep, w, k, V)
+    assert np.array_equal(a, b)
+    q = g.standard_normal((H, D))
+    f = o.indexer_scores(q, w, k, V, q_fp4=True)
+    assert not np.allclose(f, o.indexer_scores(q, w, k, V), rtol=1e-3, atol=0)
+    # each quantised element errs by less than 2 (saturation; half a grid step
+    # below 6) block scales, a scale at most amax / 4, so by amax / 2 of its
+    # head row; ReLU is 1-Lipschitz, which bounds the score change
+    err = np.abs(f - o.indexer_scores(q, w, k, V))
+    bound = np.abs(k).sum(axis=1) * np.sum(w * 0.5 * np.abs(q).max(axis=1))
+    assert np.all(err <= bound + 1e-12)
+
+
 ALL_CHECKS = [v for k_, v in sorted(globals().items()) if k_.startswith("check_")]

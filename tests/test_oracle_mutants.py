@@ -81,6 +81,32 @@ def _visible_floor_p(p, n_comp, m):
     return max(0, min(int(n_comp), int(p) // m))
 
 
+def _quantize_variant(kind):
+    def f(x):
+        x = np.asarray(x, float)
+        D = x.shape[-1]
+        xb = x.reshape(x.shape[:-1] + (D // 32, 32))
+        amax = np.abs(xb).max(axis=-1)
+        _, ex = np.frexp(amax)
+        off = 1 if kind == "emax_1" else 2
+        E = np.where(amax > 0, np.clip(ex - 1 - off + 127, 1, 254), 127).astype(np.int64)
+        y = xb * np.exp2(127.0 - E)[..., None]
+        a = np.abs(y)
+        step = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+        r = np.floor(a / step + 0.5) if kind == "ties_away" else np.rint(a / step)
+        mag = np.minimum(r * step, 6.0)
+        code = np.where(mag < 2.0, 2.0 * mag, np.where(mag < 4.0, mag + 2.0, 0.5 * mag + 4.0)).astype(np.int64)
+        code = code | (((y < 0) & (code > 0)).astype(np.int64) << 3)
+        code = code.reshape(x.shape)
+        lo, hi = (code[..., 1::2], code[..., 0::2]) if kind == "nibbles_swapped" else (code[..., 0::2], code[..., 1::2])
+        return (lo | (hi << 4)).astype(np.uint8), E.astype(np.uint8)
+    return f
+
+
+def _scores_fp4_query_ignored(q_idx, w, k_idx, V, k_scale=None, q_fp4=False):
+    return ref.indexer_scores(q_idx, w, k_idx, V, k_scale)
+
+
 MUTANTS = {
     "compress_b_reads_next_block": dict(compress=_compress_variant("b_reads_next_block")),
     "compress_softmax_over_channels": dict(compress=_compress_variant("softmax_over_channels")),
@@ -94,6 +120,10 @@ MUTANTS = {
     "attend_wrong_logit_scale": dict(attend=_attend_tau_squared),
     "window_excludes_current_token": dict(window_rows=_window_excl_current),
     "visibility_off_by_one": dict(visible=_visible_floor_p),
+    "mxfp4_quantize_ties_away": dict(mxfp4_quantize=_quantize_variant("ties_away")),
+    "mxfp4_quantize_emax_1": dict(mxfp4_quantize=_quantize_variant("emax_1")),
+    "mxfp4_quantize_nibbles_swapped": dict(mxfp4_quantize=_quantize_variant("nibbles_swapped")),
+    "indexer_ignores_fp4_query": dict(indexer_scores=_scores_fp4_query_ignored),
 }
 
 

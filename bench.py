@@ -18,10 +18,11 @@ Other workloads: c5 (1M context, E4M3 indexer keys), c2x (c2 with MXFP4
 indexer keys), c4 (HCA decode 1M), c3 (CSA prefill 64K), c6 (HCA prefill 64K),
 c4f / c2f / c3f (c4 / c2 / c3 with the main KV rows in E4M3 + bf16 RoPE dims),
 c2r (c2 with the query RMSNorm + RoPE prologue and the output inverse RoPE),
-c2m (c2 with two query tokens per sequence and step).
+c2m (c2 with two query tokens per sequence and step), c2q (c2x with the
+indexer query quantised to MXFP4 in the call: FP4 x FP4 on the scaled MFMA).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
-                       [--workload c2|c5|c4|c3|c2x|c6|c4f|c2f|c3f|c2r|c2m]
+                       [--workload c2|c5|c4|c3|c2x|c6|c4f|c2f|c3f|c2r|c2m|c2q]
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -50,7 +51,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2",
-                    choices=["c2", "c5", "c4", "c3", "c2x", "c6", "c4f", "c2f", "c3f", "c2r", "c2m"])
+                    choices=["c2", "c5", "c4", "c3", "c2x", "c6", "c4f", "c2f", "c3f", "c2r", "c2m", "c2q"])
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--extra-cpu-seconds", type=float, default=4.0,
@@ -200,7 +201,7 @@ def run_workload(w, a, torch, L, gen, dev, steps, warmup, cpu_s, copy_gbs):
     if w == "c6":
         return bench_hca_prefill(a, torch, L, gen, dev, steps, warmup, cpu_s)
     cfg = {"c2": gen.C2, "c5": gen.C5, "c4": gen.C4, "c2x": gen.C2X, "c4f": gen.C4F, "c2f": gen.C2F,
-           "c2r": gen.C2R, "c2m": gen.C2M}[w]
+           "c2r": gen.C2R, "c2m": gen.C2M, "c2q": gen.C2Q}[w]
     return bench_decode(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, copy_gbs, w)
 
 
@@ -283,7 +284,7 @@ def bench_decode(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, copy_gbs, wna
                               r["q"] if Tq > 1 else r["q"].view(B, 1, H, D), r["kv_comp"], r["kv_win"],
                               shared["win_len"], shared["sink"], idx, out if Tq > 1 else out.view(B, 1, H, D),
                               m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, scale=att_scale,
-                              ws=ws_t, stream=s)
+                              ws=ws_t, q_fp4=cfg.q_fp4, stream=s)
         else:
             # HCA: the token completes block N-1 (m' divides n): its single-
             # branch entry, the dense attention and the split merge in one call
@@ -344,9 +345,12 @@ def bench_decode(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, copy_gbs, wna
         res["config"] = {"workload": cfg.name, "batch": B, "context_tokens": cfg.n, "compressed_entries": N,
                          "m": m, "top_k": k, "indexer_heads": cfg.H_I, "indexer_dim": cfg.D_I,
                          "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype,
-                         "kv_dtype": cfg.kv_dtype, "qk_norm_rope": cfg.qk_rope, "query_tokens_per_sequence": Tq}
+                         "kv_dtype": cfg.kv_dtype, "qk_norm_rope": cfg.qk_rope, "query_tokens_per_sequence": Tq,
+                         "indexer_query": "mxfp4 (quantised in the call)" if cfg.q_fp4 else "bf16"}
         kname = {"fp8": "idx_scan_lp_kernel<2, 1> (E4M3 keys, with the entry's compression)",
-                 "mxfp4": "idx_scan_lp_kernel<3, 1> (MXFP4 keys, with the entry's compression)"}.get(
+                 "mxfp4": "idx_scan_fp4_kernel<1> (MXFP4 keys and the FP4-quantised query on the scaled FP4 "
+                          "MFMA, with the entry's compression)" if cfg.q_fp4 else
+                          "idx_scan_lp_kernel<3, 1> (MXFP4 keys, with the entry's compression)"}.get(
             cfg.k_dtype, "idx_scan_bf16_kernel<2, 1> (two query rows per workgroup, with the entry's compression)"
             if Tq % 2 == 0 else "idx_scan_bf16_kernel<1, 1> (with the entry's compression)")
         # (3) the step's first launch (compression + scan, the same kernel
@@ -360,7 +364,7 @@ def bench_decode(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, copy_gbs, wna
             L.csa_compress_indexer_score(r["Ca"], r["Cb"], r["Za"], r["Zb"], shared["Ba"], shared["Bb"],
                                          r["kv_comp"], r["q_idx"], r["w"], r["k_idx"], r.get("k_scale"),
                                          shared["q_pos"], shared["n_comp"], scores, m_c=m, m=m,
-                                         tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
+                                         tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N, q_fp4=cfg.q_fp4)
 
         scan_ms = _graph_loop_ms(torch, scan, steps)
         res["roofline"] = _roofline("hbm", kname, scan_bytes, scan_ms, HBM_PEAK_GBS, "GB/s",
@@ -689,7 +693,8 @@ def cpu_baseline(cfg, x, budget_s: float):
                     tau = 1.0 / math.sqrt(cfg.D)
                 hi = len(win) - cfg.Tq + t
                 _, o, _, _ = oracle.csa_query(q, qi_, w_, comp, keys, p, cfg.N, m, cfg.top_k,
-                                              win[max(0, hi - cfg.W + 1):hi + 1], x["sink"], k_scale=sc, tau=tau)
+                                              win[max(0, hi - cfg.W + 1):hi + 1], x["sink"], k_scale=sc, tau=tau,
+                                              q_fp4=cfg.q_fp4)
                 if cfg.qk_rope:
                     oracle.rope_rotate(o[None], [p], inverse=True)
         else:

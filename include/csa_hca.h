@@ -41,8 +41,17 @@
  *     describe: RoPE dims in BF16, the rest in FP8 -- for a row of D dims,
  *     bytes 0 .. D-65 are the OCP E4M3 codes of dims 0 .. D-65 and the next
  *     128 bytes the last 64 dims as bf16, little endian: D + 64 bytes per row,
- *     no scale). Arithmetic is fp32 (bf16 x bf16 products accumulate in fp32;
- *     fp8 and FP4 values are widened to bf16 exactly first).
+ *     no scale), CSA_BF16_MXFP4 (indexer queries only: bf16 values that the
+ *     call quantises to MXFP4 -- per 32-dim block of each head row, the OCP
+ *     rule: E8M0 exponent floor(log2 amax) - 2 kept in 1..254, 127 for an
+ *     all-zero block, elements rounded to nearest even on the E2M1 grid and
+ *     saturated at 6 -- so that both operands of the indexer's QK product are
+ *     FP4, the lightning indexer's FP4 QK path of [CSDN] CSA step 2 and
+ *     其他辅助设计; with MXFP4 keys only).
+ *     Arithmetic is fp32 (bf16 x bf16 products accumulate in fp32; fp8 and FP4
+ *     keys against a bf16 query are widened to bf16 exactly first; FP4 x FP4
+ *     products with their block scales run on the scaled FP4 MFMA, exact
+ *     before the fp32 sum).
  *   - Return codes: CSA_OK, CSA_INVALID_ARG (a null pointer that must not be
  *     null, a negative or inconsistent size), CSA_UNSUPPORTED (a valid
  *     combination with no kernel instantiation), CSA_WORKSPACE_TOO_SMALL,
@@ -72,7 +81,7 @@ extern "C" {
 
 #define CSA_HCA_VERSION 1
 
-enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3, CSA_KV_FP8 = 4 };
+enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3, CSA_KV_FP8 = 4, CSA_BF16_MXFP4 = 5 };
 
 enum {
   CSA_OK = 0,
@@ -140,7 +149,9 @@ int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb,
  *   q_pos   : [B, Tq] int32                      n_comp : [B] int32
  *   scores  : [B, Tq, N_max] fp32; entries i >= V are left unspecified.
  * Supported: (H_I, D_I) in {(64, 128) with q_dt BF16 and k_dt BF16, FP8_E4M3
- * or MXFP4, (4, 32) with q_dt = k_dt = F32}. N_max <= 2^24.
+ * or MXFP4, (64, 128) with q_dt BF16_MXFP4 and k_dt MXFP4 (the query's
+ * quantised values take q_idx's place in the sum above), (4, 32) with
+ * q_dt = k_dt = F32}. N_max <= 2^24.
  */
 int indexer_score(const void* q_idx, const float* w, const void* k_idx, const void* k_scale,
                   const int32_t* q_pos, const int32_t* n_comp,

@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa_hca.so")
 
-F32, BF16, FP8_E4M3, MXFP4, KV_FP8 = 0, 1, 2, 3, 4
+F32, BF16, FP8_E4M3, MXFP4, KV_FP8, BF16_MXFP4 = 0, 1, 2, 3, 4, 5
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = 0, -1, -2, -3, -4
 OVERLAP, JOINT_SOFTMAX = 1, 2
 RMSNORM, ROPE, ROPE_INVERSE = 1, 2, 4
@@ -117,6 +117,16 @@ def _dt(t) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def _qdt(q_idx, q_fp4: bool) -> int:
+    """Indexer query dtype: with q_fp4 a bf16 query that the call quantises
+    to MXFP4 for the FP4 x FP4 QK product (MXFP4 keys only)."""
+    if q_fp4:
+        if q_idx.dtype != torch.bfloat16:
+            raise ValueError("q_fp4 takes a bf16 query")
+        return BF16_MXFP4
+    return _dt(q_idx)
+
+
 def _kv_dt(q, kv) -> int:
     """Row dtype of a KV cache: uint8 rows D + 64 bytes wide are the
     mixed-precision layout (D - 64 E4M3 bytes, then 64 bf16 RoPE dims) read
@@ -174,19 +184,20 @@ def csa_compress(Ca, Cb, Za, Zb, Ba, Bb, out, *, m: int, tok_begin: int = 0, blk
 
 # -------------------------------------------------------------------- indexer
 
-def indexer_score(q_idx, w, k_idx, k_scale, q_pos, n_comp, scores, *, m: int, stream=None) -> None:
+def indexer_score(q_idx, w, k_idx, k_scale, q_pos, n_comp, scores, *, m: int, q_fp4: bool = False,
+                  stream=None) -> None:
     """q_idx [B, Tq, H_I, D_I]; w [B, Tq, H_I]; k_idx [B, N_max, D_I] (MXFP4: [B, N_max, D_I/2] of
     float4_e2m1fn_x2); k_scale: fp8 keys [B, N_max] fp32, MXFP4 keys [B, N_max, D_I/32] E8M0 bytes,
     else None; q_pos [B, Tq] int32; n_comp [B] int32; scores [B, Tq, N_max] fp32."""
     B, Tq, H_I, D_I = q_idx.shape
     N_max = k_idx.shape[1]
     _check(lib.indexer_score(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q_pos), _ptr(n_comp), B, Tq,
-                             H_I, D_I, N_max, m, _dt(q_idx), _dt(k_idx), _ptr(scores), _stream(stream)))
+                             H_I, D_I, N_max, m, _qdt(q_idx, q_fp4), _dt(k_idx), _ptr(scores), _stream(stream)))
 
 
 def csa_compress_indexer_score(Ca, Cb, Za, Zb, Ba, Bb, kv_out, q_idx, w, k_idx, k_scale, q_pos, n_comp, scores, *,
                                m_c: int, m: int, tok_begin: int = 0, blk_begin: int = 0, blk_end: Optional[int] = None,
-                               overlap: bool = True, joint: bool = False, stream=None) -> None:
+                               overlap: bool = True, joint: bool = False, q_fp4: bool = False, stream=None) -> None:
     """csa_compress(Ca .. Bb -> kv_out) and indexer_score(q_idx .. -> scores) in one call."""
     Bc, n_rows, d = Ca.shape
     out_cap = kv_out.shape[1]
@@ -199,13 +210,14 @@ def csa_compress_indexer_score(Ca, Cb, Za, Zb, Ba, Bb, kv_out, q_idx, w, k_idx, 
     _check(lib.csa_compress_indexer_score(
         _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), _ptr(kv_out), Bc, n_rows, tok_begin, d, m_c,
         blk_begin, blk_end, out_cap, flags, _dt(Ca), out_dt, _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale),
-        _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I, N_max, m, _dt(q_idx), _dt(k_idx), _ptr(scores), _stream(stream)))
+        _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I, N_max, m, _qdt(q_idx, q_fp4), _dt(k_idx), _ptr(scores),
+        _stream(stream)))
 
 
 def csa_compress_indexer_score_topk(Ca, Cb, Za, Zb, Ba, Bb, kv_out, q_idx, w, k_idx, k_scale, q_pos, n_comp,
                                     topk_idx, topk_score=None, *, m_c: int, m: int, tok_begin: int = 0,
                                     blk_begin: int = 0, blk_end: Optional[int] = None, overlap: bool = True,
-                                    joint: bool = False, ws=None, stream=None) -> None:
+                                    joint: bool = False, ws=None, q_fp4: bool = False, stream=None) -> None:
     """csa_compress(Ca .. Bb -> kv_out) and indexer_score_topk(q_idx .. -> topk_idx) in one call, the
     scores living in the workspace (indexer_score_topk_workspace_bytes)."""
     Bc, n_rows, d = Ca.shape
@@ -221,7 +233,7 @@ def csa_compress_indexer_score_topk(Ca, Cb, Za, Zb, Ba, Bb, kv_out, q_idx, w, k_
     _check(lib.csa_compress_indexer_score_topk(
         _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), _ptr(kv_out), Bc, n_rows, tok_begin, d, m_c,
         blk_begin, blk_end, out_cap, flags, _dt(Ca), out_dt, _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale),
-        _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I, N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(topk_idx),
+        _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I, N_max, m, top_k, _qdt(q_idx, q_fp4), _dt(k_idx), _ptr(topk_idx),
         _ptr(topk_score), _ptr(ws), nb, _stream(stream)))
 
 
@@ -232,7 +244,7 @@ def csa_decode_step_workspace_bytes(B: int, Tq: int, N_max: int, top_k: int, H: 
 def csa_decode_step(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, n_comp, q, kv_comp, kv_win, win_len,
                     sink, topk_idx, out, lse=None, topk_score=None, *, m_c: int, m: int, tok_begin: int = 0,
                     blk_begin: int = 0, blk_end: Optional[int] = None, overlap: bool = True, joint: bool = False,
-                    scale: float = 1.0, ws=None, stream=None) -> None:
+                    scale: float = 1.0, ws=None, q_fp4: bool = False, stream=None) -> None:
     """One CSA decode step: compression of blocks [blk_begin, blk_end) into kv_comp, indexer scores,
     top-k (-> topk_idx [B, Tq, top_k]) and sparse MQA (q [B, Tq, H, D] or [B, H, D] -> out)."""
     _, n_rows, d = Ca.shape
@@ -248,7 +260,8 @@ def csa_decode_step(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, n_c
     _check(lib.csa_decode_step(
         _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), n_rows, tok_begin, d, m_c, blk_begin, blk_end,
         flags, _dt(Ca), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I,
-        N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len), _ptr(sink),
+        N_max, m, top_k, _qdt(q_idx, q_fp4), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len),
+        _ptr(sink),
         scale, H, D, W, _kv_dt(q, kv_comp), _dt(out), _ptr(topk_idx), _ptr(topk_score), _ptr(out), _ptr(lse),
         _ptr(ws), nb, _stream(stream)))
 
@@ -261,7 +274,8 @@ def csa_decode_step_qk(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, 
                        sink, topk_idx, out, lse=None, topk_score=None, *, m_c: int, m: int, q_gamma=None,
                        eps: float = 1e-6, rope_dims: int = 64, rope_theta: float = 10000.0, norm: bool = True,
                        rope: bool = True, tok_begin: int = 0, blk_begin: int = 0, blk_end: Optional[int] = None,
-                       overlap: bool = True, joint: bool = False, scale: float = 1.0, ws=None, stream=None) -> None:
+                       overlap: bool = True, joint: bool = False, scale: float = 1.0, ws=None, q_fp4: bool = False,
+                       stream=None) -> None:
     """csa_decode_step on raw queries: RMSNorm (q_gamma) + RoPE of the last rope_dims dims at q_pos
     before the attention, the inverse rotation of the output after it."""
     _, n_rows, d = Ca.shape
@@ -278,7 +292,8 @@ def csa_decode_step_qk(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, 
     _check(lib.csa_decode_step_qk(
         _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), n_rows, tok_begin, d, m_c, blk_begin, blk_end,
         flags, _dt(Ca), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I,
-        N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len), _ptr(sink),
+        N_max, m, top_k, _qdt(q_idx, q_fp4), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len),
+        _ptr(sink),
         scale, H, D, W, _kv_dt(q, kv_comp), _dt(out), _ptr(topk_idx), _ptr(topk_score), _ptr(out), _ptr(lse),
         _ptr(q_gamma), eps, rope_dims, rope_theta, qk_flags, _ptr(ws), nb, _stream(stream)))
 
@@ -303,7 +318,8 @@ STEP_SCRATCH_BYTES = 64 << 20  # CSA_STEP_SCRATCH_BYTES: the scratch csa_decode_
 def csa_decode_step_noalloc(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_pos, n_comp, q, kv_comp, kv_win,
                             win_len, sink, topk_idx, out, lse=None, topk_score=None, *, m_c: int, m: int,
                             tok_begin: int = 0, blk_begin: int = 0, blk_end: Optional[int] = None,
-                            overlap: bool = True, joint: bool = False, scale: float = 1.0, stream=None) -> None:
+                            overlap: bool = True, joint: bool = False, scale: float = 1.0, q_fp4: bool = False,
+                            stream=None) -> None:
     """csa_decode_step with the library's own per-device scratch: allocates nothing."""
     _, n_rows, d = Ca.shape
     if blk_end is None:
@@ -317,7 +333,8 @@ def csa_decode_step_noalloc(Ca, Cb, Za, Zb, Ba, Bb, q_idx, w, k_idx, k_scale, q_
     _check(lib.csa_decode_step_noalloc(
         _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(Ba), _ptr(Bb), n_rows, tok_begin, d, m_c, blk_begin, blk_end,
         flags, _dt(Ca), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q_pos), _ptr(n_comp), B, Tq, H_I, D_I,
-        N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len), _ptr(sink),
+        N_max, m, top_k, _qdt(q_idx, q_fp4), _dt(k_idx), _ptr(q), _ptr(kv_comp), _ptr(kv_win), _ptr(win_len),
+        _ptr(sink),
         scale, H, D, W, _kv_dt(q, kv_comp), _dt(out), _ptr(topk_idx), _ptr(topk_score), _ptr(out), _ptr(lse),
         _stream(stream)))
 
@@ -340,13 +357,13 @@ def indexer_score_topk_workspace_bytes(B: int, Tq: int, N_max: int, top_k: int) 
 
 
 def indexer_score_topk(q_idx, w, k_idx, k_scale, q_pos, n_comp, topk_idx, topk_score=None, *, m: int, ws=None,
-                       stream=None) -> None:
+                       q_fp4: bool = False, stream=None) -> None:
     B, Tq, H_I, D_I = q_idx.shape
     N_max = k_idx.shape[1]
     top_k = topk_idx.shape[-1]
     ws, nb = _ws(indexer_score_topk_workspace_bytes(B, Tq, N_max, top_k), ws, q_idx.device)
     _check(lib.indexer_score_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scale), _ptr(q_pos), _ptr(n_comp), B,
-                                  Tq, H_I, D_I, N_max, m, top_k, _dt(q_idx), _dt(k_idx), _ptr(topk_idx),
+                                  Tq, H_I, D_I, N_max, m, top_k, _qdt(q_idx, q_fp4), _dt(k_idx), _ptr(topk_idx),
                                   _ptr(topk_score), _ptr(ws), nb, _stream(stream)))
 
 

@@ -80,17 +80,19 @@ int check_indexer(const void* q_idx, const float* w, const void* k_idx, const vo
   REQ(B * Tq * N_max == 0 || k_idx, CSA_INVALID_ARG, "k_idx must not be NULL");
   REQ(H_I > 0 && D_I > 0, CSA_INVALID_ARG, "H_I and D_I must be positive");
   REQ(m >= 1, CSA_INVALID_ARG, "m must be >= 1");
-  REQ(q_dt >= CSA_F32 && q_dt <= CSA_FP8_E4M3 && k_dt >= CSA_F32 && k_dt <= CSA_MXFP4, CSA_INVALID_ARG,
-      "unknown dtype");
+  REQ(((q_dt >= CSA_F32 && q_dt <= CSA_FP8_E4M3) || q_dt == CSA_BF16_MXFP4) && k_dt >= CSA_F32 && k_dt <= CSA_MXFP4,
+      CSA_INVALID_ARG, "unknown dtype");
   REQ((k_dt != CSA_FP8_E4M3 && k_dt != CSA_MXFP4) || k_scale, CSA_INVALID_ARG, "fp8 and MXFP4 keys need k_scale");
   REQ(k_dt != CSA_MXFP4 || D_I % 32 == 0, CSA_INVALID_ARG, "MXFP4 keys need D_I a multiple of 32");
   REQ(N_max <= (int64_t(1) << 24), CSA_UNSUPPORTED, "N_max above 2^24");
   REQ(B * Tq <= 65535, CSA_UNSUPPORTED, "B*Tq above 65535 rows per call");
-  const bool big =
-      H_I == 64 && D_I == 128 && q_dt == CSA_BF16 && (k_dt == CSA_BF16 || k_dt == CSA_FP8_E4M3 || k_dt == CSA_MXFP4);
+  const bool big = H_I == 64 && D_I == 128 &&
+                   ((q_dt == CSA_BF16 && (k_dt == CSA_BF16 || k_dt == CSA_FP8_E4M3 || k_dt == CSA_MXFP4)) ||
+                    (q_dt == CSA_BF16_MXFP4 && k_dt == CSA_MXFP4));
   const bool tiny = H_I <= 32 && D_I == 32 && q_dt == CSA_F32 && k_dt == CSA_F32;
   REQ(big || tiny, CSA_UNSUPPORTED,
-      "unsupported indexer shape/dtype: (64, 128) bf16 q with bf16/fp8/MXFP4 keys, or (<=32, 32) fp32");
+      "unsupported indexer shape/dtype: (64, 128) bf16 q with bf16/fp8/MXFP4 keys, FP4-quantised q with MXFP4 "
+      "keys, or (<=32, 32) fp32");
   REQ(aligned16(q_idx) && aligned16(k_idx), CSA_INVALID_ARG, "q_idx and k_idx must be 16-byte aligned");
   REQ(!k_scale || ((uintptr_t)k_scale & 3) == 0, CSA_INVALID_ARG, "k_scale must be 4-byte aligned");
   return CSA_OK;

@@ -74,6 +74,57 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t codes, float scale)
                            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3))});
 }
 
+// One OCP MXFP4 block (Microscaling Formats v1.0: 32 values, one E8M0 scale)
+// from 32 bf16 values: x[j] holds values 8j .. 8j + 7, value 8j + 2c + h in
+// half h of dword c. The shared exponent is floor(log2 amax) - 2 (2 being the
+// largest E2M1 exponent), which for a bf16 amax is its exponent field minus
+// 2, kept in 1..254 (127 for an all-zero block). Each value times
+// 2^(127 - E) (exact: a power of two) is rounded half-to-even on the E2M1
+// grid -- spacing 0.5 below 2, 1 below 4, 2 above, so round-half-even of the
+// value over its spacing -- and saturated at 6 (code 7); a value that rounds
+// to zero keeps no sign. Codes are packed as MXFP4 stores them: value 8j + i
+// in bits 4i .. 4i + 3 of codes[j]. Returns the scale byte.
+__device__ __forceinline__ int mxfp4_quant_block(const u32x4_t (&x)[4], u32x4_t& codes) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) amax = max(amax, max(x[j][c] & 0x7fffu, (x[j][c] >> 16) & 0x7fffu));
+  const int E = amax == 0 ? 127 : min(max((int)(amax >> 7) - 2, 1), 254);
+  // 2^(127 - E) has the fp32 exponent field 254 - E, in 2..253 for every
+  // finite amax (a finite bf16's field is at most 254, so E <= 252)
+  const float inv = __uint_as_float((uint32_t)(254 - E) << 23);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t bits = h ? (x[j][c] & 0xffff0000u) : (x[j][c] << 16);
+        const float a = fabsf(__uint_as_float(bits)) * inv;
+        const float sp = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+        const int off = a < 2.0f ? 0 : (a < 4.0f ? 2 : 4);
+        const uint32_t n = (uint32_t)min((int)__builtin_rintf(a * sp) + off, 7);
+        d |= (n | ((bits >> 28) & (n ? 8u : 0u))) << (8 * c + 4 * h);
+      }
+    codes[j] = d;
+  }
+  return E;
+}
+
+// S[16 heads x 16 entries] of one 128-dim FP4 x FP4 product with E8M0 block
+// scales on gfx950's scaled MFMA (format 4 = E2M1 for both operands). Lane
+// (group G, column l16) gives, for row l16 of each operand, the 32 codes of
+// dims 32G .. 32G + 31 (four dwords, the MXFP4 packing) and that block's
+// scale byte; the result has the layout of v_mfma_f32_16x16x32_bf16.
+__device__ __forceinline__ f32x4_t mfma_fp4(const u32x4_t& a, int sa, const u32x4_t& b, int sb) {
+  typedef int v8i_t __attribute__((ext_vector_type(8)));
+  const v8i_t av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const v8i_t bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, sa, 0, sb);
+}
+
 // bf16 keys, 64 heads x 128 dims.  Grid: (workgroups per row, rows).
 // A workgroup walks tiles of TE = 64 entries of one query row with a stride
 // of gridDim.x tiles; wave w owns entries 16 w .. 16 w + 15 of each tile and
@@ -225,6 +276,144 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
     for (int i = tid; i < NQ * DIG_BINS; i += 256) {
       const uint32_t v = lds_h[i];
       if (v) atomicAdd(&hint[(row0 + i / DIG_BINS) * DIG_BINS + (i % DIG_BINS)], v);
+    }
+  }
+}
+
+// The FP4 QK path (MXFP4 keys, the query quantised to MXFP4 in the call), 64
+// heads x 128 dims. Grid: (workgroups per row, rows); one query row per
+// workgroup. As in the bf16 scan the waves load their MFMA operands straight
+// from memory and never wait for each other: a workgroup tile is 256 entries,
+// wave w owns entries 64 w .. 64 w + 63 of it as four 16-entry N tiles, and
+// for N tile n lane (group G, entry l16) loads the 16 code bytes of block G of
+// its entry (one instruction reads 1 KB: 16 consecutive 64-byte key rows) and
+// the entry's four scale bytes. A three-slot register ring keeps two tiles in
+// flight. Each N tile is four scaled FP4 MFMAs (v_mfma_scale_f32_16x16x128_
+// f8f6f4, one per 16-head M tile, all 128 dims in one instruction) with the
+// key block's scale byte; no code is widened. The query is quantised once per
+// workgroup: thread t makes block t % 4 of head t / 4 (mxfp4_quant_block) and
+// the codes reach the operand lanes through 4 KB of LDS.
+template <int CO>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+idx_scan_fp4_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+                    const uint8_t* __restrict__ k_idx, const uint32_t* __restrict__ k_scale,
+                    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
+                    int64_t N_max, int m, float* __restrict__ scores, CompressArgs ca, unsigned scan_y,
+                    uint32_t* __restrict__ hint, uint32_t* __restrict__ zero, int64_t zero_n) {
+  if constexpr (CO != 0) {
+    if (blockIdx.y >= scan_y) {
+      compress_entry<DT_BF16, CO>(ca, ((int64_t)(blockIdx.y - scan_y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x);
+      return;
+    }
+  }
+  constexpr int H = 64, DI = 128;
+  constexpr int KROW = DI / 2;  // code bytes per key row
+  constexpr int TE = 256;       // entries per workgroup tile: 4 waves x 4 N tiles x 16
+  constexpr int NT = 4;         // N tiles per wave and tile
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_qc[H * 4];  // codes of block g of head h at [4 h + g]
+  __shared__ __attribute__((aligned(16))) int lds_qs[H * 4];      // and its scale byte
+  __shared__ __attribute__((aligned(16))) uint32_t lds_h[DIG_BINS];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63, wv = tid >> 6;
+  const int G = l >> 4, l16 = l & 15;
+  const int64_t row = blockIdx.y;
+  const int64_t b = row / Tq;
+  const uint8_t* kb = k_idx + b * N_max * KROW + G * 16;
+  const uint32_t* ksb = k_scale + b * N_max;
+
+  u32x4_t rc[3][NT];  // ring: codes of block G of entry (tile, wave, n, l16)
+  uint32_t rs[3][NT];  // and that entry's four scale bytes
+  // unconditional loads, the entry clamped to lim - 1 (lim >= 1), as in the
+  // bf16 scan: the number of loads in flight is the same on every path
+  auto load = [&](auto SLOT, int64_t tile, int64_t lim) {
+    constexpr int slot = decltype(SLOT)::value;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int64_t e = min(tile * TE + wv * (16 * NT) + n * 16 + l16, lim - 1);
+      rc[slot][n] = ld16(kb + e * KROW);
+      rs[slot][n] = ksb[e];
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  load(I0{}, blockIdx.x, N_max);
+  load(I1{}, blockIdx.x + gridDim.x, N_max);
+
+  const int64_t V = max((int64_t)0, min(min((int64_t)n_comp[b], ((int64_t)q_pos[row] + 1) / m), N_max));
+  const int64_t ntiles = (V + TE - 1) / TE;
+  if ((int64_t)blockIdx.x >= ntiles) {
+    zero_counters(zero, zero_n);
+    return;
+  }
+  const int64_t nmine = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+
+  {
+    // thread t: block g = t % 4 (dims 32 g .. 32 g + 31) of head h = t / 4
+    const int h = tid >> 2, g = tid & 3;
+    const uint16_t* qp = q_idx + (row * H + h) * DI + g * 32;
+    u32x4_t xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[j] = ld16(qp + j * 8);
+    u32x4_t c;
+    lds_qs[tid] = mxfp4_quant_block(xv, c);
+    lds_qc[tid] = c;
+  }
+  f32x4_t wr[4];  // weights of heads mt*16 + G*4 + 0..3 (the accumulator rows of this lane)
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wr[mt][r] = w[row * H + mt * 16 + G * 4 + r];
+  if (hint)
+    for (int i = tid; i < DIG_BINS; i += 256) lds_h[i] = 0u;
+  __syncthreads();
+  u32x4_t qc[4];  // A operand of M tile mt: block G of head mt*16 + l16
+  int qsb[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    qc[mt] = lds_qc[(mt * 16 + l16) * 4 + G];
+    qsb[mt] = lds_qs[(mt * 16 + l16) * 4 + G];
+  }
+  // the weights' loads complete here, not inside the loop
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) asm volatile("" ::"v"(wr[mt]));
+  const __amdgpu_buffer_rsrc_t srow =
+      __builtin_amdgcn_make_buffer_rsrc(scores + row * N_max, (short)0, (int)(V * 4), BUF_RSRC_WORD3);
+
+  auto body = [&](int64_t it, auto SLOT, auto NEXT) {
+    constexpr int slot = decltype(SLOT)::value;
+    const int64_t tile = blockIdx.x + it * gridDim.x;
+    load(NEXT, blockIdx.x + (it + 2) * gridDim.x, V);  // past the last tile: clamped, unused
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int e = (int)(tile * TE) + wv * (16 * NT) + n * 16 + l16;
+      const int kscale = (int)((rs[slot][n] >> (8 * G)) & 0xffu);
+      float part = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4_t acc = mfma_fp4(qc[mt], qsb[mt], rc[slot][n], kscale);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part += wr[mt][r] * relu_bits(acc[r]);
+      }
+      part = sum_rows16(part);
+      // lanes of groups 1..3 hold the same sums: their offset is past the end
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow, G == 0 ? e * 4 : (int)(V * 4), 0, 0);
+      if (hint && G == 0 && e < V) atomicAdd(&lds_h[f32_key(part) >> DIG_SHIFT], 1u);
+    }
+  };
+  for (int64_t it = 0; it < nmine; it += 3) {
+    body(it, I0{}, I2{});
+    body(it + 1, I1{}, I0{});
+    body(it + 2, I2{}, I1{});
+  }
+  zero_counters(zero, zero_n);
+  if (hint) {
+    __syncthreads();
+    uint32_t* gh = hint + row * DIG_BINS;
+    for (int i = tid; i < DIG_BINS; i += 256) {
+      const uint32_t v = lds_h[i];
+      if (v) atomicAdd(&gh[i], v);
     }
   }
 }
@@ -818,13 +1007,31 @@ idx_scan_f32_kernel(const float* __restrict__ q_idx, const float* __restrict__ w
 }
 
 int indexer_hint_mode(const IndexerLaunch& a) {
+  if (a.q_dt == DT_BF16_MXFP4) return TOPK_HINT_ACCUMULATED;  // the row scan, whatever Tq
   if (!(a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16)) return TOPK_HINT_NONE;  // the tiny fp32 scan counts nothing
   return a.Tq >= 8 ? TOPK_HINT_WRITTEN : TOPK_HINT_ACCUMULATED;
+}
+
+// Workgroups per row of the low-precision row scan: a few per CU in total,
+// each walking a strided run of its row's tiles.
+static int64_t lp_per_row(const IndexerLaunch& a, int64_t rows) {
+  const int64_t te = a.k_dt == DT_FP8 ? 128 : 256;
+  const int64_t ntiles = (a.N_max + te - 1) / te;
+  return max((int64_t)1, min(ntiles, (512 + rows - 1) / rows));
 }
 
 hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
   const int64_t rows = a.B * a.Tq;
   if (rows == 0 || a.N_max == 0) return hipSuccess;
+  if (a.q_dt == DT_BF16_MXFP4) {
+    // the FP4 QK path (MXFP4 keys, 64 x 128): the row scan for any query count
+    hipLaunchKernelGGL((idx_scan_fp4_kernel<0>), dim3((unsigned)lp_per_row(a, rows), (unsigned)rows),
+                       dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx), a.w,
+                       reinterpret_cast<const uint8_t*>(a.k_idx), reinterpret_cast<const uint32_t*>(a.k_scale),
+                       a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)rows, a.hint,
+                       a.zero, a.zero_n);
+    return hipGetLastError();
+  }
   if (a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16 && a.Tq >= 8) {
     // many queries per sequence: key tiles shared by 8 queries per workgroup
     dim3 grid((unsigned)((a.Tq + 7) / 8), (unsigned)a.B);
@@ -885,7 +1092,8 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
 hipError_t run_compress_indexer(const CompressLaunch& c, const IndexerLaunch& a, hipStream_t st) {
   const int64_t rows = a.B * a.Tq;
   const int64_t nblk = c.blk_end - c.blk_begin;
-  const bool scan_dec = a.H_I == 64 && a.D_I == 128 && a.q_dt == DT_BF16 && a.Tq < 8;
+  const bool qf4 = a.q_dt == DT_BF16_MXFP4;
+  const bool scan_dec = a.H_I == 64 && a.D_I == 128 && ((a.q_dt == DT_BF16 && a.Tq < 8) || qf4);
   const bool comp_ok = c.in_dt == DT_BF16 && (c.out_dt == DT_BF16 || c.out_dt == DT_KV_FP8) &&
                        (c.overlap || c.m < 16) && c.B > 0 && nblk > 0;
   // the compression's grid rows go after the scan's: keep the total within
@@ -909,8 +1117,9 @@ hipError_t run_compress_indexer(const CompressLaunch& c, const IndexerLaunch& a,
     const auto* k = reinterpret_cast<const uint8_t*>(a.k_idx);
     const auto* ks = reinterpret_cast<const uint32_t*>(a.k_scale);
     const bool f8 = a.k_dt == DT_FP8, o8 = c.out_dt == DT_KV_FP8;
-    auto kern = f8 ? (o8 ? idx_scan_lp_kernel<DT_FP8, DT_KV_FP8> : idx_scan_lp_kernel<DT_FP8, DT_BF16>)
-                   : (o8 ? idx_scan_lp_kernel<DT_MXFP4, DT_KV_FP8> : idx_scan_lp_kernel<DT_MXFP4, DT_BF16>);
+    auto kern = f8    ? (o8 ? idx_scan_lp_kernel<DT_FP8, DT_KV_FP8> : idx_scan_lp_kernel<DT_FP8, DT_BF16>)
+                : qf4 ? (o8 ? idx_scan_fp4_kernel<DT_KV_FP8> : idx_scan_fp4_kernel<DT_BF16>)
+                      : (o8 ? idx_scan_lp_kernel<DT_MXFP4, DT_KV_FP8> : idx_scan_lp_kernel<DT_MXFP4, DT_BF16>);
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, a.w, k, ks, a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores,
                        ca0, (unsigned)rows, a.hint, a.zero, a.zero_n);
     return hipGetLastError();

@@ -183,6 +183,7 @@ class Cfg:
     kv_dtype: str = "bf16"  # main KV rows: "bf16", or "fp8" (E4M3 + bf16 RoPE dims)
     qk_rope: bool = False   # decode step with the query prologue (RMSNorm, RoPE) and output inverse RoPE
     Tq: int = 1          # queries per sequence (decode: the last Tq tokens, e.g. 2 with a drafted token)
+    q_fp4: bool = False  # indexer query quantised to MXFP4 by the call (FP4 x FP4 QK; MXFP4 keys)
 
     @property
     def N(self) -> int:  # compressed entries; tail tokens (n mod m) are dropped
@@ -218,7 +219,10 @@ C2R = dataclasses.replace(C2, name="c2r_csa_decode_flash_128k_qk_rope", qk_rope=
 # C2 with two query tokens per sequence and step (the current token and a
 # drafted one, as a depth-1 multi-token predictor verifies them)
 C2M = dataclasses.replace(C2, name="c2m_csa_decode_flash_128k_2tok", Tq=2)
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6, C4F, C2F, C3F, C2R, C2M)}
+# C2X with both operands of the indexer's QK product in FP4: the bf16 indexer
+# query is quantised to MXFP4 inside the call
+C2Q = dataclasses.replace(C2X, name="c2q_csa_decode_flash_128k_fp4_qk", q_fp4=True)
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5, C2X, C6, C4F, C2F, C3F, C2R, C2M, C2Q)}
 
 
 def scaled(cfg: Cfg, **kw) -> Cfg:

@@ -103,11 +103,21 @@ def test_compress_single_branch_long_blocks():
 
 # ------------------------------------------------------------------ indexer
 
-def _indexer_case(B, Tq, N_max, n_comp, q_pos, m, top_k, kdt, seed=0, H_I=64, D_I=128, wdist="normal"):
-    _say("indexer", B, Tq, N_max, n_comp, m, top_k, kdt)
+def _indexer_case(B, Tq, N_max, n_comp, q_pos, m, top_k, kdt, seed=0, H_I=64, D_I=128, wdist="normal",
+                  q_fp4=False):
+    _say("indexer", B, Tq, N_max, n_comp, m, top_k, kdt, "fp4 query" if q_fp4 else "")
     g = _g(seed)
     qdt = "f32" if kdt == "f32" else "bf16"
     q_idx = g.standard_normal((B, Tq, H_I, D_I)).astype(np.float32) / math.sqrt(D_I)
+    if q_fp4:
+        # blocks that reach every branch of the query's MXFP4 rounding: ties of
+        # the E2M1 grid (to the even code), values that saturate, an all-zero
+        # block, a block of tiny values, a block already in MXFP4
+        ties = np.array([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, -0.25, -1.75, 7.0, 0.3, -2.9])
+        q_idx[:, :, 0, :14] = ties * 2.0 ** -4
+        q_idx[:, :, 1, 32:64] = 0.0
+        q_idx[:, :, 2, 64:96] *= 2.0 ** -40
+        q_idx[:, :, 3, :32] = np.tile([4.0, -3.0, 1.5, 0.5, 0.0, -6.0, 2.0, 1.0], 4) * 2.0 ** -3
     if qdt == "bf16":
         q_idx = gen.bf16_round(q_idx)
     w = (g.standard_normal((B, Tq, H_I)) if wdist == "normal" else g.uniform(0, 1, (B, Tq, H_I))).astype(np.float32)
@@ -134,7 +144,7 @@ def _indexer_case(B, Tq, N_max, n_comp, q_pos, m, top_k, kdt, seed=0, H_I=64, D_
     qp = dev(np.asarray(q_pos, np.int32).reshape(B, Tq))
     nc = dev(np.asarray(n_comp, np.int32))
     scores = torch.full((B, Tq, N_max), float("nan"), device=DEV)
-    L.indexer_score(q_t, dev(w), k_t, sc_t, qp, nc, scores, m=m)
+    L.indexer_score(q_t, dev(w), k_t, sc_t, qp, nc, scores, m=m, q_fp4=q_fp4)
     idx = torch.empty((B, Tq, top_k), dtype=torch.int32, device=DEV)
     idx2 = torch.empty_like(idx)
     tsc = torch.empty((B, Tq, top_k), device=DEV)
@@ -145,10 +155,10 @@ def _indexer_case(B, Tq, N_max, n_comp, q_pos, m, top_k, kdt, seed=0, H_I=64, D_
     nb = L.indexer_score_topk_workspace_bytes(B, Tq, N_max, top_k)
     ws = torch.zeros(max(nb, 1), dtype=torch.uint8, device=DEV)
     idx3, idx4 = torch.empty_like(idx), torch.empty_like(idx)
-    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx2, m=m, ws=ws)
-    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx3, m=m, ws=ws)
+    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx2, m=m, ws=ws, q_fp4=q_fp4)
+    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx3, m=m, ws=ws, q_fp4=q_fp4)
     junk = torch.randint(0, 256, (max(nb, 1),), dtype=torch.uint8, device=DEV)
-    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx4, m=m, ws=junk)
+    L.indexer_score_topk(q_t, dev(w), k_t, sc_t, qp, nc, idx4, m=m, ws=junk, q_fp4=q_fp4)
     torch.cuda.synchronize()
     S, I, I2, TS = host(scores), host(idx), host(idx2), host(tsc)
     assert np.array_equal(I, I2), "indexer_score_topk != indexer_score + indexer_topk"
@@ -160,7 +170,7 @@ def _indexer_case(B, Tq, N_max, n_comp, q_pos, m, top_k, kdt, seed=0, H_I=64, D_
             V = oracle.visible(qpos[b, t], n_comp[b], m)
             V = min(V, N_max)
             ref = oracle.indexer_scores(q_idx[b, t], w[b, t], kval[b], V,
-                                        None if (scale is None or kdt == "mxfp4") else scale[b])
+                                        None if (scale is None or kdt == "mxfp4") else scale[b], q_fp4=q_fp4)
             got = S[b, t, :V]
             err = np.abs(got - ref).max() if V else 0.0
             # fp32 accumulation of bf16 products over 128 dims, 64 heads
@@ -193,13 +203,17 @@ def test_indexer_bf16_decode_query_pairs():
 
 
 @pytest.mark.parametrize("kdt,kv,Tq", [("bf16", "bf16", 1), ("bf16", "fp8", 1), ("bf16", "bf16", 2),
-                                        ("fp8", "bf16", 1), ("mxfp4", "fp8", 1), ("fp8", "bf16", 8)])
+                                        ("fp8", "bf16", 1), ("mxfp4", "fp8", 1), ("fp8", "bf16", 8),
+                                        ("mxfp4_q4", "bf16", 1), ("mxfp4_q4", "fp8", 2)])
 def test_compress_indexer_fused_equals_separate(kdt, kv, Tq):
     """The one-call decode front (compression of the completed block and the
     indexer scan) gives the bits of csa_compress followed by indexer_score,
-    with bf16, E4M3 and MXFP4 keys; eight query rows (the many-query scan)
-    take the two launches in turn."""
+    with bf16, E4M3 and MXFP4 keys, and MXFP4 keys with the FP4-quantised
+    query; eight query rows (the many-query scan) take the two launches in
+    turn."""
     _say("fused front", kdt, kv, Tq)
+    q4 = kdt == "mxfp4_q4"
+    kdt = "mxfp4" if q4 else kdt
     cfg = gen.scaled(gen.C2F if kv == "fp8" else gen.C2, B=4, n=16384, k_dtype=kdt, Tq=Tq)
     x = gen.gen_decode(cfg)
     B, N, m = cfg.B, cfg.N, cfg.m
@@ -222,10 +236,11 @@ def test_compress_indexer_fused_equals_separate(kdt, kv, Tq):
         scores = torch.full((B, Tq, N), float("nan"), device=DEV)
         kw = dict(tok_begin=cfg.n - 2 * m, blk_begin=N - 1, blk_end=N)
         if fused:
-            L.csa_compress_indexer_score(*raw, Ba, Bb, kvd, qi, w, k_t, sc, pos, nc, scores, m_c=m, m=m, **kw)
+            L.csa_compress_indexer_score(*raw, Ba, Bb, kvd, qi, w, k_t, sc, pos, nc, scores, m_c=m, m=m, q_fp4=q4,
+                                         **kw)
         else:
             L.csa_compress(*raw, Ba, Bb, kvd, m=m, **kw)
-            L.indexer_score(qi, w, k_t, sc, pos, nc, scores, m=m)
+            L.indexer_score(qi, w, k_t, sc, pos, nc, scores, m=m, q_fp4=q4)
         torch.cuda.synchronize()
         outs.append((host(kvd[:, N - 2:]), host(scores)))
     assert np.array_equal(outs[0][0], outs[1][0]), "compressed entries differ"
@@ -269,6 +284,19 @@ def test_indexer_mxfp4_decode():
     # MXFP4 keys (OCP FP4 E2M1, E8M0 scale per 32 dims): ragged tail of the
     # 256-entry tiles, a short sequence
     _indexer_case(3, 1, 2300, [2300, 1777, 9], [9199, 9199, 9199], 4, 256, "mxfp4", seed=14)
+
+
+def test_indexer_fp4_query_decode():
+    # the FP4 QK path: the bf16 query quantised to MXFP4 in the scan, FP4 x FP4
+    # on the scaled MFMA; ragged tail of the 256-entry tiles, a short sequence
+    _indexer_case(3, 1, 2300, [2300, 1777, 9], [9199, 9199, 9199], 4, 256, "mxfp4", seed=18, q_fp4=True)
+
+
+def test_indexer_fp4_query_many_rows():
+    # many query rows of one sequence (a prefill chunk) on the FP4 QK path:
+    # the row scan serves them, each row with its own visible count
+    pos = list(range(0, 2400, 60))
+    _indexer_case(1, 40, 600, [600], pos, 4, 32, "mxfp4", seed=19, q_fp4=True)
 
 
 def test_indexer_mxfp4_prefill_rows():

@@ -75,7 +75,7 @@ def run_csa_decode(cfg, x):
         L.csa_compress_indexer_score_topk(_bf(x["Ca"]), _bf(x["Cb"]), _bf(x["Za"]), _bf(x["Zb"]), _t(x["Ba"]),
                                           _t(x["Bb"]), kv, _bf(x["q_idx"][:, None]), _t(x["w"][:, None]), k_t, sc,
                                           q_pos, n_comp, dst, m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1,
-                                          blk_end=N, ws=ws)
+                                          blk_end=N, ws=ws, q_fp4=cfg.q_fp4)
     scores = ws[:B * N * 4].view(torch.float32).view(B, 1, N)
     out = torch.empty((B, cfg.H, cfg.D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, cfg.H), device=DEV)
@@ -122,7 +122,7 @@ def check_csa_decode(cfg, x, seqs):
             tau = 1.0 / np.sqrt(cfg.D)
         oidx, o_ref, lse_ref, s = oracle.csa_query(q, x["q_idx"][b], x["w"][b], comp, keys, cfg.n - 1, N,
                                                    m, cfg.top_k, _kv_values(cfg, x["kv_win"][b]), x["sink"],
-                                                   k_scale=sc, tau=tau)
+                                                   k_scale=sc, tau=tau, q_fp4=cfg.q_fp4)
         if cfg.qk_rope:
             o_ref = oracle.rope_rotate(o_ref[None], [cfg.n - 1], inverse=True)[0]
         assert np.abs(S[b] - s).max() <= 2e-5 * 8 * (1 + np.abs(s).max())
@@ -443,6 +443,16 @@ def test_csa_decode_flash_mxfp4_full_size_sampled():
     check_csa_decode(cfg, gen.gen_decode(cfg), [0, 17, 31])
 
 
+def test_csa_decode_flash_fp4_qk_reduced():
+    cfg = gen.scaled(gen.C2Q, B=4, n=16384)
+    check_csa_decode(cfg, gen.gen_decode(cfg), range(cfg.B))
+
+
+def test_csa_decode_flash_fp4_qk_full_size_sampled():
+    cfg = gen.C2Q  # C2X with the indexer query quantised to MXFP4 in the call, as bench.py runs it
+    check_csa_decode(cfg, gen.gen_decode(cfg), [0, 13, 31])
+
+
 def check_hca_prefill(cfg, chunks, picks):
     """Single-branch compression of the whole sequence at m' (HCA), then
     hca_prefill by 4096-query chunks, as bench.py runs it."""
@@ -533,11 +543,11 @@ def run_decode_step(cfg, x, ws=None, seqs_nc=None):
         if fused:
             L.csa_decode_step(*comp, _t(x["Ba"]), _t(x["Bb"]), qi, wt, k_t, sc, q_pos, n_comp, q, kv, win, wl,
                               _t(x["sink"]), idx, out, lse, tsc, m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1,
-                              blk_end=N, ws=ws)
+                              blk_end=N, ws=ws, q_fp4=cfg.q_fp4)
         else:
             L.csa_compress_indexer_score_topk(*comp, _t(x["Ba"]), _t(x["Bb"]), kv, qi, wt, k_t, sc, q_pos, n_comp,
                                               idx, tsc, m_c=m, m=m, tok_begin=cfg.n - 2 * m, blk_begin=N - 1,
-                                              blk_end=N)
+                                              blk_end=N, q_fp4=cfg.q_fp4)
             L.sparse_mqa_decode_multi(q, kv, idx, win, wl, _t(x["sink"]), out, lse)
         torch.cuda.synchronize()
         res.append((host(kv[:, N - 1]), host(idx), host(tsc), host(out), host(lse)))
@@ -549,10 +559,11 @@ def _same(a, b, what):
         assert np.array_equal(a[i], b[i], equal_nan=True), f"{what}: {nm} differs between the fused and separate paths"
 
 
-@pytest.mark.parametrize("name", ["c2_reduced", "c2m_reduced", "c2f_reduced", "c2x_reduced", "c5_reduced"])
+@pytest.mark.parametrize("name", ["c2_reduced", "c2m_reduced", "c2f_reduced", "c2x_reduced", "c2q_reduced",
+                                  "c5_reduced"])
 def test_decode_step_equals_separate_reduced(name):
     base = {"c2_reduced": gen.C2, "c2m_reduced": gen.C2M, "c2f_reduced": gen.C2F, "c2x_reduced": gen.C2X,
-            "c5_reduced": gen.C5}[name]
+            "c2q_reduced": gen.C2Q, "c5_reduced": gen.C5}[name]
     cfg = gen.scaled(base, B=6, n=4 * 40000 if base is gen.C5 else 16384)
     x = gen.gen_decode(cfg)
     print(f"[case] decode step {name}", flush=True)

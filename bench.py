@@ -347,10 +347,10 @@ def bench_decode(a, torch, L, gen, dev, cfg, steps, warmup, cpu_s, copy_gbs, wna
                          "heads": H, "head_dim": D, "window": W, "indexer_key_dtype": cfg.k_dtype,
                          "kv_dtype": cfg.kv_dtype, "qk_norm_rope": cfg.qk_rope, "query_tokens_per_sequence": Tq,
                          "indexer_query": "mxfp4 (quantised in the call)" if cfg.q_fp4 else "bf16"}
-        kname = {"fp8": "idx_scan_lp_kernel<2, 1> (E4M3 keys, with the entry's compression)",
-                 "mxfp4": "idx_scan_fp4_kernel<1> (MXFP4 keys and the FP4-quantised query on the scaled FP4 "
-                          "MFMA, with the entry's compression)" if cfg.q_fp4 else
-                          "idx_scan_lp_kernel<3, 1> (MXFP4 keys, with the entry's compression)"}.get(
+        kname = {"fp8": "idx_scan_reg_kernel<2, false, 1> (E4M3 keys, with the entry's compression)",
+                 "mxfp4": "idx_scan_reg_kernel<3, true, 1> (MXFP4 keys and the FP4-quantised query on the scaled "
+                          "FP4 MFMA, with the entry's compression)" if cfg.q_fp4 else
+                          "idx_scan_reg_kernel<3, false, 1> (MXFP4 keys, with the entry's compression)"}.get(
             cfg.k_dtype, "idx_scan_bf16_kernel<2, 1> (two query rows per workgroup, with the entry's compression)"
             if Tq % 2 == 0 else "idx_scan_bf16_kernel<1, 1> (with the entry's compression)")
         # (3) the step's first launch (compression + scan, the same kernel

@@ -9,15 +9,18 @@
 //
 // Design: the scan over keys is the dominant HBM stream of CSA decode. It is
 // a [64 heads x 128] x [128 x entries] contraction, run on
-// v_mfma_f32_16x16x32_bf16 with heads as M (four 16-row tiles) and entries as
-// N (16 per wave). The query operand stays in registers for the whole
-// workgroup. Keys go HBM -> registers (coalesced) -> LDS (swizzled) -> MFMA
-// operands; FP8 keys are decoded exactly to bf16 after the LDS read and their
-// scale is applied after the head sum (it is positive). The epilogue never leaves registers: a lane
-// holds 16 heads of one entry per tile, applies ReLU and w, sums, and two
-// cross-lane shuffles complete the 64-head sum. K dims are visited in a
-// permuted order (lane group G covers dims G*32..G*32+31), identical for q and
-// k, which leaves the dot products unchanged.
+// v_mfma_f32_16x16x32_bf16 (or, for the FP4 QK path, the scaled FP4 MFMA)
+// with heads as M (four 16-row tiles) and entries as N (16 per wave). The
+// query operand stays in registers for the whole workgroup. Decode scans
+// load the key operands straight from HBM into a register ring (no LDS tile,
+// no barrier per tile); FP8 and FP4 keys are widened exactly to bf16 in
+// registers, the FP8 scale applied after the head sum (it is positive). The
+// prefill scan shares each key tile of LDS among eight query rows. The
+// epilogue never leaves registers: a lane holds 16 heads of one entry per
+// tile, applies ReLU and w, sums, and two cross-lane shuffles complete the
+// 64-head sum. K dims are visited in a permuted order (lane group G covers
+// dims G*32..G*32+31), identical for q and k, which leaves the dot products
+// unchanged.
 #include <type_traits>
 
 #include "common.h"
@@ -44,9 +47,10 @@ __device__ __forceinline__ void zero_counters(uint32_t* zero, int64_t n) {
     for (int64_t i = threadIdx.x; i < n; i += blockDim.x) zero[i] = 0u;
 }
 
-// XOR swizzle of the 16-byte chunk index of key row r in an LDS tile. The
-// operand reads take one chunk of each of 16 consecutive rows; with 64 banks
-// of 4 bytes those 16 chunks must fall in 16 different 16-byte bank groups.
+// XOR swizzle of the 16-byte chunk index of key row r in a prefill LDS tile.
+// The operand reads take one chunk of each of 16 consecutive rows; with 64
+// banks of 4 bytes those 16 chunks must fall in 16 different 16-byte bank
+// groups.
 // fp8 rows are 128 bytes (odd rows start in group 8): chunk ^ ((r >> 1) & 7).
 // MXFP4 rows are 64 bytes (four rows per 256 bytes): chunk ^ ((r >> 2) & 3).
 // bf16 rows (256 bytes, every row starts in group 0) serve the prefill
@@ -280,38 +284,50 @@ idx_scan_bf16_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict
   }
 }
 
-// The FP4 QK path (MXFP4 keys, the query quantised to MXFP4 in the call), 64
-// heads x 128 dims. Grid: (workgroups per row, rows); one query row per
-// workgroup. As in the bf16 scan the waves load their MFMA operands straight
-// from memory and never wait for each other: a workgroup tile is 256 entries,
-// wave w owns entries 64 w .. 64 w + 63 of it as four 16-entry N tiles, and
-// for N tile n lane (group G, entry l16) loads the 16 code bytes of block G of
-// its entry (one instruction reads 1 KB: 16 consecutive 64-byte key rows) and
-// the entry's four scale bytes. A three-slot register ring keeps two tiles in
-// flight. Each N tile is four scaled FP4 MFMAs (v_mfma_scale_f32_16x16x128_
-// f8f6f4, one per 16-head M tile, all 128 dims in one instruction) with the
-// key block's scale byte; no code is widened. The query is quantised once per
-// workgroup: thread t makes block t % 4 of head t / 4 (mxfp4_quant_block) and
-// the codes reach the operand lanes through 4 KB of LDS.
-template <int CO>
+// Decode scan of low-precision keys (E4M3 with a per-entry fp32 scale, or
+// MXFP4), 64 heads x 128 dims. Grid: (workgroups per row, rows); one query
+// row per workgroup. As in the bf16 scan the waves load their MFMA operands
+// straight from memory and never wait for each other: a workgroup tile is
+// 64 NT entries, wave w owns entries 16 NT w .. 16 NT w + 16 NT - 1 of it as
+// NT 16-entry N tiles, and for N tile n lane (group G, entry l16) loads the
+// codes of dims 32 G .. 32 G + 31 of its entry (E4M3: 32 bytes, so one load
+// instruction reads two 1 KB halves of 16 consecutive 128-byte rows; MXFP4:
+// block G, 16 bytes, 1 KB of 16 consecutive 64-byte rows) and the entry's
+// scale word. A three-slot register ring keeps two tiles in flight.
+//   bf16 query (QF4 false): codes are widened exactly to bf16 (two per
+//   scaled convert) in the k order of the query operand (k-step s takes dims
+//   32 G + 8 s .. + 7, a permutation applied to both sides), and a tile's
+//   16 entries x 64 heads are 4 x 4 v_mfma_f32_16x16x32_bf16; the E4M3 scale
+//   multiplies the head-weighted sum (it is positive).
+//   FP4 query (QF4, MXFP4 keys: the FP4 QK path): the query is quantised
+//   once per workgroup (thread t makes block t % 4 of head t / 4,
+//   mxfp4_quant_block; the codes reach the operand lanes through 4 KB of
+//   LDS) and each N tile is four scaled FP4 MFMAs (v_mfma_scale_f32_16x16x128
+//   _f8f6f4, one per 16-head M tile over all 128 dims) with the key block's
+//   scale byte; no code is widened.
+template <int KDT, bool QF4, int CO>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-idx_scan_fp4_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+idx_scan_reg_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
                     const uint8_t* __restrict__ k_idx, const uint32_t* __restrict__ k_scale,
                     const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
                     int64_t N_max, int m, float* __restrict__ scores, CompressArgs ca, unsigned scan_y,
                     uint32_t* __restrict__ hint, uint32_t* __restrict__ zero, int64_t zero_n) {
+  static_assert(KDT == DT_FP8 || KDT == DT_MXFP4, "low-precision keys");
+  static_assert(!QF4 || KDT == DT_MXFP4, "the FP4 query goes with MXFP4 keys");
   if constexpr (CO != 0) {
     if (blockIdx.y >= scan_y) {
       compress_entry<DT_BF16, CO>(ca, ((int64_t)(blockIdx.y - scan_y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x);
       return;
     }
   }
-  constexpr int H = 64, DI = 128;
-  constexpr int KROW = DI / 2;  // code bytes per key row
-  constexpr int TE = 256;       // entries per workgroup tile: 4 waves x 4 N tiles x 16
-  constexpr int NT = 4;         // N tiles per wave and tile
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_qc[H * 4];  // codes of block g of head h at [4 h + g]
-  __shared__ __attribute__((aligned(16))) int lds_qs[H * 4];      // and its scale byte
+  constexpr bool MX = KDT == DT_MXFP4;
+  constexpr int H = 64, DI = 128, KS = 4;  // k-steps of 32 (bf16 query)
+  constexpr int KROW = MX ? DI / 2 : DI;   // code bytes per key row
+  constexpr int CPL = MX ? 1 : 2;          // 16-byte code chunks per lane and N tile
+  constexpr int NT = MX ? 4 : 2;           // N tiles per wave and tile (4 KB of codes per wave)
+  constexpr int TE = 64 * NT;              // entries per workgroup tile
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_qc[QF4 ? H * 4 : 1];  // FP4 query: block g of head h at [4 h + g]
+  __shared__ __attribute__((aligned(16))) int lds_qs[QF4 ? H * 4 : 1];      // and its scale byte
   __shared__ __attribute__((aligned(16))) uint32_t lds_h[DIG_BINS];
 
   const int tid = threadIdx.x;
@@ -319,11 +335,11 @@ idx_scan_fp4_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
   const int G = l >> 4, l16 = l & 15;
   const int64_t row = blockIdx.y;
   const int64_t b = row / Tq;
-  const uint8_t* kb = k_idx + b * N_max * KROW + G * 16;
-  const uint32_t* ksb = k_scale + b * N_max;
+  const uint8_t* kb = k_idx + b * N_max * KROW + G * (16 * CPL);
+  const uint32_t* ksw = k_scale + b * N_max;
 
-  u32x4_t rc[3][NT];  // ring: codes of block G of entry (tile, wave, n, l16)
-  uint32_t rs[3][NT];  // and that entry's four scale bytes
+  u32x4_t rc[3][NT][CPL];  // ring: the lane's codes of entry (tile, wave, n, l16)
+  uint32_t rs[3][NT];      // and that entry's scale word
   // unconditional loads, the entry clamped to lim - 1 (lim >= 1), as in the
   // bf16 scan: the number of loads in flight is the same on every path
   auto load = [&](auto SLOT, int64_t tile, int64_t lim) {
@@ -331,8 +347,9 @@ idx_scan_fp4_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int64_t e = min(tile * TE + wv * (16 * NT) + n * 16 + l16, lim - 1);
-      rc[slot][n] = ld16(kb + e * KROW);
-      rs[slot][n] = ksb[e];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) rc[slot][n][c] = ld16(kb + e * KROW + c * 16);
+      rs[slot][n] = ksw[e];
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -349,9 +366,11 @@ idx_scan_fp4_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
   }
   const int64_t nmine = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
 
-  {
-    // thread t: block g = t % 4 (dims 32 g .. 32 g + 31) of head h = t / 4
-    const int h = tid >> 2, g = tid & 3;
+  bf16x8_t qa[QF4 ? 1 : 4][KS];  // bf16 query: lane (head mt*16 + l16, group G) holds dims 32 G + 8 s .. + 7
+  u32x4_t qc[4];                 // FP4 query: block G of head mt*16 + l16, and its scale byte
+  int qsb[4];
+  if constexpr (QF4) {
+    const int h = tid >> 2, g = tid & 3;  // thread t: block g (dims 32 g .. 32 g + 31) of head h
     const uint16_t* qp = q_idx + (row * H + h) * DI + g * 32;
     u32x4_t xv[4];
 #pragma unroll
@@ -359,6 +378,13 @@ idx_scan_fp4_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
     u32x4_t c;
     lds_qs[tid] = mxfp4_quant_block(xv, c);
     lds_qc[tid] = c;
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint16_t* qp = q_idx + (row * H + mt * 16 + l16) * DI + G * 32;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qa[mt][s] = as_bf16x8(ld16(qp + s * 8));
+    }
   }
   f32x4_t wr[4];  // weights of heads mt*16 + G*4 + 0..3 (the accumulator rows of this lane)
 #pragma unroll
@@ -368,14 +394,19 @@ idx_scan_fp4_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
   if (hint)
     for (int i = tid; i < DIG_BINS; i += 256) lds_h[i] = 0u;
   __syncthreads();
-  u32x4_t qc[4];  // A operand of M tile mt: block G of head mt*16 + l16
-  int qsb[4];
+  if constexpr (QF4) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    qc[mt] = lds_qc[(mt * 16 + l16) * 4 + G];
-    qsb[mt] = lds_qs[(mt * 16 + l16) * 4 + G];
+    for (int mt = 0; mt < 4; ++mt) {
+      qc[mt] = lds_qc[(mt * 16 + l16) * 4 + G];
+      qsb[mt] = lds_qs[(mt * 16 + l16) * 4 + G];
+    }
+  } else {
+    // the query's loads complete here, not inside the loop
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qa[mt][s]));
   }
-  // the weights' loads complete here, not inside the loop
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) asm volatile("" ::"v"(wr[mt]));
   const __amdgpu_buffer_rsrc_t srow =
@@ -388,15 +419,53 @@ idx_scan_fp4_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int e = (int)(tile * TE) + wv * (16 * NT) + n * 16 + l16;
-      const int kscale = (int)((rs[slot][n] >> (8 * G)) & 0xffu);
       float part = 0.0f;
+      if constexpr (QF4) {
+        const int kscale = (int)((rs[slot][n] >> (8 * G)) & 0xffu);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f32x4_t acc = mfma_fp4(qc[mt], qsb[mt], rc[slot][n], kscale);
+        for (int mt = 0; mt < 4; ++mt) {
+          const f32x4_t acc = mfma_fp4(qc[mt], qsb[mt], rc[slot][n][0], kscale);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part += wr[mt][r] * relu_bits(acc[r]);
+          for (int r = 0; r < 4; ++r) part += wr[mt][r] * relu_bits(acc[r]);
+        }
+      } else {
+        bf16x8_t kbv[KS];
+        if constexpr (MX) {
+          // block G's E8M0 byte as the fp32 2^(E - 127), applied in the convert
+          const float sc = __uint_as_float(((rs[slot][n] >> (8 * G)) & 0xffu) << 23);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) kbv[s] = fp4x8_to_bf16x8(rc[slot][n][0][s], sc);
+        } else {
+          // k-step s: bytes 8 s .. 8 s + 7 of the lane's 32, i.e. chunk s / 2, half s % 2
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const u32x4_t v = rc[slot][n][c];
+            u32x4_t lo, hi;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              lo[2 * q] = fp8x2_to_bf16x2(v[q], false);
+              lo[2 * q + 1] = fp8x2_to_bf16x2(v[q], true);
+              hi[2 * q] = fp8x2_to_bf16x2(v[2 + q], false);
+              hi[2 * q + 1] = fp8x2_to_bf16x2(v[2 + q], true);
+            }
+            kbv[2 * c] = as_bf16x8(lo);
+            kbv[2 * c + 1] = as_bf16x8(hi);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], kbv[s], acc);
+          // accumulator row r of this lane is head mt*16 + G*4 + r
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part += wr[mt][r] * relu_bits(acc[r]);
+        }
       }
       part = sum_rows16(part);
+      // E4M3: sigma_i scales the head-weighted sum (ReLU commutes with a
+      // positive scale); MXFP4 scales are inside the products
+      if constexpr (!MX) part *= __uint_as_float(rs[slot][n]);
       // lanes of groups 1..3 hold the same sums: their offset is past the end
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow, G == 0 ? e * 4 : (int)(V * 4), 0, 0);
       if (hint && G == 0 && e < V) atomicAdd(&lds_h[f32_key(part) >> DIG_SHIFT], 1u);
@@ -414,217 +483,6 @@ idx_scan_fp4_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict_
     for (int i = tid; i < DIG_BINS; i += 256) {
       const uint32_t v = lds_h[i];
       if (v) atomicAdd(&gh[i], v);
-    }
-  }
-}
-
-// fp8 (E4M3) keys with a per-entry fp32 scale, 64 heads x 128 dims. Grid:
-// (workgroups per row, rows). A workgroup (4 waves) walks tiles of 128
-// entries (16 KB) of one query row with a stride of gridDim.x tiles. Tiles
-// move HBM -> LDS by DMA (global_load_lds, 1 KB per wave instruction) into a
-// ring of four, so the bytes in flight cover the memory latency without
-// costing registers; the scales travel with their tile (a 4-byte DMA per
-// entry). The 16-byte chunk index is XOR-swizzled (kswz) on the way in, by
-// permuting the lanes' source addresses, and read back in the operand layout
-// of v_mfma_f32_16x16x32_bf16 with conflict-free ds_read_b128: wave w owns
-// entries 32w .. 32w+31 of the tile as two 16-entry N tiles, heads are four
-// 16-row M tiles. Codes become bf16 with v_cvt_scalef32_pk_bf16_fp8 (two per
-// instruction, exact: every E4M3 value is a bf16 value); the scale multiplies
-// the head-weighted sum. Scores collect in LDS and are written out every
-// SC_TILES tiles: no store is in flight while DMA waits are counted.
-// CO != 0: grid rows past scan_y are a decode step's compression, as in the
-// bf16 scan.
-template <int KDT, int CO>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-idx_scan_lp_kernel(const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-                   const uint8_t* __restrict__ k_idx, const uint32_t* __restrict__ k_scale,
-                   const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_comp, int64_t Tq,
-                   int64_t N_max, int m, float* __restrict__ scores, CompressArgs ca, unsigned scan_y,
-                   uint32_t* __restrict__ hint, uint32_t* __restrict__ zero, int64_t zero_n) {
-  static_assert(KDT == DT_FP8 || KDT == DT_MXFP4, "low-precision keys");
-  if constexpr (CO != 0) {
-    if (blockIdx.y >= scan_y) {
-      compress_entry<DT_BF16, CO>(ca, ((int64_t)(blockIdx.y - scan_y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x);
-      return;
-    }
-  }
-  constexpr bool MX = KDT == DT_MXFP4;
-  constexpr int H = 64, DI = 128, KS = 4;   // k-steps of 32
-  constexpr int KROW = MX ? DI / 2 : DI;    // bytes per key row
-  constexpr int TE = MX ? 256 : 128;        // entries per tile
-  constexpr int NE = TE / 64;               // 16-entry N tiles per wave
-  constexpr int TB = TE * KROW;             // 16 KB
-  constexpr int NBUF = 4;                   // 64 KB ring
-  constexpr int DPW = TB / 1024 / 4;        // 1 KB DMAs per wave per tile
-  constexpr int PER_TILE = DPW + 1;         // + the scales (one dword per entry)
-  constexpr int SC_TILES = MX ? 6 : 16;     // score buffer (6 or 8 KB: two workgroups' LDS fit a CU)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[NBUF][TB];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_s[NBUF][TE];  // fp32 scale bits, or four E8M0 bytes
-  __shared__ __attribute__((aligned(16))) float lds_sc[SC_TILES][TE];
-  __shared__ __attribute__((aligned(16))) float lds_w[H];
-  // digit histogram, two 16-bit counts per word (a count that wraps only
-  // spoils the hint)
-  __shared__ __attribute__((aligned(16))) uint32_t lds_h[DIG_BINS / 2];
-
-  const int tid = threadIdx.x;
-  const int l = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = l >> 4, l16 = l & 15;  // k-group (4 x 8 dims) and column of the MFMA operands
-  const int64_t row = blockIdx.y;
-  const int64_t b = row / Tq;
-  int64_t V = min((int64_t)n_comp[b], ((int64_t)q_pos[row] + 1) / m);
-  V = max((int64_t)0, min(V, N_max));
-  const int64_t ntiles = (V + TE - 1) / TE;
-  if ((int64_t)blockIdx.x >= ntiles) {
-    zero_counters(zero, zero_n);
-    return;
-  }
-  const int64_t nmine = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // tiles of this workgroup
-  if (hint)
-    for (int i = tid; i < DIG_BINS / 2; i += 256) lds_h[i] = 0u;  // visible after the first barrier
-
-  // query operand A[m = head][k]: lane (head mt*16 + l16, group G) holds dims
-  // G*32 + s*8 + 0..7 for k-step s (a fixed permutation of the 128 dims,
-  // applied identically to the keys)
-  bf16x8_t qa[4][KS];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const uint16_t* qp = q_idx + (row * H + mt * 16 + l16) * DI + G * 32;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qa[mt][s] = as_bf16x8(ld16(qp + s * 8));
-  }
-  if (tid < H) lds_w[tid] = w[row * H + tid];  // visible after the first barrier
-  const uint8_t* kb = k_idx + b * N_max * KROW;
-  float* srow = scores + row * N_max;
-
-  // DMA j of wave wv fills tile bytes [(DPW wv + j) KB, +1 KB): lane l lands
-  // at row r, chunk slot p, and so fetches chunk p ^ kswz(r) of row r
-  int drow[DPW];
-  uint32_t dcol[DPW];
-#pragma unroll
-  for (int j = 0; j < DPW; ++j) {
-    const int byte = (DPW * wv + j) * 1024 + 16 * l;
-    drow[j] = byte / KROW;
-    dcol[j] = (uint32_t)((((byte % KROW) / 16) ^ kswz<KDT>(drow[j])) * 16);
-  }
-  auto issue = [&](int64_t it) {
-    const int64_t tile = blockIdx.x + it * gridDim.x;
-    const int buf = (int)(it & (NBUF - 1));
-    const int last = (int)min((int64_t)(TE - 1), N_max - 1 - tile * TE);  // rows past the cache repeat its end
-    const uint8_t* tb = uniform_ptr(kb + tile * TB);
-#pragma unroll
-    for (int j = 0; j < DPW; ++j)
-      dma_row(tb, (uint32_t)(min(drow[j], last) * KROW) + dcol[j], lds_addr(&lds_k[buf][(DPW * wv + j) * 1024]));
-    if (l < TE / 4)  // wave wv moves the scales of entries TE/4 wv .. TE/4 wv + TE/4 - 1
-      dma_dword(uniform_ptr(k_scale + b * N_max + tile * TE), (uint32_t)(min(TE / 4 * wv + l, last) * 4),
-                lds_addr(&lds_s[buf][TE / 4 * wv]));
-  };
-  auto flush = [&](int64_t it_begin, int64_t it_end) {  // scores of tiles [it_begin, it_end)
-    const int cnt = (int)(it_end - it_begin) * TE;
-    for (int k = tid; k < cnt; k += 256) {
-      const int64_t tile = blockIdx.x + (it_begin + k / TE) * gridDim.x;
-      const int64_t e = tile * TE + (k % TE);
-      if (e < V) srow[e] = lds_sc[k / TE][k % TE];
-    }
-    vm_wait_all();  // the stores retire before DMA counting resumes
-  };
-
-  // consume the query here: the compiler's wait for its loads lands before the
-  // first DMA, never inside the loop
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(qa[mt][s]));
-  for (int64_t it = 0; it < nmine && it < NBUF - 1; ++it) issue(it);
-  int64_t it_flushed = 0;
-  for (int64_t it = 0; it < nmine; ++it) {
-    const int ahead = (int)min((int64_t)(NBUF - 2), nmine - 1 - it);  // tiles issued after this one
-    if (ahead >= 2)
-      vm_barrier<2 * PER_TILE>();
-    else if (ahead == 1)
-      vm_barrier<PER_TILE>();
-    else
-      vm_barrier<0>();
-    // every wave is done with tile it-1: its buffer takes tile it+NBUF-1
-    if (it + NBUF - 1 < nmine) issue(it + NBUF - 1);
-    const int buf = (int)(it & (NBUF - 1));
-    float part[NE];
-#pragma unroll
-    for (int n = 0; n < NE; ++n) {
-      const int el = wv * (16 * NE) + n * 16 + l16;  // entry inside the tile
-      const uint8_t* kr = &lds_k[buf][el * KROW];
-      const int sw = kswz<KDT>(el);
-      bf16x8_t kbv[KS];
-      if constexpr (MX) {
-        // dims G*32 + s*8 .. : block G, bytes G*16 + s*4 (one chunk), scaled
-        // by the block's E8M0 byte G as the fp32 2^(E - 127)
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + ((G ^ sw) * 16));
-        const float sc = __uint_as_float(((lds_s[buf][el] >> (8 * G)) & 0xffu) << 23);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kbv[s] = fp4x8_to_bf16x8(v[s], sc);
-      } else {
-        // dims G*32 + s*8 .. : bytes G*32 + s*8, i.e. chunk G*2 + s/2, half s%2
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + (((G * 2 + c) ^ sw) * 16));
-          u32x4_t lo, hi;
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            lo[2 * q] = fp8x2_to_bf16x2(v[q], false);
-            lo[2 * q + 1] = fp8x2_to_bf16x2(v[q], true);
-            hi[2 * q] = fp8x2_to_bf16x2(v[2 + q], false);
-            hi[2 * q + 1] = fp8x2_to_bf16x2(v[2 + q], true);
-          }
-          kbv[2 * c] = as_bf16x8(lo);
-          kbv[2 * c + 1] = as_bf16x8(hi);
-        }
-      }
-      part[n] = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) acc = mfma16(qa[mt][s], kbv[s], acc);
-        // accumulator row r of this lane is head mt*16 + G*4 + r
-        const f32x4_t wv4 = *reinterpret_cast<const f32x4_t*>(&lds_w[mt * 16 + G * 4]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[n] += wv4[r] * relu_bits(acc[r]);
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < NE; ++n) {
-      part[n] = sum_rows16(part[n]);
-    }
-    if (G == 0) {
-      const int64_t tile = blockIdx.x + it * gridDim.x;
-#pragma unroll
-      for (int n = 0; n < NE; ++n) {
-        const int el = wv * (16 * NE) + n * 16 + l16;
-        // fp8: sigma_i scales the head-weighted sum (ReLU commutes with a
-        // positive scale); MXFP4 scales are already inside the key values
-        const float sc = MX ? part[n] : part[n] * __uint_as_float(lds_s[buf][el]);
-        lds_sc[(it - it_flushed) % SC_TILES][el] = sc;
-        if (hint && tile * TE + el < V) {
-          const uint32_t d = f32_key(sc) >> DIG_SHIFT;
-          atomicAdd(&lds_h[d >> 1], 1u << ((d & 1u) << 4));
-        }
-      }
-    }
-    if (it + 1 - it_flushed == SC_TILES && it + 1 < nmine) {
-      __syncthreads();
-      flush(it_flushed, it + 1);
-      it_flushed = it + 1;
-    }
-  }
-  __syncthreads();
-  flush(it_flushed, nmine);
-  zero_counters(zero, zero_n);
-  if (hint) {
-    uint32_t* g = hint + row * DIG_BINS;
-    for (int i = tid; i < DIG_BINS / 2; i += 256) {
-      const uint32_t v = lds_h[i];
-      if (v & 0xffffu) atomicAdd(&g[2 * i], v & 0xffffu);
-      if (v >> 16) atomicAdd(&g[2 * i + 1], v >> 16);
     }
   }
 }
@@ -1025,7 +883,7 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
   if (rows == 0 || a.N_max == 0) return hipSuccess;
   if (a.q_dt == DT_BF16_MXFP4) {
     // the FP4 QK path (MXFP4 keys, 64 x 128): the row scan for any query count
-    hipLaunchKernelGGL((idx_scan_fp4_kernel<0>), dim3((unsigned)lp_per_row(a, rows), (unsigned)rows),
+    hipLaunchKernelGGL((idx_scan_reg_kernel<DT_MXFP4, true, 0>), dim3((unsigned)lp_per_row(a, rows), (unsigned)rows),
                        dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx), a.w,
                        reinterpret_cast<const uint8_t*>(a.k_idx), reinterpret_cast<const uint32_t*>(a.k_scale),
                        a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)rows, a.hint,
@@ -1062,7 +920,8 @@ hipError_t run_indexer(const IndexerLaunch& a, hipStream_t st) {
       return hipGetLastError();
     }
     if (a.k_dt == DT_FP8 || a.k_dt == DT_MXFP4)
-      hipLaunchKernelGGL((a.k_dt == DT_FP8 ? idx_scan_lp_kernel<DT_FP8, 0> : idx_scan_lp_kernel<DT_MXFP4, 0>), grid,
+      hipLaunchKernelGGL((a.k_dt == DT_FP8 ? idx_scan_reg_kernel<DT_FP8, false, 0>
+                                           : idx_scan_reg_kernel<DT_MXFP4, false, 0>), grid,
                          dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.q_idx), a.w,
                          reinterpret_cast<const uint8_t*>(a.k_idx), reinterpret_cast<const uint32_t*>(a.k_scale),
                          a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores, CompressArgs{}, (unsigned)rows, a.hint,
@@ -1117,9 +976,11 @@ hipError_t run_compress_indexer(const CompressLaunch& c, const IndexerLaunch& a,
     const auto* k = reinterpret_cast<const uint8_t*>(a.k_idx);
     const auto* ks = reinterpret_cast<const uint32_t*>(a.k_scale);
     const bool f8 = a.k_dt == DT_FP8, o8 = c.out_dt == DT_KV_FP8;
-    auto kern = f8    ? (o8 ? idx_scan_lp_kernel<DT_FP8, DT_KV_FP8> : idx_scan_lp_kernel<DT_FP8, DT_BF16>)
-                : qf4 ? (o8 ? idx_scan_fp4_kernel<DT_KV_FP8> : idx_scan_fp4_kernel<DT_BF16>)
-                      : (o8 ? idx_scan_lp_kernel<DT_MXFP4, DT_KV_FP8> : idx_scan_lp_kernel<DT_MXFP4, DT_BF16>);
+    auto kern = f8 ? (o8 ? idx_scan_reg_kernel<DT_FP8, false, DT_KV_FP8> : idx_scan_reg_kernel<DT_FP8, false, DT_BF16>)
+                   : qf4 ? (o8 ? idx_scan_reg_kernel<DT_MXFP4, true, DT_KV_FP8>
+                               : idx_scan_reg_kernel<DT_MXFP4, true, DT_BF16>)
+                         : (o8 ? idx_scan_reg_kernel<DT_MXFP4, false, DT_KV_FP8>
+                               : idx_scan_reg_kernel<DT_MXFP4, false, DT_BF16>);
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, a.w, k, ks, a.q_pos, a.n_comp, a.Tq, a.N_max, a.m, a.scores,
                        ca0, (unsigned)rows, a.hint, a.zero, a.zero_n);
     return hipGetLastError();

@@ -16,9 +16,7 @@ typedef int i32x2_t __attribute__((ext_vector_type(2)));
 #define LN2_F 0.6931471805599453f
 
 // dtype tags (match the ABI codes)
-// DT_BF16_MXFP4 (indexer queries only): bf16 values that the scan quantises
-// to MXFP4 before an FP4 x FP4 product with MXFP4 keys.
-enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3, DT_KV_FP8 = 4, DT_BF16_MXFP4 = 5 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3, DT_KV_FP8 = 4 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 

@@ -17,6 +17,11 @@ struct CompressLaunch {
 };
 hipError_t run_compress(const CompressLaunch& a, hipStream_t st);
 
+// Indexer query dtype beside common.h's storage tags (the ABI's
+// CSA_BF16_MXFP4): bf16 values that the scan quantises to MXFP4 for an FP4 x
+// FP4 product with MXFP4 keys.
+constexpr int DT_BF16_MXFP4 = 5;
+
 struct IndexerLaunch {
   const void* q_idx;
   const float* w;

@@ -50,7 +50,7 @@ constexpr int TK_BINS = BINS;
 constexpr int TK_BPL = TK_BINS / TK_NT;    // histogram bins per thread
 constexpr int TK_DSHIFT = DSHIFT;
 constexpr int TK_ROW_MAX = 16384;          // keys of a row finished by one workgroup
-constexpr int TK_ROW_CAP = 4096;           // candidates of topk_row_kernel (32 KB of LDS)
+constexpr int TK_ROW_CAP = 3968;           // candidates of topk_row_kernel (31 KB of LDS: four workgroups per CU)
 constexpr int TK_FCH = 4096;               // keys per chunk workgroup: four wave segments of 1024
 constexpr int TK_SEG = TK_FCH / TK_NW;     // keys per wave segment
 constexpr int TK_WCAP = 512;               // candidates kept per wave segment
@@ -151,7 +151,7 @@ __device__ __forceinline__ void clear_hint(uint32_t* h) {
 // Rows of up to TK_ROW_MAX keys: one workgroup per row, keys in registers
 // ----------------------------------------------------------------------------
 template <int KPT>
-__global__ void __launch_bounds__(TK_NT) topk_row_kernel(TopkArgs a) {
+__global__ void __launch_bounds__(TK_NT) __attribute__((amdgpu_waves_per_eu(4, 4))) topk_row_kernel(TopkArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[TK_BINS];
   __shared__ __attribute__((aligned(16))) int red[2 * TK_NW], res[4];
   __shared__ __attribute__((aligned(16))) uint32_t ck[TK_ROW_CAP];

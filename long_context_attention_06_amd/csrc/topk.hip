@@ -355,12 +355,13 @@ __global__ void __launch_bounds__(TK_NT) topk_chunk_kernel(TopkArgs a) {
   }
   if (M >= K && M <= a.cap) {
     // gather: P threads per segment, each copying every P-th candidate (up to
-    // 16 loads in flight per thread)
+    // 16 loads in flight per thread); a segment's count is the step of the
+    // offsets (no second read of the counts)
     const int P = nseg >= TK_NT ? 1 : TK_NT / nseg;
     for (int s0 = 0; s0 < nseg; s0 += TK_NT / P) {
       const int sg = s0 + t / P, sub = t % P;
       if (sg < nseg) {
-        const int n = min(ld_dev(&a.wcnt[row * a.nseg + sg]), TK_WCAP), o = off[sg];
+        const int o = off[sg], n = (sg + 1 < nseg ? off[sg + 1] : M) - o;
         const int64_t lb = (row * a.nseg + sg) * (int64_t)TK_WCAP;
         for (int j0 = sub; j0 < n; j0 += 16 * P) {
           uint32_t kv[16];

@@ -31,12 +31,19 @@ int hip_status(hipError_t e, const char* op) {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Rows per split of the decode attention. Depends only on per-query shape
-// arguments, so a sequence's result never depends on the batch.
+// Rows per split of the sparse decode attention: 128 per query token of a
+// sequence, so a step with Tq tokens per sequence keeps about the same number
+// of workgroups per sequence as a one-token step (longer splits rather than
+// more of them). Depends only on per-sequence shape arguments, so a
+// sequence's result never depends on the batch.
 constexpr int SPARSE_SPLIT_ROWS = 128;
 constexpr int HCA_MAX_SPLITS = 16;  // dense rows are long: at most 16 splits of whole 32-row tiles
 
 int nsplit_for(int64_t slots, int rows) { return slots <= rows ? 1 : (int)((slots + rows - 1) / rows); }
+
+// at most 1024 rows: the fp32 decode kernel stages a split's top-k codes in
+// 1024 LDS slots (the bf16 kernel's row table holds 2048)
+int64_t sparse_split_rows(int64_t Tq) { return std::min<int64_t>(SPARSE_SPLIT_ROWS * std::max<int64_t>(1, Tq), 1024); }
 
 int hca_split_rows(int64_t slots) {
   const int64_t per = (slots + HCA_MAX_SPLITS - 1) / HCA_MAX_SPLITS;
@@ -324,16 +331,17 @@ struct QkOpts {
   float theta;
 };
 
-static size_t step_split_rows(int slots, int* nsplit) {
-  *nsplit = nsplit_for(slots, SPARSE_SPLIT_ROWS);
-  return *nsplit > 1 ? SPARSE_SPLIT_ROWS : slots;
+static size_t step_split_rows(int slots, int64_t Tq, int* nsplit) {
+  const int rows = (int)sparse_split_rows(Tq);
+  *nsplit = nsplit_for(slots, rows);
+  return *nsplit > 1 ? rows : slots;
 }
 
 size_t csa_decode_step_workspace_bytes(int64_t B, int64_t Tq, int64_t N_max, int top_k, int H, int D, int W) {
   if (B < 0 || Tq < 1 || N_max < 0 || top_k < 1 || H <= 0 || D <= 0 || W < 0) return 0;
   const int64_t nq = B * Tq;
   int ns = 0;
-  const int sr = (int)step_split_rows(top_k + W, &ns);
+  const int sr = (int)step_split_rows(top_k + W, Tq, &ns);
   (void)sr;
   return round256((size_t)nq * N_max * 4) + round256(csa::topk_ws_bytes(B, Tq, N_max, top_k, true)) +
          round256(attn_ws(nq, H, D, ns));
@@ -379,7 +387,7 @@ static int decode_step_impl(const void* Ca, const void* Cb, const void* Za, cons
 
   const int slots = top_k + W;
   int ns = 0;
-  const int sr = (int)step_split_rows(slots, &ns);
+  const int sr = (int)step_split_rows(slots, Tq, &ns);
   uint8_t* p = reinterpret_cast<uint8_t*>(ws);
   float* scores = reinterpret_cast<float*>(p);
   p += round256((size_t)nq * N_max * 4);
@@ -583,7 +591,9 @@ int csa_decode_step_noalloc(const void* Ca, const void* Cb, const void* Za, cons
 
 size_t sparse_mqa_decode_multi_workspace_bytes(int64_t B, int64_t Tq, int H, int D, int top_k, int W) {
   if (B < 0 || Tq < 1 || H <= 0 || D <= 0 || top_k < 0 || W < 0) return 0;
-  return attn_ws(B * Tq, H, D, nsplit_for((int64_t)top_k + W, SPARSE_SPLIT_ROWS));
+  int ns = 0;
+  step_split_rows(top_k + W, Tq, &ns);
+  return attn_ws(B * Tq, H, D, ns);
 }
 
 size_t sparse_mqa_decode_workspace_bytes(int64_t B, int H, int D, int top_k, int W) {
@@ -602,7 +612,8 @@ int sparse_mqa_decode_multi(const void* q, const void* kv_comp, const int32_t* t
   REQ(nq == 0 || top_k == 0 || (kv_comp && topk_idx), CSA_INVALID_ARG, "kv_comp and topk_idx must not be NULL");
   REQ(nq == 0 || W == 0 || (kv_win && win_len), CSA_INVALID_ARG, "kv_win and win_len must not be NULL");
   REQ((int64_t)top_k + W <= (1 << 24), CSA_UNSUPPORTED, "too many rows per query");
-  const int ns = nsplit_for((int64_t)top_k + W, SPARSE_SPLIT_ROWS);
+  int ns = 0;
+  const int sr = (int)step_split_rows(top_k + W, Tq, &ns);
   const size_t need = attn_ws(nq, H, D, ns);
   REQ(ws_bytes >= need, CSA_WORKSPACE_TOO_SMALL, "workspace too small");
   REQ(need == 0 || ws, CSA_INVALID_ARG, "ws must not be NULL");
@@ -629,7 +640,7 @@ int sparse_mqa_decode_multi(const void* q, const void* kv_comp, const int32_t* t
   a.kv_dt = kv_dt;
   a.out_dt = out_dt;
   a.slots = top_k + W;
-  a.split_rows = ns > 1 ? SPARSE_SPLIT_ROWS : a.slots;
+  a.split_rows = sr;
   a.nsplit = ns;
   a.part_o = reinterpret_cast<float*>(ws);
   a.part_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + round256((size_t)nq * ns * H * D * 4));

@@ -95,6 +95,14 @@ def test_indexer_validation():
     assert f(P, P, P, P, P, P, 1, 1, 64, 48, 100, 4, 1, 3, P, None) == L.INVALID_ARG
     assert f(P, P, P, P + 2, P, P, 1, 1, 64, 128, 100, 4, 1, 3, P, None) == L.INVALID_ARG
     assert f(P, P, P, P, P, P, 1, 1, 64, 128, 100, 4, 1, 4, P, None) == L.INVALID_ARG
+    # the FP4-quantised query (BF16_MXFP4) goes with MXFP4 keys and the 64 x 128 indexer only;
+    # KV_FP8 and codes past BF16_MXFP4 are no query dtype
+    assert f(P, P, P, None, P, P, 1, 1, 64, 128, 100, 4, L.BF16_MXFP4, L.BF16, P, None) == L.UNSUPPORTED
+    assert f(P, P, P, P, P, P, 1, 1, 64, 128, 100, 4, L.BF16_MXFP4, L.FP8_E4M3, P, None) == L.UNSUPPORTED
+    assert f(P, P, P, P, P, P, 1, 1, 32, 128, 100, 4, L.BF16_MXFP4, L.MXFP4, P, None) == L.UNSUPPORTED
+    assert f(P, P, P, None, P, P, 1, 1, 64, 128, 100, 4, L.BF16_MXFP4, L.MXFP4, P, None) == L.INVALID_ARG
+    assert f(P, P, P, P, P, P, 1, 1, 64, 128, 100, 4, L.KV_FP8, L.MXFP4, P, None) == L.INVALID_ARG
+    assert f(P, P, P, P, P, P, 1, 1, 64, 128, 100, 4, 6, L.MXFP4, P, None) == L.INVALID_ARG
     # unsupported head shape
     assert f(P, P, P, None, P, P, 1, 1, 32, 128, 100, 4, 1, 1, P, None) == L.UNSUPPORTED
     # fp32 keys with bf16 queries
@@ -158,3 +166,11 @@ def test_attention_validation():
     assert hp(P, P, P, P, P, 0.0, 4, 64, 512, 512, 128, 65536, 128, 1, 1, P, None, None, 0, None) == L.INVALID_ARG
     # no entries and no window is valid (out = 0 or the sink alone); kv_comp may then be null
     assert L.hca_prefill_workspace_bytes(4096, 64, 512, 8192, 128) == 0
+
+
+def test_fp4_query_binding():
+    import torch
+    assert L._qdt(torch.zeros(1, dtype=torch.bfloat16), True) == L.BF16_MXFP4
+    assert L._qdt(torch.zeros(1, dtype=torch.bfloat16), False) == L.BF16
+    with pytest.raises(ValueError):
+        L._qdt(torch.zeros(1, dtype=torch.float32), True)

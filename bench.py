@@ -7,11 +7,11 @@ heads x 512, a 128-token window and a sink, bf16. One step is one decode token
 per sequence through the whole path:
     csa_compress   (entry N-1 completes at this token: n is a multiple of m)
     indexer_score  (the dominant HBM stream; one launch with the compression)
-    top-k, sparse MQA and the merge of its splits (one launch)
+    top-k, sparse MQA and the merge of its splits (three launches)
 as one csa_decode_step call. Inputs are synthetic (seeded generator),
 resident in HBM before timing, and rotated over several device replicas so
 that no step reads cache-resident data from the previous one. The default
-line also carries c5, c4 and c3 (below), each timed the same way, under
+line also carries c5, c4, c3 and c2q (below), each timed the same way, under
 "workloads".
 
 Other workloads: c5 (1M context, E4M3 indexer keys), c2x (c2 with MXFP4
@@ -58,14 +58,14 @@ def _args():
                     help="budget of the CPU baseline of each secondary workload")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="with the default workload, skip the secondary workloads (c5, c4, c3)")
+                    help="with the default workload, skip the secondary workloads (c5, c4, c3, c2q)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run plain 1 GiB device-to-device copies: the known-size reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
-EXTRAS = ("c5", "c4", "c3")  # secondary workloads carried by the default line
+EXTRAS = ("c5", "c4", "c3", "c2q")  # secondary workloads carried by the default line
 
 
 def _src_hash(names):
